@@ -1,0 +1,107 @@
+"""fp64 CPU oracle for causal linear attention -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The product path (the HIP library and its
+binding in ``chunkwise_linear_rnn_causal_amd``) never imports, links or calls it,
+and the oracle imports nothing from the product path.
+
+The arithmetic lives in ``oracle.c`` (plain C, float64, naive per-token recurrence;
+see that file's header for the definitions and the passages they follow). This
+module is a ctypes wrapper: it converts arrays to contiguous float64 and calls it.
+All functions here are pinned by ``tests/test_oracle_pins.py``; no function is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import build as _build
+
+VARIANT_ID = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3}
+
+_lib = None
+_lib_path = None
+
+
+def load(path: Optional[str] = None):
+    """Load (building first if missing or stale) the oracle shared library."""
+    global _lib, _lib_path
+    path = path or _build.LIB
+    if _lib is not None and _lib_path == path:
+        return _lib
+    if path == _build.LIB and _build.stale():
+        _build.build()
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    L = ctypes.c_long
+    lib.oracle_forward.argtypes = [ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                   L, L, L, L, ctypes.c_int]
+    lib.oracle_forward.restype = ctypes.c_int
+    lib.oracle_decode_step.argtypes = [ctypes.c_int, dp, dp, dp, dp, dp, dp, L, L, L, ctypes.c_int]
+    lib.oracle_decode_step.restype = ctypes.c_int
+    lib.oracle_abi_version.restype = ctypes.c_int
+    _lib, _lib_path = lib, path
+    return lib
+
+
+def _p(x):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _c64(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def forward(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in=None,
+            threads: int = 0, lib=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Run the recurrence over every leading (batch, head) slice.
+
+    q, k: [..., L, dk]; v: [..., L, dv]; log_gate, beta: [..., L];
+    state_in: [..., dk, dv]; z_in: [..., dk]. Returns (o [..., L, dv],
+    state_out [..., dk, dv], z_out [..., dk]) in float64.
+    """
+    lib = lib or load()
+    q, k, v = _c64(q), _c64(k), _c64(v)
+    lead = q.shape[:-2]
+    L, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    assert k.shape == q.shape and v.shape[:-1] == q.shape[:-1]
+    lg, be = _c64(log_gate), _c64(beta)
+    s_in, zi = _c64(state_in), _c64(z_in)
+    for x, shp in ((lg, lead + (L,)), (be, lead + (L,)), (s_in, lead + (dk, dv)), (zi, lead + (dk,))):
+        assert x is None or x.shape == shp, (x.shape, shp)
+    o = np.zeros(lead + (L, dv), np.float64)
+    s_out = np.zeros(lead + (dk, dv), np.float64)
+    z_out = np.zeros(lead + (dk,), np.float64)
+    st = lib.oracle_forward(VARIANT_ID[variant], _p(q), _p(k), _p(v), _p(lg), _p(be), _p(s_in),
+                            _p(zi), _p(o), _p(s_out), _p(z_out), BH, L, dk, dv, int(threads))
+    if st != 0:
+        raise ValueError(f"oracle_forward failed with status {st}")
+    return o, s_out, z_out
+
+
+def decode_step(variant: str, q, k, v, log_gate, state, threads: int = 0, lib=None):
+    """One in-place decode step on a copy of ``state``; returns (o, new_state).
+
+    q, k: [..., dk]; v: [..., dv]; log_gate: [...]; state: [..., dk, dv].
+    """
+    lib = lib or load()
+    q, k, v = _c64(q), _c64(k), _c64(v)
+    lead = q.shape[:-1]
+    dk, dv = q.shape[-1], v.shape[-1]
+    NH = int(np.prod(lead)) if lead else 1
+    S = np.array(state, dtype=np.float64, copy=True, order="C")
+    lg = _c64(log_gate)
+    o = np.zeros(lead + (dv,), np.float64)
+    st = lib.oracle_decode_step(VARIANT_ID[variant], _p(q), _p(k), _p(v), _p(lg), _p(S), _p(o),
+                                NH, dk, dv, int(threads))
+    if st != 0:
+        raise ValueError(f"oracle_decode_step failed with status {st}")
+    return o, S

@@ -1,0 +1,173 @@
+/*
+ * oracle.c -- fp64 CPU oracle for causal linear attention (TEST INFRASTRUCTURE).
+ *
+ * Only the tests, the package's smoke check and the benchmark's CPU-baseline leg
+ * may load this library. It shares no code with the GPU path. It is deliberately
+ * plain and slow: the naive per-token recurrence, in float64, with sequential
+ * summation over t, exactly as the pages state the method.
+ *
+ * Canonical orientation: the state S is d_k x d_v (row = key channel), S_t =
+ * S_{t-1} + k_t v_t^T and o_t = S_t^T q_t  (tensorplay "Talk Linear Attention",
+ * section 2.1, the recurrence and output equations). Pages that write the state
+ * as v k^T (wln20 "LLM注意力优化：线性注意力", RNN form; tensorplay section 6)
+ * describe its transpose; outputs are identical.
+ *
+ * Variants (per batch-head, independently):
+ *   PLAIN        S <- S + k v^T;                      o = S^T q
+ *                (tensorplay section 2.1)
+ *   NORMALIZED   S <- S + k v^T;  z <- z + k;         o = S^T q / (q . z)
+ *                q and k arrive already feature-mapped (proig-chaa notes
+ *                sections 13-14: causal recurrence of S and z)
+ *   DECAY        S <- gamma S + k v^T, gamma = exp(l); o = S^T q
+ *                (wln20, data-dependent decay equation; proig-chaa section 20)
+ *   GATED_DELTA  r = S^T k (retrieve); S <- alpha (S - beta k r^T) + beta k v^T;
+ *                o = S^T q, alpha = exp(l) (alpha = 1 when no log-gate is given)
+ *                This is the transpose of S'_t = S'_{t-1} alpha_t (I - beta_t k_t
+ *                k_t^T) + beta_t v_t k_t^T, o_t = S'_t q_t (wln20, Gated DeltaNet
+ *                section; tensorplay section 6.2 reparameterised delta rule).
+ *
+ * Inputs are float64 copies of exactly the values the GPU reads (bf16 or fp32
+ * widened without rounding). Gates are log-gates l = log(gamma) or log(alpha);
+ * the oracle forms gamma = exp(l) in float64.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q, k  [BH, L, dk]     v, o  [BH, L, dv]     log_gate, beta  [BH, L]
+ *   state_in, state_out  [BH, dk, dv]          z_in, z_out  [BH, dk]
+ * NULL state_in / z_in mean zero; NULL state_out / z_out mean "not returned".
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_PLAIN 0
+#define OR_NORMALIZED 1
+#define OR_DECAY 2
+#define OR_GATED_DELTA 3
+
+#define OR_OK 0
+#define OR_BAD_ARG 1
+#define OR_NO_MEM 2
+
+int oracle_abi_version(void) { return 1; }
+
+/* One batch-head: the whole sequence, token by token. */
+static int run_head(int variant, const double *q, const double *k, const double *v,
+                    const double *lg, const double *beta, const double *s_in,
+                    const double *z_in, double *o, double *s_out, double *z_out,
+                    long L, long dk, long dv)
+{
+    double *S = (double *)malloc(sizeof(double) * (size_t)(dk * dv));
+    double *z = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *r = (double *)malloc(sizeof(double) * (size_t)dv);
+    if (!S || !z || !r) {
+        free(S); free(z); free(r);
+        return OR_NO_MEM;
+    }
+    for (long i = 0; i < dk * dv; ++i) S[i] = s_in ? s_in[i] : 0.0;
+    for (long i = 0; i < dk; ++i) z[i] = z_in ? z_in[i] : 0.0;
+
+    for (long t = 0; t < L; ++t) {
+        const double *qt = q + t * dk;
+        const double *kt = k + t * dk;
+        const double *vt = v + t * dv;
+        double *ot = o + t * dv;
+
+        if (variant == OR_PLAIN || variant == OR_NORMALIZED) {
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j)
+                    S[i * dv + j] += kt[i] * vt[j];
+            if (variant == OR_NORMALIZED)
+                for (long i = 0; i < dk; ++i) z[i] += kt[i];
+        } else if (variant == OR_DECAY) {
+            double g = exp(lg[t]);
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j)
+                    S[i * dv + j] = g * S[i * dv + j] + kt[i] * vt[j];
+        } else { /* OR_GATED_DELTA */
+            double a = lg ? exp(lg[t]) : 1.0;
+            double b = beta[t];
+            for (long j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < dk; ++i) acc += S[i * dv + j] * kt[i];
+                r[j] = acc;
+            }
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j)
+                    S[i * dv + j] = a * (S[i * dv + j] - b * kt[i] * r[j]) + b * kt[i] * vt[j];
+        }
+
+        for (long j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < dk; ++i) acc += S[i * dv + j] * qt[i];
+            ot[j] = acc;
+        }
+        if (variant == OR_NORMALIZED) {
+            double den = 0.0;
+            for (long i = 0; i < dk; ++i) den += qt[i] * z[i];
+            for (long j = 0; j < dv; ++j) ot[j] /= den;
+        }
+    }
+    if (s_out) memcpy(s_out, S, sizeof(double) * (size_t)(dk * dv));
+    if (z_out) memcpy(z_out, z, sizeof(double) * (size_t)dk);
+    free(S); free(z); free(r);
+    return OR_OK;
+}
+
+/*
+ * Full forward over BH independent batch-heads. nthreads <= 0 uses the OpenMP
+ * default. Returns OR_OK, OR_BAD_ARG or OR_NO_MEM.
+ */
+int oracle_forward(int variant, const double *q, const double *k, const double *v,
+                   const double *log_gate, const double *beta, const double *state_in,
+                   const double *z_in, double *o, double *state_out, double *z_out,
+                   long BH, long L, long dk, long dv, int nthreads)
+{
+    if (variant < OR_PLAIN || variant > OR_GATED_DELTA) return OR_BAD_ARG;
+    if (BH < 0 || L < 0 || dk <= 0 || dv <= 0) return OR_BAD_ARG;
+    if ((BH > 0 && L > 0) && (!q || !k || !v || !o)) return OR_BAD_ARG;
+    if (variant == OR_DECAY && L > 0 && !log_gate) return OR_BAD_ARG;
+    if (variant == OR_GATED_DELTA && L > 0 && !beta) return OR_BAD_ARG;
+
+    int status = OR_OK;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) reduction(max : status)
+#endif
+    for (long h = 0; h < BH; ++h) {
+        int st = run_head(variant, q + h * L * dk, k + h * L * dk, v + h * L * dv,
+                          log_gate ? log_gate + h * L : NULL, beta ? beta + h * L : NULL,
+                          state_in ? state_in + h * dk * dv : NULL, z_in ? z_in + h * dk : NULL,
+                          o + h * L * dv, state_out ? state_out + h * dk * dv : NULL,
+                          z_out ? z_out + h * dk : NULL, L, dk, dv);
+        if (st > status) status = st;
+    }
+    return status;
+}
+
+/*
+ * One-token decode step of the DECAY (or PLAIN, log_gate NULL) recurrence, in
+ * place on the state: S <- exp(l) S + k v^T, then o = S^T q  (tensorplay
+ * section 2.2: constant-size state carried from token to token; wln20 decay
+ * equation). Layouts: q, k [NH, dk]; v, o [NH, dv]; log_gate [NH]; state [NH, dk, dv].
+ */
+int oracle_decode_step(int variant, const double *q, const double *k, const double *v,
+                       const double *log_gate, double *state, double *o,
+                       long NH, long dk, long dv, int nthreads)
+{
+    if (variant != OR_PLAIN && variant != OR_DECAY) return OR_BAD_ARG;
+    if (variant == OR_DECAY && !log_gate) return OR_BAD_ARG;
+    if (NH < 0 || dk <= 0 || dv <= 0 || !state) return OR_BAD_ARG;
+    int status = OR_OK;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) reduction(max : status)
+#endif
+    for (long h = 0; h < NH; ++h) {
+        int st = run_head(variant, q + h * dk, k + h * dk, v + h * dv,
+                          log_gate ? log_gate + h : NULL, NULL, state + h * dk * dv, NULL,
+                          o + h * dv, state + h * dk * dv, NULL, 1, dk, dv);
+        if (st > status) status = st;
+    }
+    return status;
+}

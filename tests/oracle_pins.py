@@ -1,0 +1,495 @@
+"""Pins of the fp64 oracle against facts other than itself.
+
+Each pin takes the loaded oracle library and raises AssertionError when the oracle
+disagrees with a closed form, an invariant, a special case that reduces to a
+textbook formula, or an exact rational brute force. None of them re-types the
+oracle's recurrence: the references here are the parallel (quadratic) forms, the
+explicit product expansion, the retrieve/merge/overwrite form and a chunkwise WY
+form, each written from the passage it cites.
+
+Used twice: tests/test_oracle_pins.py runs every pin on the real oracle, and
+tests/test_oracle_mutants.py runs them on deliberately broken copies of the
+oracle to show that each plausible mistake fails at least one pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = math.sqrt(float(np.mean(b * b))) or 1.0
+    return float(np.max(np.abs(a - b))) / scale
+
+
+def _mask(L):
+    # inclusive causal mask j <= t (tensorplay section 2.1, sum over j = 1..t)
+    return np.tril(np.ones((L, L)))
+
+
+# ---------------------------------------------------------------------------
+# PLAIN
+# ---------------------------------------------------------------------------
+def pin_plain_quadratic(lib):
+    """O = (Q K^T (.) M) V  (tensorplay section 2.1, parallel form)."""
+    r = _rng(1)
+    q, k = r.standard_normal((3, 37, 5)), r.standard_normal((3, 37, 5))
+    v = r.standard_normal((3, 37, 4))
+    o, _, _ = oracle.forward("plain", q, k, v, lib=lib)
+    ref = (q @ k.transpose(0, 2, 1) * _mask(37)) @ v
+    assert _rel(o, ref) <= 1e-12, _rel(o, ref)
+
+
+def pin_plain_fraction_bruteforce(lib):
+    """o_t = sum_{j<=t} (q_t . k_j) v_j in exact integer arithmetic
+    (tensorplay section 2.1, per-token sum form). Small integers make every fp64
+    operation of the oracle exact, so agreement must be bit-exact."""
+    r = _rng(2)
+    L, dk, dv = 7, 3, 2
+    q = r.integers(-3, 4, (L, dk))
+    k = r.integers(-3, 4, (L, dk))
+    v = r.integers(-3, 4, (L, dv))
+    ref = np.zeros((L, dv), dtype=object)
+    for t in range(L):
+        for j in range(t + 1):
+            w = sum(int(q[t, i]) * int(k[j, i]) for i in range(dk))
+            for c in range(dv):
+                ref[t, c] += w * int(v[j, c])
+    o, _, _ = oracle.forward("plain", q.astype(float), k.astype(float), v.astype(float), lib=lib)
+    assert np.array_equal(o, ref.astype(np.float64)), (o, ref)
+
+
+def pin_plain_final_state(lib):
+    """With S_0 given, S_L = S_0 + K^T V: the re-associated product of the
+    non-causal form (proig-chaa notes section 3; tensorplay section 2.1)."""
+    r = _rng(3)
+    q, k = r.standard_normal((2, 19, 6)), r.standard_normal((2, 19, 6))
+    v = r.standard_normal((2, 19, 3))
+    s0 = r.standard_normal((2, 6, 3))
+    o, s, _ = oracle.forward("plain", q, k, v, state_in=s0, lib=lib)
+    assert _rel(s, s0 + k.transpose(0, 2, 1) @ v) <= 1e-12
+    # outputs with a carried-in state: Q S_0 + (Q K^T (.) M) V
+    ref = q @ s0 + (q @ k.transpose(0, 2, 1) * _mask(19)) @ v
+    assert _rel(o, ref) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# NORMALIZED
+# ---------------------------------------------------------------------------
+def _phi(x):
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def pin_normalized_quadratic(lib):
+    """y_i = sum_{j<=i} (phi_i . phi_j) v_j / sum_{j<=i} phi_i . phi_j, with an
+    optional carried-in (S_0, z_0) adding phi_i^T S_0 and phi_i . z_0
+    (proig-chaa notes sections 13-14)."""
+    r = _rng(4)
+    q, k = _phi(r.standard_normal((2, 29, 5))), _phi(r.standard_normal((2, 29, 5)))
+    v = r.standard_normal((2, 29, 3))
+    A = q @ k.transpose(0, 2, 1) * _mask(29)
+    o, s, z = oracle.forward("normalized", q, k, v, lib=lib)
+    ref = (A @ v) / A.sum(-1, keepdims=True)
+    assert _rel(o, ref) <= 1e-12, _rel(o, ref)
+    assert _rel(z, k.sum(1)) <= 1e-13
+    s0 = r.standard_normal((2, 5, 3))
+    z0 = 1.0 + r.random((2, 5))
+    o2, s2, z2 = oracle.forward("normalized", q, k, v, state_in=s0, z_in=z0, lib=lib)
+    num = q @ s0 + A @ v
+    den = (q * z0[:, None, :]).sum(-1, keepdims=True) + A.sum(-1, keepdims=True)
+    assert _rel(o2, num / den) <= 1e-12
+    assert _rel(z2, z0 + k.sum(1)) <= 1e-13
+    assert _rel(s2, s0 + k.transpose(0, 2, 1) @ v) <= 1e-12
+
+
+def pin_normalized_constant_v(lib):
+    """The normalised output is a weighted average of v_1..v_i (weights sum to
+    one), so v == c gives o == c (proig-chaa notes section 13)."""
+    r = _rng(5)
+    q, k = _phi(r.standard_normal((1, 40, 4))), _phi(r.standard_normal((1, 40, 4)))
+    v = np.broadcast_to(np.array([2.5, -1.0, 0.125]), (1, 40, 3)).copy()
+    o, _, _ = oracle.forward("normalized", q, k, v, lib=lib)
+    assert np.max(np.abs(o - v)) <= 1e-13
+
+
+def pin_normalized_hull(lib):
+    """Positive weights summing to one: each o_i lies within the per-column range
+    of v_1..v_i."""
+    r = _rng(6)
+    q, k = _phi(r.standard_normal((1, 50, 4))), _phi(r.standard_normal((1, 50, 4)))
+    v = r.standard_normal((1, 50, 3))
+    o, _, _ = oracle.forward("normalized", q, k, v, lib=lib)
+    lo = np.minimum.accumulate(v[0], axis=0)
+    hi = np.maximum.accumulate(v[0], axis=0)
+    assert np.all(o[0] >= lo - 1e-12) and np.all(o[0] <= hi + 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# DECAY
+# ---------------------------------------------------------------------------
+def pin_decay_quadratic(lib):
+    """Cumulative decay b_t = prod_{j<=t} gamma_j turns the recurrence into
+    O = ((Q K^T) (.) D) V with D_ij = b_i / b_j for j <= i (tensorplay section 5.2),
+    evaluated here with the global log cumsum G; a carried-in S_0 adds
+    diag(b) Q S_0 and the final state is b_L S_0 + sum_j (b_L/b_j) k_j v_j^T."""
+    r = _rng(7)
+    L = 33
+    q, k = r.standard_normal((2, L, 5)), r.standard_normal((2, L, 5))
+    v = r.standard_normal((2, L, 4))
+    lg = np.log(1.0 / (1.0 + np.exp(-r.normal(2.0, 1.0, (2, L)))))
+    s0 = r.standard_normal((2, 5, 4))
+    G = np.cumsum(lg, axis=1)
+    D = np.exp(G[:, :, None] - G[:, None, :]) * _mask(L)
+    ref = np.exp(G)[:, :, None] * (q @ s0) + (q @ k.transpose(0, 2, 1) * D) @ v
+    o, s, _ = oracle.forward("decay", q, k, v, log_gate=lg, state_in=s0, lib=lib)
+    assert _rel(o, ref) <= 1e-12, _rel(o, ref)
+    sref = np.exp(G[:, -1])[:, None, None] * s0 + \
+        (k * np.exp(G[:, -1:] - G)[:, :, None]).transpose(0, 2, 1) @ v
+    assert _rel(s, sref) <= 1e-12
+
+
+def pin_decay_zero_gate_is_plain(lib):
+    """gamma == 1 (log-gate 0) reduces the decayed recurrence to the plain one."""
+    r = _rng(8)
+    q, k, v = (r.standard_normal((2, 21, 4)) for _ in range(3))
+    o1, s1, _ = oracle.forward("decay", q, k, v, log_gate=np.zeros((2, 21)), lib=lib)
+    o2, s2, _ = oracle.forward("plain", q, k, v, lib=lib)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+def pin_decay_fraction_half(lib):
+    """Constant gamma = 1/2 with integer inputs: o_t = sum_{j<=t} 2^{-(t-j)}
+    (q_t . k_j) v_j in exact rationals (wln20, data-independent decay with a
+    constant 0 < gamma < 1). The oracle forms gamma = exp(log 1/2), which may be
+    one ulp off, hence a 1e-13 relative bound instead of equality."""
+    r = _rng(9)
+    L, dk, dv = 8, 3, 2
+    q = r.integers(-3, 4, (L, dk))
+    k = r.integers(-3, 4, (L, dk))
+    v = r.integers(-3, 4, (L, dv))
+    ref = np.zeros((L, dv), dtype=object)
+    for t in range(L):
+        for j in range(t + 1):
+            w = Fraction(sum(int(q[t, i]) * int(k[j, i]) for i in range(dk)), 2 ** (t - j))
+            for c in range(dv):
+                ref[t, c] += w * int(v[j, c])
+    o, _, _ = oracle.forward("decay", q.astype(float), k.astype(float), v.astype(float),
+                             log_gate=np.full(L, math.log(0.5)), lib=lib)
+    assert _rel(o, ref.astype(np.float64)) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# GATED DELTA
+# ---------------------------------------------------------------------------
+def _gdn_retrieve_merge_overwrite(q, k, v, alpha, beta, s0=None):
+    """DeltaNet written as retrieve / merge / overwrite on the decayed state, in the
+    pages' v k^T orientation (S' is d_v x d_k): S~ = alpha S'; v_old = S~ k;
+    v_new = beta v + (1 - beta) v_old; S' = S~ - v_old k^T + v_new k^T; o = S' q
+    (tensorplay section 6.1; wln20 DeltaNet and Gated DeltaNet sections)."""
+    L, dk = q.shape
+    dv = v.shape[1]
+    Sp = np.zeros((dv, dk)) if s0 is None else s0.T.copy()
+    o = np.zeros((L, dv))
+    for t in range(L):
+        St = alpha[t] * Sp
+        v_old = St @ k[t]
+        v_new = beta[t] * v[t] + (1.0 - beta[t]) * v_old
+        Sp = St - np.outer(v_old, k[t]) + np.outer(v_new, k[t])
+        o[t] = Sp @ q[t]
+    return o, Sp.T
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def pin_gdn_retrieve_merge_overwrite(lib):
+    r = _rng(10)
+    L, dk, dv = 31, 6, 5
+    q, k = _unit(r.standard_normal((L, dk))), _unit(r.standard_normal((L, dk)))
+    v = r.standard_normal((L, dv))
+    lg = np.log(1.0 / (1.0 + np.exp(-r.normal(3.0, 1.0, L))))
+    beta = 1.0 / (1.0 + np.exp(-r.normal(0.0, 1.0, L)))
+    s0 = r.standard_normal((dk, dv))
+    ref_o, ref_s = _gdn_retrieve_merge_overwrite(q, k, v, np.exp(lg), beta, s0)
+    o, s, _ = oracle.forward("gated_delta", q[None], k[None], v[None], log_gate=lg[None],
+                             beta=beta[None], state_in=s0[None], lib=lib)
+    assert _rel(o[0], ref_o) <= 1e-12, _rel(o[0], ref_o)
+    assert _rel(s[0], ref_s) <= 1e-12
+
+
+def pin_gdn_alpha_one_is_deltanet(lib):
+    """alpha == 1 gives DeltaNet (tensorplay section 6.2); an absent log-gate means
+    alpha == 1."""
+    r = _rng(11)
+    L, dk, dv = 17, 4, 3
+    q, k = _unit(r.standard_normal((1, L, dk))), _unit(r.standard_normal((1, L, dk)))
+    v = r.standard_normal((1, L, dv))
+    beta = r.random((1, L))
+    o1, s1, _ = oracle.forward("gated_delta", q, k, v, log_gate=None, beta=beta, lib=lib)
+    o2, s2, _ = oracle.forward("gated_delta", q, k, v, log_gate=np.zeros((1, L)), beta=beta, lib=lib)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+    ref_o, _ = _gdn_retrieve_merge_overwrite(q[0], k[0], v[0], np.ones(L), beta[0])
+    assert _rel(o1[0], ref_o) <= 1e-12
+
+
+def pin_gdn_beta_zero_pure_decay(lib):
+    """beta == 0: nothing is written, S_t = (prod alpha) S_0 and o_t = S_t^T q_t."""
+    r = _rng(12)
+    L, dk, dv = 15, 4, 3
+    q, k = r.standard_normal((1, L, dk)), _unit(r.standard_normal((1, L, dk)))
+    v = r.standard_normal((1, L, dv))
+    lg = -r.random((1, L)) * 0.3
+    s0 = r.standard_normal((1, dk, dv))
+    o, s, _ = oracle.forward("gated_delta", q, k, v, log_gate=lg, beta=np.zeros((1, L)),
+                             state_in=s0, lib=lib)
+    a = np.exp(np.cumsum(lg[0]))
+    assert _rel(o[0], a[:, None] * (q[0] @ s0[0])) <= 1e-12
+    assert _rel(s[0], a[-1] * s0[0]) <= 1e-12
+
+
+RECALL_FIXTURES = ("recall_a4b3c6.txt", "recall_rebind.txt")
+
+
+def _read_golden_recall(name):
+    """A tests/golden/recall_*.txt fixture: keys, values, queries, expected outputs."""
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, val = line.split(":", 1)
+            rows[key.strip()] = val.split()
+    return rows
+
+
+def pin_gdn_onehot_recall(lib):
+    """Associative recall with orthonormal (one-hot) keys, beta = 1, alpha = 1:
+    the delta rule returns exactly the last value bound to the queried key, while
+    plain linear attention returns the sum of every value bound to it
+    (tensorplay section 6: A4B3C6 -> A?C? -> 4,6; proig-chaa sections 18-19 on
+    interference). Values from tests/golden/recall_*.txt."""
+    for name in RECALL_FIXTURES:
+        _check_recall(lib, _read_golden_recall(name))
+
+
+def _check_recall(lib, g):
+    alphabet = g["alphabet"]
+    d = len(alphabet)
+    writes = [(w[0], float(w[1:])) for w in g["writes"]]
+    queries = g["queries"]
+    toks = len(writes) + len(queries)
+    q = np.zeros((1, toks, d)); k = np.zeros((1, toks, d)); v = np.zeros((1, toks, 1))
+    for t, (key, val) in enumerate(writes):
+        k[0, t, alphabet.index(key)] = 1.0
+        v[0, t, 0] = val
+    for i, key in enumerate(queries):
+        q[0, len(writes) + i, alphabet.index(key)] = 1.0
+    beta = np.ones((1, toks))
+    o, _, _ = oracle.forward("gated_delta", q, k, v, beta=beta, lib=lib)
+    got = o[0, len(writes):, 0]
+    assert np.array_equal(got, np.array([float(x) for x in g["delta_expect"]])), got
+    o2, _, _ = oracle.forward("plain", q, k, v, lib=lib)
+    got2 = o2[0, len(writes):, 0]
+    assert np.array_equal(got2, np.array([float(x) for x in g["plain_expect"]])), got2
+
+
+def pin_gdn_unit_key_identity(lib):
+    """With |k_t| = 1 the reparameterised rule gives S_t^T k_t =
+    alpha_t (1 - beta_t) S_{t-1}^T k_t + beta_t v_t at every step (from
+    S'_t = alpha S'_{t-1}(I - beta k k^T) + beta v k^T, tensorplay section 6.2:
+    the written value is the beta-merge of old and new)."""
+    r = _rng(13)
+    L, dk, dv = 12, 5, 4
+    q, k = r.standard_normal((L, dk)), _unit(r.standard_normal((L, dk)))
+    v = r.standard_normal((L, dv))
+    lg = -r.random(L) * 0.2
+    beta = r.random(L)
+    S = r.standard_normal((dk, dv))
+    for t in range(L):
+        _, S1, _ = oracle.forward("gated_delta", q[None, t:t + 1], k[None, t:t + 1],
+                                  v[None, t:t + 1], log_gate=lg[None, t:t + 1],
+                                  beta=beta[None, t:t + 1], state_in=S[None], lib=lib)
+        lhs = S1[0].T @ k[t]
+        rhs = math.exp(lg[t]) * (1 - beta[t]) * (S.T @ k[t]) + beta[t] * v[t]
+        assert np.max(np.abs(lhs - rhs)) <= 1e-12
+        S = S1[0]
+
+
+def pin_gdn_fraction_product_expansion(lib):
+    """Exact rationals: S_t = sum_{j<=t} [A_t ... A_{j+1}] beta_j k_j v_j^T with
+    A_s = alpha_s (I - beta_s k_s k_s^T), o_t = S_t^T q_t: the unrolled
+    identity-plus-low-rank products (tensorplay sections 6.2 and 7.1, canonical
+    d_k x d_v orientation). The oracle receives alpha as log(alpha) and forms
+    exp in fp64, hence a 1e-12 relative bound."""
+    r = _rng(14)
+    L, dk, dv = 6, 3, 2
+    Fr = Fraction
+    q = [[Fr(int(x)) for x in row] for row in r.integers(-2, 3, (L, dk))]
+    k = [[Fr(int(x)) for x in row] for row in r.integers(-1, 2, (L, dk))]
+    v = [[Fr(int(x)) for x in row] for row in r.integers(-3, 4, (L, dv))]
+    alpha = [Fr(int(a), 8) for a in r.integers(5, 9, L)]
+    beta = [Fr(int(b), 4) for b in r.integers(0, 5, L)]
+
+    def eye(n):
+        return [[Fr(int(i == j)) for j in range(n)] for i in range(n)]
+
+    def matmul(A, B):
+        return [[sum((A[i][m] * B[m][j] for m in range(len(B))), Fr(0)) for j in range(len(B[0]))]
+                for i in range(len(A))]
+
+    def transition(s):
+        return [[alpha[s] * ((1 if i == j else 0) - beta[s] * k[s][i] * k[s][j]) for j in range(dk)]
+                for i in range(dk)]
+
+    o_ref = []
+    for t in range(L):
+        S = [[Fr(0)] * dv for _ in range(dk)]
+        for j in range(t + 1):
+            P = eye(dk)
+            for s in range(t, j, -1):
+                P = matmul(P, transition(s))
+            w = [[beta[j] * k[j][i] * v[j][c] for c in range(dv)] for i in range(dk)]
+            PW = matmul(P, w)
+            S = [[S[i][c] + PW[i][c] for c in range(dv)] for i in range(dk)]
+        o_ref.append([sum((S[i][c] * q[t][i] for i in range(dk)), Fr(0)) for c in range(dv)])
+    f = lambda M: np.array([[float(x) for x in row] for row in M])
+    o, _, _ = oracle.forward("gated_delta", f(q)[None], f(k)[None], f(v)[None],
+                             log_gate=np.log(np.array([float(a) for a in alpha]))[None],
+                             beta=np.array([float(b) for b in beta])[None], lib=lib)
+    assert _rel(o[0], f(o_ref)) <= 1e-12, _rel(o[0], f(o_ref))
+
+
+def gdn_chunkwise_wy(q, k, v, lg, beta, C, s0=None):
+    """Chunkwise WY/UT form of Gated DeltaNet (the tensorplay section 6.2 statement
+    that Householder-style products become chunk-parallel accumulations, worked out
+    for the canonical orientation). Per chunk, with G_r the within-chunk log-gate
+    cumsum, a_r = exp(G_r) and Gamma_rs = exp(G_r - G_s):
+      P = strict_lower(diag(beta) (Gamma (.) K K^T)),  T = (I + P)^-1
+      W = T diag(beta a) K,   U~ = T diag(beta) V,   U = U~ - W S_0
+      O = diag(a) Q S_0 + (Gamma (.) Q K^T (.) M) U
+      S_C = a_C S_0 + (diag(a_C / a) K)^T U
+    With lg == 0 this is DeltaNet; with T = I and U = V it is the decay form."""
+    L, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if s0 is None else s0.copy()
+    o = np.zeros((L, dv))
+    for c0 in range(0, L, C):
+        sl = slice(c0, min(L, c0 + C))
+        Q, K, V, b = q[sl], k[sl], v[sl], beta[sl]
+        n = Q.shape[0]
+        G = np.cumsum(lg[sl])
+        a = np.exp(G)
+        Gam = np.exp(G[:, None] - G[None, :])
+        P = np.tril(b[:, None] * Gam * (K @ K.T), -1)
+        T = np.linalg.inv(np.eye(n) + P)
+        W = T @ ((b * a)[:, None] * K)
+        U = T @ (b[:, None] * V) - W @ S
+        o[sl] = a[:, None] * (Q @ S) + (np.tril(Gam * (Q @ K.T))) @ U
+        S = a[-1] * S + ((a[-1] / a)[:, None] * K).T @ U
+    return o, S
+
+
+def pin_gdn_chunkwise_wy(lib):
+    """The chunk algebra the GPU path uses equals the recurrence for C in
+    {1, 4, 16, L} (tensorplay section 3.3: C = 1 is the recurrent form, C = L the
+    parallel one)."""
+    r = _rng(15)
+    L, dk, dv = 48, 8, 6
+    q, k = _unit(r.standard_normal((L, dk))), _unit(r.standard_normal((L, dk)))
+    v = r.standard_normal((L, dv))
+    lg = np.log(1.0 / (1.0 + np.exp(-r.normal(3.0, 1.0, L))))
+    beta = 1.0 / (1.0 + np.exp(-r.normal(0.0, 1.0, L)))
+    s0 = r.standard_normal((dk, dv)) * 0.3
+    o, s, _ = oracle.forward("gated_delta", q[None], k[None], v[None], log_gate=lg[None],
+                             beta=beta[None], state_in=s0[None], lib=lib)
+    for C in (1, 4, 16, L):
+        oc, sc = gdn_chunkwise_wy(q, k, v, lg, beta, C, s0)
+        assert _rel(o[0], oc) <= 1e-10, (C, _rel(o[0], oc))
+        assert _rel(s[0], sc) <= 1e-10, C
+
+
+# ---------------------------------------------------------------------------
+# DECODE and state carry
+# ---------------------------------------------------------------------------
+def pin_decode_one_decay_step(lib):
+    """Decode step = S' = gamma S + k v^T, o = S'^T q, written out in numpy
+    (wln20 data-dependent decay; tensorplay section 2.1 output read-out)."""
+    r = _rng(16)
+    NH, dk, dv = 6, 5, 4
+    q, k = r.standard_normal((NH, dk)), r.standard_normal((NH, dk))
+    v = r.standard_normal((NH, dv))
+    lg = -r.random(NH)
+    S = r.standard_normal((NH, dk, dv))
+    o, S1 = oracle.decode_step("decay", q, k, v, lg, S, lib=lib)
+    S_ref = np.exp(lg)[:, None, None] * S + k[:, :, None] * v[:, None, :]
+    assert _rel(S1, S_ref) <= 1e-14
+    assert _rel(o, np.einsum("nij,ni->nj", S_ref, q)) <= 1e-13
+
+
+def pin_prefill_then_decode(lib):
+    """The state is the whole memory (tensorplay section 2.2): prefill L tokens,
+    then one decode step on token L+1, equals the forward over L+1 tokens."""
+    r = _rng(17)
+    L, dk, dv = 20, 4, 3
+    q, k = r.standard_normal((2, L + 1, dk)), r.standard_normal((2, L + 1, dk))
+    v = r.standard_normal((2, L + 1, dv))
+    lg = -r.random((2, L + 1)) * 0.1
+    o_full, s_full, _ = oracle.forward("decay", q, k, v, log_gate=lg, lib=lib)
+    _, s_pre, _ = oracle.forward("decay", q[:, :L], k[:, :L], v[:, :L], log_gate=lg[:, :L], lib=lib)
+    o_dec, s_dec = oracle.decode_step("decay", q[:, L], k[:, L], v[:, L], lg[:, L], s_pre, lib=lib)
+    assert _rel(o_dec, o_full[:, L]) <= 1e-13 and _rel(s_dec, s_full) <= 1e-13
+
+
+def pin_resume_all_variants(lib):
+    """Splitting a sequence and carrying (S, z) across the split gives the same
+    result as one pass, for every variant."""
+    r = _rng(18)
+    L1, L2, dk, dv = 13, 11, 4, 3
+    L = L1 + L2
+    q = _phi(r.standard_normal((2, L, dk)))
+    k = _unit(_phi(r.standard_normal((2, L, dk))))
+    v = r.standard_normal((2, L, dv))
+    lg = -r.random((2, L)) * 0.2
+    beta = r.random((2, L))
+    for var in ("plain", "normalized", "decay", "gated_delta"):
+        kw = {}
+        if var in ("decay", "gated_delta"):
+            kw["log_gate"] = lg
+        if var == "gated_delta":
+            kw["beta"] = beta
+        o, s, z = oracle.forward(var, q, k, v, lib=lib, **kw)
+        k1 = {n: x[:, :L1] for n, x in kw.items()}
+        k2 = {n: x[:, L1:] for n, x in kw.items()}
+        oa, sa, za = oracle.forward(var, q[:, :L1], k[:, :L1], v[:, :L1], lib=lib, **k1)
+        ob, sb, zb = oracle.forward(var, q[:, L1:], k[:, L1:], v[:, L1:], state_in=sa,
+                                    z_in=za, lib=lib, **k2)
+        assert _rel(np.concatenate([oa, ob], 1), o) <= 1e-12, var
+        assert _rel(sb, s) <= 1e-12, var
+        if var == "normalized":
+            assert _rel(zb, z) <= 1e-13
+
+
+ALL_PINS = [
+    pin_plain_quadratic, pin_plain_fraction_bruteforce, pin_plain_final_state,
+    pin_normalized_quadratic, pin_normalized_constant_v, pin_normalized_hull,
+    pin_decay_quadratic, pin_decay_zero_gate_is_plain, pin_decay_fraction_half,
+    pin_gdn_retrieve_merge_overwrite, pin_gdn_alpha_one_is_deltanet,
+    pin_gdn_beta_zero_pure_decay, pin_gdn_onehot_recall, pin_gdn_unit_key_identity,
+    pin_gdn_fraction_product_expansion, pin_gdn_chunkwise_wy,
+    pin_decode_one_decay_step, pin_prefill_then_decode, pin_resume_all_variants,
+]

@@ -1,0 +1,60 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins catch
+each one: a dropped term, a wrong sign, a wrong index or operand, a misplaced gate.
+The mistakes are planted in the oracle, on the CPU, in a temporary copy; the real
+oracle is untouched."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as obuild
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+MUTANTS = {
+    "decay_dropped": ("S[i * dv + j] = g * S[i * dv + j] + kt[i] * vt[j];",
+                      "S[i * dv + j] = S[i * dv + j] + kt[i] * vt[j];"),
+    "decay_gate_off_by_one": ("double g = exp(lg[t]);",
+                              "double g = exp(lg[t > 0 ? t - 1 : 0]);"),
+    "gdn_sign": ("a * (S[i * dv + j] - b * kt[i] * r[j])", "a * (S[i * dv + j] + b * kt[i] * r[j])"),
+    "gdn_beta_dropped_on_write": ("+ b * kt[i] * vt[j];", "+ kt[i] * vt[j];"),
+    "gdn_alpha_on_write": ("a * (S[i * dv + j] - b * kt[i] * r[j]) + b * kt[i] * vt[j];",
+                           "a * (S[i * dv + j] - b * kt[i] * r[j] + b * kt[i] * vt[j]);"),
+    "gdn_retrieve_with_query": ("for (long i = 0; i < dk; ++i) acc += S[i * dv + j] * kt[i];",
+                                "for (long i = 0; i < dk; ++i) acc += S[i * dv + j] * qt[i];"),
+    "normalizer_wrong_operand": ("for (long i = 0; i < dk; ++i) z[i] += kt[i];",
+                                 "for (long i = 0; i < dk; ++i) z[i] += qt[i];"),
+    "normalizer_dropped": ("for (long j = 0; j < dv; ++j) ot[j] /= den;", "(void)den;"),
+    "state_in_ignored": ("S[i] = s_in ? s_in[i] : 0.0;", "S[i] = 0.0;"),
+    "plain_transposed_write": ("S[i * dv + j] += kt[i] * vt[j];", "S[i * dv + j] += kt[j % dk] * vt[i % dv];"),
+    "readout_uses_key": ("acc += S[i * dv + j] * qt[i];\n            ot[j] = acc;",
+                         "acc += S[i * dv + j] * kt[i];\n            ot[j] = acc;"),
+    "exclusive_mask": ("double *ot = o + t * dv;\n",
+                       "double *ot = o + t * dv;\n        if (t > 0) { for (long j = 0; j < dv; ++j) { double acc = 0.0; for (long i = 0; i < dk; ++i) acc += S[i * dv + j] * qt[i]; ot[j] = acc; } }\n"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {name}"
+    if name == "exclusive_mask":
+        # The output is read before the update (strict mask j < t); the read-out
+        # below the update is disabled.
+        src = src.replace("for (long j = 0; j < dv; ++j) {\n            double acc = 0.0;\n"
+                          "            for (long i = 0; i < dk; ++i) acc += S[i * dv + j] * qt[i];",
+                          "for (long j = 0; j < 0; ++j) {\n            double acc = 0.0;\n"
+                          "            for (long i = 0; i < dk; ++i) acc += S[i * dv + j] * qt[i];")
+    n_before = src.count(old)
+    src = src.replace(old, new)
+    assert n_before == 1 and src.count(new) >= 1
+    msrc = tmp_path / "oracle_mutant.c"
+    msrc.write_text(src)
+    lib = obuild.build(src=str(msrc), out=str(tmp_path / "liboracle_mutant.so"))
+    res = subprocess.run([sys.executable, os.path.join(HERE, "pin_runner.py"), lib],
+                         capture_output=True, text=True, timeout=300)
+    fails = [l for l in res.stdout.splitlines() if l.startswith("FAIL")]
+    crashed = res.returncode != 0
+    assert fails or crashed, f"mutant {name} passed every pin:\n{res.stdout}"
