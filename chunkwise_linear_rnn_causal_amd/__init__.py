@@ -1,0 +1,158 @@
+"""Python binding of liblinattn: causal linear attention on MI355X (gfx950).
+
+Thin ctypes layer over the C ABI declared in include/linattn.h, with the same
+entry-point names. It only marshals arguments: PyTorch provides device memory
+and the current stream; every step of the computation runs in the library's HIP
+kernels. There is no fallback: if the library is not built, or the device is not
+gfx950, calls raise.
+
+    o, state, z = la_chunk_fwd("decay", q, k, v, log_gate=lg, C=64, want_state=True)
+    o = la_decode_step("decay", q, k, v, log_gate, state)   # state updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblinattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "linattn.h")
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
+VARIANTS = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3}
+EXPORTS = ("la_chunk_fwd_workspace_size", "la_chunk_fwd", "la_decode_step",
+           "la_status_str", "la_abi_version")
+
+_lib = None
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {la_status_str(status)} ({status})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblinattn.so (built in-tree by chunkwise_linear_rnn_causal_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m chunkwise_linear_rnn_causal_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.la_abi_version.restype = i
+    lib.la_abi_version.argtypes = []
+    lib.la_status_str.restype = ctypes.c_char_p
+    lib.la_status_str.argtypes = [i]
+    lib.la_chunk_fwd_workspace_size.restype = i
+    lib.la_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.la_chunk_fwd.restype = i
+    lib.la_chunk_fwd.argtypes = [i, i, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp,
+                                 i, i, i, i, i, i, vp, sz, vp]
+    lib.la_decode_step.restype = i
+    lib.la_decode_step.argtypes = [i, i, vp, vp, vp, fp, fp, fp, vp, i, i, i, i, vp]
+    _lib = lib
+    return lib
+
+
+def la_abi_version() -> int:
+    return load_library().la_abi_version()
+
+
+def la_status_str(status: int) -> str:
+    return load_library().la_status_str(int(status)).decode()
+
+
+def _dt(x) -> int:
+    import torch
+    if x.dtype == torch.bfloat16:
+        return 1
+    if x.dtype == torch.float32:
+        return 0
+    raise TypeError(f"unsupported dtype {x.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if not x.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(dev, stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def la_chunk_fwd_workspace_size(variant: str, dtype_code: int, B: int, H: int, L: int,
+                                d_k: int, d_v: int, C: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().la_chunk_fwd_workspace_size(VARIANTS[variant], dtype_code, B, H, L, d_k,
+                                                    d_v, C, ctypes.byref(out))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_chunk_fwd_workspace_size")
+    return out.value
+
+
+def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in=None, *,
+                 C: int = 64, o=None, state_out=None, z_out=None, want_state: bool = False,
+                 want_z: bool = False, workspace=None, stream=None) -> Tuple:
+    """Chunkwise causal linear-attention forward.
+
+    q, k: [B, H, L, d_k]; v: [B, H, L, d_v] (bf16 or fp32, contiguous, on the GPU).
+    log_gate, beta: [B, H, L] fp32; state_in: [B, H, d_k, d_v] fp32;
+    z_in: [B, H, d_k] fp32. Returns (o, state_out or None, z_out or None).
+    Output buffers may be passed in (o, state_out, z_out); state_out may be
+    state_in for an in-place carry.
+    """
+    import torch
+    lib = load_library()
+    B, H, L, d_k = q.shape
+    d_v = v.shape[-1]
+    dt = _dt(q)
+    if o is None:
+        o = torch.empty((B, H, L, d_v), dtype=q.dtype, device=q.device)
+    if want_state and state_out is None:
+        state_out = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=q.device)
+    if want_z and z_out is None:
+        z_out = torch.empty((B, H, d_k), dtype=torch.float32, device=q.device)
+    ws_bytes = 0
+    if workspace is None:
+        ws_bytes = la_chunk_fwd_workspace_size(variant, dt, B, H, L, d_k, d_v, C)
+        if ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.la_chunk_fwd(VARIANTS[variant], dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
+                          _ptr(beta), _ptr(state_in), _ptr(z_in), _ptr(o), _ptr(state_out),
+                          _ptr(z_out), B, H, L, d_k, d_v, C, _ptr(workspace), ws_bytes,
+                          _stream(q.device, stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_chunk_fwd")
+    return o, state_out, z_out
+
+
+def la_decode_step(variant: str, q, k, v, log_gate, state, *, o=None, beta=None, stream=None):
+    """One decode step for [N, H] sequence-heads; ``state`` [N, H, d_k, d_v] fp32 is
+    updated in place. Returns o [N, H, d_v]."""
+    import torch
+    lib = load_library()
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, d_v), dtype=q.dtype, device=q.device)
+    st = lib.la_decode_step(VARIANTS[variant], _dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
+                            _ptr(beta), _ptr(state), _ptr(o), N, H, d_k, d_v,
+                            _stream(q.device, stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_decode_step")
+    return o
+
+
+__all__ = ["la_chunk_fwd", "la_chunk_fwd_workspace_size", "la_decode_step", "la_status_str",
+           "la_abi_version", "LinAttnError", "VARIANTS", "load_library"]

@@ -1,0 +1,281 @@
+// abi.hip -- the C ABI of liblinattn (declared in include/linattn.h).
+//
+// Every entry point validates all arguments on the host before anything is
+// launched, selects the compiled kernel instance for (variant, dtype, d_k, C) and
+// launches it asynchronously on the caller's stream. Nothing is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/linattn.h"
+#include "la_common.hpp"
+#include "la_kernels.hpp"
+
+using namespace la;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    const void *p;
+    size_t bytes;
+};
+
+bool overlap(Span a, Span b) {
+    if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+la_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return LA_ERR_UNSUPPORTED;
+    int st = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LA_ERR_HIP;
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_device_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? LA_OK : LA_ERR_UNSUPPORTED;
+}
+
+la_status from_hip(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
+
+size_t elem_size(la_dtype dt) { return dt == LA_BF16 ? 2 : 4; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Shape checks shared by the workspace query and the forward call.
+la_status check_chunk_shape(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v,
+                            int C) {
+    if (var < LA_PLAIN || var > LA_GATED_DELTA) return LA_ERR_INVALID_ARG;
+    if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || L < 0) return LA_ERR_INVALID_ARG;
+    if (d_k != 32 && d_k != 64 && d_k != 128) return LA_ERR_UNSUPPORTED;
+    if (d_v < 32 || d_v > 128 || d_v % kDVT != 0) return LA_ERR_UNSUPPORTED;
+    if (C != 64 && C != 128) return LA_ERR_UNSUPPORTED;
+    if (var == LA_GATED_DELTA && C != 64) return LA_ERR_UNSUPPORTED;
+    if (dt == LA_F32 && d_k == 128 && C == 128) return LA_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H;
+    if (BH * (d_v / kDVT) > INT32_MAX || BH * ((L + C - 1) / C) > INT32_MAX) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
+size_t gdn_w_bytes(la_dtype dt, int64_t BH, int64_t Lp, int d_k) {
+    return round_up((size_t)BH * Lp * d_k * elem_size(dt), 256);
+}
+
+size_t chunk_workspace(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v, int C) {
+    if (var != LA_GATED_DELTA || L == 0) return 0;
+    const int64_t BH = (int64_t)B * H, Lp = (int64_t)((L + C - 1) / C) * C;
+    return gdn_w_bytes(dt, BH, Lp, d_k) + (size_t)BH * Lp * d_v * elem_size(dt);
+}
+
+template <typename T, int DK, int C>
+hipError_t dispatch_chunk_c(la_variant var, const ChunkArgs &a, hipStream_t st) {
+    switch (var) {
+        case LA_PLAIN: return launch_chunk<V_PLAIN, T, DK, kDVT, C>(a, st);
+        case LA_NORMALIZED: return launch_chunk<V_NORM, T, DK, kDVT, C>(a, st);
+        case LA_DECAY: return launch_chunk<V_DECAY, T, DK, kDVT, C>(a, st);
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T, int DK>
+hipError_t dispatch_chunk(la_variant var, int C, const ChunkArgs &a, hipStream_t st) {
+    if (var == LA_GATED_DELTA) return launch_chunk<V_GDN, T, DK, kDVT, 64>(a, st);
+    if (C == 64) return dispatch_chunk_c<T, DK, 64>(var, a, st);
+    if constexpr (!(sizeof(T) == 4 && DK == 128)) return dispatch_chunk_c<T, DK, 128>(var, a, st);
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t dispatch_chunk_dk(la_variant var, int d_k, int C, const ChunkArgs &a, hipStream_t st) {
+    switch (d_k) {
+        case 32: return dispatch_chunk<T, 32>(var, C, a, st);
+        case 64: return dispatch_chunk<T, 64>(var, C, a, st);
+        case 128: return dispatch_chunk<T, 128>(var, C, a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t dispatch_prep(int d_k, const PrepArgs &a, hipStream_t st) {
+    switch (d_k) {
+        case 32: return launch_gdn_prep<T, 32, 64>(a, st);
+        case 64: return launch_gdn_prep<T, 64, 64>(a, st);
+        case 128: return launch_gdn_prep<T, 128, 64>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int VAR, typename T, int DK>
+hipError_t dispatch_decode_dv(int d_v, const DecodeArgs &a, hipStream_t st) {
+    switch (d_v) {
+        case 32: return launch_decode<VAR, T, DK, 32>(a, st);
+        case 64: return launch_decode<VAR, T, DK, 64>(a, st);
+        case 128: return launch_decode<VAR, T, DK, 128>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int VAR, typename T>
+hipError_t dispatch_decode(int d_k, int d_v, const DecodeArgs &a, hipStream_t st) {
+    switch (d_k) {
+        case 32: return dispatch_decode_dv<VAR, T, 32>(d_v, a, st);
+        case 64: return dispatch_decode_dv<VAR, T, 64>(d_v, a, st);
+        case 128: return dispatch_decode_dv<VAR, T, 128>(d_v, a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_abi_version(void) { return LA_ABI_VERSION; }
+
+const char *la_status_str(la_status s) {
+    switch (s) {
+        case LA_OK: return "LA_OK";
+        case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
+        case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+        case LA_ERR_HIP: return "LA_ERR_HIP";
+    }
+    return "LA_ERR_UNKNOWN";
+}
+
+la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H, int L, int d_k,
+                                      int d_v, int C, size_t *bytes) {
+    if (!bytes) return LA_ERR_INVALID_ARG;
+    const la_status s = check_chunk_shape(var, dt, B, H, L, d_k, d_v, C);
+    if (s != LA_OK) return s;
+    *bytes = chunk_workspace(var, dt, B, H, L, d_k, d_v, C);
+    return LA_OK;
+}
+
+la_status la_chunk_fwd(la_variant var, la_dtype dt, const void *q, const void *k, const void *v,
+                       const float *log_gate, const float *beta, const float *state_in,
+                       const float *z_in, void *o, float *state_out, float *z_out, int B, int H,
+                       int L, int d_k, int d_v, int C, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    la_status s = check_chunk_shape(var, dt, B, H, L, d_k, d_v, C);
+    if (s != LA_OK) return s;
+    const int64_t BH = (int64_t)B * H;
+    const size_t es = elem_size(dt);
+    const bool has_tokens = L > 0;
+    // required / forbidden pointers
+    if (has_tokens && (!q || !k || !o)) return LA_ERR_INVALID_ARG;
+    if (has_tokens && !v) return LA_ERR_INVALID_ARG;
+    if (var == LA_DECAY && has_tokens && !log_gate) return LA_ERR_INVALID_ARG;
+    if ((var == LA_PLAIN || var == LA_NORMALIZED) && log_gate) return LA_ERR_INVALID_ARG;
+    if (var == LA_GATED_DELTA && has_tokens && !beta) return LA_ERR_INVALID_ARG;
+    if (var != LA_GATED_DELTA && beta) return LA_ERR_INVALID_ARG;
+    if (var != LA_NORMALIZED && (z_in || z_out)) return LA_ERR_INVALID_ARG;
+    // alignment
+    const void *ptrs[] = {q, k, v, o, log_gate, beta, state_in, z_in, state_out, z_out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
+    // aliasing: outputs must not overlap inputs (state_out == state_in is allowed)
+    const size_t qk_b = (size_t)BH * L * d_k * es, v_b = (size_t)BH * L * d_v * es;
+    const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4, z_b = (size_t)BH * d_k * 4;
+    const Span o_sp{o, v_b}, so_sp{state_out, s_b}, zo_sp{z_out, z_b};
+    const Span ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {log_gate, g_b}, {beta, g_b}, {z_in, z_b}};
+    for (const Span &in : ins) {
+        if (overlap(o_sp, in) || overlap(so_sp, in) || overlap(zo_sp, in)) return LA_ERR_INVALID_ARG;
+    }
+    if (overlap(o_sp, Span{state_in, s_b}) || overlap(o_sp, so_sp) || overlap(o_sp, zo_sp) ||
+        overlap(so_sp, zo_sp) || overlap(zo_sp, Span{state_in, s_b}))
+        return LA_ERR_INVALID_ARG;
+    if (state_out && state_in && state_out != state_in && overlap(so_sp, Span{state_in, s_b}))
+        return LA_ERR_INVALID_ARG;
+    // workspace
+    const size_t need = chunk_workspace(var, dt, B, H, L, d_k, d_v, C);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return LA_ERR_INVALID_ARG;
+        if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
+        const Span ws{workspace, need};
+        for (const Span &in : ins)
+            if (overlap(ws, in)) return LA_ERR_INVALID_ARG;
+        if (overlap(ws, o_sp) || overlap(ws, so_sp) || overlap(ws, Span{state_in, s_b}))
+            return LA_ERR_INVALID_ARG;
+    }
+
+    s = check_device();
+    if (s != LA_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+    const int nchunks = (L + C - 1) / C;
+    const int Lp = nchunks * C;
+    ChunkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.lg = log_gate;
+    a.s_in = state_in; a.z_in = z_in; a.o = o; a.s_out = state_out; a.z_out = z_out;
+    a.BH = (int)BH; a.L = L; a.Lp = Lp; a.dv = d_v; a.nsplit = d_v / kDVT;
+
+    if (var == LA_GATED_DELTA && has_tokens) {
+        char *ws = static_cast<char *>(workspace);
+        a.w = ws;
+        a.ut = ws + gdn_w_bytes(dt, BH, Lp, d_k);
+        PrepArgs p{};
+        p.k = k; p.v = v; p.lg = log_gate; p.beta = beta;
+        p.w = const_cast<void *>(a.w); p.ut = const_cast<void *>(a.ut);
+        p.BH = (int)BH; p.L = L; p.Lp = Lp; p.dv = d_v; p.nchunks = nchunks;
+        const hipError_t e = (dt == LA_BF16) ? dispatch_prep<bf16>(d_k, p, st)
+                                             : dispatch_prep<float>(d_k, p, st);
+        if (e != hipSuccess) return LA_ERR_HIP;
+    }
+    const hipError_t e = (dt == LA_BF16) ? dispatch_chunk_dk<bf16>(var, d_k, C, a, st)
+                                         : dispatch_chunk_dk<float>(var, d_k, C, a, st);
+    return from_hip(e);
+}
+
+la_status la_decode_step(la_variant var, la_dtype dt, const void *q, const void *k, const void *v,
+                         const float *log_gate, const float *beta, float *state, void *o, int N,
+                         int H, int d_k, int d_v, void *stream) {
+    if (var < LA_PLAIN || var > LA_GATED_DELTA) return LA_ERR_INVALID_ARG;
+    if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (var == LA_NORMALIZED || var == LA_GATED_DELTA) return LA_ERR_UNSUPPORTED;
+    if (N < 1 || H < 1) return LA_ERR_INVALID_ARG;
+    if ((int64_t)N * H > INT32_MAX) return LA_ERR_UNSUPPORTED;
+    if ((d_k != 32 && d_k != 64 && d_k != 128) || (d_v != 32 && d_v != 64 && d_v != 128))
+        return LA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !state || !o) return LA_ERR_INVALID_ARG;
+    if (var == LA_DECAY && !log_gate) return LA_ERR_INVALID_ARG;
+    if (var == LA_PLAIN && log_gate) return LA_ERR_INVALID_ARG;
+    if (beta) return LA_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, k, v, o, log_gate, state};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
+    const int64_t NH = (int64_t)N * H;
+    const size_t es = elem_size(dt);
+    const Span o_sp{o, (size_t)NH * d_v * es}, s_sp{state, (size_t)NH * d_k * d_v * 4};
+    const Span ins[] = {{q, (size_t)NH * d_k * es}, {k, (size_t)NH * d_k * es},
+                        {v, (size_t)NH * d_v * es}, {log_gate, (size_t)NH * 4}};
+    for (const Span &in : ins)
+        if (overlap(o_sp, in) || overlap(s_sp, in)) return LA_ERR_INVALID_ARG;
+    if (overlap(o_sp, s_sp)) return LA_ERR_INVALID_ARG;
+
+    const la_status s = check_device();
+    if (s != LA_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    DecodeArgs a{q, k, v, log_gate, state, o, (int)NH};
+    hipError_t e;
+    if (var == LA_DECAY)
+        e = (dt == LA_BF16) ? dispatch_decode<V_DECAY, bf16>(d_k, d_v, a, st)
+                            : dispatch_decode<V_DECAY, float>(d_k, d_v, a, st);
+    else
+        e = (dt == LA_BF16) ? dispatch_decode<V_PLAIN, bf16>(d_k, d_v, a, st)
+                            : dispatch_decode<V_PLAIN, float>(d_k, d_v, a, st);
+    return from_hip(e);
+}
+
+}  // extern "C"

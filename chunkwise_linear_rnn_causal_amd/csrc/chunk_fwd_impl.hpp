@@ -1,0 +1,425 @@
+// chunk_fwd_impl.hpp -- fused chunkwise causal linear-attention forward (gfx950).
+//
+// Method (tensorplay "Talk Linear Attention", section 3.2, chunkwise parallel
+// form; section 5.2 for the decayed variant): for chunk c of C tokens with
+// chunk-local cumulative log-gate G_r and a_r = exp(G_r),
+//   O_c    = diag(a) Q_c S_prev  +  (Gamma (.) Q_c K_c^T (.) M) V_c
+//   S_next = a_C S_prev + (diag(a_C / a) K_c)^T V_c,   Gamma_rs = exp(G_r - G_s)
+// with M the inclusive causal mask. Without gates a = 1. The normalized variant
+// divides each output row by rowsum(Q_c K_c^T (.) M) + q_r . z_prev and carries
+// z_next = z_prev + sum_s k_s (proig-chaa notes, sections 13-14). The gated delta
+// rule replaces V_c by U_c = U~_c - W_c S_prev, with W and U~ prepared per chunk
+// by gdn_prep (see gdn_prep_impl.hpp for the derivation).
+//
+// Mapping. One workgroup (4 waves) owns one (batch*head, 32-column value slice)
+// and walks the chunks in order, keeping its d_k x 32 slice of S in fp32 MFMA
+// accumulators for the whole sequence (nothing but Q, K, V, gates and O crosses
+// HBM). Value slices of one head are placed on one XCD so Q and K are shared
+// through that XCD's L2. Per chunk:
+//   1. K staged to LDS row-major (score operand) and transposed + scaled by
+//      exp(g_C - G_s) (state-update operand); V transposed; S_prev written to LDS
+//      transposed in the operand type.
+//   2. Wave w owns query rows 16w..16w+15 (and the mirrored block for C = 128).
+//      It computes the inter term (S^T Q^T on MFMA), the score tiles
+//      K_sb Q_rb^T for sb <= rb, masks/decays/rounds them in registers and feeds
+//      them straight back as the B operand of the intra term V^T A^T: the D
+//      layout of a score tile is exactly the B-operand layout of the next MFMA
+//      with the key index in the K slots. Output rows are lane-indexed, so the
+//      per-row scales (exp(G_r), 1/den_r) are per-lane scalars and each lane
+//      stores four consecutive output columns.
+//   3. S <- exp(g_C) S + K~^T V on MFMA into the accumulators.
+#pragma once
+
+#include "la_common.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+
+template <typename T> __device__ inline float frag_elem(const typename Mfma<T>::frag &f, int i);
+template <> __device__ inline float frag_elem<bf16>(const bf16x8 &f, int i) { return (float)f[i]; }
+template <> __device__ inline float frag_elem<float>(const float &f, int) { return f; }
+
+template <int VAR, typename T, int DK, int DVT, int C>
+struct ChunkCfg {
+    static constexpr int NW = 4;
+    static constexpr int PAD = 16 / (int)sizeof(T);
+    static constexpr int KP = DK + PAD;  // row pitch of Ks / STs (elements)
+    static constexpr size_t lds_bytes =
+        sizeof(T) * ((size_t)C * KP + (size_t)DK * C + (size_t)DVT * C + (size_t)DVT * KP) +
+        sizeof(float) * (C + (VAR == V_NORM ? 2 * DK : 1));
+};
+
+template <int VAR, typename T, int DK, int DVT, int C>
+__global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
+    using MF = Mfma<T>;
+    using frag = typename MF::frag;
+    using Cfg = ChunkCfg<VAR, T, DK, DVT, C>;
+    constexpr int E = MF::E;
+    constexpr int NW = Cfg::NW;
+    constexpr int NRB = C / 16;          // 16-row blocks per chunk
+    constexpr int RBW = NRB / NW;        // row blocks per wave (1 or 2)
+    constexpr bool DECAYED = (VAR == V_DECAY || VAR == V_GDN);
+    constexpr int KP = Cfg::KP;
+    constexpr int NTI = DK / 16, NTJ = DVT / 16;
+    constexpr int NTS = (NTI * NTJ + NW - 1) / NW;  // state tiles per wave
+    constexpr int NKS = DK / (4 * E);    // k-steps over channels
+    constexpr int NTK = C / (4 * E);     // k-steps over tokens
+    constexpr int PER = C / 64;          // tokens per lane in the gate scan
+    static_assert(NRB % NW == 0 && (RBW == 1 || RBW == 2), "C must be 64 or 128");
+    static_assert(DVT % 16 == 0 && DK % 32 == 0, "tile sizes");
+
+    __shared__ __attribute__((aligned(16))) T Ks[C * KP];
+    __shared__ __attribute__((aligned(16))) T KTs[DK * C];
+    __shared__ __attribute__((aligned(16))) T VTs[DVT * C];
+    __shared__ __attribute__((aligned(16))) T STs[DVT * KP];
+    __shared__ float Gs[C];
+    __shared__ float Zs[VAR == V_NORM ? 2 * DK : 1];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
+    const int vid = xcd_virtual_block();
+    const int bh = vid / a.nsplit, split = vid - bh * a.nsplit;
+    const int j0 = split * DVT;
+    const int L = a.L, dv = a.dv;
+
+    const T *qg = (const T *)a.q + (size_t)bh * L * DK;
+    const T *kg = (const T *)a.k + (size_t)bh * L * DK;
+    const T *vg = (VAR == V_GDN) ? nullptr : (const T *)a.v + (size_t)bh * L * dv + j0;
+    T *og = (T *)a.o + (size_t)bh * L * dv + j0;
+    const float *lgg = (DECAYED && a.lg) ? a.lg + (size_t)bh * L : nullptr;
+    const T *wg = (VAR == V_GDN) ? (const T *)a.w + (size_t)bh * a.Lp * DK : nullptr;
+    const T *utg = (VAR == V_GDN) ? (const T *)a.ut + ((size_t)bh * dv + j0) * a.Lp : nullptr;
+
+    // ---- initial state slice in accumulator layout: lane (g, n) of tile (ti, tj)
+    // holds S[ti*16 + 4g + e][j0 + tj*16 + n].
+    f32x4 Sacc[NTS];
+#pragma unroll
+    for (int m = 0; m < NTS; ++m) {
+        const int tile = wv + NW * m;
+        Sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tile < NTI * NTJ && a.s_in) {
+            const int ti = tile / NTJ, tj = tile % NTJ;
+            const float *sp = a.s_in + (size_t)bh * DK * dv + (size_t)(ti * 16 + 4 * g) * dv + j0 +
+                              tj * 16 + n;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sacc[m][e] = sp[(size_t)e * dv];
+        }
+    }
+    if constexpr (VAR == V_NORM) {
+        for (int i = tid; i < DK; i += 256) Zs[i] = a.z_in ? a.z_in[(size_t)bh * DK + i] : 0.f;
+    }
+
+    const int nchunks = (L + C - 1) / C;
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        __syncthreads();  // previous chunk is done with every LDS tile
+
+        // S_prev, transposed, in the operand type: STs[j][i].
+#pragma unroll
+        for (int m = 0; m < NTS; ++m) {
+            const int tile = wv + NW * m;
+            if (tile < NTI * NTJ) {
+                const int ti = tile / NTJ, tj = tile % NTJ;
+                st4<T>(&STs[(tj * 16 + n) * KP + ti * 16 + 4 * g], Sacc[m]);
+            }
+        }
+
+        // Chunk-local inclusive cumulative log-gate, computed by every wave.
+        float gl[PER];
+        float gC = 0.f;
+        if constexpr (DECAYED) {
+            float run = 0.f;
+#pragma unroll
+            for (int p = 0; p < PER; ++p) {
+                const int t = t0 + lane * PER + p;
+                run += (lgg && t < L) ? lgg[t] : 0.f;
+                gl[p] = run;
+            }
+            float incl = run;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const float y = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += y;
+            }
+            float excl = __shfl_up(incl, 1, 64);
+            if (lane == 0) excl = 0.f;
+#pragma unroll
+            for (int p = 0; p < PER; ++p) gl[p] += excl;
+            gC = __shfl(incl, 63, 64);
+            if (wv == 0) {
+#pragma unroll
+                for (int p = 0; p < PER; ++p) Gs[lane * PER + p] = gl[p];
+            }
+        }
+        auto G_of = [&](int s) -> float {
+            if constexpr (PER == 1) {
+                return __shfl(gl[0], s, 64);
+            } else {
+                const float x0 = __shfl(gl[0], s >> 1, 64);
+                const float x1 = __shfl(gl[1], s >> 1, 64);
+                return (s & 1) ? x1 : x0;
+            }
+        };
+
+        // ---- stage K: units of 4 tokens x 8 channels. In each 16-lane group,
+        // lanes with equal channel block own consecutive token quads, so the
+        // transposed writes of a group cover one 128-byte bank window.
+        {
+            constexpr int CB = DK / 8, CBL = CB < 4 ? CB : 4, TQL = 16 / CBL, NCBG = CB / CBL;
+            constexpr int UNITS = (C / 4) * CB;
+            static_assert(UNITS % 64 == 0, "wave-uniform staging loop");
+            for (int u = tid; u < UNITS; u += 256) {
+                const int gi = u >> 4, l16 = u & 15;
+                const int tq = (gi / NCBG) * TQL + (l16 % TQL);
+                const int cb = (gi % NCBG) * CBL + (l16 / TQL);
+                float x[4][8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = t0 + 4 * tq + r;
+                    if (t < L) {
+                        ld8<T>(kg + (size_t)t * DK + 8 * cb, x[r]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
+                    }
+                    st8<T>(&Ks[(4 * tq + r) * KP + 8 * cb], x[r]);
+                }
+                float wsc[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) wsc[r] = DECAYED ? __expf(gC - G_of(4 * tq + r)) : 1.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    f32x4 col = {x[0][e] * wsc[0], x[1][e] * wsc[1], x[2][e] * wsc[2], x[3][e] * wsc[3]};
+                    st4<T>(&KTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+                }
+            }
+        }
+        // ---- stage V (transposed) for the value slice.
+        if constexpr (VAR != V_GDN) {
+            constexpr int CB = DVT / 8, CBL = CB < 4 ? CB : 4, TQL = 16 / CBL, NCBG = CB / CBL;
+            constexpr int UNITS = (C / 4) * CB;
+            static_assert(UNITS % 64 == 0, "wave-uniform staging loop");
+            for (int u = tid; u < UNITS; u += 256) {
+                const int gi = u >> 4, l16 = u & 15;
+                const int tq = (gi / NCBG) * TQL + (l16 % TQL);
+                const int cb = (gi % NCBG) * CBL + (l16 / TQL);
+                float x[4][8];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = t0 + 4 * tq + r;
+                    if (t < L) {
+                        ld8<T>(vg + (size_t)t * dv + 8 * cb, x[r]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    f32x4 col = {x[0][e], x[1][e], x[2][e], x[3][e]};
+                    st4<T>(&VTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+                }
+            }
+        }
+        __syncthreads();  // staged tiles, STs and Gs visible
+
+        // ---- gated delta rule: U = U~ - W S_prev, written transposed into VTs.
+        if constexpr (VAR == V_GDN) {
+            constexpr int NU = (C / 16) * NTJ;
+            for (int u = wv; u < NU; u += NW) {
+                const int sbk = u / NTJ, tj = u % NTJ;
+                const int jj = tj * 16 + n;
+                // D[s][j] tile: lane (g, n) holds s = sbk*16 + 4g + e, j = jj.
+                f32x4 acc = ld4<T>(utg + (size_t)jj * a.Lp + t0 + sbk * 16 + 4 * g);
+                const T *wrow = wg + (size_t)(t0 + sbk * 16 + n) * DK + g * (DK / 4);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const frag wa = neg_frag<T>(ld_frag<T>(wrow + ks * E));
+                    const frag sb = ld_frag<T>(&STs[jj * KP + g * (DK / 4) + ks * E]);
+                    acc = MF::mma(wa, sb, acc);
+                }
+                st4<T>(&VTs[tidx<C>(jj, sbk * 16 + 4 * g)], acc);
+            }
+            __syncthreads();
+        }
+
+        // ---- normalizer carry: z_next = z_prev + sum_s k_s (fp32).
+        const int zc = (c & 1) * DK, zn = ((c + 1) & 1) * DK;
+        if constexpr (VAR == V_NORM) {
+            for (int i = tid; i < DK; i += 256) {
+                float sacc = 0.f;
+                for (int s = 0; s < C; ++s) sacc += to_f32<T>(Ks[s * KP + i]);
+                Zs[zn + i] = Zs[zc + i] + sacc;
+            }
+        }
+
+        // ---- outputs for the row blocks this wave owns.
+#pragma unroll
+        for (int rr = 0; rr < RBW; ++rr) {
+            const int rb = (rr == 0) ? wv : (NRB - 1 - wv);
+            const int rl = rb * 16 + n;   // chunk-local query row of this lane
+            const int rrow = t0 + rl;
+            frag qf[NKS];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                qf[ks] = (rrow < L) ? ld_frag<T>(qg + (size_t)rrow * DK + g * (DK / 4) + ks * E)
+                                    : zero_frag<T>();
+            const float Gr = DECAYED ? Gs[rl] : 0.f;
+
+            // inter-chunk term: D[j][r] = sum_i S[i][j] q_r[i]
+            f32x4 oacc[NTJ];
+#pragma unroll
+            for (int tj = 0; tj < NTJ; ++tj) {
+                oacc[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    oacc[tj] = MF::mma(ld_frag<T>(&STs[(tj * 16 + n) * KP + g * (DK / 4) + ks * E]),
+                                       qf[ks], oacc[tj]);
+            }
+            if constexpr (DECAYED) {
+                const float er = __expf(Gr);
+#pragma unroll
+                for (int tj = 0; tj < NTJ; ++tj) oacc[tj] *= er;
+            }
+
+            // score tiles D[s][r] = k_s . q_r for key blocks sb <= rb.
+            f32x4 sc[NRB];
+            float rowsum = 0.f;
+#pragma unroll
+            for (int sb = 0; sb < NRB; ++sb) {
+                sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (sb <= rb) {
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        sc[sb] = MF::mma(ld_frag<T>(&Ks[(sb * 16 + n) * KP + g * (DK / 4) + ks * E]),
+                                         qf[ks], sc[sb]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int sl = sb * 16 + 4 * g + e;
+                        float x = sc[sb][e];
+                        if (sl > rl) {
+                            x = 0.f;
+                        } else if constexpr (DECAYED) {
+                            x *= __expf(Gr - Gs[sl]);
+                        }
+                        x = to_f32<T>(from_f32<T>(x));
+                        sc[sb][e] = x;
+                        if constexpr (VAR == V_NORM) rowsum += x;
+                    }
+                }
+            }
+
+            // intra-chunk term: D[j][r] += sum_s V[s][j] A[r][s]
+            if constexpr (E == 8) {
+#pragma unroll
+                for (int p = 0; p < NRB / 2; ++p) {
+                    if (2 * p <= rb) {
+                        bf16x8 bop;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            bop[e] = (bf16)sc[2 * p][e];
+                            bop[4 + e] = (bf16)sc[2 * p + 1][e];
+                        }
+                        const bool hi = (2 * p + 1 <= rb);
+#pragma unroll
+                        for (int tj = 0; tj < NTJ; ++tj) {
+                            const int jj = tj * 16 + n;
+                            const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(&VTs[tidx<C>(jj, 32 * p + 4 * g)]);
+                            bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(&VTs[tidx<C>(jj, 32 * p + 16 + 4 * g)]);
+                            if (!hi) {
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) hi4[e] = (bf16)0.0f;
+                            }
+                            bf16x8 aop;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                aop[e] = lo4[e];
+                                aop[4 + e] = hi4[e];
+                            }
+                            oacc[tj] = MF::mma(aop, bop, oacc[tj]);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int sb = 0; sb < NRB; ++sb) {
+                    if (sb <= rb) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                            for (int tj = 0; tj < NTJ; ++tj)
+                                oacc[tj] = MF::mma(VTs[tidx<C>(tj * 16 + n, sb * 16 + 4 * g + e)],
+                                                   sc[sb][e], oacc[tj]);
+                        }
+                    }
+                }
+            }
+
+            if constexpr (VAR == V_NORM) {
+                float qz = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int el = 0; el < E; ++el)
+                        qz += frag_elem<T>(qf[ks], el) * Zs[zc + g * (DK / 4) + ks * E + el];
+                float den = rowsum + qz;
+                den += __shfl_xor(den, 16, 64);
+                den += __shfl_xor(den, 32, 64);
+                const float inv = 1.0f / den;
+#pragma unroll
+                for (int tj = 0; tj < NTJ; ++tj) oacc[tj] *= inv;
+            }
+
+            if (rrow < L) {
+#pragma unroll
+                for (int tj = 0; tj < NTJ; ++tj) st4<T>(og + (size_t)rrow * dv + tj * 16 + 4 * g, oacc[tj]);
+            }
+        }
+
+        // ---- state update: S <- exp(g_C) S + K~^T V
+        if constexpr (DECAYED) {
+            const float eg = __expf(gC);
+#pragma unroll
+            for (int m = 0; m < NTS; ++m) Sacc[m] *= eg;
+        }
+#pragma unroll
+        for (int m = 0; m < NTS; ++m) {
+            const int tile = wv + NW * m;
+            if (tile < NTI * NTJ) {
+                const int ti = tile / NTJ, tj = tile % NTJ;
+#pragma unroll
+                for (int ks = 0; ks < NTK; ++ks) {
+                    const int s0 = g * (C / 4) + ks * E;
+                    Sacc[m] = MF::mma(ld_frag<T>(&KTs[tidx<C>(ti * 16 + n, s0)]),
+                                      ld_frag<T>(&VTs[tidx<C>(tj * 16 + n, s0)]), Sacc[m]);
+                }
+            }
+        }
+    }
+
+    if (a.s_out) {
+#pragma unroll
+        for (int m = 0; m < NTS; ++m) {
+            const int tile = wv + NW * m;
+            if (tile < NTI * NTJ) {
+                const int ti = tile / NTJ, tj = tile % NTJ;
+                float *sp = a.s_out + (size_t)bh * DK * dv + (size_t)(ti * 16 + 4 * g) * dv + j0 + tj * 16 + n;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sp[(size_t)e * dv] = Sacc[m][e];
+            }
+        }
+    }
+    if constexpr (VAR == V_NORM) {
+        // The threads that wrote the last z update read it back: no barrier needed.
+        if (a.z_out && split == 0)
+            for (int i = tid; i < DK; i += 256) a.z_out[(size_t)bh * DK + i] = Zs[(nchunks & 1) * DK + i];
+    }
+}
+
+template <int VAR, typename T, int DK, int DVT, int C>
+hipError_t launch_chunk(const ChunkArgs &a, hipStream_t st) {
+    const int blocks = a.BH * a.nsplit;
+    hipLaunchKernelGGL((chunk_fwd_kernel<VAR, T, DK, DVT, C>), dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace la

@@ -1,0 +1,78 @@
+// decode_impl.hpp -- one-token recurrent decode step (gfx950), HBM-bound.
+//
+// Per sequence-head: S <- gamma S + k v^T in place, then o = S^T q with the
+// updated state (tensorplay "Talk Linear Attention", sections 2.1-2.2: the
+// constant-size state is all that is carried between tokens; wln20
+// "LLM注意力优化：线性注意力", data-dependent decay). The fp32 state dominates the
+// traffic (2 x d_k x d_v x 4 bytes per head and step), so the kernel is a
+// streaming read-modify-write: one 256-thread workgroup per head, each thread
+// owning d_k / RG consecutive rows of one 16-byte column group, all of its state
+// loads issued before any arithmetic, non-temporal loads and stores for the state
+// (it is touched once per step), and a shuffle + LDS reduction of o over rows.
+#pragma once
+
+#include "la_common.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+
+template <int VAR, typename T, int DK, int DV>
+__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
+    constexpr int CG = DV / 4;        // 16-byte column groups per row
+    constexpr int RG = 256 / CG;      // row groups
+    constexpr int RPT = DK / RG;      // rows per thread
+    static_assert(RPT >= 1 && DK % RG == 0, "shape");
+    constexpr int RGW = 64 / CG;      // row groups inside one wave
+
+    __shared__ f32x4 red[4][CG];
+
+    const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+    const size_t h = blockIdx.x;
+    float *S = a.S + h * DK * DV + (size_t)rg * RPT * DV + 4 * cg;
+
+    f32x4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m)
+        s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)m * DV));
+
+    const T *qp = (const T *)a.q + h * DK + rg * RPT;
+    const T *kp = (const T *)a.k + h * DK + rg * RPT;
+    float qr[RPT], kr[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        qr[m] = to_f32<T>(qp[m]);
+        kr[m] = to_f32<T>(kp[m]);
+    }
+    const f32x4 vv = ld4<T>((const T *)a.v + h * DV + 4 * cg);
+    const float gam = (VAR == V_DECAY) ? __expf(a.lg[h]) : 1.f;
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const f32x4 ns = gam * s[m] + kr[m] * vv;
+        __builtin_nontemporal_store(ns, reinterpret_cast<f32x4 *>(S + (size_t)m * DV));
+        acc += qr[m] * ns;
+    }
+    // reduce over the row groups of this wave, then over the four waves
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+    }
+    const int wv = tid >> 6;
+    if ((tid & 63) < CG) red[wv][cg] = acc;
+    __syncthreads();
+    if (tid < CG) {
+        const f32x4 o = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+        st4<T>((T *)a.o + h * DV + 4 * tid, o);
+    }
+    (void)RGW;
+}
+
+template <int VAR, typename T, int DK, int DV>
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL((decode_kernel<VAR, T, DK, DV>), dim3(a.NH), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace la

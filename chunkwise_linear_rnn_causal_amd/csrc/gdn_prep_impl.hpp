@@ -1,0 +1,222 @@
+// gdn_prep_impl.hpp -- chunk-parallel preparation for the gated delta rule.
+//
+// The delta rule S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T
+// (wln20 "LLM注意力优化：线性注意力", Gated DeltaNet section, written in the d_k x d_v
+// orientation) can be rewritten as S_t = alpha_t S_{t-1} + k_t u_t^T with the
+// pseudo-value u_t = beta_t (v_t - alpha_t S_{t-1}^T k_t). tensorplay "Talk Linear
+// Attention" section 6.2 names the obstacle (u_t depends on S_{t-1}) and the cure
+// (a WY / Householder-product representation that makes it chunk-parallel) without
+// spelling it out; worked out for one chunk with a_r = exp(G_r), G the chunk-local
+// cumulative log-gate:
+//   (I + P) U = diag(beta) V - diag(beta a) K S_0,
+//   P_rs = beta_r exp(G_r - G_s) (k_r . k_s) for s < r, 0 otherwise,
+// so with T = (I + P)^-1:  W = T diag(beta a) K,  U~ = T diag(beta) V,  U = U~ - W S_0.
+// W and U~ do not depend on the state, so this kernel computes them for every
+// chunk in parallel (one workgroup per chunk); the serial chunk pass then only
+// forms U = U~ - W S_prev.
+//
+// Layout of the results: W row-major [BH, Lp, DK]; U~ transposed [BH, dv, Lp]
+// (so the serial pass reads four consecutive tokens per lane). Padded tokens
+// (t >= L) have beta = 0 and k = v = 0, which makes their rows of W and U~ zero.
+#pragma once
+
+#include "la_common.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+
+template <typename T, int DK, int C>
+struct PrepCfg {
+    static constexpr int DVMAX = 128;
+    static constexpr int PAD = 16 / (int)sizeof(T);
+    static constexpr int KP = DK + PAD;
+    static constexpr int TP = C + 1;  // fp32 row pitch of P and T
+    static constexpr size_t lds_bytes =
+        sizeof(T) * ((size_t)C * KP + (size_t)DK * C + (size_t)DVMAX * C) +
+        sizeof(float) * (2 * (size_t)C * TP + 2 * C);
+};
+
+template <typename T, int DK, int C>
+__global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
+    using MF = Mfma<T>;
+    using frag = typename MF::frag;
+    using Cfg = PrepCfg<T, DK, C>;
+    constexpr int E = MF::E;
+    constexpr int NW = 4;
+    constexpr int NRB = C / 16;
+    constexpr int KP = Cfg::KP, TP = Cfg::TP;
+    constexpr int NKS = DK / (4 * E);
+    constexpr int NTK = C / (4 * E);
+    static_assert(C == 64, "the row-by-row inverse assigns one column per lane: C = 64");
+
+    __shared__ __attribute__((aligned(16))) T Ks[C * KP];
+    __shared__ __attribute__((aligned(16))) T KTs[DK * C];
+    __shared__ __attribute__((aligned(16))) T VTs[Cfg::DVMAX * C];
+    __shared__ float Pm[C * TP];
+    __shared__ float Tm[C * TP];
+    __shared__ float Gs[C];
+    __shared__ float Bs[C];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
+    const int bh = blockIdx.x / a.nchunks, c = blockIdx.x - bh * a.nchunks;
+    const int t0 = c * C, L = a.L, dv = a.dv;
+    const T *kg = (const T *)a.k + (size_t)bh * L * DK;
+    const T *vg = (const T *)a.v + (size_t)bh * L * dv;
+    const float *lgg = a.lg ? a.lg + (size_t)bh * L : nullptr;
+    const float *bg = a.beta + (size_t)bh * L;
+
+    // Gates: inclusive scan of the chunk's log-gates (one token per lane).
+    const int tl = t0 + lane;
+    const float lgv = (lgg && tl < L) ? lgg[tl] : 0.f;
+    const float bv = (tl < L) ? bg[tl] : 0.f;
+    float G = lgv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(G, off, 64);
+        if (lane >= off) G += y;
+    }
+    if (wv == 0) {
+        Gs[lane] = G;
+        Bs[lane] = bv;
+    }
+
+    // Stage K row-major, K transposed scaled by beta_s a_s, V transposed scaled by beta_s.
+    {
+        constexpr int CB = DK / 8, CBL = CB < 4 ? CB : 4, TQL = 16 / CBL, NCBG = CB / CBL;
+        constexpr int UNITS = (C / 4) * CB;
+        static_assert(UNITS % 64 == 0, "wave-uniform staging loop");
+        for (int u = tid; u < UNITS; u += 256) {
+            const int gi = u >> 4, l16 = u & 15;
+            const int tq = (gi / NCBG) * TQL + (l16 % TQL);
+            const int cb = (gi % NCBG) * CBL + (l16 / TQL);
+            float x[4][8], sc[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = 4 * tq + r, t = t0 + s;
+                if (t < L) {
+                    ld8<T>(kg + (size_t)t * DK + 8 * cb, x[r]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
+                }
+                st8<T>(&Ks[s * KP + 8 * cb], x[r]);
+                sc[r] = __shfl(bv, s, 64) * __expf(__shfl(G, s, 64));
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                f32x4 col = {x[0][e] * sc[0], x[1][e] * sc[1], x[2][e] * sc[2], x[3][e] * sc[3]};
+                st4<T>(&KTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+            }
+        }
+    }
+    {
+        const int CB = dv / 8;
+        const int CBL = CB < 4 ? CB : 4, TQL = 16 / CBL, NCBG = CB / CBL;
+        const int UNITS = (C / 4) * CB;  // multiple of 64 for dv in {32, 64, 96, 128}
+        for (int u = tid; u < UNITS; u += 256) {
+            const int gi = u >> 4, l16 = u & 15;
+            const int tq = (gi / NCBG) * TQL + (l16 % TQL);
+            const int cb = (gi % NCBG) * CBL + (l16 / TQL);
+            float x[4][8], sc[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = 4 * tq + r, t = t0 + s;
+                if (t < L) {
+                    ld8<T>(vg + (size_t)t * dv + 8 * cb, x[r]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
+                }
+                sc[r] = __shfl(bv, s, 64);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                f32x4 col = {x[0][e] * sc[0], x[1][e] * sc[1], x[2][e] * sc[2], x[3][e] * sc[3]};
+                st4<T>(&VTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+            }
+        }
+    }
+    __syncthreads();
+
+    // P = strict_lower(diag(beta) (Gamma (.) K K^T)) from 16x16 tiles rb >= sb.
+    // D[r][s]: lane (g, n) holds r = rb*16 + 4g + e, s = sb*16 + n.
+    for (int tile = wv; tile < NRB * (NRB + 1) / 2; tile += NW) {
+        int rb = 0, rem = tile;
+        while (rem > rb) { rem -= rb + 1; ++rb; }
+        const int sb = rem;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            d = MF::mma(ld_frag<T>(&Ks[(rb * 16 + n) * KP + g * (DK / 4) + ks * E]),
+                        ld_frag<T>(&Ks[(sb * 16 + n) * KP + g * (DK / 4) + ks * E]), d);
+        const int s = sb * 16 + n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rb * 16 + 4 * g + e;
+            Pm[r * TP + s] = (s < r) ? Bs[r] * __expf(Gs[r] - Gs[s]) * d[e] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // T = (I + P)^-1 by forward substitution, one row per step:
+    // T[r][col] = -sum_{col <= s < r} P[r][s] T[s][col]  (col < r), T[r][r] = 1.
+    // Wave w owns columns 16w..16w+15; the four lane groups split the s range.
+    {
+        const int col = wv * 16 + n;
+        for (int r = 0; r < C; ++r) {
+            float part = 0.f;
+            for (int s = col + g; s < r; s += 4) part += Pm[r * TP + s] * Tm[s * TP + col];
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            if (g == 0) Tm[r * TP + col] = (col < r) ? -part : (col == r ? 1.f : 0.f);
+            __syncthreads();
+        }
+    }
+
+    // T operand fragment: lane (g, n) holds T[r][s0 .. s0+E-1] with r = rb*16 + n.
+    auto t_frag = [&](int r, int s0) -> frag {
+        if constexpr (E == 8) {
+            bf16x8 f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = (bf16)Tm[r * TP + s0 + e];
+            return f;
+        } else {
+            return Tm[r * TP + s0];
+        }
+    };
+
+    // W^T tiles D[ch][r] = sum_s (beta a K)[s][ch] T[r][s]; lane holds ch = cbk*16 + 4g + e.
+    T *wout = (T *)a.w + ((size_t)bh * a.Lp + t0) * DK;
+    for (int tile = wv; tile < (DK / 16) * NRB; tile += NW) {
+        const int cbk = tile / NRB, rb = tile % NRB;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NTK; ++ks) {
+            const int s0 = g * (C / 4) + ks * E;
+            d = MF::mma(ld_frag<T>(&KTs[tidx<C>(cbk * 16 + n, s0)]), t_frag(rb * 16 + n, s0), d);
+        }
+        st4<T>(wout + (size_t)(rb * 16 + n) * DK + cbk * 16 + 4 * g, d);
+    }
+    // U~ tiles D[r][j] = sum_s T[r][s] (beta V)[s][j]; lane holds r = rb*16 + 4g + e.
+    T *uout = (T *)a.ut + (size_t)bh * dv * a.Lp + t0;
+    const int NJB = dv / 16;
+    for (int tile = wv; tile < NRB * NJB; tile += NW) {
+        const int rb = tile / NJB, jb = tile % NJB;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NTK; ++ks) {
+            const int s0 = g * (C / 4) + ks * E;
+            d = MF::mma(t_frag(rb * 16 + n, s0), ld_frag<T>(&VTs[tidx<C>(jb * 16 + n, s0)]), d);
+        }
+        st4<T>(uout + (size_t)(jb * 16 + n) * a.Lp + rb * 16 + 4 * g, d);
+    }
+}
+
+template <typename T, int DK, int C>
+hipError_t launch_gdn_prep(const PrepArgs &a, hipStream_t st) {
+    const int blocks = a.BH * a.nchunks;
+    hipLaunchKernelGGL((gdn_prep_kernel<T, DK, C>), dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace la

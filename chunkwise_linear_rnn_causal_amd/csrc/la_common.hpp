@@ -1,0 +1,126 @@
+// la_common.hpp -- device helpers shared by the gfx950 kernels of liblinattn.
+//
+// MFMA operand layout used throughout (16x16 output tiles, 64-lane wavefront):
+// lane l belongs to lane group g = l / 16 and column n = l % 16.
+//   A operand (M x K): lane (g, n) supplies row m = n, E consecutive K-slots.
+//   B operand (K x N): lane (g, n) supplies column n, the same E K-slots.
+//   D (M x N, fp32):   lane (g, n) holds rows m = 4g + e (e = 0..3), column n.
+// Which real contraction index sits in which K-slot is free as long as A and B
+// agree; the kernels use that freedom to feed D tiles back as operands.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum Variant { V_PLAIN = 0, V_NORM = 1, V_DECAY = 2, V_GDN = 3 };
+
+// MFMA traits per storage/operand type.
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+    static constexpr int E = 8;  // operand elements per lane (K = 32)
+    using frag = bf16x8;
+    __device__ static inline f32x4 mma(const frag &a, const frag &b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mfma<float> {
+    static constexpr int E = 1;  // K = 4
+    using frag = float;
+    __device__ static inline f32x4 mma(float a, float b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+template <typename T> __device__ inline T from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+template <typename T> __device__ inline float to_f32(T x);
+template <> __device__ inline float to_f32<float>(float x) { return x; }
+template <> __device__ inline float to_f32<bf16>(bf16 x) { return (float)x; }
+
+// E contiguous elements -> operand fragment (p must be E*sizeof(T) aligned).
+template <typename T> __device__ inline typename Mfma<T>::frag ld_frag(const T *p);
+template <> __device__ inline bf16x8 ld_frag<bf16>(const bf16 *p) {
+    return *reinterpret_cast<const bf16x8 *>(p);
+}
+template <> __device__ inline float ld_frag<float>(const float *p) { return *p; }
+
+template <typename T> __device__ inline typename Mfma<T>::frag zero_frag();
+template <> __device__ inline bf16x8 zero_frag<bf16>() {
+    bf16x8 z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+    return z;
+}
+template <> __device__ inline float zero_frag<float>() { return 0.0f; }
+
+// Negated fragment (exact: flips the sign bit).
+template <typename T> __device__ inline typename Mfma<T>::frag neg_frag(typename Mfma<T>::frag f);
+template <> __device__ inline bf16x8 neg_frag<bf16>(bf16x8 f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = -f[i];
+    return f;
+}
+template <> __device__ inline float neg_frag<float>(float f) { return -f; }
+
+// Four consecutive elements to / from memory (vectorised for both types).
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<float> { typedef f32x4 type; };
+
+template <typename T> __device__ inline void st4(T *p, f32x4 x) {
+    typename Vec4<T>::type v;
+    v[0] = from_f32<T>(x[0]); v[1] = from_f32<T>(x[1]);
+    v[2] = from_f32<T>(x[2]); v[3] = from_f32<T>(x[3]);
+    *reinterpret_cast<typename Vec4<T>::type *>(p) = v;
+}
+template <typename T> __device__ inline f32x4 ld4(const T *p) {
+    typename Vec4<T>::type v = *reinterpret_cast<const typename Vec4<T>::type *>(p);
+    f32x4 r;
+    r[0] = to_f32<T>(v[0]); r[1] = to_f32<T>(v[1]);
+    r[2] = to_f32<T>(v[2]); r[3] = to_f32<T>(v[3]);
+    return r;
+}
+
+// Eight consecutive elements held as fp32 (global or LDS).
+template <typename T> struct Row8 { float x[8]; };
+
+template <typename T> __device__ inline void ld8(const T *p, float (&x)[8]) {
+    f32x4 a = ld4<T>(p), b = ld4<T>(p + 4);
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+    x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+template <typename T> __device__ inline void st8(T *p, const float (&x)[8]) {
+    f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
+    st4<T>(p, a);
+    st4<T>(p + 4, b);
+}
+
+// Transposed, swizzled [rows][C] tile (token index innermost). Tokens are
+// grouped in 4-element chunks; the chunk index is XORed with a per-row even
+// offset so that transposed 4-token writes from lanes that own rows 8 apart
+// land in different banks, while 8-token aligned reads stay contiguous.
+template <int C> __device__ inline int tidx(int row, int s) {
+    const int swz = (4 * (row >> 3)) & (C / 4 - 1);
+    return row * C + ((((s >> 2) ^ swz)) << 2) + (s & 3);
+}
+
+// XCD-aware block order: consecutive virtual ids go to the same XCD (blocks are
+// handed to the 8 XCDs round-robin), so the d_v slices of one head share L2.
+__device__ inline int xcd_virtual_block() {
+    const int total = gridDim.x, bid = blockIdx.x;
+    const int xcd = bid & 7, slot = bid >> 3;
+    return xcd * (total >> 3) + min(xcd, total & 7) + slot;
+}
+
+}  // namespace la

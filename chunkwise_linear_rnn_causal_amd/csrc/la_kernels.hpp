@@ -1,0 +1,53 @@
+// la_kernels.hpp -- argument blocks and launcher templates of the gfx950 kernels.
+// Launchers are explicitly instantiated in the per-dtype translation units and
+// called by the C ABI layer (abi.hip) after it has validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace la {
+
+// One chunkwise forward pass. Pointers are device pointers; sizes are validated.
+struct ChunkArgs {
+    const void *q, *k, *v;      // [BH, L, DK], [BH, L, DK], [BH, L, dv]
+    const float *lg;            // [BH, L] log-gates or nullptr
+    const float *s_in;          // [BH, DK, dv] or nullptr
+    const float *z_in;          // [BH, DK] or nullptr (normalized only)
+    void *o;                    // [BH, L, dv]
+    float *s_out;               // [BH, DK, dv] or nullptr
+    float *z_out;               // [BH, DK] or nullptr (normalized only)
+    const void *w;              // gated delta: W  [BH, Lp, DK]
+    const void *ut;             // gated delta: U~ transposed [BH, dv, Lp]
+    int BH, L, Lp, dv, nsplit;  // Lp = ceil(L / C) * C; nsplit = dv / DVT
+};
+
+// Chunk-parallel preparation of the gated delta rule (one block per chunk).
+struct PrepArgs {
+    const void *k, *v;          // [BH, L, DK], [BH, L, dv]
+    const float *lg, *beta;     // [BH, L] (lg may be nullptr)
+    void *w, *ut;               // outputs, layouts as in ChunkArgs
+    int BH, L, Lp, dv, nchunks;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;      // [NH, DK], [NH, DK], [NH, DV]
+    const float *lg;            // [NH] or nullptr
+    float *S;                   // [NH, DK, DV], updated in place
+    void *o;                    // [NH, DV]
+    int NH;
+};
+
+// Value-column slice width handled by one workgroup of the chunk kernel.
+constexpr int kDVT = 32;
+
+template <int VAR, typename T, int DK, int DVT, int C>
+hipError_t launch_chunk(const ChunkArgs &a, hipStream_t st);
+
+template <typename T, int DK, int C>
+hipError_t launch_gdn_prep(const PrepArgs &a, hipStream_t st);
+
+template <int VAR, typename T, int DK, int DV>
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+
+}  // namespace la

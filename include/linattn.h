@@ -1,0 +1,149 @@
+/*
+ * linattn.h -- C ABI of the MI355X (gfx950) causal linear-attention library
+ * (liblinattn.so). Plain C: pointers, sizes and enums; no C++ or framework types.
+ *
+ * What is computed. Per batch b and head h, for tokens t = 1..L, with a matrix
+ * state S of shape d_k x d_v (row index = key channel):
+ *
+ *   LA_PLAIN        S_t = S_{t-1} + k_t v_t^T,            o_t = S_t^T q_t
+ *                   i.e. O = (Q K^T (.) M) V with M the causal mask including
+ *                   the diagonal (tensorplay "Talk Linear Attention", section 2.1,
+ *                   parallel form, per-token sum and recurrence).
+ *   LA_NORMALIZED   as PLAIN, plus z_t = z_{t-1} + k_t and
+ *                   o_t = (S_t^T q_t) / (q_t . z_t). q and k are passed already
+ *                   feature-mapped; the library applies no feature map
+ *                   (proig-chaa notes "线性注意力", sections 13-14).
+ *   LA_DECAY        S_t = gamma_t S_{t-1} + k_t v_t^T with gamma_t = exp(l_t)
+ *                   (wln20 "LLM注意力优化：线性注意力", data-dependent decay
+ *                   equation; a constant l gives the data-independent decay).
+ *   LA_GATED_DELTA  S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *                   alpha_t = exp(l_t) (alpha = 1 when log_gate is NULL, i.e. the
+ *                   DeltaNet rule), o_t = S_t^T q_t. This is the transpose of the
+ *                   pages' S'_t = S'_{t-1} alpha_t (I - beta_t k_t k_t^T) +
+ *                   beta_t v_t k_t^T (wln20, Gated DeltaNet section; tensorplay
+ *                   section 6.2); outputs are identical.
+ *
+ * la_chunk_fwd evaluates these in the chunkwise-parallel form (tensorplay
+ * section 3.2): per chunk of C tokens an intra-chunk masked product, an
+ * inter-chunk term Q S_prev, and a serial state pass from chunk to chunk.
+ * la_decode_step applies one token of the recurrence to a stored state
+ * (tensorplay section 2.2: constant-size state at inference).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    allocates and frees nothing and keeps no state between calls except the
+ *    loaded code objects and a per-process record of the device check.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never synchronise the host.
+ *  - Arguments are validated before anything is launched; on any error nothing
+ *    is launched and no output is touched.
+ *  - Layouts are row-major and contiguous:
+ *      q, k [B, H, L, d_k];  v, o [B, H, L, d_v];  log_gate, beta [B, H, L];
+ *      state [B, H, d_k, d_v];  z [B, H, d_k].
+ *    Tensor pointers must be 16-byte aligned.
+ *  - dtype: LA_BF16 means q, k, v, o are bfloat16 (o rounded to nearest even
+ *    from the fp32 accumulators); LA_F32 means they are float32. Gates, beta,
+ *    states and normalizers are always float32.
+ *  - No C++ exception crosses this boundary. Thread-safe for distinct streams.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+
+typedef enum la_status {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARG = 1, /* null required pointer, bad size, misalignment,
+                               workspace missing or too small, aliasing */
+    LA_ERR_UNSUPPORTED = 2, /* size/variant/dtype combination not built, or the
+                               current device is not gfx950 */
+    LA_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} la_status;
+
+typedef enum la_variant {
+    LA_PLAIN = 0,
+    LA_NORMALIZED = 1,
+    LA_DECAY = 2,
+    LA_GATED_DELTA = 3
+} la_variant;
+
+typedef enum la_dtype {
+    LA_F32 = 0,
+    LA_BF16 = 1
+} la_dtype;
+
+/*
+ * Workspace bytes la_chunk_fwd needs for this problem (written to *bytes).
+ * Zero for LA_PLAIN, LA_NORMALIZED and LA_DECAY, which run in one fused pass.
+ * LA_GATED_DELTA runs a chunk-parallel preparation pass first and stores its
+ * per-chunk products (W and U~ of the chunkwise delta-rule form) there:
+ * B*H*ceil(L/C)*C*(d_k + d_v) elements of the input dtype.
+ * Returns LA_ERR_INVALID_ARG / LA_ERR_UNSUPPORTED like la_chunk_fwd.
+ */
+la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H, int L,
+                                      int d_k, int d_v, int C, size_t *bytes);
+
+/*
+ * Chunkwise forward over a whole sequence.
+ *   q, k, v     inputs (dtype dt), required.
+ *   log_gate    [B,H,L] float32 log-gates l_t <= 0 (finite): required for
+ *               LA_DECAY; optional for LA_GATED_DELTA (NULL = alpha 1); must be
+ *               NULL for LA_PLAIN and LA_NORMALIZED.
+ *   beta        [B,H,L] float32 in [0,1]: required for LA_GATED_DELTA, NULL
+ *               otherwise.
+ *   state_in    [B,H,d_k,d_v] float32 initial state, NULL = zero.
+ *   z_in        [B,H,d_k] float32 initial normalizer (LA_NORMALIZED only),
+ *               NULL = zero. Must be NULL for the other variants.
+ *   o           [B,H,L,d_v] output (dtype dt), required; must not overlap any
+ *               input.
+ *   state_out   [B,H,d_k,d_v] float32 final state, NULL = not written. May be
+ *               equal to state_in (in-place carry); must not partially overlap it.
+ *   z_out       [B,H,d_k] float32 final normalizer (LA_NORMALIZED only), NULL =
+ *               not written.
+ *   B, H, L     batch, heads, tokens: B, H >= 1; L >= 0 (L = 0 only copies
+ *               state_in/z_in, or zeros, to state_out/z_out).
+ *   d_k         32, 64 or 128.   d_v  32, 64, 96 or 128 (a multiple of 32).
+ *   C           chunk length: 64 or 128 (LA_GATED_DELTA: 64). L need not be a
+ *               multiple of C; a ragged last chunk is handled.
+ *   workspace   device buffer of at least la_chunk_fwd_workspace_size() bytes
+ *               (may be NULL when that size is 0), 256-byte aligned.
+ */
+la_status la_chunk_fwd(la_variant var, la_dtype dt, const void *q, const void *k,
+                       const void *v, const float *log_gate, const float *beta,
+                       const float *state_in, const float *z_in, void *o,
+                       float *state_out, float *z_out, int B, int H, int L, int d_k,
+                       int d_v, int C, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * One recurrent decode step for N sequences x H heads, updating the state in
+ * place: S <- exp(l) S + k v^T (LA_DECAY) or S <- S + k v^T (LA_PLAIN, log_gate
+ * NULL), then o = S^T q with the updated S (tensorplay section 2.1-2.2; wln20
+ * decay equation).
+ *   q, k [N,H,d_k], v [N,H,d_v], o [N,H,d_v] in dtype dt; log_gate [N,H] float32;
+ *   beta must be NULL (reserved for the delta-rule step); state [N,H,d_k,d_v]
+ *   float32, read and written in place. o must not overlap the state or inputs.
+ *   N, H >= 1; d_k, d_v in {32, 64, 128}.
+ */
+la_status la_decode_step(la_variant var, la_dtype dt, const void *q, const void *k,
+                         const void *v, const float *log_gate, const float *beta,
+                         float *state, void *o, int N, int H, int d_k, int d_v,
+                         void *stream);
+
+/* Static string naming a status code. */
+const char *la_status_str(la_status s);
+
+/* LA_ABI_VERSION of the built library. */
+int la_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before touching the HIP runtime."""
+import ctypes
+import re
+
+import pytest
+
+import chunkwise_linear_rnn_causal_amd as la
+
+PLAIN, NORM, DECAY, GDN = 0, 1, 2, 3
+F32, BF16 = 0, 1
+INVALID, UNSUPPORTED = la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def header_functions():
+    src = open(la.HEADER_PATH).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_names():
+    assert header_functions() == sorted(la.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = la.load_library()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert la.la_abi_version() == 1
+    assert la.la_status_str(0) == "LA_OK"
+    assert la.la_status_str(1) == "LA_ERR_INVALID_ARG"
+    assert la.la_status_str(2) == "LA_ERR_UNSUPPORTED"
+    assert la.la_status_str(3) == "LA_ERR_HIP"
+
+
+def chunk(var=PLAIN, dt=BF16, q=FAKE, k=FAKE, v=FAKE, lg=None, beta=None, s_in=None, z_in=None,
+          o=0x800000000, s_out=None, z_out=None, B=1, H=1, L=128, dk=64, dv=64, C=64, ws=None,
+          ws_bytes=0):
+    return la.load_library().la_chunk_fwd(var, dt, q, k, v, lg, beta, s_in, z_in, o, s_out, z_out,
+                                          B, H, L, dk, dv, C, ws, ws_bytes, None)
+
+
+def wsize(var=GDN, dt=BF16, B=2, H=3, L=100, dk=64, dv=32, C=64):
+    out = ctypes.c_size_t(123)
+    st = la.load_library().la_chunk_fwd_workspace_size(var, dt, B, H, L, dk, dv, C, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_sizes():
+    # one fused pass for the variants without the delta rule
+    for var in (PLAIN, NORM, DECAY):
+        assert wsize(var=var) == (0, 0)
+    # delta rule: W [BH, Lp, dk] (rounded to 256 B) + U~ [BH, dv, Lp], Lp = 128
+    st, n = wsize()
+    w = -(-2 * 3 * 128 * 64 * 2 // 256) * 256
+    assert st == 0 and n == w + 2 * 3 * 128 * 32 * 2
+    assert wsize(L=0) == (0, 0)
+    assert wsize(C=128)[0] == UNSUPPORTED      # delta rule is built for C = 64
+    assert la.load_library().la_chunk_fwd_workspace_size(GDN, BF16, 1, 1, 8, 64, 64, 64, None) == INVALID
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(var=7), INVALID), (dict(dt=5), INVALID),
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(L=-3), INVALID),
+    (dict(dk=48), UNSUPPORTED), (dict(dk=256), UNSUPPORTED),
+    (dict(dv=48), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
+    (dict(C=32), UNSUPPORTED), (dict(C=256), UNSUPPORTED),
+    (dict(dt=F32, dk=128, C=128), UNSUPPORTED),
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
+    (dict(var=DECAY), INVALID),                       # decay needs a log-gate
+    (dict(var=PLAIN, lg=FAKE + 0x100000), INVALID),   # gate given to an ungated variant
+    (dict(var=GDN, lg=FAKE + 0x100000), INVALID),     # delta rule needs beta
+    (dict(var=DECAY, lg=FAKE + 0x100000, beta=FAKE + 0x200000), INVALID),
+    (dict(var=PLAIN, z_in=FAKE + 0x100000), INVALID), # normalizer given to another variant
+    (dict(q=FAKE + 2), INVALID),                      # misaligned
+    (dict(o=FAKE), INVALID),                          # output aliases an input
+    (dict(s_in=0x900000000, s_out=0x900000010), INVALID),  # partial state overlap
+    (dict(var=GDN, beta=FAKE + 0x100000), INVALID),   # workspace missing
+    (dict(var=GDN, beta=FAKE + 0x100000, ws=0x700000000, ws_bytes=16), INVALID),  # too small
+])
+def test_chunk_fwd_rejects(kw, expect):
+    assert chunk(**kw) == expect
+
+
+def dec(var=DECAY, dt=BF16, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, lg=FAKE + 0x3000, beta=None,
+        S=0x900000000, o=0x800000000, N=4, H=2, dk=128, dv=128):
+    return la.load_library().la_decode_step(var, dt, q, k, v, lg, beta, S, o, N, H, dk, dv, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(var=9), INVALID), (dict(var=NORM), UNSUPPORTED), (dict(var=GDN), UNSUPPORTED),
+    (dict(N=0), INVALID), (dict(dk=96), UNSUPPORTED), (dict(dv=16), UNSUPPORTED),
+    (dict(q=None), INVALID), (dict(S=None), INVALID), (dict(lg=None), INVALID),
+    (dict(var=PLAIN), INVALID),                       # plain step takes no gate
+    (dict(beta=FAKE + 0x4000), INVALID),
+    (dict(o=FAKE), INVALID),                          # o overlaps q
+    (dict(o=0x900000000 + 64), INVALID),              # o inside the state
+    (dict(S=0x900000008), INVALID),                   # misaligned state
+])
+def test_decode_step_rejects(kw, expect):
+    assert dec(**kw) == expect

@@ -1,0 +1,196 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, element by
+element on the same seeded inputs. Sizes span several chunks and a ragged tail;
+edge cases cover empty and tiny sequences, state carry, determinism and head
+isolation. The full-size workloads are in test_gpu_configs.py."""
+import numpy as np
+import pytest
+import torch
+
+import chunkwise_linear_rnn_causal_amd as la
+import oracle
+import workloads as W
+from gpu_util import TOL, assert_close, dev, gpu_chunk, host64, oracle_chunk
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(32, 32), (64, 64), (128, 128), (64, 128), (128, 96)]
+
+
+def _cases():
+    out = []
+    for var in ("plain", "normalized", "decay", "gated_delta"):
+        for dt in ("bf16", "f32"):
+            for C in (64, 128):
+                if var == "gated_delta" and C != 64:
+                    continue
+                for dk, dv in SHAPES:
+                    if dt == "f32" and dk == 128 and C == 128:
+                        continue
+                    out.append((var, dt, C, dk, dv))
+    return out
+
+
+@pytest.mark.parametrize("var,dt,C,dk,dv", _cases(), ids=lambda x: str(x))
+def test_chunk_matches_oracle(var, dt, C, dk, dv):
+    """B=2, H=3, L = 3C + 17 (three full chunks and a ragged one), with a random
+    initial state (and normalizer), against the oracle."""
+    L = 3 * C + 17
+    inp = W.make_chunk_inputs(var, dt, 2, 3, L, dk, dv, seed=11, with_state=True,
+                              with_z=(var == "normalized"))
+    o, s, z = gpu_chunk(inp, C)
+    ro, rs, rz = oracle_chunk(inp)
+    assert_close(o, ro, TOL[dt], "o")
+    assert_close(s, rs, TOL[dt], "state")
+    if var == "normalized":
+        assert_close(z, rz, 1e-5, "z")
+
+
+@pytest.mark.parametrize("var", ["plain", "normalized", "decay", "gated_delta"])
+@pytest.mark.parametrize("L", [0, 1, 5, 63, 64, 65])
+def test_edge_lengths(var, L):
+    """Empty, single-token, shorter-than-a-chunk and chunk-boundary sequences."""
+    inp = W.make_chunk_inputs(var, "bf16", 1, 2, L, 64, 64, seed=3, with_state=True,
+                              with_z=(var == "normalized"))
+    o, s, z = gpu_chunk(inp, 64)
+    ro, rs, rz = oracle_chunk(inp)
+    if L > 0:
+        assert_close(o, ro, TOL["bf16"], "o")
+    assert_close(s, rs, TOL["bf16"] if L else 1e-7, "state")
+    if var == "normalized":
+        assert_close(z, rz, 1e-5, "z")
+
+
+@pytest.mark.parametrize("var", ["plain", "decay", "gated_delta"])
+def test_no_initial_state(var):
+    inp = W.make_chunk_inputs(var, "bf16", 1, 2, 200, 128, 128, seed=4)
+    o, s, _ = gpu_chunk(inp, 64, state_in=False)
+    ro, rs, _ = oracle_chunk(inp, state_in=False)
+    assert_close(o, ro, TOL["bf16"], "o")
+    assert_close(s, rs, TOL["bf16"], "state")
+
+
+@pytest.mark.parametrize("var", ["plain", "normalized", "decay", "gated_delta"])
+def test_resume_in_place_equals_one_pass(var):
+    """Carry (S, z) across a split with state_out == state_in (in-place), and
+    compare with a single pass and with the oracle."""
+    L1, L2 = 130, 77
+    inp = W.make_chunk_inputs(var, "f32", 1, 2, L1 + L2, 64, 64, seed=5)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    lg, be = dev(inp.log_gate), dev(inp.beta)
+    norm = var == "normalized"
+    o_full, s_full, z_full = la.la_chunk_fwd(var, q, k, v, lg, be, want_state=True, want_z=norm)
+    sl = lambda x, a, b: None if x is None else x[:, :, a:b].contiguous()
+    S = torch.zeros((1, 2, 64, 64), dtype=torch.float32, device="cuda")
+    Z = torch.zeros((1, 2, 64), dtype=torch.float32, device="cuda") if norm else None
+    Z2 = torch.zeros_like(Z) if norm else None
+    o1, _, _ = la.la_chunk_fwd(var, sl(q, 0, L1), sl(k, 0, L1), sl(v, 0, L1), sl(lg, 0, L1),
+                               sl(be, 0, L1), S, Z, state_out=S, z_out=Z2)
+    o2, _, _ = la.la_chunk_fwd(var, sl(q, L1, None), sl(k, L1, None), sl(v, L1, None),
+                               sl(lg, L1, None), sl(be, L1, None), S, Z2, state_out=S, z_out=Z)
+    torch.cuda.synchronize()
+    o_split = np.concatenate([host64(o1), host64(o2)], axis=2)
+    assert_close(o_split, host64(o_full), 1e-5, "split vs one pass")
+    assert_close(host64(S), host64(s_full), 1e-5, "state")
+    ro, rs, rz = oracle_chunk(inp, state_in=False, z_in=False)
+    assert_close(o_split, ro, TOL["f32"], "o vs oracle")
+    assert_close(host64(S), rs, TOL["f32"], "state vs oracle")
+    if norm:
+        assert_close(host64(Z), rz, 1e-6, "z vs oracle")
+
+
+@pytest.mark.parametrize("var", ["decay", "gated_delta", "normalized"])
+def test_deterministic(var):
+    inp = W.make_chunk_inputs(var, "bf16", 2, 4, 300, 128, 128, seed=6)
+    a = gpu_chunk(inp, 64)
+    b = gpu_chunk(inp, 64)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("var", ["plain", "decay", "gated_delta"])
+def test_chunk_sizes_agree(var):
+    """C = 64 and C = 128 compute the same result (tensorplay section 3.3: the
+    chunk size changes the schedule, not the value)."""
+    if var == "gated_delta":
+        pytest.skip("the delta rule is built for C = 64")
+    inp = W.make_chunk_inputs(var, "bf16", 1, 2, 500, 64, 64, seed=7)
+    o64, s64, _ = gpu_chunk(inp, 64, state_in=False)
+    o128, s128, _ = gpu_chunk(inp, 128, state_in=False)
+    ro, rs, _ = oracle_chunk(inp, state_in=False)
+    assert_close(o64, ro, TOL["bf16"], "C=64")
+    assert_close(o128, ro, TOL["bf16"], "C=128")
+
+
+@pytest.mark.parametrize("var", ["plain", "normalized", "decay", "gated_delta"])
+def test_nan_head_does_not_leak(var):
+    """Heads are independent: a NaN in one head's query stays in that head."""
+    inp = W.make_chunk_inputs(var, "bf16", 2, 2, 150, 64, 64, seed=8)
+    clean = gpu_chunk(inp, 64, state_in=False)[0]
+    inp.q = inp.q.copy()
+    inp.q[1, 0, 70, 5] = 0x7FC0  # bf16 quiet NaN
+    dirty = gpu_chunk(inp, 64, state_in=False)[0]
+    others = [(0, 0), (0, 1), (1, 1)]
+    for b, h in others:
+        assert np.array_equal(clean[b, h], dirty[b, h]), (b, h)
+    assert np.isnan(dirty[1, 0, 70]).any()
+
+
+def test_associative_recall_on_gpu():
+    """One-hot keys, beta = 1, alpha = 1 (tensorplay section 6 example, extended
+    with a rebinding): the delta rule returns the last value bound to each key,
+    plain linear attention the sum of the values bound to it."""
+    d = 32
+    writes = [(0, 4.0), (1, 3.0), (2, 6.0), (0, 9.0)]
+    queries = [0, 2, 1]
+    T = len(writes) + len(queries)
+    q = np.zeros((1, 1, T, d), np.float32); k = np.zeros_like(q); v = np.zeros((1, 1, T, d), np.float32)
+    for t, (key, val) in enumerate(writes):
+        k[0, 0, t, key] = 1.0
+        v[0, 0, t, 0] = val
+    for i, key in enumerate(queries):
+        q[0, 0, len(writes) + i, key] = 1.0
+    beta = np.ones((1, 1, T), np.float32)
+    o, _, _ = la.la_chunk_fwd("gated_delta", dev(q), dev(k), dev(v), None, dev(beta))
+    o2, _, _ = la.la_chunk_fwd("plain", dev(q), dev(k), dev(v))
+    torch.cuda.synchronize()
+    got = host64(o)[0, 0, len(writes):, 0]
+    got2 = host64(o2)[0, 0, len(writes):, 0]
+    assert np.allclose(got, [9.0, 6.0, 3.0], atol=1e-5), got
+    assert np.allclose(got2, [13.0, 6.0, 3.0], atol=1e-5), got2
+
+
+# ---------------------------------------------------------------------------
+# decode step
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("var", ["plain", "decay"])
+def test_decode_matches_oracle(var, dt, dk, dv):
+    N, H = 5, 3
+    S0 = W.make_decode_state(N, H, dk, dv, seed=2)
+    S = dev(S0)
+    Sref = S0.astype(np.float64)
+    for step in range(3):
+        st = W.make_decode_step(N, H, dk, dv, step=step, seed=2, dtype=dt)
+        lg = st.log_gate if var == "decay" else None
+        o = la.la_decode_step(var, dev(st.q), dev(st.k), dev(st.v), dev(lg), S)
+        torch.cuda.synchronize()
+        ro, Sref = oracle.decode_step(var, W.to_f64(st.q), W.to_f64(st.k), W.to_f64(st.v),
+                                      None if lg is None else lg.astype(np.float64), Sref)
+        assert_close(host64(o), ro, TOL[dt], f"o step {step}")
+        assert_close(host64(S), Sref, 1e-4, f"state step {step}")
+
+
+def test_prefill_then_decode():
+    """Prefill L tokens with the chunk kernel, then decode token L+1 from its
+    final state: equals the oracle over L+1 tokens (tensorplay section 2.2)."""
+    B, H, L, d = 2, 3, 190, 128
+    inp = W.make_chunk_inputs("decay", "bf16", B, H, L + 1, d, d, seed=9)
+    q, k, v, lg = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.log_gate)
+    pre = lambda x: x[:, :, :L].contiguous()
+    _, S, _ = la.la_chunk_fwd("decay", pre(q), pre(k), pre(v), pre(lg), want_state=True)
+    last = lambda x: x[:, :, L].contiguous()
+    o = la.la_decode_step("decay", last(q), last(k), last(v), last(lg), S)
+    torch.cuda.synchronize()
+    ro, rs, _ = oracle_chunk(inp, state_in=False)
+    assert_close(host64(o), ro[:, :, L], TOL["bf16"], "o")
+    assert_close(host64(S), rs, TOL["bf16"], "state")
