@@ -49,10 +49,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_chunk_fwd_workspace_size.restype = i
     lib.la_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.la_chunk_fwd.restype = i
-    lib.la_chunk_fwd.argtypes = [i, i, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp,
+    lib.la_chunk_fwd.argtypes = [i, i, i, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp,
                                  i, i, i, i, i, i, vp, sz, vp]
     lib.la_decode_step.restype = i
-    lib.la_decode_step.argtypes = [i, i, vp, vp, vp, fp, fp, fp, vp, i, i, i, i, vp]
+    lib.la_decode_step.argtypes = [i, i, i, vp, vp, vp, fp, fp, fp, vp, i, i, i, i, vp]
     _lib = lib
     return lib
 
@@ -67,11 +67,12 @@ def la_status_str(status: int) -> str:
 
 def _dt(x) -> int:
     import torch
-    if x.dtype == torch.bfloat16:
+    dtype = x if isinstance(x, torch.dtype) else x.dtype
+    if dtype == torch.bfloat16:
         return 1
-    if x.dtype == torch.float32:
+    if dtype == torch.float32:
         return 0
-    raise TypeError(f"unsupported dtype {x.dtype}: use torch.bfloat16 or torch.float32")
+    raise TypeError(f"unsupported dtype {dtype}: use torch.bfloat16 or torch.float32")
 
 
 def _ptr(x) -> Optional[int]:
@@ -100,15 +101,17 @@ def la_chunk_fwd_workspace_size(variant: str, dtype_code: int, B: int, H: int, L
 
 
 def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in=None, *,
-                 C: int = 64, o=None, state_out=None, z_out=None, want_state: bool = False,
-                 want_z: bool = False, workspace=None, stream=None) -> Tuple:
+                 C: int = 64, o=None, out_dtype=None, state_out=None, z_out=None,
+                 want_state: bool = False, want_z: bool = False, workspace=None,
+                 stream=None) -> Tuple:
     """Chunkwise causal linear-attention forward.
 
     q, k: [B, H, L, d_k]; v: [B, H, L, d_v] (bf16 or fp32, contiguous, on the GPU).
     log_gate, beta: [B, H, L] fp32; state_in: [B, H, d_k, d_v] fp32;
     z_in: [B, H, d_k] fp32. Returns (o, state_out or None, z_out or None).
-    Output buffers may be passed in (o, state_out, z_out); state_out may be
-    state_in for an in-place carry.
+    o is fp32 unless out_dtype=torch.bfloat16 (bf16 inputs only) or a bf16 ``o``
+    is passed. Output buffers may be passed in (o, state_out, z_out); state_out
+    may be state_in for an in-place carry.
     """
     import torch
     lib = load_library()
@@ -116,7 +119,7 @@ def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None,
     d_v = v.shape[-1]
     dt = _dt(q)
     if o is None:
-        o = torch.empty((B, H, L, d_v), dtype=q.dtype, device=q.device)
+        o = torch.empty((B, H, L, d_v), dtype=out_dtype or torch.float32, device=q.device)
     if want_state and state_out is None:
         state_out = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=q.device)
     if want_z and z_out is None:
@@ -128,7 +131,7 @@ def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None,
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     else:
         ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.la_chunk_fwd(VARIANTS[variant], dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
+    st = lib.la_chunk_fwd(VARIANTS[variant], dt, _dt(o), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
                           _ptr(beta), _ptr(state_in), _ptr(z_in), _ptr(o), _ptr(state_out),
                           _ptr(z_out), B, H, L, d_k, d_v, C, _ptr(workspace), ws_bytes,
                           _stream(q.device, stream))
@@ -137,16 +140,17 @@ def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None,
     return o, state_out, z_out
 
 
-def la_decode_step(variant: str, q, k, v, log_gate, state, *, o=None, beta=None, stream=None):
+def la_decode_step(variant: str, q, k, v, log_gate, state, *, o=None, out_dtype=None, beta=None,
+                   stream=None):
     """One decode step for [N, H] sequence-heads; ``state`` [N, H, d_k, d_v] fp32 is
-    updated in place. Returns o [N, H, d_v]."""
+    updated in place. Returns o [N, H, d_v] (fp32 unless out_dtype/o say bf16)."""
     import torch
     lib = load_library()
     N, H, d_k = q.shape
     d_v = v.shape[-1]
     if o is None:
-        o = torch.empty((N, H, d_v), dtype=q.dtype, device=q.device)
-    st = lib.la_decode_step(VARIANTS[variant], _dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
+        o = torch.empty((N, H, d_v), dtype=out_dtype or torch.float32, device=q.device)
+    st = lib.la_decode_step(VARIANTS[variant], _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
                             _ptr(beta), _ptr(state), _ptr(o), N, H, d_k, d_v,
                             _stream(q.device, stream))
     if st != LA_OK:

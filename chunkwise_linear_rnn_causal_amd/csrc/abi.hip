@@ -79,31 +79,31 @@ size_t chunk_workspace(la_variant var, la_dtype dt, int B, int H, int L, int d_k
     return gdn_w_bytes(dt, BH, Lp, d_k) + (size_t)BH * Lp * d_v * elem_size(dt);
 }
 
-template <typename T, int DK, int C>
+template <typename TI, typename TO, int DK, int C>
 hipError_t dispatch_chunk_c(la_variant var, const ChunkArgs &a, hipStream_t st) {
     switch (var) {
-        case LA_PLAIN: return launch_chunk<V_PLAIN, T, DK, kDVT, C>(a, st);
-        case LA_NORMALIZED: return launch_chunk<V_NORM, T, DK, kDVT, C>(a, st);
-        case LA_DECAY: return launch_chunk<V_DECAY, T, DK, kDVT, C>(a, st);
+        case LA_PLAIN: return launch_chunk<V_PLAIN, TI, TO, DK, kDVT, C>(a, st);
+        case LA_NORMALIZED: return launch_chunk<V_NORM, TI, TO, DK, kDVT, C>(a, st);
+        case LA_DECAY: return launch_chunk<V_DECAY, TI, TO, DK, kDVT, C>(a, st);
         default: break;
     }
     return hipErrorInvalidValue;
 }
 
-template <typename T, int DK>
+template <typename TI, typename TO, int DK>
 hipError_t dispatch_chunk(la_variant var, int C, const ChunkArgs &a, hipStream_t st) {
-    if (var == LA_GATED_DELTA) return launch_chunk<V_GDN, T, DK, kDVT, 64>(a, st);
-    if (C == 64) return dispatch_chunk_c<T, DK, 64>(var, a, st);
-    if constexpr (!(sizeof(T) == 4 && DK == 128)) return dispatch_chunk_c<T, DK, 128>(var, a, st);
+    if (var == LA_GATED_DELTA) return launch_chunk<V_GDN, TI, TO, DK, kDVT, 64>(a, st);
+    if (C == 64) return dispatch_chunk_c<TI, TO, DK, 64>(var, a, st);
+    if constexpr (!(sizeof(TI) == 4 && DK == 128)) return dispatch_chunk_c<TI, TO, DK, 128>(var, a, st);
     return hipErrorInvalidValue;
 }
 
-template <typename T>
+template <typename TI, typename TO>
 hipError_t dispatch_chunk_dk(la_variant var, int d_k, int C, const ChunkArgs &a, hipStream_t st) {
     switch (d_k) {
-        case 32: return dispatch_chunk<T, 32>(var, C, a, st);
-        case 64: return dispatch_chunk<T, 64>(var, C, a, st);
-        case 128: return dispatch_chunk<T, 128>(var, C, a, st);
+        case 32: return dispatch_chunk<TI, TO, 32>(var, C, a, st);
+        case 64: return dispatch_chunk<TI, TO, 64>(var, C, a, st);
+        case 128: return dispatch_chunk<TI, TO, 128>(var, C, a, st);
     }
     return hipErrorInvalidValue;
 }
@@ -118,24 +118,29 @@ hipError_t dispatch_prep(int d_k, const PrepArgs &a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
-template <int VAR, typename T, int DK>
+template <int VAR, typename TI, typename TO, int DK>
 hipError_t dispatch_decode_dv(int d_v, const DecodeArgs &a, hipStream_t st) {
     switch (d_v) {
-        case 32: return launch_decode<VAR, T, DK, 32>(a, st);
-        case 64: return launch_decode<VAR, T, DK, 64>(a, st);
-        case 128: return launch_decode<VAR, T, DK, 128>(a, st);
+        case 32: return launch_decode<VAR, TI, TO, DK, 32>(a, st);
+        case 64: return launch_decode<VAR, TI, TO, DK, 64>(a, st);
+        case 128: return launch_decode<VAR, TI, TO, DK, 128>(a, st);
     }
     return hipErrorInvalidValue;
 }
 
-template <int VAR, typename T>
+template <int VAR, typename TI, typename TO>
 hipError_t dispatch_decode(int d_k, int d_v, const DecodeArgs &a, hipStream_t st) {
     switch (d_k) {
-        case 32: return dispatch_decode_dv<VAR, T, 32>(d_v, a, st);
-        case 64: return dispatch_decode_dv<VAR, T, 64>(d_v, a, st);
-        case 128: return dispatch_decode_dv<VAR, T, 128>(d_v, a, st);
+        case 32: return dispatch_decode_dv<VAR, TI, TO, 32>(d_v, a, st);
+        case 64: return dispatch_decode_dv<VAR, TI, TO, 64>(d_v, a, st);
+        case 128: return dispatch_decode_dv<VAR, TI, TO, 128>(d_v, a, st);
     }
     return hipErrorInvalidValue;
+}
+
+// Supported (input, output) dtype pairs: bf16 -> fp32, bf16 -> bf16, fp32 -> fp32.
+bool dtype_pair_ok(la_dtype dt, la_dtype o_dt) {
+    return (dt == LA_BF16 && (o_dt == LA_F32 || o_dt == LA_BF16)) || (dt == LA_F32 && o_dt == LA_F32);
 }
 
 }  // namespace
@@ -163,15 +168,17 @@ la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
     return LA_OK;
 }
 
-la_status la_chunk_fwd(la_variant var, la_dtype dt, const void *q, const void *k, const void *v,
-                       const float *log_gate, const float *beta, const float *state_in,
-                       const float *z_in, void *o, float *state_out, float *z_out, int B, int H,
-                       int L, int d_k, int d_v, int C, void *workspace, size_t workspace_bytes,
-                       void *stream) {
+la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q, const void *k,
+                       const void *v, const float *log_gate, const float *beta,
+                       const float *state_in, const float *z_in, void *o, float *state_out,
+                       float *z_out, int B, int H, int L, int d_k, int d_v, int C, void *workspace,
+                       size_t workspace_bytes, void *stream) {
     la_status s = check_chunk_shape(var, dt, B, H, L, d_k, d_v, C);
     if (s != LA_OK) return s;
+    if (o_dt != LA_F32 && o_dt != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (!dtype_pair_ok(dt, o_dt)) return LA_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
-    const size_t es = elem_size(dt);
+    const size_t es = elem_size(dt), oes = elem_size(o_dt);
     const bool has_tokens = L > 0;
     // required / forbidden pointers
     if (has_tokens && (!q || !k || !o)) return LA_ERR_INVALID_ARG;
@@ -188,7 +195,7 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, const void *q, const void *k
     // aliasing: outputs must not overlap inputs (state_out == state_in is allowed)
     const size_t qk_b = (size_t)BH * L * d_k * es, v_b = (size_t)BH * L * d_v * es;
     const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4, z_b = (size_t)BH * d_k * 4;
-    const Span o_sp{o, v_b}, so_sp{state_out, s_b}, zo_sp{z_out, z_b};
+    const Span o_sp{o, (size_t)BH * L * d_v * oes}, so_sp{state_out, s_b}, zo_sp{z_out, z_b};
     const Span ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {log_gate, g_b}, {beta, g_b}, {z_in, z_b}};
     for (const Span &in : ins) {
         if (overlap(o_sp, in) || overlap(so_sp, in) || overlap(zo_sp, in)) return LA_ERR_INVALID_ARG;
@@ -233,16 +240,23 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, const void *q, const void *k
                                              : dispatch_prep<float>(d_k, p, st);
         if (e != hipSuccess) return LA_ERR_HIP;
     }
-    const hipError_t e = (dt == LA_BF16) ? dispatch_chunk_dk<bf16>(var, d_k, C, a, st)
-                                         : dispatch_chunk_dk<float>(var, d_k, C, a, st);
+    hipError_t e;
+    if (dt == LA_F32)
+        e = dispatch_chunk_dk<float, float>(var, d_k, C, a, st);
+    else if (o_dt == LA_F32)
+        e = dispatch_chunk_dk<bf16, float>(var, d_k, C, a, st);
+    else
+        e = dispatch_chunk_dk<bf16, bf16>(var, d_k, C, a, st);
     return from_hip(e);
 }
 
-la_status la_decode_step(la_variant var, la_dtype dt, const void *q, const void *k, const void *v,
-                         const float *log_gate, const float *beta, float *state, void *o, int N,
-                         int H, int d_k, int d_v, void *stream) {
+la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void *q, const void *k,
+                         const void *v, const float *log_gate, const float *beta, float *state,
+                         void *o, int N, int H, int d_k, int d_v, void *stream) {
     if (var < LA_PLAIN || var > LA_GATED_DELTA) return LA_ERR_INVALID_ARG;
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (o_dt != LA_F32 && o_dt != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (!dtype_pair_ok(dt, o_dt)) return LA_ERR_UNSUPPORTED;
     if (var == LA_NORMALIZED || var == LA_GATED_DELTA) return LA_ERR_UNSUPPORTED;
     if (N < 1 || H < 1) return LA_ERR_INVALID_ARG;
     if ((int64_t)N * H > INT32_MAX) return LA_ERR_UNSUPPORTED;
@@ -257,7 +271,7 @@ la_status la_decode_step(la_variant var, la_dtype dt, const void *q, const void 
         if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
     const int64_t NH = (int64_t)N * H;
     const size_t es = elem_size(dt);
-    const Span o_sp{o, (size_t)NH * d_v * es}, s_sp{state, (size_t)NH * d_k * d_v * 4};
+    const Span o_sp{o, (size_t)NH * d_v * elem_size(o_dt)}, s_sp{state, (size_t)NH * d_k * d_v * 4};
     const Span ins[] = {{q, (size_t)NH * d_k * es}, {k, (size_t)NH * d_k * es},
                         {v, (size_t)NH * d_v * es}, {log_gate, (size_t)NH * 4}};
     for (const Span &in : ins)
@@ -269,12 +283,15 @@ la_status la_decode_step(la_variant var, la_dtype dt, const void *q, const void 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     DecodeArgs a{q, k, v, log_gate, state, o, (int)NH};
     hipError_t e;
-    if (var == LA_DECAY)
-        e = (dt == LA_BF16) ? dispatch_decode<V_DECAY, bf16>(d_k, d_v, a, st)
-                            : dispatch_decode<V_DECAY, float>(d_k, d_v, a, st);
-    else
-        e = (dt == LA_BF16) ? dispatch_decode<V_PLAIN, bf16>(d_k, d_v, a, st)
-                            : dispatch_decode<V_PLAIN, float>(d_k, d_v, a, st);
+    if (var == LA_DECAY) {
+        if (dt == LA_F32) e = dispatch_decode<V_DECAY, float, float>(d_k, d_v, a, st);
+        else if (o_dt == LA_F32) e = dispatch_decode<V_DECAY, bf16, float>(d_k, d_v, a, st);
+        else e = dispatch_decode<V_DECAY, bf16, bf16>(d_k, d_v, a, st);
+    } else {
+        if (dt == LA_F32) e = dispatch_decode<V_PLAIN, float, float>(d_k, d_v, a, st);
+        else if (o_dt == LA_F32) e = dispatch_decode<V_PLAIN, bf16, float>(d_k, d_v, a, st);
+        else e = dispatch_decode<V_PLAIN, bf16, bf16>(d_k, d_v, a, st);
+    }
     return from_hip(e);
 }
 

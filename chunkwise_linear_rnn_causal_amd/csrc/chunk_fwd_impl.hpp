@@ -36,24 +36,27 @@
 namespace la {
 
 template <typename T> __device__ inline float frag_elem(const typename Mfma<T>::frag &f, int i);
-template <> __device__ inline float frag_elem<bf16>(const bf16x8 &f, int i) { return (float)f[i]; }
+template <> __device__ inline float frag_elem<f16>(const f16x8 &f, int i) { return (float)f[i]; }
 template <> __device__ inline float frag_elem<float>(const float &f, int) { return f; }
 
-template <int VAR, typename T, int DK, int DVT, int C>
+template <int VAR, typename TM, int DK, int DVT, int C>
 struct ChunkCfg {
     static constexpr int NW = 4;
-    static constexpr int PAD = 16 / (int)sizeof(T);
+    static constexpr int PAD = 16 / (int)sizeof(TM);
     static constexpr int KP = DK + PAD;  // row pitch of Ks / STs (elements)
     static constexpr size_t lds_bytes =
-        sizeof(T) * ((size_t)C * KP + (size_t)DK * C + (size_t)DVT * C + (size_t)DVT * KP) +
+        sizeof(TM) * ((size_t)C * KP + (size_t)DK * C + (size_t)DVT * C + (size_t)DVT * KP) +
         sizeof(float) * (C + (VAR == V_NORM ? 2 * DK : 1));
 };
 
-template <int VAR, typename T, int DK, int DVT, int C>
+// TI: input storage type (bf16 or fp32); TO: output type (fp32 or bf16); the
+// tensor-core operand type TM is fp16 for bf16 inputs and fp32 for fp32 inputs.
+template <int VAR, typename TI, typename TO, int DK, int DVT, int C>
 __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
-    using MF = Mfma<T>;
+    using TM = typename OpOf<TI>::type;
+    using MF = Mfma<TM>;
     using frag = typename MF::frag;
-    using Cfg = ChunkCfg<VAR, T, DK, DVT, C>;
+    using Cfg = ChunkCfg<VAR, TM, DK, DVT, C>;
     constexpr int E = MF::E;
     constexpr int NW = Cfg::NW;
     constexpr int NRB = C / 16;          // 16-row blocks per chunk
@@ -68,10 +71,10 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
     static_assert(NRB % NW == 0 && (RBW == 1 || RBW == 2), "C must be 64 or 128");
     static_assert(DVT % 16 == 0 && DK % 32 == 0, "tile sizes");
 
-    __shared__ __attribute__((aligned(16))) T Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) T KTs[DK * C];
-    __shared__ __attribute__((aligned(16))) T VTs[DVT * C];
-    __shared__ __attribute__((aligned(16))) T STs[DVT * KP];
+    __shared__ __attribute__((aligned(16))) TM Ks[C * KP];
+    __shared__ __attribute__((aligned(16))) TM KTs[DK * C];
+    __shared__ __attribute__((aligned(16))) TM VTs[DVT * C];
+    __shared__ __attribute__((aligned(16))) TM STs[DVT * KP];
     __shared__ float Gs[C];
     __shared__ float Zs[VAR == V_NORM ? 2 * DK : 1];
 
@@ -81,13 +84,13 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
     const int j0 = split * DVT;
     const int L = a.L, dv = a.dv;
 
-    const T *qg = (const T *)a.q + (size_t)bh * L * DK;
-    const T *kg = (const T *)a.k + (size_t)bh * L * DK;
-    const T *vg = (VAR == V_GDN) ? nullptr : (const T *)a.v + (size_t)bh * L * dv + j0;
-    T *og = (T *)a.o + (size_t)bh * L * dv + j0;
+    const TI *qg = (const TI *)a.q + (size_t)bh * L * DK;
+    const TI *kg = (const TI *)a.k + (size_t)bh * L * DK;
+    const TI *vg = (VAR == V_GDN) ? nullptr : (const TI *)a.v + (size_t)bh * L * dv + j0;
+    TO *og = (TO *)a.o + (size_t)bh * L * dv + j0;
     const float *lgg = (DECAYED && a.lg) ? a.lg + (size_t)bh * L : nullptr;
-    const T *wg = (VAR == V_GDN) ? (const T *)a.w + (size_t)bh * a.Lp * DK : nullptr;
-    const T *utg = (VAR == V_GDN) ? (const T *)a.ut + ((size_t)bh * dv + j0) * a.Lp : nullptr;
+    const TM *wg = (VAR == V_GDN) ? (const TM *)a.w + (size_t)bh * a.Lp * DK : nullptr;
+    const TM *utg = (VAR == V_GDN) ? (const TM *)a.ut + ((size_t)bh * dv + j0) * a.Lp : nullptr;
 
     // ---- initial state slice in accumulator layout: lane (g, n) of tile (ti, tj)
     // holds S[ti*16 + 4g + e][j0 + tj*16 + n].
@@ -119,7 +122,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
             const int tile = wv + NW * m;
             if (tile < NTI * NTJ) {
                 const int ti = tile / NTJ, tj = tile % NTJ;
-                st4<T>(&STs[(tj * 16 + n) * KP + ti * 16 + 4 * g], Sacc[m]);
+                st4<TM>(&STs[(tj * 16 + n) * KP + ti * 16 + 4 * g], Sacc[m]);
             }
         }
 
@@ -176,20 +179,22 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int t = t0 + 4 * tq + r;
                     if (t < L) {
-                        ld8<T>(kg + (size_t)t * DK + 8 * cb, x[r]);
+                        ld8<TI>(kg + (size_t)t * DK + 8 * cb, x[r]);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
                     }
-                    st8<T>(&Ks[(4 * tq + r) * KP + 8 * cb], x[r]);
+                    st8<TM>(&Ks[(4 * tq + r) * KP + 8 * cb], x[r]);
                 }
-                float wsc[4];
+                float wsc[4] = {1.f, 1.f, 1.f, 1.f};
+                if constexpr (DECAYED) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) wsc[r] = DECAYED ? __expf(gC - G_of(4 * tq + r)) : 1.f;
+                    for (int r = 0; r < 4; ++r) wsc[r] = __expf(gC - G_of(4 * tq + r));
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     f32x4 col = {x[0][e] * wsc[0], x[1][e] * wsc[1], x[2][e] * wsc[2], x[3][e] * wsc[3]};
-                    st4<T>(&KTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+                    st4<TM>(&KTs[tidx<C>(8 * cb + e, 4 * tq)], col);
                 }
             }
         }
@@ -207,7 +212,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int t = t0 + 4 * tq + r;
                     if (t < L) {
-                        ld8<T>(vg + (size_t)t * dv + 8 * cb, x[r]);
+                        ld8<TI>(vg + (size_t)t * dv + 8 * cb, x[r]);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
@@ -216,7 +221,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     f32x4 col = {x[0][e], x[1][e], x[2][e], x[3][e]};
-                    st4<T>(&VTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+                    st4<TM>(&VTs[tidx<C>(8 * cb + e, 4 * tq)], col);
                 }
             }
         }
@@ -229,15 +234,15 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
                 const int sbk = u / NTJ, tj = u % NTJ;
                 const int jj = tj * 16 + n;
                 // D[s][j] tile: lane (g, n) holds s = sbk*16 + 4g + e, j = jj.
-                f32x4 acc = ld4<T>(utg + (size_t)jj * a.Lp + t0 + sbk * 16 + 4 * g);
-                const T *wrow = wg + (size_t)(t0 + sbk * 16 + n) * DK + g * (DK / 4);
+                f32x4 acc = ld4<TM>(utg + (size_t)jj * a.Lp + t0 + sbk * 16 + 4 * g);
+                const TM *wrow = wg + (size_t)(t0 + sbk * 16 + n) * DK + g * (DK / 4);
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
-                    const frag wa = neg_frag<T>(ld_frag<T>(wrow + ks * E));
-                    const frag sb = ld_frag<T>(&STs[jj * KP + g * (DK / 4) + ks * E]);
+                    const frag wa = neg_frag<TM>(ld_frag<TM>(wrow + ks * E));
+                    const frag sb = ld_frag<TM>(&STs[jj * KP + g * (DK / 4) + ks * E]);
                     acc = MF::mma(wa, sb, acc);
                 }
-                st4<T>(&VTs[tidx<C>(jj, sbk * 16 + 4 * g)], acc);
+                st4<TM>(&VTs[tidx<C>(jj, sbk * 16 + 4 * g)], acc);
             }
             __syncthreads();
         }
@@ -247,7 +252,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
         if constexpr (VAR == V_NORM) {
             for (int i = tid; i < DK; i += 256) {
                 float sacc = 0.f;
-                for (int s = 0; s < C; ++s) sacc += to_f32<T>(Ks[s * KP + i]);
+                for (int s = 0; s < C; ++s) sacc += to_f32<TM>(Ks[s * KP + i]);
                 Zs[zn + i] = Zs[zc + i] + sacc;
             }
         }
@@ -261,8 +266,8 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
             frag qf[NKS];
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                qf[ks] = (rrow < L) ? ld_frag<T>(qg + (size_t)rrow * DK + g * (DK / 4) + ks * E)
-                                    : zero_frag<T>();
+                qf[ks] = (rrow < L) ? ld_frag_as<TI, TM>(qg + (size_t)rrow * DK + g * (DK / 4) + ks * E)
+                                    : zero_frag<TM>();
             const float Gr = DECAYED ? Gs[rl] : 0.f;
 
             // inter-chunk term: D[j][r] = sum_i S[i][j] q_r[i]
@@ -272,7 +277,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
                 oacc[tj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
-                    oacc[tj] = MF::mma(ld_frag<T>(&STs[(tj * 16 + n) * KP + g * (DK / 4) + ks * E]),
+                    oacc[tj] = MF::mma(ld_frag<TM>(&STs[(tj * 16 + n) * KP + g * (DK / 4) + ks * E]),
                                        qf[ks], oacc[tj]);
             }
             if constexpr (DECAYED) {
@@ -290,7 +295,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
                 if (sb <= rb) {
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
-                        sc[sb] = MF::mma(ld_frag<T>(&Ks[(sb * 16 + n) * KP + g * (DK / 4) + ks * E]),
+                        sc[sb] = MF::mma(ld_frag<TM>(&Ks[(sb * 16 + n) * KP + g * (DK / 4) + ks * E]),
                                          qf[ks], sc[sb]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -301,7 +306,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
                         } else if constexpr (DECAYED) {
                             x *= __expf(Gr - Gs[sl]);
                         }
-                        x = to_f32<T>(from_f32<T>(x));
+                        x = to_f32<TM>(from_f32<TM>(x));
                         sc[sb][e] = x;
                         if constexpr (VAR == V_NORM) rowsum += x;
                     }
@@ -310,26 +315,27 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
 
             // intra-chunk term: D[j][r] += sum_s V[s][j] A[r][s]
             if constexpr (E == 8) {
+                using V4 = typename Vec4<TM>::type;
 #pragma unroll
                 for (int p = 0; p < NRB / 2; ++p) {
                     if (2 * p <= rb) {
-                        bf16x8 bop;
+                        frag bop;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            bop[e] = (bf16)sc[2 * p][e];
-                            bop[4 + e] = (bf16)sc[2 * p + 1][e];
+                            bop[e] = from_f32<TM>(sc[2 * p][e]);
+                            bop[4 + e] = from_f32<TM>(sc[2 * p + 1][e]);
                         }
                         const bool hi = (2 * p + 1 <= rb);
 #pragma unroll
                         for (int tj = 0; tj < NTJ; ++tj) {
                             const int jj = tj * 16 + n;
-                            const bf16x4 lo4 = *reinterpret_cast<const bf16x4 *>(&VTs[tidx<C>(jj, 32 * p + 4 * g)]);
-                            bf16x4 hi4 = *reinterpret_cast<const bf16x4 *>(&VTs[tidx<C>(jj, 32 * p + 16 + 4 * g)]);
+                            const V4 lo4 = *reinterpret_cast<const V4 *>(&VTs[tidx<C>(jj, 32 * p + 4 * g)]);
+                            V4 hi4 = *reinterpret_cast<const V4 *>(&VTs[tidx<C>(jj, 32 * p + 16 + 4 * g)]);
                             if (!hi) {
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) hi4[e] = (bf16)0.0f;
+                                for (int e = 0; e < 4; ++e) hi4[e] = from_f32<TM>(0.0f);
                             }
-                            bf16x8 aop;
+                            frag aop;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 aop[e] = lo4[e];
@@ -360,7 +366,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
                 for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
                     for (int el = 0; el < E; ++el)
-                        qz += frag_elem<T>(qf[ks], el) * Zs[zc + g * (DK / 4) + ks * E + el];
+                        qz += frag_elem<TM>(qf[ks], el) * Zs[zc + g * (DK / 4) + ks * E + el];
                 float den = rowsum + qz;
                 den += __shfl_xor(den, 16, 64);
                 den += __shfl_xor(den, 32, 64);
@@ -371,7 +377,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
 
             if (rrow < L) {
 #pragma unroll
-                for (int tj = 0; tj < NTJ; ++tj) st4<T>(og + (size_t)rrow * dv + tj * 16 + 4 * g, oacc[tj]);
+                for (int tj = 0; tj < NTJ; ++tj) st4<TO>(og + (size_t)rrow * dv + tj * 16 + 4 * g, oacc[tj]);
             }
         }
 
@@ -389,8 +395,8 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < NTK; ++ks) {
                     const int s0 = g * (C / 4) + ks * E;
-                    Sacc[m] = MF::mma(ld_frag<T>(&KTs[tidx<C>(ti * 16 + n, s0)]),
-                                      ld_frag<T>(&VTs[tidx<C>(tj * 16 + n, s0)]), Sacc[m]);
+                    Sacc[m] = MF::mma(ld_frag<TM>(&KTs[tidx<C>(ti * 16 + n, s0)]),
+                                      ld_frag<TM>(&VTs[tidx<C>(tj * 16 + n, s0)]), Sacc[m]);
                 }
             }
         }
@@ -415,10 +421,10 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
     }
 }
 
-template <int VAR, typename T, int DK, int DVT, int C>
+template <int VAR, typename TI, typename TO, int DK, int DVT, int C>
 hipError_t launch_chunk(const ChunkArgs &a, hipStream_t st) {
     const int blocks = a.BH * a.nsplit;
-    hipLaunchKernelGGL((chunk_fwd_kernel<VAR, T, DK, DVT, C>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((chunk_fwd_kernel<VAR, TI, TO, DK, DVT, C>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

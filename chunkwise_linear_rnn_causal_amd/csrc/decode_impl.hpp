@@ -16,7 +16,7 @@
 
 namespace la {
 
-template <int VAR, typename T, int DK, int DV>
+template <int VAR, typename TI, typename TO, int DK, int DV>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     constexpr int CG = DV / 4;        // 16-byte column groups per row
     constexpr int RG = 256 / CG;      // row groups
@@ -35,15 +35,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     for (int m = 0; m < RPT; ++m)
         s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)m * DV));
 
-    const T *qp = (const T *)a.q + h * DK + rg * RPT;
-    const T *kp = (const T *)a.k + h * DK + rg * RPT;
+    const TI *qp = (const TI *)a.q + h * DK + rg * RPT;
+    const TI *kp = (const TI *)a.k + h * DK + rg * RPT;
     float qr[RPT], kr[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
-        qr[m] = to_f32<T>(qp[m]);
-        kr[m] = to_f32<T>(kp[m]);
+        qr[m] = to_f32<TI>(qp[m]);
+        kr[m] = to_f32<TI>(kp[m]);
     }
-    const f32x4 vv = ld4<T>((const T *)a.v + h * DV + 4 * cg);
+    const f32x4 vv = ld4<TI>((const TI *)a.v + h * DV + 4 * cg);
     const float gam = (VAR == V_DECAY) ? __expf(a.lg[h]) : 1.f;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -64,14 +64,14 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     __syncthreads();
     if (tid < CG) {
         const f32x4 o = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-        st4<T>((T *)a.o + h * DV + 4 * tid, o);
+        st4<TO>((TO *)a.o + h * DV + 4 * tid, o);
     }
     (void)RGW;
 }
 
-template <int VAR, typename T, int DK, int DV>
+template <int VAR, typename TI, typename TO, int DK, int DV>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((decode_kernel<VAR, T, DK, DV>), dim3(a.NH), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<VAR, TI, TO, DK, DV>), dim3(a.NH), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

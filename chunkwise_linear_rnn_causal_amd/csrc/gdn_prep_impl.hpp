@@ -15,7 +15,8 @@
 // chunk in parallel (one workgroup per chunk); the serial chunk pass then only
 // forms U = U~ - W S_prev.
 //
-// Layout of the results: W row-major [BH, Lp, DK]; U~ transposed [BH, dv, Lp]
+// Layout of the results, in the tensor-core operand type (fp16 for bf16
+// inputs, fp32 for fp32 inputs): W row-major [BH, Lp, DK]; U~ transposed [BH, dv, Lp]
 // (so the serial pass reads four consecutive tokens per lane). Padded tokens
 // (t >= L) have beta = 0 and k = v = 0, which makes their rows of W and U~ zero.
 #pragma once
@@ -25,22 +26,23 @@
 
 namespace la {
 
-template <typename T, int DK, int C>
+template <typename TM, int DK, int C>
 struct PrepCfg {
     static constexpr int DVMAX = 128;
-    static constexpr int PAD = 16 / (int)sizeof(T);
+    static constexpr int PAD = 16 / (int)sizeof(TM);
     static constexpr int KP = DK + PAD;
     static constexpr int TP = C + 1;  // fp32 row pitch of P and T
     static constexpr size_t lds_bytes =
-        sizeof(T) * ((size_t)C * KP + (size_t)DK * C + (size_t)DVMAX * C) +
+        sizeof(TM) * ((size_t)C * KP + (size_t)DK * C + (size_t)DVMAX * C) +
         sizeof(float) * (2 * (size_t)C * TP + 2 * C);
 };
 
-template <typename T, int DK, int C>
+template <typename TI, int DK, int C>
 __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
-    using MF = Mfma<T>;
+    using TM = typename OpOf<TI>::type;
+    using MF = Mfma<TM>;
     using frag = typename MF::frag;
-    using Cfg = PrepCfg<T, DK, C>;
+    using Cfg = PrepCfg<TM, DK, C>;
     constexpr int E = MF::E;
     constexpr int NW = 4;
     constexpr int NRB = C / 16;
@@ -49,9 +51,9 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     constexpr int NTK = C / (4 * E);
     static_assert(C == 64, "the row-by-row inverse assigns one column per lane: C = 64");
 
-    __shared__ __attribute__((aligned(16))) T Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) T KTs[DK * C];
-    __shared__ __attribute__((aligned(16))) T VTs[Cfg::DVMAX * C];
+    __shared__ __attribute__((aligned(16))) TM Ks[C * KP];
+    __shared__ __attribute__((aligned(16))) TM KTs[DK * C];
+    __shared__ __attribute__((aligned(16))) TM VTs[Cfg::DVMAX * C];
     __shared__ float Pm[C * TP];
     __shared__ float Tm[C * TP];
     __shared__ float Gs[C];
@@ -60,8 +62,8 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
     const int bh = blockIdx.x / a.nchunks, c = blockIdx.x - bh * a.nchunks;
     const int t0 = c * C, L = a.L, dv = a.dv;
-    const T *kg = (const T *)a.k + (size_t)bh * L * DK;
-    const T *vg = (const T *)a.v + (size_t)bh * L * dv;
+    const TI *kg = (const TI *)a.k + (size_t)bh * L * DK;
+    const TI *vg = (const TI *)a.v + (size_t)bh * L * dv;
     const float *lgg = a.lg ? a.lg + (size_t)bh * L : nullptr;
     const float *bg = a.beta + (size_t)bh * L;
 
@@ -94,18 +96,18 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int s = 4 * tq + r, t = t0 + s;
                 if (t < L) {
-                    ld8<T>(kg + (size_t)t * DK + 8 * cb, x[r]);
+                    ld8<TI>(kg + (size_t)t * DK + 8 * cb, x[r]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
                 }
-                st8<T>(&Ks[s * KP + 8 * cb], x[r]);
+                st8<TM>(&Ks[s * KP + 8 * cb], x[r]);
                 sc[r] = __shfl(bv, s, 64) * __expf(__shfl(G, s, 64));
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 f32x4 col = {x[0][e] * sc[0], x[1][e] * sc[1], x[2][e] * sc[2], x[3][e] * sc[3]};
-                st4<T>(&KTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+                st4<TM>(&KTs[tidx<C>(8 * cb + e, 4 * tq)], col);
             }
         }
     }
@@ -122,7 +124,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int s = 4 * tq + r, t = t0 + s;
                 if (t < L) {
-                    ld8<T>(vg + (size_t)t * dv + 8 * cb, x[r]);
+                    ld8<TI>(vg + (size_t)t * dv + 8 * cb, x[r]);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
@@ -132,7 +134,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 f32x4 col = {x[0][e] * sc[0], x[1][e] * sc[1], x[2][e] * sc[2], x[3][e] * sc[3]};
-                st4<T>(&VTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+                st4<TM>(&VTs[tidx<C>(8 * cb + e, 4 * tq)], col);
             }
         }
     }
@@ -147,8 +149,8 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-            d = MF::mma(ld_frag<T>(&Ks[(rb * 16 + n) * KP + g * (DK / 4) + ks * E]),
-                        ld_frag<T>(&Ks[(sb * 16 + n) * KP + g * (DK / 4) + ks * E]), d);
+            d = MF::mma(ld_frag<TM>(&Ks[(rb * 16 + n) * KP + g * (DK / 4) + ks * E]),
+                        ld_frag<TM>(&Ks[(sb * 16 + n) * KP + g * (DK / 4) + ks * E]), d);
         const int s = sb * 16 + n;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -176,9 +178,9 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     // T operand fragment: lane (g, n) holds T[r][s0 .. s0+E-1] with r = rb*16 + n.
     auto t_frag = [&](int r, int s0) -> frag {
         if constexpr (E == 8) {
-            bf16x8 f;
+            frag f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = (bf16)Tm[r * TP + s0 + e];
+            for (int e = 0; e < 8; ++e) f[e] = from_f32<TM>(Tm[r * TP + s0 + e]);
             return f;
         } else {
             return Tm[r * TP + s0];
@@ -186,19 +188,19 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     };
 
     // W^T tiles D[ch][r] = sum_s (beta a K)[s][ch] T[r][s]; lane holds ch = cbk*16 + 4g + e.
-    T *wout = (T *)a.w + ((size_t)bh * a.Lp + t0) * DK;
+    TM *wout = (TM *)a.w + ((size_t)bh * a.Lp + t0) * DK;
     for (int tile = wv; tile < (DK / 16) * NRB; tile += NW) {
         const int cbk = tile / NRB, rb = tile % NRB;
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NTK; ++ks) {
             const int s0 = g * (C / 4) + ks * E;
-            d = MF::mma(ld_frag<T>(&KTs[tidx<C>(cbk * 16 + n, s0)]), t_frag(rb * 16 + n, s0), d);
+            d = MF::mma(ld_frag<TM>(&KTs[tidx<C>(cbk * 16 + n, s0)]), t_frag(rb * 16 + n, s0), d);
         }
-        st4<T>(wout + (size_t)(rb * 16 + n) * DK + cbk * 16 + 4 * g, d);
+        st4<TM>(wout + (size_t)(rb * 16 + n) * DK + cbk * 16 + 4 * g, d);
     }
     // U~ tiles D[r][j] = sum_s T[r][s] (beta V)[s][j]; lane holds r = rb*16 + 4g + e.
-    T *uout = (T *)a.ut + (size_t)bh * dv * a.Lp + t0;
+    TM *uout = (TM *)a.ut + (size_t)bh * dv * a.Lp + t0;
     const int NJB = dv / 16;
     for (int tile = wv; tile < NRB * NJB; tile += NW) {
         const int rb = tile / NJB, jb = tile % NJB;
@@ -206,16 +208,16 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NTK; ++ks) {
             const int s0 = g * (C / 4) + ks * E;
-            d = MF::mma(t_frag(rb * 16 + n, s0), ld_frag<T>(&VTs[tidx<C>(jb * 16 + n, s0)]), d);
+            d = MF::mma(t_frag(rb * 16 + n, s0), ld_frag<TM>(&VTs[tidx<C>(jb * 16 + n, s0)]), d);
         }
-        st4<T>(uout + (size_t)(jb * 16 + n) * a.Lp + rb * 16 + 4 * g, d);
+        st4<TM>(uout + (size_t)(jb * 16 + n) * a.Lp + rb * 16 + 4 * g, d);
     }
 }
 
-template <typename T, int DK, int C>
+template <typename TI, int DK, int C>
 hipError_t launch_gdn_prep(const PrepArgs &a, hipStream_t st) {
     const int blocks = a.BH * a.nchunks;
-    hipLaunchKernelGGL((gdn_prep_kernel<T, DK, C>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gdn_prep_kernel<TI, DK, C>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -17,6 +17,9 @@ namespace la {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 enum Variant { V_PLAIN = 0, V_NORM = 1, V_DECAY = 2, V_GDN = 3 };
@@ -32,6 +35,22 @@ template <> struct Mfma<bf16> {
     }
 };
 
+template <> struct Mfma<f16> {
+    static constexpr int E = 8;  // operand elements per lane (K = 32)
+    using frag = f16x8;
+    __device__ static inline f32x4 mma(const frag &a, const frag &b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Tensor-core operand type for an input storage type. bf16 inputs are computed
+// on fp16 operands: every bf16 value of magnitude in [2^-14, 65504] is exact in
+// fp16, and the intermediates (state, scores, pseudo-values) then round to 11
+// significant bits instead of 8, at the same MFMA rate.
+template <typename TI> struct OpOf;
+template <> struct OpOf<bf16> { using type = f16; };
+template <> struct OpOf<float> { using type = float; };
+
 template <> struct Mfma<float> {
     static constexpr int E = 1;  // K = 4
     using frag = float;
@@ -43,15 +62,20 @@ template <> struct Mfma<float> {
 template <typename T> __device__ inline T from_f32(float x);
 template <> __device__ inline float from_f32<float>(float x) { return x; }
 template <> __device__ inline bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ inline f16 from_f32<f16>(float x) { return (f16)x; }
 
 template <typename T> __device__ inline float to_f32(T x);
 template <> __device__ inline float to_f32<float>(float x) { return x; }
 template <> __device__ inline float to_f32<bf16>(bf16 x) { return (float)x; }
+template <> __device__ inline float to_f32<f16>(f16 x) { return (float)x; }
 
 // E contiguous elements -> operand fragment (p must be E*sizeof(T) aligned).
 template <typename T> __device__ inline typename Mfma<T>::frag ld_frag(const T *p);
 template <> __device__ inline bf16x8 ld_frag<bf16>(const bf16 *p) {
     return *reinterpret_cast<const bf16x8 *>(p);
+}
+template <> __device__ inline f16x8 ld_frag<f16>(const f16 *p) {
+    return *reinterpret_cast<const f16x8 *>(p);
 }
 template <> __device__ inline float ld_frag<float>(const float *p) { return *p; }
 
@@ -60,6 +84,12 @@ template <> __device__ inline bf16x8 zero_frag<bf16>() {
     bf16x8 z;
 #pragma unroll
     for (int i = 0; i < 8; ++i) z[i] = (bf16)0.0f;
+    return z;
+}
+template <> __device__ inline f16x8 zero_frag<f16>() {
+    f16x8 z;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) z[i] = (f16)0.0f;
     return z;
 }
 template <> __device__ inline float zero_frag<float>() { return 0.0f; }
@@ -71,11 +101,17 @@ template <> __device__ inline bf16x8 neg_frag<bf16>(bf16x8 f) {
     for (int i = 0; i < 8; ++i) f[i] = -f[i];
     return f;
 }
+template <> __device__ inline f16x8 neg_frag<f16>(f16x8 f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = -f[i];
+    return f;
+}
 template <> __device__ inline float neg_frag<float>(float f) { return -f; }
 
 // Four consecutive elements to / from memory (vectorised for both types).
 template <typename T> struct Vec4;
 template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<f16> { typedef f16x4 type; };
 template <> struct Vec4<float> { typedef f32x4 type; };
 
 template <typename T> __device__ inline void st4(T *p, f32x4 x) {
@@ -93,8 +129,6 @@ template <typename T> __device__ inline f32x4 ld4(const T *p) {
 }
 
 // Eight consecutive elements held as fp32 (global or LDS).
-template <typename T> struct Row8 { float x[8]; };
-
 template <typename T> __device__ inline void ld8(const T *p, float (&x)[8]) {
     f32x4 a = ld4<T>(p), b = ld4<T>(p + 4);
     x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
@@ -104,6 +138,21 @@ template <typename T> __device__ inline void st8(T *p, const float (&x)[8]) {
     f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
     st4<T>(p, a);
     st4<T>(p + 4, b);
+}
+
+// Operand fragment of type TM read from memory holding type TI (converted).
+template <typename TI, typename TM>
+__device__ inline typename Mfma<TM>::frag ld_frag_as(const TI *p) {
+    if constexpr (sizeof(TI) == sizeof(TM) && Mfma<TM>::E == 1) {
+        return (typename Mfma<TM>::frag)(*p);
+    } else {
+        typename Mfma<TM>::frag f;
+        float x[8];
+        ld8<TI>(p, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = from_f32<TM>(x[i]);
+        return f;
+    }
 }
 
 // Transposed, swizzled [rows][C] tile (token index innermost). Tokens are

@@ -17,8 +17,8 @@ struct ChunkArgs {
     void *o;                    // [BH, L, dv]
     float *s_out;               // [BH, DK, dv] or nullptr
     float *z_out;               // [BH, DK] or nullptr (normalized only)
-    const void *w;              // gated delta: W  [BH, Lp, DK]
-    const void *ut;             // gated delta: U~ transposed [BH, dv, Lp]
+    const void *w;              // gated delta: W  [BH, Lp, DK] (operand type)
+    const void *ut;             // gated delta: U~ transposed [BH, dv, Lp] (operand type)
     int BH, L, Lp, dv, nsplit;  // Lp = ceil(L / C) * C; nsplit = dv / DVT
 };
 
@@ -41,13 +41,14 @@ struct DecodeArgs {
 // Value-column slice width handled by one workgroup of the chunk kernel.
 constexpr int kDVT = 32;
 
-template <int VAR, typename T, int DK, int DVT, int C>
+// TI: input type (bf16 or float); TO: output type (float or bf16).
+template <int VAR, typename TI, typename TO, int DK, int DVT, int C>
 hipError_t launch_chunk(const ChunkArgs &a, hipStream_t st);
 
-template <typename T, int DK, int C>
+template <typename TI, int DK, int C>
 hipError_t launch_gdn_prep(const PrepArgs &a, hipStream_t st);
 
-template <int VAR, typename T, int DK, int DV>
+template <int VAR, typename TI, typename TO, int DK, int DV>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
 
 }  // namespace la

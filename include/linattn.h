@@ -41,9 +41,16 @@
  *      q, k [B, H, L, d_k];  v, o [B, H, L, d_v];  log_gate, beta [B, H, L];
  *      state [B, H, d_k, d_v];  z [B, H, d_k].
  *    Tensor pointers must be 16-byte aligned.
- *  - dtype: LA_BF16 means q, k, v, o are bfloat16 (o rounded to nearest even
- *    from the fp32 accumulators); LA_F32 means they are float32. Gates, beta,
- *    states and normalizers are always float32.
+ *  - dt is the dtype of q, k, v: LA_BF16 or LA_F32. o_dt is the dtype of o:
+ *    LA_F32 (any dt) or LA_BF16 (dt = LA_BF16 only; rounded to nearest even from
+ *    the fp32 accumulators). Gates, beta, states and normalizers are float32.
+ *  - Numerics. fp32 inputs are computed on fp32 tensor-core operands. bf16
+ *    inputs are computed on fp16 tensor-core operands with fp32 accumulation:
+ *    bf16 values are exact in fp16 for magnitudes in [2^-14, 65504]; smaller
+ *    ones keep an absolute error below 2^-25, larger ones (and intermediate
+ *    scores or states beyond 65504) are outside the supported range. The state
+ *    carried from chunk to chunk stays in fp32. Choose o_dt = LA_F32 when the
+ *    output is compared at a tolerance finer than bf16's 2^-8 relative spacing.
  *  - No C++ exception crosses this boundary. Thread-safe for distinct streams.
  */
 #ifndef LINATTN_H
@@ -83,7 +90,8 @@ typedef enum la_dtype {
  * Zero for LA_PLAIN, LA_NORMALIZED and LA_DECAY, which run in one fused pass.
  * LA_GATED_DELTA runs a chunk-parallel preparation pass first and stores its
  * per-chunk products (W and U~ of the chunkwise delta-rule form) there:
- * B*H*ceil(L/C)*C*(d_k + d_v) elements of the input dtype.
+ * B*H*ceil(L/C)*C*d_k elements (rounded up to 256 bytes) plus B*H*ceil(L/C)*C*d_v
+ * elements, 2 bytes each for bf16 inputs and 4 for fp32.
  * Returns LA_ERR_INVALID_ARG / LA_ERR_UNSUPPORTED like la_chunk_fwd.
  */
 la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H, int L,
@@ -91,7 +99,7 @@ la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
 
 /*
  * Chunkwise forward over a whole sequence.
- *   q, k, v     inputs (dtype dt), required.
+ *   q, k, v     inputs (dtype dt), required when L > 0.
  *   log_gate    [B,H,L] float32 log-gates l_t <= 0 (finite): required for
  *               LA_DECAY; optional for LA_GATED_DELTA (NULL = alpha 1); must be
  *               NULL for LA_PLAIN and LA_NORMALIZED.
@@ -100,12 +108,13 @@ la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
  *   state_in    [B,H,d_k,d_v] float32 initial state, NULL = zero.
  *   z_in        [B,H,d_k] float32 initial normalizer (LA_NORMALIZED only),
  *               NULL = zero. Must be NULL for the other variants.
- *   o           [B,H,L,d_v] output (dtype dt), required; must not overlap any
- *               input.
+ *   o           [B,H,L,d_v] output (dtype o_dt), required when L > 0; must not
+ *               overlap any input or other output.
  *   state_out   [B,H,d_k,d_v] float32 final state, NULL = not written. May be
  *               equal to state_in (in-place carry); must not partially overlap it.
  *   z_out       [B,H,d_k] float32 final normalizer (LA_NORMALIZED only), NULL =
- *               not written.
+ *               not written; must not overlap z_in (every value slice of a head
+ *               reads z_in while one of them writes z_out).
  *   B, H, L     batch, heads, tokens: B, H >= 1; L >= 0 (L = 0 only copies
  *               state_in/z_in, or zeros, to state_out/z_out).
  *   d_k         32, 64 or 128.   d_v  32, 64, 96 or 128 (a multiple of 32).
@@ -114,11 +123,11 @@ la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
  *   workspace   device buffer of at least la_chunk_fwd_workspace_size() bytes
  *               (may be NULL when that size is 0), 256-byte aligned.
  */
-la_status la_chunk_fwd(la_variant var, la_dtype dt, const void *q, const void *k,
-                       const void *v, const float *log_gate, const float *beta,
-                       const float *state_in, const float *z_in, void *o,
-                       float *state_out, float *z_out, int B, int H, int L, int d_k,
-                       int d_v, int C, void *workspace, size_t workspace_bytes,
+la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q,
+                       const void *k, const void *v, const float *log_gate,
+                       const float *beta, const float *state_in, const float *z_in,
+                       void *o, float *state_out, float *z_out, int B, int H, int L,
+                       int d_k, int d_v, int C, void *workspace, size_t workspace_bytes,
                        void *stream);
 
 /*
@@ -126,15 +135,16 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, const void *q, const void *k
  * place: S <- exp(l) S + k v^T (LA_DECAY) or S <- S + k v^T (LA_PLAIN, log_gate
  * NULL), then o = S^T q with the updated S (tensorplay section 2.1-2.2; wln20
  * decay equation).
- *   q, k [N,H,d_k], v [N,H,d_v], o [N,H,d_v] in dtype dt; log_gate [N,H] float32;
+ *   q, k [N,H,d_k], v [N,H,d_v] in dtype dt; o [N,H,d_v] in dtype o_dt (the
+ *   step itself is computed in fp32); log_gate [N,H] float32;
  *   beta must be NULL (reserved for the delta-rule step); state [N,H,d_k,d_v]
  *   float32, read and written in place. o must not overlap the state or inputs.
  *   N, H >= 1; d_k, d_v in {32, 64, 128}.
  */
-la_status la_decode_step(la_variant var, la_dtype dt, const void *q, const void *k,
-                         const void *v, const float *log_gate, const float *beta,
-                         float *state, void *o, int N, int H, int d_k, int d_v,
-                         void *stream);
+la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void *q,
+                         const void *k, const void *v, const float *log_gate,
+                         const float *beta, float *state, void *o, int N, int H, int d_k,
+                         int d_v, void *stream);
 
 /* Static string naming a status code. */
 const char *la_status_str(la_status s);

@@ -37,10 +37,10 @@ def test_version_and_status_strings():
     assert la.la_status_str(3) == "LA_ERR_HIP"
 
 
-def chunk(var=PLAIN, dt=BF16, q=FAKE, k=FAKE, v=FAKE, lg=None, beta=None, s_in=None, z_in=None,
+def chunk(var=PLAIN, dt=BF16, odt=F32, q=FAKE, k=FAKE, v=FAKE, lg=None, beta=None, s_in=None, z_in=None,
           o=0x800000000, s_out=None, z_out=None, B=1, H=1, L=128, dk=64, dv=64, C=64, ws=None,
           ws_bytes=0):
-    return la.load_library().la_chunk_fwd(var, dt, q, k, v, lg, beta, s_in, z_in, o, s_out, z_out,
+    return la.load_library().la_chunk_fwd(var, dt, odt, q, k, v, lg, beta, s_in, z_in, o, s_out, z_out,
                                           B, H, L, dk, dv, C, ws, ws_bytes, None)
 
 
@@ -64,7 +64,8 @@ def test_workspace_sizes():
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(var=7), INVALID), (dict(dt=5), INVALID),
+    (dict(var=7), INVALID), (dict(dt=5), INVALID), (dict(odt=5), INVALID),
+    (dict(dt=F32, odt=BF16), UNSUPPORTED),
     (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(L=-3), INVALID),
     (dict(dk=48), UNSUPPORTED), (dict(dk=256), UNSUPPORTED),
     (dict(dv=48), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
@@ -86,13 +87,14 @@ def test_chunk_fwd_rejects(kw, expect):
     assert chunk(**kw) == expect
 
 
-def dec(var=DECAY, dt=BF16, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, lg=FAKE + 0x3000, beta=None,
+def dec(var=DECAY, dt=BF16, odt=F32, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, lg=FAKE + 0x3000, beta=None,
         S=0x900000000, o=0x800000000, N=4, H=2, dk=128, dv=128):
-    return la.load_library().la_decode_step(var, dt, q, k, v, lg, beta, S, o, N, H, dk, dv, None)
+    return la.load_library().la_decode_step(var, dt, odt, q, k, v, lg, beta, S, o, N, H, dk, dv, None)
 
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(var=9), INVALID), (dict(var=NORM), UNSUPPORTED), (dict(var=GDN), UNSUPPORTED),
+    (dict(odt=7), INVALID), (dict(dt=F32, odt=BF16), UNSUPPORTED),
     (dict(N=0), INVALID), (dict(dk=96), UNSUPPORTED), (dict(dv=16), UNSUPPORTED),
     (dict(q=None), INVALID), (dict(S=None), INVALID), (dict(lg=None), INVALID),
     (dict(var=PLAIN), INVALID),                       # plain step takes no gate

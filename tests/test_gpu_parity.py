@@ -194,3 +194,26 @@ def test_prefill_then_decode():
     ro, rs, _ = oracle_chunk(inp, state_in=False)
     assert_close(host64(o), ro[:, :, L], TOL["bf16"], "o")
     assert_close(host64(S), rs, TOL["bf16"], "state")
+
+
+@pytest.mark.parametrize("var", ["plain", "normalized", "decay", "gated_delta"])
+@pytest.mark.parametrize("C", [64, 128])
+def test_bf16_output(var, C):
+    """o_dt = bf16: the same kernels, with the output rounded to nearest even.
+    Bound: the fp32-output tolerance plus bf16's rounding of each value
+    (|err| <= 2e-2 RMS + 2^-8 |o|)."""
+    if var == "gated_delta" and C != 64:
+        pytest.skip("the delta rule is built for C = 64")
+    inp = W.make_chunk_inputs(var, "bf16", 2, 2, 2 * C + 9, 128, 64, seed=12)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    o, _, _ = la.la_chunk_fwd(var, q, k, v, dev(inp.log_gate), dev(inp.beta), C=C,
+                              out_dtype=torch.bfloat16)
+    o32, _, _ = la.la_chunk_fwd(var, q, k, v, dev(inp.log_gate), dev(inp.beta), C=C)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    ro, _, _ = oracle_chunk(inp, state_in=False)
+    got = host64(o)
+    rms = float(np.sqrt(np.mean(ro ** 2)))
+    assert np.all(np.abs(got - ro) <= TOL["bf16"] * rms + 2.0 ** -8 * np.abs(ro))
+    # bf16 output is the RNE rounding of the fp32 output of the same kernel
+    assert torch.equal(o, o32.to(torch.bfloat16))
