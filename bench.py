@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Throughput of the chunkwise causal linear-attention path on one MI355X.
+
+A step is one call of the hot path over one batch of synthetic input that is
+already resident in HBM:
+  - chunk workloads: one la_chunk_fwd (C = 64, fp32 output and final state);
+  - decode workload: 100 back-to-back la_decode_step calls (one "step" = 100
+    tokens per sequence-head, as the workload is quoted).
+The headline workload (the JSON line's value) is the normalized kernel linear
+attention at B=8, H=16, L=2048, d=64; --all (default) also times the four other
+workloads and reports them under "workloads". Every workload is timed with HIP
+events on the stream the kernels run on, over K timed steps after W warm-up steps.
+Working sets below twice the 256 MB Infinity Cache are rotated over several
+input copies so that the timed steps read HBM, not the cache.
+
+Roofline: the algorithmic bytes and flops of one step (inputs read once, outputs
+written once; flop counts of the chunkwise method, no credit for masking) divided
+by the measured time, against 8 TB/s HBM and 2.517 PFLOP/s dense fp16/bf16 MFMA.
+`traffic` is filled from profiles/traffic.json when its recorded kernel-source
+hash matches the current sources, else null.
+
+The CPU baseline times the fp64 oracle (tests' reference implementation) over the
+whole headline workload on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--only] [--no-cpu-baseline] [--copy-calibration BYTES]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HEADLINE = "normalized_bf16_b8h16_l2048_d64"
+METRIC = "tokens/sec + % bf16 MFMA peak (chunk fwd); decode state GB/s % of HBM peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2517.0     # 256 CU x 4096 flop/clk x 2.4 GHz, dense fp16/bf16
+CACHE_BYTES = 256 * 2 ** 20   # Infinity Cache (MALL)
+KERNEL_SOURCES = ("chunk_fwd_impl.hpp", "gdn_prep_impl.hpp", "decode_impl.hpp", "la_common.hpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "chunkwise_linear_rnn_causal_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per step (chunkwise method; see the design doc for the derivation)
+# ---------------------------------------------------------------------------
+def chunk_work(c: dict) -> tuple[float, float]:
+    """(flop, bytes) of one chunk forward over the workload, fp32 output + state."""
+    B, H, L, dk, dv, C = c["B"], c["H"], c["L"], c["dk"], c["dv"], c["C"]
+    BH = B * H
+    esz = 2 if c["dtype"] == "bf16" else 4
+    if c["variant"] == "gated_delta":
+        per_tok = (2 * C * C * (3 * dk + 2 * dv) + 6 * C * dk * dv + C ** 3 / 3) / C
+    else:
+        per_tok = 2 * C * (dk + dv) + 4 * dk * dv
+    flop = per_tok * BH * L
+    nbytes = BH * L * ((2 * dk + dv) * esz + dv * 4)           # q, k, v in; o out (fp32)
+    if c["variant"] in ("decay", "gated_delta"):
+        nbytes += BH * L * 4                                     # log-gates
+    if c["variant"] == "gated_delta":
+        nbytes += BH * L * 4                                     # beta
+    nbytes += BH * dk * dv * 4                                   # final state
+    return flop, nbytes
+
+
+def decode_work(c: dict) -> tuple[float, float]:
+    """(flop, bytes) of ONE decode step over all sequence-heads."""
+    NH, dk, dv = c["N"] * c["H"], c["dk"], c["dv"]
+    flop = 5.0 * dk * dv * NH                                    # gamma*S + k v^T, then S^T q
+    nbytes = NH * (2 * dk * dv * 4 + (2 * dk + dv) * 2 + 4 + dv * 4)
+    return flop, nbytes
+
+
+# ---------------------------------------------------------------------------
+def to_dev(x, device):
+    import torch
+    if x is None:
+        return None
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def time_steps(fn, steps: int, warmup: int, stream):
+    """Run fn(i) warmup + steps times; return (wall seconds, per-step event ms list)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        fn(warmup + i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in evs]
+
+
+def bench_chunk(name: str, steps: int, warmup: int, device) -> dict:
+    import torch
+    import chunkwise_linear_rnn_causal_amd as la
+    c = W.CONFIGS[name]
+    inp = W.config_chunk_inputs(name, seed=0)
+    flop, nbytes = chunk_work(c)
+    copies = max(1, min(4, math.ceil(2 * CACHE_BYTES / nbytes)))
+    sets = []
+    for _ in range(copies):
+        s = dict(q=to_dev(inp.q, device), k=to_dev(inp.k, device), v=to_dev(inp.v, device),
+                 lg=to_dev(inp.log_gate, device), beta=to_dev(inp.beta, device))
+        s["o"] = torch.empty((c["B"], c["H"], c["L"], c["dv"]), dtype=torch.float32, device=device)
+        s["S"] = torch.empty((c["B"], c["H"], c["dk"], c["dv"]), dtype=torch.float32, device=device)
+        dt = 1 if c["dtype"] == "bf16" else 0
+        wsb = la.la_chunk_fwd_workspace_size(c["variant"], dt, c["B"], c["H"], c["L"], c["dk"], c["dv"], c["C"])
+        s["ws"] = torch.empty(max(wsb, 1), dtype=torch.uint8, device=device) if wsb else None
+        sets.append(s)
+    stream = torch.cuda.current_stream(device)
+
+    def step(i):
+        s = sets[i % copies]
+        la.la_chunk_fwd(c["variant"], s["q"], s["k"], s["v"], s["lg"], s["beta"], C=c["C"],
+                        o=s["o"], state_out=s["S"], workspace=s["ws"], stream=stream)
+
+    wall, ms = time_steps(step, steps, warmup, stream)
+    t = float(np.mean(ms)) / 1e3
+    toks = c["B"] * c["L"]
+    return dict(workload=name, variant=c["variant"], tokens_per_s=toks / t, ms_per_step=t * 1e3,
+                wall_ms_per_step=wall / steps * 1e3, flop=flop, bytes=nbytes,
+                achieved_gbs=nbytes / t / 1e9, achieved_tflops=flop / t / 1e12,
+                hbm_frac=nbytes / t / 1e9 / HBM_PEAK_GBS, mfma_frac=flop / t / 1e12 / MFMA_PEAK_TFLOPS,
+                roofline_frac=max(nbytes / (HBM_PEAK_GBS * 1e9), flop / (MFMA_PEAK_TFLOPS * 1e12)) / t,
+                input_copies=copies, B=c["B"], H=c["H"], L=c["L"], d_k=c["dk"], d_v=c["dv"], C=c["C"])
+
+
+def bench_decode(name: str, steps: int, warmup: int, device) -> dict:
+    import torch
+    import chunkwise_linear_rnn_causal_amd as la
+    c = W.CONFIGS[name]
+    N, H, dk, dv, nsteps = c["N"], c["H"], c["dk"], c["dv"], c["steps"]
+    S = to_dev(W.make_decode_state(N, H, dk, dv, seed=0), device)
+    with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+        host = list(ex.map(lambda i: W.make_decode_step(N, H, dk, dv, step=i, seed=0), range(nsteps)))
+    ins = [(to_dev(h.q, device), to_dev(h.k, device), to_dev(h.v, device), to_dev(h.log_gate, device))
+           for h in host]
+    o = torch.empty((N, H, dv), dtype=torch.float32, device=device)
+    flop1, bytes1 = decode_work(c)
+    stream = torch.cuda.current_stream(device)
+
+    def step(_):
+        for (q, k, v, lg) in ins:
+            la.la_decode_step("decay", q, k, v, lg, S, o=o, stream=stream)
+
+    wall, ms = time_steps(step, steps, warmup, stream)
+    t = float(np.mean(ms)) / 1e3            # one step = nsteps decode launches
+    t1 = t / nsteps
+    # tokens: one new token per sequence per decode launch (all H heads of it)
+    return dict(workload=name, variant="decay_decode", tokens_per_s=N * nsteps / t,
+                ms_per_step=t * 1e3, ms_per_decode_launch=t1 * 1e3,
+                wall_ms_per_step=wall / steps * 1e3, flop=flop1 * nsteps, bytes=bytes1 * nsteps,
+                achieved_gbs=bytes1 / t1 / 1e9, achieved_tflops=flop1 / t1 / 1e12,
+                hbm_frac=bytes1 / t1 / 1e9 / HBM_PEAK_GBS, mfma_frac=None,
+                roofline_frac=bytes1 / (HBM_PEAK_GBS * 1e9) / t1,
+                N=N, H=H, d_k=dk, d_v=dv, decode_launches_per_step=nsteps)
+
+
+def cpu_baseline(name: str, min_seconds: float = 3.0) -> dict:
+    """Time the fp64 oracle over the whole workload on the host cores."""
+    import oracle
+    c = W.CONFIGS[name]
+    inp = W.config_chunk_inputs(name, seed=0)
+    args = [inp.f64(x) for x in ("q", "k", "v")]
+    kw = dict(log_gate=inp.f64("log_gate"), beta=inp.f64("beta"))
+    cores = min(16, len(os.sched_getaffinity(0)))
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(c["variant"], *args, threads=cores, **kw)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    toks = c["B"] * c["L"] * passes
+    return dict(value=toks / el, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"whole workload ({c['B'] * c['H']} batch-heads x {c['L']} tokens), "
+                       f"{passes} passes, {el:.1f} s wall, fp64 per-token recurrence")
+
+
+def traffic_for(workload: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("workloads", {}).get(workload, {}).get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes: int) -> None:
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE /
+    WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": 3}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(W.CONFIGS))
+    ap.add_argument("--only", action="store_true", help="time only --workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(independent batch-heads shard across GPUs with no exchange; see DESIGN.md).",
+              file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return 0
+
+    import torch
+    import chunkwise_linear_rnn_causal_amd as la
+    la.load_library()
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+
+    names = [args.workload] if args.only else [args.workload] + [n for n in W.CONFIGS if n != args.workload]
+    results = {}
+    for name in names:
+        kind = W.CONFIGS[name]["kind"]
+        print(f"[bench] {name}", file=sys.stderr, flush=True)
+        steps = args.steps if kind == "chunk" else max(1, min(args.steps, 5))
+        warm = args.warmup if kind == "chunk" else max(1, min(args.warmup, 2))
+        results[name] = (bench_chunk if kind == "chunk" else bench_decode)(name, steps, warm, device)
+        r = results[name]
+        print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['achieved_gbs']:.0f} GB/s, "
+              f"{r['achieved_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+
+    head = results[args.workload]
+    c = W.CONFIGS[args.workload]
+    bound = "hbm" if head["bytes"] / HBM_PEAK_GBS >= head["flop"] / 1e3 / MFMA_PEAK_TFLOPS else "mfma"
+    if bound == "hbm":
+        roof = dict(bound="hbm", achieved=head["achieved_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=head["achieved_gbs"] / HBM_PEAK_GBS)
+    else:
+        roof = dict(bound="mfma", achieved=head["achieved_tflops"], peak=MFMA_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=head["achieved_tflops"] / MFMA_PEAK_TFLOPS)
+    roof["traffic"] = traffic_for(args.workload)
+
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "variant": c.get("variant"), "B": c.get("B"),
+                   "H": c.get("H"), "L": c.get("L"), "d_k": c["dk"], "d_v": c["dv"], "C": c.get("C"),
+                   "inputs": c["dtype"], "mfma_operands": "f16" if c["dtype"] == "bf16" else "f32",
+                   "accumulate": "f32", "output": "f32", "parallelism": "single-gpu"},
+        "roofline": roof,
+        "mfma": {"achieved": head["achieved_tflops"], "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": head["mfma_frac"]},
+        "kernel_source_hash": kernel_source_hash(),
+        "workloads": {n: {k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()}
+                      for n, r in results.items() if n != args.workload},
+    }
+    if not args.no_cpu_baseline and c["kind"] == "chunk":
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

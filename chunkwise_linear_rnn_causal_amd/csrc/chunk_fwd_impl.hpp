@@ -16,9 +16,11 @@
 // accumulators for the whole sequence (nothing but Q, K, V, gates and O crosses
 // HBM). Value slices of one head are placed on one XCD so Q and K are shared
 // through that XCD's L2. Per chunk:
-//   1. K staged to LDS row-major (score operand) and transposed + scaled by
-//      exp(g_C - G_s) (state-update operand); V transposed; S_prev written to LDS
-//      transposed in the operand type.
+//   1. Q and K staged to LDS row-major (score / inter operands), K also
+//      transposed + scaled by exp(g_C - G_s) (state-update operand), V
+//      transposed; S_prev written to LDS transposed in the operand type. The
+//      global loads of chunk c+1 are issued right after chunk c is staged, into
+//      registers, so their latency hides behind chunk c's math.
 //   2. Wave w owns query rows 16w..16w+15 (and the mirrored block for C = 128).
 //      It computes the inter term (S^T Q^T on MFMA), the score tiles
 //      K_sb Q_rb^T for sb <= rb, masks/decays/rounds them in registers and feeds
@@ -29,6 +31,8 @@
 //      stores four consecutive output columns.
 //   3. S <- exp(g_C) S + K~^T V on MFMA into the accumulators.
 #pragma once
+
+#include <type_traits>
 
 #include "la_common.hpp"
 #include "la_kernels.hpp"
@@ -45,7 +49,7 @@ struct ChunkCfg {
     static constexpr int PAD = 16 / (int)sizeof(TM);
     static constexpr int KP = DK + PAD;  // row pitch of Ks / STs (elements)
     static constexpr size_t lds_bytes =
-        sizeof(TM) * ((size_t)C * KP + (size_t)DK * C + (size_t)DVT * C + (size_t)DVT * KP) +
+        sizeof(TM) * (2 * (size_t)C * KP + (size_t)DK * C + (size_t)DVT * C + (size_t)DVT * KP) +
         sizeof(float) * (C + (VAR == V_NORM ? 2 * DK : 1));
 };
 
@@ -68,9 +72,18 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
     constexpr int NKS = DK / (4 * E);    // k-steps over channels
     constexpr int NTK = C / (4 * E);     // k-steps over tokens
     constexpr int PER = C / 64;          // tokens per lane in the gate scan
+    constexpr int NQR = DK / 32;         // 8-element runs of one lane's channels (DK/4)
+    // K / V staging units of 4 tokens x 8 channels
+    constexpr int KCB = DK / 8, KCBL = KCB < 4 ? KCB : 4, KTQL = 16 / KCBL, KNCBG = KCB / KCBL;
+    constexpr int KUNITS = (C / 4) * KCB, NUK = (KUNITS + 255) / 256;
+    constexpr int VCB = DVT / 8, VCBL = VCB < 4 ? VCB : 4, VTQL = 16 / VCBL, VNCBG = VCB / VCBL;
+    constexpr int VUNITS = (C / 4) * VCB, NUV = (VUNITS + 255) / 256;
     static_assert(NRB % NW == 0 && (RBW == 1 || RBW == 2), "C must be 64 or 128");
     static_assert(DVT % 16 == 0 && DK % 32 == 0, "tile sizes");
+    static_assert(KUNITS % 64 == 0, "K staging must be wave-uniform (it shuffles gates)");
+    static_assert(VAR != V_GDN || NRB == NW, "one U row block per wave");
 
+    __shared__ __attribute__((aligned(16))) TM Qs[C * KP];
     __shared__ __attribute__((aligned(16))) TM Ks[C * KP];
     __shared__ __attribute__((aligned(16))) TM KTs[DK * C];
     __shared__ __attribute__((aligned(16))) TM VTs[DVT * C];
@@ -110,11 +123,85 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
     if constexpr (VAR == V_NORM) {
         for (int i = tid; i < DK; i += 256) Zs[i] = a.z_in ? a.z_in[(size_t)bh * DK + i] : 0.f;
     }
+    // Settle the prologue's loads here, so that no load is pending at the loop
+    // head and the per-chunk waits can be exact (leaving output stores in flight).
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // ---- registers of the next chunk, loaded one chunk ahead so that global
+    // latency overlaps the current chunk's math. Loads are unconditional from
+    // clamped (always valid) rows; rows past L are zeroed when the registers are
+    // consumed, so no load waits on a branch.
+    Raw8<TI> kpre[NUK][4];
+    Raw8<TI> qpre[NUK][4];
+    Raw8<TI> vpre[NUV][4];
+    float gpre[PER];
+    Raw8<TM> wpre[NQR];           // gated delta: W row of this wave's U row block
+    f32x4 upre[NTJ];              // gated delta: U~ of this wave's U row block
+
+    // Every memory operation of a full chunk is unconditional (threads without a
+    // staging unit load a duplicate address), so the compiler's wait counts stay
+    // exact; only the ragged last chunk clamps rows.
+    const float *gsrc = lgg ? lgg : reinterpret_cast<const float *>(qg);
+    auto load_chunk = [&](int c, auto ragged_tag) {
+        constexpr bool RAGGED = decltype(ragged_tag)::value;
+        const int t0 = c * C;
+        auto row = [&](int t) { return RAGGED ? min(t, L - 1) : t; };
+#pragma unroll
+        for (int i = 0; i < NUK; ++i) {
+            const int u = (tid + 256 * i) % KUNITS;
+            const int gi = u >> 4, l16 = u & 15;
+            const int tq = (gi / KNCBG) * KTQL + (l16 % KTQL);
+            const int cb = (gi % KNCBG) * KCBL + (l16 / KTQL);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = row(t0 + 4 * tq + r);
+                kpre[i][r] = ld_raw8<TI>(kg + (size_t)t * DK + 8 * cb);
+                qpre[i][r] = ld_raw8<TI>(qg + (size_t)t * DK + 8 * cb);
+            }
+        }
+        if constexpr (VAR != V_GDN) {
+#pragma unroll
+            for (int i = 0; i < NUV; ++i) {
+                const int u = (tid + 256 * i) % VUNITS;
+                const int gi = u >> 4, l16 = u & 15;
+                const int tq = (gi / VNCBG) * VTQL + (l16 % VTQL);
+                const int cb = (gi % VNCBG) * VCBL + (l16 / VTQL);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = row(t0 + 4 * tq + r);
+                    vpre[i][r] = ld_raw8<TI>(vg + (size_t)t * dv + 8 * cb);
+                }
+            }
+        }
+        if constexpr (DECAYED) {
+#pragma unroll
+            for (int p = 0; p < PER; ++p) gpre[p] = gsrc[row(t0 + lane * PER + p)];
+        }
+        if constexpr (VAR == V_GDN) {
+            const int srow = t0 + wv * 16 + n;  // W and U~ have Lp rows: always in range
+#pragma unroll
+            for (int i = 0; i < NQR; ++i) wpre[i] = ld_raw8<TM>(wg + (size_t)srow * DK + g * (DK / 4) + 8 * i);
+#pragma unroll
+            for (int tj = 0; tj < NTJ; ++tj)
+                upre[tj] = ld4<TM>(utg + (size_t)(tj * 16 + n) * a.Lp + t0 + wv * 16 + 4 * g);
+        }
+    };
 
     const int nchunks = (L + C - 1) / C;
-    for (int c = 0; c < nchunks; ++c) {
+    const int nfull = L / C;  // chunks with all C rows valid
+    const std::true_type ragged_t{};
+    const std::false_type full_t{};
+    using NextNone = std::integral_constant<int, 0>;
+    using NextFull = std::integral_constant<int, 1>;
+    using NextTail = std::integral_constant<int, 2>;  // ragged next chunk if L % C != 0
+
+    // One chunk. ragged_tag: this chunk has rows past L. next_tag: which loads to
+    // issue for chunk c + 1.
+    auto chunk_body = [&](int c, auto ragged_tag, auto next_tag) {
+        constexpr bool RAGGED = decltype(ragged_tag)::value;
+        constexpr int NEXT = decltype(next_tag)::value;
         const int t0 = c * C;
-        __syncthreads();  // previous chunk is done with every LDS tile
+        __syncthreads();  // the previous chunk is done with every LDS tile
 
         // S_prev, transposed, in the operand type: STs[j][i].
 #pragma unroll
@@ -133,8 +220,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
             float run = 0.f;
 #pragma unroll
             for (int p = 0; p < PER; ++p) {
-                const int t = t0 + lane * PER + p;
-                run += (lgg && t < L) ? lgg[t] : 0.f;
+                run += (lgg && (!RAGGED || t0 + lane * PER + p < L)) ? gpre[p] : 0.f;
                 gl[p] = run;
             }
             float incl = run;
@@ -153,43 +239,43 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
                 for (int p = 0; p < PER; ++p) Gs[lane * PER + p] = gl[p];
             }
         }
-        auto G_of = [&](int s) -> float {
-            if constexpr (PER == 1) {
-                return __shfl(gl[0], s, 64);
-            } else {
-                const float x0 = __shfl(gl[0], s >> 1, 64);
-                const float x1 = __shfl(gl[1], s >> 1, 64);
-                return (s & 1) ? x1 : x0;
-            }
-        };
 
-        // ---- stage K: units of 4 tokens x 8 channels. In each 16-lane group,
-        // lanes with equal channel block own consecutive token quads, so the
-        // transposed writes of a group cover one 128-byte bank window.
-        {
-            constexpr int CB = DK / 8, CBL = CB < 4 ? CB : 4, TQL = 16 / CBL, NCBG = CB / CBL;
-            constexpr int UNITS = (C / 4) * CB;
-            static_assert(UNITS % 64 == 0, "wave-uniform staging loop");
-            for (int u = tid; u < UNITS; u += 256) {
+        // ---- stage K row-major and transposed (scaled by exp(g_C - G_s)).
+#pragma unroll
+        for (int i = 0; i < NUK; ++i) {
+            const int u = tid + 256 * i;
+            if (KUNITS % 256 == 0 || u < KUNITS) {
                 const int gi = u >> 4, l16 = u & 15;
-                const int tq = (gi / NCBG) * TQL + (l16 % TQL);
-                const int cb = (gi % NCBG) * CBL + (l16 / TQL);
+                const int tq = (gi / KNCBG) * KTQL + (l16 % KTQL);
+                const int cb = (gi % KNCBG) * KCBL + (l16 / KTQL);
                 float x[4][8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = t0 + 4 * tq + r;
-                    if (t < L) {
-                        ld8<TI>(kg + (size_t)t * DK + 8 * cb, x[r]);
-                    } else {
+                    const bool valid = !RAGGED || t0 + 4 * tq + r < L;
+                    float y[8];
+                    unpack8<TI>(qpre[i][r], y);
+                    unpack8<TI>(kpre[i][r], x[r]);
+                    if (!valid) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
+                        for (int e = 0; e < 8; ++e) x[r][e] = y[e] = 0.f;
                     }
+                    st8<TM>(&Qs[(4 * tq + r) * KP + 8 * cb], y);
                     st8<TM>(&Ks[(4 * tq + r) * KP + 8 * cb], x[r]);
                 }
                 float wsc[4] = {1.f, 1.f, 1.f, 1.f};
                 if constexpr (DECAYED) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) wsc[r] = __expf(gC - G_of(4 * tq + r));
+                    for (int r = 0; r < 4; ++r) {
+                        const int s = 4 * tq + r;
+                        float Gsv;
+                        if constexpr (PER == 1) {
+                            Gsv = __shfl(gl[0], s, 64);
+                        } else {
+                            const float x0 = __shfl(gl[0], s >> 1, 64), x1 = __shfl(gl[1], s >> 1, 64);
+                            Gsv = (s & 1) ? x1 : x0;
+                        }
+                        wsc[r] = __expf(gC - Gsv);
+                    }
                 }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -200,59 +286,89 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
         }
         // ---- stage V (transposed) for the value slice.
         if constexpr (VAR != V_GDN) {
-            constexpr int CB = DVT / 8, CBL = CB < 4 ? CB : 4, TQL = 16 / CBL, NCBG = CB / CBL;
-            constexpr int UNITS = (C / 4) * CB;
-            static_assert(UNITS % 64 == 0, "wave-uniform staging loop");
-            for (int u = tid; u < UNITS; u += 256) {
-                const int gi = u >> 4, l16 = u & 15;
-                const int tq = (gi / NCBG) * TQL + (l16 % TQL);
-                const int cb = (gi % NCBG) * CBL + (l16 / TQL);
-                float x[4][8];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = t0 + 4 * tq + r;
-                    if (t < L) {
-                        ld8<TI>(vg + (size_t)t * dv + 8 * cb, x[r]);
-                    } else {
+            for (int i = 0; i < NUV; ++i) {
+                const int u = tid + 256 * i;
+                if (VUNITS % 256 == 0 || u < VUNITS) {
+                    const int gi = u >> 4, l16 = u & 15;
+                    const int tq = (gi / VNCBG) * VTQL + (l16 % VTQL);
+                    const int cb = (gi % VNCBG) * VCBL + (l16 / VTQL);
+                    float x[4][8];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
+                    for (int r = 0; r < 4; ++r) {
+                        unpack8<TI>(vpre[i][r], x[r]);
+                        if (RAGGED && t0 + 4 * tq + r >= L) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
+                        }
                     }
-                }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    f32x4 col = {x[0][e], x[1][e], x[2][e], x[3][e]};
-                    st4<TM>(&VTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+                    for (int e = 0; e < 8; ++e) {
+                        f32x4 col = {x[0][e], x[1][e], x[2][e], x[3][e]};
+                        st4<TM>(&VTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+                    }
                 }
             }
         }
+
+        // Delta rule: this chunk's W row and U~ as operands (the prefetch
+        // registers are refilled right after the barrier).
+        frag wf[VAR == V_GDN ? NKS : 1];
+        f32x4 ucur[VAR == V_GDN ? NTJ : 1];
+        if constexpr (VAR == V_GDN) {
+#pragma unroll
+            for (int i = 0; i < NQR; ++i) {
+                if constexpr (E == 8) {
+                    wf[i] = neg_frag<TM>(*reinterpret_cast<const frag *>(&wpre[i].v[0]));
+                } else {
+                    float x[8];
+                    unpack8<TM>(wpre[i], x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) wf[8 * i + e] = -x[e];
+                }
+            }
+#pragma unroll
+            for (int tj = 0; tj < NTJ; ++tj) ucur[tj] = upre[tj];
+        }
         __syncthreads();  // staged tiles, STs and Gs visible
 
-        // ---- gated delta rule: U = U~ - W S_prev, written transposed into VTs.
+        if constexpr (NEXT == 1) {
+            load_chunk(c + 1, full_t);
+        } else if constexpr (NEXT == 2) {
+            if (c + 1 < nchunks) load_chunk(c + 1, ragged_t);
+        }
+        // Keep the prefetch here: the scheduler would otherwise sink the loads
+        // towards their use in the next chunk and expose their latency.
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- gated delta rule: U = U~ - W S_prev for this wave's 16 rows,
+        // written transposed into VTs. D[s][j]: lane (g, n) holds s = wv*16 + 4g + e.
         if constexpr (VAR == V_GDN) {
-            constexpr int NU = (C / 16) * NTJ;
-            for (int u = wv; u < NU; u += NW) {
-                const int sbk = u / NTJ, tj = u % NTJ;
-                const int jj = tj * 16 + n;
-                // D[s][j] tile: lane (g, n) holds s = sbk*16 + 4g + e, j = jj.
-                f32x4 acc = ld4<TM>(utg + (size_t)jj * a.Lp + t0 + sbk * 16 + 4 * g);
-                const TM *wrow = wg + (size_t)(t0 + sbk * 16 + n) * DK + g * (DK / 4);
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const frag wa = neg_frag<TM>(ld_frag<TM>(wrow + ks * E));
-                    const frag sb = ld_frag<TM>(&STs[jj * KP + g * (DK / 4) + ks * E]);
-                    acc = MF::mma(wa, sb, acc);
-                }
-                st4<TM>(&VTs[tidx<C>(jj, sbk * 16 + 4 * g)], acc);
+            for (int tj = 0; tj < NTJ; ++tj) {
+                const int jj = tj * 16 + n;
+                f32x4 acc = ucur[tj];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    acc = MF::mma(wf[ks], ld_frag<TM>(&STs[jj * KP + g * (DK / 4) + ks * E]), acc);
+                st4<TM>(&VTs[tidx<C>(jj, wv * 16 + 4 * g)], acc);
             }
             __syncthreads();
         }
 
-        // ---- normalizer carry: z_next = z_prev + sum_s k_s (fp32).
+        // ---- normalizer carry: z_next = z_prev + sum_s k_s (fp32), from the
+        // transposed K tile (unscaled for this variant).
         const int zc = (c & 1) * DK, zn = ((c + 1) & 1) * DK;
         if constexpr (VAR == V_NORM) {
             for (int i = tid; i < DK; i += 256) {
                 float sacc = 0.f;
-                for (int s = 0; s < C; ++s) sacc += to_f32<TM>(Ks[s * KP + i]);
+#pragma unroll
+                for (int s0 = 0; s0 < C; s0 += 8) {
+                    float x[8];
+                    ld8<TM>(&KTs[tidx<C>(i, s0)], x);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sacc += x[e];
+                }
                 Zs[zn + i] = Zs[zc + i] + sacc;
             }
         }
@@ -263,12 +379,10 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
             const int rb = (rr == 0) ? wv : (NRB - 1 - wv);
             const int rl = rb * 16 + n;   // chunk-local query row of this lane
             const int rrow = t0 + rl;
+            const float Gr = DECAYED ? Gs[rl] : 0.f;
             frag qf[NKS];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                qf[ks] = (rrow < L) ? ld_frag_as<TI, TM>(qg + (size_t)rrow * DK + g * (DK / 4) + ks * E)
-                                    : zero_frag<TM>();
-            const float Gr = DECAYED ? Gs[rl] : 0.f;
+            for (int ks = 0; ks < NKS; ++ks) qf[ks] = ld_frag<TM>(&Qs[rl * KP + g * (DK / 4) + ks * E]);
 
             // inter-chunk term: D[j][r] = sum_i S[i][j] q_r[i]
             f32x4 oacc[NTJ];
@@ -375,7 +489,7 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
                 for (int tj = 0; tj < NTJ; ++tj) oacc[tj] *= inv;
             }
 
-            if (rrow < L) {
+            if (!RAGGED || rrow < L) {
 #pragma unroll
                 for (int tj = 0; tj < NTJ; ++tj) st4<TO>(og + (size_t)rrow * dv + tj * 16 + 4 * g, oacc[tj]);
             }
@@ -400,7 +514,23 @@ __global__ void __launch_bounds__(256) chunk_fwd_kernel(ChunkArgs a) {
                 }
             }
         }
+    };
+
+    // Schedule: the first full chunk is peeled so that both edges into the
+    // steady-state loop leave the same memory operations in flight (the wait
+    // counts inside the loop are then exact and let output stores drain in the
+    // background); the last full chunk prefetches the ragged tail, if any.
+    if (nfull > 0) {
+        load_chunk(0, full_t);
+    } else if (nchunks > 0) {
+        load_chunk(0, ragged_t);
     }
+    if (nfull >= 2) {
+        chunk_body(0, full_t, NextFull{});
+        for (int c = 1; c < nfull - 1; ++c) chunk_body(c, full_t, NextFull{});
+    }
+    if (nfull >= 1) chunk_body(nfull - 1, full_t, NextTail{});
+    if (nfull < nchunks) chunk_body(nfull, ragged_t, NextNone{});
 
     if (a.s_out) {
 #pragma unroll

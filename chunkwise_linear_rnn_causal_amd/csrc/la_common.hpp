@@ -155,6 +155,45 @@ __device__ inline typename Mfma<TM>::frag ld_frag_as(const TI *p) {
     }
 }
 
+// Eight consecutive elements kept in their storage format (16 bytes for 2-byte
+// types, 32 for fp32), so a prefetch holds raw registers until it is staged.
+template <typename T> struct Raw8 { uint4 v[sizeof(T) / 2]; };
+
+template <typename T> __device__ inline Raw8<T> ld_raw8(const T *p) {
+    Raw8<T> r;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.v[i] = reinterpret_cast<const uint4 *>(p)[i];
+    return r;
+}
+template <typename T> __device__ inline Raw8<T> zero_raw8() {
+    Raw8<T> r;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.v[i] = make_uint4(0u, 0u, 0u, 0u);
+    return r;
+}
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <typename T> __device__ inline void unpack8(const Raw8<T> &r, float (&x)[8]);
+template <> __device__ inline void unpack8<bf16>(const Raw8<bf16> &r, float (&x)[8]) {
+    const uint32_t w[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+template <> __device__ inline void unpack8<f16>(const Raw8<f16> &r, float (&x)[8]) {
+    const f16x8 h = *reinterpret_cast<const f16x8 *>(&r.v[0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
+}
+template <> __device__ inline void unpack8<float>(const Raw8<float> &r, float (&x)[8]) {
+    const uint32_t w[8] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w, r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(w[i]);
+}
+
 // Transposed, swizzled [rows][C] tile (token index innermost). Tokens are
 // grouped in 4-element chunks; the chunk index is XORed with a per-row even
 // offset so that transposed 4-token writes from lanes that own rows 8 apart
