@@ -60,12 +60,12 @@ la_status check_chunk_shape(la_variant var, la_dtype dt, int B, int H, int L, in
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || L < 0) return LA_ERR_INVALID_ARG;
     if (d_k != 32 && d_k != 64 && d_k != 128) return LA_ERR_UNSUPPORTED;
-    if (d_v < 32 || d_v > 128 || d_v % kDVT != 0) return LA_ERR_UNSUPPORTED;
+    if (d_v < 32 || d_v > 128 || d_v % 32 != 0) return LA_ERR_UNSUPPORTED;
     if (C != 64 && C != 128) return LA_ERR_UNSUPPORTED;
     if (var == LA_GATED_DELTA && C != 64) return LA_ERR_UNSUPPORTED;
     if (dt == LA_F32 && d_k == 128 && C == 128) return LA_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
-    if (BH * (d_v / kDVT) > INT32_MAX || BH * ((L + C - 1) / C) > INT32_MAX) return LA_ERR_UNSUPPORTED;
+    if (BH * (d_v / 16) > INT32_MAX || BH * ((L + C - 1) / C) > INT32_MAX) return LA_ERR_UNSUPPORTED;
     return LA_OK;
 }
 
@@ -79,31 +79,65 @@ size_t chunk_workspace(la_variant var, la_dtype dt, int B, int H, int L, int d_k
     return gdn_w_bytes(dt, BH, Lp, d_k) + (size_t)BH * Lp * d_v * elem_size(dt);
 }
 
-template <typename TI, typename TO, int DK, int C>
-hipError_t dispatch_chunk_c(la_variant var, const ChunkArgs &a, hipStream_t st) {
+// Workgroup geometry of the chunk kernel: value columns per workgroup (DVT) and
+// waves per workgroup (NW). fp32 inputs and C = 128 use 4 waves over 32 columns.
+// For bf16 inputs and C = 64, 8-wave workgroups (wave pairs share a 16-row block
+// and split its columns) take 64 columns when that still gives at least one
+// workgroup per CU (fewer duplicate Q/K loads), else 32. The delta rule, whose
+// serial pass is the heaviest, falls back to 16-column, 4-wave workgroups when
+// 32-column ones would leave CUs idle.
+struct Geometry {
+    int dvt, nw;
+};
+constexpr int kNumCU = 256;
+
+Geometry choose_geometry(la_variant var, la_dtype dt, int64_t BH, int d_v, int C) {
+    if (dt == LA_F32 || C == 128) return {32, 4};
+    if (var == LA_GATED_DELTA) return (BH * (d_v / 32) >= kNumCU) ? Geometry{32, 8} : Geometry{16, 4};
+    if (d_v % 64 == 0 && BH * (d_v / 64) >= kNumCU) return {64, 8};
+    return {32, 8};
+}
+
+template <typename TI, typename TO, int DK, int DVT, int C, int NW>
+hipError_t launch_var(la_variant var, const ChunkArgs &a, hipStream_t st) {
     switch (var) {
-        case LA_PLAIN: return launch_chunk<V_PLAIN, TI, TO, DK, kDVT, C>(a, st);
-        case LA_NORMALIZED: return launch_chunk<V_NORM, TI, TO, DK, kDVT, C>(a, st);
-        case LA_DECAY: return launch_chunk<V_DECAY, TI, TO, DK, kDVT, C>(a, st);
+        case LA_PLAIN: return launch_chunk<V_PLAIN, TI, TO, DK, DVT, C, NW>(a, st);
+        case LA_NORMALIZED: return launch_chunk<V_NORM, TI, TO, DK, DVT, C, NW>(a, st);
+        case LA_DECAY: return launch_chunk<V_DECAY, TI, TO, DK, DVT, C, NW>(a, st);
         default: break;
     }
     return hipErrorInvalidValue;
 }
 
 template <typename TI, typename TO, int DK>
-hipError_t dispatch_chunk(la_variant var, int C, const ChunkArgs &a, hipStream_t st) {
-    if (var == LA_GATED_DELTA) return launch_chunk<V_GDN, TI, TO, DK, kDVT, 64>(a, st);
-    if (C == 64) return dispatch_chunk_c<TI, TO, DK, 64>(var, a, st);
-    if constexpr (!(sizeof(TI) == 4 && DK == 128)) return dispatch_chunk_c<TI, TO, DK, 128>(var, a, st);
+hipError_t dispatch_chunk(la_variant var, int C, Geometry geo, const ChunkArgs &a, hipStream_t st) {
+    constexpr bool F32 = sizeof(TI) == 4;
+    if (var == LA_GATED_DELTA) {
+        if constexpr (F32) return launch_chunk<V_GDN, TI, TO, DK, 32, 64, 4>(a, st);
+        if constexpr (!F32) {
+            if (geo.dvt == 32) return launch_chunk<V_GDN, TI, TO, DK, 32, 64, 8>(a, st);
+            return launch_chunk<V_GDN, TI, TO, DK, 16, 64, 4>(a, st);
+        }
+    }
+    if (C == 128) {
+        if constexpr (!(F32 && DK == 128)) return launch_var<TI, TO, DK, 32, 128, 4>(var, a, st);
+        return hipErrorInvalidValue;
+    }
+    if constexpr (F32) return launch_var<TI, TO, DK, 32, 64, 4>(var, a, st);
+    if constexpr (!F32) {
+        if (geo.dvt == 64) return launch_var<TI, TO, DK, 64, 64, 8>(var, a, st);
+        return launch_var<TI, TO, DK, 32, 64, 8>(var, a, st);
+    }
     return hipErrorInvalidValue;
 }
 
 template <typename TI, typename TO>
-hipError_t dispatch_chunk_dk(la_variant var, int d_k, int C, const ChunkArgs &a, hipStream_t st) {
+hipError_t dispatch_chunk_dk(la_variant var, int d_k, int C, Geometry geo, const ChunkArgs &a,
+                             hipStream_t st) {
     switch (d_k) {
-        case 32: return dispatch_chunk<TI, TO, 32>(var, C, a, st);
-        case 64: return dispatch_chunk<TI, TO, 64>(var, C, a, st);
-        case 128: return dispatch_chunk<TI, TO, 128>(var, C, a, st);
+        case 32: return dispatch_chunk<TI, TO, 32>(var, C, geo, a, st);
+        case 64: return dispatch_chunk<TI, TO, 64>(var, C, geo, a, st);
+        case 128: return dispatch_chunk<TI, TO, 128>(var, C, geo, a, st);
     }
     return hipErrorInvalidValue;
 }
@@ -226,7 +260,8 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
     ChunkArgs a{};
     a.q = q; a.k = k; a.v = v; a.lg = log_gate;
     a.s_in = state_in; a.z_in = z_in; a.o = o; a.s_out = state_out; a.z_out = z_out;
-    a.BH = (int)BH; a.L = L; a.Lp = Lp; a.dv = d_v; a.nsplit = d_v / kDVT;
+    const Geometry geo = choose_geometry(var, dt, BH, d_v, C);
+    a.BH = (int)BH; a.L = L; a.Lp = Lp; a.dv = d_v; a.nsplit = d_v / geo.dvt;
 
     if (var == LA_GATED_DELTA && has_tokens) {
         char *ws = static_cast<char *>(workspace);
@@ -242,11 +277,11 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
     }
     hipError_t e;
     if (dt == LA_F32)
-        e = dispatch_chunk_dk<float, float>(var, d_k, C, a, st);
+        e = dispatch_chunk_dk<float, float>(var, d_k, C, geo, a, st);
     else if (o_dt == LA_F32)
-        e = dispatch_chunk_dk<bf16, float>(var, d_k, C, a, st);
+        e = dispatch_chunk_dk<bf16, float>(var, d_k, C, geo, a, st);
     else
-        e = dispatch_chunk_dk<bf16, bf16>(var, d_k, C, a, st);
+        e = dispatch_chunk_dk<bf16, bf16>(var, d_k, C, geo, a, st);
     return from_hip(e);
 }
 

@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 f32x4 col = {x[0][e] * sc[0], x[1][e] * sc[1], x[2][e] * sc[2], x[3][e] * sc[3]};
-                st4<TM>(&KTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+                st4<TM>(&KTs[tidx<C, TM>(8 * cb + e, 4 * tq)], col);
             }
         }
     }
@@ -134,7 +134,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 f32x4 col = {x[0][e] * sc[0], x[1][e] * sc[1], x[2][e] * sc[2], x[3][e] * sc[3]};
-                st4<TM>(&VTs[tidx<C>(8 * cb + e, 4 * tq)], col);
+                st4<TM>(&VTs[tidx<C, TM>(8 * cb + e, 4 * tq)], col);
             }
         }
     }
@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NTK; ++ks) {
             const int s0 = g * (C / 4) + ks * E;
-            d = MF::mma(ld_frag<TM>(&KTs[tidx<C>(cbk * 16 + n, s0)]), t_frag(rb * 16 + n, s0), d);
+            d = MF::mma(ld_frag<TM>(&KTs[tidx<C, TM>(cbk * 16 + n, s0)]), t_frag(rb * 16 + n, s0), d);
         }
         st4<TM>(wout + (size_t)(rb * 16 + n) * DK + cbk * 16 + 4 * g, d);
     }
@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NTK; ++ks) {
             const int s0 = g * (C / 4) + ks * E;
-            d = MF::mma(t_frag(rb * 16 + n, s0), ld_frag<TM>(&VTs[tidx<C>(jb * 16 + n, s0)]), d);
+            d = MF::mma(t_frag(rb * 16 + n, s0), ld_frag<TM>(&VTs[tidx<C, TM>(jb * 16 + n, s0)]), d);
         }
         st4<TM>(uout + (size_t)(jb * 16 + n) * a.Lp + rb * 16 + 4 * g, d);
     }

@@ -5,17 +5,59 @@
 
 namespace la {
 
-#define LA_CHUNK(VAR, DK, C) template hipError_t launch_chunk<VAR, bf16, bf16, DK, kDVT, C>(const ChunkArgs &, hipStream_t);
-#define LA_CHUNK_ALL_C(VAR, DK) LA_CHUNK(VAR, DK, 64) LA_CHUNK(VAR, DK, 128)
-#define LA_CHUNK_VARS(DK) LA_CHUNK_ALL_C(V_PLAIN, DK) LA_CHUNK_ALL_C(V_NORM, DK) LA_CHUNK_ALL_C(V_DECAY, DK) LA_CHUNK(V_GDN, DK, 64)
-LA_CHUNK_VARS(32)
-LA_CHUNK_VARS(64)
-LA_CHUNK_VARS(128)
+// chunk forward: (variant, d_k, value columns per workgroup, chunk, waves)
+template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 32, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 32, 64, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 32, 32, 128, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_NORM, bf16, bf16, 32, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_NORM, bf16, bf16, 32, 64, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_NORM, bf16, bf16, 32, 32, 128, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_DECAY, bf16, bf16, 32, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_DECAY, bf16, bf16, 32, 64, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_DECAY, bf16, bf16, 32, 32, 128, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_GDN, bf16, bf16, 32, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_GDN, bf16, bf16, 32, 16, 64, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 64, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 64, 64, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 64, 32, 128, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_NORM, bf16, bf16, 64, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_NORM, bf16, bf16, 64, 64, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_NORM, bf16, bf16, 64, 32, 128, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_DECAY, bf16, bf16, 64, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_DECAY, bf16, bf16, 64, 64, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_DECAY, bf16, bf16, 64, 32, 128, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_GDN, bf16, bf16, 64, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_GDN, bf16, bf16, 64, 16, 64, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 128, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 128, 64, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 128, 32, 128, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_NORM, bf16, bf16, 128, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_NORM, bf16, bf16, 128, 64, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_NORM, bf16, bf16, 128, 32, 128, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_DECAY, bf16, bf16, 128, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_DECAY, bf16, bf16, 128, 64, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_DECAY, bf16, bf16, 128, 32, 128, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_GDN, bf16, bf16, 128, 32, 64, 8>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_GDN, bf16, bf16, 128, 16, 64, 4>(const ChunkArgs &, hipStream_t);
 
-#define LA_DEC(VAR, DK, DV) template hipError_t launch_decode<VAR, bf16, bf16, DK, DV>(const DecodeArgs &, hipStream_t);
-#define LA_DEC_DV(VAR, DK) LA_DEC(VAR, DK, 32) LA_DEC(VAR, DK, 64) LA_DEC(VAR, DK, 128)
-#define LA_DEC_ALL(VAR) LA_DEC_DV(VAR, 32) LA_DEC_DV(VAR, 64) LA_DEC_DV(VAR, 128)
-LA_DEC_ALL(V_PLAIN)
-LA_DEC_ALL(V_DECAY)
+// decode step: (variant, d_k, d_v)
+template hipError_t launch_decode<V_PLAIN, bf16, bf16, 32, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_PLAIN, bf16, bf16, 32, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_PLAIN, bf16, bf16, 32, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_PLAIN, bf16, bf16, 64, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_PLAIN, bf16, bf16, 64, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_PLAIN, bf16, bf16, 64, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_PLAIN, bf16, bf16, 128, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_PLAIN, bf16, bf16, 128, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_PLAIN, bf16, bf16, 128, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_DECAY, bf16, bf16, 32, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_DECAY, bf16, bf16, 32, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_DECAY, bf16, bf16, 32, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_DECAY, bf16, bf16, 64, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_DECAY, bf16, bf16, 64, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_DECAY, bf16, bf16, 64, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_DECAY, bf16, bf16, 128, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_DECAY, bf16, bf16, 128, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_DECAY, bf16, bf16, 128, 128>(const DecodeArgs &, hipStream_t);
 
 }  // namespace la

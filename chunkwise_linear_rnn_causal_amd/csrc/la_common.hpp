@@ -194,13 +194,42 @@ template <> __device__ inline void unpack8<float>(const Raw8<float> &r, float (&
     for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(w[i]);
 }
 
-// Transposed, swizzled [rows][C] tile (token index innermost). Tokens are
-// grouped in 4-element chunks; the chunk index is XORed with a per-row even
-// offset so that transposed 4-token writes from lanes that own rows 8 apart
-// land in different banks, while 8-token aligned reads stay contiguous.
-template <int C> __device__ inline int tidx(int row, int s) {
-    const int swz = (4 * (row >> 3)) & (C / 4 - 1);
-    return row * C + ((((s >> 2) ^ swz)) << 2) + (s & 3);
+// Transposed [rows][C] tile (token index innermost) with an XOR swizzle on
+// 16-byte units: unit' = unit ^ f(row), f(row) = (row & 7) ^ 2 * ((row >> 3) & 3).
+// Rows start on the same bank (the row pitch is a multiple of 128 bytes), so
+//  - 16-byte operand reads by 8 lanes of consecutive rows hit 8 distinct units;
+//  - 8-byte transposed writes by lanes of rows 8 apart (same row & 7) and
+//    consecutive 4-token groups hit 16 distinct 8-byte slots.
+// Reads of 8 aligned tokens (fp16) and writes of 4 aligned tokens stay
+// contiguous because they never cross a unit.
+template <int C, typename T> __device__ inline int tidx(int row, int s) {
+    constexpr int EU = 16 / (int)sizeof(T);  // elements per 16-byte unit
+    constexpr int NU = C / EU;               // units per row
+    const int f = ((row & 7) ^ (2 * ((row >> 3) & 3))) & (NU - 1);
+    return row * C + (((s / EU) ^ f) * EU) + (s % EU);
+}
+
+// DPP move of a float (row_mask / bank_mask select written rows / banks; lanes
+// whose source is invalid or masked keep `old`).
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ inline float dpp_f32(float old, float src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, src), CTRL,
+                                                                 ROW_MASK, BANK_MASK, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP only: row shifts
+// by 1, 2, 4, 8 scan each 16-lane row, then row broadcasts of lanes 15 and 31
+// carry the row totals forward (row_shr = 0x110 + n, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143).
+__device__ inline float wave_inclusive_sum(float x) {
+    x += dpp_f32<0x111>(0.f, x);
+    x += dpp_f32<0x112>(0.f, x);
+    x += dpp_f32<0x114>(0.f, x);
+    x += dpp_f32<0x118>(0.f, x);
+    x += dpp_f32<0x142, 0xa>(0.f, x);
+    x += dpp_f32<0x143, 0xc>(0.f, x);
+    return x;
 }
 
 // XCD-aware block order: consecutive virtual ids go to the same XCD (blocks are

@@ -19,7 +19,7 @@ struct ChunkArgs {
     float *z_out;               // [BH, DK] or nullptr (normalized only)
     const void *w;              // gated delta: W  [BH, Lp, DK] (operand type)
     const void *ut;             // gated delta: U~ transposed [BH, dv, Lp] (operand type)
-    int BH, L, Lp, dv, nsplit;  // Lp = ceil(L / C) * C; nsplit = dv / DVT
+    int BH, L, Lp, dv, nsplit;  // Lp = ceil(L / C) * C; nsplit = dv / DVT (workgroups per head)
 };
 
 // Chunk-parallel preparation of the gated delta rule (one block per chunk).
@@ -38,11 +38,10 @@ struct DecodeArgs {
     int NH;
 };
 
-// Value-column slice width handled by one workgroup of the chunk kernel.
-constexpr int kDVT = 32;
-
-// TI: input type (bf16 or float); TO: output type (float or bf16).
-template <int VAR, typename TI, typename TO, int DK, int DVT, int C>
+// TI: input type (bf16 or float); TO: output type (float or bf16); DVT: value
+// columns per workgroup; NW: waves per workgroup. The instantiated combinations
+// are listed in kernels_*.hip and selected by abi.hip.
+template <int VAR, typename TI, typename TO, int DK, int DVT, int C, int NW>
 hipError_t launch_chunk(const ChunkArgs &a, hipStream_t st);
 
 template <typename TI, int DK, int C>

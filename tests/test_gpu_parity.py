@@ -217,3 +217,22 @@ def test_bf16_output(var, C):
     assert np.all(np.abs(got - ro) <= TOL["bf16"] * rms + 2.0 ** -8 * np.abs(ro))
     # bf16 output is the RNE rounding of the fp32 output of the same kernel
     assert torch.equal(o, o32.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("var,B,H,dk,dv", [
+    ("plain", 4, 64, 64, 64),          # 256 heads x 64 columns: 64-column, 8-wave workgroups
+    ("normalized", 2, 128, 32, 128),
+    ("decay", 2, 64, 128, 128),
+    ("gated_delta", 2, 32, 64, 128),   # 64 heads x 4 slices: 32-column, 8-wave delta rule
+])
+def test_wide_grid_geometry(var, B, H, dk, dv):
+    """Workload shapes with enough heads to select the wider workgroup
+    geometries; a ragged tail included."""
+    inp = W.make_chunk_inputs(var, "bf16", B, H, 150, dk, dv, seed=13, with_state=True,
+                              with_z=(var == "normalized"))
+    o, s, z = gpu_chunk(inp, 64)
+    ro, rs, rz = oracle_chunk(inp)
+    assert_close(o, ro, TOL["bf16"], "o")
+    assert_close(s, rs, TOL["bf16"], "state")
+    if var == "normalized":
+        assert_close(z, rz, 1e-5, "z")
