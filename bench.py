@@ -48,14 +48,20 @@ METRIC = "tokens/sec + % bf16 MFMA peak (chunk fwd); decode state GB/s % of HBM 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2517.0     # 256 CU x 4096 flop/clk x 2.4 GHz, dense fp16/bf16
 CACHE_BYTES = 256 * 2 ** 20   # Infinity Cache (MALL)
-KERNEL_SOURCES = ("chunk_fwd_impl.hpp", "gdn_prep_impl.hpp", "decode_impl.hpp", "la_common.hpp")
+CSRC = os.path.join(ROOT, "chunkwise_linear_rnn_causal_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the library sources (csrc/) with comments and blank lines removed, so
+    that a counter record stays valid across comment-only edits and no longer."""
+    import re
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "chunkwise_linear_rnn_causal_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update("\n".join(l.rstrip() for l in src.splitlines() if l.strip()).encode())
     return h.hexdigest()[:16]
 
 
@@ -100,21 +106,23 @@ def to_dev(x, device):
 
 
 def time_steps(fn, steps: int, warmup: int, stream):
-    """Run fn(i) warmup + steps times; return (wall seconds, per-step event ms list)."""
+    """Run fn(i) warmup times untimed, then exactly `steps` times inside one timed
+    region bracketed by device synchronisation and a pair of HIP events recorded on
+    `stream` (the stream every kernel of the step is launched on). Returns
+    (event ms per step, wall ms per step)."""
     import torch
     for i in range(warmup):
         fn(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(steps):
-        evs[i][0].record(stream)
         fn(warmup + i)
-        evs[i][1].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [a.elapsed_time(b) for a, b in evs]
+    return start.elapsed_time(end) / steps, wall * 1e3 / steps
 
 
 def bench_chunk(name: str, steps: int, warmup: int, device) -> dict:
@@ -141,11 +149,11 @@ def bench_chunk(name: str, steps: int, warmup: int, device) -> dict:
         la.la_chunk_fwd(c["variant"], s["q"], s["k"], s["v"], s["lg"], s["beta"], C=c["C"],
                         o=s["o"], state_out=s["S"], workspace=s["ws"], stream=stream)
 
-    wall, ms = time_steps(step, steps, warmup, stream)
-    t = float(np.mean(ms)) / 1e3
+    ms, wall_ms = time_steps(step, steps, warmup, stream)
+    t = ms / 1e3
     toks = c["B"] * c["L"]
     return dict(workload=name, variant=c["variant"], tokens_per_s=toks / t, ms_per_step=t * 1e3,
-                wall_ms_per_step=wall / steps * 1e3, flop=flop, bytes=nbytes,
+                wall_ms_per_step=wall_ms, flop=flop, bytes=nbytes,
                 achieved_gbs=nbytes / t / 1e9, achieved_tflops=flop / t / 1e12,
                 hbm_frac=nbytes / t / 1e9 / HBM_PEAK_GBS, mfma_frac=flop / t / 1e12 / MFMA_PEAK_TFLOPS,
                 roofline_frac=max(nbytes / (HBM_PEAK_GBS * 1e9), flop / (MFMA_PEAK_TFLOPS * 1e12)) / t,
@@ -170,20 +178,20 @@ def bench_decode(name: str, steps: int, warmup: int, device) -> dict:
         for (q, k, v, lg) in ins:
             la.la_decode_step("decay", q, k, v, lg, S, o=o, stream=stream)
 
-    wall, ms = time_steps(step, steps, warmup, stream)
-    t = float(np.mean(ms)) / 1e3            # one step = nsteps decode launches
+    ms, wall_ms = time_steps(step, steps, warmup, stream)
+    t = ms / 1e3                            # one step = nsteps decode launches
     t1 = t / nsteps
     # tokens: one new token per sequence per decode launch (all H heads of it)
     return dict(workload=name, variant="decay_decode", tokens_per_s=N * nsteps / t,
                 ms_per_step=t * 1e3, ms_per_decode_launch=t1 * 1e3,
-                wall_ms_per_step=wall / steps * 1e3, flop=flop1 * nsteps, bytes=bytes1 * nsteps,
+                wall_ms_per_step=wall_ms, flop=flop1 * nsteps, bytes=bytes1 * nsteps,
                 achieved_gbs=bytes1 / t1 / 1e9, achieved_tflops=flop1 / t1 / 1e12,
                 hbm_frac=bytes1 / t1 / 1e9 / HBM_PEAK_GBS, mfma_frac=None,
                 roofline_frac=bytes1 / (HBM_PEAK_GBS * 1e9) / t1,
                 N=N, H=H, d_k=dk, d_v=dv, decode_launches_per_step=nsteps)
 
 
-def cpu_baseline(name: str, min_seconds: float = 3.0) -> dict:
+def cpu_baseline(name: str, min_seconds: float = 10.0) -> dict:
     """Time the fp64 oracle over the whole workload on the host cores."""
     import oracle
     c = W.CONFIGS[name]

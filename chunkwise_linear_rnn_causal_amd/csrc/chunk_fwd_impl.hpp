@@ -11,25 +11,30 @@
 // rule replaces V_c by U_c = U~_c - W_c S_prev, with W and U~ prepared per chunk
 // by gdn_prep (see gdn_prep_impl.hpp for the derivation).
 //
-// Mapping. One workgroup (4 waves) owns one (batch*head, 32-column value slice)
-// and walks the chunks in order, keeping its d_k x 32 slice of S in fp32 MFMA
-// accumulators for the whole sequence (nothing but Q, K, V, gates and O crosses
-// HBM). Value slices of one head are placed on one XCD so Q and K are shared
-// through that XCD's L2. Per chunk:
-//   1. Q and K staged to LDS row-major (score / inter operands), K also
-//      transposed + scaled by exp(g_C - G_s) (state-update operand), V
-//      transposed; S_prev written to LDS transposed in the operand type. The
-//      global loads of chunk c+1 are issued right after chunk c is staged, into
-//      registers, so their latency hides behind chunk c's math.
-//   2. Wave w owns query rows 16w..16w+15 (and the mirrored block for C = 128).
-//      It computes the inter term (S^T Q^T on MFMA), the score tiles
-//      K_sb Q_rb^T for sb <= rb, masks/decays/rounds them in registers and feeds
-//      them straight back as the B operand of the intra term V^T A^T: the D
+// Mapping. One workgroup (NW waves) owns one (batch*head, DVT-column value
+// slice) and walks the chunks in order, keeping its d_k x DVT slice of S in fp32
+// MFMA accumulators for the whole sequence (nothing but Q, K, V, gates and O
+// crosses HBM). Value slices of one head are placed on one XCD so Q and K are
+// shared through that XCD's L2. Per chunk:
+//   1. Wave 0 has built the gate tables (G, exp(G), exp(g_C - G), exp(g_C)) one
+//      chunk ahead with a DPP prefix scan. All waves stage Q and K to LDS
+//      row-major (score / inter operands), K also transposed and scaled by
+//      exp(g_C - G_s) (state-update operand), V transposed, and S_prev
+//      transposed in the operand type; transposed tiles are XOR-swizzled in
+//      16-byte units. The global loads of chunk c+1 are issued right after chunk
+//      c is staged, into registers, so their latency hides behind chunk c's math.
+//   2. Query row blocks of 16 rows are assigned to waves by Roles: with C/8
+//      waves, wave pairs split the value columns of one row block; with C/32
+//      waves, each wave takes a row block and its mirror so the triangular score
+//      work balances. A wave computes the inter term (S^T Q^T on MFMA), the score
+//      tiles K_sb Q_rb^T for sb <= rb, masks/decays/rounds them in registers and
+//      feeds them straight back as the B operand of the intra term V^T A^T: the D
 //      layout of a score tile is exactly the B-operand layout of the next MFMA
 //      with the key index in the K slots. Output rows are lane-indexed, so the
 //      per-row scales (exp(G_r), 1/den_r) are per-lane scalars and each lane
 //      stores four consecutive output columns.
-//   3. S <- exp(g_C) S + K~^T V on MFMA into the accumulators.
+//   3. S <- exp(g_C) S + K~^T V on MFMA into the accumulators; the state tiles
+//      are split greedily so waves with fewer score tiles take more of them.
 #pragma once
 
 #include <type_traits>
