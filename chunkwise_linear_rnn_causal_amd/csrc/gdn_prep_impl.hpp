@@ -30,11 +30,21 @@ template <typename TM, int DK, int C>
 struct PrepCfg {
     static constexpr int DVMAX = 128;
     static constexpr int PAD = 16 / (int)sizeof(TM);
-    static constexpr int KP = DK + PAD;
-    static constexpr int TP = C + 1;  // fp32 row pitch of P and T
-    static constexpr size_t lds_bytes =
-        sizeof(TM) * ((size_t)C * KP + (size_t)DK * C + (size_t)DVMAX * C) +
-        sizeof(float) * (2 * (size_t)C * TP + 2 * C);
+    static constexpr int KP = DK + PAD;   // row pitch of K
+    static constexpr int TP = C + 1;      // fp32 row pitch of P and T
+    static constexpr int OP = C + PAD;    // row pitch of T in the operand type
+    static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
+    static constexpr size_t up16(size_t x) { return (x + 15) / 16 * 16; }
+    // Lifetimes allow two aliases: K is dead once P is formed (its bytes then
+    // hold T in fp32), and P is dead once T is complete (its bytes then hold T
+    // in the operand type).
+    static constexpr size_t o_k = 0;
+    static constexpr size_t o_kt = o_k + up16(cmax(sizeof(TM) * C * KP, 4 * C * TP));
+    static constexpr size_t o_vt = o_kt + sizeof(TM) * DK * C;
+    static constexpr size_t o_p = o_vt + sizeof(TM) * DVMAX * C;
+    static constexpr size_t o_y = o_p + up16(cmax(4 * C * TP, sizeof(TM) * C * OP));
+    static constexpr size_t o_g = o_y + 4 * 4 * 256;
+    static constexpr size_t lds_bytes = o_g + 4 * 2 * C;
 };
 
 template <typename TI, int DK, int C>
@@ -46,18 +56,21 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     constexpr int E = MF::E;
     constexpr int NW = 4;
     constexpr int NRB = C / 16;
-    constexpr int KP = Cfg::KP, TP = Cfg::TP;
+    constexpr int KP = Cfg::KP, TP = Cfg::TP, OP = Cfg::OP;
     constexpr int NKS = DK / (4 * E);
     constexpr int NTK = C / (4 * E);
-    static_assert(C == 64, "the row-by-row inverse assigns one column per lane: C = 64");
+    static_assert(C == 64 && NRB == NW, "one 16-row diagonal block of T per wave: C = 64");
 
-    __shared__ __attribute__((aligned(16))) TM Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) TM KTs[DK * C];
-    __shared__ __attribute__((aligned(16))) TM VTs[Cfg::DVMAX * C];
-    __shared__ float Pm[C * TP];
-    __shared__ float Tm[C * TP];
-    __shared__ float Gs[C];
-    __shared__ float Bs[C];
+    __shared__ __attribute__((aligned(16))) char lds[Cfg::lds_bytes];
+    TM *Ks = reinterpret_cast<TM *>(lds + Cfg::o_k);
+    float *Tm = reinterpret_cast<float *>(lds + Cfg::o_k);   // after P is formed
+    TM *KTs = reinterpret_cast<TM *>(lds + Cfg::o_kt);
+    TM *VTs = reinterpret_cast<TM *>(lds + Cfg::o_vt);
+    float *Pm = reinterpret_cast<float *>(lds + Cfg::o_p);
+    TM *To = reinterpret_cast<TM *>(lds + Cfg::o_p);         // after T is complete
+    float *Ysc = reinterpret_cast<float *>(lds + Cfg::o_y);
+    float *Gs = reinterpret_cast<float *>(lds + Cfg::o_g);
+    float *Bs = Gs + C;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
     const int bh = blockIdx.x / a.nchunks, c = blockIdx.x - bh * a.nchunks;
@@ -82,7 +95,9 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
         Bs[lane] = bv;
     }
 
-    // Stage K row-major, K transposed scaled by beta_s a_s, V transposed scaled by beta_s.
+    // Stage K row-major, K transposed scaled by beta_s a_s, V transposed scaled by
+    // beta_s. Rows past the end of the sequence are read from the last token (so
+    // every load is unconditional) and then zeroed.
     {
         constexpr int CB = DK / 8, CBL = CB < 4 ? CB : 4, TQL = 16 / CBL, NCBG = CB / CBL;
         constexpr int UNITS = (C / 4) * CB;
@@ -94,10 +109,13 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
             float x[4][8], sc[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int s = 4 * tq + r, t = t0 + s;
-                if (t < L) {
-                    ld8<TI>(kg + (size_t)t * DK + 8 * cb, x[r]);
-                } else {
+                const int t = t0 + 4 * tq + r;
+                ld8<TI>(kg + (size_t)(t < L ? t : L - 1) * DK + 8 * cb, x[r]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = 4 * tq + r;
+                if (t0 + s >= L) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
                 }
@@ -122,15 +140,11 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
             float x[4][8], sc[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int s = 4 * tq + r, t = t0 + s;
-                if (t < L) {
-                    ld8<TI>(vg + (size_t)t * dv + 8 * cb, x[r]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
-                }
-                sc[r] = __shfl(bv, s, 64);
+                const int t = t0 + 4 * tq + r;
+                ld8<TI>(vg + (size_t)(t < L ? t : L - 1) * dv + 8 * cb, x[r]);
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[r] = __shfl(bv, 4 * tq + r, 64);  // beta = 0 past the end
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 f32x4 col = {x[0][e] * sc[0], x[1][e] * sc[1], x[2][e] * sc[2], x[3][e] * sc[3]};
@@ -158,34 +172,71 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
             Pm[r * TP + s] = (s < r) ? Bs[r] * __expf(Gs[r] - Gs[s]) * d[e] : 0.f;
         }
     }
-    __syncthreads();
+    __syncthreads();  // P complete; K row-major is dead from here (Tm reuses it)
 
-    // T = (I + P)^-1 by forward substitution, one row per step:
-    // T[r][col] = -sum_{col <= s < r} P[r][s] T[s][col]  (col < r), T[r][r] = 1.
-    // Wave w owns columns 16w..16w+15; the four lane groups split the s range.
+    // T = (I + P)^-1, blocked by 16 rows. T is unit lower triangular, and so are
+    // its diagonal blocks T_ii = (I + P_ii)^-1; the blocks below the diagonal
+    // follow from (I + P) T = I as T_ij = -T_ii sum_{j <= k < i} P_ik T_kj.
+    //
+    // Diagonal blocks: wave w inverts block w by forward substitution, lane n
+    // holding column n of the block in registers (the four lane groups compute
+    // the same column; group 0 writes it).
     {
-        const int col = wv * 16 + n;
-        for (int r = 0; r < C; ++r) {
-            float part = 0.f;
-            for (int s = col + g; s < r; s += 4) part += Pm[r * TP + s] * Tm[s * TP + col];
-            part += __shfl_xor(part, 16, 64);
-            part += __shfl_xor(part, 32, 64);
-            if (g == 0) Tm[r * TP + col] = (col < r) ? -part : (col == r ? 1.f : 0.f);
-            __syncthreads();
+        const int base = 16 * wv;
+        float tc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < r; ++s) acc = fmaf(Pm[(base + r) * TP + base + s], tc[s], acc);
+            tc[r] = (r == n) ? 1.f : ((r < n) ? 0.f : -acc);
+        }
+        if (g == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Tm[(base + r) * TP + base + n] = tc[r];
         }
     }
+    __syncthreads();
 
-    // T operand fragment: lane (g, n) holds T[r][s0 .. s0+E-1] with r = rb*16 + n.
-    auto t_frag = [&](int r, int s0) -> frag {
-        if constexpr (E == 8) {
-            frag f;
+    // Below-diagonal block (i, j) on fp32 MFMA (16x16x4): Y = sum_k P_ik T_kj,
+    // then T_ij = -T_ii Y. Y passes through a per-wave LDS tile to move from the
+    // accumulator layout to the B-operand layout; LDS operations of one wave
+    // complete in order, so the wave needs no barrier for it.
+    auto below_block = [&](int i, int j) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = j; kb < i; ++kb) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = from_f32<TM>(Tm[r * TP + s0 + e]);
-            return f;
-        } else {
-            return Tm[r * TP + s0];
+            for (int q = 0; q < 4; ++q)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(Pm[(16 * i + n) * TP + 16 * kb + 4 * q + g],
+                                                         Tm[(16 * kb + 4 * q + g) * TP + 16 * j + n], y,
+                                                         0, 0, 0);
         }
+        float *Y = Ysc + wv * 256;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Y[(4 * g + e) * 16 + n] = y[e];
+        __builtin_amdgcn_wave_barrier();
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            t = __builtin_amdgcn_mfma_f32_16x16x4f32(Tm[(16 * i + n) * TP + 16 * i + 4 * q + g],
+                                                     Y[(4 * q + g) * 16 + n], t, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Tm[(16 * i + 4 * g + e) * TP + 16 * j + n] = -t[e];
     };
+    // Blocks one, two and three below the diagonal, each group after the last.
+    if (wv < 3) below_block(wv + 1, wv);
+    __syncthreads();
+    if (wv < 2) below_block(wv + 2, wv);
+    __syncthreads();
+    if (wv == 0) below_block(3, 0);
+    __syncthreads();  // T complete; P is dead from here (To reuses it)
+
+    // T in the operand type, zero above the diagonal blocks.
+    for (int idx = tid; idx < C * C; idx += 256) {
+        const int r = idx / C, s = idx % C;
+        To[r * OP + s] = from_f32<TM>((s >> 4) > (r >> 4) ? 0.f : Tm[r * TP + s]);
+    }
+    __syncthreads();
 
     // W^T tiles D[ch][r] = sum_s (beta a K)[s][ch] T[r][s]; lane holds ch = cbk*16 + 4g + e.
     TM *wout = (TM *)a.w + ((size_t)bh * a.Lp + t0) * DK;
@@ -195,7 +246,8 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NTK; ++ks) {
             const int s0 = g * (C / 4) + ks * E;
-            d = MF::mma(ld_frag<TM>(&KTs[tidx<C, TM>(cbk * 16 + n, s0)]), t_frag(rb * 16 + n, s0), d);
+            d = MF::mma(ld_frag<TM>(&KTs[tidx<C, TM>(cbk * 16 + n, s0)]),
+                        ld_frag<TM>(&To[(rb * 16 + n) * OP + s0]), d);
         }
         st4<TM>(wout + (size_t)(rb * 16 + n) * DK + cbk * 16 + 4 * g, d);
     }
@@ -208,7 +260,8 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NTK; ++ks) {
             const int s0 = g * (C / 4) + ks * E;
-            d = MF::mma(t_frag(rb * 16 + n, s0), ld_frag<TM>(&VTs[tidx<C, TM>(jb * 16 + n, s0)]), d);
+            d = MF::mma(ld_frag<TM>(&To[(rb * 16 + n) * OP + s0]),
+                        ld_frag<TM>(&VTs[tidx<C, TM>(jb * 16 + n, s0)]), d);
         }
         st4<TM>(uout + (size_t)(jb * 16 + n) * a.Lp + rb * 16 + 4 * g, d);
     }
