@@ -4,7 +4,7 @@
 // form; section 5.2 for the decayed variant): for chunk c of C tokens with
 // chunk-local cumulative log-gate G_r and a_r = exp(G_r),
 //   O_c    = diag(a) Q_c S_prev  +  (Gamma (.) Q_c K_c^T (.) M) V_c
-//   S_next = a_C S_prev + (diag(a_C / a) K_c)^T V_c,   Gamma_rs = exp(G_r - G_s)
+//   S_next = a_C S_prev + K_c^T diag(a_C / a) V_c,   Gamma_rs = exp(G_r - G_s)
 // with M the inclusive causal mask. Without gates a = 1. The normalized variant
 // divides each output row by rowsum(Q_c K_c^T (.) M) + q_r . z_prev and carries
 // z_next = z_prev + sum_s k_s (proig-chaa notes, sections 13-14). The gated delta
@@ -16,13 +16,14 @@
 // MFMA accumulators for the whole sequence (nothing but Q, K, V, gates and O
 // crosses HBM). Value slices of one head are placed on one XCD so Q and K are
 // shared through that XCD's L2. Per chunk:
-//   1. Wave 0 has built the gate tables (G, exp(G), exp(g_C - G), exp(g_C)) one
-//      chunk ahead with a DPP prefix scan. All waves stage Q and K to LDS
-//      row-major (score / inter operands), K also transposed and scaled by
-//      exp(g_C - G_s) (state-update operand), V transposed, and S_prev
-//      transposed in the operand type; transposed tiles are XOR-swizzled in
-//      16-byte units. The global loads of chunk c+1 are issued right after chunk
-//      c is staged, into registers, so their latency hides behind chunk c's math.
+//   1. Q, K and V arrive as whole 16-byte row segments (every wave load covers
+//      complete rows), are converted to the operand type and written row-major
+//      into XOR-swizzled LDS tiles; V is also written scaled by exp(g_C - G_s)
+//      for the state update. Operands that need the token index in the K slots
+//      (K^T and V^T) are read from the row-major tiles with the gfx950
+//      transpose load. The loads of chunk c+1 are issued right after chunk c is
+//      staged, so their latency hides behind chunk c's math. Wave 0 has built
+//      the gate tables (G, exp(G), exp(g_C - G), exp(g_C)) one chunk ahead.
 //   2. Query row blocks of 16 rows are assigned to waves by Roles: with C/8
 //      waves, wave pairs split the value columns of one row block; with C/32
 //      waves, each wave takes a row block and its mirror so the triangular score
@@ -33,8 +34,8 @@
 //      with the key index in the K slots. Output rows are lane-indexed, so the
 //      per-row scales (exp(G_r), 1/den_r) are per-lane scalars and each lane
 //      stores four consecutive output columns.
-//   3. S <- exp(g_C) S + K~^T V on MFMA into the accumulators; the state tiles
-//      are split greedily so waves with fewer score tiles take more of them.
+//   3. S <- exp(g_C) S + K^T (w V) on MFMA into the accumulators; the state
+//      tiles are split greedily so waves with fewer score tiles take more.
 #pragma once
 
 #include <type_traits>
@@ -48,80 +49,41 @@ template <typename T> __device__ inline float frag_elem(const typename Mfma<T>::
 template <> __device__ inline float frag_elem<f16>(const f16x8 &f, int i) { return (float)f[i]; }
 template <> __device__ inline float frag_elem<float>(const float &f, int) { return f; }
 
-// N dwords from global memory (N in {1, 2, 4, 8}; p aligned to the load size).
-template <int N> __device__ inline void ld_dwords(const void *p, uint32_t (&d)[N]) {
-    if constexpr (N == 1) {
-        d[0] = *reinterpret_cast<const uint32_t *>(p);
-    } else if constexpr (N == 2) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(p);
-        d[0] = v.x; d[1] = v.y;
-    } else {
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i) {
-            const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
-            d[4 * i] = v.x; d[4 * i + 1] = v.y; d[4 * i + 2] = v.z; d[4 * i + 3] = v.w;
-        }
-    }
-}
-// Dwords holding elements of type T, widened to fp32.
-template <typename T, int N> __device__ inline float dw_elem(const uint32_t (&d)[N], int i) {
-    if constexpr (sizeof(T) == 2) {
-        return (i & 1) ? bf16_hi(d[i >> 1]) : bf16_lo(d[i >> 1]);
-    } else {
-        return __uint_as_float(d[i]);
-    }
-}
-
-// Staging geometry: units of 4 tokens x X channels of a [C][D] tile. A 16-lane
-// group covers 4 token quads x 4 channel groups, which keeps the transposed
-// 4-token writes of a group on distinct LDS slots and loads rows in runs of
-// 4 * X elements.
-template <int C, int D, int X> struct Units {
-    static constexpr int NCG = D / X;              // channel groups per token row
-    static constexpr int CGL = NCG < 4 ? NCG : 4;  // channel groups per 16-lane group
-    static constexpr int TQL = 16 / CGL;           // token quads per 16-lane group
-    static constexpr int NCGG = NCG / CGL;
-    static constexpr int N = (C / 4) * NCG;        // number of units
-    static_assert(N % 16 == 0 && NCG % CGL == 0, "unit geometry");
-    __device__ static inline void pos(int u, int &tq, int &cg) {
-        const int gi = u >> 4, l16 = u & 15;
-        tq = (gi / NCGG) * TQL + (l16 % TQL);
-        cg = (gi % NCGG) * CGL + (l16 / TQL);
-    }
+// ---------------------------------------------------------------------------
+// Row-major LDS tiles [rows][W] of the operand type, padded by PAD elements per
+// row (fp16; fp32 tiles pad by 4). Padding rather than an XOR swizzle keeps
+// every address a per-lane base plus a compile-time offset. The pads are chosen
+// for gfx950's LDS (64 banks; 8-byte reads served 32 lanes at a time): with a
+// 32-byte pad the transpose loads below (16 consecutive rows x 32 bytes per
+// half-wave) are conflict-free, 16-byte staging writes of whole rows are too,
+// and 16-byte operand reads of 16 rows see at most 2-way conflicts; the Q tile,
+// which only sees operand reads, pads by 16 bytes (conflict-free).
+template <typename TM, int W, int PAD> struct RowTile {
+    static constexpr int P = sizeof(TM) == 2 ? W + PAD : W + 4;  // row pitch (elements)
+    static constexpr int SIZE_ROWS(int rows) { return rows * P; }
+    __device__ static constexpr int at(int row, int col) { return row * P + col; }
 };
 
-// Channels per staging unit so that nthreads threads get one unit each when the
-// tile allows (2 <= X <= 8).
-constexpr int unit_width(int C, int D, int nthreads) {
-    const int x = C * D / (4 * nthreads);
-    return x < 2 ? 2 : (x > 8 ? 8 : x);
+// Operand fragment X[k][col0 + n] for the K-slots {r0 .. r0+3, r0+16 .. r0+19}
+// of this lane's group, from a row-major fp16 tile of pitch P, with two
+// transpose loads. In a 16-lane group the transpose load hands lane i element e
+// of the 8-byte row piece addressed by lane 4e + i/4, column i % 4; so lane j
+// addresses row r + (j >> 2), columns col0 + 4 (j & 3).
+template <int P>
+__device__ inline f16x8 tr_frag(const f16 *X, int r0, int col0, int lane) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const int j = lane & 15;
+    const f16 *p0 = X + (r0 + (j >> 2)) * P + col0 + 4 * (j & 3);
+    const f16 *p1 = p0 + 16 * P;
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p0));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p1));
+    const f16x4 ha = __builtin_bit_cast(f16x4, a), hb = __builtin_bit_cast(f16x4, b);
+    return f16x8{ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
 }
 
-// X consecutive elements (as fp32) stored in type T.
-template <typename T, int X> __device__ inline void st_row(T *p, const float *x) {
-    if constexpr (X == 8) {
-        f32x4 a = {x[0], x[1], x[2], x[3]}, b = {x[4], x[5], x[6], x[7]};
-        st4<T>(p, a);
-        st4<T>(p + 4, b);
-    } else if constexpr (X == 4) {
-        f32x4 a = {x[0], x[1], x[2], x[3]};
-        st4<T>(p, a);
-    } else {
-        static_assert(X == 2, "row width");
-        if constexpr (sizeof(T) == 2) {
-            typedef T T2 __attribute__((ext_vector_type(2)));
-            T2 v = {from_f32<T>(x[0]), from_f32<T>(x[1])};
-            *reinterpret_cast<T2 *>(p) = v;
-        } else {
-            *reinterpret_cast<float2 *>(p) = make_float2(x[0], x[1]);
-        }
-    }
-}
-
-// Output-phase roles of wave w. Mode 0: NW == NRB, wave w owns row block w and
-// every value column. Mode 1: NW == 2 NRB, waves w and w + NRB share row block w
-// and take one half of the value columns each. Mode 2: NW == NRB / 2, wave w owns
-// row blocks w and NRB - 1 - w (balanced triangle).
+// ---------------------------------------------------------------------------
+// Contiguous ranges of state tiles per wave, filled greedily so that waves with
+// fewer score tiles take more state tiles.
 template <int NW, int NRB> struct Roles {
     static constexpr int MODE = (NW == NRB) ? 0 : (NW == 2 * NRB) ? 1 : (2 * NW == NRB) ? 2 : -1;
     static_assert(MODE >= 0, "wave count must be C/16, C/8 or C/32");
@@ -132,21 +94,20 @@ template <int NW, int NRB> struct Roles {
     static constexpr int score_tiles(int w) { return MODE == 2 ? NRB + 1 : (w % NRB) + 1; }
 };
 
-// Contiguous ranges of state tiles per wave, filled greedily so that waves with
-// fewer score tiles take more state tiles.
 template <int NTT, int NW> struct TileSplit {
     int start[NW];
     int cnt[NW];
     int maxcnt;
 };
 template <int NTT, int NW, int NRB>
-constexpr TileSplit<NTT, NW> make_tile_split() {
+constexpr TileSplit<NTT, NW> make_tile_split(int extra0) {
     TileSplit<NTT, NW> t{};
     for (int w = 0; w < NW; ++w) t.cnt[w] = 0;
+    auto load = [&](int w) { return Roles<NW, NRB>::score_tiles(w) + t.cnt[w] + (w == 0 ? extra0 : 0); };
     for (int i = 0; i < NTT; ++i) {
         int best = 0;
         for (int w = 1; w < NW; ++w)
-            if (Roles<NW, NRB>::score_tiles(w) + t.cnt[w] < Roles<NW, NRB>::score_tiles(best) + t.cnt[best]) best = w;
+            if (load(w) < load(best)) best = w;
         ++t.cnt[best];
     }
     int acc = 0;
@@ -163,11 +124,10 @@ template <int VAR, typename TM, int DK, int DVT, int C>
 struct ChunkCfg {
     static constexpr bool DECAYED = (VAR == V_DECAY || VAR == V_GDN);
     static constexpr int PAD = 16 / (int)sizeof(TM);
-    static constexpr int KP = DK + PAD;  // row pitch of Qs / Ks / STs (elements)
-    static constexpr size_t lds_bytes =
-        sizeof(TM) * (2 * (size_t)C * KP + (size_t)DK * C + (DECAYED ? 2 : 1) * (size_t)DVT * C +
-                      (size_t)DVT * KP) +
-        sizeof(float) * ((DECAYED ? 8 * C + 2 : 0) + (VAR == V_NORM ? 2 * DK : 0));
+    static constexpr int KP = DK + PAD;  // row pitch of STs (elements)
+    using QT = RowTile<TM, DK, 8>;                        // Q: operand reads only
+    using KT = RowTile<TM, DK, 16>;                       // K: operand and transpose reads
+    using VT = RowTile<TM, DVT, DVT == 16 ? 0 : 16>;      // V, wV: transpose reads
 };
 
 // TI: input storage type (bf16 or fp32); TO: output type (fp32 or bf16); the
@@ -179,42 +139,51 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     using MF = Mfma<TM>;
     using frag = typename MF::frag;
     using Cfg = ChunkCfg<VAR, TM, DK, DVT, C>;
-    constexpr int NT = NW * 64;          // threads
+    using QT = typename Cfg::QT;          // Q tile
+    using KT = typename Cfg::KT;          // K tile
+    using VT = typename Cfg::VT;          // V (or U) tiles
+    constexpr bool H = sizeof(TM) == 2;
+    constexpr int NT = NW * 64;           // threads
     constexpr int E = MF::E;
-    constexpr int NRB = C / 16;          // 16-row blocks per chunk
+    constexpr int NRB = C / 16;           // 16-row blocks per chunk
     using R = Roles<NW, NRB>;
     constexpr bool DECAYED = Cfg::DECAYED;
     constexpr int KP = Cfg::KP;
     constexpr int NTI = DK / 16, NTJ = DVT / 16;
     constexpr int NTJW = R::MODE == 1 ? NTJ / 2 : NTJ;  // output column tiles per wave
-    constexpr int NKS = DK / (4 * E);    // k-steps over channels
-    constexpr int NTK = C / (4 * E);     // k-steps over tokens
-    constexpr int PER = C / 64;          // tokens per lane in the gate scan
-    constexpr int NQR = DK / 32;         // 8-element runs of one lane's channels (DK/4)
-    constexpr int XK = unit_width(C, DK, NT), XV = unit_width(C, DVT, NT);
-    using UK = Units<C, DK, XK>;
-    using UV = Units<C, DVT, XV>;
-    constexpr int NUK = (UK::N + NT - 1) / NT, NUV = (UV::N + NT - 1) / NT;
-    constexpr int KRAW = XK * (int)sizeof(TI) / 4, VRAW = XV * (int)sizeof(TI) / 4;
-    constexpr auto TS = make_tile_split<NTI * NTJ, NW, NRB>();
-    constexpr int NTS = TS.maxcnt;       // state tiles per wave (at most)
+    constexpr int NKS = DK / (4 * E);     // k-steps over channels
+    constexpr int NTK = C / (4 * E);      // k-steps over tokens
+    constexpr int PER = C / 64;           // tokens per lane in the gate scan
+    constexpr int NQR = DK / 32;          // 8-element runs of one lane's channels (DK/4)
+    // Staging: 16-byte row segments; one wave load covers 64/SEG whole rows.
+    constexpr int EPS = 16 / (int)sizeof(TI);              // input elements per segment
+    constexpr int SEGQ = DK / EPS, SEGV = DVT / EPS;        // segments per row
+    constexpr int NIQ = C * SEGQ / 64;                      // wave loads per chunk for Q (and K)
+    constexpr int NIV = (VAR == V_GDN) ? 0 : C * SEGV / 64;
+    constexpr int NI = 2 * NIQ + NIV;
+    constexpr int NSLOT = (NI + NW - 1) / NW;
+    static_assert(64 % SEGQ == 0 && (VAR == V_GDN || 64 % SEGV == 0) && C * SEGQ % 64 == 0 &&
+                  C * SEGV % 64 == 0, "staging geometry");
+    constexpr int ZW = 0;                 // wave that carries the normalizer
+    constexpr auto TS = make_tile_split<NTI * NTJ, NW, NRB>(VAR == V_NORM ? NTI : 0);
+    constexpr int NTS = TS.maxcnt;        // state tiles per wave (at most)
     static_assert(NTJW >= 1 && (R::MODE != 1 || NTJ % 2 == 0), "value slice too narrow for the roles");
     static_assert(VAR != V_GDN || (R::MODE <= 1 && NRB == 4), "delta rule: one U row block per wave (pair)");
 
-    __shared__ __attribute__((aligned(16))) TM Qs[C * KP];
-    __shared__ __attribute__((aligned(16))) TM Ks[C * KP];
-    __shared__ __attribute__((aligned(16))) TM KTs[DK * C];
-    __shared__ __attribute__((aligned(16))) TM VTs[DVT * C];
-    __shared__ __attribute__((aligned(16))) TM VWs[DECAYED ? DVT * C : 1];  // V (or U) scaled by w_s
+    __shared__ __attribute__((aligned(16))) TM Qs[C * QT::P];
+    __shared__ __attribute__((aligned(16))) TM Ks[C * KT::P];
+    __shared__ __attribute__((aligned(16))) TM Vs[C * VT::P];
+    __shared__ __attribute__((aligned(16))) TM VWs[DECAYED ? C * VT::P : 1];  // V (or U) scaled by w_s
     __shared__ __attribute__((aligned(16))) TM STs[DVT * KP];
     // Gate tables per buffer: [0] G_s, [1] exp(G_s), [2] w_s = exp(g_C - G_s),
     // [3] exp(G_{end of s's 16-block} - G_s); Tsc = exp(g_C).
     __shared__ __attribute__((aligned(16))) float Tg[DECAYED ? 2 * 4 * C : 1];
     __shared__ float Tsc[DECAYED ? 2 : 1];
-    __shared__ float Zs[VAR == V_NORM ? 2 * DK : 1];
-    TM *VW = DECAYED ? VWs : VTs;
+    __shared__ __attribute__((aligned(16))) float Zs[VAR == V_NORM ? 2 * DK : 1];
+    TM *VW = DECAYED ? VWs : Vs;
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int vid = xcd_virtual_block();
     const int bh = vid / a.nsplit, split = vid - bh * a.nsplit;
     const int j0 = split * DVT;
@@ -228,13 +197,15 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         }
     }
 
+    // Per-head bases; offsets inside a head are 32-bit (L * d < 2^31 is checked
+    // by the ABI layer).
     const TI *qg = (const TI *)a.q + (size_t)bh * L * DK;
     const TI *kg = (const TI *)a.k + (size_t)bh * L * DK;
     const TI *vg = (VAR == V_GDN) ? nullptr : (const TI *)a.v + (size_t)bh * L * dv + j0;
     TO *og = (TO *)a.o + (size_t)bh * L * dv + j0;
     const float *lgg = (DECAYED && a.lg) ? a.lg + (size_t)bh * L : nullptr;
     const TM *wg = (VAR == V_GDN) ? (const TM *)a.w + (size_t)bh * a.Lp * DK : nullptr;
-    const TM *utg = (VAR == V_GDN) ? (const TM *)a.ut + ((size_t)bh * dv + j0) * a.Lp : nullptr;
+    const TM *utg = (VAR == V_GDN) ? (const TM *)a.ut + (size_t)bh * a.Lp * dv + j0 : nullptr;
 
     // ---- initial state slice in accumulator layout: lane (g, n) of tile (ti, tj)
     // holds S[ti*16 + 4g + e][j0 + tj*16 + n].
@@ -250,7 +221,15 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             for (int e = 0; e < 4; ++e) Sacc[m][e] = sp[(size_t)e * dv];
         }
     }
+    // Normalizer z in accumulator layout (wave ZW): lane (g, n) of tile ti holds
+    // z[ti*16 + 4g + e] (every column n alike).
+    f32x4 zacc[VAR == V_NORM ? NTI : 1];
     if constexpr (VAR == V_NORM) {
+#pragma unroll
+        for (int ti = 0; ti < NTI; ++ti) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) zacc[ti][e] = a.z_in ? a.z_in[(size_t)bh * DK + ti * 16 + 4 * g + e] : 0.f;
+        }
         for (int i = tid; i < DK; i += NT) Zs[i] = a.z_in ? a.z_in[(size_t)bh * DK + i] : 0.f;
     }
     // Settle the prologue's loads here, so that no load is pending at the loop
@@ -258,17 +237,35 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
 
     // ---- registers of the next chunk, loaded one chunk ahead so that global
-    // latency overlaps the current chunk's math. Every memory operation of a full
-    // chunk is unconditional (threads without a staging unit load a duplicate
-    // address), so the compiler's wait counts stay exact; only the ragged last
-    // chunk clamps rows, which are zeroed when the registers are consumed.
-    uint32_t kpre[NUK][4][KRAW];
-    uint32_t qpre[NUK][4][KRAW];
-    uint32_t vpre[NUV][4][VRAW];
+    // latency overlaps the current chunk's math. Wave load i (i < NI) covers
+    // rows i*64/SEG .. of Q, K or V; wave w issues loads w, w + NW, ... and waves
+    // past the end repeat the last load, so every memory operation of a full
+    // chunk is unconditional and the compiler's wait counts stay exact. Only the
+    // ragged last chunk clamps rows, which are zeroed when staged.
+    uint4 pre[NSLOT];
     float gpre[PER];
     Raw8<TM> wpre[NQR];           // gated delta: W row of this wave's U row block
-    f32x4 upre[NTJW];             // gated delta: U~ of this wave's U tiles
+    f32x4 upre[NTJW];             // gated delta: U~ of this wave's U tiles (transposed layout)
     const float *gsrc = lgg ? lgg : reinterpret_cast<const float *>(qg);
+
+    // Geometry of slot m of this wave: tensor (0 Q, 1 K, 2 V), chunk row, segment.
+    auto slot_geom = [&](int m, int &kind, int &row, int &seg) {
+        int i = wv + NW * m;
+        i = i < NI ? i : NI - 1;
+        if (i < NIQ) {
+            kind = 0;
+            row = i * (64 / SEGQ) + lane / SEGQ;
+            seg = lane % SEGQ;
+        } else if (i < 2 * NIQ) {
+            kind = 1;
+            row = (i - NIQ) * (64 / SEGQ) + lane / SEGQ;
+            seg = lane % SEGQ;
+        } else {
+            kind = 2;
+            row = (i - 2 * NIQ) * (64 / SEGV) + lane / SEGV;
+            seg = lane % SEGV;
+        }
+    };
 
     auto load_chunk = [&](int c, auto ragged_tag) {
         constexpr bool RAGGED = decltype(ragged_tag)::value;
@@ -279,36 +276,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             for (int p = 0; p < PER; ++p) gpre[p] = gsrc[row(t0 + lane * PER + p)];
         }
 #pragma unroll
-        for (int i = 0; i < NUK; ++i) {
-            int tq, cg;
-            UK::pos((tid + NT * i) % UK::N, tq, cg);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = row(t0 + 4 * tq + r);
-                ld_dwords<KRAW>(kg + (size_t)t * DK + cg * XK, kpre[i][r]);
-                ld_dwords<KRAW>(qg + (size_t)t * DK + cg * XK, qpre[i][r]);
-            }
-        }
-        if constexpr (VAR != V_GDN) {
-#pragma unroll
-            for (int i = 0; i < NUV; ++i) {
-                int tq, cg;
-                UV::pos((tid + NT * i) % UV::N, tq, cg);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = row(t0 + 4 * tq + r);
-                    ld_dwords<VRAW>(vg + (size_t)t * dv + cg * XV, vpre[i][r]);
-                }
-            }
+        for (int m = 0; m < NSLOT; ++m) {
+            int kind, r, seg;
+            slot_geom(m, kind, r, seg);
+            const int t = row(t0 + r);
+            const TI *p = kind == 0 ? qg + t * DK : kind == 1 ? kg + t * DK : vg + t * dv;
+            pre[m] = *reinterpret_cast<const uint4 *>(p + seg * EPS);
         }
         if constexpr (VAR == V_GDN) {
             const int srow = t0 + (wv % NRB) * 16 + n;  // W and U~ have Lp rows: always in range
 #pragma unroll
-            for (int i = 0; i < NQR; ++i) wpre[i] = ld_raw8<TM>(wg + (size_t)srow * DK + g * (DK / 4) + 8 * i);
+            for (int i = 0; i < NQR; ++i) wpre[i] = ld_raw8<TM>(wg + srow * DK + g * (DK / 4) + 8 * i);
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) {
                 const int tj = R::half(wv) * NTJW + jt;
-                upre[jt] = ld4<TM>(utg + (size_t)(tj * 16 + n) * a.Lp + t0 + (wv % NRB) * 16 + 4 * g);
+                upre[jt] = ld4<TM>(utg + srow * dv + tj * 16 + 4 * g);
             }
         }
     };
@@ -359,6 +341,19 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         }
     };
 
+    // Token-slot operand of a row-major tile: X[k][col0 + n] for the K-slots of
+    // k-step ks over tokens. fp16: lane group g carries tokens 32 ks + 4g + (0..3)
+    // and 32 ks + 16 + 4g + (0..3), the same slots as the score tiles 2 ks and
+    // 2 ks + 1 hold in accumulator layout; fp32: token 4 ks + g.
+    auto tok_frag = [&](const TM *X, auto p_tag, int ks, int col0) -> frag {
+        constexpr int P = decltype(p_tag)::value;
+        if constexpr (H) {
+            return tr_frag<P>(X, 32 * ks + 4 * g, col0, lane);
+        } else {
+            return X[(4 * ks + g) * P + col0 + n];
+        }
+    };
+
     const int nchunks = (L + C - 1) / C;
     const int nfull = L / C;  // chunks with all C rows valid
     const std::true_type ragged_t{};
@@ -366,6 +361,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     using NextNone = std::integral_constant<int, 0>;
     using NextFull = std::integral_constant<int, 1>;
     using NextTail = std::integral_constant<int, 2>;  // ragged next chunk if L % C != 0
+    using PK = std::integral_constant<int, KT::P>;
+    using PV = std::integral_constant<int, VT::P>;
 
     // One chunk. ragged_tag: this chunk has rows past L. next_tag: which loads to
     // issue for chunk c + 1.
@@ -386,53 +383,44 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             }
         }
 
-        // ---- stage Q and K row-major, K transposed.
+        // ---- stage this chunk's Q, K, V segments row-major (V also scaled by w_s).
 #pragma unroll
-        for (int i = 0; i < NUK; ++i) {
-            const int u = tid + NT * i;
-            if (UK::N % NT == 0 || u < UK::N) {
-                int tq, cg;
-                UK::pos(u, tq, cg);
-                float x[4][XK];
+        for (int m = 0; m < NSLOT; ++m) {
+            if (NW * m + NW <= NI || wv + NW * m < NI) {
+                int kind, r, seg;
+                slot_geom(m, kind, r, seg);
+                const bool valid = !RAGGED || t0 + r < L;
+                const uint32_t w4[4] = {pre[m].x, pre[m].y, pre[m].z, pre[m].w};
+                if constexpr (H) {
+                    f16x8 h;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool valid = !RAGGED || t0 + 4 * tq + r < L;
-                    float y[XK];
-#pragma unroll
-                    for (int e = 0; e < XK; ++e) {
-                        y[e] = valid ? dw_elem<TI, KRAW>(qpre[i][r], e) : 0.f;
-                        x[r][e] = valid ? dw_elem<TI, KRAW>(kpre[i][r], e) : 0.f;
+                    for (int i = 0; i < 4; ++i) {
+                        h[2 * i] = (f16)(valid ? bf16_lo(w4[i]) : 0.f);
+                        h[2 * i + 1] = (f16)(valid ? bf16_hi(w4[i]) : 0.f);
                     }
-                    st_row<TM, XK>(&Qs[(4 * tq + r) * KP + cg * XK], y);
-                    st_row<TM, XK>(&Ks[(4 * tq + r) * KP + cg * XK], x[r]);
-                }
-#pragma unroll
-                for (int e = 0; e < XK; ++e) {
-                    f32x4 col = {x[0][e], x[1][e], x[2][e], x[3][e]};
-                    st4<TM>(&KTs[tidx<C, TM>(cg * XK + e, 4 * tq)], col);
-                }
-            }
-        }
-        // ---- stage V transposed, and V scaled by w_s for the state update.
-        if constexpr (VAR != V_GDN) {
-#pragma unroll
-            for (int i = 0; i < NUV; ++i) {
-                const int u = tid + NT * i;
-                if (UV::N % NT == 0 || u < UV::N) {
-                    int tq, cg;
-                    UV::pos(u, tq, cg);
-                    f32x4 w4 = {1.f, 1.f, 1.f, 1.f};
-                    if constexpr (DECAYED) w4 = *reinterpret_cast<const f32x4 *>(&T[2 * C + 4 * tq]);
-#pragma unroll
-                    for (int e = 0; e < XV; ++e) {
-                        f32x4 col;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const bool valid = !RAGGED || t0 + 4 * tq + r < L;
-                            col[r] = valid ? dw_elem<TI, VRAW>(vpre[i][r], e) : 0.f;
+                    if (kind == 2) {
+                        *reinterpret_cast<f16x8 *>(&Vs[VT::at(r, seg * 8)]) = h;
+                        if constexpr (DECAYED) {
+                            const f16 w = (f16)T[2 * C + r];
+                            *reinterpret_cast<f16x8 *>(&VWs[VT::at(r, seg * 8)]) = h * w;
                         }
-                        st4<TM>(&VTs[tidx<C, TM>(cg * XV + e, 4 * tq)], col);
-                        if constexpr (DECAYED) st4<TM>(&VWs[tidx<C, TM>(cg * XV + e, 4 * tq)], col * w4);
+                    } else if (kind == 1) {
+                        *reinterpret_cast<f16x8 *>(&Ks[KT::at(r, seg * 8)]) = h;
+                    } else {
+                        *reinterpret_cast<f16x8 *>(&Qs[QT::at(r, seg * 8)]) = h;
+                    }
+                } else {
+                    f32x4 x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = valid ? __uint_as_float(w4[i]) : 0.f;
+                    if (kind == 2) {
+                        *reinterpret_cast<f32x4 *>(&Vs[VT::at(r, seg * 4)]) = x;
+                        if constexpr (DECAYED)
+                            *reinterpret_cast<f32x4 *>(&VWs[VT::at(r, seg * 4)]) = x * T[2 * C + r];
+                    } else if (kind == 1) {
+                        *reinterpret_cast<f32x4 *>(&Ks[KT::at(r, seg * 4)]) = x;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(&Qs[QT::at(r, seg * 4)]) = x;
                     }
                 }
             }
@@ -469,38 +457,28 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- gated delta rule: U = U~ - W S_prev for this wave's 16 rows and
-        // column tiles, written transposed into VTs (intra operand) and scaled by
-        // w_s into VWs (state operand). D[s][j]: lane (g, n) holds s = ub*16 + 4g + e.
+        // column tiles, computed transposed, D[j][s] = sum_i S[i][j] (-W[s][i]),
+        // so that lane (g, n) holds U[s = ub*16 + n][j = jj + 4g + e] and writes
+        // four consecutive columns of the row-major V tile (and of the w_s-scaled
+        // copy for the state update).
         if constexpr (VAR == V_GDN) {
             const int ub = wv % NRB;
-            const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&T[2 * C + ub * 16 + 4 * g]);
+            const int s = ub * 16 + n;
+            const float ws = T[2 * C + s];
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) {
-                const int jj = (R::half(wv) * NTJW + jt) * 16 + n;
+                const int jj = (R::half(wv) * NTJW + jt) * 16;
                 f32x4 acc = ucur[jt];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
-                    acc = MF::mma(wf[ks], ld_frag<TM>(&STs[jj * KP + g * (DK / 4) + ks * E]), acc);
-                st4<TM>(&VTs[tidx<C, TM>(jj, ub * 16 + 4 * g)], acc);
-                st4<TM>(&VWs[tidx<C, TM>(jj, ub * 16 + 4 * g)], acc * w4);
+                    acc = MF::mma(ld_frag<TM>(&STs[(jj + n) * KP + g * (DK / 4) + ks * E]), wf[ks], acc);
+                st4<TM>(&Vs[VT::at(s, jj + 4 * g)], acc);
+                st4<TM>(&VWs[VT::at(s, jj + 4 * g)], acc * ws);
             }
             __syncthreads();
         }
 
-        // ---- normalizer carry: z_next = z_prev + sum_s k_s (fp32), from the
-        // transposed K tile.
         const int zc = (c & 1) * DK, zn = ((c + 1) & 1) * DK;
-        if constexpr (VAR == V_NORM) {
-            for (int i = tid; i < DK; i += NT) {
-                float sacc = 0.f;
-#pragma unroll
-                for (int s0 = 0; s0 < C; s0 += 4) {  // 4 tokens never cross a swizzle unit
-                    const f32x4 x = ld4<TM>(&KTs[tidx<C, TM>(i, s0)]);
-                    sacc += (x[0] + x[1]) + (x[2] + x[3]);
-                }
-                Zs[zn + i] = Zs[zc + i] + sacc;
-            }
-        }
 
         // ---- outputs for one 16-row block and one range of value tiles; both
         // are compile-time constants so every score tile is straight-line code.
@@ -511,7 +489,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             const int rrow = t0 + rl;
             frag qf[NKS];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) qf[ks] = ld_frag<TM>(&Qs[rl * KP + g * (DK / 4) + ks * E]);
+            for (int ks = 0; ks < NKS; ++ks) qf[ks] = ld_frag<TM>(&Qs[QT::at(rl, g * (DK / 4) + ks * E)]);
             const float Gr = DECAYED ? T[rl] : 0.f;
 
             // inter-chunk term: D[j][r] = exp(G_r) sum_i S[i][j] q_r[i]
@@ -543,7 +521,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                 if (sb <= rb) {
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
-                        sc[sb] = MF::mma(ld_frag<TM>(&Ks[(sb * 16 + n) * KP + g * (DK / 4) + ks * E]),
+                        sc[sb] = MF::mma(ld_frag<TM>(&Ks[KT::at(sb * 16 + n, g * (DK / 4) + ks * E)]),
                                          qf[ks], sc[sb]);
                     if (sb == rb) {
 #pragma unroll
@@ -568,9 +546,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                 }
             }
 
-            // intra-chunk term: D[j][r] += sum_s V[s][j] A[r][s]
+            // intra-chunk term: D[j][r] += sum_s V[s][j] A[r][s]; the V^T operand
+            // holds the tokens of the two score tiles 2p, 2p+1 that lane group g
+            // carries: s = 32p + 4g + (0..3) and 32p + 16 + 4g + (0..3).
             if constexpr (E == 8) {
-                using V4 = typename Vec4<TM>::type;
 #pragma unroll
                 for (int p = 0; p < NRB / 2; ++p) {
                     if (2 * p <= rb) {
@@ -583,18 +562,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                         const bool hi = (2 * p + 1 <= rb);
 #pragma unroll
                         for (int jt = 0; jt < NTJW; ++jt) {
-                            const int jj = (tj0 + jt) * 16 + n;
-                            const V4 lo4 = *reinterpret_cast<const V4 *>(&VTs[tidx<C, TM>(jj, 32 * p + 4 * g)]);
-                            V4 hi4 = *reinterpret_cast<const V4 *>(&VTs[tidx<C, TM>(jj, 32 * p + 16 + 4 * g)]);
+                            frag aop = tok_frag(Vs, PV{}, p, (tj0 + jt) * 16);
                             if (!hi) {
 #pragma unroll
-                                for (int e = 0; e < 4; ++e) hi4[e] = from_f32<TM>(0.0f);
-                            }
-                            frag aop;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                aop[e] = lo4[e];
-                                aop[4 + e] = hi4[e];
+                                for (int e = 0; e < 4; ++e) aop[4 + e] = from_f32<TM>(0.0f);
                             }
                             oacc[jt] = MF::mma(aop, bop, oacc[jt]);
                         }
@@ -608,7 +579,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                         for (int e = 0; e < 4; ++e) {
 #pragma unroll
                             for (int jt = 0; jt < NTJW; ++jt)
-                                oacc[jt] = MF::mma(VTs[tidx<C, TM>((tj0 + jt) * 16 + n, sb * 16 + 4 * g + e)],
+                                oacc[jt] = MF::mma(Vs[VT::at(sb * 16 + 4 * g + e, (tj0 + jt) * 16 + n)],
                                                    sc[sb][e], oacc[jt]);
                         }
                     }
@@ -633,7 +604,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             if (!RAGGED || rrow < L) {
 #pragma unroll
                 for (int jt = 0; jt < NTJW; ++jt)
-                    st4<TO>(og + (size_t)rrow * dv + (tj0 + jt) * 16 + 4 * g, oacc[jt]);
+                    st4<TO>(og + rrow * dv + (tj0 + jt) * 16 + 4 * g, oacc[jt]);
             }
         };
         auto wave_role = [&](auto w_tag) {
@@ -660,7 +631,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                 break;
         }
 
-        // ---- state update: S <- exp(g_C) S + K^T (w (.) V)
+        // ---- state update: S <- exp(g_C) S + K^T (w (.) V), both operands read
+        // from the row-major tiles with the token index in the K slots.
         if constexpr (DECAYED) {
             const float eg = Tsc[buf];
 #pragma unroll
@@ -671,10 +643,25 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             if (m < tsn) {
                 const int tile = ts0 + m, ti = tile / NTJ, tj = tile % NTJ;
 #pragma unroll
-                for (int ks = 0; ks < NTK; ++ks) {
-                    const int s0 = g * (C / 4) + ks * E;
-                    Sacc[m] = MF::mma(ld_frag<TM>(&KTs[tidx<C, TM>(ti * 16 + n, s0)]),
-                                      ld_frag<TM>(&VW[tidx<C, TM>(tj * 16 + n, s0)]), Sacc[m]);
+                for (int ks = 0; ks < NTK; ++ks)
+                    Sacc[m] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), tok_frag(VW, PV{}, ks, tj * 16), Sacc[m]);
+            }
+        }
+        // ---- normalizer carry: z_next = z_prev + K^T 1 (fp32 accumulators).
+        if constexpr (VAR == V_NORM) {
+            if (wv == ZW) {
+                frag ones;
+                if constexpr (E == 8) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ones[e] = from_f32<TM>(1.0f);
+                } else {
+                    ones = 1.0f;
+                }
+#pragma unroll
+                for (int ti = 0; ti < NTI; ++ti) {
+#pragma unroll
+                    for (int ks = 0; ks < NTK; ++ks) zacc[ti] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), ones, zacc[ti]);
+                    if (n == 0) *reinterpret_cast<f32x4 *>(&Zs[zn + ti * 16 + 4 * g]) = zacc[ti];
                 }
             }
         }
@@ -717,9 +704,12 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         }
     }
     if constexpr (VAR == V_NORM) {
-        // The threads that wrote the last z update read it back: no barrier needed.
-        if (a.z_out && split == 0)
-            for (int i = tid; i < DK; i += NT) a.z_out[(size_t)bh * DK + i] = Zs[(nchunks & 1) * DK + i];
+        if (a.z_out && split == 0 && wv == ZW && n == 0) {
+#pragma unroll
+            for (int ti = 0; ti < NTI; ++ti)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a.z_out[(size_t)bh * DK + ti * 16 + 4 * g + e] = zacc[ti][e];
+        }
     }
 }
 

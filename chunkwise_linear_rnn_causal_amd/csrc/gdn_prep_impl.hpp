@@ -16,8 +16,8 @@
 // forms U = U~ - W S_prev.
 //
 // Layout of the results, in the tensor-core operand type (fp16 for bf16
-// inputs, fp32 for fp32 inputs): W row-major [BH, Lp, DK]; U~ transposed [BH, dv, Lp]
-// (so the serial pass reads four consecutive tokens per lane). Padded tokens
+// inputs, fp32 for fp32 inputs): W row-major [BH, Lp, DK]; U~ row-major
+// [BH, Lp, dv] (the serial pass reads four consecutive columns per lane). Padded tokens
 // (t >= L) have beta = 0 and k = v = 0, which makes their rows of W and U~ zero.
 #pragma once
 
@@ -251,8 +251,9 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
         }
         st4<TM>(wout + (size_t)(rb * 16 + n) * DK + cbk * 16 + 4 * g, d);
     }
-    // U~ tiles D[r][j] = sum_s T[r][s] (beta V)[s][j]; lane holds r = rb*16 + 4g + e.
-    TM *uout = (TM *)a.ut + (size_t)bh * dv * a.Lp + t0;
+    // U~ row-major, from transposed tiles D[j][r] = sum_s (beta V)[s][j] T[r][s];
+    // lane holds r = rb*16 + n and four consecutive columns j = jb*16 + 4g + e.
+    TM *uout = (TM *)a.ut + ((size_t)bh * a.Lp + t0) * dv;
     const int NJB = dv / 16;
     for (int tile = wv; tile < NRB * NJB; tile += NW) {
         const int rb = tile / NJB, jb = tile % NJB;
@@ -260,10 +261,10 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
 #pragma unroll
         for (int ks = 0; ks < NTK; ++ks) {
             const int s0 = g * (C / 4) + ks * E;
-            d = MF::mma(ld_frag<TM>(&To[(rb * 16 + n) * OP + s0]),
-                        ld_frag<TM>(&VTs[tidx<C, TM>(jb * 16 + n, s0)]), d);
+            d = MF::mma(ld_frag<TM>(&VTs[tidx<C, TM>(jb * 16 + n, s0)]),
+                        ld_frag<TM>(&To[(rb * 16 + n) * OP + s0]), d);
         }
-        st4<TM>(uout + (size_t)(jb * 16 + n) * a.Lp + rb * 16 + 4 * g, d);
+        st4<TM>(uout + (size_t)(rb * 16 + n) * dv + jb * 16 + 4 * g, d);
     }
 }
 

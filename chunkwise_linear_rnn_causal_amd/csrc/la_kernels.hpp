@@ -18,7 +18,7 @@ struct ChunkArgs {
     float *s_out;               // [BH, DK, dv] or nullptr
     float *z_out;               // [BH, DK] or nullptr (normalized only)
     const void *w;              // gated delta: W  [BH, Lp, DK] (operand type)
-    const void *ut;             // gated delta: U~ transposed [BH, dv, Lp] (operand type)
+    const void *ut;             // gated delta: U~ [BH, Lp, dv] (operand type)
     int BH, L, Lp, dv, nsplit;  // Lp = ceil(L / C) * C; nsplit = dv / DVT (workgroups per head)
 };
 
