@@ -267,24 +267,30 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         }
     };
 
-    auto load_chunk = [&](int c, auto ragged_tag) {
+    // Loads of chunk c: the log-gates (first, so that the gate tables wait only
+    // for them), the Q/K/V segments of slot m, and the delta-rule W row and U~.
+    auto load_gates = [&](int c, auto ragged_tag) {
         constexpr bool RAGGED = decltype(ragged_tag)::value;
         const int t0 = c * C;
-        auto row = [&](int t) { return RAGGED ? min(t, L - 1) : t; };
-        if constexpr (DECAYED) {  // first: the gate tables wait only for these
+        if constexpr (DECAYED) {
 #pragma unroll
-            for (int p = 0; p < PER; ++p) gpre[p] = gsrc[row(t0 + lane * PER + p)];
+            for (int p = 0; p < PER; ++p) {
+                const int t = t0 + lane * PER + p;
+                gpre[p] = gsrc[RAGGED ? min(t, L - 1) : t];
+            }
         }
-#pragma unroll
-        for (int m = 0; m < NSLOT; ++m) {
-            int kind, r, seg;
-            slot_geom(m, kind, r, seg);
-            const int t = row(t0 + r);
-            const TI *p = kind == 0 ? qg + t * DK : kind == 1 ? kg + t * DK : vg + t * dv;
-            pre[m] = *reinterpret_cast<const uint4 *>(p + seg * EPS);
-        }
+    };
+    auto load_slot = [&](int c, int m, auto ragged_tag) {
+        constexpr bool RAGGED = decltype(ragged_tag)::value;
+        int kind, r, seg;
+        slot_geom(m, kind, r, seg);
+        const int t = RAGGED ? min(c * C + r, L - 1) : c * C + r;
+        const TI *p = kind == 0 ? qg + t * DK : kind == 1 ? kg + t * DK : vg + t * dv;
+        pre[m] = *reinterpret_cast<const uint4 *>(p + seg * EPS);
+    };
+    auto load_wu = [&](int c) {
         if constexpr (VAR == V_GDN) {
-            const int srow = t0 + (wv % NRB) * 16 + n;  // W and U~ have Lp rows: always in range
+            const int srow = c * C + (wv % NRB) * 16 + n;  // W and U~ have Lp rows: always in range
 #pragma unroll
             for (int i = 0; i < NQR; ++i) wpre[i] = ld_raw8<TM>(wg + srow * DK + g * (DK / 4) + 8 * i);
 #pragma unroll
@@ -293,6 +299,12 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                 upre[jt] = ld4<TM>(utg + srow * dv + tj * 16 + 4 * g);
             }
         }
+    };
+    auto load_chunk = [&](int c, auto ragged_tag) {
+        load_gates(c, ragged_tag);
+#pragma unroll
+        for (int m = 0; m < NSLOT; ++m) load_slot(c, m, ragged_tag);
+        load_wu(c);
     };
 
     // Gate tables of chunk c into buffer buf, from the prefetched log-gates.
@@ -383,7 +395,22 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             }
         }
 
-        // ---- stage this chunk's Q, K, V segments row-major (V also scaled by w_s).
+        // ---- stage this chunk's Q, K, V segments row-major (V also scaled by w_s),
+        // refilling each slot with chunk c+1 as soon as it is consumed: the load
+        // issue (bounded by the per-CU address rate) then overlaps the staging
+        // of the other slots instead of stalling every wave after the barrier.
+        auto load_next_slot = [&](int m) {
+            if constexpr (NEXT == 1) {
+                load_slot(c + 1, m, full_t);
+            } else if constexpr (NEXT == 2) {
+                if (c + 1 < nchunks) load_slot(c + 1, m, ragged_t);
+            }
+        };
+        if constexpr (NEXT == 1) {
+            load_gates(c + 1, full_t);
+        } else if constexpr (NEXT == 2) {
+            if (c + 1 < nchunks) load_gates(c + 1, ragged_t);
+        }
 #pragma unroll
         for (int m = 0; m < NSLOT; ++m) {
             if (NW * m + NW <= NI || wv + NW * m < NI) {
@@ -424,10 +451,12 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                     }
                 }
             }
+            load_next_slot(m);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
-        // Delta rule: this chunk's W row and U~ as operands (the prefetch
-        // registers are refilled right after the barrier).
+        // Delta rule: this chunk's W row and U~ as operands; their prefetch
+        // registers are then refilled with chunk c+1.
         frag wf[VAR == V_GDN ? NKS : 1];
         f32x4 ucur[VAR == V_GDN ? NTJW : 1];
         if constexpr (VAR == V_GDN) {
@@ -444,17 +473,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             }
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) ucur[jt] = upre[jt];
-        }
-        __syncthreads();  // staged tiles and STs visible
-
-        if constexpr (NEXT == 1) {
-            load_chunk(c + 1, full_t);
-        } else if constexpr (NEXT == 2) {
-            if (c + 1 < nchunks) load_chunk(c + 1, ragged_t);
+            if constexpr (NEXT == 1) {
+                load_wu(c + 1);
+            } else if constexpr (NEXT == 2) {
+                if (c + 1 < nchunks) load_wu(c + 1);
+            }
         }
         // Keep the prefetch here: the scheduler would otherwise sink the loads
         // towards their use in the next chunk and expose their latency.
         __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();  // staged tiles and STs visible
 
         // ---- gated delta rule: U = U~ - W S_prev for this wave's 16 rows and
         // column tiles, computed transposed, D[j][s] = sum_i S[i][j] (-W[s][i]),
