@@ -84,14 +84,19 @@ __device__ inline f16x8 tr_frag(const f16 *X, int r0, int col0, int lane) {
 // ---------------------------------------------------------------------------
 // Contiguous ranges of state tiles per wave, filled greedily so that waves with
 // fewer score tiles take more state tiles.
+// Waves w and w + 4 of a workgroup share a SIMD, so with C/8 waves the second
+// half of the value columns of row block rb goes to wave 2*NRB - 1 - rb: every
+// SIMD then carries one light and one heavy row block.
 template <int NW, int NRB> struct Roles {
     static constexpr int MODE = (NW == NRB) ? 0 : (NW == 2 * NRB) ? 1 : (2 * NW == NRB) ? 2 : -1;
     static_assert(MODE >= 0, "wave count must be C/16, C/8 or C/32");
     static constexpr int RBW = MODE == 2 ? 2 : 1;
-    static constexpr int rb(int w, int i) { return MODE == 2 ? (i == 0 ? w : NRB - 1 - w) : (w % NRB); }
+    static constexpr int rb(int w, int i) {
+        return MODE == 2 ? (i == 0 ? w : NRB - 1 - w) : MODE == 1 ? (w < NRB ? w : 2 * NRB - 1 - w) : w;
+    }
     static constexpr int half(int w) { return MODE == 1 ? w / NRB : 0; }
     // relative score work of wave w (16 x 16 score tiles)
-    static constexpr int score_tiles(int w) { return MODE == 2 ? NRB + 1 : (w % NRB) + 1; }
+    static constexpr int score_tiles(int w) { return MODE == 2 ? NRB + 1 : rb(w, 0) + 1; }
 };
 
 template <int NTT, int NW> struct TileSplit {
@@ -120,6 +125,47 @@ constexpr TileSplit<NTT, NW> make_tile_split(int extra0) {
     return t;
 }
 
+// Compile-time helpers: iterate an integer range, and the staging geometry.
+template <typename F, int... I>
+__device__ __attribute__((always_inline)) inline void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __attribute__((always_inline)) inline void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Staging of one chunk: Q, K (and V) arrive as 16-byte row segments; wave load
+// i covers 64/SEG whole rows of one tensor. Wave w issues loads w, w + NW, ...;
+// waves past the end repeat the last load (so every wave issues the same
+// memory operations and the wait counts stay exact) without staging it.
+template <typename TI, int DK, int DVT, int C, int NW, bool HAS_V>
+struct StageGeo {
+    static constexpr int EPS = 16 / (int)sizeof(TI);   // input elements per segment
+    static constexpr int SEGQ = DK / EPS, SEGV = DVT / EPS;
+    static constexpr int NIQ = C * SEGQ / 64;           // wave loads per chunk for Q (and for K)
+    static constexpr int NIV = HAS_V ? C * SEGV / 64 : 0;
+    static constexpr int NI = 2 * NIQ + NIV;
+    static constexpr int NSLOT = (NI + NW - 1) / NW;
+    static_assert(64 % SEGQ == 0 && (!HAS_V || 64 % SEGV == 0) && NIQ * 64 == C * SEGQ &&
+                  NIV * 64 == (HAS_V ? C * SEGV : 0), "staging geometry");
+    struct Slot {
+        bool real;  // staged (false: a repeated load only)
+        int kind;   // 0 Q, 1 K, 2 V
+        int ii;     // wave load index within the tensor
+        int seg;    // segments per row
+        int rpi;    // rows per wave load
+    };
+    static constexpr Slot slot(int w, int m) {
+        int i = w + NW * m;
+        const bool real = i < NI;
+        if (!real) i = NI - 1;
+        const int kind = i < NIQ ? 0 : (i < 2 * NIQ ? 1 : 2);
+        const int ii = kind == 2 ? i - 2 * NIQ : i - kind * NIQ;
+        const int seg = kind == 2 ? SEGV : SEGQ;
+        return Slot{real, kind, ii, seg, 64 / seg};
+    }
+};
+
 template <int VAR, typename TM, int DK, int DVT, int C>
 struct ChunkCfg {
     static constexpr bool DECAYED = (VAR == V_DECAY || VAR == V_GDN);
@@ -128,6 +174,19 @@ struct ChunkCfg {
     using QT = RowTile<TM, DK, 8>;                        // Q: operand reads only
     using KT = RowTile<TM, DK, 16>;                       // K: operand and transpose reads
     using VT = RowTile<TM, DVT, DVT == 16 ? 0 : 16>;      // V, wV: transpose reads
+    // one set of tiles (Q, K, V, wV, S_prev^T), in elements
+    static constexpr int OQ = 0;
+    static constexpr int OK = OQ + C * QT::P;
+    static constexpr int OV = OK + C * KT::P;
+    static constexpr int OVW = OV + C * VT::P;
+    static constexpr int OS = OVW + (DECAYED ? C * VT::P : 0);
+    static constexpr int SET = OS + DVT * KP;
+    // Double buffering: chunk c+1 is staged into a second set of tiles while
+    // chunk c is computed, with one barrier per chunk; used when both sets fit
+    // in LDS (otherwise chunk c is staged between two barriers).
+    static constexpr bool DB = 2 * SET * sizeof(TM) + 4096 <= 160 * 1024;
+    static constexpr int NB = DB ? 2 : 1;   // tile sets
+    static constexpr int NTB = DB ? 3 : 2;  // gate-table buffers (chunk c uses buffer c % NTB)
 };
 
 // TI: input storage type (bf16 or fp32); TO: output type (fp32 or bf16); the
@@ -139,15 +198,18 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     using MF = Mfma<TM>;
     using frag = typename MF::frag;
     using Cfg = ChunkCfg<VAR, TM, DK, DVT, C>;
-    using QT = typename Cfg::QT;          // Q tile
-    using KT = typename Cfg::KT;          // K tile
-    using VT = typename Cfg::VT;          // V (or U) tiles
+    using QT = typename Cfg::QT;
+    using KT = typename Cfg::KT;
+    using VT = typename Cfg::VT;
+    using Geo = StageGeo<TI, DK, DVT, C, NW, VAR != V_GDN>;
     constexpr bool H = sizeof(TM) == 2;
     constexpr int NT = NW * 64;           // threads
     constexpr int E = MF::E;
     constexpr int NRB = C / 16;           // 16-row blocks per chunk
     using R = Roles<NW, NRB>;
     constexpr bool DECAYED = Cfg::DECAYED;
+    constexpr bool DB = Cfg::DB;
+    constexpr int NTB = Cfg::NTB;
     constexpr int KP = Cfg::KP;
     constexpr int NTI = DK / 16, NTJ = DVT / 16;
     constexpr int NTJW = R::MODE == 1 ? NTJ / 2 : NTJ;  // output column tiles per wave
@@ -155,32 +217,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     constexpr int NTK = C / (4 * E);      // k-steps over tokens
     constexpr int PER = C / 64;           // tokens per lane in the gate scan
     constexpr int NQR = DK / 32;          // 8-element runs of one lane's channels (DK/4)
-    // Staging: 16-byte row segments; one wave load covers 64/SEG whole rows.
-    constexpr int EPS = 16 / (int)sizeof(TI);              // input elements per segment
-    constexpr int SEGQ = DK / EPS, SEGV = DVT / EPS;        // segments per row
-    constexpr int NIQ = C * SEGQ / 64;                      // wave loads per chunk for Q (and K)
-    constexpr int NIV = (VAR == V_GDN) ? 0 : C * SEGV / 64;
-    constexpr int NI = 2 * NIQ + NIV;
-    constexpr int NSLOT = (NI + NW - 1) / NW;
-    static_assert(64 % SEGQ == 0 && (VAR == V_GDN || 64 % SEGV == 0) && C * SEGQ % 64 == 0 &&
-                  C * SEGV % 64 == 0, "staging geometry");
+    constexpr int EPS = Geo::EPS;
+    constexpr int NSLOT = Geo::NSLOT;
     constexpr int ZW = 0;                 // wave that carries the normalizer
     constexpr auto TS = make_tile_split<NTI * NTJ, NW, NRB>(VAR == V_NORM ? NTI : 0);
     constexpr int NTS = TS.maxcnt;        // state tiles per wave (at most)
     static_assert(NTJW >= 1 && (R::MODE != 1 || NTJ % 2 == 0), "value slice too narrow for the roles");
     static_assert(VAR != V_GDN || (R::MODE <= 1 && NRB == 4), "delta rule: one U row block per wave (pair)");
 
-    __shared__ __attribute__((aligned(16))) TM Qs[C * QT::P];
-    __shared__ __attribute__((aligned(16))) TM Ks[C * KT::P];
-    __shared__ __attribute__((aligned(16))) TM Vs[C * VT::P];
-    __shared__ __attribute__((aligned(16))) TM VWs[DECAYED ? C * VT::P : 1];  // V (or U) scaled by w_s
-    __shared__ __attribute__((aligned(16))) TM STs[DVT * KP];
-    // Gate tables per buffer: [0] G_s, [1] exp(G_s), [2] w_s = exp(g_C - G_s),
-    // [3] exp(G_{end of s's 16-block} - G_s); Tsc = exp(g_C).
-    __shared__ __attribute__((aligned(16))) float Tg[DECAYED ? 2 * 4 * C : 1];
-    __shared__ float Tsc[DECAYED ? 2 : 1];
+    // Tile sets: [set][Q | K | V | wV | S_prev^T]. Gate tables per buffer:
+    // [0] G_s, [1] exp(G_s), [2] w_s = exp(g_C - G_s), [3] exp(G_{end of s's
+    // 16-block} - G_s); Tsc = exp(g_C).
+    __shared__ __attribute__((aligned(16))) TM Tiles[Cfg::NB * Cfg::SET];
+    __shared__ __attribute__((aligned(16))) float Tg[DECAYED ? NTB * 4 * C : 1];
+    __shared__ float Tsc[DECAYED ? NTB : 1];
     __shared__ __attribute__((aligned(16))) float Zs[VAR == V_NORM ? 2 * DK : 1];
-    TM *VW = DECAYED ? VWs : Vs;
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -188,14 +239,6 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     const int bh = vid / a.nsplit, split = vid - bh * a.nsplit;
     const int j0 = split * DVT;
     const int L = a.L, dv = a.dv;
-    int ts0 = 0, tsn = 0;  // this wave's state tiles (selected without indexing a table)
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        if (wv == w) {
-            ts0 = TS.start[w];
-            tsn = TS.cnt[w];
-        }
-    }
 
     // Per-head bases; offsets inside a head are 32-bit (L * d < 2^31 is checked
     // by the ABI layer).
@@ -207,8 +250,17 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     const TM *wg = (VAR == V_GDN) ? (const TM *)a.w + (size_t)bh * a.Lp * DK : nullptr;
     const TM *utg = (VAR == V_GDN) ? (const TM *)a.ut + (size_t)bh * a.Lp * dv + j0 : nullptr;
 
-    // ---- initial state slice in accumulator layout: lane (g, n) of tile (ti, tj)
-    // holds S[ti*16 + 4g + e][j0 + tj*16 + n].
+    // ---- this wave's state tiles (a contiguous range of tile ids ti*NTJ + tj),
+    // in accumulator layout: lane (g, n) of tile (ti, tj) holds
+    // S[ti*16 + 4g + e][j0 + tj*16 + n].
+    int ts0 = 0, tsn = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        if (wv == w) {
+            ts0 = TS.start[w];
+            tsn = TS.cnt[w];
+        }
+    }
     f32x4 Sacc[NTS];
 #pragma unroll
     for (int m = 0; m < NTS; ++m) {
@@ -236,59 +288,51 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // head and the per-chunk waits can be exact (leaving output stores in flight).
     __builtin_amdgcn_s_waitcnt(0);
 
-    // ---- registers of the next chunk, loaded one chunk ahead so that global
-    // latency overlaps the current chunk's math. Wave load i (i < NI) covers
-    // rows i*64/SEG .. of Q, K or V; wave w issues loads w, w + NW, ... and waves
-    // past the end repeat the last load, so every memory operation of a full
-    // chunk is unconditional and the compiler's wait counts stay exact. Only the
-    // ragged last chunk clamps rows, which are zeroed when staged.
+    // ---- registers of the next chunk(s): loads are issued one chunk ahead of
+    // the staging that consumes them, so global latency overlaps the math.
     uint4 pre[NSLOT];
     float gpre[PER];
     Raw8<TM> wpre[NQR];           // gated delta: W row of this wave's U row block
     f32x4 upre[NTJW];             // gated delta: U~ of this wave's U tiles (transposed layout)
     const float *gsrc = lgg ? lgg : reinterpret_cast<const float *>(qg);
+    // per-lane byte offsets of a slot's segment within its row block (the row
+    // block's start is uniform, so full-chunk loads use a scalar base)
+    const uint32_t off_qk = ((lane / Geo::SEGQ) * DK + (lane % Geo::SEGQ) * EPS) * (uint32_t)sizeof(TI);
+    const uint32_t off_v = ((lane / Geo::SEGV) * dv + (lane % Geo::SEGV) * EPS) * (uint32_t)sizeof(TI);
 
-    // Geometry of slot m of this wave: tensor (0 Q, 1 K, 2 V), chunk row, segment.
-    auto slot_geom = [&](int m, int &kind, int &row, int &seg) {
-        int i = wv + NW * m;
-        i = i < NI ? i : NI - 1;
-        if (i < NIQ) {
-            kind = 0;
-            row = i * (64 / SEGQ) + lane / SEGQ;
-            seg = lane % SEGQ;
-        } else if (i < 2 * NIQ) {
-            kind = 1;
-            row = (i - NIQ) * (64 / SEGQ) + lane / SEGQ;
-            seg = lane % SEGQ;
-        } else {
-            kind = 2;
-            row = (i - 2 * NIQ) * (64 / SEGV) + lane / SEGV;
-            seg = lane % SEGV;
-        }
-    };
+    const int nchunks = (L + C - 1) / C;
+    const int nfull = L / C;  // chunks with all C rows valid
+    using PK = std::integral_constant<int, KT::P>;
+    using PV = std::integral_constant<int, VT::P>;
 
-    // Loads of chunk c: the log-gates (first, so that the gate tables wait only
-    // for them), the Q/K/V segments of slot m, and the delta-rule W row and U~.
-    auto load_gates = [&](int c, auto ragged_tag) {
-        constexpr bool RAGGED = decltype(ragged_tag)::value;
-        const int t0 = c * C;
+    // Loads of chunk c: the log-gates, slot M of wave W, and the delta-rule W row
+    // and U~. FULL: all rows of chunk c are valid (scalar base + lane offset);
+    // otherwise rows are clamped to L - 1 and zeroed when staged.
+    auto load_gates = [&](int c, auto full_tag) __attribute__((always_inline)) {
+        constexpr bool FULL = decltype(full_tag)::value;
         if constexpr (DECAYED) {
 #pragma unroll
             for (int p = 0; p < PER; ++p) {
-                const int t = t0 + lane * PER + p;
-                gpre[p] = gsrc[RAGGED ? min(t, L - 1) : t];
+                const int t = c * C + lane * PER + p;
+                gpre[p] = gsrc[FULL ? t : min(t, L - 1)];
             }
         }
     };
-    auto load_slot = [&](int c, int m, auto ragged_tag) {
-        constexpr bool RAGGED = decltype(ragged_tag)::value;
-        int kind, r, seg;
-        slot_geom(m, kind, r, seg);
-        const int t = RAGGED ? min(c * C + r, L - 1) : c * C + r;
-        const TI *p = kind == 0 ? qg + t * DK : kind == 1 ? kg + t * DK : vg + t * dv;
-        pre[m] = *reinterpret_cast<const uint4 *>(p + seg * EPS);
+    auto load_slot = [&](auto w_tag, auto m_tag, int c, auto full_tag) __attribute__((always_inline)) {
+        constexpr auto S = Geo::slot(decltype(w_tag)::value, decltype(m_tag)::value);
+        constexpr int M = decltype(m_tag)::value;
+        constexpr bool FULL = decltype(full_tag)::value;
+        const TI *tb = S.kind == 0 ? qg : (S.kind == 1 ? kg : vg);
+        const int pitch = S.kind == 2 ? dv : DK;
+        if constexpr (FULL) {
+            const char *base = reinterpret_cast<const char *>(tb + (size_t)(c * C + S.ii * S.rpi) * pitch);
+            pre[M] = *reinterpret_cast<const uint4 *>(base + (S.kind == 2 ? off_v : off_qk));
+        } else {
+            const int t = min(c * C + S.ii * S.rpi + lane / S.seg, L - 1);
+            pre[M] = *reinterpret_cast<const uint4 *>(tb + t * pitch + (lane % S.seg) * EPS);
+        }
     };
-    auto load_wu = [&](int c) {
+    auto load_wu = [&](int c) __attribute__((always_inline)) {
         if constexpr (VAR == V_GDN) {
             const int srow = c * C + (wv % NRB) * 16 + n;  // W and U~ have Lp rows: always in range
 #pragma unroll
@@ -300,16 +344,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             }
         }
     };
-    auto load_chunk = [&](int c, auto ragged_tag) {
-        load_gates(c, ragged_tag);
-#pragma unroll
-        for (int m = 0; m < NSLOT; ++m) load_slot(c, m, ragged_tag);
-        load_wu(c);
-    };
 
     // Gate tables of chunk c into buffer buf, from the prefetched log-gates.
-    // Called by wave 0 only (wave-uniform), one chunk ahead of its use.
-    auto gate_tables = [&](int c, int buf) {
+    // Called by wave 0 only (wave-uniform), ahead of the chunk's staging.
+    auto gate_tables = [&](int c, int buf) __attribute__((always_inline)) {
         const int t0 = c * C;
         float *T = Tg + buf * 4 * C;
         if constexpr (PER == 1) {
@@ -357,7 +395,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // k-step ks over tokens. fp16: lane group g carries tokens 32 ks + 4g + (0..3)
     // and 32 ks + 16 + 4g + (0..3), the same slots as the score tiles 2 ks and
     // 2 ks + 1 hold in accumulator layout; fp32: token 4 ks + g.
-    auto tok_frag = [&](const TM *X, auto p_tag, int ks, int col0) -> frag {
+    auto tok_frag = [&](const TM *X, auto p_tag, int ks, int col0) __attribute__((always_inline)) -> frag {
         constexpr int P = decltype(p_tag)::value;
         if constexpr (H) {
             return tr_frag<P>(X, 32 * ks + 4 * g, col0, lane);
@@ -366,99 +404,170 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         }
     };
 
-    const int nchunks = (L + C - 1) / C;
-    const int nfull = L / C;  // chunks with all C rows valid
-    const std::true_type ragged_t{};
-    const std::false_type full_t{};
-    using NextNone = std::integral_constant<int, 0>;
-    using NextFull = std::integral_constant<int, 1>;
-    using NextTail = std::integral_constant<int, 2>;  // ragged next chunk if L % C != 0
-    using PK = std::integral_constant<int, KT::P>;
-    using PV = std::integral_constant<int, VT::P>;
+    // Run fn(W) with W = this wave's index as a compile-time constant.
+    auto for_wave = [&](auto &&fn) __attribute__((always_inline)) {
+        switch (wv) {
+            case 0: fn(std::integral_constant<int, 0>{}); break;
+            case 1: fn(std::integral_constant<int, 1 % NW>{}); break;
+            case 2: fn(std::integral_constant<int, 2 % NW>{}); break;
+            case 3: fn(std::integral_constant<int, 3 % NW>{}); break;
+            default:
+                if constexpr (NW == 8) {
+                    switch (wv) {
+                        case 4: fn(std::integral_constant<int, 4>{}); break;
+                        case 5: fn(std::integral_constant<int, 5>{}); break;
+                        case 6: fn(std::integral_constant<int, 6>{}); break;
+                        default: fn(std::integral_constant<int, 7>{}); break;
+                    }
+                }
+                break;
+        }
+    };
 
-    // One chunk. ragged_tag: this chunk has rows past L. next_tag: which loads to
-    // issue for chunk c + 1.
-    auto chunk_body = [&](int c, auto ragged_tag, auto next_tag) {
-        constexpr bool RAGGED = decltype(ragged_tag)::value;
-        constexpr int NEXT = decltype(next_tag)::value;
-        const int t0 = c * C;
-        const int buf = c & 1;
-        const float *T = Tg + buf * 4 * C;
-        __syncthreads();  // previous chunk done with every tile; gate tables visible
+    // ---- per-wave pieces of a chunk; W (the wave) is a compile-time constant, so
+    // every tile, slot and row index below folds into address immediates.
 
-        // S_prev, transposed, in the operand type: STs[j][i].
+    // Stage slot M of chunk cs (in registers) into tile set X: convert to the
+    // operand type and write row-major; V also scaled by w_s of chunk cs.
+    // CHECK: rows past L are zeroed.
+    auto stage_slot = [&](auto w_tag, auto m_tag, int cs, TM *X, auto check_tag) __attribute__((always_inline)) {
+        constexpr auto S = Geo::slot(decltype(w_tag)::value, decltype(m_tag)::value);
+        constexpr int M = decltype(m_tag)::value;
+        constexpr bool CHECK = decltype(check_tag)::value;
+        if constexpr (S.real) {
+            const int r = S.ii * S.rpi + lane / S.seg, seg = lane % S.seg;
+            const bool valid = !CHECK || cs * C + r < L;
+            const uint32_t w4[4] = {pre[M].x, pre[M].y, pre[M].z, pre[M].w};
+            if constexpr (H) {
+                f16x8 h;
 #pragma unroll
-        for (int m = 0; m < NTS; ++m) {
-            if (m < tsn) {
-                const int tile = ts0 + m, ti = tile / NTJ, tj = tile % NTJ;
-                st4<TM>(&STs[(tj * 16 + n) * KP + ti * 16 + 4 * g], Sacc[m]);
+                for (int i = 0; i < 4; ++i) {
+                    h[2 * i] = (f16)(valid ? bf16_lo(w4[i]) : 0.f);
+                    h[2 * i + 1] = (f16)(valid ? bf16_hi(w4[i]) : 0.f);
+                }
+                if constexpr (S.kind == 2) {
+                    *reinterpret_cast<f16x8 *>(&X[Cfg::OV + VT::at(r, seg * 8)]) = h;
+                    if constexpr (DECAYED) {
+                        const f16 w = (f16)Tg[(cs % NTB) * 4 * C + 2 * C + r];
+                        *reinterpret_cast<f16x8 *>(&X[Cfg::OVW + VT::at(r, seg * 8)]) = h * w;
+                    }
+                } else if constexpr (S.kind == 1) {
+                    *reinterpret_cast<f16x8 *>(&X[Cfg::OK + KT::at(r, seg * 8)]) = h;
+                } else {
+                    *reinterpret_cast<f16x8 *>(&X[Cfg::OQ + QT::at(r, seg * 8)]) = h;
+                }
+            } else {
+                f32x4 x;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = valid ? __uint_as_float(w4[i]) : 0.f;
+                if constexpr (S.kind == 2) {
+                    *reinterpret_cast<f32x4 *>(&X[Cfg::OV + VT::at(r, seg * 4)]) = x;
+                    if constexpr (DECAYED)
+                        *reinterpret_cast<f32x4 *>(&X[Cfg::OVW + VT::at(r, seg * 4)]) =
+                            x * Tg[(cs % NTB) * 4 * C + 2 * C + r];
+                } else if constexpr (S.kind == 1) {
+                    *reinterpret_cast<f32x4 *>(&X[Cfg::OK + KT::at(r, seg * 4)]) = x;
+                } else {
+                    *reinterpret_cast<f32x4 *>(&X[Cfg::OQ + QT::at(r, seg * 4)]) = x;
+                }
             }
         }
+    };
 
-        // ---- stage this chunk's Q, K, V segments row-major (V also scaled by w_s),
-        // refilling each slot with chunk c+1 as soon as it is consumed: the load
-        // issue (bounded by the per-CU address rate) then overlaps the staging
-        // of the other slots instead of stalling every wave after the barrier.
-        auto load_next_slot = [&](int m) {
-            if constexpr (NEXT == 1) {
-                load_slot(c + 1, m, full_t);
-            } else if constexpr (NEXT == 2) {
-                if (c + 1 < nchunks) load_slot(c + 1, m, ragged_t);
-            }
-        };
-        if constexpr (NEXT == 1) {
-            load_gates(c + 1, full_t);
-        } else if constexpr (NEXT == 2) {
-            if (c + 1 < nchunks) load_gates(c + 1, ragged_t);
-        }
-#pragma unroll
-        for (int m = 0; m < NSLOT; ++m) {
-            if (NW * m + NW <= NI || wv + NW * m < NI) {
-                int kind, r, seg;
-                slot_geom(m, kind, r, seg);
-                const bool valid = !RAGGED || t0 + r < L;
-                const uint32_t w4[4] = {pre[m].x, pre[m].y, pre[m].z, pre[m].w};
+    // Slot M of this wave in common code (one code path for all waves): the
+    // slot's tensor must be the same for every wave; the wave's row offset is
+    // then a scalar. Otherwise the per-wave versions above are dispatched.
+    auto slot_uniform = [&](auto m_tag) __attribute__((always_inline)) {
+        constexpr int M = decltype(m_tag)::value;
+        constexpr auto S0 = Geo::slot(0, M);
+        constexpr auto S1 = Geo::slot(NW - 1, M);
+        return std::bool_constant<S0.kind == S1.kind>{};
+    };
+    auto stage_any = [&](auto m_tag, int cs, TM *X, auto check_tag) __attribute__((always_inline)) {
+        constexpr int M = decltype(m_tag)::value;
+        constexpr bool CHECK = decltype(check_tag)::value;
+        if constexpr (decltype(slot_uniform(m_tag))::value) {
+            constexpr auto S = Geo::slot(0, M);
+            const int i = wv + NW * M;
+            if (i < Geo::NI) {
+                const int ii = S.kind == 2 ? i - 2 * Geo::NIQ : i - S.kind * Geo::NIQ;
+                const int r = ii * S.rpi + lane / S.seg, seg = lane % S.seg;
+                const bool valid = !CHECK || cs * C + r < L;
+                const uint32_t w4[4] = {pre[M].x, pre[M].y, pre[M].z, pre[M].w};
                 if constexpr (H) {
                     f16x8 h;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        h[2 * i] = (f16)(valid ? bf16_lo(w4[i]) : 0.f);
-                        h[2 * i + 1] = (f16)(valid ? bf16_hi(w4[i]) : 0.f);
+                    for (int q = 0; q < 4; ++q) {
+                        h[2 * q] = (f16)(valid ? bf16_lo(w4[q]) : 0.f);
+                        h[2 * q + 1] = (f16)(valid ? bf16_hi(w4[q]) : 0.f);
                     }
-                    if (kind == 2) {
-                        *reinterpret_cast<f16x8 *>(&Vs[VT::at(r, seg * 8)]) = h;
+                    if constexpr (S.kind == 2) {
+                        *reinterpret_cast<f16x8 *>(&X[Cfg::OV + VT::at(r, seg * 8)]) = h;
                         if constexpr (DECAYED) {
-                            const f16 w = (f16)T[2 * C + r];
-                            *reinterpret_cast<f16x8 *>(&VWs[VT::at(r, seg * 8)]) = h * w;
+                            const f16 w = (f16)Tg[(cs % NTB) * 4 * C + 2 * C + r];
+                            *reinterpret_cast<f16x8 *>(&X[Cfg::OVW + VT::at(r, seg * 8)]) = h * w;
                         }
-                    } else if (kind == 1) {
-                        *reinterpret_cast<f16x8 *>(&Ks[KT::at(r, seg * 8)]) = h;
+                    } else if constexpr (S.kind == 1) {
+                        *reinterpret_cast<f16x8 *>(&X[Cfg::OK + KT::at(r, seg * 8)]) = h;
                     } else {
-                        *reinterpret_cast<f16x8 *>(&Qs[QT::at(r, seg * 8)]) = h;
+                        *reinterpret_cast<f16x8 *>(&X[Cfg::OQ + QT::at(r, seg * 8)]) = h;
                     }
                 } else {
                     f32x4 x;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) x[i] = valid ? __uint_as_float(w4[i]) : 0.f;
-                    if (kind == 2) {
-                        *reinterpret_cast<f32x4 *>(&Vs[VT::at(r, seg * 4)]) = x;
+                    for (int q = 0; q < 4; ++q) x[q] = valid ? __uint_as_float(w4[q]) : 0.f;
+                    if constexpr (S.kind == 2) {
+                        *reinterpret_cast<f32x4 *>(&X[Cfg::OV + VT::at(r, seg * 4)]) = x;
                         if constexpr (DECAYED)
-                            *reinterpret_cast<f32x4 *>(&VWs[VT::at(r, seg * 4)]) = x * T[2 * C + r];
-                    } else if (kind == 1) {
-                        *reinterpret_cast<f32x4 *>(&Ks[KT::at(r, seg * 4)]) = x;
+                            *reinterpret_cast<f32x4 *>(&X[Cfg::OVW + VT::at(r, seg * 4)]) =
+                                x * Tg[(cs % NTB) * 4 * C + 2 * C + r];
+                    } else if constexpr (S.kind == 1) {
+                        *reinterpret_cast<f32x4 *>(&X[Cfg::OK + KT::at(r, seg * 4)]) = x;
                     } else {
-                        *reinterpret_cast<f32x4 *>(&Qs[QT::at(r, seg * 4)]) = x;
+                        *reinterpret_cast<f32x4 *>(&X[Cfg::OQ + QT::at(r, seg * 4)]) = x;
                     }
                 }
             }
-            load_next_slot(m);
-            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            for_wave([&](auto w_tag) __attribute__((always_inline)) { stage_slot(w_tag, m_tag, cs, X, check_tag); });
         }
+    };
+    auto load_any = [&](auto m_tag, int c, auto full_tag) __attribute__((always_inline)) {
+        constexpr int M = decltype(m_tag)::value;
+        constexpr bool FULL = decltype(full_tag)::value;
+        if constexpr (decltype(slot_uniform(m_tag))::value) {
+            constexpr auto S = Geo::slot(0, M);
+            int i = wv + NW * M;
+            i = i < Geo::NI ? i : Geo::NI - 1;  // repeat the last load past the end
+            const int ii = S.kind == 2 ? i - 2 * Geo::NIQ : i - S.kind * Geo::NIQ;
+            const TI *tb = S.kind == 0 ? qg : (S.kind == 1 ? kg : vg);
+            const int pitch = S.kind == 2 ? dv : DK;
+            if constexpr (FULL) {
+                const char *base = reinterpret_cast<const char *>(tb + (size_t)(c * C + ii * S.rpi) * pitch);
+                pre[M] = *reinterpret_cast<const uint4 *>(base + (S.kind == 2 ? off_v : off_qk));
+            } else {
+                const int t = min(c * C + ii * S.rpi + lane / S.seg, L - 1);
+                pre[M] = *reinterpret_cast<const uint4 *>(tb + t * pitch + (lane % S.seg) * EPS);
+            }
+        } else {
+            for_wave([&](auto w_tag) __attribute__((always_inline)) { load_slot(w_tag, m_tag, c, full_tag); });
+        }
+    };
 
-        // Delta rule: this chunk's W row and U~ as operands; their prefetch
-        // registers are then refilled with chunk c+1.
-        frag wf[VAR == V_GDN ? NKS : 1];
-        f32x4 ucur[VAR == V_GDN ? NTJW : 1];
+    // S_prev, transposed, in the operand type: X[OS + j*KP + i].
+    auto write_sts = [&](auto w_tag, TM *X) __attribute__((always_inline)) {
+        constexpr int W = decltype(w_tag)::value;
+#pragma unroll
+        for (int m = 0; m < TS.cnt[W]; ++m) {
+            const int tile = TS.start[W] + m, ti = tile / NTJ, tj = tile % NTJ;
+            st4<TM>(&X[Cfg::OS + (tj * 16 + n) * KP + ti * 16 + 4 * g], Sacc[m]);
+        }
+    };
+
+    // Delta rule: this chunk's W row and U~ as operands, from the prefetch
+    // registers (which are then free for the next chunk).
+    auto take_wu = [&](frag (&wf)[VAR == V_GDN ? NKS : 1],
+                       f32x4 (&ucur)[VAR == V_GDN ? NTJW : 1]) __attribute__((always_inline)) {
         if constexpr (VAR == V_GDN) {
 #pragma unroll
             for (int i = 0; i < NQR; ++i) {
@@ -473,22 +582,15 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             }
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) ucur[jt] = upre[jt];
-            if constexpr (NEXT == 1) {
-                load_wu(c + 1);
-            } else if constexpr (NEXT == 2) {
-                if (c + 1 < nchunks) load_wu(c + 1);
-            }
         }
-        // Keep the prefetch here: the scheduler would otherwise sink the loads
-        // towards their use in the next chunk and expose their latency.
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();  // staged tiles and STs visible
+    };
 
-        // ---- gated delta rule: U = U~ - W S_prev for this wave's 16 rows and
-        // column tiles, computed transposed, D[j][s] = sum_i S[i][j] (-W[s][i]),
-        // so that lane (g, n) holds U[s = ub*16 + n][j = jj + 4g + e] and writes
-        // four consecutive columns of the row-major V tile (and of the w_s-scaled
-        // copy for the state update).
+    // Gated delta rule: U = U~ - W S_prev for this wave's 16 rows and column
+    // tiles, computed transposed, D[j][s] = sum_i S[i][j] (-W[s][i]), so that lane
+    // (g, n) holds U[s = ub*16 + n][j = jj + 4g + e] and writes four consecutive
+    // columns of the row-major V tile (and of the w_s-scaled copy).
+    auto gdn_u = [&](TM *X, const float *T, const frag (&wf)[VAR == V_GDN ? NKS : 1],
+                     const f32x4 (&ucur)[VAR == V_GDN ? NTJW : 1]) __attribute__((always_inline)) {
         if constexpr (VAR == V_GDN) {
             const int ub = wv % NRB;
             const int s = ub * 16 + n;
@@ -499,226 +601,334 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                 f32x4 acc = ucur[jt];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
-                    acc = MF::mma(ld_frag<TM>(&STs[(jj + n) * KP + g * (DK / 4) + ks * E]), wf[ks], acc);
-                st4<TM>(&Vs[VT::at(s, jj + 4 * g)], acc);
-                st4<TM>(&VWs[VT::at(s, jj + 4 * g)], acc * ws);
+                    acc = MF::mma(ld_frag<TM>(&X[Cfg::OS + (jj + n) * KP + g * (DK / 4) + ks * E]), wf[ks], acc);
+                st4<TM>(&X[Cfg::OV + VT::at(s, jj + 4 * g)], acc);
+                st4<TM>(&X[Cfg::OVW + VT::at(s, jj + 4 * g)], acc * ws);
             }
-            __syncthreads();
-        }
-
-        const int zc = (c & 1) * DK, zn = ((c + 1) & 1) * DK;
-
-        // ---- outputs for one 16-row block and one range of value tiles; both
-        // are compile-time constants so every score tile is straight-line code.
-        auto row_block = [&](auto rb_tag, auto tj_tag) {
-            constexpr int rb = decltype(rb_tag)::value;
-            constexpr int tj0 = decltype(tj_tag)::value;
-            const int rl = rb * 16 + n;   // chunk-local query row of this lane
-            const int rrow = t0 + rl;
-            frag qf[NKS];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) qf[ks] = ld_frag<TM>(&Qs[QT::at(rl, g * (DK / 4) + ks * E)]);
-            const float Gr = DECAYED ? T[rl] : 0.f;
-
-            // inter-chunk term: D[j][r] = exp(G_r) sum_i S[i][j] q_r[i]
-            f32x4 oacc[NTJW];
-#pragma unroll
-            for (int jt = 0; jt < NTJW; ++jt) {
-                const int tj = tj0 + jt;
-                oacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    oacc[jt] = MF::mma(ld_frag<TM>(&STs[(tj * 16 + n) * KP + g * (DK / 4) + ks * E]),
-                                       qf[ks], oacc[jt]);
-            }
-            if constexpr (DECAYED) {
-                const float er = T[C + rl];
-#pragma unroll
-                for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= er;
-            }
-
-            // score tiles D[s][r] = k_s . q_r for key blocks sb <= rb. Off the
-            // diagonal, exp(G_r - G_s) = exp(G_r - G_e) exp(G_e - G_s) with e the
-            // last token of block sb: both factors <= 1, so no overflow for any
-            // gates, and one exp per tile.
-            f32x4 sc[NRB];
-            float rowsum = 0.f;
-#pragma unroll
-            for (int sb = 0; sb < NRB; ++sb) {
-                sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (sb <= rb) {
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks)
-                        sc[sb] = MF::mma(ld_frag<TM>(&Ks[KT::at(sb * 16 + n, g * (DK / 4) + ks * E)]),
-                                         qf[ks], sc[sb]);
-                    if (sb == rb) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int sl = sb * 16 + 4 * g + e;
-                            float x = sc[sb][e];
-                            if constexpr (DECAYED) x *= __expf(Gr - T[sl]);
-                            sc[sb][e] = (sl > rl) ? 0.f : x;
-                        }
-                    } else if constexpr (DECAYED) {
-                        const float fr = __expf(Gr - T[sb * 16 + 15]);
-                        const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&T[3 * C + sb * 16 + 4 * g]);
-                        sc[sb] *= fr * b4;
-                    }
-                    if constexpr (VAR == V_NORM) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            sc[sb][e] = to_f32<TM>(from_f32<TM>(sc[sb][e]));
-                            rowsum += sc[sb][e];
-                        }
-                    }
-                }
-            }
-
-            // intra-chunk term: D[j][r] += sum_s V[s][j] A[r][s]; the V^T operand
-            // holds the tokens of the two score tiles 2p, 2p+1 that lane group g
-            // carries: s = 32p + 4g + (0..3) and 32p + 16 + 4g + (0..3).
-            if constexpr (E == 8) {
-#pragma unroll
-                for (int p = 0; p < NRB / 2; ++p) {
-                    if (2 * p <= rb) {
-                        frag bop;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            bop[e] = from_f32<TM>(sc[2 * p][e]);
-                            bop[4 + e] = from_f32<TM>(sc[2 * p + 1][e]);
-                        }
-                        const bool hi = (2 * p + 1 <= rb);
-#pragma unroll
-                        for (int jt = 0; jt < NTJW; ++jt) {
-                            frag aop = tok_frag(Vs, PV{}, p, (tj0 + jt) * 16);
-                            if (!hi) {
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) aop[4 + e] = from_f32<TM>(0.0f);
-                            }
-                            oacc[jt] = MF::mma(aop, bop, oacc[jt]);
-                        }
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int sb = 0; sb < NRB; ++sb) {
-                    if (sb <= rb) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-#pragma unroll
-                            for (int jt = 0; jt < NTJW; ++jt)
-                                oacc[jt] = MF::mma(Vs[VT::at(sb * 16 + 4 * g + e, (tj0 + jt) * 16 + n)],
-                                                   sc[sb][e], oacc[jt]);
-                        }
-                    }
-                }
-            }
-
-            if constexpr (VAR == V_NORM) {
-                float qz = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-                    for (int el = 0; el < E; ++el)
-                        qz += frag_elem<TM>(qf[ks], el) * Zs[zc + g * (DK / 4) + ks * E + el];
-                float den = rowsum + qz;
-                den += __shfl_xor(den, 16, 64);
-                den += __shfl_xor(den, 32, 64);
-                const float inv = 1.0f / den;
-#pragma unroll
-                for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= inv;
-            }
-
-            if (!RAGGED || rrow < L) {
-#pragma unroll
-                for (int jt = 0; jt < NTJW; ++jt)
-                    st4<TO>(og + rrow * dv + (tj0 + jt) * 16 + 4 * g, oacc[jt]);
-            }
-        };
-        auto wave_role = [&](auto w_tag) {
-            constexpr int W = decltype(w_tag)::value;
-            row_block(std::integral_constant<int, R::rb(W, 0)>{},
-                      std::integral_constant<int, R::half(W) * NTJW>{});
-            if constexpr (R::RBW == 2)
-                row_block(std::integral_constant<int, R::rb(W, 1)>{}, std::integral_constant<int, 0>{});
-        };
-        switch (wv) {
-            case 0: wave_role(std::integral_constant<int, 0>{}); break;
-            case 1: wave_role(std::integral_constant<int, 1>{}); break;
-            case 2: wave_role(std::integral_constant<int, 2>{}); break;
-            case 3: wave_role(std::integral_constant<int, 3>{}); break;
-            default:
-                if constexpr (NW == 8) {
-                    switch (wv) {
-                        case 4: wave_role(std::integral_constant<int, 4 % NW>{}); break;
-                        case 5: wave_role(std::integral_constant<int, 5 % NW>{}); break;
-                        case 6: wave_role(std::integral_constant<int, 6 % NW>{}); break;
-                        default: wave_role(std::integral_constant<int, 7 % NW>{}); break;
-                    }
-                }
-                break;
-        }
-
-        // ---- state update: S <- exp(g_C) S + K^T (w (.) V), both operands read
-        // from the row-major tiles with the token index in the K slots.
-        if constexpr (DECAYED) {
-            const float eg = Tsc[buf];
-#pragma unroll
-            for (int m = 0; m < NTS; ++m) Sacc[m] *= eg;
-        }
-#pragma unroll
-        for (int m = 0; m < NTS; ++m) {
-            if (m < tsn) {
-                const int tile = ts0 + m, ti = tile / NTJ, tj = tile % NTJ;
-#pragma unroll
-                for (int ks = 0; ks < NTK; ++ks)
-                    Sacc[m] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), tok_frag(VW, PV{}, ks, tj * 16), Sacc[m]);
-            }
-        }
-        // ---- normalizer carry: z_next = z_prev + K^T 1 (fp32 accumulators).
-        if constexpr (VAR == V_NORM) {
-            if (wv == ZW) {
-                frag ones;
-                if constexpr (E == 8) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ones[e] = from_f32<TM>(1.0f);
-                } else {
-                    ones = 1.0f;
-                }
-#pragma unroll
-                for (int ti = 0; ti < NTI; ++ti) {
-#pragma unroll
-                    for (int ks = 0; ks < NTK; ++ks) zacc[ti] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), ones, zacc[ti]);
-                    if (n == 0) *reinterpret_cast<f32x4 *>(&Zs[zn + ti * 16 + 4 * g]) = zacc[ti];
-                }
-            }
-        }
-
-        // ---- wave 0 prepares the next chunk's gate tables (its loads arrived
-        // during this chunk's math).
-        if constexpr (DECAYED) {
-            if (NEXT != 0 && wv == 0 && c + 1 < nchunks) gate_tables(c + 1, buf ^ 1);
         }
     };
 
-    // Schedule: the first full chunk is peeled so that both edges into the
+    // Outputs of one 16-row block rb and one range of value tiles (from tj0) of
+    // chunk c, from tile set X. CHECK: rows past L are not stored.
+    auto row_block = [&](auto rb_tag, auto tj_tag, int c, const TM *X, const float *T,
+                         auto check_tag) __attribute__((always_inline)) {
+        constexpr int rb = decltype(rb_tag)::value;
+        constexpr int tj0 = decltype(tj_tag)::value;
+        constexpr bool CHECK = decltype(check_tag)::value;
+        const TM *Qs = X + Cfg::OQ, *Ks = X + Cfg::OK, *Vs = X + Cfg::OV, *STs = X + Cfg::OS;
+        const int t0 = c * C;
+        const int zc = (c & 1) * DK;
+        const int rl = rb * 16 + n;   // chunk-local query row of this lane
+        frag qf[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = ld_frag<TM>(&Qs[QT::at(rl, g * (DK / 4) + ks * E)]);
+        const float Gr = DECAYED ? T[rl] : 0.f;
+
+        // inter-chunk term: D[j][r] = exp(G_r) sum_i S[i][j] q_r[i]
+        f32x4 oacc[NTJW];
+#pragma unroll
+        for (int jt = 0; jt < NTJW; ++jt) {
+            const int tj = tj0 + jt;
+            oacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                oacc[jt] = MF::mma(ld_frag<TM>(&STs[(tj * 16 + n) * KP + g * (DK / 4) + ks * E]), qf[ks], oacc[jt]);
+        }
+        if constexpr (DECAYED) {
+            const float er = T[C + rl];
+#pragma unroll
+            for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= er;
+        }
+
+        // score tiles D[s][r] = k_s . q_r for key blocks sb <= rb. Off the
+        // diagonal, exp(G_r - G_s) = exp(G_r - G_e) exp(G_e - G_s) with e the
+        // last token of block sb: both factors <= 1, so no overflow for any
+        // gates, and one exp per tile.
+        f32x4 sc[NRB];
+        float rowsum = 0.f;
+#pragma unroll
+        for (int sb = 0; sb < NRB; ++sb) {
+            sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (sb <= rb) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    sc[sb] = MF::mma(ld_frag<TM>(&Ks[KT::at(sb * 16 + n, g * (DK / 4) + ks * E)]), qf[ks], sc[sb]);
+                if (sb == rb) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int sl = sb * 16 + 4 * g + e;
+                        float x = sc[sb][e];
+                        if constexpr (DECAYED) x *= __expf(Gr - T[sl]);
+                        sc[sb][e] = (sl > rl) ? 0.f : x;
+                    }
+                } else if constexpr (DECAYED) {
+                    const float fr = __expf(Gr - T[sb * 16 + 15]);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&T[3 * C + sb * 16 + 4 * g]);
+                    sc[sb] *= fr * b4;
+                }
+                if constexpr (VAR == V_NORM) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        sc[sb][e] = to_f32<TM>(from_f32<TM>(sc[sb][e]));
+                        rowsum += sc[sb][e];
+                    }
+                }
+            }
+        }
+
+        // intra-chunk term: D[j][r] += sum_s V[s][j] A[r][s]; the V^T operand
+        // holds the tokens of the two score tiles 2p, 2p+1 that lane group g
+        // carries: s = 32p + 4g + (0..3) and 32p + 16 + 4g + (0..3).
+        if constexpr (E == 8) {
+#pragma unroll
+            for (int p = 0; p < NRB / 2; ++p) {
+                if (2 * p <= rb) {
+                    frag bop;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bop[e] = from_f32<TM>(sc[2 * p][e]);
+                        bop[4 + e] = from_f32<TM>(sc[2 * p + 1][e]);
+                    }
+                    const bool hi = (2 * p + 1 <= rb);
+#pragma unroll
+                    for (int jt = 0; jt < NTJW; ++jt) {
+                        frag aop = tok_frag(Vs, PV{}, p, (tj0 + jt) * 16);
+                        if (!hi) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) aop[4 + e] = from_f32<TM>(0.0f);
+                        }
+                        oacc[jt] = MF::mma(aop, bop, oacc[jt]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int sb = 0; sb < NRB; ++sb) {
+                if (sb <= rb) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                        for (int jt = 0; jt < NTJW; ++jt)
+                            oacc[jt] = MF::mma(Vs[VT::at(sb * 16 + 4 * g + e, (tj0 + jt) * 16 + n)], sc[sb][e], oacc[jt]);
+                    }
+                }
+            }
+        }
+
+        if constexpr (VAR == V_NORM) {
+            float qz = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int el = 0; el < E; ++el)
+                    qz += frag_elem<TM>(qf[ks], el) * Zs[zc + g * (DK / 4) + ks * E + el];
+            float den = rowsum + qz;
+            den += __shfl_xor(den, 16, 64);
+            den += __shfl_xor(den, 32, 64);
+            const float inv = 1.0f / den;
+#pragma unroll
+            for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= inv;
+        }
+
+        // rows of this block start at a uniform offset: scalar base + lane offset
+        TO *ob = og + (size_t)(t0 + rb * 16) * dv + tj0 * 16;
+        if (!CHECK || t0 + rl < L) {
+#pragma unroll
+            for (int jt = 0; jt < NTJW; ++jt) st4<TO>(ob + (uint32_t)(n * dv + jt * 16 + 4 * g), oacc[jt]);
+        }
+    };
+
+    // The rows of wave W.
+    auto rows_of = [&](auto w_tag, int c, const TM *X, const float *T, auto check_tag) __attribute__((always_inline)) {
+        constexpr int W = decltype(w_tag)::value;
+        row_block(std::integral_constant<int, R::rb(W, 0)>{}, std::integral_constant<int, R::half(W) * NTJW>{}, c,
+                  X, T, check_tag);
+        if constexpr (R::RBW == 2)
+            row_block(std::integral_constant<int, R::rb(W, 1)>{}, std::integral_constant<int, 0>{}, c, X, T,
+                      check_tag);
+    };
+
+    // State update S <- exp(g_C) S + K^T (w (.) V) of wave W's tiles from tile set
+    // X, both operands read from the row-major tiles with the token index in the
+    // K slots; then the normalizer carry z_next = z_prev + K^T 1 (wave ZW).
+    auto state_update = [&](auto w_tag, int c, const TM *X, float eg) __attribute__((always_inline)) {
+        constexpr int W = decltype(w_tag)::value;
+        if constexpr (DECAYED) {
+#pragma unroll
+            for (int m = 0; m < TS.cnt[W]; ++m) Sacc[m] *= eg;
+        }
+        const TM *Ks = X + Cfg::OK;
+        const TM *VW = X + (DECAYED ? Cfg::OVW : Cfg::OV);
+#pragma unroll
+        for (int m = 0; m < TS.cnt[W]; ++m) {
+            const int tile = TS.start[W] + m, ti = tile / NTJ, tj = tile % NTJ;
+#pragma unroll
+            for (int ks = 0; ks < NTK; ++ks)
+                Sacc[m] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), tok_frag(VW, PV{}, ks, tj * 16), Sacc[m]);
+        }
+        if constexpr (VAR == V_NORM && W == ZW) {
+            const int zn = ((c + 1) & 1) * DK;
+            frag ones;
+            if constexpr (E == 8) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ones[e] = from_f32<TM>(1.0f);
+            } else {
+                ones = 1.0f;
+            }
+#pragma unroll
+            for (int ti = 0; ti < NTI; ++ti) {
+#pragma unroll
+                for (int ks = 0; ks < NTK; ++ks) zacc[ti] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), ones, zacc[ti]);
+                if (n == 0) *reinterpret_cast<f32x4 *>(&Zs[zn + ti * 16 + 4 * g]) = zacc[ti];
+            }
+        }
+    };
+
+    // ---- double-buffered chunk: tile set b = c & 1 holds chunk c; chunk c+1 is
+    // staged into set b ^ 1 right after this wave's rows are done (no barrier in
+    // between), and each slot is refilled with chunk c+2. FAST: chunks c .. c+2
+    // are all full.
+    auto chunk_db = [&](int c, auto fast_tag) __attribute__((always_inline)) {
+        constexpr bool FAST = decltype(fast_tag)::value;
+        using Check = std::bool_constant<!FAST>;
+        TM *X = Tiles + (c & 1) * Cfg::SET, *Xn = Tiles + ((c + 1) & 1) * Cfg::SET;
+        const float *T = Tg + (c % NTB) * 4 * C;
+        __syncthreads();  // chunk c staged, its gate tables and S_prev visible; chunk c-1 done
+        if constexpr (FAST) {
+            load_gates(c + 2, std::true_type{});
+        } else {
+            if (c + 2 < nchunks) load_gates(c + 2, std::false_type{});
+        }
+        frag wf[VAR == V_GDN ? NKS : 1];
+        f32x4 ucur[VAR == V_GDN ? NTJW : 1];
+        if constexpr (VAR == V_GDN) {
+            take_wu(wf, ucur);
+            if (FAST || c + 1 < nchunks) load_wu(c + 1);
+        }
+        // Keep the prefetch here: the scheduler would otherwise sink the loads
+        // towards their use and expose their latency.
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (VAR == V_GDN) {
+            gdn_u(X, T, wf, ucur);
+            __syncthreads();  // U rows of every wave visible
+        }
+        const bool next = FAST || c + 1 < nchunks;
+        const float eg = DECAYED ? Tsc[c % NTB] : 1.f;
+        for_wave([&](auto w_tag) __attribute__((always_inline)) { rows_of(w_tag, c, X, T, Check{}); });
+        if (next) {
+            static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                stage_any(m_tag, c + 1, Xn, Check{});
+                if constexpr (FAST) {
+                    load_any(m_tag, c + 2, std::true_type{});
+                } else {
+                    if (c + 2 < nchunks) load_any(m_tag, c + 2, std::false_type{});
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+        for_wave([&](auto w_tag) __attribute__((always_inline)) {
+            state_update(w_tag, c, X, eg);
+            if (next) write_sts(w_tag, Xn);
+        });
+        if constexpr (DECAYED) {
+            if (wv == 0 && (FAST || c + 2 < nchunks)) gate_tables(c + 2, (c + 2) % NTB);
+        }
+    };
+
+    // ---- single-buffered chunk: chunk c is staged between two barriers and
+    // each slot is refilled with chunk c+1. FAST: chunks c and c+1 are full.
+    auto chunk_sb = [&](int c, auto fast_tag) __attribute__((always_inline)) {
+        constexpr bool FAST = decltype(fast_tag)::value;
+        using Check = std::bool_constant<!FAST>;
+        TM *X = Tiles;
+        const float *T = Tg + (c % NTB) * 4 * C;
+        __syncthreads();  // previous chunk done with every tile; gate tables visible
+        if constexpr (FAST) {
+            load_gates(c + 1, std::true_type{});
+        } else {
+            if (c + 1 < nchunks) load_gates(c + 1, std::false_type{});
+        }
+        for_wave([&](auto w_tag) __attribute__((always_inline)) { write_sts(w_tag, X); });
+        static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+            stage_any(m_tag, c, X, Check{});
+            if constexpr (FAST) {
+                load_any(m_tag, c + 1, std::true_type{});
+            } else {
+                if (c + 1 < nchunks) load_any(m_tag, c + 1, std::false_type{});
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        frag wf[VAR == V_GDN ? NKS : 1];
+        f32x4 ucur[VAR == V_GDN ? NTJW : 1];
+        if constexpr (VAR == V_GDN) {
+            take_wu(wf, ucur);
+            if (FAST || c + 1 < nchunks) load_wu(c + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();  // staged tiles and STs visible
+        if constexpr (VAR == V_GDN) {
+            gdn_u(X, T, wf, ucur);
+            __syncthreads();
+        }
+        const float eg = DECAYED ? Tsc[c % NTB] : 1.f;
+        for_wave([&](auto w_tag) __attribute__((always_inline)) {
+            rows_of(w_tag, c, X, T, Check{});
+            state_update(w_tag, c, X, eg);
+        });
+        if constexpr (DECAYED) {
+            if (wv == 0 && (FAST || c + 1 < nchunks)) gate_tables(c + 1, (c + 1) % NTB);
+        }
+    };
+
+    // Schedule. The first FAST chunk is peeled so that both edges into the
     // steady-state loop leave the same memory operations in flight (the wait
     // counts inside the loop are then exact and let output stores drain in the
-    // background); the last full chunk prefetches the ragged tail, if any.
-    if (nfull > 0) {
-        load_chunk(0, full_t);
-    } else if (nchunks > 0) {
-        load_chunk(0, ragged_t);
+    // background); the last chunks take the checked path.
+    if constexpr (DB) {
+        if (nchunks > 0) {
+            load_gates(0, std::false_type{});
+            static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                load_any(m_tag, 0, std::false_type{});
+            });
+            load_wu(0);
+            if constexpr (DECAYED) {
+                if (wv == 0) gate_tables(0, 0);
+                if (nchunks > 1) {
+                    load_gates(1, std::false_type{});
+                    if (wv == 0) gate_tables(1, 1);
+                }
+            }
+            __syncthreads();  // gate tables of chunk 0 visible
+            static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                stage_any(m_tag, 0, Tiles, std::true_type{});
+                if (nchunks > 1) load_any(m_tag, 1, std::false_type{});
+            });
+            for_wave([&](auto w_tag) __attribute__((always_inline)) { write_sts(w_tag, Tiles); });
+        }
+        int c = 0;
+        if (nfull >= 3) {
+            chunk_db(0, std::true_type{});
+            for (c = 1; c < nfull - 2; ++c) chunk_db(c, std::true_type{});
+        }
+        for (; c < nchunks; ++c) chunk_db(c, std::false_type{});
+    } else {
+        if (nchunks > 0) {
+            load_gates(0, std::false_type{});
+            static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                load_any(m_tag, 0, std::false_type{});
+            });
+            load_wu(0);
+            if constexpr (DECAYED) {
+                if (wv == 0) gate_tables(0, 0);
+            }
+        }
+        int c = 0;
+        if (nfull >= 2) {
+            chunk_sb(0, std::true_type{});
+            for (c = 1; c < nfull - 1; ++c) chunk_sb(c, std::true_type{});
+        }
+        for (; c < nchunks; ++c) chunk_sb(c, std::false_type{});
     }
-    if constexpr (DECAYED) {
-        if (nchunks > 0 && wv == 0) gate_tables(0, 0);
-    }
-    if (nfull >= 2) {
-        chunk_body(0, full_t, NextFull{});
-        for (int c = 1; c < nfull - 1; ++c) chunk_body(c, full_t, NextFull{});
-    }
-    if (nfull >= 1) chunk_body(nfull - 1, full_t, NextTail{});
-    if (nfull < nchunks) chunk_body(nfull, ragged_t, NextNone{});
 
     if (a.s_out) {
 #pragma unroll
