@@ -231,7 +231,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(16))) TM Tiles[Cfg::NB * Cfg::SET];
     __shared__ __attribute__((aligned(16))) float Tg[DECAYED ? NTB * 4 * C : 1];
     __shared__ float Tsc[DECAYED ? NTB : 1];
-    __shared__ __attribute__((aligned(16))) float Zs[VAR == V_NORM ? 2 * DK : 1];
+    // Normalizer z of the previous chunk, double-buffered: fp16 path as hi and lo
+    // halves (z = hi + lo to 2^-22) for the q . z MFMA; fp32 path in fp32.
+    __shared__ __attribute__((aligned(16))) TM Zs[VAR == V_NORM ? (H ? 4 * DK : 2 * DK) : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -282,7 +284,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) zacc[ti][e] = a.z_in ? a.z_in[(size_t)bh * DK + ti * 16 + 4 * g + e] : 0.f;
         }
-        for (int i = tid; i < DK; i += NT) Zs[i] = a.z_in ? a.z_in[(size_t)bh * DK + i] : 0.f;
+        for (int i = tid; i < DK; i += NT) {
+            const float z = a.z_in ? a.z_in[(size_t)bh * DK + i] : 0.f;
+            if constexpr (H) {
+                const TM hi = from_f32<TM>(z);
+                Zs[i] = hi;
+                Zs[DK + i] = from_f32<TM>(z - to_f32<TM>(hi));
+            } else {
+                Zs[i] = z;
+            }
+        }
     }
     // Settle the prologue's loads here, so that no load is pending at the loop
     // head and the per-chunk waits can be exact (leaving output stores in flight).
@@ -610,34 +621,80 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 
     // Outputs of one 16-row block rb and one range of value tiles (from tj0) of
     // chunk c, from tile set X. CHECK: rows past L are not stored.
+    // Every LDS operand of the block is read before the math when the fragments
+    // fit in registers (HOIST), so the reads overlap instead of each waiting.
     auto row_block = [&](auto rb_tag, auto tj_tag, int c, const TM *X, const float *T,
                          auto check_tag) __attribute__((always_inline)) {
         constexpr int rb = decltype(rb_tag)::value;
         constexpr int tj0 = decltype(tj_tag)::value;
         constexpr bool CHECK = decltype(check_tag)::value;
+        constexpr int FR = (int)sizeof(frag) / 4;  // VGPRs per fragment
+        constexpr bool HOIST = H && FR * (NKS * (1 + NTJW + rb + 1) + NTJW * (rb / 2 + 1)) <= 80;
+        constexpr bool NZ = H && VAR == V_NORM;   // normalizer on MFMA (fp16 path)
         const TM *Qs = X + Cfg::OQ, *Ks = X + Cfg::OK, *Vs = X + Cfg::OV, *STs = X + Cfg::OS;
         const int t0 = c * C;
-        const int zc = (c & 1) * DK;
         const int rl = rb * 16 + n;   // chunk-local query row of this lane
-        frag qf[NKS];
+
+        // ---- operands
+        frag qf[NKS], sf[NTJW][NKS], kf[rb + 1][NKS], vf[rb / 2 + 1][NTJW];
+        frag zf[NZ ? 2 * NKS : 1];
+        auto load_k = [&](int sb) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) kf[sb][ks] = ld_frag<TM>(&Ks[KT::at(sb * 16 + n, g * (DK / 4) + ks * E)]);
+        };
+        auto load_v = [&](int p) __attribute__((always_inline)) {
+            if constexpr (E == 8) {
+#pragma unroll
+                for (int jt = 0; jt < NTJW; ++jt) vf[p][jt] = tok_frag(Vs, PV{}, p, (tj0 + jt) * 16);
+            }
+        };
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) qf[ks] = ld_frag<TM>(&Qs[QT::at(rl, g * (DK / 4) + ks * E)]);
+#pragma unroll
+        for (int jt = 0; jt < NTJW; ++jt)
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                sf[jt][ks] = ld_frag<TM>(&STs[((tj0 + jt) * 16 + n) * KP + g * (DK / 4) + ks * E]);
+        if constexpr (NZ) {
+            const TM *Zc = Zs + (c & 1) * 2 * DK;  // z of chunk c-1: hi halves, then lo halves
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                zf[2 * ks] = ld_frag<TM>(&Zc[g * (DK / 4) + ks * E]);
+                zf[2 * ks + 1] = ld_frag<TM>(&Zc[DK + g * (DK / 4) + ks * E]);
+            }
+        }
+        if constexpr (HOIST) {
+#pragma unroll
+            for (int sb = 0; sb <= rb; ++sb) load_k(sb);
+#pragma unroll
+            for (int p = 0; p <= rb / 2; ++p) load_v(p);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         const float Gr = DECAYED ? T[rl] : 0.f;
 
         // inter-chunk term: D[j][r] = exp(G_r) sum_i S[i][j] q_r[i]
         f32x4 oacc[NTJW];
 #pragma unroll
         for (int jt = 0; jt < NTJW; ++jt) {
-            const int tj = tj0 + jt;
             oacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                oacc[jt] = MF::mma(ld_frag<TM>(&STs[(tj * 16 + n) * KP + g * (DK / 4) + ks * E]), qf[ks], oacc[jt]);
+            for (int ks = 0; ks < NKS; ++ks) oacc[jt] = MF::mma(sf[jt][ks], qf[ks], oacc[jt]);
         }
         if constexpr (DECAYED) {
             const float er = T[C + rl];
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= er;
+        }
+        // normalizer, fp16 path: den[r] = q_r . z_prev + rowsum_r, accumulated in
+        // a tile whose rows are all alike (every lane gets its row's value):
+        // q . z from z's hi and lo halves, rowsums from a ones operand below.
+        f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (NZ) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                dacc = MF::mma(zf[2 * ks], qf[ks], dacc);
+                dacc = MF::mma(zf[2 * ks + 1], qf[ks], dacc);
+            }
         }
 
         // score tiles D[s][r] = k_s . q_r for key blocks sb <= rb. Off the
@@ -645,14 +702,14 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         // last token of block sb: both factors <= 1, so no overflow for any
         // gates, and one exp per tile.
         f32x4 sc[NRB];
-        float rowsum = 0.f;
+        float rowsum = 0.f;  // fp32 path only
 #pragma unroll
         for (int sb = 0; sb < NRB; ++sb) {
             sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (sb <= rb) {
+                if constexpr (!HOIST) load_k(sb);
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    sc[sb] = MF::mma(ld_frag<TM>(&Ks[KT::at(sb * 16 + n, g * (DK / 4) + ks * E)]), qf[ks], sc[sb]);
+                for (int ks = 0; ks < NKS; ++ks) sc[sb] = MF::mma(kf[sb][ks], qf[ks], sc[sb]);
                 if (sb == rb) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -666,12 +723,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                     const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&T[3 * C + sb * 16 + 4 * g]);
                     sc[sb] *= fr * b4;
                 }
-                if constexpr (VAR == V_NORM) {
+                if constexpr (VAR == V_NORM && !NZ) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        sc[sb][e] = to_f32<TM>(from_f32<TM>(sc[sb][e]));
-                        rowsum += sc[sb][e];
-                    }
+                    for (int e = 0; e < 4; ++e) rowsum += sc[sb][e];
                 }
             }
         }
@@ -680,6 +734,11 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         // holds the tokens of the two score tiles 2p, 2p+1 that lane group g
         // carries: s = 32p + 4g + (0..3) and 32p + 16 + 4g + (0..3).
         if constexpr (E == 8) {
+            frag ones;
+            if constexpr (NZ) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ones[e] = from_f32<TM>(1.0f);
+            }
 #pragma unroll
             for (int p = 0; p < NRB / 2; ++p) {
                 if (2 * p <= rb) {
@@ -689,16 +748,18 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                         bop[e] = from_f32<TM>(sc[2 * p][e]);
                         bop[4 + e] = from_f32<TM>(sc[2 * p + 1][e]);
                     }
+                    if constexpr (!HOIST) load_v(p);
                     const bool hi = (2 * p + 1 <= rb);
 #pragma unroll
                     for (int jt = 0; jt < NTJW; ++jt) {
-                        frag aop = tok_frag(Vs, PV{}, p, (tj0 + jt) * 16);
+                        frag aop = vf[p][jt];
                         if (!hi) {
 #pragma unroll
                             for (int e = 0; e < 4; ++e) aop[4 + e] = from_f32<TM>(0.0f);
                         }
                         oacc[jt] = MF::mma(aop, bop, oacc[jt]);
                     }
+                    if constexpr (NZ) dacc = MF::mma(ones, bop, dacc);  // rowsums of the rounded scores
                 }
             }
         } else {
@@ -715,7 +776,12 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             }
         }
 
-        if constexpr (VAR == V_NORM) {
+        if constexpr (NZ) {
+            const float inv = 1.0f / dacc[0];
+#pragma unroll
+            for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= inv;
+        } else if constexpr (VAR == V_NORM) {
+            const int zc = (c & 1) * DK;
             float qz = 0.f;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
@@ -767,7 +833,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                 Sacc[m] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), tok_frag(VW, PV{}, ks, tj * 16), Sacc[m]);
         }
         if constexpr (VAR == V_NORM && W == ZW) {
-            const int zn = ((c + 1) & 1) * DK;
+            const int zn = ((c + 1) & 1) * (H ? 2 * DK : DK);
             frag ones;
             if constexpr (E == 8) {
 #pragma unroll
@@ -779,7 +845,17 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             for (int ti = 0; ti < NTI; ++ti) {
 #pragma unroll
                 for (int ks = 0; ks < NTK; ++ks) zacc[ti] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), ones, zacc[ti]);
-                if (n == 0) *reinterpret_cast<f32x4 *>(&Zs[zn + ti * 16 + 4 * g]) = zacc[ti];
+                if (n == 0) {
+                    if constexpr (H) {
+                        f32x4 lo;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) lo[e] = zacc[ti][e] - to_f32<TM>(from_f32<TM>(zacc[ti][e]));
+                        st4<TM>(&Zs[zn + ti * 16 + 4 * g], zacc[ti]);
+                        st4<TM>(&Zs[zn + DK + ti * 16 + 4 * g], lo);
+                    } else {
+                        *reinterpret_cast<f32x4 *>(&Zs[zn + ti * 16 + 4 * g]) = zacc[ti];
+                    }
+                }
             }
         }
     };
