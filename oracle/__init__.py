@@ -41,7 +41,7 @@ def load(path: Optional[str] = None):
     lib.oracle_forward.argtypes = [ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
                                    L, L, L, L, ctypes.c_int]
     lib.oracle_forward.restype = ctypes.c_int
-    lib.oracle_decode_step.argtypes = [ctypes.c_int, dp, dp, dp, dp, dp, dp, L, L, L, ctypes.c_int]
+    lib.oracle_decode_step.argtypes = [ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, L, L, L, ctypes.c_int]
     lib.oracle_decode_step.restype = ctypes.c_int
     lib.oracle_abi_version.restype = ctypes.c_int
     _lib, _lib_path = lib, path
@@ -87,10 +87,11 @@ def forward(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in
     return o, s_out, z_out
 
 
-def decode_step(variant: str, q, k, v, log_gate, state, threads: int = 0, lib=None):
+def decode_step(variant: str, q, k, v, log_gate, state, beta=None, threads: int = 0, lib=None):
     """One in-place decode step on a copy of ``state``; returns (o, new_state).
 
-    q, k: [..., dk]; v: [..., dv]; log_gate: [...]; state: [..., dk, dv].
+    q, k: [..., dk]; v: [..., dv]; log_gate, beta: [...]; state: [..., dk, dv].
+    beta is required for "gated_delta" (log_gate may then be None: alpha = 1).
     """
     lib = lib or load()
     q, k, v = _c64(q), _c64(k), _c64(v)
@@ -99,9 +100,10 @@ def decode_step(variant: str, q, k, v, log_gate, state, threads: int = 0, lib=No
     NH = int(np.prod(lead)) if lead else 1
     S = np.array(state, dtype=np.float64, copy=True, order="C")
     lg = _c64(log_gate)
+    be = _c64(beta)
     o = np.zeros(lead + (dv,), np.float64)
-    st = lib.oracle_decode_step(VARIANT_ID[variant], _p(q), _p(k), _p(v), _p(lg), _p(S), _p(o),
-                                NH, dk, dv, int(threads))
+    st = lib.oracle_decode_step(VARIANT_ID[variant], _p(q), _p(k), _p(v), _p(lg), _p(be), _p(S),
+                                _p(o), NH, dk, dv, int(threads))
     if st != 0:
         raise ValueError(f"oracle_decode_step failed with status {st}")
     return o, S

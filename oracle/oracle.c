@@ -147,17 +147,23 @@ int oracle_forward(int variant, const double *q, const double *k, const double *
 }
 
 /*
- * One-token decode step of the DECAY (or PLAIN, log_gate NULL) recurrence, in
- * place on the state: S <- exp(l) S + k v^T, then o = S^T q  (tensorplay
- * section 2.2: constant-size state carried from token to token; wln20 decay
- * equation). Layouts: q, k [NH, dk]; v, o [NH, dv]; log_gate [NH]; state [NH, dk, dv].
+ * One-token decode step, in place on the state (tensorplay section 2.2:
+ * constant-size state carried from token to token), with the same per-token
+ * update as the forward pass:
+ *   DECAY (PLAIN: log_gate NULL)  S <- exp(l) S + k v^T            (wln20 decay equation)
+ *   GATED_DELTA                   r = S^T k; S <- a (S - b k r^T) + b k v^T,
+ *                                 a = exp(l) (1 when log_gate is NULL), b = beta
+ *                                 (wln20 Gated DeltaNet section)
+ * then o = S^T q. Layouts: q, k [NH, dk]; v, o [NH, dv]; log_gate, beta [NH];
+ * state [NH, dk, dv].
  */
 int oracle_decode_step(int variant, const double *q, const double *k, const double *v,
-                       const double *log_gate, double *state, double *o,
+                       const double *log_gate, const double *beta, double *state, double *o,
                        long NH, long dk, long dv, int nthreads)
 {
-    if (variant != OR_PLAIN && variant != OR_DECAY) return OR_BAD_ARG;
+    if (variant != OR_PLAIN && variant != OR_DECAY && variant != OR_GATED_DELTA) return OR_BAD_ARG;
     if (variant == OR_DECAY && !log_gate) return OR_BAD_ARG;
+    if (variant == OR_GATED_DELTA && !beta) return OR_BAD_ARG;
     if (NH < 0 || dk <= 0 || dv <= 0 || !state) return OR_BAD_ARG;
     int status = OR_OK;
 #ifdef _OPENMP
@@ -165,8 +171,8 @@ int oracle_decode_step(int variant, const double *q, const double *k, const doub
 #endif
     for (long h = 0; h < NH; ++h) {
         int st = run_head(variant, q + h * dk, k + h * dk, v + h * dv,
-                          log_gate ? log_gate + h : NULL, NULL, state + h * dk * dv, NULL,
-                          o + h * dv, state + h * dk * dv, NULL, 1, dk, dv);
+                          log_gate ? log_gate + h : NULL, beta ? beta + h : NULL,
+                          state + h * dk * dv, NULL, o + h * dv, state + h * dk * dv, NULL, 1, dk, dv);
         if (st > status) status = st;
     }
     return status;

@@ -455,6 +455,44 @@ def pin_prefill_then_decode(lib):
     assert _rel(o_dec, o_full[:, L]) <= 1e-13 and _rel(s_dec, s_full) <= 1e-13
 
 
+def pin_decode_gdn_step(lib):
+    """Delta-rule decode step against the retrieve / merge / overwrite form of one
+    token on the decayed state, written in the pages' v k^T orientation
+    (tensorplay section 6.1; wln20 DeltaNet and Gated DeltaNet sections); also
+    alpha = 1 when no log-gate is given."""
+    r = _rng(21)
+    NH, dk, dv = 5, 6, 4
+    q, k = _unit(r.standard_normal((NH, dk))), _unit(r.standard_normal((NH, dk)))
+    v = r.standard_normal((NH, dv))
+    lg = np.log(1.0 / (1.0 + np.exp(-r.normal(3.0, 1.0, NH))))
+    beta = 1.0 / (1.0 + np.exp(-r.normal(0.0, 1.0, NH)))
+    S = r.standard_normal((NH, dk, dv))
+    for gate in (lg, None):
+        o, S1 = oracle.decode_step("gated_delta", q, k, v, gate, S, beta=beta, lib=lib)
+        alpha = np.ones(NH) if gate is None else np.exp(gate)
+        for h in range(NH):
+            ro, rs = _gdn_retrieve_merge_overwrite(q[h:h + 1], k[h:h + 1], v[h:h + 1], alpha[h:h + 1],
+                                                   beta[h:h + 1], S[h])
+            assert _rel(o[h], ro[0]) <= 1e-13 and _rel(S1[h], rs) <= 1e-13
+
+
+def pin_prefill_then_decode_gdn(lib):
+    """Prefill L tokens with the delta rule, then one decode step on token L+1,
+    equals the forward over L+1 tokens (the state is the whole memory)."""
+    r = _rng(22)
+    L, dk, dv = 17, 5, 3
+    q, k = _unit(r.standard_normal((2, L + 1, dk))), _unit(r.standard_normal((2, L + 1, dk)))
+    v = r.standard_normal((2, L + 1, dv))
+    lg = np.log(1.0 / (1.0 + np.exp(-r.normal(3.0, 1.0, (2, L + 1)))))
+    beta = 1.0 / (1.0 + np.exp(-r.normal(0.0, 1.0, (2, L + 1))))
+    o_full, s_full, _ = oracle.forward("gated_delta", q, k, v, log_gate=lg, beta=beta, lib=lib)
+    _, s_pre, _ = oracle.forward("gated_delta", q[:, :L], k[:, :L], v[:, :L], log_gate=lg[:, :L],
+                                 beta=beta[:, :L], lib=lib)
+    o_dec, s_dec = oracle.decode_step("gated_delta", q[:, L], k[:, L], v[:, L], lg[:, L], s_pre,
+                                      beta=beta[:, L], lib=lib)
+    assert _rel(o_dec, o_full[:, L]) <= 1e-12 and _rel(s_dec, s_full) <= 1e-12
+
+
 def pin_resume_all_variants(lib):
     """Splitting a sequence and carrying (S, z) across the split gives the same
     result as one pass, for every variant."""
@@ -492,4 +530,5 @@ ALL_PINS = [
     pin_gdn_beta_zero_pure_decay, pin_gdn_onehot_recall, pin_gdn_unit_key_identity,
     pin_gdn_fraction_product_expansion, pin_gdn_chunkwise_wy,
     pin_decode_one_decay_step, pin_prefill_then_decode, pin_resume_all_variants,
+    pin_decode_gdn_step, pin_prefill_then_decode_gdn,
 ]
