@@ -160,29 +160,35 @@ def bench_chunk(name: str, steps: int, warmup: int, device) -> dict:
                 input_copies=copies, B=c["B"], H=c["H"], L=c["L"], d_k=c["dk"], d_v=c["dv"], C=c["C"])
 
 
-def bench_decode(name: str, steps: int, warmup: int, device) -> dict:
+def bench_decode(name: str, steps: int, warmup: int, device, variant: str = "decay") -> dict:
     import torch
     import chunkwise_linear_rnn_causal_amd as la
     c = W.CONFIGS[name]
     N, H, dk, dv, nsteps = c["N"], c["H"], c["dk"], c["dv"], c["steps"]
+    delta = variant == "gated_delta"
     S = to_dev(W.make_decode_state(N, H, dk, dv, seed=0), device)
     with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
-        host = list(ex.map(lambda i: W.make_decode_step(N, H, dk, dv, step=i, seed=0), range(nsteps)))
-    ins = [(to_dev(h.q, device), to_dev(h.k, device), to_dev(h.v, device), to_dev(h.log_gate, device))
-           for h in host]
+        host = list(ex.map(lambda i: W.make_decode_step(N, H, dk, dv, step=i, seed=0, with_beta=delta),
+                           range(nsteps)))
+    ins = [(to_dev(h.q, device), to_dev(h.k, device), to_dev(h.v, device), to_dev(h.log_gate, device),
+            to_dev(h.beta, device)) for h in host]
     o = torch.empty((N, H, dv), dtype=torch.float32, device=device)
     flop1, bytes1 = decode_work(c)
+    if delta:  # + retrieval S^T k (2 d_k d_v flop) and beta (4 bytes) per head
+        flop1 += 2.0 * dk * dv * N * H
+        bytes1 += 4 * N * H
     stream = torch.cuda.current_stream(device)
 
     def step(_):
-        for (q, k, v, lg) in ins:
-            la.la_decode_step("decay", q, k, v, lg, S, o=o, stream=stream)
+        for (q, k, v, lg, be) in ins:
+            la.la_decode_step(variant, q, k, v, lg, S, o=o, beta=be, stream=stream)
 
     ms, wall_ms = time_steps(step, steps, warmup, stream)
     t = ms / 1e3                            # one step = nsteps decode launches
     t1 = t / nsteps
     # tokens: one new token per sequence per decode launch (all H heads of it)
-    return dict(workload=name, variant="decay_decode", tokens_per_s=N * nsteps / t,
+    return dict(workload=name if not delta else name.replace("decode_decay", "decode_gated_delta"),
+                variant=variant + "_decode", tokens_per_s=N * nsteps / t,
                 ms_per_step=t * 1e3, ms_per_decode_launch=t1 * 1e3,
                 wall_ms_per_step=wall_ms, flop=flop1 * nsteps, bytes=bytes1 * nsteps,
                 achieved_gbs=bytes1 / t1 / 1e9, achieved_tflops=flop1 / t1 / 1e12,
@@ -274,6 +280,13 @@ def main() -> int:
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['achieved_gbs']:.0f} GB/s, "
               f"{r['achieved_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
+        if kind == "decode" and not args.only:
+            # the delta-rule decode step at the same shape (not one of the quoted workloads)
+            r = bench_decode(name, steps, warm, device, variant="gated_delta")
+            results[r["workload"]] = r
+            print(f"[bench] {r['workload']}: {r['ms_per_step']:.4f} ms/step, {r['achieved_gbs']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
 
     head = results[args.workload]
     c = W.CONFIGS[args.workload]

@@ -292,7 +292,7 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (o_dt != LA_F32 && o_dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (!dtype_pair_ok(dt, o_dt)) return LA_ERR_UNSUPPORTED;
-    if (var == LA_NORMALIZED || var == LA_GATED_DELTA) return LA_ERR_UNSUPPORTED;
+    if (var == LA_NORMALIZED) return LA_ERR_UNSUPPORTED;
     if (N < 1 || H < 1) return LA_ERR_INVALID_ARG;
     if ((int64_t)N * H > INT32_MAX) return LA_ERR_UNSUPPORTED;
     if ((d_k != 32 && d_k != 64 && d_k != 128) || (d_v != 32 && d_v != 64 && d_v != 128))
@@ -300,15 +300,15 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
     if (!q || !k || !v || !state || !o) return LA_ERR_INVALID_ARG;
     if (var == LA_DECAY && !log_gate) return LA_ERR_INVALID_ARG;
     if (var == LA_PLAIN && log_gate) return LA_ERR_INVALID_ARG;
-    if (beta) return LA_ERR_INVALID_ARG;
-    const void *ptrs[] = {q, k, v, o, log_gate, state};
+    if ((var == LA_GATED_DELTA) != (beta != nullptr)) return LA_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, k, v, o, log_gate, beta, state};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
     const int64_t NH = (int64_t)N * H;
     const size_t es = elem_size(dt);
     const Span o_sp{o, (size_t)NH * d_v * elem_size(o_dt)}, s_sp{state, (size_t)NH * d_k * d_v * 4};
     const Span ins[] = {{q, (size_t)NH * d_k * es}, {k, (size_t)NH * d_k * es},
-                        {v, (size_t)NH * d_v * es}, {log_gate, (size_t)NH * 4}};
+                        {v, (size_t)NH * d_v * es}, {log_gate, (size_t)NH * 4}, {beta, (size_t)NH * 4}};
     for (const Span &in : ins)
         if (overlap(o_sp, in) || overlap(s_sp, in)) return LA_ERR_INVALID_ARG;
     if (overlap(o_sp, s_sp)) return LA_ERR_INVALID_ARG;
@@ -316,9 +316,13 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
     const la_status s = check_device();
     if (s != LA_OK) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    DecodeArgs a{q, k, v, log_gate, state, o, (int)NH};
+    DecodeArgs a{q, k, v, log_gate, beta, state, o, (int)NH};
     hipError_t e;
-    if (var == LA_DECAY) {
+    if (var == LA_GATED_DELTA) {
+        if (dt == LA_F32) e = dispatch_decode<V_GDN, float, float>(d_k, d_v, a, st);
+        else if (o_dt == LA_F32) e = dispatch_decode<V_GDN, bf16, float>(d_k, d_v, a, st);
+        else e = dispatch_decode<V_GDN, bf16, bf16>(d_k, d_v, a, st);
+    } else if (var == LA_DECAY) {
         if (dt == LA_F32) e = dispatch_decode<V_DECAY, float, float>(d_k, d_v, a, st);
         else if (o_dt == LA_F32) e = dispatch_decode<V_DECAY, bf16, float>(d_k, d_v, a, st);
         else e = dispatch_decode<V_DECAY, bf16, bf16>(d_k, d_v, a, st);

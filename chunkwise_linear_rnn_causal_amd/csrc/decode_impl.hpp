@@ -1,9 +1,15 @@
 // decode_impl.hpp -- one-token recurrent decode step (gfx950), HBM-bound.
 //
-// Per sequence-head: S <- gamma S + k v^T in place, then o = S^T q with the
-// updated state (tensorplay "Talk Linear Attention", sections 2.1-2.2: the
-// constant-size state is all that is carried between tokens; wln20
-// "LLM注意力优化：线性注意力", data-dependent decay). The fp32 state dominates the
+// Per sequence-head, in place on the state, then o = S^T q with the updated
+// state (tensorplay "Talk Linear Attention", sections 2.1-2.2: the constant-size
+// state is all that is carried between tokens):
+//   decay (plain: gamma = 1)  S <- gamma S + k v^T   (wln20 "LLM注意力优化：线性注意力",
+//                                                     data-dependent decay)
+//   gated delta rule          r = S^T k;  S <- alpha S + k (beta (v - alpha r))^T
+//                             (wln20, Gated DeltaNet section, d_k x d_v orientation:
+//                             alpha (S - beta k r^T) + beta k v^T regrouped)
+// The delta rule needs the retrieval r over all rows before any row is updated:
+// the state stays in registers between the two reductions. The fp32 state dominates the
 // traffic (2 x d_k x d_v x 4 bytes per head and step), so the kernel is a
 // streaming read-modify-write: one 256-thread workgroup per head, each thread
 // owning d_k / RG consecutive rows of one 16-byte column group, all of its state
@@ -44,12 +50,41 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         kr[m] = to_f32<TI>(kp[m]);
     }
     const f32x4 vv = ld4<TI>((const TI *)a.v + h * DV + 4 * cg);
-    const float gam = (VAR == V_DECAY) ? __expf(a.lg[h]) : 1.f;
+    const int wv = tid >> 6;
+    // sum of a per-thread partial over all row groups, returned to every thread
+    // of the column group: shuffles inside the wave, then the four waves'
+    // partials through LDS
+    auto rows_total = [&](f32x4 acc, f32x4 (&buf)[4][CG]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int off = CG; off < 64; off <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+        }
+        if ((tid & 63) < CG) buf[wv][cg] = acc;
+        __syncthreads();
+        return buf[0][cg] + buf[1][cg] + buf[2][cg] + buf[3][cg];
+    };
+
+    // new state column group: ns = al * s + kr * u (u per column group)
+    float al = 1.f;
+    f32x4 u = vv;
+    if constexpr (VAR == V_DECAY) {
+        al = __expf(a.lg[h]);
+    } else if constexpr (VAR == V_GDN) {
+        __shared__ f32x4 rred[4][CG];
+        al = a.lg ? __expf(a.lg[h]) : 1.f;
+        const float be = a.beta[h];
+        f32x4 racc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) racc += kr[m] * s[m];
+        const f32x4 r = rows_total(racc, rred);  // r = S^T k for this column group
+        u = be * (vv - al * r);
+    }
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
-        const f32x4 ns = gam * s[m] + kr[m] * vv;
+        const f32x4 ns = al * s[m] + kr[m] * u;
         __builtin_nontemporal_store(ns, reinterpret_cast<f32x4 *>(S + (size_t)m * DV));
         acc += qr[m] * ns;
     }
@@ -59,7 +94,6 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
     }
-    const int wv = tid >> 6;
     if ((tid & 63) < CG) red[wv][cg] = acc;
     __syncthreads();
     if (tid < CG) {

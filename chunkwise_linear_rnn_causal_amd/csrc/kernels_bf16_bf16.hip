@@ -51,13 +51,22 @@ template hipError_t launch_decode<V_PLAIN, bf16, bf16, 128, 32>(const DecodeArgs
 template hipError_t launch_decode<V_PLAIN, bf16, bf16, 128, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_PLAIN, bf16, bf16, 128, 128>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, bf16, bf16, 32, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, bf16, bf16, 32, 32>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, bf16, bf16, 32, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, bf16, bf16, 32, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, bf16, bf16, 32, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, bf16, bf16, 32, 128>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, bf16, bf16, 64, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, bf16, bf16, 64, 32>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, bf16, bf16, 64, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, bf16, bf16, 64, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, bf16, bf16, 64, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, bf16, bf16, 64, 128>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, bf16, bf16, 128, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, bf16, bf16, 128, 32>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, bf16, bf16, 128, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, bf16, bf16, 128, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, bf16, bf16, 128, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, bf16, bf16, 128, 128>(const DecodeArgs &, hipStream_t);
 
 }  // namespace la

@@ -36,14 +36,23 @@ template hipError_t launch_decode<V_PLAIN, float, float, 128, 32>(const DecodeAr
 template hipError_t launch_decode<V_PLAIN, float, float, 128, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_PLAIN, float, float, 128, 128>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, float, float, 32, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, float, float, 32, 32>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, float, float, 32, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, float, float, 32, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, float, float, 32, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, float, float, 32, 128>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, float, float, 64, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, float, float, 64, 32>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, float, float, 64, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, float, float, 64, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, float, float, 64, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, float, float, 64, 128>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, float, float, 128, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, float, float, 128, 32>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, float, float, 128, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, float, float, 128, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, float, float, 128, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_GDN, float, float, 128, 128>(const DecodeArgs &, hipStream_t);
 
 // delta-rule chunk preparation: (d_k, chunk)
 template hipError_t launch_gdn_prep<float, 32, 64>(const PrepArgs &, hipStream_t);

@@ -33,6 +33,7 @@ struct PrepArgs {
 struct DecodeArgs {
     const void *q, *k, *v;      // [NH, DK], [NH, DK], [NH, DV]
     const float *lg;            // [NH] or nullptr
+    const float *beta;          // [NH] (gated delta rule) or nullptr
     float *S;                   // [NH, DK, DV], updated in place
     void *o;                    // [NH, DV]
     int NH;

@@ -132,14 +132,18 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
 
 /*
  * One recurrent decode step for N sequences x H heads, updating the state in
- * place: S <- exp(l) S + k v^T (LA_DECAY) or S <- S + k v^T (LA_PLAIN, log_gate
- * NULL), then o = S^T q with the updated S (tensorplay section 2.1-2.2; wln20
- * decay equation).
+ * place, then o = S^T q with the updated S (tensorplay section 2.1-2.2):
+ *   LA_DECAY        S <- exp(l) S + k v^T (wln20 decay equation)
+ *   LA_PLAIN        S <- S + k v^T (log_gate NULL)
+ *   LA_GATED_DELTA  r = S^T k;  S <- alpha (S - beta k r^T) + beta k v^T,
+ *                   alpha = exp(l), or 1 when log_gate is NULL (DeltaNet)
+ *                   (wln20 Gated DeltaNet section, d_k x d_v orientation)
  *   q, k [N,H,d_k], v [N,H,d_v] in dtype dt; o [N,H,d_v] in dtype o_dt (the
- *   step itself is computed in fp32); log_gate [N,H] float32;
- *   beta must be NULL (reserved for the delta-rule step); state [N,H,d_k,d_v]
- *   float32, read and written in place. o must not overlap the state or inputs.
- *   N, H >= 1; d_k, d_v in {32, 64, 128}.
+ *   step itself is computed in fp32); log_gate [N,H] float32 (required for
+ *   LA_DECAY, optional for LA_GATED_DELTA, NULL for LA_PLAIN); beta [N,H] float32,
+ *   required for LA_GATED_DELTA and NULL otherwise; state [N,H,d_k,d_v] float32,
+ *   read and written in place. o must not overlap the state or inputs.
+ *   N, H >= 1; d_k, d_v in {32, 64, 128}. LA_NORMALIZED is not supported.
  */
 la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void *q,
                          const void *k, const void *v, const float *log_gate,

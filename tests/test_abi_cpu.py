@@ -93,7 +93,9 @@ def dec(var=DECAY, dt=BF16, odt=F32, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, l
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(var=9), INVALID), (dict(var=NORM), UNSUPPORTED), (dict(var=GDN), UNSUPPORTED),
+    (dict(var=9), INVALID), (dict(var=NORM), UNSUPPORTED),
+    (dict(var=GDN), INVALID),                         # delta rule needs beta
+    (dict(var=GDN, beta=FAKE + 0x5000, o=FAKE + 0x5000), INVALID),  # o overlaps beta
     (dict(odt=7), INVALID), (dict(dt=F32, odt=BF16), UNSUPPORTED),
     (dict(N=0), INVALID), (dict(dk=96), UNSUPPORTED), (dict(dv=16), UNSUPPORTED),
     (dict(q=None), INVALID), (dict(S=None), INVALID), (dict(lg=None), INVALID),

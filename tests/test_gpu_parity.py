@@ -163,19 +163,24 @@ def test_associative_recall_on_gpu():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 64), (128, 128)])
-@pytest.mark.parametrize("var", ["plain", "decay"])
+@pytest.mark.parametrize("var", ["plain", "decay", "gated_delta", "deltanet"])
 def test_decode_matches_oracle(var, dt, dk, dv):
+    """One-token steps, three in a row on the same state; "deltanet" is the delta
+    rule without a log-gate (alpha = 1)."""
     N, H = 5, 3
     S0 = W.make_decode_state(N, H, dk, dv, seed=2)
     S = dev(S0)
     Sref = S0.astype(np.float64)
+    delta = var in ("gated_delta", "deltanet")
+    kind = "gated_delta" if delta else var
     for step in range(3):
-        st = W.make_decode_step(N, H, dk, dv, step=step, seed=2, dtype=dt)
-        lg = st.log_gate if var == "decay" else None
-        o = la.la_decode_step(var, dev(st.q), dev(st.k), dev(st.v), dev(lg), S)
+        st = W.make_decode_step(N, H, dk, dv, step=step, seed=2, dtype=dt, with_beta=delta)
+        lg = st.log_gate if var in ("decay", "gated_delta") else None
+        o = la.la_decode_step(kind, dev(st.q), dev(st.k), dev(st.v), dev(lg), S, beta=dev(st.beta))
         torch.cuda.synchronize()
-        ro, Sref = oracle.decode_step(var, W.to_f64(st.q), W.to_f64(st.k), W.to_f64(st.v),
-                                      None if lg is None else lg.astype(np.float64), Sref)
+        ro, Sref = oracle.decode_step(kind, W.to_f64(st.q), W.to_f64(st.k), W.to_f64(st.v),
+                                      None if lg is None else lg.astype(np.float64), Sref,
+                                      beta=None if st.beta is None else st.beta.astype(np.float64))
         assert_close(host64(o), ro, TOL[dt], f"o step {step}")
         assert_close(host64(S), Sref, 1e-4, f"state step {step}")
 
@@ -190,6 +195,22 @@ def test_prefill_then_decode():
     _, S, _ = la.la_chunk_fwd("decay", pre(q), pre(k), pre(v), pre(lg), want_state=True)
     last = lambda x: x[:, :, L].contiguous()
     o = la.la_decode_step("decay", last(q), last(k), last(v), last(lg), S)
+    torch.cuda.synchronize()
+    ro, rs, _ = oracle_chunk(inp, state_in=False)
+    assert_close(host64(o), ro[:, :, L], TOL["bf16"], "o")
+    assert_close(host64(S), rs, TOL["bf16"], "state")
+
+
+def test_prefill_then_decode_gated_delta():
+    """Delta rule: prefill L tokens with the chunk kernel, then decode token L+1
+    from its final state; equals the oracle over L+1 tokens."""
+    B, H, L, d = 2, 3, 150, 128
+    inp = W.make_chunk_inputs("gated_delta", "bf16", B, H, L + 1, d, d, seed=12)
+    q, k, v, lg, be = dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.log_gate), dev(inp.beta)
+    pre = lambda x: x[:, :, :L].contiguous()
+    _, S, _ = la.la_chunk_fwd("gated_delta", pre(q), pre(k), pre(v), pre(lg), pre(be), want_state=True)
+    last = lambda x: x[:, :, L].contiguous()
+    o = la.la_decode_step("gated_delta", last(q), last(k), last(v), last(lg), S, beta=last(be))
     torch.cuda.synchronize()
     ro, rs, _ = oracle_chunk(inp, state_in=False)
     assert_close(host64(o), ro[:, :, L], TOL["bf16"], "o")

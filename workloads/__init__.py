@@ -251,6 +251,7 @@ class DecodeStep:
     k: np.ndarray          # [N, H, dk]
     v: np.ndarray          # [N, H, dv]
     log_gate: np.ndarray   # [N, H] float32
+    beta: Optional[np.ndarray] = None  # [N, H] float32 (delta rule), when requested
 
 
 def make_decode_state(N: int, H: int, dk: int, dv: int, seed: int = 0,
@@ -268,8 +269,9 @@ def make_decode_state(N: int, H: int, dk: int, dv: int, seed: int = 0,
 
 
 def make_decode_step(N: int, H: int, dk: int, dv: int, step: int, seed: int = 0,
-                     dtype: str = "bf16") -> DecodeStep:
-    """Inputs of decode step ``step``: q,k,v ~ N(0,1)/sqrt(dk); gate log sigmoid(N(4,1))."""
+                     dtype: str = "bf16", with_beta: bool = False) -> DecodeStep:
+    """Inputs of decode step ``step``: q,k,v ~ N(0,1)/sqrt(dk); gate log sigmoid(N(4,1));
+    with_beta: also beta = sigmoid(N(0,1)) (delta rule)."""
     def qkv(tag: int, d: int) -> np.ndarray:
         x = stream(seed, tag, 1000 + step).standard_normal((N, H, d), dtype=np.float32)
         return _store((x / np.float32(math.sqrt(dk))).astype(np.float32), dtype)
@@ -278,7 +280,8 @@ def make_decode_step(N: int, H: int, dk: int, dv: int, step: int, seed: int = 0,
     k = qkv(TAG_K, dk)
     v = qkv(TAG_V, dv)
     lg = _sigmoid_log(stream(seed, TAG_GATE, 1000 + step).normal(4.0, 1.0, size=(N, H)))
-    return DecodeStep(q=q, k=k, v=v, log_gate=lg)
+    beta = _sigmoid(stream(seed, TAG_BETA, 1000 + step).normal(0.0, 1.0, size=(N, H))) if with_beta else None
+    return DecodeStep(q=q, k=k, v=v, log_gate=lg, beta=beta)
 
 
 def to_f64(x: np.ndarray) -> np.ndarray:
