@@ -18,12 +18,14 @@
 // shared through that XCD's L2. Per chunk:
 //   1. Q, K and V arrive as whole 16-byte row segments (every wave load covers
 //      complete rows), are converted to the operand type and written row-major
-//      into XOR-swizzled LDS tiles; V is also written scaled by exp(g_C - G_s)
-//      for the state update. Operands that need the token index in the K slots
+//      into padded LDS tiles; V is also written scaled by exp(g_C - G_s) for
+//      the state update. Operands that need the token index in the K slots
 //      (K^T and V^T) are read from the row-major tiles with the gfx950
-//      transpose load. The loads of chunk c+1 are issued right after chunk c is
-//      staged, so their latency hides behind chunk c's math. Wave 0 has built
-//      the gate tables (G, exp(G), exp(g_C - G), exp(g_C)) one chunk ahead.
+//      transpose load. When two chunks' tiles fit in LDS they are double
+//      buffered: chunk c+1 is staged while chunk c is computed and chunk c+2 is
+//      loaded into registers, with one barrier per chunk; otherwise a single
+//      buffer is staged between two barriers. Wave 0 builds the gate tables
+//      (G, exp(G), exp(g_C - G), exp(g_C)) ahead of the chunk that uses them.
 //   2. Query row blocks of 16 rows are assigned to waves by Roles: with C/8
 //      waves, wave pairs split the value columns of one row block; with C/32
 //      waves, each wave takes a row block and its mirror so the triangular score
