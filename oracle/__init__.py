@@ -43,6 +43,8 @@ def load(path: Optional[str] = None):
     lib.oracle_forward.restype = ctypes.c_int
     lib.oracle_decode_step.argtypes = [ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, L, L, L, ctypes.c_int]
     lib.oracle_decode_step.restype = ctypes.c_int
+    lib.oracle_short_conv.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, ctypes.c_int]
+    lib.oracle_short_conv.restype = ctypes.c_int
     lib.oracle_abi_version.restype = ctypes.c_int
     _lib, _lib_path = lib, path
     return lib
@@ -107,3 +109,25 @@ def decode_step(variant: str, q, k, v, log_gate, state, beta=None, threads: int 
     if st != 0:
         raise ValueError(f"oracle_decode_step failed with status {st}")
     return o, S
+
+
+def short_conv(x, w, state_in=None, threads: int = 0, lib=None):
+    """Causal depthwise short convolution over tokens (see ``oracle_short_conv``).
+
+    x: [B, H, L, d]; w: [H, d, K] (tap tau multiplies the input tau tokens back);
+    state_in: [B, H, K-1, d] previous inputs, oldest first (None = zeros).
+    Returns (y [B, H, L, d], state_out [B, H, K-1, d]) in float64.
+    """
+    lib = lib or load()
+    x, w = _c64(x), _c64(w)
+    B, H, L, d = x.shape
+    K = w.shape[-1]
+    assert w.shape == (H, d, K), (w.shape, (H, d, K))
+    s_in = _c64(state_in)
+    assert s_in is None or s_in.shape == (B, H, K - 1, d), s_in.shape
+    y = np.zeros((B, H, L, d), np.float64)
+    s_out = np.zeros((B, H, K - 1, d), np.float64)
+    st = lib.oracle_short_conv(_p(x), _p(w), _p(s_in), _p(y), _p(s_out), B, H, L, d, K, int(threads))
+    if st != 0:
+        raise ValueError(f"oracle_short_conv failed with status {st}")
+    return y, s_out

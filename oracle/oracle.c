@@ -177,3 +177,57 @@ int oracle_decode_step(int variant, const double *q, const double *k, const doub
     }
     return status;
 }
+
+/*
+ * Causal depthwise short convolution over the token axis, applied to one of the
+ * projected q, k or v (wln20 "LLM注意力优化：线性注意力", DeltaNet section: a
+ * short convolution after the q/k/v projections mixes each token with its
+ * nearest predecessors, kernel size 4 in DeltaNet). Per batch b, head h and
+ * channel c, independently ("depthwise"), with tap tau multiplying the input
+ * tau tokens back:
+ *     y_t[c] = sum_{tau=0}^{K-1} w[h][c][tau] * x_{t-tau}[c]
+ * The page writes the taps as w_tau; one set per channel is the depthwise
+ * reading. Inputs before the first token come from the sliding window of the K-1
+ * previous inputs (state_in, oldest first) or are zero when state_in is NULL.
+ * state_out receives the window after the last token: the K-1 most recent
+ * inputs, oldest first. No activation is applied.
+ * Layouts: x, y [B, H, L, d]; w [H, d, K]; state_in, state_out [B, H, K-1, d].
+ * Summation is sequential in tau, in float64.
+ */
+int oracle_short_conv(const double *x, const double *w, const double *state_in, double *y,
+                      double *state_out, long B, long H, long L, long d, long K, int nthreads)
+{
+    if (B < 0 || H < 0 || L < 0 || d <= 0 || K < 1) return OR_BAD_ARG;
+    if (B * H > 0 && L > 0 && (!x || !y || !w)) return OR_BAD_ARG;
+    const long W = K - 1;
+    int status = OR_OK;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) reduction(max : status)
+#endif
+    for (long bh = 0; bh < B * H; ++bh) {
+        const long h = bh % H;
+        /* the whole history of this head: W window values, then the L inputs */
+        double *hist = (double *)malloc(sizeof(double) * (size_t)((W + L) * d + 1));
+        if (!hist) {
+            status = OR_NO_MEM;
+            continue;
+        }
+        for (long j = 0; j < W; ++j)
+            for (long c = 0; c < d; ++c)
+                hist[j * d + c] = state_in ? state_in[(bh * W + j) * d + c] : 0.0;
+        for (long t = 0; t < L; ++t)
+            for (long c = 0; c < d; ++c) hist[(W + t) * d + c] = x[(bh * L + t) * d + c];
+        for (long t = 0; t < L; ++t)
+            for (long c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (long tau = 0; tau < K; ++tau)
+                    acc += w[(h * d + c) * K + tau] * hist[(W + t - tau) * d + c];
+                y[(bh * L + t) * d + c] = acc;
+            }
+        if (state_out)
+            for (long j = 0; j < W; ++j)
+                for (long c = 0; c < d; ++c) state_out[(bh * W + j) * d + c] = hist[(L + j) * d + c];
+        free(hist);
+    }
+    return status;
+}

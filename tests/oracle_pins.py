@@ -522,6 +522,92 @@ def pin_resume_all_variants(lib):
             assert _rel(zb, z) <= 1e-13
 
 
+# ---------------------------------------------------------------------------
+# Short causal depthwise convolution (wln20, DeltaNet section)
+# ---------------------------------------------------------------------------
+def pin_conv_library_convolve(lib):
+    """Each channel's output is the head of the full 1-D convolution of its
+    history (window, then inputs) with its own taps: numpy.convolve's
+    definition sum_tau w[tau] x[n - tau] is the page's formula, with the window
+    prepended (a textbook routine, not the oracle's loop)."""
+    r = _rng(30)
+    B, H, L, d, K = 2, 3, 19, 5, 4
+    x = r.standard_normal((B, H, L, d))
+    w = r.standard_normal((H, d, K))
+    st = r.standard_normal((B, H, K - 1, d))
+    y, so = oracle.short_conv(x, w, st, lib=lib)
+    ref = np.empty_like(y)
+    for b in range(B):
+        for h in range(H):
+            for c in range(d):
+                hist = np.concatenate([st[b, h, :, c], x[b, h, :, c]])
+                ref[b, h, :, c] = np.convolve(hist, w[h, c], mode="full")[K - 1:K - 1 + L]
+    assert _rel(y, ref) <= 1e-13, _rel(y, ref)
+    assert np.array_equal(so, x[:, :, L - K + 1:, :])
+    # no window: the sequence starts from zeros
+    y0, _ = oracle.short_conv(x, w, None, lib=lib)
+    for c in range(d):
+        ref0 = np.convolve(x[1, 2, :, c], w[2, c], mode="full")[:L]
+        assert _rel(y0[1, 2, :, c], ref0) <= 1e-13
+
+
+def pin_conv_fraction_bruteforce(lib):
+    """Exact rational evaluation of y_t = sum_tau w_tau x_{t-tau} on small
+    integers and halves (every fp64 step of the oracle is then exact)."""
+    r = _rng(31)
+    B, H, L, d, K = 1, 2, 7, 3, 3
+    x = r.integers(-4, 5, (B, H, L, d)).astype(np.float64)
+    w = r.integers(-3, 4, (H, d, K)).astype(np.float64) / 2
+    st = r.integers(-4, 5, (B, H, K - 1, d)).astype(np.float64)
+    y, _ = oracle.short_conv(x, w, st, lib=lib)
+    for h in range(H):
+        for c in range(d):
+            hist = [Fraction(int(v)) for v in st[0, h, :, c]] + [Fraction(int(v)) for v in x[0, h, :, c]]
+            for t in range(L):
+                acc = Fraction(0)
+                for tau in range(K):
+                    acc += Fraction(w[h, c, tau]) * hist[K - 1 + t - tau]
+                assert Fraction(y[0, h, t, c]) == acc, (h, c, t)
+
+
+def pin_conv_delta_taps_shift(lib):
+    """A one-hot tap at tau turns the convolution into a delay by tau tokens, with
+    the window supplying the first tau outputs; K = 1 is a per-channel scale."""
+    r = _rng(32)
+    B, H, L, d, K = 2, 2, 9, 4, 4
+    x = r.standard_normal((B, H, L, d))
+    st = r.standard_normal((B, H, K - 1, d))
+    hist = np.concatenate([st, x], axis=2)
+    for tau in range(K):
+        w = np.zeros((H, d, K))
+        w[:, :, tau] = 1.0
+        y, _ = oracle.short_conv(x, w, st, lib=lib)
+        assert np.array_equal(y, hist[:, :, K - 1 - tau:K - 1 - tau + L, :]), tau
+    w1 = r.standard_normal((H, d, 1))
+    y1, s1 = oracle.short_conv(x, w1, None, lib=lib)
+    assert np.array_equal(y1, x * w1[None, :, None, :, 0])
+    assert s1.shape == (B, H, 0, d)
+
+
+def pin_conv_chunked_carry(lib):
+    """Convolving a sequence in pieces, carrying the window of the last K-1
+    inputs, equals one pass; pieces shorter than the window shift it."""
+    r = _rng(33)
+    B, H, d, K = 2, 2, 3, 4
+    x = r.standard_normal((B, H, 20, d))
+    w = r.standard_normal((H, d, K))
+    st0 = r.standard_normal((B, H, K - 1, d))
+    y, s = oracle.short_conv(x, w, st0, lib=lib)
+    for cuts in ((7,), (1, 2, 3), (2, 17)):
+        parts, st, t0 = [], st0, 0
+        for t1 in list(cuts) + [20]:
+            yp, st = oracle.short_conv(x[:, :, t0:t1], w, st, lib=lib)
+            parts.append(yp)
+            t0 = t1
+        assert np.array_equal(np.concatenate(parts, axis=2), y), cuts
+        assert np.array_equal(st, s), cuts
+
+
 ALL_PINS = [
     pin_plain_quadratic, pin_plain_fraction_bruteforce, pin_plain_final_state,
     pin_normalized_quadratic, pin_normalized_constant_v, pin_normalized_hull,
@@ -531,4 +617,6 @@ ALL_PINS = [
     pin_gdn_fraction_product_expansion, pin_gdn_chunkwise_wy,
     pin_decode_one_decay_step, pin_prefill_then_decode, pin_resume_all_variants,
     pin_decode_gdn_step, pin_prefill_then_decode_gdn,
+    pin_conv_library_convolve, pin_conv_fraction_bruteforce, pin_conv_delta_taps_shift,
+    pin_conv_chunked_carry,
 ]

@@ -30,6 +30,13 @@ MUTANTS = {
     "plain_transposed_write": ("S[i * dv + j] += kt[i] * vt[j];", "S[i * dv + j] += kt[j % dk] * vt[i % dv];"),
     "readout_uses_key": ("acc += S[i * dv + j] * qt[i];\n            ot[j] = acc;",
                          "acc += S[i * dv + j] * kt[i];\n            ot[j] = acc;"),
+    "conv_taps_reversed": ("acc += w[(h * d + c) * K + tau] * hist[(W + t - tau) * d + c];",
+                           "acc += w[(h * d + c) * K + (K - 1 - tau)] * hist[(W + t - tau) * d + c];"),
+    "conv_head_weights_shared": ("acc += w[(h * d + c) * K + tau]", "acc += w[c * K + tau]"),
+    "conv_window_ignored": ("hist[j * d + c] = state_in ? state_in[(bh * W + j) * d + c] : 0.0;",
+                            "hist[j * d + c] = 0.0;"),
+    "conv_window_out_stale": ("state_out[(bh * W + j) * d + c] = hist[(L + j) * d + c];",
+                              "state_out[(bh * W + j) * d + c] = hist[(L + j - (L > 0)) * d + c];"),
     "exclusive_mask": ("double *ot = o + t * dv;\n",
                        "double *ot = o + t * dv;\n        if (t > 0) { for (long j = 0; j < dv; ++j) { double acc = 0.0; for (long i = 0; i < dk; ++i) acc += S[i * dv + j] * qt[i]; ot[j] = acc; } }\n"),
 }
