@@ -6,9 +6,10 @@ already resident in HBM:
   - chunk workloads: one la_chunk_fwd (C = 64, fp32 output and final state);
   - decode workload: 100 back-to-back la_decode_step calls (one "step" = 100
     tokens per sequence-head, as the workload is quoted).
+  - short-convolution workload: one la_short_conv over q, k and v.
 The headline workload (the JSON line's value) is the normalized kernel linear
-attention at B=8, H=16, L=2048, d=64; --all (default) also times the four other
-workloads and reports them under "workloads". Every workload is timed with HIP
+attention at B=8, H=16, L=2048, d=64; by default the other workloads are timed
+too and reported under "workloads". Every workload is timed with HIP
 events on the stream the kernels run on, over K timed steps after W warm-up steps.
 Working sets below twice the 256 MB Infinity Cache are rotated over several
 input copies so that the timed steps read HBM, not the cache.
@@ -84,6 +85,17 @@ def chunk_work(c: dict) -> tuple[float, float]:
     if c["variant"] == "gated_delta":
         nbytes += BH * L * 4                                     # beta
     nbytes += BH * dk * dv * 4                                   # final state
+    return flop, nbytes
+
+
+def conv_work(c: dict) -> tuple[float, float]:
+    """(flop, bytes) of one short convolution over q, k and v: each element read
+    once and written once, K multiply-adds per output element; taps once."""
+    BH, L, K = c["B"] * c["H"], c["L"], c["K"]
+    esz = 2 if c["dtype"] == "bf16" else 4
+    elems = BH * L * (2 * c["dk"] + c["dv"])
+    flop = 2.0 * K * elems
+    nbytes = 2 * elems * esz + c["H"] * (2 * c["dk"] + c["dv"]) * K * 4
     return flop, nbytes
 
 
@@ -197,6 +209,36 @@ def bench_decode(name: str, steps: int, warmup: int, device, variant: str = "dec
                 N=N, H=H, d_k=dk, d_v=dv, decode_launches_per_step=nsteps)
 
 
+def bench_conv(name: str, steps: int, warmup: int, device) -> dict:
+    import torch
+    import chunkwise_linear_rnn_causal_amd as la
+    c = W.CONFIGS[name]
+    ci = W.config_conv_inputs(name, seed=0)
+    flop, nbytes = conv_work(c)
+    copies = max(1, min(4, math.ceil(2 * CACHE_BYTES / nbytes)))
+    taps = [to_dev(t, device) for t in ci.taps]
+    sets = []
+    for _ in range(copies):
+        xs = [to_dev(x, device) for x in ci.x]
+        ys = [torch.empty_like(x) for x in xs]
+        sets.append((xs, ys))
+    stream = torch.cuda.current_stream(device)
+
+    def step(i):
+        xs, ys = sets[i % copies]
+        la.la_short_conv(*xs, *taps, q_out=ys[0], k_out=ys[1], v_out=ys[2], stream=stream)
+
+    ms, wall_ms = time_steps(step, steps, warmup, stream)
+    t = ms / 1e3
+    toks = c["B"] * c["L"]
+    return dict(workload=name, variant="short_conv_qkv", tokens_per_s=toks / t, ms_per_step=t * 1e3,
+                wall_ms_per_step=wall_ms, flop=flop, bytes=nbytes,
+                achieved_gbs=nbytes / t / 1e9, achieved_tflops=flop / t / 1e12,
+                hbm_frac=nbytes / t / 1e9 / HBM_PEAK_GBS, mfma_frac=None,
+                roofline_frac=nbytes / (HBM_PEAK_GBS * 1e9) / t, input_copies=copies,
+                B=c["B"], H=c["H"], L=c["L"], d_k=c["dk"], d_v=c["dv"], K=c["K"])
+
+
 def cpu_baseline(name: str, min_seconds: float = 10.0) -> dict:
     """Time the fp64 oracle over the whole workload on the host cores."""
     import oracle
@@ -273,9 +315,10 @@ def main() -> int:
     for name in names:
         kind = W.CONFIGS[name]["kind"]
         print(f"[bench] {name}", file=sys.stderr, flush=True)
-        steps = args.steps if kind == "chunk" else max(1, min(args.steps, 5))
-        warm = args.warmup if kind == "chunk" else max(1, min(args.warmup, 2))
-        results[name] = (bench_chunk if kind == "chunk" else bench_decode)(name, steps, warm, device)
+        steps = args.steps if kind != "decode" else max(1, min(args.steps, 5))
+        warm = args.warmup if kind != "decode" else max(1, min(args.warmup, 2))
+        fn = {"chunk": bench_chunk, "decode": bench_decode, "conv": bench_conv}[kind]
+        results[name] = fn(name, steps, warm, device)
         r = results[name]
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['achieved_gbs']:.0f} GB/s, "
               f"{r['achieved_tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)

@@ -8,6 +8,7 @@ gfx950, calls raise.
 
     o, state, z = la_chunk_fwd("decay", q, k, v, log_gate=lg, C=64, want_state=True)
     o = la_decode_step("decay", q, k, v, log_gate, state)   # state updated in place
+    qc, kc, vc, *_ = la_short_conv(q, k, v, w_q, w_k, w_v)  # causal depthwise conv
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "linattn.h")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 VARIANTS = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3}
-EXPORTS = ("la_chunk_fwd_workspace_size", "la_chunk_fwd", "la_decode_step",
+EXPORTS = ("la_chunk_fwd_workspace_size", "la_chunk_fwd", "la_decode_step", "la_short_conv",
            "la_status_str", "la_abi_version")
 
 _lib = None
@@ -53,6 +54,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  i, i, i, i, i, i, vp, sz, vp]
     lib.la_decode_step.restype = i
     lib.la_decode_step.argtypes = [i, i, i, vp, vp, vp, fp, fp, fp, vp, i, i, i, i, vp]
+    lib.la_short_conv.restype = i
+    lib.la_short_conv.argtypes = [i, vp, vp, vp, fp, fp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  i, i, i, i, i, i, vp]
     _lib = lib
     return lib
 
@@ -158,5 +162,49 @@ def la_decode_step(variant: str, q, k, v, log_gate, state, *, o=None, out_dtype=
     return o
 
 
-__all__ = ["la_chunk_fwd", "la_chunk_fwd_workspace_size", "la_decode_step", "la_status_str",
-           "la_abi_version", "LinAttnError", "VARIANTS", "load_library"]
+def la_short_conv(q=None, k=None, v=None, w_q=None, w_k=None, w_v=None, *, q_state_in=None,
+                  k_state_in=None, v_state_in=None, q_out=None, k_out=None, v_out=None,
+                  q_state_out=None, k_state_out=None, v_state_out=None, want_state: bool = False,
+                  stream=None) -> Tuple:
+    """Causal depthwise short convolution of any of q, k, v in one launch.
+
+    q, k: [B, H, L, d_k]; v: [B, H, L, d_v] (bf16 or fp32, all the same dtype);
+    w_*: [H, d, K] fp32 taps (tap tau multiplies the input tau tokens back);
+    *_state_in: [B, H, K-1, d] windows of preceding inputs (None = zeros).
+    Returns (q_out, k_out, v_out, q_state_out, k_state_out, v_state_out); entries
+    of skipped tensors are None, windows are None unless requested (want_state or
+    a passed *_state_out, which may be the same tensor's *_state_in).
+    """
+    import torch
+    lib = load_library()
+    xs = [q, k, v]
+    ws = [w_q, w_k, w_v]
+    given = [x for x in xs if x is not None]
+    if not given or any((x is None) != (w is None) for x, w in zip(xs, ws)):
+        raise ValueError("la_short_conv needs at least one of q, k, v, each with its taps")
+    ref = given[0]
+    B, H, L = ref.shape[:3]
+    d_k = q.shape[-1] if q is not None else (k.shape[-1] if k is not None else 8)
+    d_v = v.shape[-1] if v is not None else 8
+    K = next(w for w, x in zip(ws, xs) if x is not None).shape[-1]
+    outs = [q_out, k_out, v_out]
+    sins = [q_state_in, k_state_in, v_state_in]
+    souts = [q_state_out, k_state_out, v_state_out]
+    for i, x in enumerate(xs):
+        if x is None:
+            continue
+        if outs[i] is None:
+            outs[i] = torch.empty_like(x)
+        if want_state and souts[i] is None:
+            souts[i] = torch.empty((B, H, K - 1, x.shape[-1]), dtype=x.dtype, device=x.device)
+    st = lib.la_short_conv(_dt(ref), *[_ptr(x) for x in xs], *[_ptr(w) for w in ws],
+                           *[_ptr(x) for x in sins], *[_ptr(x) for x in outs],
+                           *[_ptr(x) for x in souts], B, H, L, d_k, d_v, K,
+                           _stream(ref.device, stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_short_conv")
+    return (*outs, *souts)
+
+
+__all__ = ["la_chunk_fwd", "la_chunk_fwd_workspace_size", "la_decode_step", "la_short_conv",
+           "la_status_str", "la_abi_version", "LinAttnError", "VARIANTS", "load_library"]

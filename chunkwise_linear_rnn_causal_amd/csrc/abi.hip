@@ -173,6 +173,18 @@ hipError_t dispatch_decode(int d_k, int d_v, const DecodeArgs &a, hipStream_t st
 }
 
 // Supported (input, output) dtype pairs: bf16 -> fp32, bf16 -> bf16, fp32 -> fp32.
+template <typename T>
+hipError_t dispatch_short_conv(int K, const ConvArgs &a, unsigned blocks, hipStream_t st) {
+    switch (K) {
+        case 1: return launch_short_conv<T, 1>(a, blocks, st);
+        case 2: return launch_short_conv<T, 2>(a, blocks, st);
+        case 3: return launch_short_conv<T, 3>(a, blocks, st);
+        case 4: return launch_short_conv<T, 4>(a, blocks, st);
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
 bool dtype_pair_ok(la_dtype dt, la_dtype o_dt) {
     return (dt == LA_BF16 && (o_dt == LA_F32 || o_dt == LA_BF16)) || (dt == LA_F32 && o_dt == LA_F32);
 }
@@ -331,6 +343,90 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
         else if (o_dt == LA_F32) e = dispatch_decode<V_PLAIN, bf16, float>(d_k, d_v, a, st);
         else e = dispatch_decode<V_PLAIN, bf16, bf16>(d_k, d_v, a, st);
     }
+    return from_hip(e);
+}
+
+la_status la_short_conv(la_dtype dt, const void *q, const void *k, const void *v,
+                        const float *w_q, const float *w_k, const float *w_v,
+                        const void *q_state_in, const void *k_state_in, const void *v_state_in,
+                        void *q_out, void *k_out, void *v_out, void *q_state_out,
+                        void *k_state_out, void *v_state_out, int B, int H, int L, int d_k,
+                        int d_v, int K, void *stream) {
+    if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || L < 0 || K < 1 || d_k < 1 || d_v < 1) return LA_ERR_INVALID_ARG;
+    if (K > 4) return LA_ERR_UNSUPPORTED;
+    if (d_k % 8 || d_v % 8 || d_k > 4096 || d_v > 4096) return LA_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H;
+    const size_t es = elem_size(dt);
+    struct Tensor {
+        const void *x;
+        const float *w;
+        const void *si;
+        void *y;
+        void *so;
+        int d;
+    };
+    const Tensor all[3] = {{q, w_q, q_state_in, q_out, q_state_out, d_k},
+                           {k, w_k, k_state_in, k_out, k_state_out, d_k},
+                           {v, w_v, v_state_in, v_out, v_state_out, d_v}};
+    Tensor use[3];
+    int n = 0;
+    for (const Tensor &t : all) {  // a tensor is convolved when its taps are given
+        if (!t.w) {
+            if (t.x || t.si || t.y || t.so) return LA_ERR_INVALID_ARG;
+            continue;
+        }
+        if (L > 0 && (!t.x || !t.y)) return LA_ERR_INVALID_ARG;
+        use[n++] = t;
+    }
+    if (n == 0) return LA_ERR_INVALID_ARG;
+    // alignment, then aliasing: outputs overlap nothing except that a window may
+    // be updated in place (state_out == state_in of the same tensor)
+    Span in_sp[9], out_sp[6];
+    int ni = 0, no = 0;
+    for (int i = 0; i < n; ++i) {
+        const Tensor &t = use[i];
+        const void *ptrs[] = {t.x, t.w, t.si, t.y, t.so};
+        for (const void *p : ptrs)
+            if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
+        const size_t xb = (size_t)BH * L * t.d * es, wb = (size_t)H * t.d * K * 4;
+        const size_t sb = (size_t)BH * (K - 1) * t.d * es;
+        if (t.so && t.si && t.so != t.si && overlap(Span{t.so, sb}, Span{t.si, sb}))
+            return LA_ERR_INVALID_ARG;
+        in_sp[ni++] = Span{t.x, xb};
+        in_sp[ni++] = Span{t.w, wb};
+        if (t.si != t.so) in_sp[ni++] = Span{t.si, sb};
+        out_sp[no++] = Span{t.y, xb};
+        out_sp[no++] = Span{t.so, sb};
+    }
+    for (int o = 0; o < no; ++o) {
+        for (int i = 0; i < ni; ++i)
+            if (overlap(out_sp[o], in_sp[i])) return LA_ERR_INVALID_ARG;
+        for (int o2 = o + 1; o2 < no; ++o2)
+            if (overlap(out_sp[o], out_sp[o2])) return LA_ERR_INVALID_ARG;
+    }
+    const int tt = dt == LA_BF16 ? conv_tile<bf16>() : conv_tile<float>();
+    const int64_t NT = L > 0 ? ((int64_t)L + tt - 1) / tt : 1;
+    int64_t blk[3] = {0, 0, 0}, total = 0;
+    for (int i = 0; i < n; ++i) {
+        blk[i] = (BH * NT * (use[i].d / 8) + 255) / 256;
+        total += blk[i];
+    }
+    if (total * 256 > (int64_t)UINT32_MAX || NT > INT32_MAX || BH > INT32_MAX)
+        return LA_ERR_UNSUPPORTED;
+
+    const la_status s = check_device();
+    if (s != LA_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    ConvArgs a{};
+    ConvTensor *slots[3] = {&a.t0, &a.t1, &a.t2};
+    for (int i = 0; i < n; ++i)
+        *slots[i] = ConvTensor{use[i].x, use[i].y, use[i].si, use[i].so, use[i].w, use[i].d};
+    a.blk1 = (unsigned)(n > 1 ? blk[0] : total);
+    a.blk2 = (unsigned)(n > 2 ? blk[0] + blk[1] : total);
+    a.BH = (int)BH; a.H = H; a.L = L; a.NT = (int)NT;
+    const hipError_t e = dt == LA_BF16 ? dispatch_short_conv<bf16>(K, a, (unsigned)total, st)
+                                       : dispatch_short_conv<float>(K, a, (unsigned)total, st);
     return from_hip(e);
 }
 

@@ -2,6 +2,7 @@
 #include "chunk_fwd_impl.hpp"
 #include "decode_impl.hpp"
 #include "gdn_prep_impl.hpp"
+#include "short_conv_impl.hpp"
 
 namespace la {
 
@@ -68,5 +69,12 @@ template hipError_t launch_decode<V_DECAY, bf16, bf16, 128, 64>(const DecodeArgs
 template hipError_t launch_decode<V_GDN, bf16, bf16, 128, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_DECAY, bf16, bf16, 128, 128>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_GDN, bf16, bf16, 128, 128>(const DecodeArgs &, hipStream_t);
+
+
+// short convolution: (type, taps)
+template hipError_t launch_short_conv<bf16, 1>(const ConvArgs &, unsigned, hipStream_t);
+template hipError_t launch_short_conv<bf16, 2>(const ConvArgs &, unsigned, hipStream_t);
+template hipError_t launch_short_conv<bf16, 3>(const ConvArgs &, unsigned, hipStream_t);
+template hipError_t launch_short_conv<bf16, 4>(const ConvArgs &, unsigned, hipStream_t);
 
 }  // namespace la

@@ -2,6 +2,7 @@
 #include "chunk_fwd_impl.hpp"
 #include "decode_impl.hpp"
 #include "gdn_prep_impl.hpp"
+#include "short_conv_impl.hpp"
 
 namespace la {
 
@@ -58,5 +59,12 @@ template hipError_t launch_decode<V_GDN, float, float, 128, 128>(const DecodeArg
 template hipError_t launch_gdn_prep<float, 32, 64>(const PrepArgs &, hipStream_t);
 template hipError_t launch_gdn_prep<float, 64, 64>(const PrepArgs &, hipStream_t);
 template hipError_t launch_gdn_prep<float, 128, 64>(const PrepArgs &, hipStream_t);
+
+
+// short convolution: (type, taps)
+template hipError_t launch_short_conv<float, 1>(const ConvArgs &, unsigned, hipStream_t);
+template hipError_t launch_short_conv<float, 2>(const ConvArgs &, unsigned, hipStream_t);
+template hipError_t launch_short_conv<float, 3>(const ConvArgs &, unsigned, hipStream_t);
+template hipError_t launch_short_conv<float, 4>(const ConvArgs &, unsigned, hipStream_t);
 
 }  // namespace la

@@ -39,6 +39,22 @@ struct DecodeArgs {
     int NH;
 };
 
+// Causal depthwise short convolution: up to three tensors (any of q, k, v) in one
+// launch; tensor i owns blocks [blk_i, blk_{i+1}).
+struct ConvTensor {
+    const void *x;              // [BH, L, d] input
+    void *y;                    // [BH, L, d] output (same type)
+    const void *s_in;           // [BH, K-1, d] incoming window, oldest first, or nullptr (zeros)
+    void *s_out;                // [BH, K-1, d] outgoing window or nullptr; may equal s_in
+    const float *w;             // [H, d, K] taps, tap tau multiplies x_{t-tau}
+    int d;                      // channels, a multiple of 8
+};
+struct ConvArgs {
+    ConvTensor t0, t1, t2;
+    unsigned blk1, blk2;        // first block of tensors 1 and 2 (unused ones: past the grid)
+    int BH, H, L, NT;           // NT = max(1, ceil(L / TT)) token tiles
+};
+
 // TI: input type (bf16 or float); TO: output type (float or bf16); DVT: value
 // columns per workgroup; NW: waves per workgroup. The instantiated combinations
 // are listed in kernels_*.hip and selected by abi.hip.
@@ -50,5 +66,11 @@ hipError_t launch_gdn_prep(const PrepArgs &a, hipStream_t st);
 
 template <int VAR, typename TI, typename TO, int DK, int DV>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+
+// Tokens per thread of the short convolution (the host sizes the grid with it).
+template <typename T> constexpr int conv_tile() { return sizeof(T) == 2 ? 16 : 8; }
+
+template <typename T, int K>
+hipError_t launch_short_conv(const ConvArgs &a, unsigned blocks, hipStream_t st);
 
 }  // namespace la

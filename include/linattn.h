@@ -150,6 +150,44 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
                          const float *beta, float *state, void *o, int N, int H, int d_k,
                          int d_v, void *stream);
 
+/*
+ * Causal depthwise short convolution over the token axis: the token-mixing step
+ * applied to the projected q, k and v before the linear-attention recurrence
+ * (wln20 "LLM注意力优化：线性注意力", DeltaNet section; kernel size 4 there).
+ * For each of q, k, v that is given, per batch b, head h and channel c, with one
+ * set of K taps per channel (depthwise):
+ *     y_t[c] = sum_{tau=0}^{K-1} w[h][c][tau] * x_{t-tau}[c],   t = 0..L-1,
+ * summed in fp32 and rounded to dt (bf16: to nearest even). Inputs before t = 0
+ * come from the window state_in, the K-1 inputs preceding this call, oldest
+ * first (NULL = zeros). state_out receives the window after the call: the K-1
+ * most recent inputs, oldest first, the older ones taken from state_in when
+ * L < K-1. A sequence can therefore be convolved in pieces, and L = 1 is the
+ * decode step. No activation is applied. One launch covers all given tensors.
+ *   dt           dtype of every input, output and window: LA_BF16 or LA_F32.
+ *   w_q, w_k, w_v  float32 taps [H, d, K] (d = d_k or d_v); tap tau multiplies
+ *                the input tau tokens back. A tensor is convolved when its taps
+ *                are given; NULL taps skip it, and then its input, windows and
+ *                output must be NULL too. At least one tensor is convolved.
+ *   q, k, v      inputs [B,H,L,d_k], [B,H,L,d_k], [B,H,L,d_v] of the convolved
+ *                tensors, required when L > 0.
+ *   *_state_in   [B,H,K-1,d] or NULL.
+ *   q_out, k_out, v_out  outputs, shaped and typed like their inputs; required
+ *                for a given tensor when L > 0. They must not overlap any input,
+ *                tap array, window or other output (no in-place y = x).
+ *   *_state_out  [B,H,K-1,d] or NULL (not written). May equal the same tensor's
+ *                state_in (window updated in place); must not otherwise overlap
+ *                any other buffer.
+ *   B, H >= 1; L >= 0; d_k, d_v multiples of 8, at most 4096 (else
+ *   LA_ERR_UNSUPPORTED); K in 1..4 (K > 4: LA_ERR_UNSUPPORTED). Pointers 16-byte
+ *   aligned.
+ */
+la_status la_short_conv(la_dtype dt, const void *q, const void *k, const void *v,
+                        const float *w_q, const float *w_k, const float *w_v,
+                        const void *q_state_in, const void *k_state_in, const void *v_state_in,
+                        void *q_out, void *k_out, void *v_out, void *q_state_out,
+                        void *k_state_out, void *v_state_out, int B, int H, int L, int d_k,
+                        int d_v, int K, void *stream);
+
 /* Static string naming a status code. */
 const char *la_status_str(la_status s);
 

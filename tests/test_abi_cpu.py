@@ -54,7 +54,7 @@ def test_workspace_sizes():
     # one fused pass for the variants without the delta rule
     for var in (PLAIN, NORM, DECAY):
         assert wsize(var=var) == (0, 0)
-    # delta rule: W [BH, Lp, dk] (rounded to 256 B) + U~ [BH, dv, Lp], Lp = 128
+    # delta rule: W [BH, Lp, dk] (rounded to 256 B) + U~ [BH, Lp, dv], Lp = 128
     st, n = wsize()
     w = -(-2 * 3 * 128 * 64 * 2 // 256) * 256
     assert st == 0 and n == w + 2 * 3 * 128 * 32 * 2
@@ -107,3 +107,43 @@ def dec(var=DECAY, dt=BF16, odt=F32, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, l
 ])
 def test_decode_step_rejects(kw, expect):
     assert dec(**kw) == expect
+
+
+def conv(dt=BF16, q=FAKE, k=None, v=None, wq=0x200000, wk=None, wv=None, qsi=None, ksi=None, vsi=None,
+         qo=0x800000000, ko=None, vo=None, qso=None, kso=None, vso=None, B=1, H=2, L=64, dk=64, dv=64,
+         K=4):
+    return la.load_library().la_short_conv(dt, q, k, v, wq, wk, wv, qsi, ksi, vsi, qo, ko, vo, qso, kso,
+                                           vso, B, H, L, dk, dv, K, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dt=5), INVALID), (dict(B=0), INVALID), (dict(L=-1), INVALID), (dict(K=0), INVALID),
+    (dict(K=5), UNSUPPORTED), (dict(dk=12), UNSUPPORTED), (dict(dk=8192), UNSUPPORTED),
+    (dict(q=None, wq=None, qo=None), INVALID),            # nothing to convolve
+    (dict(wq=None), INVALID),                             # input without taps
+    (dict(q=None), INVALID),                              # taps without input (L > 0)
+    (dict(qo=None), INVALID),                             # output missing
+    (dict(ko=0x900000000), INVALID),                      # output for a skipped tensor
+    (dict(ksi=0x900000000), INVALID),                     # window for a skipped tensor
+    (dict(q=FAKE + 8), INVALID),                          # misaligned
+    (dict(qo=FAKE), INVALID),                             # in place y = x
+    (dict(qo=FAKE + 0x1000), INVALID),                    # output overlaps the input
+    (dict(k=0x300000, wk=0x400000, ko=0x800000000 + 0x2000), INVALID),  # outputs overlap
+    (dict(k=0x300000, wk=0x400000, ko=0x300000 + 0x100), INVALID),      # k output overlaps k
+    (dict(v=0x300000, wv=0x400000, vo=FAKE + 0x10), INVALID),           # v output overlaps q
+    (dict(qsi=0xA00000000, qso=0xA00000010), INVALID),    # partial window overlap
+    (dict(qso=0x200000), INVALID),                        # window written over the taps
+])
+def test_short_conv_rejects(kw, expect):
+    assert conv(**kw) == expect
+
+
+@pytest.mark.parametrize("kw", [
+    dict(), dict(qsi=0xA00000000, qso=0xA00000000),       # window updated in place
+    dict(L=0, qo=None), dict(L=0, q=None, qo=None), dict(K=1), dict(q=None, wq=None, qo=None, v=0x300000, wv=0x400000,
+                                        vo=0x900000000, dv=32),
+])
+def test_short_conv_valid_arguments_reach_the_device_check(kw):
+    # on a host without a usable gfx950 device the call fails only at the device
+    # check, after every argument was accepted
+    assert conv(**kw) not in (INVALID,)

@@ -1,8 +1,9 @@
-"""GPU parity at the full sizes of the five workloads, in the launch configuration
+"""GPU parity at the full sizes of the workloads, in the launch configuration
 the benchmark times (la_chunk_fwd with C = 64 and a final-state output; 100
-back-to-back la_decode_step calls). The oracle checks sampled batch-heads, which
-the seeded generator regenerates on their own (every (tensor, b, h) slice has its
-own random stream), plus the whole first decode step."""
+back-to-back la_decode_step calls; one la_short_conv). The oracle checks sampled
+batch-heads, which the seeded generator regenerates on their own (every (tensor,
+b, h) slice has its own random stream), the whole first decode step, and every
+element of the short convolution."""
 import numpy as np
 import pytest
 import torch
@@ -74,3 +75,25 @@ def test_full_size_decode_config():
     e_o = assert_close(got_o, ro, TOL["bf16"], "step 100 o")
     e_s = assert_close(got_S, Sref, 1e-4, "step 100 state")
     print(f"[config] decode step100 err_o={e_o:.2e} err_state={e_s:.2e}", flush=True)
+
+
+def test_full_size_short_conv_config():
+    """The short convolution at the benchmark's size (q, k, v of the delta-rule
+    workload, K = 4), one launch as timed; every element against the oracle
+    within the per-element fp32-sum + bf16-rounding bound."""
+    name = "short_conv_qkv_bf16_b2h16_l8192_d128_k4"
+    print(f"[config] {name}", flush=True)
+    ci = W.config_conv_inputs(name, seed=0)
+    xs = [dev(x) for x in ci.x]
+    ws = [dev(t) for t in ci.taps]
+    outs = la.la_short_conv(*xs, *ws, want_state=True)
+    torch.cuda.synchronize()
+    for i, tname in enumerate("qkv"):
+        x = ci.f64("x", i)
+        ry, rs = oracle.short_conv(x, ci.taps[i], None)
+        got = host64(outs[i])
+        bound_src, _ = oracle.short_conv(np.abs(x), np.abs(ci.taps[i]), None)
+        lim = 1e-6 * bound_src + 2.0 ** -8 * np.abs(ry)
+        assert bool(np.all(np.abs(got - ry) <= lim)), f"{tname}: out of bound"
+        assert np.array_equal(host64(outs[3 + i]), rs), f"{tname} window"
+        print(f"[config] {name} {tname} max|err|={float(np.abs(got - ry).max()):.2e}", flush=True)

@@ -14,7 +14,10 @@ q=1, k=2, v=3, gate=4, beta=5, state=6. A slice can therefore be regenerated alo
 (the oracle checks sampled heads at full size) and the full tensors can be filled
 from several threads. Decode workloads draw their initial state from
 SeedSequence([seed, 6, n]) per sequence n and the inputs of step i from
-SeedSequence([seed, tag, 1000 + i]) as whole [N, H, d] arrays.
+SeedSequence([seed, tag, 1000 + i]) as whole [N, H, d] arrays. Short-convolution
+inputs draw each (tensor, b, h) slice like the chunk workloads (tags 1-3), their
+taps per tensor from SeedSequence([seed, 7, tensor]) and their incoming windows
+per slice from SeedSequence([seed, 8, tensor, b, h]).
 
 bf16 values are produced by round-to-nearest-even from float32 and kept as their
 raw uint16 bit patterns; ``bf16_bits_to_f32`` widens them exactly.
@@ -30,6 +33,7 @@ from typing import Dict, Optional, Sequence, Tuple
 import numpy as np
 
 TAG_Q, TAG_K, TAG_V, TAG_GATE, TAG_BETA, TAG_STATE = 1, 2, 3, 4, 5, 6
+TAG_CONV_W, TAG_CONV_WINDOW = 7, 8
 
 VARIANTS = ("plain", "normalized", "decay", "gated_delta")
 
@@ -51,6 +55,9 @@ CONFIGS: Dict[str, dict] = {
     "gated_delta_bf16_b2h16_l8192_d128": dict(
         kind="chunk", variant="gated_delta", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, C=64,
         recipe="gdn"),
+    # the short convolution in front of the delta rule, at that workload's q, k, v shapes
+    "short_conv_qkv_bf16_b2h16_l8192_d128_k4": dict(
+        kind="conv", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, K=4, recipe="conv"),
 }
 
 # Recipe used for each variant when a test builds a small case of that variant.
@@ -286,3 +293,69 @@ def make_decode_step(N: int, H: int, dk: int, dv: int, step: int, seed: int = 0,
 
 def to_f64(x: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(x).astype(np.float64) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Short causal depthwise convolution
+# ----------------------------------------------------------------------------
+@dataclass
+class ConvInputs:
+    """Inputs of one short-convolution call over q, k and v.
+
+    x[i], window[i]: storage dtype (uint16 bf16 bits or float32); taps: float32.
+    i = 0, 1, 2 for q, k, v."""
+    dtype: str
+    B: int
+    H: int
+    L: int
+    dk: int
+    dv: int
+    K: int
+    x: list
+    taps: list
+    window: list
+
+    def f64(self, what: str, i: int) -> Optional[np.ndarray]:
+        arr = getattr(self, what)[i]
+        return None if arr is None else to_f64(arr)
+
+
+def make_conv_inputs(dtype: str, B: int, H: int, L: int, dk: int, dv: int, K: int = 4,
+                     seed: int = 0, with_window: bool = False,
+                     threads: Optional[int] = None) -> ConvInputs:
+    """q, k, v ~ N(0, 1) (the projections' outputs before the convolution); taps
+    U(-1/sqrt(K), 1/sqrt(K)) per channel, the usual initialisation of a depthwise
+    1-D convolution (fan-in K); windows N(0, 1) when requested."""
+    sdt = np.uint16 if dtype == "bf16" else np.float32
+    ds = (dk, dk, dv)
+    xs = [np.empty((B * H, L, d), sdt) for d in ds]
+
+    def fill(j: int) -> None:
+        i, bh = divmod(j, B * H)
+        b, h = divmod(bh, H)
+        xs[i][bh] = _store(stream(seed, (TAG_Q, TAG_K, TAG_V)[i], b, h).standard_normal(
+            (L, ds[i]), dtype=np.float32), dtype)
+
+    nthr = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(nthr) as ex:
+        list(ex.map(fill, range(3 * B * H)))
+    bound = 1.0 / math.sqrt(K)
+    taps = [stream(seed, TAG_CONV_W, i).uniform(-bound, bound, size=(H, ds[i], K)).astype(np.float32)
+            for i in range(3)]
+    win = [None, None, None]
+    if with_window:
+        for i in range(3):
+            w = np.empty((B * H, K - 1, ds[i]), sdt)
+            for bh in range(B * H):
+                b, h = divmod(bh, H)
+                w[bh] = _store(stream(seed, TAG_CONV_WINDOW, i, b, h).standard_normal(
+                    (K - 1, ds[i]), dtype=np.float32), dtype)
+            win[i] = w.reshape(B, H, K - 1, ds[i])
+    return ConvInputs(dtype=dtype, B=B, H=H, L=L, dk=dk, dv=dv, K=K,
+                      x=[x.reshape(B, H, L, d) for x, d in zip(xs, ds)], taps=taps, window=win)
+
+
+def config_conv_inputs(name: str, seed: int = 0) -> ConvInputs:
+    c = CONFIGS[name]
+    assert c["kind"] == "conv", name
+    return make_conv_inputs(c["dtype"], c["B"], c["H"], c["L"], c["dk"], c["dv"], c["K"], seed=seed)
