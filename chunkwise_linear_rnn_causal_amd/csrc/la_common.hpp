@@ -171,6 +171,37 @@ template <typename T> __device__ inline Raw8<T> zero_raw8() {
     for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.v[i] = make_uint4(0u, 0u, 0u, 0u);
     return r;
 }
+// Streaming (non-temporal) variants for data touched once.
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+template <typename T> __device__ inline Raw8<T> ld_raw8_nt(const T *p) {
+    Raw8<T> r;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 2); ++i) {
+        const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p) + i);
+        r.v[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+    return r;
+}
+template <typename T> __device__ inline void st8_nt(T *p, const float (&x)[8]) {
+    typename Vec4<T>::type a, b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        a[j] = from_f32<T>(x[j]);
+        b[j] = from_f32<T>(x[4 + j]);
+    }
+    if constexpr (sizeof(T) == 2) {
+        u32x4_nt v;
+        v[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 0, 1));
+        v[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 2, 3));
+        v[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(b, b, 0, 1));
+        v[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(b, b, 2, 3));
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_nt *>(p));
+    } else {
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, a), reinterpret_cast<u32x4_nt *>(p));
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, b), reinterpret_cast<u32x4_nt *>(p) + 1);
+    }
+}
+
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 

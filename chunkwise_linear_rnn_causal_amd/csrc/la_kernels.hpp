@@ -68,7 +68,7 @@ template <int VAR, typename TI, typename TO, int DK, int DV>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
 
 // Tokens per thread of the short convolution (the host sizes the grid with it).
-template <typename T> constexpr int conv_tile() { return sizeof(T) == 2 ? 16 : 8; }
+template <typename T> constexpr int conv_tile() { return sizeof(T) == 2 ? 8 : 4; }
 
 template <typename T, int K>
 hipError_t launch_short_conv(const ConvArgs &a, unsigned blocks, hipStream_t st);
