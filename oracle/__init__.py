@@ -21,7 +21,7 @@ import numpy as np
 
 from . import build as _build
 
-VARIANT_ID = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3}
+VARIANT_ID = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3, "vector_decay": 4}
 
 _lib = None
 _lib_path = None
@@ -64,8 +64,8 @@ def forward(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in
             threads: int = 0, lib=None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Run the recurrence over every leading (batch, head) slice.
 
-    q, k: [..., L, dk]; v: [..., L, dv]; log_gate, beta: [..., L];
-    state_in: [..., dk, dv]; z_in: [..., dk]. Returns (o [..., L, dv],
+    q, k: [..., L, dk]; v: [..., L, dv]; log_gate, beta: [..., L]
+    ("vector_decay": log_gate [..., L, dk]); state_in: [..., dk, dv]; z_in: [..., dk]. Returns (o [..., L, dv],
     state_out [..., dk, dv], z_out [..., dk]) in float64.
     """
     lib = lib or load()
@@ -77,7 +77,8 @@ def forward(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in
     assert k.shape == q.shape and v.shape[:-1] == q.shape[:-1]
     lg, be = _c64(log_gate), _c64(beta)
     s_in, zi = _c64(state_in), _c64(z_in)
-    for x, shp in ((lg, lead + (L,)), (be, lead + (L,)), (s_in, lead + (dk, dv)), (zi, lead + (dk,))):
+    lg_shape = lead + ((L, dk) if variant == "vector_decay" else (L,))
+    for x, shp in ((lg, lg_shape), (be, lead + (L,)), (s_in, lead + (dk, dv)), (zi, lead + (dk,))):
         assert x is None or x.shape == shp, (x.shape, shp)
     o = np.zeros(lead + (L, dv), np.float64)
     s_out = np.zeros(lead + (dk, dv), np.float64)
@@ -92,7 +93,8 @@ def forward(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in
 def decode_step(variant: str, q, k, v, log_gate, state, beta=None, threads: int = 0, lib=None):
     """One in-place decode step on a copy of ``state``; returns (o, new_state).
 
-    q, k: [..., dk]; v: [..., dv]; log_gate, beta: [...]; state: [..., dk, dv].
+    q, k: [..., dk]; v: [..., dv]; log_gate, beta: [...] ("vector_decay": log_gate
+    [..., dk]); state: [..., dk, dv].
     beta is required for "gated_delta" (log_gate may then be None: alpha = 1).
     """
     lib = lib or load()

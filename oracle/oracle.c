@@ -20,6 +20,13 @@
  *                sections 13-14: causal recurrence of S and z)
  *   DECAY        S <- gamma S + k v^T, gamma = exp(l); o = S^T q
  *                (wln20, data-dependent decay equation; proig-chaa section 20)
+ *   VECTOR_DECAY S <- Diag(exp(l)) S + k v^T, l in R^{dk}; o = S^T q. One
+ *                log-gate per key channel: tensorplay section 5.1 writes the GLA
+ *                update as G_t (.) S_{t-1} + k_t v_t^T with G_t the gate alpha_t
+ *                (a projection output) broadcast over the value columns, whose
+ *                parallel form in section 5.2 scales Q and K per channel by the
+ *                cumulative product B; wln20's Kimi Delta Attention section uses
+ *                the same diagonal gate Diag(alpha_t) (here without the delta rule)
  *   GATED_DELTA  r = S^T k (retrieve); S <- alpha (S - beta k r^T) + beta k v^T;
  *                o = S^T q, alpha = exp(l) (alpha = 1 when no log-gate is given)
  *                This is the transpose of S'_t = S'_{t-1} alpha_t (I - beta_t k_t
@@ -32,6 +39,7 @@
  *
  * Layouts (all row-major, contiguous):
  *   q, k  [BH, L, dk]     v, o  [BH, L, dv]     log_gate, beta  [BH, L]
+ *   (VECTOR_DECAY: log_gate [BH, L, dk])
  *   state_in, state_out  [BH, dk, dv]          z_in, z_out  [BH, dk]
  * NULL state_in / z_in mean zero; NULL state_out / z_out mean "not returned".
  */
@@ -46,6 +54,7 @@
 #define OR_NORMALIZED 1
 #define OR_DECAY 2
 #define OR_GATED_DELTA 3
+#define OR_VECTOR_DECAY 4
 
 #define OR_OK 0
 #define OR_BAD_ARG 1
@@ -86,6 +95,12 @@ static int run_head(int variant, const double *q, const double *k, const double 
             for (long i = 0; i < dk; ++i)
                 for (long j = 0; j < dv; ++j)
                     S[i * dv + j] = g * S[i * dv + j] + kt[i] * vt[j];
+        } else if (variant == OR_VECTOR_DECAY) {
+            for (long i = 0; i < dk; ++i) {
+                double g = exp(lg[t * dk + i]);
+                for (long j = 0; j < dv; ++j)
+                    S[i * dv + j] = g * S[i * dv + j] + kt[i] * vt[j];
+            }
         } else { /* OR_GATED_DELTA */
             double a = lg ? exp(lg[t]) : 1.0;
             double b = beta[t];
@@ -125,10 +140,11 @@ int oracle_forward(int variant, const double *q, const double *k, const double *
                    const double *z_in, double *o, double *state_out, double *z_out,
                    long BH, long L, long dk, long dv, int nthreads)
 {
-    if (variant < OR_PLAIN || variant > OR_GATED_DELTA) return OR_BAD_ARG;
+    if (variant < OR_PLAIN || variant > OR_VECTOR_DECAY) return OR_BAD_ARG;
     if (BH < 0 || L < 0 || dk <= 0 || dv <= 0) return OR_BAD_ARG;
     if ((BH > 0 && L > 0) && (!q || !k || !v || !o)) return OR_BAD_ARG;
-    if (variant == OR_DECAY && L > 0 && !log_gate) return OR_BAD_ARG;
+    if ((variant == OR_DECAY || variant == OR_VECTOR_DECAY) && L > 0 && !log_gate) return OR_BAD_ARG;
+    const long gstride = variant == OR_VECTOR_DECAY ? L * dk : L;
     if (variant == OR_GATED_DELTA && L > 0 && !beta) return OR_BAD_ARG;
 
     int status = OR_OK;
@@ -137,7 +153,7 @@ int oracle_forward(int variant, const double *q, const double *k, const double *
 #endif
     for (long h = 0; h < BH; ++h) {
         int st = run_head(variant, q + h * L * dk, k + h * L * dk, v + h * L * dv,
-                          log_gate ? log_gate + h * L : NULL, beta ? beta + h * L : NULL,
+                          log_gate ? log_gate + h * gstride : NULL, beta ? beta + h * L : NULL,
                           state_in ? state_in + h * dk * dv : NULL, z_in ? z_in + h * dk : NULL,
                           o + h * L * dv, state_out ? state_out + h * dk * dv : NULL,
                           z_out ? z_out + h * dk : NULL, L, dk, dv);
@@ -151,18 +167,22 @@ int oracle_forward(int variant, const double *q, const double *k, const double *
  * constant-size state carried from token to token), with the same per-token
  * update as the forward pass:
  *   DECAY (PLAIN: log_gate NULL)  S <- exp(l) S + k v^T            (wln20 decay equation)
+ *   VECTOR_DECAY                  S <- Diag(exp(l)) S + k v^T, l [dk] per head
  *   GATED_DELTA                   r = S^T k; S <- a (S - b k r^T) + b k v^T,
  *                                 a = exp(l) (1 when log_gate is NULL), b = beta
  *                                 (wln20 Gated DeltaNet section)
  * then o = S^T q. Layouts: q, k [NH, dk]; v, o [NH, dv]; log_gate, beta [NH];
- * state [NH, dk, dv].
+ * state [NH, dk, dv] (VECTOR_DECAY: log_gate [NH, dk]).
  */
 int oracle_decode_step(int variant, const double *q, const double *k, const double *v,
                        const double *log_gate, const double *beta, double *state, double *o,
                        long NH, long dk, long dv, int nthreads)
 {
-    if (variant != OR_PLAIN && variant != OR_DECAY && variant != OR_GATED_DELTA) return OR_BAD_ARG;
-    if (variant == OR_DECAY && !log_gate) return OR_BAD_ARG;
+    if (variant != OR_PLAIN && variant != OR_DECAY && variant != OR_GATED_DELTA &&
+        variant != OR_VECTOR_DECAY)
+        return OR_BAD_ARG;
+    if ((variant == OR_DECAY || variant == OR_VECTOR_DECAY) && !log_gate) return OR_BAD_ARG;
+    const long gstride = variant == OR_VECTOR_DECAY ? dk : 1;
     if (variant == OR_GATED_DELTA && !beta) return OR_BAD_ARG;
     if (NH < 0 || dk <= 0 || dv <= 0 || !state) return OR_BAD_ARG;
     int status = OR_OK;
@@ -171,7 +191,7 @@ int oracle_decode_step(int variant, const double *q, const double *k, const doub
 #endif
     for (long h = 0; h < NH; ++h) {
         int st = run_head(variant, q + h * dk, k + h * dk, v + h * dv,
-                          log_gate ? log_gate + h : NULL, beta ? beta + h : NULL,
+                          log_gate ? log_gate + h * gstride : NULL, beta ? beta + h : NULL,
                           state + h * dk * dv, NULL, o + h * dv, state + h * dk * dv, NULL, 1, dk, dv);
         if (st > status) status = st;
     }

@@ -523,6 +523,102 @@ def pin_resume_all_variants(lib):
 
 
 # ---------------------------------------------------------------------------
+# VECTOR_DECAY (one log-gate per key channel)
+# ---------------------------------------------------------------------------
+def pin_vector_decay_parallel_form(lib):
+    """O = ((Q (.) B)(K / B)^T (.) M) V with B the per-channel cumulative product of
+    the gates (tensorplay section 5.2, GLA parallel form), and the final state
+    S_L = sum_s Diag(B_L / B_s) k_s v_s^T. Moderate gates keep K / B finite."""
+    r = _rng(40)
+    L, dk, dv = 37, 6, 5
+    q, k = r.standard_normal((2, L, dk)), r.standard_normal((2, L, dk))
+    v = r.standard_normal((2, L, dv))
+    lg = -0.3 * r.random((2, L, dk))
+    o, s, _ = oracle.forward("vector_decay", q, k, v, log_gate=lg, lib=lib)
+    Bm = np.exp(np.cumsum(lg, axis=1))
+    ref = ((q * Bm) @ (k / Bm).transpose(0, 2, 1) * _mask(L)) @ v
+    assert _rel(o, ref) <= 1e-10, _rel(o, ref)
+    sref = np.einsum("bsc,bsj->bcj", k * (Bm[:, -1:, :] / Bm), v)
+    assert _rel(s, sref) <= 1e-12, _rel(s, sref)
+
+
+def pin_vector_decay_uniform_is_scalar(lib):
+    """The same gate on every key channel is the scalar decay, bit for bit; zero
+    gates are the plain recurrence."""
+    r = _rng(41)
+    L, dk, dv = 23, 5, 4
+    q, k, v = r.standard_normal((3, L, dk)), r.standard_normal((3, L, dk)), r.standard_normal((3, L, dv))
+    lg1 = -r.random((3, L)) * 0.5
+    s0 = r.standard_normal((3, dk, dv))
+    ov, sv, _ = oracle.forward("vector_decay", q, k, v, log_gate=np.repeat(lg1[..., None], dk, -1),
+                               state_in=s0, lib=lib)
+    od, sd, _ = oracle.forward("decay", q, k, v, log_gate=lg1, state_in=s0, lib=lib)
+    assert np.array_equal(ov, od) and np.array_equal(sv, sd)
+    o0, _, _ = oracle.forward("vector_decay", q, k, v, log_gate=np.zeros((3, L, dk)), lib=lib)
+    op, _, _ = oracle.forward("plain", q, k, v, lib=lib)
+    assert np.array_equal(o0, op)
+
+
+def pin_vector_decay_fraction(lib):
+    """Exact rational brute force of o_t = sum_{s<=t} sum_c q_t[c] gamma_c^{t-s}
+    k_s[c] v_s with constant per-channel gates gamma_c in {1, 1/2, 1/4}
+    (the oracle forms gamma as exp(log gamma), so agreement is to rounding)."""
+    r = _rng(42)
+    L, dk, dv = 7, 3, 2
+    q = r.integers(-3, 4, (1, L, dk)).astype(np.float64)
+    k = r.integers(-3, 4, (1, L, dk)).astype(np.float64)
+    v = r.integers(-3, 4, (1, L, dv)).astype(np.float64)
+    gam = [Fraction(1), Fraction(1, 2), Fraction(1, 4)]
+    lg = np.tile(np.array([math.log(float(g)) for g in gam]), (1, L, 1))
+    o, _, _ = oracle.forward("vector_decay", q, k, v, log_gate=lg, lib=lib)
+    for t in range(L):
+        for j in range(dv):
+            acc = Fraction(0)
+            for s_ in range(t + 1):
+                w = sum(Fraction(int(q[0, t, c])) * gam[c] ** (t - s_) * Fraction(int(k[0, s_, c]))
+                        for c in range(dk))
+                acc += w * Fraction(int(v[0, s_, j]))
+            assert abs(o[0, t, j] - float(acc)) <= 1e-13 * max(1.0, abs(float(acc))), (t, j)
+
+
+def pin_vector_decay_channel_isolation(lib):
+    """A gate of exp(-200) on one key channel erases that channel's history at every
+    step while the others keep theirs: o_t = sum_{s<=t} sum_{c != c0} q_t[c] k_s[c] v_s
+    + q_t[c0] k_t[c0] v_t. This fails if the gate is applied along the value axis."""
+    r = _rng(43)
+    L, dk, dv, c0 = 11, 4, 6, 2
+    q, k, v = r.standard_normal((1, L, dk)), r.standard_normal((1, L, dk)), r.standard_normal((1, L, dv))
+    lg = np.zeros((1, L, dk))
+    lg[:, :, c0] = -200.0
+    o, s, _ = oracle.forward("vector_decay", q, k, v, log_gate=lg, lib=lib)
+    keep = np.ones(dk)
+    keep[c0] = 0.0
+    ref = (((q * keep) @ k[0].T) * _mask(L)) @ v[0] + (q[0, :, c0] * k[0, :, c0])[:, None] * v[0]
+    assert _rel(o, ref) <= 1e-12
+    assert np.allclose(s[0, c0], k[0, -1, c0] * v[0, -1], rtol=1e-14, atol=0)
+
+
+def pin_vector_decay_resume_and_decode(lib):
+    """Splitting the sequence and carrying the state equals one pass, and one decode
+    step on the carried state equals the next token of a longer pass."""
+    r = _rng(44)
+    L1, L2, dk, dv = 9, 8, 4, 3
+    L = L1 + L2
+    q, k, v = r.standard_normal((2, L, dk)), r.standard_normal((2, L, dk)), r.standard_normal((2, L, dv))
+    lg = -r.random((2, L, dk)) * 0.4
+    o, s, _ = oracle.forward("vector_decay", q, k, v, log_gate=lg, lib=lib)
+    oa, sa, _ = oracle.forward("vector_decay", q[:, :L1], k[:, :L1], v[:, :L1], log_gate=lg[:, :L1], lib=lib)
+    ob, sb, _ = oracle.forward("vector_decay", q[:, L1:], k[:, L1:], v[:, L1:], log_gate=lg[:, L1:],
+                               state_in=sa, lib=lib)
+    assert _rel(np.concatenate([oa, ob], 1), o) <= 1e-12 and _rel(sb, s) <= 1e-12
+    t = L - 1
+    o_prev, s_prev, _ = oracle.forward("vector_decay", q[:, :t], k[:, :t], v[:, :t], log_gate=lg[:, :t],
+                                       lib=lib)
+    od, sd = oracle.decode_step("vector_decay", q[:, t], k[:, t], v[:, t], lg[:, t], s_prev, lib=lib)
+    assert _rel(od, o[:, t]) <= 1e-12 and _rel(sd, s) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
 # Short causal depthwise convolution (wln20, DeltaNet section)
 # ---------------------------------------------------------------------------
 def pin_conv_library_convolve(lib):
@@ -619,4 +715,6 @@ ALL_PINS = [
     pin_decode_gdn_step, pin_prefill_then_decode_gdn,
     pin_conv_library_convolve, pin_conv_fraction_bruteforce, pin_conv_delta_taps_shift,
     pin_conv_chunked_carry,
+    pin_vector_decay_parallel_form, pin_vector_decay_uniform_is_scalar, pin_vector_decay_fraction,
+    pin_vector_decay_channel_isolation, pin_vector_decay_resume_and_decode,
 ]

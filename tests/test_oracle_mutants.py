@@ -13,8 +13,7 @@ from oracle import build as obuild
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 MUTANTS = {
-    "decay_dropped": ("S[i * dv + j] = g * S[i * dv + j] + kt[i] * vt[j];",
-                      "S[i * dv + j] = S[i * dv + j] + kt[i] * vt[j];"),
+    "decay_dropped": ("double g = exp(lg[t]);", "double g = 1.0;"),
     "decay_gate_off_by_one": ("double g = exp(lg[t]);",
                               "double g = exp(lg[t > 0 ? t - 1 : 0]);"),
     "gdn_sign": ("a * (S[i * dv + j] - b * kt[i] * r[j])", "a * (S[i * dv + j] + b * kt[i] * r[j])"),
@@ -30,6 +29,10 @@ MUTANTS = {
     "plain_transposed_write": ("S[i * dv + j] += kt[i] * vt[j];", "S[i * dv + j] += kt[j % dk] * vt[i % dv];"),
     "readout_uses_key": ("acc += S[i * dv + j] * qt[i];\n            ot[j] = acc;",
                          "acc += S[i * dv + j] * kt[i];\n            ot[j] = acc;"),
+    "vector_gate_channel_reversed": ("double g = exp(lg[t * dk + i]);",
+                                     "double g = exp(lg[t * dk + (dk - 1 - i)]);"),
+    "vector_gate_one_token_late": ("double g = exp(lg[t * dk + i]);",
+                                   "double g = exp(lg[(t > 0 ? t - 1 : 0) * dk + i]);"),
     "conv_taps_reversed": ("acc += w[(h * d + c) * K + tau] * hist[(W + t - tau) * d + c];",
                            "acc += w[(h * d + c) * K + (K - 1 - tau)] * hist[(W + t - tau) * d + c];"),
     "conv_head_weights_shared": ("acc += w[(h * d + c) * K + tau]", "acc += w[c * K + tau]"),
