@@ -82,6 +82,8 @@ def chunk_work(c: dict) -> tuple[float, float]:
     nbytes = BH * L * ((2 * dk + dv) * esz + dv * 4)           # q, k, v in; o out (fp32)
     if c["variant"] in ("decay", "gated_delta"):
         nbytes += BH * L * 4                                     # log-gates
+    if c["variant"] == "vector_decay":
+        nbytes += BH * L * dk * 4                                # one log-gate per key channel
     if c["variant"] == "gated_delta":
         nbytes += BH * L * 4                                     # beta
     nbytes += BH * dk * dv * 4                                   # final state

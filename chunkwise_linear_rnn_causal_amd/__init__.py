@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "liblinattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "linattn.h")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
-VARIANTS = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3}
+VARIANTS = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3, "vector_decay": 4}
 EXPORTS = ("la_chunk_fwd_workspace_size", "la_chunk_fwd", "la_decode_step", "la_short_conv",
            "la_status_str", "la_abi_version")
 
@@ -111,7 +111,8 @@ def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None,
     """Chunkwise causal linear-attention forward.
 
     q, k: [B, H, L, d_k]; v: [B, H, L, d_v] (bf16 or fp32, contiguous, on the GPU).
-    log_gate, beta: [B, H, L] fp32; state_in: [B, H, d_k, d_v] fp32;
+    log_gate, beta: [B, H, L] fp32 ("vector_decay": log_gate [B, H, L, d_k]);
+    state_in: [B, H, d_k, d_v] fp32;
     z_in: [B, H, d_k] fp32. Returns (o, state_out or None, z_out or None).
     o is fp32 unless out_dtype=torch.bfloat16 (bf16 inputs only) or a bf16 ``o``
     is passed. Output buffers may be passed in (o, state_out, z_out); state_out

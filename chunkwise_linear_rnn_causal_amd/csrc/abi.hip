@@ -56,13 +56,14 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Shape checks shared by the workspace query and the forward call.
 la_status check_chunk_shape(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v,
                             int C) {
-    if (var < LA_PLAIN || var > LA_GATED_DELTA) return LA_ERR_INVALID_ARG;
+    if (var < LA_PLAIN || var > LA_VECTOR_DECAY) return LA_ERR_INVALID_ARG;
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || L < 0) return LA_ERR_INVALID_ARG;
     if (d_k != 32 && d_k != 64 && d_k != 128) return LA_ERR_UNSUPPORTED;
     if (d_v < 32 || d_v > 128 || d_v % 32 != 0) return LA_ERR_UNSUPPORTED;
     if (C != 64 && C != 128) return LA_ERR_UNSUPPORTED;
-    if (var == LA_GATED_DELTA && C != 64) return LA_ERR_UNSUPPORTED;
+    if ((var == LA_GATED_DELTA || var == LA_VECTOR_DECAY) && C != 64) return LA_ERR_UNSUPPORTED;
+    if (var == LA_VECTOR_DECAY && dt == LA_F32 && d_k == 128) return LA_ERR_UNSUPPORTED;
     if (dt == LA_F32 && d_k == 128 && C == 128) return LA_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
     if (BH * (d_v / 16) > INT32_MAX || BH * ((L + C - 1) / C) > INT32_MAX) return LA_ERR_UNSUPPORTED;
@@ -132,6 +133,18 @@ hipError_t dispatch_chunk(la_variant var, int C, Geometry geo, const ChunkArgs &
 }
 
 template <typename TI, typename TO>
+hipError_t dispatch_vdecay(int d_k, const ChunkArgs &a, hipStream_t st) {
+    switch (d_k) {
+        case 32: return launch_vdecay<TI, TO, 32>(a, st);
+        case 64: return launch_vdecay<TI, TO, 64>(a, st);
+        case 128:
+            if constexpr (sizeof(TI) == 2) return launch_vdecay<TI, TO, 128>(a, st);
+            break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename TI, typename TO>
 hipError_t dispatch_chunk_dk(la_variant var, int d_k, int C, Geometry geo, const ChunkArgs &a,
                              hipStream_t st) {
     switch (d_k) {
@@ -172,7 +185,6 @@ hipError_t dispatch_decode(int d_k, int d_v, const DecodeArgs &a, hipStream_t st
     return hipErrorInvalidValue;
 }
 
-// Supported (input, output) dtype pairs: bf16 -> fp32, bf16 -> bf16, fp32 -> fp32.
 template <typename T>
 hipError_t dispatch_short_conv(int K, const ConvArgs &a, unsigned blocks, hipStream_t st) {
     switch (K) {
@@ -185,6 +197,7 @@ hipError_t dispatch_short_conv(int K, const ConvArgs &a, unsigned blocks, hipStr
     return hipErrorInvalidValue;
 }
 
+// Supported (input, output) dtype pairs: bf16 -> fp32, bf16 -> bf16, fp32 -> fp32.
 bool dtype_pair_ok(la_dtype dt, la_dtype o_dt) {
     return (dt == LA_BF16 && (o_dt == LA_F32 || o_dt == LA_BF16)) || (dt == LA_F32 && o_dt == LA_F32);
 }
@@ -229,7 +242,7 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
     // required / forbidden pointers
     if (has_tokens && (!q || !k || !o)) return LA_ERR_INVALID_ARG;
     if (has_tokens && !v) return LA_ERR_INVALID_ARG;
-    if (var == LA_DECAY && has_tokens && !log_gate) return LA_ERR_INVALID_ARG;
+    if ((var == LA_DECAY || var == LA_VECTOR_DECAY) && has_tokens && !log_gate) return LA_ERR_INVALID_ARG;
     if ((var == LA_PLAIN || var == LA_NORMALIZED) && log_gate) return LA_ERR_INVALID_ARG;
     if (var == LA_GATED_DELTA && has_tokens && !beta) return LA_ERR_INVALID_ARG;
     if (var != LA_GATED_DELTA && beta) return LA_ERR_INVALID_ARG;
@@ -241,8 +254,9 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
     // aliasing: outputs must not overlap inputs (state_out == state_in is allowed)
     const size_t qk_b = (size_t)BH * L * d_k * es, v_b = (size_t)BH * L * d_v * es;
     const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4, z_b = (size_t)BH * d_k * 4;
+    const size_t lg_b = var == LA_VECTOR_DECAY ? g_b * d_k : g_b;
     const Span o_sp{o, (size_t)BH * L * d_v * oes}, so_sp{state_out, s_b}, zo_sp{z_out, z_b};
-    const Span ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {log_gate, g_b}, {beta, g_b}, {z_in, z_b}};
+    const Span ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {log_gate, lg_b}, {beta, g_b}, {z_in, z_b}};
     for (const Span &in : ins) {
         if (overlap(o_sp, in) || overlap(so_sp, in) || overlap(zo_sp, in)) return LA_ERR_INVALID_ARG;
     }
@@ -288,6 +302,16 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
         if (e != hipSuccess) return LA_ERR_HIP;
     }
     hipError_t e;
+    if (var == LA_VECTOR_DECAY) {
+        a.nsplit = d_v / 32;
+        if (dt == LA_F32)
+            e = dispatch_vdecay<float, float>(d_k, a, st);
+        else if (o_dt == LA_F32)
+            e = dispatch_vdecay<bf16, float>(d_k, a, st);
+        else
+            e = dispatch_vdecay<bf16, bf16>(d_k, a, st);
+        return from_hip(e);
+    }
     if (dt == LA_F32)
         e = dispatch_chunk_dk<float, float>(var, d_k, C, geo, a, st);
     else if (o_dt == LA_F32)
@@ -300,7 +324,7 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
 la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void *q, const void *k,
                          const void *v, const float *log_gate, const float *beta, float *state,
                          void *o, int N, int H, int d_k, int d_v, void *stream) {
-    if (var < LA_PLAIN || var > LA_GATED_DELTA) return LA_ERR_INVALID_ARG;
+    if (var < LA_PLAIN || var > LA_VECTOR_DECAY) return LA_ERR_INVALID_ARG;
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (o_dt != LA_F32 && o_dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (!dtype_pair_ok(dt, o_dt)) return LA_ERR_UNSUPPORTED;
@@ -310,7 +334,7 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
     if ((d_k != 32 && d_k != 64 && d_k != 128) || (d_v != 32 && d_v != 64 && d_v != 128))
         return LA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !state || !o) return LA_ERR_INVALID_ARG;
-    if (var == LA_DECAY && !log_gate) return LA_ERR_INVALID_ARG;
+    if ((var == LA_DECAY || var == LA_VECTOR_DECAY) && !log_gate) return LA_ERR_INVALID_ARG;
     if (var == LA_PLAIN && log_gate) return LA_ERR_INVALID_ARG;
     if ((var == LA_GATED_DELTA) != (beta != nullptr)) return LA_ERR_INVALID_ARG;
     const void *ptrs[] = {q, k, v, o, log_gate, beta, state};
@@ -320,7 +344,9 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
     const size_t es = elem_size(dt);
     const Span o_sp{o, (size_t)NH * d_v * elem_size(o_dt)}, s_sp{state, (size_t)NH * d_k * d_v * 4};
     const Span ins[] = {{q, (size_t)NH * d_k * es}, {k, (size_t)NH * d_k * es},
-                        {v, (size_t)NH * d_v * es}, {log_gate, (size_t)NH * 4}, {beta, (size_t)NH * 4}};
+                        {v, (size_t)NH * d_v * es},
+                        {log_gate, (size_t)NH * 4 * (var == LA_VECTOR_DECAY ? d_k : 1)},
+                        {beta, (size_t)NH * 4}};
     for (const Span &in : ins)
         if (overlap(o_sp, in) || overlap(s_sp, in)) return LA_ERR_INVALID_ARG;
     if (overlap(o_sp, s_sp)) return LA_ERR_INVALID_ARG;
@@ -330,7 +356,11 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     DecodeArgs a{q, k, v, log_gate, beta, state, o, (int)NH};
     hipError_t e;
-    if (var == LA_GATED_DELTA) {
+    if (var == LA_VECTOR_DECAY) {
+        if (dt == LA_F32) e = dispatch_decode<V_VDECAY, float, float>(d_k, d_v, a, st);
+        else if (o_dt == LA_F32) e = dispatch_decode<V_VDECAY, bf16, float>(d_k, d_v, a, st);
+        else e = dispatch_decode<V_VDECAY, bf16, bf16>(d_k, d_v, a, st);
+    } else if (var == LA_GATED_DELTA) {
         if (dt == LA_F32) e = dispatch_decode<V_GDN, float, float>(d_k, d_v, a, st);
         else if (o_dt == LA_F32) e = dispatch_decode<V_GDN, bf16, float>(d_k, d_v, a, st);
         else e = dispatch_decode<V_GDN, bf16, bf16>(d_k, d_v, a, st);

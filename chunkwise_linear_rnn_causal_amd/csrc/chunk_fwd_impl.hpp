@@ -66,23 +66,6 @@ template <typename TM, int W, int PAD> struct RowTile {
     __device__ static constexpr int at(int row, int col) { return row * P + col; }
 };
 
-// Operand fragment X[k][col0 + n] for the K-slots {r0 .. r0+3, r0+16 .. r0+19}
-// of this lane's group, from a row-major fp16 tile of pitch P, with two
-// transpose loads. In a 16-lane group the transpose load hands lane i element e
-// of the 8-byte row piece addressed by lane 4e + i/4, column i % 4; so lane j
-// addresses row r + (j >> 2), columns col0 + 4 (j & 3).
-template <int P>
-__device__ inline f16x8 tr_frag(const f16 *X, int r0, int col0, int lane) {
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    const int j = lane & 15;
-    const f16 *p0 = X + (r0 + (j >> 2)) * P + col0 + 4 * (j & 3);
-    const f16 *p1 = p0 + 16 * P;
-    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p0));
-    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p1));
-    const f16x4 ha = __builtin_bit_cast(f16x4, a), hb = __builtin_bit_cast(f16x4, b);
-    return f16x8{ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
-}
-
 // ---------------------------------------------------------------------------
 // Contiguous ranges of state tiles per wave, filled greedily so that waves with
 // fewer score tiles take more state tiles.

@@ -5,6 +5,8 @@
 // state is all that is carried between tokens):
 //   decay (plain: gamma = 1)  S <- gamma S + k v^T   (wln20 "LLM注意力优化：线性注意力",
 //                                                     data-dependent decay)
+//   per-key-channel decay     S <- Diag(alpha) S + k v^T (tensorplay section 5.1,
+//                                                     the GLA gate; one gate per row)
 //   gated delta rule          r = S^T k;  S <- alpha S + k (beta (v - alpha r))^T
 //                             (wln20, Gated DeltaNet section, d_k x d_v orientation:
 //                             alpha (S - beta k r^T) + beta k v^T regrouped)
@@ -68,7 +70,12 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     // new state column group: ns = al * s + kr * u (u per column group)
     float al = 1.f;
     f32x4 u = vv;
-    if constexpr (VAR == V_DECAY) {
+    float alr[VAR == V_VDECAY ? RPT : 1];  // per-row (key channel) gates
+    if constexpr (VAR == V_VDECAY) {
+        const float *lp = a.lg + h * DK + rg * RPT;
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) alr[m] = __expf(lp[m]);
+    } else if constexpr (VAR == V_DECAY) {
         al = __expf(a.lg[h]);
     } else if constexpr (VAR == V_GDN) {
         __shared__ f32x4 rred[4][CG];
@@ -84,7 +91,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
-        const f32x4 ns = al * s[m] + kr[m] * u;
+        const f32x4 ns = (VAR == V_VDECAY ? alr[m] : al) * s[m] + kr[m] * u;
         __builtin_nontemporal_store(ns, reinterpret_cast<f32x4 *>(S + (size_t)m * DV));
         acc += qr[m] * ns;
     }

@@ -2,6 +2,7 @@
 #include "chunk_fwd_impl.hpp"
 #include "decode_impl.hpp"
 #include "gdn_prep_impl.hpp"
+#include "vdecay_fwd_impl.hpp"
 
 namespace la {
 
@@ -73,5 +74,22 @@ template hipError_t launch_decode<V_GDN, bf16, float, 128, 128>(const DecodeArgs
 template hipError_t launch_gdn_prep<bf16, 32, 64>(const PrepArgs &, hipStream_t);
 template hipError_t launch_gdn_prep<bf16, 64, 64>(const PrepArgs &, hipStream_t);
 template hipError_t launch_gdn_prep<bf16, 128, 64>(const PrepArgs &, hipStream_t);
+
+
+// per-key-channel decay: (input, output, d_k)
+template hipError_t launch_vdecay<bf16, float, 32>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_vdecay<bf16, float, 64>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_vdecay<bf16, float, 128>(const ChunkArgs &, hipStream_t);
+
+// per-key-channel decay decode step
+template hipError_t launch_decode<V_VDECAY, bf16, float, 32, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, bf16, float, 32, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, bf16, float, 32, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, bf16, float, 64, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, bf16, float, 64, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, bf16, float, 64, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, bf16, float, 128, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, bf16, float, 128, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, bf16, float, 128, 128>(const DecodeArgs &, hipStream_t);
 
 }  // namespace la

@@ -2,6 +2,7 @@
 #include "chunk_fwd_impl.hpp"
 #include "decode_impl.hpp"
 #include "gdn_prep_impl.hpp"
+#include "vdecay_fwd_impl.hpp"
 #include "short_conv_impl.hpp"
 
 namespace la {
@@ -66,5 +67,21 @@ template hipError_t launch_short_conv<float, 1>(const ConvArgs &, unsigned, hipS
 template hipError_t launch_short_conv<float, 2>(const ConvArgs &, unsigned, hipStream_t);
 template hipError_t launch_short_conv<float, 3>(const ConvArgs &, unsigned, hipStream_t);
 template hipError_t launch_short_conv<float, 4>(const ConvArgs &, unsigned, hipStream_t);
+
+
+// per-key-channel decay: (input, output, d_k)
+template hipError_t launch_vdecay<float, float, 32>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_vdecay<float, float, 64>(const ChunkArgs &, hipStream_t);
+
+// per-key-channel decay decode step
+template hipError_t launch_decode<V_VDECAY, float, float, 32, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, float, float, 32, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, float, float, 32, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, float, float, 64, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, float, float, 64, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, float, float, 64, 128>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, float, float, 128, 32>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, float, float, 128, 64>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_decode<V_VDECAY, float, float, 128, 128>(const DecodeArgs &, hipStream_t);
 
 }  // namespace la

@@ -22,7 +22,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-enum Variant { V_PLAIN = 0, V_NORM = 1, V_DECAY = 2, V_GDN = 3 };
+enum Variant { V_PLAIN = 0, V_NORM = 1, V_DECAY = 2, V_GDN = 3, V_VDECAY = 4 };
 
 // MFMA traits per storage/operand type.
 template <typename T> struct Mfma;
@@ -238,6 +238,23 @@ template <int C, typename T> __device__ inline int tidx(int row, int s) {
     constexpr int NU = C / EU;               // units per row
     const int f = ((row & 7) ^ (2 * ((row >> 3) & 3))) & (NU - 1);
     return row * C + (((s / EU) ^ f) * EU) + (s % EU);
+}
+
+// Operand fragment X[k][col0 + n] for the K-slots {r0 .. r0+3, r0+16 .. r0+19}
+// of this lane's group, from a row-major fp16 tile of pitch P, with two
+// transpose loads. In a 16-lane group the transpose load hands lane i element e
+// of the 8-byte row piece addressed by lane 4e + i/4, column i % 4; so lane j
+// addresses row r + (j >> 2), columns col0 + 4 (j & 3).
+template <int P>
+__device__ inline f16x8 tr_frag(const f16 *X, int r0, int col0, int lane) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const int j = lane & 15;
+    const f16 *p0 = X + (r0 + (j >> 2)) * P + col0 + 4 * (j & 3);
+    const f16 *p1 = p0 + 16 * P;
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p0));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(p1));
+    const f16x4 ha = __builtin_bit_cast(f16x4, a), hb = __builtin_bit_cast(f16x4, b);
+    return f16x8{ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
 }
 
 // DPP move of a float (row_mask / bank_mask select written rows / banks; lanes

@@ -11,7 +11,7 @@ namespace la {
 // One chunkwise forward pass. Pointers are device pointers; sizes are validated.
 struct ChunkArgs {
     const void *q, *k, *v;      // [BH, L, DK], [BH, L, DK], [BH, L, dv]
-    const float *lg;            // [BH, L] log-gates or nullptr
+    const float *lg;            // [BH, L] log-gates ([BH, L, DK] per key channel) or nullptr
     const float *s_in;          // [BH, DK, dv] or nullptr
     const float *z_in;          // [BH, DK] or nullptr (normalized only)
     void *o;                    // [BH, L, dv]
@@ -32,7 +32,7 @@ struct PrepArgs {
 
 struct DecodeArgs {
     const void *q, *k, *v;      // [NH, DK], [NH, DK], [NH, DV]
-    const float *lg;            // [NH] or nullptr
+    const float *lg;            // [NH] ([NH, DK] per key channel) or nullptr
     const float *beta;          // [NH] (gated delta rule) or nullptr
     float *S;                   // [NH, DK, DV], updated in place
     void *o;                    // [NH, DV]
@@ -63,6 +63,10 @@ hipError_t launch_chunk(const ChunkArgs &a, hipStream_t st);
 
 template <typename TI, int DK, int C>
 hipError_t launch_gdn_prep(const PrepArgs &a, hipStream_t st);
+
+// Chunk forward with one decay gate per key channel (C = 64, 32-column slices).
+template <typename TI, typename TO, int DK>
+hipError_t launch_vdecay(const ChunkArgs &a, hipStream_t st);
 
 template <int VAR, typename TI, typename TO, int DK, int DV>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);

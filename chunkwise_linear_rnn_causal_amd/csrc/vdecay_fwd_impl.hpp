@@ -1,0 +1,406 @@
+// vdecay_fwd_impl.hpp -- chunkwise forward with one decay gate per key channel
+// (gfx950).
+//
+// Method. The update S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t
+// (tensorplay "Talk Linear Attention", section 5.1: the GLA gate matrix G_t (.)
+// S_{t-1} with alpha_t broadcast over the value columns; wln20 "LLM注意力优化：
+// 线性注意力", Kimi Delta Attention section, the diagonal gate Diag(alpha_t)).
+// With the chunk-local cumulative log-gate G_r[c] = sum_{u<=r} l_u[c], the
+// chunk form is the per-channel version of the scalar one (tensorplay section
+// 5.2, (Q (.) B)(K / B)^T with B the cumulative product):
+//   O_c    = (Q (.) e^G) S_prev + A V,   A_rs = sum_c q_r[c] k_s[c] e^{G_r[c] - G_s[c]}  (s <= r)
+//   S_next = Diag(e^{G_end}) S_prev + (K (.) e^{G_end - G})^T V
+// The decay no longer factors out of A, and e^{-G} alone overflows, so A is
+// formed per 16-token block pair around each block's middle token m_i:
+//   q_r e^{G_r - G_{m_i}}  and  k_s e^{G_{m_j} - G_s}   (row r in block i, key s in block j)
+// are each within 8 tokens of their reference, and the pair is joined by the
+// per-channel factor D_ij = e^{G_{m_i} - G_{m_j}} <= 1 folded into the key
+// operand. Every factor is bounded by e^{8 max|l|}; with l >= -10 (the
+// documented domain) all of them stay below e^80 and fit the fp32 range of the
+// score operands (bf16 for bf16 inputs, fp32 for fp32 inputs). One exp per
+// element per chunk plus 15 per channel, instead of one per (row, key, channel).
+// The diagonal score q_t . k_t carries no decay; it is taken in fp32 from the
+// inputs, so bf16's rounding only touches terms damped by at least one gate.
+//
+// Mapping. One workgroup (8 waves) owns one (batch*head, 32-column value
+// slice) and walks the chunks in order with its d_k x 32 slice of S in fp32
+// MFMA accumulators. Per chunk: the gates are scanned per channel in LDS, the
+// operand tiles above are derived from the chunk's q and k registers, then each
+// wave computes the output tile of one query row block and one 16-column half
+// (inter term, score tiles, intra term V^T A^T with the score accumulators fed
+// straight in as the B operand, as in the scalar kernel) and its share of the
+// state tiles. The next chunk's loads are issued before the math.
+#pragma once
+
+#include "la_common.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+
+// Score operand type: bf16 for bf16 inputs (the exponent range of fp32), fp32
+// for fp32 inputs.
+template <typename TI> struct ScoreOp;
+template <> struct ScoreOp<bf16> { using type = bf16; };
+template <> struct ScoreOp<float> { using type = float; };
+
+template <typename TI, int DK, int DVT> struct VdCfg {
+    using TM = typename OpOf<TI>::type;
+    using TS = typename ScoreOp<TI>::type;
+    static constexpr int C = 64, NT = 512, NRB = 4;
+    static constexpr bool H = sizeof(TM) == 2;
+    static constexpr int PG = DK;                      // gate tile pitch (fp32)
+    static constexpr int PQ = H ? DK + 8 : DK + 4;     // Qh, Qe, Kx, St pitch
+    static constexpr int PK = H ? DK + 16 : DK + 4;    // Kt pitch (transpose reads)
+    static constexpr int PV = H ? DVT + 16 : DVT + 4;  // V pitch (transpose reads)
+    static constexpr int NP = NT / DK;                 // scan parts per channel
+    static constexpr int R = C / NP;                   // rows per scan part
+    static constexpr int KXR = 160;                    // Kx rows: 16 + 32 + 48 + 64
+    // factor rows: e^{G_m_i} (4), e^{G_end - G_m_j} (4), D_ij (6), e^{G_end} (1)
+    static constexpr int NF = 15, FQ = 0, FKT = 4, FD = 8, FEND = 14;
+    static constexpr size_t oG = 0;
+    static constexpr size_t oTot = oG + (size_t)C * PG * 4;
+    static constexpr size_t oF = oTot + (size_t)NP * DK * 4;
+    static constexpr size_t oQh = oF + (size_t)NF * DK * 4;
+    static constexpr size_t oQe = oQh + (size_t)C * PQ * sizeof(TS);
+    static constexpr size_t oKx = oQe + (size_t)C * PQ * sizeof(TM);
+    static constexpr size_t oKt = oKx + (size_t)KXR * PQ * sizeof(TS);
+    static constexpr size_t oV = oKt + (size_t)C * PK * sizeof(TM);
+    static constexpr size_t oSt = oV + (size_t)C * PV * sizeof(TM);
+    static constexpr size_t oQK = oSt + 2 * (size_t)DVT * PQ * sizeof(TM);
+    static constexpr size_t BYTES = oQK + (size_t)C * 4;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(NP * R == C && NP * DK == NT, "scan split");
+};
+
+// row offset of Kx_i (keys 0 .. 16 i + 15 referenced to block i's middle token)
+__device__ constexpr int kx_off(int i) { return 8 * i * (i + 1); }
+// factor row of D_ij, i > j
+__device__ constexpr int d_row(int i, int j) { return j == 0 ? i - 1 : (j == 1 ? i + 1 : 5); }
+
+template <typename TI, typename TO, int DK, int DVT>
+__global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
+    using Cfg = VdCfg<TI, DK, DVT>;
+    using TM = typename Cfg::TM;
+    using TS = typename Cfg::TS;
+    using MF = Mfma<TM>;
+    using MS = Mfma<TS>;
+    using frag = typename MF::frag;
+    using sfrag = typename MS::frag;
+    constexpr int C = Cfg::C, NRB = Cfg::NRB, PG = Cfg::PG, PQ = Cfg::PQ, PK = Cfg::PK, PV = Cfg::PV;
+    constexpr bool H = Cfg::H;
+    constexpr int E = MF::E;
+    static_assert(MS::E == E, "operand shapes");
+    constexpr int NKS = DK / (4 * E);       // k-steps over channels
+    constexpr int NTK = C / (4 * E);        // k-steps over tokens (state update)
+    constexpr int NTJ = DVT / 16, NTI = DK / 16, NTILE = NTI * NTJ;
+    constexpr int TPW = (NTILE + 7) / 8;    // state tiles per wave
+    constexpr int SEGQ = DK / 8, SEGV = DVT / 8;
+    constexpr int NQS = (C * SEGQ + 511) / 512;
+    constexpr int NVS = (C * SEGV + 511) / 512;
+    static_assert(DVT == 32, "two 16-column halves per row block");
+
+    __shared__ __align__(16) unsigned char smem[Cfg::BYTES];
+    float *Gs = reinterpret_cast<float *>(smem + Cfg::oG);
+    float *Tot = reinterpret_cast<float *>(smem + Cfg::oTot);
+    float *F = reinterpret_cast<float *>(smem + Cfg::oF);
+    TS *Qh = reinterpret_cast<TS *>(smem + Cfg::oQh);
+    TM *Qe = reinterpret_cast<TM *>(smem + Cfg::oQe);
+    TS *Kx = reinterpret_cast<TS *>(smem + Cfg::oKx);
+    TM *Kt = reinterpret_cast<TM *>(smem + Cfg::oKt);
+    TM *Vs = reinterpret_cast<TM *>(smem + Cfg::oV);
+    TM *St = reinterpret_cast<TM *>(smem + Cfg::oSt);
+    float *QK = reinterpret_cast<float *>(smem + Cfg::oQK);  // q_t . k_t per row
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
+    const int vid = xcd_virtual_block();
+    const int bh = vid / a.nsplit, split = vid % a.nsplit;
+    const int L = a.L, dv = a.dv, j0 = split * DVT;
+    const TI *qg = (const TI *)a.q + (size_t)bh * L * DK;
+    const TI *kg = (const TI *)a.k + (size_t)bh * L * DK;
+    const TI *vg = (const TI *)a.v + (size_t)bh * L * dv + j0;
+    const float *lgg = a.lg + (size_t)bh * L * DK;
+    TO *og = (TO *)a.o + (size_t)bh * L * dv + j0;
+    const int nchunks = (L + C - 1) / C;
+    const int rb = wv < 4 ? wv : 7 - wv;  // query row block (waves w, w+4 share a SIMD)
+    const int hh = wv >> 2;               // 16-column half of the value slice
+
+    // ---- carried state: tile wv + 8 m covers rows 16 ci + 4g + e, columns 16 cj + n
+    f32x4 Sacc[TPW];
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+        Sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = wv + 8 * m;
+        if (tile < NTILE && a.s_in) {
+            const int ci = tile / NTJ, cj = tile % NTJ;
+            const float *sp = a.s_in + (size_t)bh * DK * dv + (size_t)(ci * 16 + 4 * g) * dv + j0 + cj * 16 + n;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sacc[m][e] = sp[(size_t)e * dv];
+        }
+    }
+    auto write_st = [&](TM *Sdst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int tile = wv + 8 * m;
+            if (tile < NTILE) {
+                const int ci = tile / NTJ, cj = tile % NTJ;
+                st4<TM>(&Sdst[(cj * 16 + n) * PQ + ci * 16 + 4 * g], Sacc[m]);
+            }
+        }
+    };
+    write_st(St);
+
+    // ---- raw chunk registers (q, k, gates: segment tid + 512 m of the [C][DK/8]
+    // grid; v: of the [C][DVT/8] grid)
+    Raw8<TI> rq[NQS], rk[NQS], rv[NVS];
+    Raw8<float> rl[NQS];
+    auto load_chunk = [&](int c) __attribute__((always_inline)) {
+        const int t0 = c * C, nv = min(C, L - t0);
+#pragma unroll
+        for (int m = 0; m < NQS; ++m) {
+            const int sid = tid + 512 * m, row = sid / SEGQ, cs = sid % SEGQ;
+            if (sid < C * SEGQ && row < nv) {
+                const size_t off = (size_t)(t0 + row) * DK + 8 * cs;
+                rq[m] = ld_raw8<TI>(qg + off);
+                rk[m] = ld_raw8<TI>(kg + off);
+                rl[m] = ld_raw8<float>(lgg + off);
+            } else {
+                rq[m] = zero_raw8<TI>();
+                rk[m] = zero_raw8<TI>();
+                rl[m] = zero_raw8<float>();
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NVS; ++m) {
+            const int sid = tid + 512 * m, row = sid / SEGV, cs = sid % SEGV;
+            rv[m] = (sid < C * SEGV && row < nv) ? ld_raw8<TI>(vg + (size_t)(t0 + row) * dv + 8 * cs)
+                                                 : zero_raw8<TI>();
+        }
+    };
+    if (nchunks > 0) load_chunk(0);
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C, nv = min(C, L - t0);
+        __syncthreads();  // previous chunk's readers are done; S^T of chunk c-1 visible
+
+        // ---- P0: gates and V into LDS (rows past the sequence hold zeros)
+#pragma unroll
+        for (int m = 0; m < NVS; ++m) {
+            const int sid = tid + 512 * m;
+            if (sid < C * SEGV) {
+                float x[8];
+                unpack8<TI>(rv[m], x);
+                st8<TM>(&Vs[(sid / SEGV) * PV + 8 * (sid % SEGV)], x);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NQS; ++m) {
+            const int sid = tid + 512 * m;
+            if (sid < C * SEGQ) {
+                float x[8];
+                unpack8<float>(rl[m], x);
+                float *p = &Gs[(sid / SEGQ) * PG + 8 * (sid % SEGQ)];
+                *reinterpret_cast<f32x4 *>(p) = f32x4{x[0], x[1], x[2], x[3]};
+                *reinterpret_cast<f32x4 *>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+            }
+        }
+        __syncthreads();
+
+        // ---- P1: per-channel prefix over the chunk's rows (parts of R rows)
+        {
+            const int ch = tid % DK, part = tid / DK;
+            float acc = 0.f;
+#pragma unroll
+            for (int r = 0; r < Cfg::R; ++r) {
+                float *p = &Gs[(part * Cfg::R + r) * PG + ch];
+                acc += *p;
+                *p = acc;
+            }
+            Tot[part * DK + ch] = acc;
+            __syncthreads();
+            float off = 0.f;
+            for (int pp = 0; pp < part; ++pp) off += Tot[pp * DK + ch];
+            if (part > 0) {
+#pragma unroll
+                for (int r = 0; r < Cfg::R; ++r) Gs[(part * Cfg::R + r) * PG + ch] += off;
+            }
+        }
+        __syncthreads();
+        // per-channel factors
+        for (int idx = tid; idx < Cfg::NF * DK; idx += 512) {
+            const int fr = idx / DK, ch = idx % DK;
+            const float gend = Gs[(C - 1) * PG + ch];
+            float x;
+            if (fr < 4) {
+                x = Gs[(16 * fr + 8) * PG + ch];
+            } else if (fr < 8) {
+                x = gend - Gs[(16 * (fr - 4) + 8) * PG + ch];
+            } else if (fr < 14) {
+                const int pidx = fr - 8;
+                const int i = pidx < 3 ? pidx + 1 : (pidx < 5 ? pidx - 1 : 3);
+                const int j = pidx < 3 ? 0 : (pidx < 5 ? 1 : 2);
+                x = Gs[(16 * i + 8) * PG + ch] - Gs[(16 * j + 8) * PG + ch];
+            } else {
+                x = gend;
+            }
+            F[idx] = __expf(x);
+        }
+        __syncthreads();
+
+        // ---- P2: operand tiles from this thread's q and k segments
+#pragma unroll
+        for (int m = 0; m < NQS; ++m) {
+            const int sid = tid + 512 * m;
+            if (sid < C * SEGQ) {
+                const int row = sid / SEGQ, c0 = 8 * (sid % SEGQ);
+                const int blk = row >> 4, mid = 16 * blk + 8;
+                float q8[8], k8[8], gr[8], gm[8];
+                unpack8<TI>(rq[m], q8);
+                unpack8<TI>(rk[m], k8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    gr[e] = Gs[row * PG + c0 + e];
+                    gm[e] = Gs[mid * PG + c0 + e];
+                }
+                // the undecayed diagonal score q_t . k_t from the inputs themselves,
+                // reduced over the row's SEGQ consecutive lanes
+                float qk = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qk += q8[e] * k8[e];
+#pragma unroll
+                for (int off = 1; off < SEGQ; off <<= 1) qk += __shfl_xor(qk, off, 64);
+                if (c0 == 0) QK[row] = qk;
+                float qh[8], qe[8], kb[8], kt[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    qh[e] = q8[e] * __expf(gr[e] - gm[e]);
+                    qe[e] = qh[e] * F[(Cfg::FQ + blk) * DK + c0 + e];
+                    kb[e] = k8[e] * __expf(gm[e] - gr[e]);
+                    kt[e] = kb[e] * F[(Cfg::FKT + blk) * DK + c0 + e];
+                }
+                st8<TS>(&Qh[row * PQ + c0], qh);
+                st8<TM>(&Qe[row * PQ + c0], qe);
+                st8<TM>(&Kt[row * PK + c0], kt);
+                st8<TS>(&Kx[(kx_off(blk) + row) * PQ + c0], kb);
+                for (int i = blk + 1; i < NRB; ++i) {
+                    float kd[8];
+                    const float *d = &F[(Cfg::FD + d_row(i, blk)) * DK + c0];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kd[e] = kb[e] * d[e];
+                    st8<TS>(&Kx[(kx_off(i) + row) * PQ + c0], kd);
+                }
+            }
+        }
+        if (c + 1 < nchunks) load_chunk(c + 1);
+        __syncthreads();
+
+        // ---- P3: this wave's output tile and state tiles
+        const TM *Stc = St + (c & 1) * DVT * PQ;
+        TM *Stn = St + ((c + 1) & 1) * DVT * PQ;
+        const int rl_ = rb * 16 + n;  // chunk-local query row of this lane (B operand column)
+        sfrag qh[NKS];
+        frag qe[NKS], sf[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int col = g * (DK / 4) + ks * E;
+            qh[ks] = ld_frag<TS>(&Qh[rl_ * PQ + col]);
+            qe[ks] = ld_frag<TM>(&Qe[rl_ * PQ + col]);
+            sf[ks] = ld_frag<TM>(&Stc[(hh * 16 + n) * PQ + col]);
+        }
+        // inter: D[j][r] = sum_c S[c][j] q_r[c] e^{G_r[c]}
+        f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) oacc = MF::mma(sf[ks], qe[ks], oacc);
+        // scores D[s][r] for key blocks sb <= rb
+        f32x4 sc[NRB];
+        const int ko = kx_off(rb);
+#pragma unroll
+        for (int sb = 0; sb < NRB; ++sb) {
+            sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (sb <= rb) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    sc[sb] = MS::mma(ld_frag<TS>(&Kx[(ko + sb * 16 + n) * PQ + g * (DK / 4) + ks * E]), qh[ks],
+                                     sc[sb]);
+                if (sb == rb) {  // causal mask; the diagonal itself is exact
+                    const float qk = QK[rl_];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (4 * g + e > n) sc[sb][e] = 0.f;
+                        if (4 * g + e == n) sc[sb][e] = qk;
+                    }
+                }
+            }
+        }
+        // intra: D[j][r] += sum_s V[s][j] A[r][s]
+        if constexpr (H) {
+#pragma unroll
+            for (int p = 0; p < NRB / 2; ++p) {
+                if (2 * p <= rb) {
+                    frag bop;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bop[e] = from_f32<TM>(sc[2 * p][e]);
+                        bop[4 + e] = from_f32<TM>(sc[2 * p + 1][e]);
+                    }
+                    oacc = MF::mma(tr_frag<PV>(Vs, 32 * p + 4 * g, hh * 16, lane), bop, oacc);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int sb = 0; sb < NRB; ++sb) {
+                if (sb <= rb) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        oacc = MF::mma(Vs[(sb * 16 + 4 * g + e) * PV + hh * 16 + n], sc[sb][e], oacc);
+                }
+            }
+        }
+        if (rl_ < nv) st4<TO>(og + (size_t)(t0 + rl_) * dv + hh * 16 + 4 * g, oacc);
+
+        // state: S <- Diag(e^{G_end}) S + (K (.) e^{G_end - G})^T V
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int tile = wv + 8 * m;
+            if (tile < NTILE) {
+                const int ci = tile / NTJ, cj = tile % NTJ;
+                const f32x4 eg = *reinterpret_cast<const f32x4 *>(&F[Cfg::FEND * DK + ci * 16 + 4 * g]);
+                Sacc[m] *= eg;
+#pragma unroll
+                for (int ks = 0; ks < NTK; ++ks) {
+                    frag ka, vb;
+                    if constexpr (H) {
+                        ka = tr_frag<PK>(Kt, 32 * ks + 4 * g, ci * 16, lane);
+                        vb = tr_frag<PV>(Vs, 32 * ks + 4 * g, cj * 16, lane);
+                    } else {
+                        ka = Kt[(4 * ks + g) * PK + ci * 16 + n];
+                        vb = Vs[(4 * ks + g) * PV + cj * 16 + n];
+                    }
+                    Sacc[m] = MF::mma(ka, vb, Sacc[m]);
+                }
+            }
+        }
+        write_st(Stn);
+    }
+
+    if (a.s_out) {
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int tile = wv + 8 * m;
+            if (tile < NTILE) {
+                const int ci = tile / NTJ, cj = tile % NTJ;
+                float *sp = a.s_out + (size_t)bh * DK * dv + (size_t)(ci * 16 + 4 * g) * dv + j0 + cj * 16 + n;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sp[(size_t)e * dv] = Sacc[m][e];
+            }
+        }
+    }
+}
+
+template <typename TI, typename TO, int DK>
+hipError_t launch_vdecay(const ChunkArgs &a, hipStream_t st) {
+    constexpr int DVT = 32;
+    hipLaunchKernelGGL((vdecay_fwd_kernel<TI, TO, DK, DVT>), dim3(a.BH * a.nsplit), dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace la

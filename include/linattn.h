@@ -16,6 +16,12 @@
  *   LA_DECAY        S_t = gamma_t S_{t-1} + k_t v_t^T with gamma_t = exp(l_t)
  *                   (wln20 "LLM注意力优化：线性注意力", data-dependent decay
  *                   equation; a constant l gives the data-independent decay).
+ *   LA_VECTOR_DECAY S_t = Diag(alpha_t) S_{t-1} + k_t v_t^T with one gate per key
+ *                   channel, alpha_t = exp(l_t), l_t in R^{d_k}; o_t = S_t^T q_t
+ *                   (tensorplay section 5.1: the GLA gate matrix G_t (.) S_{t-1},
+ *                   alpha_t broadcast over the value columns; section 5.2 gives
+ *                   its chunk form (Q (.) B)(K / B)^T with B the cumulative
+ *                   product of the gates).
  *   LA_GATED_DELTA  S_t = alpha_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
  *                   alpha_t = exp(l_t) (alpha = 1 when log_gate is NULL, i.e. the
  *                   DeltaNet rule), o_t = S_t^T q_t. This is the transpose of the
@@ -77,7 +83,8 @@ typedef enum la_variant {
     LA_PLAIN = 0,
     LA_NORMALIZED = 1,
     LA_DECAY = 2,
-    LA_GATED_DELTA = 3
+    LA_GATED_DELTA = 3,
+    LA_VECTOR_DECAY = 4
 } la_variant;
 
 typedef enum la_dtype {
@@ -87,7 +94,8 @@ typedef enum la_dtype {
 
 /*
  * Workspace bytes la_chunk_fwd needs for this problem (written to *bytes).
- * Zero for LA_PLAIN, LA_NORMALIZED and LA_DECAY, which run in one fused pass.
+ * Zero for LA_PLAIN, LA_NORMALIZED, LA_DECAY and LA_VECTOR_DECAY, which run in
+ * one fused pass.
  * LA_GATED_DELTA runs a chunk-parallel preparation pass first and stores its
  * per-chunk products (W and U~ of the chunkwise delta-rule form) there:
  * B*H*ceil(L/C)*C*d_k elements (rounded up to 256 bytes) plus B*H*ceil(L/C)*C*d_v
@@ -102,7 +110,12 @@ la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
  *   q, k, v     inputs (dtype dt), required when L > 0.
  *   log_gate    [B,H,L] float32 log-gates l_t <= 0 (finite): required for
  *               LA_DECAY; optional for LA_GATED_DELTA (NULL = alpha 1); must be
- *               NULL for LA_PLAIN and LA_NORMALIZED.
+ *               NULL for LA_PLAIN and LA_NORMALIZED. LA_VECTOR_DECAY takes
+ *               [B,H,L,d_k] (one gate per key channel), required, with every
+ *               entry in [-10, 0]: the chunk form rebases the per-channel decay
+ *               around the middle of each 16-token block, and that range keeps
+ *               every rebased factor below e^80 (results are unspecified
+ *               outside it).
  *   beta        [B,H,L] float32 in [0,1]: required for LA_GATED_DELTA, NULL
  *               otherwise.
  *   state_in    [B,H,d_k,d_v] float32 initial state, NULL = zero.
@@ -118,8 +131,9 @@ la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
  *   B, H, L     batch, heads, tokens: B, H >= 1; L >= 0 (L = 0 only copies
  *               state_in/z_in, or zeros, to state_out/z_out).
  *   d_k         32, 64 or 128.   d_v  32, 64, 96 or 128 (a multiple of 32).
- *   C           chunk length: 64 or 128 (LA_GATED_DELTA: 64). L need not be a
- *               multiple of C; a ragged last chunk is handled.
+ *   C           chunk length: 64 or 128 (LA_GATED_DELTA, LA_VECTOR_DECAY: 64).
+ *               L need not be a multiple of C; a ragged last chunk is handled.
+ *               LA_VECTOR_DECAY with LA_F32 inputs supports d_k 32 and 64.
  *   workspace   device buffer of at least la_chunk_fwd_workspace_size() bytes
  *               (may be NULL when that size is 0), 256-byte aligned.
  */
@@ -138,9 +152,12 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
  *   LA_GATED_DELTA  r = S^T k;  S <- alpha (S - beta k r^T) + beta k v^T,
  *                   alpha = exp(l), or 1 when log_gate is NULL (DeltaNet)
  *                   (wln20 Gated DeltaNet section, d_k x d_v orientation)
+ *   LA_VECTOR_DECAY S <- Diag(exp(l)) S + k v^T, l [N,H,d_k] (tensorplay
+ *                   section 5.1)
  *   q, k [N,H,d_k], v [N,H,d_v] in dtype dt; o [N,H,d_v] in dtype o_dt (the
  *   step itself is computed in fp32); log_gate [N,H] float32 (required for
- *   LA_DECAY, optional for LA_GATED_DELTA, NULL for LA_PLAIN); beta [N,H] float32,
+ *   LA_DECAY, optional for LA_GATED_DELTA, NULL for LA_PLAIN; [N,H,d_k] and
+ *   required for LA_VECTOR_DECAY); beta [N,H] float32,
  *   required for LA_GATED_DELTA and NULL otherwise; state [N,H,d_k,d_v] float32,
  *   read and written in place. o must not overlap the state or inputs.
  *   N, H >= 1; d_k, d_v in {32, 64, 128}. LA_NORMALIZED is not supported.

@@ -7,7 +7,7 @@ import pytest
 
 import chunkwise_linear_rnn_causal_amd as la
 
-PLAIN, NORM, DECAY, GDN = 0, 1, 2, 3
+PLAIN, NORM, DECAY, GDN, VDECAY = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 INVALID, UNSUPPORTED = la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
@@ -65,6 +65,10 @@ def test_workspace_sizes():
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(var=7), INVALID), (dict(dt=5), INVALID), (dict(odt=5), INVALID),
+    (dict(var=VDECAY), INVALID),                      # per-channel decay needs its gates
+    (dict(var=VDECAY, lg=FAKE + 0x100000, C=128), UNSUPPORTED),
+    (dict(var=VDECAY, lg=FAKE + 0x100000, dt=F32, dk=128), UNSUPPORTED),
+    (dict(var=VDECAY, lg=FAKE + 0x100000, o=FAKE + 0x100000 + 0x7000), INVALID),  # o inside the gates
     (dict(dt=F32, odt=BF16), UNSUPPORTED),
     (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(L=-3), INVALID),
     (dict(dk=48), UNSUPPORTED), (dict(dk=256), UNSUPPORTED),
@@ -94,6 +98,8 @@ def dec(var=DECAY, dt=BF16, odt=F32, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, l
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(var=9), INVALID), (dict(var=NORM), UNSUPPORTED),
+    (dict(var=VDECAY, lg=None), INVALID),             # per-channel decay needs its gates
+    (dict(var=VDECAY, o=FAKE + 0x3800), INVALID),     # o inside the [N,H,d_k] gates
     (dict(var=GDN), INVALID),                         # delta rule needs beta
     (dict(var=GDN, beta=FAKE + 0x5000, o=FAKE + 0x5000), INVALID),  # o overlaps beta
     (dict(odt=7), INVALID), (dict(dt=F32, odt=BF16), UNSUPPORTED),

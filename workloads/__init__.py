@@ -35,7 +35,7 @@ import numpy as np
 TAG_Q, TAG_K, TAG_V, TAG_GATE, TAG_BETA, TAG_STATE = 1, 2, 3, 4, 5, 6
 TAG_CONV_W, TAG_CONV_WINDOW = 7, 8
 
-VARIANTS = ("plain", "normalized", "decay", "gated_delta")
+VARIANTS = ("plain", "normalized", "decay", "gated_delta", "vector_decay")
 
 # The five workloads, each named by what it is. "recipe" selects the input
 # distribution (see _draw_slice); sizes are the ones the workloads are quoted at.
@@ -55,6 +55,10 @@ CONFIGS: Dict[str, dict] = {
     "gated_delta_bf16_b2h16_l8192_d128": dict(
         kind="chunk", variant="gated_delta", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, C=64,
         recipe="gdn"),
+    # the decay workload's shapes with one gate per key channel (GLA-style gates)
+    "vector_decay_bf16_b4h32_l8192_d128": dict(
+        kind="chunk", variant="vector_decay", dtype="bf16", B=4, H=32, L=8192, dk=128, dv=128, C=64,
+        recipe="gla"),
     # the short convolution in front of the delta rule, at that workload's q, k, v shapes
     "short_conv_qkv_bf16_b2h16_l8192_d128_k4": dict(
         kind="conv", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, K=4, recipe="conv"),
@@ -66,6 +70,7 @@ DEFAULT_RECIPE = {
     "normalized": "elu1",
     "decay": "gauss_scaled_gate",
     "gated_delta": "gdn",
+    "vector_decay": "gla",
 }
 
 
@@ -117,7 +122,7 @@ def _draw_slice(recipe: str, tag: int, seed: int, b: int, h: int, L: int, d: int
     rng = stream(seed, tag, b, h)
     if tag in (TAG_Q, TAG_K, TAG_V):
         x = rng.standard_normal((L, d), dtype=np.float32)
-        if recipe in ("gauss_scaled", "gauss_scaled_gate"):
+        if recipe in ("gauss_scaled", "gauss_scaled_gate", "gla", "gla_strong"):
             return (x / np.float32(math.sqrt(d))).astype(np.float32)
         if recipe == "elu1":
             return _elu1(x) if tag in (TAG_Q, TAG_K) else x
@@ -127,6 +132,12 @@ def _draw_slice(recipe: str, tag: int, seed: int, b: int, h: int, L: int, d: int
     if tag == TAG_GATE:
         if recipe == "gauss_scaled_gate" or recipe == "gdn":
             return _sigmoid_log(rng.normal(4.0, 1.0, size=L))
+        if recipe == "gla":
+            # alpha = sigmoid(x)^(1/tau) per key channel, tau = 16: l = log sigmoid(x) / 16
+            return (_sigmoid_log(rng.normal(0.0, 1.0, size=(L, d))).astype(np.float64) / 16.0).astype(np.float32)
+        if recipe == "gla_strong":
+            # per-channel gates spread over the whole supported range [-10, 0]
+            return (-10.0 * rng.random((L, d)) ** 3).astype(np.float32)
         raise ValueError(recipe)
     if tag == TAG_BETA:
         return _sigmoid(rng.normal(0.0, 1.0, size=L))
@@ -134,7 +145,12 @@ def _draw_slice(recipe: str, tag: int, seed: int, b: int, h: int, L: int, d: int
 
 
 def recipe_has_gate(recipe: str) -> bool:
-    return recipe in ("gauss_scaled_gate", "gdn")
+    return recipe in ("gauss_scaled_gate", "gdn", "gla", "gla_strong")
+
+
+def recipe_gate_width(recipe: str, dk: int) -> int:
+    """Gates per token: one (scalar decay) or one per key channel."""
+    return dk if recipe in ("gla", "gla_strong") else 1
 
 
 def recipe_has_beta(recipe: str) -> bool:
@@ -200,7 +216,8 @@ def make_chunk_inputs(variant: str, dtype: str, B: int, H: int, L: int, dk: int,
     v = np.empty((nb * nh, L, dv), sdt)
     has_gate = recipe_has_gate(recipe)
     has_beta = recipe_has_beta(recipe)
-    lg = np.empty((nb * nh, L), np.float32) if has_gate else None
+    gw = recipe_gate_width(recipe, dk)
+    lg = (np.empty((nb * nh, L, gw) if gw > 1 else (nb * nh, L), np.float32)) if has_gate else None
     be = np.empty((nb * nh, L), np.float32) if has_beta else None
 
     def fill(i: int) -> None:
@@ -209,7 +226,7 @@ def make_chunk_inputs(variant: str, dtype: str, B: int, H: int, L: int, dk: int,
         k[i] = _store(_draw_slice(recipe, TAG_K, seed, b, h, L, dk), dtype)
         v[i] = _store(_draw_slice(recipe, TAG_V, seed, b, h, L, dv), dtype)
         if lg is not None:
-            lg[i] = _draw_slice(recipe, TAG_GATE, seed, b, h, L, 1)
+            lg[i] = _draw_slice(recipe, TAG_GATE, seed, b, h, L, gw)
         if be is not None:
             be[i] = _draw_slice(recipe, TAG_BETA, seed, b, h, L, 1)
 
@@ -237,7 +254,7 @@ def make_chunk_inputs(variant: str, dtype: str, B: int, H: int, L: int, dk: int,
     return ChunkInputs(
         variant=variant, dtype=dtype, B=nb, H=nh, L=L, dk=dk, dv=dv,
         q=q.reshape(nb, nh, L, dk), k=k.reshape(nb, nh, L, dk), v=v.reshape(nb, nh, L, dv),
-        log_gate=None if lg is None else lg.reshape(nb, nh, L),
+        log_gate=None if lg is None else lg.reshape((nb, nh) + lg.shape[1:]),
         beta=None if be is None else be.reshape(nb, nh, L),
         state_in=st, z_in=z, meta=dict(seed=seed, recipe=recipe, heads=pairs))
 
