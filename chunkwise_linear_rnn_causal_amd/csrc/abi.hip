@@ -302,8 +302,7 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
         if (e != hipSuccess) return LA_ERR_HIP;
     }
     hipError_t e;
-    if (var == LA_VECTOR_DECAY) {
-        a.nsplit = d_v / 32;
+    if (var == LA_VECTOR_DECAY) {  // the launcher picks its own value slices
         if (dt == LA_F32)
             e = dispatch_vdecay<float, float>(d_k, a, st);
         else if (o_dt == LA_F32)

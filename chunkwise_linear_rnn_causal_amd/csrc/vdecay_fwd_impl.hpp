@@ -14,23 +14,29 @@
 // formed per 16-token block pair around each block's middle token m_i:
 //   q_r e^{G_r - G_{m_i}}  and  k_s e^{G_{m_j} - G_s}   (row r in block i, key s in block j)
 // are each within 8 tokens of their reference, and the pair is joined by the
-// per-channel factor D_ij = e^{G_{m_i} - G_{m_j}} <= 1 folded into the key
-// operand. Every factor is bounded by e^{8 max|l|}; with l >= -10 (the
-// documented domain) all of them stay below e^80 and fit the fp32 range of the
-// score operands (bf16 for bf16 inputs, fp32 for fp32 inputs). One exp per
+// per-channel factor D_ij = e^{G_{m_i} - G_{m_j}} <= 1, applied to the key
+// operand in registers. Every factor is bounded by e^{8 max|l|}; with l >= -10
+// (the documented domain) all of them stay below e^80 and fit the fp32 range of
+// the score operands (bf16 for bf16 inputs, fp32 for fp32 inputs). One exp per
 // element per chunk plus 15 per channel, instead of one per (row, key, channel).
 // The diagonal score q_t . k_t carries no decay; it is taken in fp32 from the
 // inputs, so bf16's rounding only touches terms damped by at least one gate.
 //
-// Mapping. One workgroup (8 waves) owns one (batch*head, 32-column value
-// slice) and walks the chunks in order with its d_k x 32 slice of S in fp32
-// MFMA accumulators. Per chunk: the gates are scanned per channel in LDS, the
-// operand tiles above are derived from the chunk's q and k registers, then each
-// wave computes the output tile of one query row block and one 16-column half
-// (inter term, score tiles, intra term V^T A^T with the score accumulators fed
-// straight in as the B operand, as in the scalar kernel) and its share of the
-// state tiles. The next chunk's loads are issued before the math.
+// Mapping. One workgroup (8 waves) owns one (batch*head, DVT-column value
+// slice) and walks the chunks in order with its d_k x DVT slice of S in fp32
+// MFMA accumulators. Per chunk:
+//  1. each wave loads the gates of d_k/8 channels with the chunk's rows in its
+//     lanes, takes the per-channel prefix with a DPP wave scan, writes G, and
+//     forms that channel's 15 reference factors with lane shuffles;
+//  2. every thread derives its q and k segments' operand rows (one exp each);
+//  3. each wave computes the output tiles of one query row block and one half
+//     of the slice's columns (inter term, score tiles, intra term V^T A^T with
+//     the score accumulators fed straight in as the B operand, as in the scalar
+//     kernel) and its share of the state tiles.
+// Three barriers per chunk; the next chunk's loads are issued before the math.
 #pragma once
+
+#include <type_traits>
 
 #include "la_common.hpp"
 #include "la_kernels.hpp"
@@ -48,32 +54,26 @@ template <typename TI, int DK, int DVT> struct VdCfg {
     using TS = typename ScoreOp<TI>::type;
     static constexpr int C = 64, NT = 512, NRB = 4;
     static constexpr bool H = sizeof(TM) == 2;
-    static constexpr int PG = DK;                      // gate tile pitch (fp32)
-    static constexpr int PQ = H ? DK + 8 : DK + 4;     // Qh, Qe, Kx, St pitch
+    static constexpr int PG = DK + 4;                  // gate tile pitch (fp32)
+    static constexpr int PQ = H ? DK + 8 : DK + 4;     // Qh, Qe, Kb, St pitch
     static constexpr int PK = H ? DK + 16 : DK + 4;    // Kt pitch (transpose reads)
     static constexpr int PV = H ? DVT + 16 : DVT + 4;  // V pitch (transpose reads)
-    static constexpr int NP = NT / DK;                 // scan parts per channel
-    static constexpr int R = C / NP;                   // rows per scan part
-    static constexpr int KXR = 160;                    // Kx rows: 16 + 32 + 48 + 64
+    static constexpr int GW = DK / 8;                  // gate channels per wave
     // factor rows: e^{G_m_i} (4), e^{G_end - G_m_j} (4), D_ij (6), e^{G_end} (1)
     static constexpr int NF = 15, FQ = 0, FKT = 4, FD = 8, FEND = 14;
     static constexpr size_t oG = 0;
-    static constexpr size_t oTot = oG + (size_t)C * PG * 4;
-    static constexpr size_t oF = oTot + (size_t)NP * DK * 4;
+    static constexpr size_t oF = oG + (size_t)C * PG * 4;
     static constexpr size_t oQh = oF + (size_t)NF * DK * 4;
     static constexpr size_t oQe = oQh + (size_t)C * PQ * sizeof(TS);
-    static constexpr size_t oKx = oQe + (size_t)C * PQ * sizeof(TM);
-    static constexpr size_t oKt = oKx + (size_t)KXR * PQ * sizeof(TS);
+    static constexpr size_t oKb = oQe + (size_t)C * PQ * sizeof(TM);
+    static constexpr size_t oKt = oKb + (size_t)C * PQ * sizeof(TS);
     static constexpr size_t oV = oKt + (size_t)C * PK * sizeof(TM);
     static constexpr size_t oSt = oV + (size_t)C * PV * sizeof(TM);
     static constexpr size_t oQK = oSt + 2 * (size_t)DVT * PQ * sizeof(TM);
     static constexpr size_t BYTES = oQK + (size_t)C * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
-    static_assert(NP * R == C && NP * DK == NT, "scan split");
 };
 
-// row offset of Kx_i (keys 0 .. 16 i + 15 referenced to block i's middle token)
-__device__ constexpr int kx_off(int i) { return 8 * i * (i + 1); }
 // factor row of D_ij, i > j
 __device__ constexpr int d_row(int i, int j) { return j == 0 ? i - 1 : (j == 1 ? i + 1 : 5); }
 
@@ -87,25 +87,26 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
     using frag = typename MF::frag;
     using sfrag = typename MS::frag;
     constexpr int C = Cfg::C, NRB = Cfg::NRB, PG = Cfg::PG, PQ = Cfg::PQ, PK = Cfg::PK, PV = Cfg::PV;
+    constexpr int GW = Cfg::GW;
     constexpr bool H = Cfg::H;
     constexpr int E = MF::E;
     static_assert(MS::E == E, "operand shapes");
     constexpr int NKS = DK / (4 * E);       // k-steps over channels
     constexpr int NTK = C / (4 * E);        // k-steps over tokens (state update)
     constexpr int NTJ = DVT / 16, NTI = DK / 16, NTILE = NTI * NTJ;
+    constexpr int NTJW = NTJ / 2;           // output tiles per wave (half the slice)
     constexpr int TPW = (NTILE + 7) / 8;    // state tiles per wave
     constexpr int SEGQ = DK / 8, SEGV = DVT / 8;
     constexpr int NQS = (C * SEGQ + 511) / 512;
     constexpr int NVS = (C * SEGV + 511) / 512;
-    static_assert(DVT == 32, "two 16-column halves per row block");
+    static_assert(DVT == 32 || DVT == 64, "value slice");
 
     __shared__ __align__(16) unsigned char smem[Cfg::BYTES];
     float *Gs = reinterpret_cast<float *>(smem + Cfg::oG);
-    float *Tot = reinterpret_cast<float *>(smem + Cfg::oTot);
     float *F = reinterpret_cast<float *>(smem + Cfg::oF);
     TS *Qh = reinterpret_cast<TS *>(smem + Cfg::oQh);
     TM *Qe = reinterpret_cast<TM *>(smem + Cfg::oQe);
-    TS *Kx = reinterpret_cast<TS *>(smem + Cfg::oKx);
+    TS *Kb = reinterpret_cast<TS *>(smem + Cfg::oKb);
     TM *Kt = reinterpret_cast<TM *>(smem + Cfg::oKt);
     TM *Vs = reinterpret_cast<TM *>(smem + Cfg::oV);
     TM *St = reinterpret_cast<TM *>(smem + Cfg::oSt);
@@ -118,11 +119,11 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
     const TI *qg = (const TI *)a.q + (size_t)bh * L * DK;
     const TI *kg = (const TI *)a.k + (size_t)bh * L * DK;
     const TI *vg = (const TI *)a.v + (size_t)bh * L * dv + j0;
-    const float *lgg = a.lg + (size_t)bh * L * DK;
+    const float *lgg = a.lg + (size_t)bh * L * DK + wv * GW;  // this wave's gate channels
     TO *og = (TO *)a.o + (size_t)bh * L * dv + j0;
     const int nchunks = (L + C - 1) / C;
     const int rb = wv < 4 ? wv : 7 - wv;  // query row block (waves w, w+4 share a SIMD)
-    const int hh = wv >> 2;               // 16-column half of the value slice
+    const int hh = wv >> 2;               // half of the value slice
 
     // ---- carried state: tile wv + 8 m covers rows 16 ci + 4g + e, columns 16 cj + n
     f32x4 Sacc[TPW];
@@ -149,10 +150,10 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
     };
     write_st(St);
 
-    // ---- raw chunk registers (q, k, gates: segment tid + 512 m of the [C][DK/8]
-    // grid; v: of the [C][DVT/8] grid)
+    // ---- chunk registers: q, k segments tid + 512 m of the [C][DK/8] grid, v of
+    // the [C][DVT/8] grid, and this wave's GW gate channels of row `lane`
     Raw8<TI> rq[NQS], rk[NQS], rv[NVS];
-    Raw8<float> rl[NQS];
+    f32x4 gl[GW / 4];
     auto load_chunk = [&](int c) __attribute__((always_inline)) {
         const int t0 = c * C, nv = min(C, L - t0);
 #pragma unroll
@@ -162,11 +163,9 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
                 const size_t off = (size_t)(t0 + row) * DK + 8 * cs;
                 rq[m] = ld_raw8<TI>(qg + off);
                 rk[m] = ld_raw8<TI>(kg + off);
-                rl[m] = ld_raw8<float>(lgg + off);
             } else {
                 rq[m] = zero_raw8<TI>();
                 rk[m] = zero_raw8<TI>();
-                rl[m] = zero_raw8<float>();
             }
         }
 #pragma unroll
@@ -175,14 +174,25 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
             rv[m] = (sid < C * SEGV && row < nv) ? ld_raw8<TI>(vg + (size_t)(t0 + row) * dv + 8 * cs)
                                                  : zero_raw8<TI>();
         }
+#pragma unroll
+        for (int u = 0; u < GW / 4; ++u)
+            gl[u] = lane < nv ? *reinterpret_cast<const f32x4 *>(lgg + (size_t)(t0 + lane) * DK + 4 * u)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
     };
     if (nchunks > 0) load_chunk(0);
+
+    // reference rows of the 15 factors (fr = lane % 16): e^{G[ra] - G[rb]}, rb < 0: none
+    const int fr = lane & 15;
+    const int ra = fr < 4 ? 16 * fr + 8 : fr < 8 ? C - 1 : fr == 8 ? 24 : fr == 9 ? 40 : fr == 10 ? 56
+                 : fr == 11 ? 40 : fr < 14 ? 56 : C - 1;
+    const int rbf = fr < 4 ? -1 : fr < 8 ? 16 * (fr - 4) + 8 : fr < 11 ? 8 : fr < 13 ? 24 : fr == 13 ? 40 : -1;
 
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * C, nv = min(C, L - t0);
         __syncthreads();  // previous chunk's readers are done; S^T of chunk c-1 visible
 
-        // ---- P0: gates and V into LDS (rows past the sequence hold zeros)
+        // ---- 1. V into LDS; gates: per-channel prefix over the rows (lanes), G
+        // and the reference factors of this wave's channels
 #pragma unroll
         for (int m = 0; m < NVS; ++m) {
             const int sid = tid + 512 * m;
@@ -193,73 +203,44 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
             }
         }
 #pragma unroll
-        for (int m = 0; m < NQS; ++m) {
-            const int sid = tid + 512 * m;
-            if (sid < C * SEGQ) {
-                float x[8];
-                unpack8<float>(rl[m], x);
-                float *p = &Gs[(sid / SEGQ) * PG + 8 * (sid % SEGQ)];
-                *reinterpret_cast<f32x4 *>(p) = f32x4{x[0], x[1], x[2], x[3]};
-                *reinterpret_cast<f32x4 *>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+        for (int u = 0; u < GW / 4; ++u) {
+            f32x4 gsum;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gsum[e] = wave_inclusive_sum(gl[u][e]);
+            *reinterpret_cast<f32x4 *>(&Gs[lane * PG + wv * GW + 4 * u]) = gsum;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float xa = __shfl(gsum[e], ra, 64);
+                const float xb = __shfl(gsum[e], rbf < 0 ? 0 : rbf, 64);
+                const float f = __expf(rbf < 0 ? xa : xa - xb);
+                if (lane < Cfg::NF) F[fr * DK + wv * GW + 4 * u + e] = f;
             }
         }
         __syncthreads();
 
-        // ---- P1: per-channel prefix over the chunk's rows (parts of R rows)
-        {
-            const int ch = tid % DK, part = tid / DK;
-            float acc = 0.f;
-#pragma unroll
-            for (int r = 0; r < Cfg::R; ++r) {
-                float *p = &Gs[(part * Cfg::R + r) * PG + ch];
-                acc += *p;
-                *p = acc;
-            }
-            Tot[part * DK + ch] = acc;
-            __syncthreads();
-            float off = 0.f;
-            for (int pp = 0; pp < part; ++pp) off += Tot[pp * DK + ch];
-            if (part > 0) {
-#pragma unroll
-                for (int r = 0; r < Cfg::R; ++r) Gs[(part * Cfg::R + r) * PG + ch] += off;
-            }
-        }
-        __syncthreads();
-        // per-channel factors
-        for (int idx = tid; idx < Cfg::NF * DK; idx += 512) {
-            const int fr = idx / DK, ch = idx % DK;
-            const float gend = Gs[(C - 1) * PG + ch];
-            float x;
-            if (fr < 4) {
-                x = Gs[(16 * fr + 8) * PG + ch];
-            } else if (fr < 8) {
-                x = gend - Gs[(16 * (fr - 4) + 8) * PG + ch];
-            } else if (fr < 14) {
-                const int pidx = fr - 8;
-                const int i = pidx < 3 ? pidx + 1 : (pidx < 5 ? pidx - 1 : 3);
-                const int j = pidx < 3 ? 0 : (pidx < 5 ? 1 : 2);
-                x = Gs[(16 * i + 8) * PG + ch] - Gs[(16 * j + 8) * PG + ch];
-            } else {
-                x = gend;
-            }
-            F[idx] = __expf(x);
-        }
-        __syncthreads();
-
-        // ---- P2: operand tiles from this thread's q and k segments
+        // ---- 2. operand rows from this thread's q and k segments
 #pragma unroll
         for (int m = 0; m < NQS; ++m) {
             const int sid = tid + 512 * m;
             if (sid < C * SEGQ) {
                 const int row = sid / SEGQ, c0 = 8 * (sid % SEGQ);
                 const int blk = row >> 4, mid = 16 * blk + 8;
-                float q8[8], k8[8], gr[8], gm[8];
+                float q8[8], k8[8], gr[8], gm[8], fq[8], fk[8];
                 unpack8<TI>(rq[m], q8);
                 unpack8<TI>(rk[m], k8);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    gr[e] = Gs[row * PG + c0 + e];
-                    gm[e] = Gs[mid * PG + c0 + e];
+                for (int h4 = 0; h4 < 2; ++h4) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&Gs[row * PG + c0 + 4 * h4]);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&Gs[mid * PG + c0 + 4 * h4]);
+                    const f32x4 c4 = *reinterpret_cast<const f32x4 *>(&F[(Cfg::FQ + blk) * DK + c0 + 4 * h4]);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&F[(Cfg::FKT + blk) * DK + c0 + 4 * h4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        gr[4 * h4 + e] = a4[e];
+                        gm[4 * h4 + e] = b4[e];
+                        fq[4 * h4 + e] = c4[e];
+                        fk[4 * h4 + e] = d4[e];
+                    }
                 }
                 // the undecayed diagonal score q_t . k_t from the inputs themselves,
                 // reduced over the row's SEGQ consecutive lanes
@@ -273,54 +254,69 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     qh[e] = q8[e] * __expf(gr[e] - gm[e]);
-                    qe[e] = qh[e] * F[(Cfg::FQ + blk) * DK + c0 + e];
+                    qe[e] = qh[e] * fq[e];
                     kb[e] = k8[e] * __expf(gm[e] - gr[e]);
-                    kt[e] = kb[e] * F[(Cfg::FKT + blk) * DK + c0 + e];
+                    kt[e] = kb[e] * fk[e];
                 }
                 st8<TS>(&Qh[row * PQ + c0], qh);
                 st8<TM>(&Qe[row * PQ + c0], qe);
+                st8<TS>(&Kb[row * PQ + c0], kb);
                 st8<TM>(&Kt[row * PK + c0], kt);
-                st8<TS>(&Kx[(kx_off(blk) + row) * PQ + c0], kb);
-                for (int i = blk + 1; i < NRB; ++i) {
-                    float kd[8];
-                    const float *d = &F[(Cfg::FD + d_row(i, blk)) * DK + c0];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) kd[e] = kb[e] * d[e];
-                    st8<TS>(&Kx[(kx_off(i) + row) * PQ + c0], kd);
-                }
             }
         }
         if (c + 1 < nchunks) load_chunk(c + 1);
         __syncthreads();
 
-        // ---- P3: this wave's output tile and state tiles
+        // ---- 3. this wave's output tiles and state tiles
         const TM *Stc = St + (c & 1) * DVT * PQ;
         TM *Stn = St + ((c + 1) & 1) * DVT * PQ;
         const int rl_ = rb * 16 + n;  // chunk-local query row of this lane (B operand column)
+        const int jw = hh * (DVT / 2);  // first value column of this wave
         sfrag qh[NKS];
-        frag qe[NKS], sf[NKS];
+        frag qe[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
             const int col = g * (DK / 4) + ks * E;
             qh[ks] = ld_frag<TS>(&Qh[rl_ * PQ + col]);
             qe[ks] = ld_frag<TM>(&Qe[rl_ * PQ + col]);
-            sf[ks] = ld_frag<TM>(&Stc[(hh * 16 + n) * PQ + col]);
         }
         // inter: D[j][r] = sum_c S[c][j] q_r[c] e^{G_r[c]}
-        f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 oacc[NTJW];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) oacc = MF::mma(sf[ks], qe[ks], oacc);
-        // scores D[s][r] for key blocks sb <= rb
+        for (int jt = 0; jt < NTJW; ++jt) {
+            oacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                oacc[jt] = MF::mma(ld_frag<TM>(&Stc[(jw + jt * 16 + n) * PQ + g * (DK / 4) + ks * E]), qe[ks],
+                                   oacc[jt]);
+        }
+        // scores D[s][r] for key blocks sb <= rb; off the diagonal block the key
+        // operand takes the factor D_{rb,sb} of its channels
         f32x4 sc[NRB];
-        const int ko = kx_off(rb);
 #pragma unroll
         for (int sb = 0; sb < NRB; ++sb) {
             sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (sb <= rb) {
+                const float *Dr = &F[(Cfg::FD + (sb < rb ? d_row(rb, sb) : 0)) * DK];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    sc[sb] = MS::mma(ld_frag<TS>(&Kx[(ko + sb * 16 + n) * PQ + g * (DK / 4) + ks * E]), qh[ks],
-                                     sc[sb]);
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int col = g * (DK / 4) + ks * E;
+                    sfrag kf = ld_frag<TS>(&Kb[(sb * 16 + n) * PQ + col]);
+                    if (sb < rb) {
+                        if constexpr (E == 8) {
+                            const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&Dr[col]);
+                            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&Dr[col + 4]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                kf[e] = from_f32<TS>(to_f32<TS>(kf[e]) * d0[e]);
+                                kf[4 + e] = from_f32<TS>(to_f32<TS>(kf[4 + e]) * d1[e]);
+                            }
+                        } else {
+                            kf = kf * Dr[col];
+                        }
+                    }
+                    sc[sb] = MS::mma(kf, qh[ks], sc[sb]);
+                }
                 if (sb == rb) {  // causal mask; the diagonal itself is exact
                     const float qk = QK[rl_];
 #pragma unroll
@@ -342,7 +338,9 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
                         bop[e] = from_f32<TM>(sc[2 * p][e]);
                         bop[4 + e] = from_f32<TM>(sc[2 * p + 1][e]);
                     }
-                    oacc = MF::mma(tr_frag<PV>(Vs, 32 * p + 4 * g, hh * 16, lane), bop, oacc);
+#pragma unroll
+                    for (int jt = 0; jt < NTJW; ++jt)
+                        oacc[jt] = MF::mma(tr_frag<PV>(Vs, 32 * p + 4 * g, jw + jt * 16, lane), bop, oacc[jt]);
                 }
             }
         } else {
@@ -351,11 +349,18 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
                 if (sb <= rb) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        oacc = MF::mma(Vs[(sb * 16 + 4 * g + e) * PV + hh * 16 + n], sc[sb][e], oacc);
+#pragma unroll
+                        for (int jt = 0; jt < NTJW; ++jt)
+                            oacc[jt] = MF::mma(Vs[(sb * 16 + 4 * g + e) * PV + jw + jt * 16 + n], sc[sb][e],
+                                               oacc[jt]);
                 }
             }
         }
-        if (rl_ < nv) st4<TO>(og + (size_t)(t0 + rl_) * dv + hh * 16 + 4 * g, oacc);
+        if (rl_ < nv) {
+#pragma unroll
+            for (int jt = 0; jt < NTJW; ++jt)
+                st4<TO>(og + (size_t)(t0 + rl_) * dv + jw + jt * 16 + 4 * g, oacc[jt]);
+        }
 
         // state: S <- Diag(e^{G_end}) S + (K (.) e^{G_end - G})^T V
 #pragma unroll
@@ -398,8 +403,15 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
 
 template <typename TI, typename TO, int DK>
 hipError_t launch_vdecay(const ChunkArgs &a, hipStream_t st) {
-    constexpr int DVT = 32;
-    hipLaunchKernelGGL((vdecay_fwd_kernel<TI, TO, DK, DVT>), dim3(a.BH * a.nsplit), dim3(512), 0, st, a);
+    // 64-column slices halve the per-head gate and operand work against 32
+    ChunkArgs b = a;
+    if (a.dv % 64 == 0) {
+        b.nsplit = a.dv / 64;
+        hipLaunchKernelGGL((vdecay_fwd_kernel<TI, TO, DK, 64>), dim3(b.BH * b.nsplit), dim3(512), 0, st, b);
+    } else {
+        b.nsplit = a.dv / 32;
+        hipLaunchKernelGGL((vdecay_fwd_kernel<TI, TO, DK, 32>), dim3(b.BH * b.nsplit), dim3(512), 0, st, b);
+    }
     return hipGetLastError();
 }
 
