@@ -27,13 +27,15 @@
 // MFMA accumulators. Per chunk:
 //  1. each wave loads the gates of d_k/8 channels with the chunk's rows in its
 //     lanes, takes the per-channel prefix with a DPP wave scan, writes G, and
-//     forms that channel's 15 reference factors with lane shuffles;
+//     forms those channels' 15 reference factors from the rows it wrote;
 //  2. every thread derives its q and k segments' operand rows (one exp each);
-//  3. each wave computes the output tiles of one query row block and one half
-//     of the slice's columns (inter term, score tiles, intra term V^T A^T with
-//     the score accumulators fed straight in as the B operand, as in the scalar
-//     kernel) and its share of the state tiles.
-// Three barriers per chunk; the next chunk's loads are issued before the math.
+//  3. the chunk's 10 score tiles are spread over the waves and written, as
+//     A[r][s] in the operand type, over the dead gate tile; after a barrier
+//     each wave computes the output tiles of one query row block and one half
+//     of the slice's columns (inter term, intra term V^T A^T) and its share of
+//     the state tiles.
+// Four barriers per chunk. The next chunk's gates and V are loaded as soon as
+// this chunk's are consumed (step 1), its q and k after step 2.
 #pragma once
 
 #include <type_traits>
@@ -61,8 +63,10 @@ template <typename TI, int DK, int DVT> struct VdCfg {
     static constexpr int GW = DK / 8;                  // gate channels per wave
     // factor rows: e^{G_m_i} (4), e^{G_end - G_m_j} (4), D_ij (6), e^{G_end} (1)
     static constexpr int NF = 15, FQ = 0, FKT = 4, FD = 8, FEND = 14;
-    static constexpr size_t oG = 0;
-    static constexpr size_t oF = oG + (size_t)C * PG * 4;
+    static constexpr int PSB = H ? C + 8 : C + 4;      // score buffer pitch
+    static constexpr size_t GBYTES = (size_t)C * PG * 4, SBYTES = (size_t)C * PSB * sizeof(TM);
+    static constexpr size_t oG = 0;                    // gates; the scores reuse it in step 3
+    static constexpr size_t oF = oG + (GBYTES > SBYTES ? GBYTES : SBYTES);
     static constexpr size_t oQh = oF + (size_t)NF * DK * 4;
     static constexpr size_t oQe = oQh + (size_t)C * PQ * sizeof(TS);
     static constexpr size_t oKb = oQe + (size_t)C * PQ * sizeof(TM);
@@ -154,7 +158,7 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
     // the [C][DVT/8] grid, and this wave's GW gate channels of row `lane`
     Raw8<TI> rq[NQS], rk[NQS], rv[NVS];
     f32x4 gl[GW / 4];
-    auto load_chunk = [&](int c) __attribute__((always_inline)) {
+    auto load_qk = [&](int c) __attribute__((always_inline)) {
         const int t0 = c * C, nv = min(C, L - t0);
 #pragma unroll
         for (int m = 0; m < NQS; ++m) {
@@ -168,6 +172,9 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
                 rk[m] = zero_raw8<TI>();
             }
         }
+    };
+    auto load_gv = [&](int c) __attribute__((always_inline)) {
+        const int t0 = c * C, nv = min(C, L - t0);
 #pragma unroll
         for (int m = 0; m < NVS; ++m) {
             const int sid = tid + 512 * m, row = sid / SEGV, cs = sid % SEGV;
@@ -179,7 +186,10 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
             gl[u] = lane < nv ? *reinterpret_cast<const f32x4 *>(lgg + (size_t)(t0 + lane) * DK + 4 * u)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
     };
-    if (nchunks > 0) load_chunk(0);
+    if (nchunks > 0) {
+        load_gv(0);
+        load_qk(0);
+    }
 
     // reference rows of the 15 factors (fr = lane % 16): e^{G[ra] - G[rb]}, rb < 0: none
     const int fr = lane & 15;
@@ -208,14 +218,20 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) gsum[e] = wave_inclusive_sum(gl[u][e]);
             *reinterpret_cast<f32x4 *>(&Gs[lane * PG + wv * GW + 4 * u]) = gsum;
+        }
+        // the wave reads back the rows it just wrote (one wave's LDS operations
+        // complete in order): factor fr of channel (lane >> 4) + 4 it
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float xa = __shfl(gsum[e], ra, 64);
-                const float xb = __shfl(gsum[e], rbf < 0 ? 0 : rbf, 64);
-                const float f = __expf(rbf < 0 ? xa : xa - xb);
-                if (lane < Cfg::NF) F[fr * DK + wv * GW + 4 * u + e] = f;
+        for (int it = 0; it < GW / 4; ++it) {
+            const int ch = wv * GW + (lane >> 4) + 4 * it;
+            if (fr < Cfg::NF) {
+                const float xa = Gs[ra * PG + ch];
+                const float xb = rbf < 0 ? 0.f : Gs[rbf * PG + ch];
+                F[fr * DK + ch] = __expf(xa - xb);
             }
         }
+        if (c + 1 < nchunks) load_gv(c + 1);  // a whole chunk of cover for the gates
         __syncthreads();
 
         // ---- 2. operand rows from this thread's q and k segments
@@ -264,45 +280,27 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
                 st8<TM>(&Kt[row * PK + c0], kt);
             }
         }
-        if (c + 1 < nchunks) load_chunk(c + 1);
+        if (c + 1 < nchunks) load_qk(c + 1);
         __syncthreads();
 
-        // ---- 3. this wave's output tiles and state tiles
-        const TM *Stc = St + (c & 1) * DVT * PQ;
-        TM *Stn = St + ((c + 1) & 1) * DVT * PQ;
-        const int rl_ = rb * 16 + n;  // chunk-local query row of this lane (B operand column)
-        const int jw = hh * (DVT / 2);  // first value column of this wave
-        sfrag qh[NKS];
-        frag qe[NKS];
+        // ---- 3a. the chunk's 10 score tiles D[s][r] (key block sb <= query block
+        // rb), spread over the waves, into the score buffer as A[r][s]; off the
+        // diagonal block the key operand takes the factor D_{rb,sb} of its channels
+        TM *SB = reinterpret_cast<TM *>(smem + Cfg::oG);
+        constexpr int PSB = Cfg::PSB;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            const int col = g * (DK / 4) + ks * E;
-            qh[ks] = ld_frag<TS>(&Qh[rl_ * PQ + col]);
-            qe[ks] = ld_frag<TM>(&Qe[rl_ * PQ + col]);
-        }
-        // inter: D[j][r] = sum_c S[c][j] q_r[c] e^{G_r[c]}
-        f32x4 oacc[NTJW];
-#pragma unroll
-        for (int jt = 0; jt < NTJW; ++jt) {
-            oacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                oacc[jt] = MF::mma(ld_frag<TM>(&Stc[(jw + jt * 16 + n) * PQ + g * (DK / 4) + ks * E]), qe[ks],
-                                   oacc[jt]);
-        }
-        // scores D[s][r] for key blocks sb <= rb; off the diagonal block the key
-        // operand takes the factor D_{rb,sb} of its channels
-        f32x4 sc[NRB];
-#pragma unroll
-        for (int sb = 0; sb < NRB; ++sb) {
-            sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (sb <= rb) {
-                const float *Dr = &F[(Cfg::FD + (sb < rb ? d_row(rb, sb) : 0)) * DK];
+        for (int m = 0; m < 2; ++m) {
+            const int tix = wv + 8 * m;
+            if (tix < NRB * (NRB + 1) / 2) {
+                const int trb = tix < 1 ? 0 : tix < 3 ? 1 : tix < 6 ? 2 : 3;
+                const int tsb = tix - trb * (trb + 1) / 2;
+                const float *Dr = &F[(Cfg::FD + (tsb < trb ? d_row(trb, tsb) : 0)) * DK];
+                f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     const int col = g * (DK / 4) + ks * E;
-                    sfrag kf = ld_frag<TS>(&Kb[(sb * 16 + n) * PQ + col]);
-                    if (sb < rb) {
+                    sfrag kf = ld_frag<TS>(&Kb[(tsb * 16 + n) * PQ + col]);
+                    if (tsb < trb) {
                         if constexpr (E == 8) {
                             const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&Dr[col]);
                             const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&Dr[col + 4]);
@@ -315,28 +313,54 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
                             kf = kf * Dr[col];
                         }
                     }
-                    sc[sb] = MS::mma(kf, qh[ks], sc[sb]);
+                    sc = MS::mma(kf, ld_frag<TS>(&Qh[(trb * 16 + n) * PQ + col]), sc);
                 }
-                if (sb == rb) {  // causal mask; the diagonal itself is exact
-                    const float qk = QK[rl_];
+                if (tsb == trb) {  // causal mask; the diagonal itself is exact
+                    const float qk = QK[trb * 16 + n];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        if (4 * g + e > n) sc[sb][e] = 0.f;
-                        if (4 * g + e == n) sc[sb][e] = qk;
+                        if (4 * g + e > n) sc[e] = 0.f;
+                        if (4 * g + e == n) sc[e] = qk;
                     }
                 }
+                st4<TM>(&SB[(trb * 16 + n) * PSB + tsb * 16 + 4 * g], sc);
             }
         }
-        // intra: D[j][r] += sum_s V[s][j] A[r][s]
+        __syncthreads();
+
+        // ---- 3b. this wave's output tiles (query block rb, half hh of the slice)
+        const TM *Stc = St + (c & 1) * DVT * PQ;
+        TM *Stn = St + ((c + 1) & 1) * DVT * PQ;
+        const int rl_ = rb * 16 + n;    // chunk-local query row of this lane (B operand column)
+        const int jw = hh * (DVT / 2);  // first value column of this wave
+        frag qe[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qe[ks] = ld_frag<TM>(&Qe[rl_ * PQ + g * (DK / 4) + ks * E]);
+        // inter: D[j][r] = sum_c S[c][j] q_r[c] e^{G_r[c]}
+        f32x4 oacc[NTJW];
+#pragma unroll
+        for (int jt = 0; jt < NTJW; ++jt) {
+            oacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                oacc[jt] = MF::mma(ld_frag<TM>(&Stc[(jw + jt * 16 + n) * PQ + g * (DK / 4) + ks * E]), qe[ks],
+                                   oacc[jt]);
+        }
+        // intra: D[j][r] += sum_s V[s][j] A[r][s], the scores read back with the
+        // token slots of the V^T operand: s = 32p + 4g + (0..3), 32p + 16 + 4g + (0..3)
         if constexpr (H) {
 #pragma unroll
             for (int p = 0; p < NRB / 2; ++p) {
                 if (2 * p <= rb) {
                     frag bop;
+                    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+                    const h4 lo = *reinterpret_cast<const h4 *>(&SB[rl_ * PSB + 32 * p + 4 * g]);
+                    h4 hi = {0, 0, 0, 0};
+                    if (2 * p + 1 <= rb) hi = *reinterpret_cast<const h4 *>(&SB[rl_ * PSB + 32 * p + 16 + 4 * g]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        bop[e] = from_f32<TM>(sc[2 * p][e]);
-                        bop[4 + e] = from_f32<TM>(sc[2 * p + 1][e]);
+                        bop[e] = lo[e];
+                        bop[4 + e] = hi[e];
                     }
 #pragma unroll
                     for (int jt = 0; jt < NTJW; ++jt)
@@ -348,11 +372,12 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
             for (int sb = 0; sb < NRB; ++sb) {
                 if (sb <= rb) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
+                    for (int e = 0; e < 4; ++e) {
+                        const float a_ = SB[rl_ * PSB + sb * 16 + 4 * g + e];
 #pragma unroll
                         for (int jt = 0; jt < NTJW; ++jt)
-                            oacc[jt] = MF::mma(Vs[(sb * 16 + 4 * g + e) * PV + jw + jt * 16 + n], sc[sb][e],
-                                               oacc[jt]);
+                            oacc[jt] = MF::mma(Vs[(sb * 16 + 4 * g + e) * PV + jw + jt * 16 + n], a_, oacc[jt]);
+                    }
                 }
             }
         }
