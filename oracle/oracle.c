@@ -251,3 +251,117 @@ int oracle_short_conv(const double *x, const double *w, const double *state_in, 
     }
     return status;
 }
+
+/*
+ * Backward pass: gradients of a scalar loss through the forward recurrence,
+ * given do = dLoss/do_t for every token and (optionally) d_state_out =
+ * dLoss/dS_L for the final state. Reverse-mode differentiation of the per-token
+ * update, written out step by step (the forward states are kept):
+ *   S_t = g_t S_{t-1} + k_t v_t^T,  o_t = S_t^T q_t     (g_t = exp(l_t); PLAIN: 1;
+ *                                                        VECTOR_DECAY: Diag(exp(l_t)))
+ * Walking t = L .. 1 with dS the gradient of the state after step t:
+ *   dS   += q_t do_t^T          (o_t reads S_t)
+ *   dq_t  = S_t do_t
+ *   dk_t  = dS v_t,   dv_t = dS^T k_t
+ *   dl_t  = g_t <dS, S_{t-1}>   (VECTOR_DECAY: per key channel, row by row)
+ *   dS    = g_t dS              (gradient of the state before step t)
+ * and d_state_in = dS at the end. Variants: PLAIN, DECAY, VECTOR_DECAY.
+ * Layouts as in oracle_forward; do like o, d_state_out like state_out;
+ * dq, dk like q; dv like v; d_log_gate like log_gate (may be NULL for PLAIN);
+ * d_state_in like state_in (NULL = not returned). The recurrence is the one of
+ * tensorplay section 2.1 (with the decay of wln20's data-dependent equation and
+ * the per-channel gate of tensorplay section 5.1); the derivative rules are
+ * those of the products above.
+ */
+static int bwd_head(int variant, const double *q, const double *k, const double *v,
+                    const double *lg, const double *s_in, const double *dout, const double *ds_out,
+                    double *dq, double *dk, double *dv, double *dlg, double *ds_in, long L, long dk_,
+                    long dv_)
+{
+    const long D = dk_ * dv_;
+    double *S = (double *)malloc(sizeof(double) * (size_t)((L + 1) * D));
+    double *dS = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!S || !dS) {
+        free(S); free(dS);
+        return OR_NO_MEM;
+    }
+    for (long i = 0; i < D; ++i) S[i] = s_in ? s_in[i] : 0.0;
+    for (long t = 0; t < L; ++t) {
+        const double *Sp = S + t * D;
+        double *Sn = S + (t + 1) * D;
+        for (long i = 0; i < dk_; ++i) {
+            double g = 1.0;
+            if (variant == OR_DECAY) g = exp(lg[t]);
+            if (variant == OR_VECTOR_DECAY) g = exp(lg[t * dk_ + i]);
+            for (long j = 0; j < dv_; ++j)
+                Sn[i * dv_ + j] = g * Sp[i * dv_ + j] + k[t * dk_ + i] * v[t * dv_ + j];
+        }
+    }
+    for (long i = 0; i < D; ++i) dS[i] = ds_out ? ds_out[i] : 0.0;
+    for (long t = L - 1; t >= 0; --t) {
+        const double *qt = q + t * dk_, *kt = k + t * dk_, *vt = v + t * dv_, *dot = dout + t * dv_;
+        const double *Sa = S + (t + 1) * D, *Sb = S + t * D;
+        for (long i = 0; i < dk_; ++i)
+            for (long j = 0; j < dv_; ++j) dS[i * dv_ + j] += qt[i] * dot[j];
+        for (long i = 0; i < dk_; ++i) {
+            double acc = 0.0;
+            for (long j = 0; j < dv_; ++j) acc += Sa[i * dv_ + j] * dot[j];
+            dq[t * dk_ + i] = acc;
+        }
+        for (long i = 0; i < dk_; ++i) {
+            double acc = 0.0;
+            for (long j = 0; j < dv_; ++j) acc += dS[i * dv_ + j] * vt[j];
+            dk[t * dk_ + i] = acc;
+        }
+        for (long j = 0; j < dv_; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < dk_; ++i) acc += dS[i * dv_ + j] * kt[i];
+            dv[t * dv_ + j] = acc;
+        }
+        if (variant == OR_DECAY) {
+            const double g = exp(lg[t]);
+            double acc = 0.0;
+            for (long i = 0; i < D; ++i) acc += dS[i] * Sb[i];
+            if (dlg) dlg[t] = g * acc;
+            for (long i = 0; i < D; ++i) dS[i] *= g;
+        } else if (variant == OR_VECTOR_DECAY) {
+            for (long i = 0; i < dk_; ++i) {
+                const double g = exp(lg[t * dk_ + i]);
+                double acc = 0.0;
+                for (long j = 0; j < dv_; ++j) acc += dS[i * dv_ + j] * Sb[i * dv_ + j];
+                if (dlg) dlg[t * dk_ + i] = g * acc;
+                for (long j = 0; j < dv_; ++j) dS[i * dv_ + j] *= g;
+            }
+        }
+    }
+    if (ds_in) memcpy(ds_in, dS, sizeof(double) * (size_t)D);
+    free(S); free(dS);
+    return OR_OK;
+}
+
+int oracle_backward(int variant, const double *q, const double *k, const double *v,
+                    const double *log_gate, const double *state_in, const double *dout,
+                    const double *d_state_out, double *dq, double *dk, double *dv,
+                    double *d_log_gate, double *d_state_in, long BH, long L, long dk_, long dv_,
+                    int nthreads)
+{
+    if (variant != OR_PLAIN && variant != OR_DECAY && variant != OR_VECTOR_DECAY) return OR_BAD_ARG;
+    if (BH < 0 || L < 0 || dk_ <= 0 || dv_ <= 0) return OR_BAD_ARG;
+    if (BH > 0 && L > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv)) return OR_BAD_ARG;
+    if (variant != OR_PLAIN && L > 0 && !log_gate) return OR_BAD_ARG;
+    const long gstride = variant == OR_VECTOR_DECAY ? L * dk_ : L;
+    int status = OR_OK;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) reduction(max : status)
+#endif
+    for (long h = 0; h < BH; ++h) {
+        int st = bwd_head(variant, q + h * L * dk_, k + h * L * dk_, v + h * L * dv_,
+                          log_gate ? log_gate + h * gstride : NULL,
+                          state_in ? state_in + h * dk_ * dv_ : NULL, dout + h * L * dv_,
+                          d_state_out ? d_state_out + h * dk_ * dv_ : NULL, dq + h * L * dk_,
+                          dk + h * L * dk_, dv + h * L * dv_, d_log_gate ? d_log_gate + h * gstride : NULL,
+                          d_state_in ? d_state_in + h * dk_ * dv_ : NULL, L, dk_, dv_);
+        if (st > status) status = st;
+    }
+    return status;
+}

@@ -704,6 +704,86 @@ def pin_conv_chunked_carry(lib):
         assert np.array_equal(st, s), cuts
 
 
+# ---------------------------------------------------------------------------
+# Backward pass (gradients through the recurrence)
+# ---------------------------------------------------------------------------
+def _bwd_case(r, variant, B=2, L=9, dk=4, dv=3):
+    q, k = r.standard_normal((B, L, dk)), r.standard_normal((B, L, dk))
+    v, do = r.standard_normal((B, L, dv)), r.standard_normal((B, L, dv))
+    lg = None
+    if variant == "decay":
+        lg = -0.6 * r.random((B, L))
+    elif variant == "vector_decay":
+        lg = -0.6 * r.random((B, L, dk))
+    s0 = r.standard_normal((B, dk, dv))
+    dso = r.standard_normal((B, dk, dv))
+    return q, k, v, do, lg, s0, dso
+
+
+def pin_backward_finite_differences(lib):
+    """Every gradient matches the central difference of the forward oracle's loss
+    <do, O> + <dS_L, S_L> along a random direction (fp64, step 1e-6)."""
+    r = _rng(50)
+    for variant in ("plain", "decay", "vector_decay"):
+        q, k, v, do, lg, s0, dso = _bwd_case(r, variant)
+
+        def loss(q_, k_, v_, lg_, s0_):
+            o, s, _ = oracle.forward(variant, q_, k_, v_, log_gate=lg_, state_in=s0_, lib=lib)
+            return float((o * do).sum() + (s * dso).sum())
+
+        dq, dk, dv, dlg, dsi = oracle.backward(variant, q, k, v, do, lg, s0, dso, lib=lib)
+        eps = 1e-6
+        args = [q, k, v, lg, s0]
+        grads = [dq, dk, dv, dlg, dsi]
+        for ai, (x, gx) in enumerate(zip(args, grads)):
+            if x is None:
+                continue
+            u = r.standard_normal(x.shape)
+            plus, minus = list(args), list(args)
+            plus[ai], minus[ai] = x + eps * u, x - eps * u
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            an = float((gx * u).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (variant, ai, fd, an)
+
+
+def pin_backward_plain_closed_form(lib):
+    """PLAIN with an initial state: O = (Q K^T (.) M) V + Q S_0 and S_L = S_0 + K^T V
+    give dQ = (dO V^T (.) M) K + dO S_0^T, dK = (dO V^T (.) M)^T Q + V dS_L^T,
+    dV = (Q K^T (.) M)^T dO + K dS_L and dS_0 = Q^T dO + dS_L (matrix calculus of the
+    parallel form, tensorplay section 2.1)."""
+    r = _rng(51)
+    q, k, v, do, _, s0, dso = _bwd_case(r, "plain", B=2, L=23, dk=5, dv=4)
+    dq, dk, dv, _, dsi = oracle.backward("plain", q, k, v, do, None, s0, dso, lib=lib)
+    M = _mask(23)
+    P = (do @ v.transpose(0, 2, 1)) * M
+    A = (q @ k.transpose(0, 2, 1)) * M
+    assert _rel(dq, P @ k + do @ s0.transpose(0, 2, 1)) <= 1e-12
+    assert _rel(dk, P.transpose(0, 2, 1) @ q + v @ dso.transpose(0, 2, 1)) <= 1e-12
+    assert _rel(dv, A.transpose(0, 2, 1) @ do + k @ dso) <= 1e-12
+    assert _rel(dsi, q.transpose(0, 2, 1) @ do + dso) <= 1e-12
+
+
+def pin_backward_gate_identity(lib):
+    """The output and final state depend on the cumulative log-gates G only through
+    differences G_r - G_s (and G_L for the final state), so
+    dl_t = sum_{u >= t} (q_u . dq_u - k_u . dk_u) + <dS_L, S_L>, summed over the key
+    channel for the scalar gate and per channel for the vector gate."""
+    r = _rng(52)
+    for variant in ("decay", "vector_decay"):
+        q, k, v, do, lg, s0, dso = _bwd_case(r, variant, L=17)
+        dq, dk, dv, dlg, _ = oracle.backward(variant, q, k, v, do, lg, s0, dso, lib=lib)
+        _, sL, _ = oracle.forward(variant, q, k, v, log_gate=lg, state_in=s0, lib=lib)
+        per = q * dq - k * dk                              # [B, L, dk]
+        tail = (dso * sL).sum(-1)                          # [B, dk]
+        if variant == "decay":
+            per = per.sum(-1)
+            tail = tail.sum(-1)[:, None]
+        else:
+            tail = tail[:, None, :]
+        ref = np.flip(np.cumsum(np.flip(per, 1), 1), 1) + tail
+        assert _rel(dlg, ref) <= 1e-12, (variant, _rel(dlg, ref))
+
+
 ALL_PINS = [
     pin_plain_quadratic, pin_plain_fraction_bruteforce, pin_plain_final_state,
     pin_normalized_quadratic, pin_normalized_constant_v, pin_normalized_hull,
@@ -717,4 +797,5 @@ ALL_PINS = [
     pin_conv_chunked_carry,
     pin_vector_decay_parallel_form, pin_vector_decay_uniform_is_scalar, pin_vector_decay_fraction,
     pin_vector_decay_channel_isolation, pin_vector_decay_resume_and_decode,
+    pin_backward_finite_differences, pin_backward_plain_closed_form, pin_backward_gate_identity,
 ]

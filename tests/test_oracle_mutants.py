@@ -13,9 +13,9 @@ from oracle import build as obuild
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 MUTANTS = {
-    "decay_dropped": ("double g = exp(lg[t]);", "double g = 1.0;"),
-    "decay_gate_off_by_one": ("double g = exp(lg[t]);",
-                              "double g = exp(lg[t > 0 ? t - 1 : 0]);"),
+    "decay_dropped": ("            double g = exp(lg[t]);\n", "            double g = 1.0;\n"),
+    "decay_gate_off_by_one": ("            double g = exp(lg[t]);\n",
+                              "            double g = exp(lg[t > 0 ? t - 1 : 0]);\n"),
     "gdn_sign": ("a * (S[i * dv + j] - b * kt[i] * r[j])", "a * (S[i * dv + j] + b * kt[i] * r[j])"),
     "gdn_beta_dropped_on_write": ("+ b * kt[i] * vt[j];", "+ kt[i] * vt[j];"),
     "gdn_alpha_on_write": ("a * (S[i * dv + j] - b * kt[i] * r[j]) + b * kt[i] * vt[j];",
@@ -25,7 +25,8 @@ MUTANTS = {
     "normalizer_wrong_operand": ("for (long i = 0; i < dk; ++i) z[i] += kt[i];",
                                  "for (long i = 0; i < dk; ++i) z[i] += qt[i];"),
     "normalizer_dropped": ("for (long j = 0; j < dv; ++j) ot[j] /= den;", "(void)den;"),
-    "state_in_ignored": ("S[i] = s_in ? s_in[i] : 0.0;", "S[i] = 0.0;"),
+    "state_in_ignored": ("for (long i = 0; i < dk * dv; ++i) S[i] = s_in ? s_in[i] : 0.0;",
+                         "for (long i = 0; i < dk * dv; ++i) S[i] = 0.0;"),
     "plain_transposed_write": ("S[i * dv + j] += kt[i] * vt[j];", "S[i * dv + j] += kt[j % dk] * vt[i % dv];"),
     "readout_uses_key": ("acc += S[i * dv + j] * qt[i];\n            ot[j] = acc;",
                          "acc += S[i * dv + j] * kt[i];\n            ot[j] = acc;"),
@@ -33,6 +34,12 @@ MUTANTS = {
                                      "double g = exp(lg[t * dk + (dk - 1 - i)]);"),
     "vector_gate_one_token_late": ("double g = exp(lg[t * dk + i]);",
                                    "double g = exp(lg[(t > 0 ? t - 1 : 0) * dk + i]);"),
+    "bwd_dq_reads_old_state": ("for (long j = 0; j < dv_; ++j) acc += Sa[i * dv_ + j] * dot[j];",
+                               "for (long j = 0; j < dv_; ++j) acc += Sb[i * dv_ + j] * dot[j];"),
+    "bwd_state_grad_not_decayed": ("for (long i = 0; i < D; ++i) dS[i] *= g;", "(void)g;"),
+    "bwd_gate_grad_without_gate": ("if (dlg) dlg[t] = g * acc;", "if (dlg) dlg[t] = acc;"),
+    "bwd_dv_transposed": ("for (long i = 0; i < dk_; ++i) acc += dS[i * dv_ + j] * kt[i];",
+                          "for (long i = 0; i < dk_; ++i) acc += dS[(i % dv_) * dv_ + (j % dk_)] * kt[i];"),
     "conv_taps_reversed": ("acc += w[(h * d + c) * K + tau] * hist[(W + t - tau) * d + c];",
                            "acc += w[(h * d + c) * K + (K - 1 - tau)] * hist[(W + t - tau) * d + c];"),
     "conv_head_weights_shared": ("acc += w[(h * d + c) * K + tau]", "acc += w[c * K + tau]"),
