@@ -22,8 +22,8 @@ HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "linattn.h")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 VARIANTS = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3, "vector_decay": 4}
-EXPORTS = ("la_chunk_fwd_workspace_size", "la_chunk_fwd", "la_decode_step", "la_short_conv",
-           "la_status_str", "la_abi_version")
+EXPORTS = ("la_chunk_fwd_workspace_size", "la_chunk_fwd", "la_chunk_bwd_workspace_size",
+           "la_chunk_bwd", "la_decode_step", "la_short_conv", "la_status_str", "la_abi_version")
 
 _lib = None
 
@@ -54,6 +54,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                  i, i, i, i, i, i, vp, sz, vp]
     lib.la_decode_step.restype = i
     lib.la_decode_step.argtypes = [i, i, i, vp, vp, vp, fp, fp, fp, vp, i, i, i, i, vp]
+    lib.la_chunk_bwd_workspace_size.restype = i
+    lib.la_chunk_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.la_chunk_bwd.restype = i
+    lib.la_chunk_bwd.argtypes = [i, i, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp, fp, fp,
+                                 i, i, i, i, i, i, vp, sz, vp]
     lib.la_short_conv.restype = i
     lib.la_short_conv.argtypes = [i, vp, vp, vp, fp, fp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   i, i, i, i, i, i, vp]
@@ -163,6 +168,50 @@ def la_decode_step(variant: str, q, k, v, log_gate, state, *, o=None, out_dtype=
     return o
 
 
+def la_chunk_bwd_workspace_size(variant: str, dtype_code: int, B: int, H: int, L: int,
+                                d_k: int, d_v: int, C: int = 64) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().la_chunk_bwd_workspace_size(VARIANTS[variant], dtype_code, B, H, L, d_k,
+                                                    d_v, C, ctypes.byref(out))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_chunk_bwd_workspace_size")
+    return out.value
+
+
+def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_state_out=None, *,
+                 C: int = 64, want_d_log_gate: bool = True, want_d_state_in: bool = False,
+                 workspace=None, stream=None) -> Tuple:
+    """Backward pass of la_chunk_fwd ("plain" or "decay").
+
+    q, k: [B, H, L, d_k]; v, d_o: [B, H, L, d_v] (bf16 or fp32, one dtype);
+    log_gate: [B, H, L] fp32 ("decay"); state_in, d_state_out: [B, H, d_k, d_v] fp32.
+    Returns (dq, dk, dv, d_log_gate or None, d_state_in or None), all fp32.
+    """
+    import torch
+    lib = load_library()
+    B, H, L, d_k = q.shape
+    d_v = v.shape[-1]
+    dt = _dt(q)
+    dev_ = q.device
+    dq = torch.empty((B, H, L, d_k), dtype=torch.float32, device=dev_)
+    dk = torch.empty((B, H, L, d_k), dtype=torch.float32, device=dev_)
+    dv = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev_)
+    dlg = (torch.empty((B, H, L), dtype=torch.float32, device=dev_)
+           if (variant == "decay" and want_d_log_gate) else None)
+    dsi = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev_) if want_d_state_in else None
+    if workspace is None:
+        ws_bytes = la_chunk_bwd_workspace_size(variant, dt, B, H, L, d_k, d_v, C)
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev_)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.la_chunk_bwd(VARIANTS[variant], dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
+                          _ptr(state_in), _ptr(d_o), _ptr(d_state_out), _ptr(dq), _ptr(dk), _ptr(dv),
+                          _ptr(dlg), _ptr(dsi), B, H, L, d_k, d_v, C, _ptr(workspace), ws_bytes,
+                          _stream(dev_, stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_chunk_bwd")
+    return dq, dk, dv, dlg, dsi
+
+
 def la_short_conv(q=None, k=None, v=None, w_q=None, w_k=None, w_v=None, *, q_state_in=None,
                   k_state_in=None, v_state_in=None, q_out=None, k_out=None, v_out=None,
                   q_state_out=None, k_state_out=None, v_state_out=None, want_state: bool = False,
@@ -207,5 +256,6 @@ def la_short_conv(q=None, k=None, v=None, w_q=None, w_k=None, w_v=None, *, q_sta
     return (*outs, *souts)
 
 
-__all__ = ["la_chunk_fwd", "la_chunk_fwd_workspace_size", "la_decode_step", "la_short_conv",
+__all__ = ["la_chunk_fwd", "la_chunk_fwd_workspace_size", "la_chunk_bwd", "la_chunk_bwd_workspace_size",
+           "la_decode_step", "la_short_conv",
            "la_status_str", "la_abi_version", "LinAttnError", "VARIANTS", "load_library"]

@@ -197,6 +197,65 @@ hipError_t dispatch_short_conv(int K, const ConvArgs &a, unsigned blocks, hipStr
     return hipErrorInvalidValue;
 }
 
+// ---- backward pass
+// fp32 inputs keep fp32 operand tiles in LDS; the chunk kernel then fits 160 KB
+// only for d_k * d_v <= 4096 or the (32, 128) / (128, 32) shapes.
+constexpr int kBwdF32MaxState = 4096;
+bool bwd_f32_fits(int d_k, int d_v) { return d_k * d_v <= kBwdF32MaxState || d_k + d_v == 160; }
+
+la_status check_bwd_shape(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v, int C) {
+    if (var < LA_PLAIN || var > LA_VECTOR_DECAY) return LA_ERR_INVALID_ARG;
+    if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || L < 0) return LA_ERR_INVALID_ARG;
+    if (var != LA_PLAIN && var != LA_DECAY) return LA_ERR_UNSUPPORTED;
+    if (C != 64) return LA_ERR_UNSUPPORTED;
+    if ((d_k != 32 && d_k != 64 && d_k != 128) || (d_v != 32 && d_v != 64 && d_v != 128))
+        return LA_ERR_UNSUPPORTED;
+    if (dt == LA_F32 && !bwd_f32_fits(d_k, d_v)) return LA_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H, nch = (L + C - 1) / C;
+    if (BH * nch > INT32_MAX || BH * 2 > INT32_MAX) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
+struct BwdLayout {
+    size_t hs, dhs, s_last, rterm, total;
+};
+BwdLayout bwd_layout(la_dtype dt, int64_t BH, int L, int d_k, int d_v) {
+    const int64_t nch = (L + 63) / 64;
+    BwdLayout w{};
+    const size_t st = (size_t)BH * nch * d_k * d_v * elem_size(dt);
+    w.hs = 0;
+    w.dhs = round_up(st, 256);
+    w.s_last = w.dhs + round_up(st, 256);
+    w.rterm = w.s_last + round_up((size_t)BH * d_k * d_v * 4, 256);
+    w.total = w.rterm + round_up((size_t)BH * L * 4, 256);
+    return w;
+}
+
+template <typename TI, bool DECAY>
+hipError_t dispatch_bwd(int d_k, int d_v, const BwdArgs &a, hipStream_t st) {
+#define LA_BWD_DV(DK)                                                            \
+    switch (d_v) {                                                               \
+        case 32: return launch_bwd<TI, DK, 32, DECAY>(a, st);                    \
+        case 64:                                                                 \
+            if constexpr (sizeof(TI) == 2 || DK * 64 <= kBwdF32MaxState)         \
+                return launch_bwd<TI, DK, 64, DECAY>(a, st);                     \
+            break;                                                               \
+        case 128:                                                                \
+            if constexpr (sizeof(TI) == 2 || DK * 128 <= kBwdF32MaxState)        \
+                return launch_bwd<TI, DK, 128, DECAY>(a, st);                    \
+            break;                                                               \
+    }                                                                            \
+    break;
+    switch (d_k) {
+        case 32: LA_BWD_DV(32)
+        case 64: LA_BWD_DV(64)
+        case 128: LA_BWD_DV(128)
+    }
+#undef LA_BWD_DV
+    return hipErrorInvalidValue;
+}
+
 // Supported (input, output) dtype pairs: bf16 -> fp32, bf16 -> bf16, fp32 -> fp32.
 bool dtype_pair_ok(la_dtype dt, la_dtype o_dt) {
     return (dt == LA_BF16 && (o_dt == LA_F32 || o_dt == LA_BF16)) || (dt == LA_F32 && o_dt == LA_F32);
@@ -456,6 +515,68 @@ la_status la_short_conv(la_dtype dt, const void *q, const void *k, const void *v
     a.BH = (int)BH; a.H = H; a.L = L; a.NT = (int)NT;
     const hipError_t e = dt == LA_BF16 ? dispatch_short_conv<bf16>(K, a, (unsigned)total, st)
                                        : dispatch_short_conv<float>(K, a, (unsigned)total, st);
+    return from_hip(e);
+}
+
+la_status la_chunk_bwd_workspace_size(la_variant var, la_dtype dt, int B, int H, int L, int d_k,
+                                      int d_v, int C, size_t *bytes) {
+    const la_status s = check_bwd_shape(var, dt, B, H, L, d_k, d_v, C);
+    if (s != LA_OK) return s;
+    if (!bytes) return LA_ERR_INVALID_ARG;
+    *bytes = bwd_layout(dt, (int64_t)B * H, L, d_k, d_v).total;
+    return LA_OK;
+}
+
+la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k, const void *v,
+                       const float *log_gate, const float *state_in, const void *d_o,
+                       const float *d_state_out, float *dq, float *dk, float *dv, float *d_log_gate,
+                       float *d_state_in, int B, int H, int L, int d_k, int d_v, int C,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    la_status s = check_bwd_shape(var, dt, B, H, L, d_k, d_v, C);
+    if (s != LA_OK) return s;
+    const bool tok = L > 0;
+    if (tok && (!q || !k || !v || !d_o || !dq || !dk || !dv)) return LA_ERR_INVALID_ARG;
+    if (var == LA_DECAY && tok && !log_gate) return LA_ERR_INVALID_ARG;
+    if (var == LA_PLAIN && (log_gate || d_log_gate)) return LA_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, k, v, log_gate, state_in, d_o, d_state_out, dq, dk, dv, d_log_gate, d_state_in};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
+    const int64_t BH = (int64_t)B * H;
+    const size_t es = elem_size(dt);
+    const size_t qk_b = (size_t)BH * L * d_k * es, v_b = (size_t)BH * L * d_v * es;
+    const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4;
+    const BwdLayout lay = bwd_layout(dt, BH, L, d_k, d_v);
+    if (!workspace || workspace_bytes < lay.total) return LA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
+    const Span ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {log_gate, g_b}, {state_in, s_b}, {d_o, v_b},
+                        {d_state_out, s_b}};
+    const Span outs[] = {{dq, (size_t)BH * L * d_k * 4}, {dk, (size_t)BH * L * d_k * 4},
+                         {dv, (size_t)BH * L * d_v * 4}, {d_log_gate, g_b}, {d_state_in, s_b},
+                         {workspace, lay.total}};
+    for (size_t o = 0; o < sizeof(outs) / sizeof(outs[0]); ++o) {
+        for (const Span &in : ins)
+            if (overlap(outs[o], in)) return LA_ERR_INVALID_ARG;
+        for (size_t o2 = o + 1; o2 < sizeof(outs) / sizeof(outs[0]); ++o2)
+            if (overlap(outs[o], outs[o2])) return LA_ERR_INVALID_ARG;
+    }
+
+    s = check_device();
+    if (s != LA_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.dout = d_o; a.lg = log_gate;
+    a.s_in = state_in; a.ds_out = d_state_out;
+    a.gq = dq; a.gk = dk; a.gv = dv; a.glg = d_log_gate; a.gs_in = d_state_in;
+    a.hs = ws + lay.hs; a.dhs = ws + lay.dhs;
+    a.s_last = reinterpret_cast<float *>(ws + lay.s_last);
+    a.rterm = reinterpret_cast<float *>(ws + lay.rterm);
+    a.BH = (int)BH; a.L = L; a.dv = d_v; a.nsplit = 1;
+    hipError_t e;
+    if (dt == LA_BF16)
+        e = var == LA_DECAY ? dispatch_bwd<bf16, true>(d_k, d_v, a, st) : dispatch_bwd<bf16, false>(d_k, d_v, a, st);
+    else
+        e = var == LA_DECAY ? dispatch_bwd<float, true>(d_k, d_v, a, st) : dispatch_bwd<float, false>(d_k, d_v, a, st);
     return from_hip(e);
 }
 

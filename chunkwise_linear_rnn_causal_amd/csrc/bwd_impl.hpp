@@ -1,0 +1,524 @@
+// bwd_impl.hpp -- backward pass of the chunkwise forward (gfx950): gradients of
+// a loss with respect to q, k, v, the log-gates and the initial state, given
+// the output gradient dO and optionally the final-state gradient.
+//
+// Reverse-mode of S_t = g_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t (tensorplay
+// "Talk Linear Attention", section 2.1; the decay of wln20 "LLM注意力优化：线性注意力",
+// data-dependent decay equation), in the chunk form of tensorplay section 3.2.
+// For chunk c with chunk-local cumulative log-gate G_r, a_r = e^{G_r}, the
+// state H_c at its start and dH_c = dLoss/d(state at its end):
+//   dq_r = a_r H_c do_r + sum_{s<=r} e^{G_r - G_s} (do_r . v_s) k_s
+//   dk_s = sum_{r>=s} e^{G_r - G_s} (do_r . v_s) q_r + e^{G_end - G_s} dH_c v_s
+//   dv_s = sum_{r>=s} e^{G_r - G_s} (q_r . k_s) do_r + e^{G_end - G_s} dH_c^T k_s
+//   dH_{c-1} = e^{G_end} dH_c + sum_r a_r q_r do_r^T
+// and, since the loss sees the cumulative gates only through differences,
+//   dl_t = sum_{u>=t} (q_u . dq_u - k_u . dk_u) + <dS_L, S_L>.
+//
+// Kernels:
+//   state_scan_kernel<FWD>  one workgroup per (head, value slice) walks the chunks
+//       forward, storing each H_c (operand type) and the final state S_L; with
+//       FWD = false it walks them backward with (q (.) a, dO) in place of
+//       (k (.) e^{G_end - G}, v), storing each dH_c and returning dS_0.
+//   bwd_dqkv_kernel  one workgroup (4 waves) per (head, chunk), fully parallel:
+//       wave w owns query block w (dq) and key block w (dk, dv). Products are
+//       taken transposed (dQ^T = K^T dP^T, ...) so that the 16 x 16 score-like
+//       tiles dP = dO V^T, A = Q K^T leave the MFMA in exactly the B-operand
+//       layout of the next product, as in the forward kernel. It also writes
+//       q_t . dq_t - k_t . dk_t per token.
+//   dgate_kernel  one workgroup per head: reverse prefix sum of those terms plus
+//       <dS_L, S_L>.
+#pragma once
+
+#include <type_traits>
+
+#include "la_common.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+
+// ---------------------------------------------------------------------------
+// state scan: S <- e^{G_end} S + sum_s f_s X_s^T Y_s over chunks, forward
+// (X = k, Y = v, f_s = e^{G_end - G_s}) or backward (X = q, Y = dO, f_s = e^{G_s})
+template <typename TI, int DK, int DVT, bool FWD, bool DECAY>
+__global__ void __launch_bounds__(256) state_scan_kernel(BwdArgs a) {
+    using TM = typename OpOf<TI>::type;
+    using MF = Mfma<TM>;
+    using frag = typename MF::frag;
+    constexpr int C = 64, E = MF::E;
+    constexpr bool H = E == 8;
+    constexpr int PX = H ? DK + 16 : DK + 4, PY = H ? DVT + 16 : DVT + 4;
+    constexpr int NTI = DK / 16, NTJ = DVT / 16, NTILE = NTI * NTJ, TPW = (NTILE + 3) / 4;
+    constexpr int NTK = C / (4 * E);
+    constexpr int SEGX = DK / 8, SEGY = DVT / 8;
+    __shared__ __align__(16) TM Xs[C * PX];
+    __shared__ __align__(16) TM Ys[C * PY];
+    __shared__ float Gt[C];
+    __shared__ float Gend;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
+    const int bh = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
+    const int L = a.L, dv = a.dv, j0 = split * DVT, nchunks = (L + C - 1) / C;
+    const TI *xg = (const TI *)(FWD ? a.k : a.q) + (size_t)bh * L * DK;
+    const TI *yg = (const TI *)(FWD ? a.v : a.dout) + (size_t)bh * L * dv + j0;
+    const float *lg = DECAY ? a.lg + (size_t)bh * L : nullptr;
+    TM *hs = (TM *)(FWD ? a.hs : a.dhs) + (size_t)bh * nchunks * DK * dv;
+
+    f32x4 Sacc[TPW];
+    const float *s0 = FWD ? a.s_in : a.ds_out;
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+        Sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int tile = wv + 4 * m;
+        if (tile < NTILE && s0) {
+            const int ti = tile / NTJ, tj = tile % NTJ;
+            const float *sp = s0 + (size_t)bh * DK * dv + (size_t)(ti * 16 + 4 * g) * dv + j0 + tj * 16 + n;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sacc[m][e] = sp[(size_t)e * dv];
+        }
+    }
+
+    for (int it = 0; it < nchunks; ++it) {
+        const int c = FWD ? it : nchunks - 1 - it;
+        const int t0 = c * C, nv = min(C, L - t0);
+        // store the state this chunk starts from (forward) / ends at (backward)
+        TM *hc = hs + (size_t)c * DK * dv;
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int tile = wv + 4 * m;
+            if (tile < NTILE) {
+                const int ti = tile / NTJ, tj = tile % NTJ;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hc[(size_t)(ti * 16 + 4 * g + e) * dv + j0 + tj * 16 + n] = from_f32<TM>(Sacc[m][e]);
+            }
+        }
+        // chunk-local gate prefix (wave 0), then the scaled operands
+        if constexpr (DECAY) {
+            if (wv == 0) {
+                const float G = wave_inclusive_sum(lane < nv ? lg[t0 + lane] : 0.f);
+                Gt[lane] = G;
+                if (lane == 63) Gend = G;
+            }
+        }
+        __syncthreads();
+        const float gend = DECAY ? Gend : 0.f;
+        for (int sid = tid; sid < C * SEGX; sid += 256) {
+            const int row = sid / SEGX, cs = sid % SEGX;
+            float x[8];
+            if (row < nv) {
+                ld8<TI>(xg + (size_t)(t0 + row) * DK + 8 * cs, x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = 0.f;
+            }
+            if constexpr (DECAY) {
+                const float f = FWD ? __expf(gend - Gt[row]) : __expf(Gt[row]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] *= f;
+            }
+            st8<TM>(&Xs[row * PX + 8 * cs], x);
+        }
+        for (int sid = tid; sid < C * SEGY; sid += 256) {
+            const int row = sid / SEGY, cs = sid % SEGY;
+            float y[8];
+            if (row < nv) {
+                ld8<TI>(yg + (size_t)(t0 + row) * dv + 8 * cs, y);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = 0.f;
+            }
+            st8<TM>(&Ys[row * PY + 8 * cs], y);
+        }
+        __syncthreads();
+        const float eg = DECAY ? __expf(gend) : 1.f;
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int tile = wv + 4 * m;
+            if (tile < NTILE) {
+                const int ti = tile / NTJ, tj = tile % NTJ;
+                Sacc[m] *= eg;
+#pragma unroll
+                for (int ks = 0; ks < NTK; ++ks) {
+                    frag xa, yb;
+                    if constexpr (H) {
+                        xa = tr_frag<PX>(Xs, 32 * ks + 4 * g, ti * 16, lane);
+                        yb = tr_frag<PY>(Ys, 32 * ks + 4 * g, tj * 16, lane);
+                    } else {
+                        xa = Xs[(4 * ks + g) * PX + ti * 16 + n];
+                        yb = Ys[(4 * ks + g) * PY + tj * 16 + n];
+                    }
+                    Sacc[m] = MF::mma(xa, yb, Sacc[m]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // forward: the final state S_L; backward: dLoss/dS_0
+    float *out = FWD ? a.s_last : a.gs_in;
+    if (out) {
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int tile = wv + 4 * m;
+            if (tile < NTILE) {
+                const int ti = tile / NTJ, tj = tile % NTJ;
+                float *sp = out + (size_t)bh * DK * dv + (size_t)(ti * 16 + 4 * g) * dv + j0 + tj * 16 + n;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sp[(size_t)e * dv] = Sacc[m][e];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dq, dk, dv of one chunk (C = 64, 4 waves; wave w: query block w and key block w)
+template <typename TI, int DK, int DV, bool DECAY>
+__global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
+    using TM = typename OpOf<TI>::type;
+    using MF = Mfma<TM>;
+    using frag = typename MF::frag;
+    constexpr int C = 64, E = MF::E, NRB = 4;
+    constexpr bool H = E == 8;
+    constexpr int PK = H ? DK + 16 : DK + 4;  // q, k, H, dH tiles (natural and transpose reads)
+    constexpr int PV = H ? DV + 16 : DV + 4;  // v, dO, H, dH (value-side pitch)
+    constexpr int NKS_K = DK / (4 * E), NKS_V = DV / (4 * E);  // k-steps over d_k, d_v
+    constexpr int NCT = DK / 16, NJT = DV / 16;
+    constexpr int SEGK = DK / 8, SEGV = DV / 8;
+    __shared__ __align__(16) TM Qs[C * PK];
+    __shared__ __align__(16) TM Ks[C * PK];
+    __shared__ __align__(16) TM Vs[C * PV];
+    __shared__ __align__(16) TM Os[C * PV];   // dO
+    __shared__ __align__(16) TM Hs[DK * PV];  // H_c   [dk][dv]
+    __shared__ __align__(16) TM Ds[DK * PV];  // dH_c  [dk][dv]
+    __shared__ float Gt[C];
+    __shared__ float Gend;
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
+    const int L = a.L, nchunks = (L + C - 1) / C;
+    const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+    const int t0 = c * C, nv = min(C, L - t0);
+    const TI *qg = (const TI *)a.q + ((size_t)bh * L + t0) * DK;
+    const TI *kg = (const TI *)a.k + ((size_t)bh * L + t0) * DK;
+    const TI *vg = (const TI *)a.v + ((size_t)bh * L + t0) * DV;
+    const TI *og = (const TI *)a.dout + ((size_t)bh * L + t0) * DV;
+    const TM *hg = (const TM *)a.hs + ((size_t)bh * nchunks + c) * DK * DV;
+    const TM *dhg = (const TM *)a.dhs + ((size_t)bh * nchunks + c) * DK * DV;
+
+    // ---- stage the chunk
+    if constexpr (DECAY) {
+        if (wv == 0) {
+            const float G = wave_inclusive_sum(lane < nv ? a.lg[(size_t)bh * L + t0 + lane] : 0.f);
+            Gt[lane] = G;
+            if (lane == 63) Gend = G;
+        }
+    }
+    auto stage = [&](const TI *src, TM *dst, int SEG, int P, int W) __attribute__((always_inline)) {
+        for (int sid = tid; sid < C * SEG; sid += 256) {
+            const int row = sid / SEG, cs = sid % SEG;
+            float x[8];
+            if (row < nv) {
+                ld8<TI>(src + (size_t)row * W + 8 * cs, x);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = 0.f;
+            }
+            st8<TM>(&dst[row * P + 8 * cs], x);
+        }
+    };
+    stage(qg, Qs, SEGK, PK, DK);
+    stage(kg, Ks, SEGK, PK, DK);
+    stage(vg, Vs, SEGV, PV, DV);
+    stage(og, Os, SEGV, PV, DV);
+    for (int sid = tid; sid < DK * SEGV; sid += 256) {
+        const int row = sid / SEGV, cs = sid % SEGV;
+        float x[8], y[8];
+        ld8<TM>(hg + (size_t)row * DV + 8 * cs, x);
+        ld8<TM>(dhg + (size_t)row * DV + 8 * cs, y);
+        st8<TM>(&Hs[row * PV + 8 * cs], x);
+        st8<TM>(&Ds[row * PV + 8 * cs], y);
+    }
+    __syncthreads();
+
+    const int w = wv;
+    const float gend = DECAY ? Gend : 0.f;
+    // natural-layout operand: row `row` of X, k-step ks of a K-dim of width KW
+    auto nat = [&](const TM *X, int P, int row, int ks, int KW) __attribute__((always_inline)) -> frag {
+        return ld_frag<TM>(&X[row * P + g * (KW / 4) + ks * E]);
+    };
+    // natural-layout operand whose K-slots follow the transpose-load pattern:
+    // elements 32 ks + 4g + (0..3) and 32 ks + 16 + 4g + (0..3) of row `row`
+    auto trn = [&](const TM *X, int P, int row, int ks) __attribute__((always_inline)) -> frag {
+        if constexpr (H) {
+            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+            const h4 lo = *reinterpret_cast<const h4 *>(&X[row * P + 32 * ks + 4 * g]);
+            const h4 hi = *reinterpret_cast<const h4 *>(&X[row * P + 32 * ks + 16 + 4 * g]);
+            return frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+            return X[row * P + 4 * ks + g];
+        }
+    };
+    // token-slot operand of a row-major [token][col] tile (col0 + n per lane)
+    auto tok = [&](const TM *X, auto p_tag, int ks, int col0) __attribute__((always_inline)) -> frag {
+        constexpr int P = decltype(p_tag)::value;
+        if constexpr (H) return tr_frag<P>(X, 32 * ks + 4 * g, col0, lane);
+        else return X[(4 * ks + g) * P + col0 + n];
+    };
+    using PKt = std::integral_constant<int, PK>;
+    using PVt = std::integral_constant<int, PV>;
+    // e^{G_r - G_s}
+    auto decay_of = [&](int r, int s) __attribute__((always_inline)) -> float {
+        if constexpr (DECAY) return __expf(Gt[r] - Gt[s]);
+        else return 1.f;
+    };
+
+    float rterm = 0.f;  // q . dq - k . dk of token 16 w + n, accumulated per lane
+
+    // ---- dq for query block w: dQ^T[c][r] = a_r sum_j H[c][j] dO[r][j] + sum_s K[s][c] dP[r][s]
+    {
+        f32x4 acc[NCT];
+        const int r = 16 * w + n;
+        const float ar = DECAY ? __expf(Gt[r]) : 1.f;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS_V; ++ks)
+                acc[ct] = MF::mma(nat(Hs, PV, ct * 16 + n, ks, DV), nat(Os, PV, r, ks, DV), acc[ct]);
+            acc[ct] *= ar;
+        }
+        // dP^T tiles D[s][r] = sum_j V[s][j] dO[r][j] for key blocks sb <= w
+        f32x4 dpt[NRB];
+#pragma unroll
+        for (int sb = 0; sb < NRB; ++sb) {
+            dpt[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (sb <= w) {
+#pragma unroll
+                for (int ks = 0; ks < NKS_V; ++ks)
+                    dpt[sb] = MF::mma(nat(Vs, PV, sb * 16 + n, ks, DV), nat(Os, PV, r, ks, DV), dpt[sb]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = sb * 16 + 4 * g + e;
+                    dpt[sb][e] = (s > r) ? 0.f : dpt[sb][e] * decay_of(r, s);
+                }
+            }
+        }
+        if constexpr (H) {
+#pragma unroll
+            for (int p = 0; p < NRB / 2; ++p) {
+                if (2 * p <= w) {
+                    frag bop;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bop[e] = from_f32<TM>(dpt[2 * p][e]);
+                        bop[4 + e] = from_f32<TM>(dpt[2 * p + 1][e]);
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) acc[ct] = MF::mma(tok(Ks, PKt{}, p, ct * 16), bop, acc[ct]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int sb = 0; sb < NRB; ++sb) {
+                if (sb <= w) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+                            acc[ct] = MF::mma(Ks[(sb * 16 + 4 * g + e) * PK + ct * 16 + n], dpt[sb][e], acc[ct]);
+                }
+            }
+        }
+        // write dq[r][ct*16 + 4g .. +3]; q . dq
+        float *dqg = a.gq + ((size_t)bh * L + t0 + r) * DK;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            if (r < nv) *reinterpret_cast<f32x4 *>(dqg + ct * 16 + 4 * g) = acc[ct];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rterm += acc[ct][e] * to_f32<TM>(Qs[r * PK + ct * 16 + 4 * g + e]);
+        }
+    }
+
+    // ---- dk for key block w: dK^T[c][s] = e^{G_end - G_s} sum_j dH[c][j] V[s][j] + sum_r Q[r][c] dP[r][s]
+    // ---- dv for key block w: dV^T[j][s] = e^{G_end - G_s} sum_c dH[c][j] K[s][c] + sum_r dO[r][j] A[r][s]
+    const int s = 16 * w + n;
+    const float ws = DECAY ? __expf(gend - Gt[s]) : 1.f;
+    {
+        f32x4 acc[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS_V; ++ks)
+                acc[ct] = MF::mma(nat(Ds, PV, ct * 16 + n, ks, DV), nat(Vs, PV, s, ks, DV), acc[ct]);
+            acc[ct] *= ws;
+        }
+        // dP tiles D[r][s] = sum_j dO[r][j] V[s][j] for query blocks rbk >= w
+        f32x4 dp[NRB];
+#pragma unroll
+        for (int rbk = 0; rbk < NRB; ++rbk) {
+            dp[rbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (rbk >= w) {
+#pragma unroll
+                for (int ks = 0; ks < NKS_V; ++ks)
+                    dp[rbk] = MF::mma(nat(Os, PV, rbk * 16 + n, ks, DV), nat(Vs, PV, s, ks, DV), dp[rbk]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = rbk * 16 + 4 * g + e;
+                    dp[rbk][e] = (rr < s) ? 0.f : dp[rbk][e] * decay_of(rr, s);
+                }
+            }
+        }
+        if constexpr (H) {
+#pragma unroll
+            for (int p = 0; p < NRB / 2; ++p) {
+                if (2 * p + 1 >= w) {
+                    frag bop;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bop[e] = from_f32<TM>(dp[2 * p][e]);
+                        bop[4 + e] = from_f32<TM>(dp[2 * p + 1][e]);
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) acc[ct] = MF::mma(tok(Qs, PKt{}, p, ct * 16), bop, acc[ct]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int rbk = 0; rbk < NRB; ++rbk) {
+                if (rbk >= w) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+                            acc[ct] = MF::mma(Qs[(rbk * 16 + 4 * g + e) * PK + ct * 16 + n], dp[rbk][e], acc[ct]);
+                }
+            }
+        }
+        float *dkg = a.gk + ((size_t)bh * L + t0 + s) * DK;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            if (s < nv) *reinterpret_cast<f32x4 *>(dkg + ct * 16 + 4 * g) = acc[ct];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rterm -= acc[ct][e] * to_f32<TM>(Ks[s * PK + ct * 16 + 4 * g + e]);
+        }
+    }
+    {
+        f32x4 acc[NJT];
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+            acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS_K; ++ks)
+                acc[jt] = MF::mma(tok(Ds, PVt{}, ks, jt * 16), trn(Ks, PK, s, ks), acc[jt]);
+            acc[jt] *= ws;
+        }
+        // A tiles D[r][s] = sum_c Q[r][c] K[s][c] for query blocks rbk >= w
+        f32x4 at[NRB];
+#pragma unroll
+        for (int rbk = 0; rbk < NRB; ++rbk) {
+            at[rbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (rbk >= w) {
+#pragma unroll
+                for (int ks = 0; ks < NKS_K; ++ks)
+                    at[rbk] = MF::mma(nat(Qs, PK, rbk * 16 + n, ks, DK), nat(Ks, PK, s, ks, DK), at[rbk]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = rbk * 16 + 4 * g + e;
+                    at[rbk][e] = (rr < s) ? 0.f : at[rbk][e] * decay_of(rr, s);
+                }
+            }
+        }
+        if constexpr (H) {
+#pragma unroll
+            for (int p = 0; p < NRB / 2; ++p) {
+                if (2 * p + 1 >= w) {
+                    frag bop;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bop[e] = from_f32<TM>(at[2 * p][e]);
+                        bop[4 + e] = from_f32<TM>(at[2 * p + 1][e]);
+                    }
+#pragma unroll
+                    for (int jt = 0; jt < NJT; ++jt) acc[jt] = MF::mma(tok(Os, PVt{}, p, jt * 16), bop, acc[jt]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int rbk = 0; rbk < NRB; ++rbk) {
+                if (rbk >= w) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int jt = 0; jt < NJT; ++jt)
+                            acc[jt] = MF::mma(Os[(rbk * 16 + 4 * g + e) * PV + jt * 16 + n], at[rbk][e], acc[jt]);
+                }
+            }
+        }
+        float *dvg = a.gv + ((size_t)bh * L + t0 + s) * DV;
+        if (s < nv) {
+#pragma unroll
+            for (int jt = 0; jt < NJT; ++jt) *reinterpret_cast<f32x4 *>(dvg + jt * 16 + 4 * g) = acc[jt];
+        }
+    }
+    // q . dq - k . dk of token 16 w + n: sum over the four lane groups
+    rterm += __shfl_xor(rterm, 16, 64);
+    rterm += __shfl_xor(rterm, 32, 64);
+    if (DECAY && g == 0 && s < nv) a.rterm[(size_t)bh * L + t0 + s] = rterm;
+}
+
+// ---------------------------------------------------------------------------
+// dl_t = sum_{u >= t} rterm_u + <dS_L, S_L>, one workgroup (256 threads) per head
+template <int DK>
+__global__ void __launch_bounds__(256) dgate_kernel(BwdArgs a) {
+    constexpr int dk = DK;
+    __shared__ float part[256];
+    __shared__ float base;
+    const int tid = threadIdx.x, bh = blockIdx.x, L = a.L, dv = a.dv;
+    // <dS_L, S_L> over the head's dk x dv state
+    float acc = 0.f;
+    if (a.ds_out) {
+        const float *x = a.ds_out + (size_t)bh * dk * dv, *y = a.s_last + (size_t)bh * dk * dv;
+        for (int i = tid; i < dk * dv; i += 256) acc += x[i] * y[i];
+    }
+    part[tid] = acc;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off) part[tid] += part[tid + off];
+        __syncthreads();
+    }
+    if (tid == 0) base = part[0];
+    __syncthreads();
+    // reverse scan: thread tid owns tokens [tid * per, (tid + 1) * per)
+    const int per = (L + 255) / 256;
+    const int b0 = min(L, tid * per), b1 = min(L, b0 + per);
+    const float *rt = a.rterm + (size_t)bh * L;
+    float tot = 0.f;
+    for (int t = b0; t < b1; ++t) tot += rt[t];
+    __syncthreads();
+    part[tid] = tot;
+    __syncthreads();
+    // exclusive suffix over the threads after this one
+    float after = 0.f;
+    for (int j = tid + 1; j < 256; ++j) after += part[j];
+    float run = base + after;
+    float *dl = a.glg + (size_t)bh * L;
+    for (int t = b1 - 1; t >= b0; --t) {
+        run += rt[t];
+        dl[t] = run;
+    }
+}
+
+template <typename TI, int DK, int DV, bool DECAY>
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t st) {
+    constexpr int DVT = DV >= 64 ? 64 : DV;  // value slices of the state scans
+    const int nchunks = (a.L + 63) / 64;
+    BwdArgs b = a;
+    b.nsplit = DV / DVT;
+    hipLaunchKernelGGL((state_scan_kernel<TI, DK, DVT, true, DECAY>), dim3(a.BH * b.nsplit), dim3(256), 0, st, b);
+    hipLaunchKernelGGL((state_scan_kernel<TI, DK, DVT, false, DECAY>), dim3(a.BH * b.nsplit), dim3(256), 0, st, b);
+    if (nchunks > 0)
+        hipLaunchKernelGGL((bwd_dqkv_kernel<TI, DK, DV, DECAY>), dim3(a.BH * nchunks), dim3(256), 0, st, b);
+    if (DECAY && nchunks > 0 && a.glg) hipLaunchKernelGGL((dgate_kernel<DK>), dim3(a.BH), dim3(256), 0, st, b);
+    return hipGetLastError();
+}
+
+}  // namespace la

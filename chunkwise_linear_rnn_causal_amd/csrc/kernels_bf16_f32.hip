@@ -3,6 +3,7 @@
 #include "decode_impl.hpp"
 #include "gdn_prep_impl.hpp"
 #include "vdecay_fwd_impl.hpp"
+#include "bwd_impl.hpp"
 
 namespace la {
 
@@ -91,5 +92,26 @@ template hipError_t launch_decode<V_VDECAY, bf16, float, 64, 128>(const DecodeAr
 template hipError_t launch_decode<V_VDECAY, bf16, float, 128, 32>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_VDECAY, bf16, float, 128, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_VDECAY, bf16, float, 128, 128>(const DecodeArgs &, hipStream_t);
+
+
+// backward: (input, d_k, d_v, decayed)
+template hipError_t launch_bwd<bf16, 32, 32, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 32, 32, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 32, 64, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 32, 64, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 32, 128, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 32, 128, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 64, 32, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 64, 32, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 64, 64, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 64, 64, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 64, 128, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 64, 128, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 128, 32, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 128, 32, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 128, 64, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 128, 64, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 128, 128, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<bf16, 128, 128, true>(const BwdArgs &, hipStream_t);
 
 }  // namespace la

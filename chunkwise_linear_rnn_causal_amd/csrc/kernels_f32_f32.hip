@@ -3,6 +3,7 @@
 #include "decode_impl.hpp"
 #include "gdn_prep_impl.hpp"
 #include "vdecay_fwd_impl.hpp"
+#include "bwd_impl.hpp"
 #include "short_conv_impl.hpp"
 
 namespace la {
@@ -83,5 +84,20 @@ template hipError_t launch_decode<V_VDECAY, float, float, 64, 128>(const DecodeA
 template hipError_t launch_decode<V_VDECAY, float, float, 128, 32>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_VDECAY, float, float, 128, 64>(const DecodeArgs &, hipStream_t);
 template hipError_t launch_decode<V_VDECAY, float, float, 128, 128>(const DecodeArgs &, hipStream_t);
+
+
+// backward: (input, d_k, d_v, decayed)
+template hipError_t launch_bwd<float, 32, 32, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 32, 32, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 32, 64, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 32, 64, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 32, 128, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 32, 128, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 64, 32, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 64, 32, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 64, 64, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 64, 64, true>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 128, 32, false>(const BwdArgs &, hipStream_t);
+template hipError_t launch_bwd<float, 128, 32, true>(const BwdArgs &, hipStream_t);
 
 }  // namespace la

@@ -55,6 +55,21 @@ struct ConvArgs {
     int BH, H, L, NT;           // NT = max(1, ceil(L / TT)) token tiles
 };
 
+// Backward pass of the chunk forward (C = 64). Gradients are fp32.
+struct BwdArgs {
+    const void *q, *k, *v, *dout;  // [BH, L, DK], [BH, L, DK], [BH, L, dv], [BH, L, dv] (input type)
+    const float *lg;               // [BH, L] log-gates or nullptr (plain)
+    const float *s_in;             // [BH, DK, dv] initial state or nullptr
+    const float *ds_out;           // [BH, DK, dv] gradient of the final state or nullptr
+    float *gq, *gk, *gv;           // gradients of q, k, v: [BH, L, DK], [BH, L, DK], [BH, L, dv]
+    float *glg;                    // gradient of the log-gates [BH, L] or nullptr
+    float *gs_in;                  // gradient of the initial state [BH, DK, dv] or nullptr
+    void *hs, *dhs;                // workspace: per-chunk states / state gradients [BH, nchunks, DK, dv] (operand type)
+    float *s_last;                 // workspace: final state [BH, DK, dv]
+    float *rterm;                  // workspace: q . dq - k . dk per token [BH, L]
+    int BH, L, dv, nsplit;
+};
+
 // TI: input type (bf16 or float); TO: output type (float or bf16); DVT: value
 // columns per workgroup; NW: waves per workgroup. The instantiated combinations
 // are listed in kernels_*.hip and selected by abi.hip.
@@ -73,6 +88,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
 
 // Tokens per thread of the short convolution (the host sizes the grid with it).
 template <typename T> constexpr int conv_tile() { return sizeof(T) == 2 ? 8 : 4; }
+
+template <typename TI, int DK, int DV, bool DECAY>
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t st);
 
 template <typename T, int K>
 hipError_t launch_short_conv(const ConvArgs &a, unsigned blocks, hipStream_t st);

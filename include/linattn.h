@@ -205,6 +205,40 @@ la_status la_short_conv(la_dtype dt, const void *q, const void *k, const void *v
                         void *k_state_out, void *v_state_out, int B, int H, int L, int d_k,
                         int d_v, int K, void *stream);
 
+/*
+ * Backward pass of la_chunk_fwd (training): gradients of a scalar loss with
+ * respect to q, k, v, the log-gates and the initial state, given d_o =
+ * dLoss/do and optionally d_state_out = dLoss/d(final state). Reverse-mode of
+ * the recurrence above, in its chunk form (tensorplay section 3.2). The forward
+ * states are recomputed from q, k, v, one per chunk, into the workspace, as in
+ * the materialized form of tensorplay section 4.1.2 (per-chunk states stored,
+ * recomputed for back-propagation instead of kept from the forward). With G
+ * the cumulative log-gate the loss sees only differences G_r - G_s and G_L, so
+ * d_log_gate_t = sum_{u>=t} (q_u . dq_u - k_u . dk_u) + <d_state_out, S_L>.
+ *   var          LA_PLAIN or LA_DECAY (others: LA_ERR_UNSUPPORTED).
+ *   dt           dtype of q, k, v and d_o (LA_BF16 or LA_F32); every gradient
+ *                is float32.
+ *   q, k, v, log_gate, state_in   as given to la_chunk_fwd.
+ *   d_o          [B,H,L,d_v] in dt, required when L > 0.
+ *   d_state_out  [B,H,d_k,d_v] float32 or NULL (zero).
+ *   dq, dk       [B,H,L,d_k] float32; dv [B,H,L,d_v] float32; required when L > 0.
+ *   d_log_gate   [B,H,L] float32 (LA_DECAY only) or NULL (not computed).
+ *   d_state_in   [B,H,d_k,d_v] float32 or NULL (not written).
+ *   C            64. d_k, d_v in {32, 64, 128}.
+ *   workspace    at least la_chunk_bwd_workspace_size() bytes, 256-byte aligned:
+ *                per-chunk states and state gradients (operand precision), the
+ *                final state and one float per token.
+ * Outputs and the workspace must not overlap any input or each other.
+ */
+la_status la_chunk_bwd_workspace_size(la_variant var, la_dtype dt, int B, int H, int L,
+                                      int d_k, int d_v, int C, size_t *bytes);
+la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k,
+                       const void *v, const float *log_gate, const float *state_in,
+                       const void *d_o, const float *d_state_out, float *dq, float *dk,
+                       float *dv, float *d_log_gate, float *d_state_in, int B, int H, int L,
+                       int d_k, int d_v, int C, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
 /* Static string naming a status code. */
 const char *la_status_str(la_status s);
 

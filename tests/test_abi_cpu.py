@@ -153,3 +153,51 @@ def test_short_conv_valid_arguments_reach_the_device_check(kw):
     # on a host without a usable gfx950 device the call fails only at the device
     # check, after every argument was accepted
     assert conv(**kw) not in (INVALID,)
+
+
+def bwd(var=DECAY, dt=BF16, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lg=FAKE + 0x300000, s_in=None,
+        do=FAKE + 0x400000, dso=None, dq=0x800000000, dk=0x810000000, dv=0x820000000, dlg=None, dsi=None,
+        B=1, H=2, L=128, dk_=64, dv_=64, C=64, ws=0x900000000, ws_bytes=1 << 30):
+    return la.load_library().la_chunk_bwd(var, dt, q, k, v, lg, s_in, do, dso, dq, dk, dv, dlg, dsi, B, H, L,
+                                          dk_, dv_, C, ws, ws_bytes, None)
+
+
+def bwd_wsize(var=DECAY, dt=BF16, B=2, H=3, L=100, dk_=64, dv_=32, C=64):
+    out = ctypes.c_size_t(123)
+    st = la.load_library().la_chunk_bwd_workspace_size(var, dt, B, H, L, dk_, dv_, C, ctypes.byref(out))
+    return st, out.value
+
+
+def test_bwd_workspace_size():
+    # per-chunk states and state gradients (fp16 operands for bf16), final state, one float per token
+    st, n = bwd_wsize()
+    r = lambda x: -(-x // 256) * 256
+    states = r(6 * 2 * 64 * 32 * 2)
+    assert st == 0 and n == 2 * states + r(6 * 64 * 32 * 4) + r(6 * 100 * 4)
+    assert bwd_wsize(var=GDN)[0] == UNSUPPORTED
+    assert bwd_wsize(C=128)[0] == UNSUPPORTED
+    assert bwd_wsize(dt=F32, dk_=128, dv_=128)[0] == UNSUPPORTED
+    assert bwd_wsize(dt=F32, dk_=128, dv_=32)[0] == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(var=9), INVALID), (dict(var=NORM), UNSUPPORTED), (dict(var=VDECAY), UNSUPPORTED),
+    (dict(C=128), UNSUPPORTED), (dict(dk_=96), UNSUPPORTED), (dict(B=0), INVALID),
+    (dict(lg=None), INVALID),                           # decay needs its gates
+    (dict(var=PLAIN), INVALID),                         # plain takes no gates
+    (dict(var=PLAIN, lg=None, dlg=0x830000000), INVALID),
+    (dict(do=None), INVALID), (dict(dq=None), INVALID),
+    (dict(ws=None), INVALID), (dict(ws_bytes=1024), INVALID), (dict(ws=0x900000010), INVALID),
+    (dict(dq=FAKE + 0x400000 + 0x100), INVALID),        # dq inside d_o
+    (dict(dk=0x800000000 + 0x1000), INVALID),           # dk inside dq
+    (dict(dsi=0x900000000 + 0x100), INVALID),           # d_state_in inside the workspace
+    (dict(q=FAKE + 4), INVALID),
+])
+def test_chunk_bwd_rejects(kw, expect):
+    assert bwd(**kw) == expect
+
+
+def test_chunk_bwd_valid_arguments_reach_the_device_check():
+    assert bwd() not in (INVALID, UNSUPPORTED)
+    assert bwd(var=PLAIN, lg=None) not in (INVALID, UNSUPPORTED)
+    assert bwd(L=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None) not in (INVALID, UNSUPPORTED)

@@ -34,6 +34,7 @@ import numpy as np
 
 TAG_Q, TAG_K, TAG_V, TAG_GATE, TAG_BETA, TAG_STATE = 1, 2, 3, 4, 5, 6
 TAG_CONV_W, TAG_CONV_WINDOW = 7, 8
+TAG_DOUT = 9
 
 VARIANTS = ("plain", "normalized", "decay", "gated_delta", "vector_decay")
 
@@ -376,3 +377,23 @@ def config_conv_inputs(name: str, seed: int = 0) -> ConvInputs:
     c = CONFIGS[name]
     assert c["kind"] == "conv", name
     return make_conv_inputs(c["dtype"], c["B"], c["H"], c["L"], c["dk"], c["dv"], c["K"], seed=seed)
+
+
+# ----------------------------------------------------------------------------
+# Backward pass
+# ----------------------------------------------------------------------------
+def make_backward_dout(dtype: str, B: int, H: int, L: int, dv: int, seed: int = 0,
+                       threads: Optional[int] = None) -> np.ndarray:
+    """Output gradient dO ~ N(0, 1) per (b, h) slice (stream [seed, 9, b, h]), in the
+    storage dtype."""
+    sdt = np.uint16 if dtype == "bf16" else np.float32
+    out = np.empty((B * H, L, dv), sdt)
+
+    def fill(i: int) -> None:
+        b, h = divmod(i, H)
+        out[i] = _store(stream(seed, TAG_DOUT, b, h).standard_normal((L, dv), dtype=np.float32), dtype)
+
+    nthr = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(nthr) as ex:
+        list(ex.map(fill, range(B * H)))
+    return out.reshape(B, H, L, dv)
