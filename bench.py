@@ -6,7 +6,8 @@ already resident in HBM:
   - chunk workloads: one la_chunk_fwd (C = 64, fp32 output and final state);
   - decode workload: 100 back-to-back la_decode_step calls (one "step" = 100
     tokens per sequence-head, as the workload is quoted).
-  - short-convolution workload: one la_short_conv over q, k and v.
+  - short-convolution workload: one la_short_conv over q, k and v;
+  - backward workload: one la_chunk_bwd (gradients of q, k, v and the gates).
 The headline workload (the JSON line's value) is the normalized kernel linear
 attention at B=8, H=16, L=2048, d=64; by default the other workloads are timed
 too and reported under "workloads". Every workload is timed with HIP
@@ -98,6 +99,20 @@ def conv_work(c: dict) -> tuple[float, float]:
     elems = BH * L * (2 * c["dk"] + c["dv"])
     flop = 2.0 * K * elems
     nbytes = 2 * elems * esz + c["H"] * (2 * c["dk"] + c["dv"]) * K * 4
+    return flop, nbytes
+
+
+def bwd_work(c: dict) -> tuple[float, float]:
+    """(flop, bytes) of one backward pass: q, k, v, dO and the gates read once;
+    dq, dk, dv and the gate gradient written once in fp32. Each forward product
+    has two gradient products, so the flop count is twice the forward's."""
+    B, H, L, dk, dv, C = c["B"], c["H"], c["L"], c["dk"], c["dv"], c["C"]
+    BH = B * H
+    esz = 2 if c["dtype"] == "bf16" else 4
+    flop = 2.0 * (2 * C * (dk + dv) + 4 * dk * dv) * BH * L
+    nbytes = BH * L * ((2 * dk + 2 * dv) * esz + (2 * dk + dv) * 4)
+    if c["variant"] == "decay":
+        nbytes += 2 * BH * L * 4                                 # gates in, gate gradient out
     return flop, nbytes
 
 
@@ -241,6 +256,35 @@ def bench_conv(name: str, steps: int, warmup: int, device) -> dict:
                 B=c["B"], H=c["H"], L=c["L"], d_k=c["dk"], d_v=c["dv"], K=c["K"])
 
 
+def bench_bwd(name: str, steps: int, warmup: int, device) -> dict:
+    import torch
+    import chunkwise_linear_rnn_causal_amd as la
+    c = W.CONFIGS[name]
+    inp = W.make_chunk_inputs(c["variant"], c["dtype"], c["B"], c["H"], c["L"], c["dk"], c["dv"],
+                              seed=0, recipe=c["recipe"])
+    do = W.make_backward_dout(c["dtype"], c["B"], c["H"], c["L"], c["dv"], seed=0)
+    flop, nbytes = bwd_work(c)
+    q, k, v, lg, dO = (to_dev(x, device) for x in (inp.q, inp.k, inp.v, inp.log_gate, do))
+    dt = 1 if c["dtype"] == "bf16" else 0
+    ws = torch.empty(la.la_chunk_bwd_workspace_size(c["variant"], dt, c["B"], c["H"], c["L"], c["dk"],
+                                                    c["dv"], c["C"]), dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device)
+
+    def step(_):
+        la.la_chunk_bwd(c["variant"], q, k, v, dO, lg, workspace=ws, stream=stream)
+
+    ms, wall_ms = time_steps(step, steps, warmup, stream)
+    t = ms / 1e3
+    toks = c["B"] * c["L"]
+    return dict(workload=name, variant=c["variant"] + "_backward", tokens_per_s=toks / t,
+                ms_per_step=t * 1e3, wall_ms_per_step=wall_ms, flop=flop, bytes=nbytes,
+                achieved_gbs=nbytes / t / 1e9, achieved_tflops=flop / t / 1e12,
+                hbm_frac=nbytes / t / 1e9 / HBM_PEAK_GBS, mfma_frac=flop / t / 1e12 / MFMA_PEAK_TFLOPS,
+                roofline_frac=max(nbytes / (HBM_PEAK_GBS * 1e9), flop / (MFMA_PEAK_TFLOPS * 1e12)) / t,
+                workspace_bytes=ws.numel(), B=c["B"], H=c["H"], L=c["L"], d_k=c["dk"], d_v=c["dv"],
+                C=c["C"])
+
+
 def cpu_baseline(name: str, min_seconds: float = 10.0) -> dict:
     """Time the fp64 oracle over the whole workload on the host cores."""
     import oracle
@@ -319,7 +363,7 @@ def main() -> int:
         print(f"[bench] {name}", file=sys.stderr, flush=True)
         steps = args.steps if kind != "decode" else max(1, min(args.steps, 5))
         warm = args.warmup if kind != "decode" else max(1, min(args.warmup, 2))
-        fn = {"chunk": bench_chunk, "decode": bench_decode, "conv": bench_conv}[kind]
+        fn = {"chunk": bench_chunk, "decode": bench_decode, "conv": bench_conv, "bwd": bench_bwd}[kind]
         results[name] = fn(name, steps, warm, device)
         r = results[name]
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['achieved_gbs']:.0f} GB/s, "

@@ -16,11 +16,12 @@
 //
 // Kernels:
 //   state_scan_kernel<FWD>  one workgroup per (head, value slice) walks the chunks
-//       forward, storing each H_c (operand type) and the final state S_L; with
+//       forward, storing each H_c (operand type, transposed) and the final state S_L; with
 //       FWD = false it walks them backward with (q (.) a, dO) in place of
 //       (k (.) e^{G_end - G}, v), storing each dH_c and returning dS_0.
-//   bwd_dqkv_kernel  one workgroup (4 waves) per (head, chunk), fully parallel:
-//       wave w owns query block w (dq) and key block w (dk, dv). Products are
+//   bwd_dqkv_kernel  one workgroup (8 waves) per (head, chunk), fully parallel:
+//       waves w, w+4 own query block w (dq) and key block w (dk, dv), each for
+//       half of the output columns. Products are
 //       taken transposed (dQ^T = K^T dP^T, ...) so that the 16 x 16 score-like
 //       tiles dP = dO V^T, A = Q K^T leave the MFMA in exactly the B-operand
 //       layout of the next product, as in the forward kernel. It also writes
@@ -38,7 +39,11 @@ namespace la {
 
 // ---------------------------------------------------------------------------
 // state scan: S <- e^{G_end} S + sum_s f_s X_s^T Y_s over chunks, forward
-// (X = k, Y = v, f_s = e^{G_end - G_s}) or backward (X = q, Y = dO, f_s = e^{G_s})
+// (X = k, Y = v, f_s = e^{G_end - G_s}) or backward (X = q, Y = dO, f_s = e^{G_s}).
+// The per-chunk states are stored transposed, [d_v][d_k] per chunk, so each lane
+// writes four consecutive d_k entries at once. The next chunk's rows and gates
+// are loaded into registers while the current chunk is folded in; every wave
+// scans the chunk's gates itself (rows in lanes), so no barrier guards them.
 template <typename TI, int DK, int DVT, bool FWD, bool DECAY>
 __global__ void __launch_bounds__(256) state_scan_kernel(BwdArgs a) {
     using TM = typename OpOf<TI>::type;
@@ -50,10 +55,9 @@ __global__ void __launch_bounds__(256) state_scan_kernel(BwdArgs a) {
     constexpr int NTI = DK / 16, NTJ = DVT / 16, NTILE = NTI * NTJ, TPW = (NTILE + 3) / 4;
     constexpr int NTK = C / (4 * E);
     constexpr int SEGX = DK / 8, SEGY = DVT / 8;
+    constexpr int NXS = (C * SEGX + 255) / 256, NYS = (C * SEGY + 255) / 256;
     __shared__ __align__(16) TM Xs[C * PX];
     __shared__ __align__(16) TM Ys[C * PY];
-    __shared__ float Gt[C];
-    __shared__ float Gend;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
     const int bh = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
@@ -77,58 +81,71 @@ __global__ void __launch_bounds__(256) state_scan_kernel(BwdArgs a) {
         }
     }
 
+    Raw8<TI> rx[NXS], ry[NYS];
+    float rg = 0.f;
+    auto load = [&](int c) __attribute__((always_inline)) {
+        const int t0 = c * C, nv = min(C, L - t0);
+#pragma unroll
+        for (int m = 0; m < NXS; ++m) {
+            const int sid = tid + 256 * m, row = sid / SEGX;
+            rx[m] = (sid < C * SEGX && row < nv) ? ld_raw8<TI>(xg + (size_t)(t0 + row) * DK + 8 * (sid % SEGX))
+                                                 : zero_raw8<TI>();
+        }
+#pragma unroll
+        for (int m = 0; m < NYS; ++m) {
+            const int sid = tid + 256 * m, row = sid / SEGY;
+            ry[m] = (sid < C * SEGY && row < nv) ? ld_raw8<TI>(yg + (size_t)(t0 + row) * dv + 8 * (sid % SEGY))
+                                                 : zero_raw8<TI>();
+        }
+        if constexpr (DECAY) rg = lane < nv ? lg[t0 + lane] : 0.f;
+    };
+    if (nchunks > 0) load(FWD ? 0 : nchunks - 1);
+
     for (int it = 0; it < nchunks; ++it) {
         const int c = FWD ? it : nchunks - 1 - it;
-        const int t0 = c * C, nv = min(C, L - t0);
-        // store the state this chunk starts from (forward) / ends at (backward)
+        // store the state this chunk starts from (forward) / ends at (backward), transposed
         TM *hc = hs + (size_t)c * DK * dv;
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int tile = wv + 4 * m;
             if (tile < NTILE) {
                 const int ti = tile / NTJ, tj = tile % NTJ;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    hc[(size_t)(ti * 16 + 4 * g + e) * dv + j0 + tj * 16 + n] = from_f32<TM>(Sacc[m][e]);
+                st4<TM>(hc + (size_t)(j0 + tj * 16 + n) * DK + ti * 16 + 4 * g, Sacc[m]);
             }
         }
-        // chunk-local gate prefix (wave 0), then the scaled operands
+        // the chunk's gate prefix, rows in lanes (every wave)
+        float G = 0.f, gend = 0.f;
         if constexpr (DECAY) {
-            if (wv == 0) {
-                const float G = wave_inclusive_sum(lane < nv ? lg[t0 + lane] : 0.f);
-                Gt[lane] = G;
-                if (lane == 63) Gend = G;
+            G = wave_inclusive_sum(rg);
+            gend = __shfl(G, 63, 64);
+        }
+        __syncthreads();  // the previous chunk's operand reads are done
+#pragma unroll
+        for (int m = 0; m < NXS; ++m) {
+            const int sid = tid + 256 * m;
+            if (sid < C * SEGX) {
+                const int row = sid / SEGX;
+                float x[8];
+                unpack8<TI>(rx[m], x);
+                if constexpr (DECAY) {
+                    const float Gr = __shfl(G, row, 64);
+                    const float f = FWD ? __expf(gend - Gr) : __expf(Gr);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) x[e] *= f;
+                }
+                st8<TM>(&Xs[row * PX + 8 * (sid % SEGX)], x);
             }
         }
-        __syncthreads();
-        const float gend = DECAY ? Gend : 0.f;
-        for (int sid = tid; sid < C * SEGX; sid += 256) {
-            const int row = sid / SEGX, cs = sid % SEGX;
-            float x[8];
-            if (row < nv) {
-                ld8<TI>(xg + (size_t)(t0 + row) * DK + 8 * cs, x);
-            } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        for (int m = 0; m < NYS; ++m) {
+            const int sid = tid + 256 * m;
+            if (sid < C * SEGY) {
+                float y[8];
+                unpack8<TI>(ry[m], y);
+                st8<TM>(&Ys[(sid / SEGY) * PY + 8 * (sid % SEGY)], y);
             }
-            if constexpr (DECAY) {
-                const float f = FWD ? __expf(gend - Gt[row]) : __expf(Gt[row]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] *= f;
-            }
-            st8<TM>(&Xs[row * PX + 8 * cs], x);
         }
-        for (int sid = tid; sid < C * SEGY; sid += 256) {
-            const int row = sid / SEGY, cs = sid % SEGY;
-            float y[8];
-            if (row < nv) {
-                ld8<TI>(yg + (size_t)(t0 + row) * dv + 8 * cs, y);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = 0.f;
-            }
-            st8<TM>(&Ys[row * PY + 8 * cs], y);
-        }
+        if (it + 1 < nchunks) load(FWD ? c + 1 : c - 1);
         __syncthreads();
         const float eg = DECAY ? __expf(gend) : 1.f;
 #pragma unroll
@@ -151,7 +168,6 @@ __global__ void __launch_bounds__(256) state_scan_kernel(BwdArgs a) {
                 }
             }
         }
-        __syncthreads();
     }
     // forward: the final state S_L; backward: dLoss/dS_0
     float *out = FWD ? a.s_last : a.gs_in;
@@ -170,26 +186,29 @@ __global__ void __launch_bounds__(256) state_scan_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dq, dk, dv of one chunk (C = 64, 4 waves; wave w: query block w and key block w)
+// dq, dk, dv of one chunk (C = 64, 8 waves): wave w takes query block w & 3 (dq)
+// and key block w & 3 (dk, dv) for half w >> 2 of the output columns; the two
+// waves of a block compute its score-like tiles each.
 template <typename TI, int DK, int DV, bool DECAY>
-__global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
     using TM = typename OpOf<TI>::type;
     using MF = Mfma<TM>;
     using frag = typename MF::frag;
     constexpr int C = 64, E = MF::E, NRB = 4;
     constexpr bool H = E == 8;
-    constexpr int PK = H ? DK + 16 : DK + 4;  // q, k, H, dH tiles (natural and transpose reads)
-    constexpr int PV = H ? DV + 16 : DV + 4;  // v, dO, H, dH (value-side pitch)
+    constexpr int PK = H ? DK + 16 : DK + 4;  // q, k and the transposed states (d_k columns)
+    constexpr int PV = H ? DV + 16 : DV + 4;  // v, dO
     constexpr int NKS_K = DK / (4 * E), NKS_V = DV / (4 * E);  // k-steps over d_k, d_v
-    constexpr int NCT = DK / 16, NJT = DV / 16;
+    constexpr int NCT = DK / 16, NJT = DV / 16, NCW = NCT / 2, NJW = NJT / 2;
     constexpr int SEGK = DK / 8, SEGV = DV / 8;
     __shared__ __align__(16) TM Qs[C * PK];
     __shared__ __align__(16) TM Ks[C * PK];
     __shared__ __align__(16) TM Vs[C * PV];
     __shared__ __align__(16) TM Os[C * PV];   // dO
-    __shared__ __align__(16) TM Hs[DK * PV];  // H_c   [dk][dv]
-    __shared__ __align__(16) TM Ds[DK * PV];  // dH_c  [dk][dv]
+    __shared__ __align__(16) TM Hs[DV * PK];  // H_c^T  [dv][dk]
+    __shared__ __align__(16) TM Ds[DV * PK];  // dH_c^T [dv][dk]
     __shared__ float Gt[C];
+    __shared__ float RT[2][C];
     __shared__ float Gend;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
@@ -211,34 +230,71 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
             if (lane == 63) Gend = G;
         }
     }
-    auto stage = [&](const TI *src, TM *dst, int SEG, int P, int W) __attribute__((always_inline)) {
-        for (int sid = tid; sid < C * SEG; sid += 256) {
-            const int row = sid / SEG, cs = sid % SEG;
-            float x[8];
-            if (row < nv) {
-                ld8<TI>(src + (size_t)row * W + 8 * cs, x);
-            } else {
+    // every load of the chunk is issued before any is used
+    constexpr int NQ = (C * SEGK + 511) / 512, NVV = (C * SEGV + 511) / 512, NS = (DV * SEGK + 511) / 512;
+    Raw8<TI> rq[NQ], rk[NQ], rv[NVV], ro[NVV];
+    Raw8<TM> rh[NS], rd[NS];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = 0.f;
-            }
-            st8<TM>(&dst[row * P + 8 * cs], x);
+    for (int m = 0; m < NQ; ++m) {
+        const int sid = tid + 512 * m, row = sid / SEGK, off = row * DK + 8 * (sid % SEGK);
+        const bool ok = sid < C * SEGK && row < nv;
+        rq[m] = ok ? ld_raw8<TI>(qg + off) : zero_raw8<TI>();
+        rk[m] = ok ? ld_raw8<TI>(kg + off) : zero_raw8<TI>();
+    }
+#pragma unroll
+    for (int m = 0; m < NVV; ++m) {
+        const int sid = tid + 512 * m, row = sid / SEGV, off = row * DV + 8 * (sid % SEGV);
+        const bool ok = sid < C * SEGV && row < nv;
+        rv[m] = ok ? ld_raw8<TI>(vg + off) : zero_raw8<TI>();
+        ro[m] = ok ? ld_raw8<TI>(og + off) : zero_raw8<TI>();
+    }
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+        const int sid = tid + 512 * m;
+        if (sid < DV * SEGK) {
+            const int off = (sid / SEGK) * DK + 8 * (sid % SEGK);
+            rh[m] = ld_raw8<TM>(hg + off);
+            rd[m] = ld_raw8<TM>(dhg + off);
         }
+    }
+    auto put = [&](const Raw8<TI> &r, TM *dst) __attribute__((always_inline)) {
+        float x[8];
+        unpack8<TI>(r, x);
+        st8<TM>(dst, x);
     };
-    stage(qg, Qs, SEGK, PK, DK);
-    stage(kg, Ks, SEGK, PK, DK);
-    stage(vg, Vs, SEGV, PV, DV);
-    stage(og, Os, SEGV, PV, DV);
-    for (int sid = tid; sid < DK * SEGV; sid += 256) {
-        const int row = sid / SEGV, cs = sid % SEGV;
-        float x[8], y[8];
-        ld8<TM>(hg + (size_t)row * DV + 8 * cs, x);
-        ld8<TM>(dhg + (size_t)row * DV + 8 * cs, y);
-        st8<TM>(&Hs[row * PV + 8 * cs], x);
-        st8<TM>(&Ds[row * PV + 8 * cs], y);
+#pragma unroll
+    for (int m = 0; m < NQ; ++m) {
+        const int sid = tid + 512 * m;
+        if (sid < C * SEGK) {
+            const int o = (sid / SEGK) * PK + 8 * (sid % SEGK);
+            put(rq[m], &Qs[o]);
+            put(rk[m], &Ks[o]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < NVV; ++m) {
+        const int sid = tid + 512 * m;
+        if (sid < C * SEGV) {
+            const int o = (sid / SEGV) * PV + 8 * (sid % SEGV);
+            put(rv[m], &Vs[o]);
+            put(ro[m], &Os[o]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+        const int sid = tid + 512 * m;
+        if (sid < DV * SEGK) {
+            const int o = (sid / SEGK) * PK + 8 * (sid % SEGK);
+#pragma unroll
+            for (int u = 0; u < (int)(sizeof(TM) / 2); ++u) {
+                reinterpret_cast<uint4 *>(&Hs[o])[u] = rh[m].v[u];
+                reinterpret_cast<uint4 *>(&Ds[o])[u] = rd[m].v[u];
+            }
+        }
     }
     __syncthreads();
 
-    const int w = wv;
+    const int w = wv & 3, half = wv >> 2;
     const float gend = DECAY ? Gend : 0.f;
     // natural-layout operand: row `row` of X, k-step ks of a K-dim of width KW
     auto nat = [&](const TM *X, int P, int row, int ks, int KW) __attribute__((always_inline)) -> frag {
@@ -256,7 +312,7 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
             return X[row * P + 4 * ks + g];
         }
     };
-    // token-slot operand of a row-major [token][col] tile (col0 + n per lane)
+    // row-slot operand of a row-major tile (rows in the K-slots, column col0 + n per lane)
     auto tok = [&](const TM *X, auto p_tag, int ks, int col0) __attribute__((always_inline)) -> frag {
         constexpr int P = decltype(p_tag)::value;
         if constexpr (H) return tr_frag<P>(X, 32 * ks + 4 * g, col0, lane);
@@ -264,26 +320,38 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
     };
     using PKt = std::integral_constant<int, PK>;
     using PVt = std::integral_constant<int, PV>;
-    // e^{G_r - G_s}
     auto decay_of = [&](int r, int s) __attribute__((always_inline)) -> float {
         if constexpr (DECAY) return __expf(Gt[r] - Gt[s]);
         else return 1.f;
     };
+    // score-like tile pairs -> B operand over 32 tokens (tiles 2p, 2p+1)
+    auto bop_of = [&](const f32x4 &t0_, const f32x4 &t1_) __attribute__((always_inline)) -> frag {
+        frag b{};
+        if constexpr (H) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                b[e] = from_f32<TM>(t0_[e]);
+                b[4 + e] = from_f32<TM>(t1_[e]);
+            }
+        }
+        return b;
+    };
 
-    float rterm = 0.f;  // q . dq - k . dk of token 16 w + n, accumulated per lane
+    float rterm = 0.f;  // (q . dq - k . dk) of token 16 w + n over this wave's columns
 
     // ---- dq for query block w: dQ^T[c][r] = a_r sum_j H[c][j] dO[r][j] + sum_s K[s][c] dP[r][s]
     {
-        f32x4 acc[NCT];
+        f32x4 acc[NCW];
         const int r = 16 * w + n;
         const float ar = DECAY ? __expf(Gt[r]) : 1.f;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q_ = 0; q_ < NCW; ++q_) {
+            const int ct = half * NCW + q_;
+            acc[q_] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS_V; ++ks)
-                acc[ct] = MF::mma(nat(Hs, PV, ct * 16 + n, ks, DV), nat(Os, PV, r, ks, DV), acc[ct]);
-            acc[ct] *= ar;
+                acc[q_] = MF::mma(tok(Hs, PKt{}, ks, ct * 16), trn(Os, PV, r, ks), acc[q_]);
+            acc[q_] *= ar;
         }
         // dP^T tiles D[s][r] = sum_j V[s][j] dO[r][j] for key blocks sb <= w
         f32x4 dpt[NRB];
@@ -296,8 +364,8 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
                     dpt[sb] = MF::mma(nat(Vs, PV, sb * 16 + n, ks, DV), nat(Os, PV, r, ks, DV), dpt[sb]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int s = sb * 16 + 4 * g + e;
-                    dpt[sb][e] = (s > r) ? 0.f : dpt[sb][e] * decay_of(r, s);
+                    const int s_ = sb * 16 + 4 * g + e;
+                    dpt[sb][e] = (s_ > r) ? 0.f : dpt[sb][e] * decay_of(r, s_);
                 }
             }
         }
@@ -305,14 +373,10 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
 #pragma unroll
             for (int p = 0; p < NRB / 2; ++p) {
                 if (2 * p <= w) {
-                    frag bop;
+                    const frag bop = bop_of(dpt[2 * p], dpt[2 * p + 1]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bop[e] = from_f32<TM>(dpt[2 * p][e]);
-                        bop[4 + e] = from_f32<TM>(dpt[2 * p + 1][e]);
-                    }
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) acc[ct] = MF::mma(tok(Ks, PKt{}, p, ct * 16), bop, acc[ct]);
+                    for (int q_ = 0; q_ < NCW; ++q_)
+                        acc[q_] = MF::mma(tok(Ks, PKt{}, p, (half * NCW + q_) * 16), bop, acc[q_]);
                 }
             }
         } else {
@@ -322,18 +386,19 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct)
-                            acc[ct] = MF::mma(Ks[(sb * 16 + 4 * g + e) * PK + ct * 16 + n], dpt[sb][e], acc[ct]);
+                        for (int q_ = 0; q_ < NCW; ++q_)
+                            acc[q_] = MF::mma(Ks[(sb * 16 + 4 * g + e) * PK + (half * NCW + q_) * 16 + n], dpt[sb][e],
+                                              acc[q_]);
                 }
             }
         }
-        // write dq[r][ct*16 + 4g .. +3]; q . dq
         float *dqg = a.gq + ((size_t)bh * L + t0 + r) * DK;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            if (r < nv) *reinterpret_cast<f32x4 *>(dqg + ct * 16 + 4 * g) = acc[ct];
+        for (int q_ = 0; q_ < NCW; ++q_) {
+            const int ct = half * NCW + q_;
+            if (r < nv) *reinterpret_cast<f32x4 *>(dqg + ct * 16 + 4 * g) = acc[q_];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rterm += acc[ct][e] * to_f32<TM>(Qs[r * PK + ct * 16 + 4 * g + e]);
+            for (int e = 0; e < 4; ++e) rterm += acc[q_][e] * to_f32<TM>(Qs[r * PK + ct * 16 + 4 * g + e]);
         }
     }
 
@@ -342,14 +407,15 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
     const int s = 16 * w + n;
     const float ws = DECAY ? __expf(gend - Gt[s]) : 1.f;
     {
-        f32x4 acc[NCT];
+        f32x4 acc[NCW];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q_ = 0; q_ < NCW; ++q_) {
+            const int ct = half * NCW + q_;
+            acc[q_] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS_V; ++ks)
-                acc[ct] = MF::mma(nat(Ds, PV, ct * 16 + n, ks, DV), nat(Vs, PV, s, ks, DV), acc[ct]);
-            acc[ct] *= ws;
+                acc[q_] = MF::mma(tok(Ds, PKt{}, ks, ct * 16), trn(Vs, PV, s, ks), acc[q_]);
+            acc[q_] *= ws;
         }
         // dP tiles D[r][s] = sum_j dO[r][j] V[s][j] for query blocks rbk >= w
         f32x4 dp[NRB];
@@ -371,14 +437,10 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
 #pragma unroll
             for (int p = 0; p < NRB / 2; ++p) {
                 if (2 * p + 1 >= w) {
-                    frag bop;
+                    const frag bop = bop_of(dp[2 * p], dp[2 * p + 1]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bop[e] = from_f32<TM>(dp[2 * p][e]);
-                        bop[4 + e] = from_f32<TM>(dp[2 * p + 1][e]);
-                    }
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) acc[ct] = MF::mma(tok(Qs, PKt{}, p, ct * 16), bop, acc[ct]);
+                    for (int q_ = 0; q_ < NCW; ++q_)
+                        acc[q_] = MF::mma(tok(Qs, PKt{}, p, (half * NCW + q_) * 16), bop, acc[q_]);
                 }
             }
         } else {
@@ -388,28 +450,31 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct)
-                            acc[ct] = MF::mma(Qs[(rbk * 16 + 4 * g + e) * PK + ct * 16 + n], dp[rbk][e], acc[ct]);
+                        for (int q_ = 0; q_ < NCW; ++q_)
+                            acc[q_] = MF::mma(Qs[(rbk * 16 + 4 * g + e) * PK + (half * NCW + q_) * 16 + n], dp[rbk][e],
+                                              acc[q_]);
                 }
             }
         }
         float *dkg = a.gk + ((size_t)bh * L + t0 + s) * DK;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            if (s < nv) *reinterpret_cast<f32x4 *>(dkg + ct * 16 + 4 * g) = acc[ct];
+        for (int q_ = 0; q_ < NCW; ++q_) {
+            const int ct = half * NCW + q_;
+            if (s < nv) *reinterpret_cast<f32x4 *>(dkg + ct * 16 + 4 * g) = acc[q_];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) rterm -= acc[ct][e] * to_f32<TM>(Ks[s * PK + ct * 16 + 4 * g + e]);
+            for (int e = 0; e < 4; ++e) rterm -= acc[q_][e] * to_f32<TM>(Ks[s * PK + ct * 16 + 4 * g + e]);
         }
     }
     {
-        f32x4 acc[NJT];
+        f32x4 acc[NJW];
 #pragma unroll
-        for (int jt = 0; jt < NJT; ++jt) {
-            acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q_ = 0; q_ < NJW; ++q_) {
+            const int jt = half * NJW + q_;
+            acc[q_] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < NKS_K; ++ks)
-                acc[jt] = MF::mma(tok(Ds, PVt{}, ks, jt * 16), trn(Ks, PK, s, ks), acc[jt]);
-            acc[jt] *= ws;
+                acc[q_] = MF::mma(nat(Ds, PK, jt * 16 + n, ks, DK), nat(Ks, PK, s, ks, DK), acc[q_]);
+            acc[q_] *= ws;
         }
         // A tiles D[r][s] = sum_c Q[r][c] K[s][c] for query blocks rbk >= w
         f32x4 at[NRB];
@@ -431,14 +496,10 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
 #pragma unroll
             for (int p = 0; p < NRB / 2; ++p) {
                 if (2 * p + 1 >= w) {
-                    frag bop;
+                    const frag bop = bop_of(at[2 * p], at[2 * p + 1]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bop[e] = from_f32<TM>(at[2 * p][e]);
-                        bop[4 + e] = from_f32<TM>(at[2 * p + 1][e]);
-                    }
-#pragma unroll
-                    for (int jt = 0; jt < NJT; ++jt) acc[jt] = MF::mma(tok(Os, PVt{}, p, jt * 16), bop, acc[jt]);
+                    for (int q_ = 0; q_ < NJW; ++q_)
+                        acc[q_] = MF::mma(tok(Os, PVt{}, p, (half * NJW + q_) * 16), bop, acc[q_]);
                 }
             }
         } else {
@@ -448,21 +509,25 @@ __global__ void __launch_bounds__(256) bwd_dqkv_kernel(BwdArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
-                        for (int jt = 0; jt < NJT; ++jt)
-                            acc[jt] = MF::mma(Os[(rbk * 16 + 4 * g + e) * PV + jt * 16 + n], at[rbk][e], acc[jt]);
+                        for (int q_ = 0; q_ < NJW; ++q_)
+                            acc[q_] = MF::mma(Os[(rbk * 16 + 4 * g + e) * PV + (half * NJW + q_) * 16 + n], at[rbk][e],
+                                              acc[q_]);
                 }
             }
         }
         float *dvg = a.gv + ((size_t)bh * L + t0 + s) * DV;
         if (s < nv) {
 #pragma unroll
-            for (int jt = 0; jt < NJT; ++jt) *reinterpret_cast<f32x4 *>(dvg + jt * 16 + 4 * g) = acc[jt];
+            for (int q_ = 0; q_ < NJW; ++q_)
+                *reinterpret_cast<f32x4 *>(dvg + (half * NJW + q_) * 16 + 4 * g) = acc[q_];
         }
     }
-    // q . dq - k . dk of token 16 w + n: sum over the four lane groups
+    // q . dq - k . dk of token 16 w + n: sum over the lane groups, then the halves
     rterm += __shfl_xor(rterm, 16, 64);
     rterm += __shfl_xor(rterm, 32, 64);
-    if (DECAY && g == 0 && s < nv) a.rterm[(size_t)bh * L + t0 + s] = rterm;
+    if (g == 0) RT[half][s] = rterm;
+    __syncthreads();
+    if (DECAY && tid < C && tid < nv) a.rterm[(size_t)bh * L + t0 + tid] = RT[0][tid] + RT[1][tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -516,7 +581,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((state_scan_kernel<TI, DK, DVT, true, DECAY>), dim3(a.BH * b.nsplit), dim3(256), 0, st, b);
     hipLaunchKernelGGL((state_scan_kernel<TI, DK, DVT, false, DECAY>), dim3(a.BH * b.nsplit), dim3(256), 0, st, b);
     if (nchunks > 0)
-        hipLaunchKernelGGL((bwd_dqkv_kernel<TI, DK, DV, DECAY>), dim3(a.BH * nchunks), dim3(256), 0, st, b);
+        hipLaunchKernelGGL((bwd_dqkv_kernel<TI, DK, DV, DECAY>), dim3(a.BH * nchunks), dim3(512), 0, st, b);
     if (DECAY && nchunks > 0 && a.glg) hipLaunchKernelGGL((dgate_kernel<DK>), dim3(a.BH), dim3(256), 0, st, b);
     return hipGetLastError();
 }
