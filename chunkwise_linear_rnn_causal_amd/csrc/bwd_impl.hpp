@@ -15,10 +15,11 @@
 //   dl_t = sum_{u>=t} (q_u . dq_u - k_u . dk_u) + <dS_L, S_L>.
 //
 // Kernels:
-//   state_scan_kernel<FWD>  one workgroup per (head, value slice) walks the chunks
+//   state_scans_kernel  one workgroup per (head, value slice) walks the chunks
 //       forward, storing each H_c (operand type, transposed) and the final state S_L; with
 //       FWD = false it walks them backward with (q (.) a, dO) in place of
-//       (k (.) e^{G_end - G}, v), storing each dH_c and returning dS_0.
+//       (k (.) e^{G_end - G}, v), storing each dH_c and returning dS_0. Both
+//       scans run in one launch.
 //   bwd_dqkv_kernel  one workgroup (8 waves) per (head, chunk), fully parallel:
 //       waves w, w+4 own query block w (dq) and key block w (dk, dv), each for
 //       half of the output columns. Products are
@@ -45,7 +46,7 @@ namespace la {
 // are loaded into registers while the current chunk is folded in; every wave
 // scans the chunk's gates itself (rows in lanes), so no barrier guards them.
 template <typename TI, int DK, int DVT, bool FWD, bool DECAY>
-__global__ void __launch_bounds__(256) state_scan_kernel(BwdArgs a) {
+__device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &a, int blk) {
     using TM = typename OpOf<TI>::type;
     using MF = Mfma<TM>;
     using frag = typename MF::frag;
@@ -60,7 +61,7 @@ __global__ void __launch_bounds__(256) state_scan_kernel(BwdArgs a) {
     __shared__ __align__(16) TM Ys[C * PY];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
-    const int bh = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
+    const int bh = blk / a.nsplit, split = blk % a.nsplit;
     const int L = a.L, dv = a.dv, j0 = split * DVT, nchunks = (L + C - 1) / C;
     const TI *xg = (const TI *)(FWD ? a.k : a.q) + (size_t)bh * L * DK;
     const TI *yg = (const TI *)(FWD ? a.v : a.dout) + (size_t)bh * L * dv + j0;
@@ -183,6 +184,17 @@ __global__ void __launch_bounds__(256) state_scan_kernel(BwdArgs a) {
             }
         }
     }
+}
+
+// The two scans are independent; one launch runs both, the forward one on the
+// first BH * nsplit workgroups.
+template <typename TI, int DK, int DVT, bool DECAY>
+__global__ void __launch_bounds__(256) state_scans_kernel(BwdArgs a) {
+    const int per = a.BH * a.nsplit;
+    if ((int)blockIdx.x < per)
+        state_scan<TI, DK, DVT, true, DECAY>(a, blockIdx.x);
+    else
+        state_scan<TI, DK, DVT, false, DECAY>(a, blockIdx.x - per);
 }
 
 // ---------------------------------------------------------------------------
@@ -578,8 +590,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t st) {
     const int nchunks = (a.L + 63) / 64;
     BwdArgs b = a;
     b.nsplit = DV / DVT;
-    hipLaunchKernelGGL((state_scan_kernel<TI, DK, DVT, true, DECAY>), dim3(a.BH * b.nsplit), dim3(256), 0, st, b);
-    hipLaunchKernelGGL((state_scan_kernel<TI, DK, DVT, false, DECAY>), dim3(a.BH * b.nsplit), dim3(256), 0, st, b);
+    hipLaunchKernelGGL((state_scans_kernel<TI, DK, DVT, DECAY>), dim3(2 * a.BH * b.nsplit), dim3(256), 0, st, b);
     if (nchunks > 0)
         hipLaunchKernelGGL((bwd_dqkv_kernel<TI, DK, DV, DECAY>), dim3(a.BH * nchunks), dim3(512), 0, st, b);
     if (DECAY && nchunks > 0 && a.glg) hipLaunchKernelGGL((dgate_kernel<DK>), dim3(a.BH), dim3(256), 0, st, b);
