@@ -21,6 +21,9 @@
 // element per chunk plus 15 per channel, instead of one per (row, key, channel).
 // The diagonal score q_t . k_t carries no decay; it is taken in fp32 from the
 // inputs, so bf16's rounding only touches terms damped by at least one gate.
+// When a chunk's rebased operands all stay below 2^14 (the common case for
+// moderate gates), they are stored and multiplied as fp16 instead, with 8x
+// finer rounding; a workgroup vote picks the type per chunk.
 //
 // Mapping. One workgroup (8 waves) owns one (batch*head, DVT-column value
 // slice) and walks the chunks in order with its d_k x DVT slice of S in fp32
@@ -78,6 +81,8 @@ template <typename TI, int DK, int DVT> struct VdCfg {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
+template <typename T> struct type_tag { using type = T; };
+
 // factor row of D_ij, i > j
 __device__ constexpr int d_row(int i, int j) { return j == 0 ? i - 1 : (j == 1 ? i + 1 : 5); }
 
@@ -115,6 +120,7 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
     TM *Vs = reinterpret_cast<TM *>(smem + Cfg::oV);
     TM *St = reinterpret_cast<TM *>(smem + Cfg::oSt);
     float *QK = reinterpret_cast<float *>(smem + Cfg::oQK);  // q_t . k_t per row
+    __shared__ float Vote[8];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
     const int vid = xcd_virtual_block();
@@ -235,6 +241,7 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
         __syncthreads();
 
         // ---- 2. operand rows from this thread's q and k segments
+        float qh[NQS][8], kb[NQS][8], big = 0.f;
 #pragma unroll
         for (int m = 0; m < NQS; ++m) {
             const int sid = tid + 512 * m;
@@ -266,18 +273,44 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int off = 1; off < SEGQ; off <<= 1) qk += __shfl_xor(qk, off, 64);
                 if (c0 == 0) QK[row] = qk;
-                float qh[8], qe[8], kb[8], kt[8];
+                float qe[8], kt[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    qh[e] = q8[e] * __expf(gr[e] - gm[e]);
-                    qe[e] = qh[e] * fq[e];
-                    kb[e] = k8[e] * __expf(gm[e] - gr[e]);
-                    kt[e] = kb[e] * fk[e];
+                    qh[m][e] = q8[e] * __expf(gr[e] - gm[e]);
+                    qe[e] = qh[m][e] * fq[e];
+                    kb[m][e] = k8[e] * __expf(gm[e] - gr[e]);
+                    kt[e] = kb[m][e] * fk[e];
+                    big = fmaxf(big, fmaxf(fabsf(qh[m][e]), fabsf(kb[m][e])));
                 }
-                st8<TS>(&Qh[row * PQ + c0], qh);
                 st8<TM>(&Qe[row * PQ + c0], qe);
-                st8<TS>(&Kb[row * PQ + c0], kb);
                 st8<TM>(&Kt[row * PK + c0], kt);
+            }
+        }
+        // fp16 score operands when every rebased value of the chunk fits fp16 with
+        // headroom (then 8x finer rounding than bf16), else bf16: a workgroup vote
+        bool sf16 = false;
+        if constexpr (H) {
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) big = fmaxf(big, __shfl_xor(big, off, 64));
+            if (lane == 0) Vote[wv] = big;
+            __syncthreads();
+            float all = Vote[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) all = fmaxf(all, Vote[i]);
+            sf16 = all < 16384.f;
+        }
+#pragma unroll
+        for (int m = 0; m < NQS; ++m) {
+            const int sid = tid + 512 * m;
+            if (sid < C * SEGQ) {
+                const int row = sid / SEGQ, c0 = 8 * (sid % SEGQ);
+                if (sf16) {
+                    st8<f16>(reinterpret_cast<f16 *>(&Qh[row * PQ + c0]), qh[m]);
+                    st8<f16>(reinterpret_cast<f16 *>(&Kb[row * PQ + c0]), kb[m]);
+                } else {
+                    st8<TS>(&Qh[row * PQ + c0], qh[m]);
+                    st8<TS>(&Kb[row * PQ + c0], kb[m]);
+                }
             }
         }
         if (c + 1 < nchunks) load_qk(c + 1);
@@ -295,25 +328,39 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
                 const int trb = tix < 1 ? 0 : tix < 3 ? 1 : tix < 6 ? 2 : 3;
                 const int tsb = tix - trb * (trb + 1) / 2;
                 const float *Dr = &F[(Cfg::FD + (tsb < trb ? d_row(trb, tsb) : 0)) * DK];
-                f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+                // the tile in score operand type T (stored in the 2- or 4-byte tiles)
+                auto score = [&](auto t_tag) __attribute__((always_inline)) -> f32x4 {
+                    using T = typename decltype(t_tag)::type;
+                    using M = Mfma<T>;
+                    const T *Kbt = reinterpret_cast<const T *>(Kb);
+                    const T *Qht = reinterpret_cast<const T *>(Qh);
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const int col = g * (DK / 4) + ks * E;
-                    sfrag kf = ld_frag<TS>(&Kb[(tsb * 16 + n) * PQ + col]);
-                    if (tsb < trb) {
-                        if constexpr (E == 8) {
-                            const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&Dr[col]);
-                            const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&Dr[col + 4]);
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const int col = g * (DK / 4) + ks * E;
+                        typename M::frag kf = ld_frag<T>(&Kbt[(tsb * 16 + n) * PQ + col]);
+                        if (tsb < trb) {
+                            if constexpr (E == 8) {
+                                const f32x4 d0 = *reinterpret_cast<const f32x4 *>(&Dr[col]);
+                                const f32x4 d1 = *reinterpret_cast<const f32x4 *>(&Dr[col + 4]);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                kf[e] = from_f32<TS>(to_f32<TS>(kf[e]) * d0[e]);
-                                kf[4 + e] = from_f32<TS>(to_f32<TS>(kf[4 + e]) * d1[e]);
+                                for (int e = 0; e < 4; ++e) {
+                                    kf[e] = from_f32<T>(to_f32<T>(kf[e]) * d0[e]);
+                                    kf[4 + e] = from_f32<T>(to_f32<T>(kf[4 + e]) * d1[e]);
+                                }
+                            } else {
+                                kf = kf * Dr[col];
                             }
-                        } else {
-                            kf = kf * Dr[col];
                         }
+                        acc = M::mma(kf, ld_frag<T>(&Qht[(trb * 16 + n) * PQ + col]), acc);
                     }
-                    sc = MS::mma(kf, ld_frag<TS>(&Qh[(trb * 16 + n) * PQ + col]), sc);
+                    return acc;
+                };
+                f32x4 sc;
+                if constexpr (H) {
+                    sc = sf16 ? score(type_tag<f16>{}) : score(type_tag<TS>{});
+                } else {
+                    sc = score(type_tag<TS>{});
                 }
                 if (tsb == trb) {  // causal mask; the diagonal itself is exact
                     const float qk = QK[trb * 16 + n];
