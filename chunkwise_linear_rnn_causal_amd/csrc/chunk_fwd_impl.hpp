@@ -67,33 +67,65 @@ template <typename TM, int W, int PAD> struct RowTile {
 };
 
 // ---------------------------------------------------------------------------
-// Contiguous ranges of state tiles per wave, filled greedily so that waves with
-// fewer score tiles take more state tiles.
-// Waves w and w + 4 of a workgroup share a SIMD, so with C/8 waves the second
-// half of the value columns of row block rb goes to wave 2*NRB - 1 - rb: every
-// SIMD then carries one light and one heavy row block.
-template <int NW, int NRB> struct Roles {
-    static constexpr int MODE = (NW == NRB) ? 0 : (NW == 2 * NRB) ? 1 : (2 * NW == NRB) ? 2 : -1;
-    static_assert(MODE >= 0, "wave count must be C/16, C/8 or C/32");
+// Wave roles. Modes 0-2 give every wave output rows, state tiles and staging:
+//   0: C/16 waves, one 16-row block each;
+//   1: C/8 waves, wave pairs split the value columns of one row block. Waves w
+//      and w + 4 of a workgroup share a SIMD, so the second half of row block rb
+//      goes to wave 2*NRB - 1 - rb: every SIMD carries one light and one heavy
+//      row block;
+//   2: C/32 waves, each with a row block and its mirror.
+// Mode 3 (SPLIT, C/8 waves) separates the two chains of a chunk: waves 0..NRB-1
+// each compute all value columns of one row block (no score tile is computed
+// twice), while waves NRB.. stage the tiles, prefetch, update the state and the
+// normalizer and build the gate tables, so the state work runs beside the rows
+// instead of after them.
+template <int NW, int NRB, bool SPLIT = false> struct Roles {
+    static constexpr int MODE =
+        SPLIT ? 3 : (NW == NRB) ? 0 : (NW == 2 * NRB) ? 1 : (2 * NW == NRB) ? 2 : -1;
+    static_assert(MODE >= 0 && (MODE != 3 || NW == 2 * NRB), "wave count must be C/16, C/8 or C/32");
     static constexpr int RBW = MODE == 2 ? 2 : 1;
+    static constexpr bool rows(int w) { return MODE != 3 || w < NRB; }    // computes output rows
+    static constexpr bool stages(int w) { return MODE != 3 || w >= NRB; } // stages tiles, owns state tiles
     static constexpr int rb(int w, int i) {
-        return MODE == 2 ? (i == 0 ? w : NRB - 1 - w) : MODE == 1 ? (w < NRB ? w : 2 * NRB - 1 - w) : w;
+        return MODE == 2 ? (i == 0 ? w : NRB - 1 - w)
+             : MODE == 1 ? (w < NRB ? w : 2 * NRB - 1 - w)
+             : MODE == 3 ? (w < NRB ? w : 0) : w;
     }
     static constexpr int half(int w) { return MODE == 1 ? w / NRB : 0; }
-    // relative score work of wave w (16 x 16 score tiles)
-    static constexpr int score_tiles(int w) { return MODE == 2 ? NRB + 1 : rb(w, 0) + 1; }
+    // relative score work of wave w (16 x 16 score tiles); mode 3 keeps state
+    // tiles off the row waves
+    static constexpr int score_tiles(int w) {
+        return MODE == 3 ? (w < NRB ? 1 << 20 : 0) : MODE == 2 ? NRB + 1 : rb(w, 0) + 1;
+    }
+    static constexpr int NWS = MODE == 3 ? NW - NRB : NW;  // staging waves
+    static constexpr int WS0 = MODE == 3 ? NRB : 0;        // first staging wave
+    static constexpr int ZW = WS0;                         // wave that carries the normalizer
+    // owner of the normalizer's 16-channel block ti (mode 3 spreads the blocks
+    // over the staging waves), and the number of blocks wave w owns
+    static constexpr int zowner(int ti) { return MODE == 3 ? WS0 + ti % NWS : ZW; }
+    static constexpr int zunits(int w, int nti) {
+        int u = 0;
+        for (int ti = 0; ti < nti; ++ti) u += zowner(ti) == w;
+        return u;
+    }
+    static constexpr int GW = MODE == 3 ? NW - 1 : 0;      // wave that builds the gate tables
 };
+
+// Contiguous ranges of state tiles per wave, filled greedily so that waves with
+// less other work take more state tiles.
 
 template <int NTT, int NW> struct TileSplit {
     int start[NW];
     int cnt[NW];
     int maxcnt;
 };
-template <int NTT, int NW, int NRB>
-constexpr TileSplit<NTT, NW> make_tile_split(int extra0) {
+// extraz: normalizer channel blocks (each weighs one state tile).
+template <int NTT, int NW, int NRB, bool SPLIT>
+constexpr TileSplit<NTT, NW> make_tile_split(int extraz) {
+    using R = Roles<NW, NRB, SPLIT>;
     TileSplit<NTT, NW> t{};
     for (int w = 0; w < NW; ++w) t.cnt[w] = 0;
-    auto load = [&](int w) { return Roles<NW, NRB>::score_tiles(w) + t.cnt[w] + (w == 0 ? extra0 : 0); };
+    auto load = [&](int w) { return R::score_tiles(w) + t.cnt[w] + R::zunits(w, extraz); };
     for (int i = 0; i < NTT; ++i) {
         int best = 0;
         for (int w = 1; w < NW; ++w)
@@ -186,12 +218,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     using QT = typename Cfg::QT;
     using KT = typename Cfg::KT;
     using VT = typename Cfg::VT;
-    using Geo = StageGeo<TI, DK, DVT, C, NW, VAR != V_GDN>;
     constexpr bool H = sizeof(TM) == 2;
     constexpr int NT = NW * 64;           // threads
     constexpr int E = MF::E;
     constexpr int NRB = C / 16;           // 16-row blocks per chunk
-    using R = Roles<NW, NRB>;
+    // C/8 waves with double-buffered tiles split the roles (mode 3)
+    using R = Roles<NW, NRB, NW == 2 * NRB && Cfg::DB>;
+    using Geo = StageGeo<TI, DK, DVT, C, R::NWS, VAR != V_GDN>;
     constexpr bool DECAYED = Cfg::DECAYED;
     constexpr bool DB = Cfg::DB;
     constexpr int NTB = Cfg::NTB;
@@ -204,11 +237,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     constexpr int NQR = DK / 32;          // 8-element runs of one lane's channels (DK/4)
     constexpr int EPS = Geo::EPS;
     constexpr int NSLOT = Geo::NSLOT;
-    constexpr int ZW = 0;                 // wave that carries the normalizer
-    constexpr auto TS = make_tile_split<NTI * NTJ, NW, NRB>(VAR == V_NORM ? NTI : 0);
+    constexpr int GW = R::GW;             // wave that builds the gate tables
+    constexpr int WS0 = R::WS0, NWS = R::NWS;
+    constexpr auto TS = make_tile_split<NTI * NTJ, NW, NRB, R::MODE == 3>(VAR == V_NORM ? NTI : 0);
     constexpr int NTS = TS.maxcnt;        // state tiles per wave (at most)
     static_assert(NTJW >= 1 && (R::MODE != 1 || NTJ % 2 == 0), "value slice too narrow for the roles");
-    static_assert(VAR != V_GDN || (R::MODE <= 1 && NRB == 4), "delta rule: one U row block per wave (pair)");
+    static_assert(VAR != V_GDN || ((R::MODE <= 1 || R::MODE == 3) && NRB == 4),
+                  "delta rule: one U row block per wave (pair)");
 
     // Tile sets: [set][Q | K | V | wV | S_prev^T]. Gate tables per buffer:
     // [0] G_s, [1] exp(G_s), [2] w_s = exp(g_C - G_s), [3] exp(G_{end of s's
@@ -260,7 +295,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             for (int e = 0; e < 4; ++e) Sacc[m][e] = sp[(size_t)e * dv];
         }
     }
-    // Normalizer z in accumulator layout (wave ZW): lane (g, n) of tile ti holds
+    // Normalizer z in accumulator layout (block ti in wave R::zowner(ti)): lane (g, n) of tile ti holds
     // z[ti*16 + 4g + e] (every column n alike).
     f32x4 zacc[VAR == V_NORM ? NTI : 1];
     if constexpr (VAR == V_NORM) {
@@ -286,8 +321,11 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 
     // ---- registers of the next chunk(s): loads are issued one chunk ahead of
     // the staging that consumes them, so global latency overlaps the math.
-    uint4 pre[NSLOT];
-    float gpre[PER];
+    // Two register sets when double buffered: the loads of chunk c+3 are issued
+    // while chunk c is computed, two chunks ahead of their staging.
+    constexpr int NPS = DB ? 2 : 1;
+    uint4 pre[NPS][NSLOT];
+    float gpre[NPS][PER];
     Raw8<TM> wpre[NQR];           // gated delta: W row of this wave's U row block
     f32x4 upre[NTJW];             // gated delta: U~ of this wave's U tiles (transposed layout)
     const float *gsrc = lgg ? lgg : reinterpret_cast<const float *>(qg);
@@ -304,32 +342,38 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // Loads of chunk c: the log-gates, slot M of wave W, and the delta-rule W row
     // and U~. FULL: all rows of chunk c are valid (scalar base + lane offset);
     // otherwise rows are clamped to L - 1 and zeroed when staged.
-    auto load_gates = [&](int c, auto full_tag) __attribute__((always_inline)) {
+    auto load_gates = [&](int c, auto full_tag, auto set_tag) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full_tag)::value;
+        constexpr int PS = decltype(set_tag)::value;
         if constexpr (DECAYED) {
 #pragma unroll
             for (int p = 0; p < PER; ++p) {
                 const int t = c * C + lane * PER + p;
-                gpre[p] = gsrc[FULL ? t : min(t, L - 1)];
+                gpre[PS][p] = gsrc[FULL ? t : min(t, L - 1)];
             }
         }
     };
-    auto load_slot = [&](auto w_tag, auto m_tag, int c, auto full_tag) __attribute__((always_inline)) {
-        constexpr auto S = Geo::slot(decltype(w_tag)::value, decltype(m_tag)::value);
+    auto load_slot = [&](auto w_tag, auto m_tag, int c, auto full_tag, auto set_tag) __attribute__((always_inline)) {
+        constexpr int W = decltype(w_tag)::value;
+        constexpr int PS = decltype(set_tag)::value;
+        if constexpr (R::stages(W)) {
+        constexpr auto S = Geo::slot(W - WS0, decltype(m_tag)::value);
         constexpr int M = decltype(m_tag)::value;
         constexpr bool FULL = decltype(full_tag)::value;
         const TI *tb = S.kind == 0 ? qg : (S.kind == 1 ? kg : vg);
         const int pitch = S.kind == 2 ? dv : DK;
         if constexpr (FULL) {
             const char *base = reinterpret_cast<const char *>(tb + (size_t)(c * C + S.ii * S.rpi) * pitch);
-            pre[M] = *reinterpret_cast<const uint4 *>(base + (S.kind == 2 ? off_v : off_qk));
+            pre[PS][M] = *reinterpret_cast<const uint4 *>(base + (S.kind == 2 ? off_v : off_qk));
         } else {
             const int t = min(c * C + S.ii * S.rpi + lane / S.seg, L - 1);
-            pre[M] = *reinterpret_cast<const uint4 *>(tb + t * pitch + (lane % S.seg) * EPS);
+            pre[PS][M] = *reinterpret_cast<const uint4 *>(tb + t * pitch + (lane % S.seg) * EPS);
+        }
         }
     };
     auto load_wu = [&](int c) __attribute__((always_inline)) {
         if constexpr (VAR == V_GDN) {
+            if (!R::rows(wv)) return;
             const int srow = c * C + (wv % NRB) * 16 + n;  // W and U~ have Lp rows: always in range
 #pragma unroll
             for (int i = 0; i < NQR; ++i) wpre[i] = ld_raw8<TM>(wg + srow * DK + g * (DK / 4) + 8 * i);
@@ -342,12 +386,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     };
 
     // Gate tables of chunk c into buffer buf, from the prefetched log-gates.
-    // Called by wave 0 only (wave-uniform), ahead of the chunk's staging.
-    auto gate_tables = [&](int c, int buf) __attribute__((always_inline)) {
+    // Called by the gate-table wave GW only (wave-uniform), ahead of the chunk's staging.
+    auto gate_tables = [&](int c, int buf, auto set_tag) __attribute__((always_inline)) {
+        constexpr int PS = decltype(set_tag)::value;
         const int t0 = c * C;
         float *T = Tg + buf * 4 * C;
         if constexpr (PER == 1) {
-            const float x = (lgg && t0 + lane < L) ? gpre[0] : 0.f;
+            const float x = (lgg && t0 + lane < L) ? gpre[PS][0] : 0.f;
             const float G = wave_inclusive_sum(x);
             const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
             // G at the last token of this lane's 16-token block (lanes 15, 31, 47, 63)
@@ -365,7 +410,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             float run = 0.f;
 #pragma unroll
             for (int p = 0; p < PER; ++p) {
-                run += (lgg && t0 + lane * PER + p < L) ? gpre[p] : 0.f;
+                run += (lgg && t0 + lane * PER + p < L) ? gpre[PS][p] : 0.f;
                 gl[p] = run;
             }
             const float incl = wave_inclusive_sum(run);
@@ -426,14 +471,16 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // Stage slot M of chunk cs (in registers) into tile set X: convert to the
     // operand type and write row-major; V also scaled by w_s of chunk cs.
     // CHECK: rows past L are zeroed.
-    auto stage_slot = [&](auto w_tag, auto m_tag, int cs, TM *X, auto check_tag) __attribute__((always_inline)) {
-        constexpr auto S = Geo::slot(decltype(w_tag)::value, decltype(m_tag)::value);
+    auto stage_slot = [&](auto w_tag, auto m_tag, int cs, TM *X, auto check_tag, auto set_tag) __attribute__((always_inline)) {
+        constexpr int W = decltype(w_tag)::value;
+        constexpr int PS = decltype(set_tag)::value;
+        constexpr auto S = Geo::slot(R::stages(W) ? W - WS0 : 0, decltype(m_tag)::value);
         constexpr int M = decltype(m_tag)::value;
         constexpr bool CHECK = decltype(check_tag)::value;
-        if constexpr (S.real) {
+        if constexpr (R::stages(W) && S.real) {
             const int r = S.ii * S.rpi + lane / S.seg, seg = lane % S.seg;
             const bool valid = !CHECK || cs * C + r < L;
-            const uint32_t w4[4] = {pre[M].x, pre[M].y, pre[M].z, pre[M].w};
+            const uint32_t w4[4] = {pre[PS][M].x, pre[PS][M].y, pre[PS][M].z, pre[PS][M].w};
             if constexpr (H) {
                 f16x8 h;
 #pragma unroll
@@ -476,20 +523,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     auto slot_uniform = [&](auto m_tag) __attribute__((always_inline)) {
         constexpr int M = decltype(m_tag)::value;
         constexpr auto S0 = Geo::slot(0, M);
-        constexpr auto S1 = Geo::slot(NW - 1, M);
+        constexpr auto S1 = Geo::slot(NWS - 1, M);
         return std::bool_constant<S0.kind == S1.kind>{};
     };
-    auto stage_any = [&](auto m_tag, int cs, TM *X, auto check_tag) __attribute__((always_inline)) {
+    auto stage_any = [&](auto m_tag, int cs, TM *X, auto check_tag, auto set_tag) __attribute__((always_inline)) {
         constexpr int M = decltype(m_tag)::value;
+        constexpr int PS = decltype(set_tag)::value;
         constexpr bool CHECK = decltype(check_tag)::value;
         if constexpr (decltype(slot_uniform(m_tag))::value) {
             constexpr auto S = Geo::slot(0, M);
-            const int i = wv + NW * M;
-            if (i < Geo::NI) {
+            const int i = (wv - WS0) + NWS * M;
+            if (wv >= WS0 && i < Geo::NI) {
                 const int ii = S.kind == 2 ? i - 2 * Geo::NIQ : i - S.kind * Geo::NIQ;
                 const int r = ii * S.rpi + lane / S.seg, seg = lane % S.seg;
                 const bool valid = !CHECK || cs * C + r < L;
-                const uint32_t w4[4] = {pre[M].x, pre[M].y, pre[M].z, pre[M].w};
+                const uint32_t w4[4] = {pre[PS][M].x, pre[PS][M].y, pre[PS][M].z, pre[PS][M].w};
                 if constexpr (H) {
                     f16x8 h;
 #pragma unroll
@@ -525,28 +573,30 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                 }
             }
         } else {
-            for_wave([&](auto w_tag) __attribute__((always_inline)) { stage_slot(w_tag, m_tag, cs, X, check_tag); });
+            for_wave([&](auto w_tag) __attribute__((always_inline)) { stage_slot(w_tag, m_tag, cs, X, check_tag, set_tag); });
         }
     };
-    auto load_any = [&](auto m_tag, int c, auto full_tag) __attribute__((always_inline)) {
+    auto load_any = [&](auto m_tag, int c, auto full_tag, auto set_tag) __attribute__((always_inline)) {
         constexpr int M = decltype(m_tag)::value;
+        constexpr int PS = decltype(set_tag)::value;
         constexpr bool FULL = decltype(full_tag)::value;
         if constexpr (decltype(slot_uniform(m_tag))::value) {
+            if (wv < WS0) return;
             constexpr auto S = Geo::slot(0, M);
-            int i = wv + NW * M;
+            int i = (wv - WS0) + NWS * M;
             i = i < Geo::NI ? i : Geo::NI - 1;  // repeat the last load past the end
             const int ii = S.kind == 2 ? i - 2 * Geo::NIQ : i - S.kind * Geo::NIQ;
             const TI *tb = S.kind == 0 ? qg : (S.kind == 1 ? kg : vg);
             const int pitch = S.kind == 2 ? dv : DK;
             if constexpr (FULL) {
                 const char *base = reinterpret_cast<const char *>(tb + (size_t)(c * C + ii * S.rpi) * pitch);
-                pre[M] = *reinterpret_cast<const uint4 *>(base + (S.kind == 2 ? off_v : off_qk));
+                pre[PS][M] = *reinterpret_cast<const uint4 *>(base + (S.kind == 2 ? off_v : off_qk));
             } else {
                 const int t = min(c * C + ii * S.rpi + lane / S.seg, L - 1);
-                pre[M] = *reinterpret_cast<const uint4 *>(tb + t * pitch + (lane % S.seg) * EPS);
+                pre[PS][M] = *reinterpret_cast<const uint4 *>(tb + t * pitch + (lane % S.seg) * EPS);
             }
         } else {
-            for_wave([&](auto w_tag) __attribute__((always_inline)) { load_slot(w_tag, m_tag, c, full_tag); });
+            for_wave([&](auto w_tag) __attribute__((always_inline)) { load_slot(w_tag, m_tag, c, full_tag, set_tag); });
         }
     };
 
@@ -588,6 +638,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     auto gdn_u = [&](TM *X, const float *T, const frag (&wf)[VAR == V_GDN ? NKS : 1],
                      const f32x4 (&ucur)[VAR == V_GDN ? NTJW : 1]) __attribute__((always_inline)) {
         if constexpr (VAR == V_GDN) {
+            if (!R::rows(wv)) return;
             const int ub = wv % NRB;
             const int s = ub * 16 + n;
             const float ws = T[2 * C + s];
@@ -792,6 +843,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // The rows of wave W.
     auto rows_of = [&](auto w_tag, int c, const TM *X, const float *T, auto check_tag) __attribute__((always_inline)) {
         constexpr int W = decltype(w_tag)::value;
+        if constexpr (!R::rows(W)) return;
         row_block(std::integral_constant<int, R::rb(W, 0)>{}, std::integral_constant<int, R::half(W) * NTJW>{}, c,
                   X, T, check_tag);
         if constexpr (R::RBW == 2)
@@ -801,7 +853,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 
     // State update S <- exp(g_C) S + K^T (w (.) V) of wave W's tiles from tile set
     // X, both operands read from the row-major tiles with the token index in the
-    // K slots; then the normalizer carry z_next = z_prev + K^T 1 (wave ZW).
+    // K slots; then the normalizer carry z_next = z_prev + K^T 1 (each channel
+    // block in its owner wave).
     auto state_update = [&](auto w_tag, int c, const TM *X, float eg) __attribute__((always_inline)) {
         constexpr int W = decltype(w_tag)::value;
         if constexpr (DECAYED) {
@@ -817,7 +870,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             for (int ks = 0; ks < NTK; ++ks)
                 Sacc[m] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), tok_frag(VW, PV{}, ks, tj * 16), Sacc[m]);
         }
-        if constexpr (VAR == V_NORM && W == ZW) {
+        if constexpr (VAR == V_NORM && R::zunits(W, NTI) > 0) {
             const int zn = ((c + 1) & 1) * (H ? 2 * DK : DK);
             frag ones;
             if constexpr (E == 8) {
@@ -826,39 +879,45 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             } else {
                 ones = 1.0f;
             }
+            static_for<NTI>([&](auto ti_tag) __attribute__((always_inline)) {
+                constexpr int ti = decltype(ti_tag)::value;
+                if constexpr (R::zowner(ti) == W) {
 #pragma unroll
-            for (int ti = 0; ti < NTI; ++ti) {
+                    for (int ks = 0; ks < NTK; ++ks) zacc[ti] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), ones, zacc[ti]);
+                    if (n == 0) {
+                        if constexpr (H) {
+                            f32x4 lo;
 #pragma unroll
-                for (int ks = 0; ks < NTK; ++ks) zacc[ti] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), ones, zacc[ti]);
-                if (n == 0) {
-                    if constexpr (H) {
-                        f32x4 lo;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) lo[e] = zacc[ti][e] - to_f32<TM>(from_f32<TM>(zacc[ti][e]));
-                        st4<TM>(&Zs[zn + ti * 16 + 4 * g], zacc[ti]);
-                        st4<TM>(&Zs[zn + DK + ti * 16 + 4 * g], lo);
-                    } else {
-                        *reinterpret_cast<f32x4 *>(&Zs[zn + ti * 16 + 4 * g]) = zacc[ti];
+                            for (int e = 0; e < 4; ++e) lo[e] = zacc[ti][e] - to_f32<TM>(from_f32<TM>(zacc[ti][e]));
+                            st4<TM>(&Zs[zn + ti * 16 + 4 * g], zacc[ti]);
+                            st4<TM>(&Zs[zn + DK + ti * 16 + 4 * g], lo);
+                        } else {
+                            *reinterpret_cast<f32x4 *>(&Zs[zn + ti * 16 + 4 * g]) = zacc[ti];
+                        }
                     }
                 }
-            }
+            });
         }
     };
 
     // ---- double-buffered chunk: tile set b = c & 1 holds chunk c; chunk c+1 is
     // staged into set b ^ 1 right after this wave's rows are done (no barrier in
-    // between), and each slot is refilled with chunk c+2. FAST: chunks c .. c+2
-    // are all full.
-    auto chunk_db = [&](int c, auto fast_tag) __attribute__((always_inline)) {
+    // between) from register set (c+1) & 1, which is then refilled with chunk
+    // c+3 (and the log-gates likewise). P = c & 1 at compile time. FAST: chunks
+    // c .. c+3 are all full.
+    auto chunk_db = [&](int c, auto fast_tag, auto par_tag) __attribute__((always_inline)) {
         constexpr bool FAST = decltype(fast_tag)::value;
+        constexpr int P = decltype(par_tag)::value;
+        using Cur = std::integral_constant<int, P>;       // register set of chunks c, c+2
+        using Nxt = std::integral_constant<int, P ^ 1>;   // register set of chunks c+1, c+3
         using Check = std::bool_constant<!FAST>;
-        TM *X = Tiles + (c & 1) * Cfg::SET, *Xn = Tiles + ((c + 1) & 1) * Cfg::SET;
+        TM *X = Tiles + P * Cfg::SET, *Xn = Tiles + (P ^ 1) * Cfg::SET;
         const float *T = Tg + (c % NTB) * 4 * C;
         __syncthreads();  // chunk c staged, its gate tables and S_prev visible; chunk c-1 done
         if constexpr (FAST) {
-            load_gates(c + 2, std::true_type{});
+            load_gates(c + 3, std::true_type{}, Nxt{});
         } else {
-            if (c + 2 < nchunks) load_gates(c + 2, std::false_type{});
+            if (c + 3 < nchunks) load_gates(c + 3, std::false_type{}, Nxt{});
         }
         frag wf[VAR == V_GDN ? NKS : 1];
         f32x4 ucur[VAR == V_GDN ? NTJW : 1];
@@ -878,11 +937,11 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         for_wave([&](auto w_tag) __attribute__((always_inline)) { rows_of(w_tag, c, X, T, Check{}); });
         if (next) {
             static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
-                stage_any(m_tag, c + 1, Xn, Check{});
+                stage_any(m_tag, c + 1, Xn, Check{}, Nxt{});
                 if constexpr (FAST) {
-                    load_any(m_tag, c + 2, std::true_type{});
+                    load_any(m_tag, c + 3, std::true_type{}, Nxt{});
                 } else {
-                    if (c + 2 < nchunks) load_any(m_tag, c + 2, std::false_type{});
+                    if (c + 3 < nchunks) load_any(m_tag, c + 3, std::false_type{}, Nxt{});
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -892,7 +951,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             if (next) write_sts(w_tag, Xn);
         });
         if constexpr (DECAYED) {
-            if (wv == 0 && (FAST || c + 2 < nchunks)) gate_tables(c + 2, (c + 2) % NTB);
+            if (wv == GW && (FAST || c + 2 < nchunks)) gate_tables(c + 2, (c + 2) % NTB, Cur{});
         }
     };
 
@@ -904,18 +963,19 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         TM *X = Tiles;
         const float *T = Tg + (c % NTB) * 4 * C;
         __syncthreads();  // previous chunk done with every tile; gate tables visible
+        using S0 = std::integral_constant<int, 0>;
         if constexpr (FAST) {
-            load_gates(c + 1, std::true_type{});
+            load_gates(c + 1, std::true_type{}, S0{});
         } else {
-            if (c + 1 < nchunks) load_gates(c + 1, std::false_type{});
+            if (c + 1 < nchunks) load_gates(c + 1, std::false_type{}, S0{});
         }
         for_wave([&](auto w_tag) __attribute__((always_inline)) { write_sts(w_tag, X); });
         static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
-            stage_any(m_tag, c, X, Check{});
+            stage_any(m_tag, c, X, Check{}, S0{});
             if constexpr (FAST) {
-                load_any(m_tag, c + 1, std::true_type{});
+                load_any(m_tag, c + 1, std::true_type{}, S0{});
             } else {
-                if (c + 1 < nchunks) load_any(m_tag, c + 1, std::false_type{});
+                if (c + 1 < nchunks) load_any(m_tag, c + 1, std::false_type{}, S0{});
             }
             __builtin_amdgcn_sched_barrier(0);
         });
@@ -937,7 +997,70 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             state_update(w_tag, c, X, eg);
         });
         if constexpr (DECAYED) {
-            if (wv == 0 && (FAST || c + 1 < nchunks)) gate_tables(c + 1, (c + 1) % NTB);
+            if (wv == GW && (FAST || c + 1 < nchunks)) gate_tables(c + 1, (c + 1) % NTB, S0{});
+        }
+    };
+
+    // ---- split roles (mode 3). Each role runs its own straight-line loop over
+    // the chunks (one dispatch on the wave index outside the loop), so every
+    // wait count stays exact; both roles execute the same barriers: one in the
+    // prologue and one per chunk (two for the delta rule).
+    // Row wave, chunk c: the outputs of its row block (delta rule: first its
+    // U rows, then a barrier).
+    auto row_iter = [&](auto w_tag, int c, auto check_tag) __attribute__((always_inline)) {
+        const TM *X = Tiles + (c & 1) * Cfg::SET;
+        const float *T = Tg + (c % NTB) * 4 * C;
+        __syncthreads();  // chunk c staged, its gate tables and S_prev visible
+        if constexpr (VAR == V_GDN) {
+            frag wf[NKS];
+            f32x4 ucur[NTJW];
+            take_wu(wf, ucur);
+            if (c + 1 < nchunks) load_wu(c + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            gdn_u(const_cast<TM *>(X), T, wf, ucur);
+            __syncthreads();  // U rows visible to the state waves
+        }
+        rows_of(w_tag, c, X, T, check_tag);
+    };
+    // State wave, chunk c (P = c & 1 at compile time): stage chunk c+1 into the
+    // other tile set from register set P^1 and refill that set with chunk c+3;
+    // then S <- update with chunk c, S_next^T into the other set, and the gate
+    // tables of chunk c+2 (log-gates of chunk c+3 prefetched). FAST: chunks
+    // c .. c+3 are full. The other tile set was last read by the rows of chunk
+    // c-1, which the barrier has retired.
+    auto state_iter = [&](auto w_tag, int c, auto fast_tag, auto par_tag) __attribute__((always_inline)) {
+        constexpr int W = decltype(w_tag)::value;
+        constexpr bool FAST = decltype(fast_tag)::value;
+        constexpr int P = decltype(par_tag)::value;
+        using Cur = std::integral_constant<int, P>;
+        using Nxt = std::integral_constant<int, P ^ 1>;
+        using Check = std::bool_constant<!FAST>;
+        const TM *X = Tiles + P * Cfg::SET;
+        TM *Xn = Tiles + (P ^ 1) * Cfg::SET;
+        __syncthreads();  // chunk c staged and visible; chunk c-1 done everywhere
+        if constexpr (FAST) {
+            load_gates(c + 3, std::true_type{}, Nxt{});
+        } else {
+            if (c + 3 < nchunks) load_gates(c + 3, std::false_type{}, Nxt{});
+        }
+        const bool next = FAST || c + 1 < nchunks;
+        if (next) {
+            static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                stage_slot(w_tag, m_tag, c + 1, Xn, Check{}, Nxt{});
+                if constexpr (FAST) {
+                    load_slot(w_tag, m_tag, c + 3, std::true_type{}, Nxt{});
+                } else {
+                    if (c + 3 < nchunks) load_slot(w_tag, m_tag, c + 3, std::false_type{}, Nxt{});
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+        if constexpr (VAR == V_GDN) __syncthreads();  // U of chunk c visible
+        const float eg = DECAYED ? Tsc[c % NTB] : 1.f;
+        state_update(w_tag, c, X, eg);
+        if (next) write_sts(w_tag, Xn);
+        if constexpr (DECAYED) {
+            if (W == GW && (FAST || c + 2 < nchunks)) gate_tables(c + 2, (c + 2) % NTB, Cur{});
         }
     };
 
@@ -945,42 +1068,121 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // steady-state loop leave the same memory operations in flight (the wait
     // counts inside the loop are then exact and let output stores drain in the
     // background); the last chunks take the checked path.
-    if constexpr (DB) {
+    using Set0 = std::integral_constant<int, 0>;
+    using Set1 = std::integral_constant<int, 1 % NPS>;
+    if constexpr (R::MODE == 3) {
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        for_wave([&](auto w_tag) __attribute__((always_inline)) {
+            constexpr int W = decltype(w_tag)::value;
+            if constexpr (R::rows(W)) {
+                if (nchunks > 0) {
+                    load_wu(0);
+                    __syncthreads();  // prologue (the state waves' gate tables)
+                }
+                int c = 0;
+                for (; c < nfull; ++c) row_iter(w_tag, c, std::false_type{});
+                for (; c < nchunks; ++c) row_iter(w_tag, c, std::true_type{});
+            } else {
+                // chunks 0 and 1 into register sets 0 and 1; gate tables of
+                // chunks 0 and 1; chunk 0 staged and chunk 2 into set 0
+                if (nchunks > 0) {
+                    load_gates(0, std::false_type{}, Set0{});
+                    static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                        load_slot(w_tag, m_tag, 0, std::false_type{}, Set0{});
+                    });
+                    if (nchunks > 1) {
+                        load_gates(1, std::false_type{}, Set1{});
+                        static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                            load_slot(w_tag, m_tag, 1, std::false_type{}, Set1{});
+                        });
+                    }
+                    if constexpr (DECAYED) {
+                        if (W == GW) {
+                            gate_tables(0, 0, Set0{});
+                            if (nchunks > 1) gate_tables(1, 1, Set1{});
+                        }
+                        if (nchunks > 2) load_gates(2, std::false_type{}, Set0{});
+                    }
+                    __syncthreads();  // gate tables of chunk 0 visible
+                    static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                        stage_slot(w_tag, m_tag, 0, Tiles, std::true_type{}, Set0{});
+                        if (nchunks > 2) load_slot(w_tag, m_tag, 2, std::false_type{}, Set0{});
+                    });
+                    write_sts(w_tag, Tiles);
+                }
+                int c = 0;
+                if (nfull >= 4) {
+                    state_iter(w_tag, 0, std::true_type{}, P0{});
+                    for (c = 1; c + 1 <= nfull - 4; c += 2) {
+                        state_iter(w_tag, c, std::true_type{}, P1{});
+                        state_iter(w_tag, c + 1, std::true_type{}, P0{});
+                    }
+                }
+                for (; c < nchunks; ++c) {
+                    if (c & 1) {
+                        state_iter(w_tag, c, std::false_type{}, P1{});
+                    } else {
+                        state_iter(w_tag, c, std::false_type{}, P0{});
+                    }
+                }
+            }
+        });
+    } else if constexpr (DB) {
+        // chunks 0 and 1 into register sets 0 and 1; chunk 0 staged; chunk 2
+        // into set 0; gate tables of chunks 0 and 1 built.
         if (nchunks > 0) {
-            load_gates(0, std::false_type{});
+            load_gates(0, std::false_type{}, Set0{});
             static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
-                load_any(m_tag, 0, std::false_type{});
+                load_any(m_tag, 0, std::false_type{}, Set0{});
             });
+            if (nchunks > 1) {
+                load_gates(1, std::false_type{}, Set1{});
+                static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                    load_any(m_tag, 1, std::false_type{}, Set1{});
+                });
+            }
             load_wu(0);
             if constexpr (DECAYED) {
-                if (wv == 0) gate_tables(0, 0);
-                if (nchunks > 1) {
-                    load_gates(1, std::false_type{});
-                    if (wv == 0) gate_tables(1, 1);
+                if (wv == GW) {
+                    gate_tables(0, 0, Set0{});
+                    if (nchunks > 1) gate_tables(1, 1, Set1{});
                 }
+                if (nchunks > 2) load_gates(2, std::false_type{}, Set0{});
             }
             __syncthreads();  // gate tables of chunk 0 visible
             static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
-                stage_any(m_tag, 0, Tiles, std::true_type{});
-                if (nchunks > 1) load_any(m_tag, 1, std::false_type{});
+                stage_any(m_tag, 0, Tiles, std::true_type{}, Set0{});
+                if (nchunks > 2) load_any(m_tag, 2, std::false_type{}, Set0{});
             });
             for_wave([&](auto w_tag) __attribute__((always_inline)) { write_sts(w_tag, Tiles); });
         }
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
         int c = 0;
-        if (nfull >= 3) {
-            chunk_db(0, std::true_type{});
-            for (c = 1; c < nfull - 2; ++c) chunk_db(c, std::true_type{});
+        if (nfull >= 4) {
+            chunk_db(0, std::true_type{}, P0{});
+            for (c = 1; c + 1 <= nfull - 4; c += 2) {
+                chunk_db(c, std::true_type{}, P1{});
+                chunk_db(c + 1, std::true_type{}, P0{});
+            }
         }
-        for (; c < nchunks; ++c) chunk_db(c, std::false_type{});
+        for (; c < nchunks; ++c) {
+            if (c & 1) {
+                chunk_db(c, std::false_type{}, P1{});
+            } else {
+                chunk_db(c, std::false_type{}, P0{});
+            }
+        }
     } else {
         if (nchunks > 0) {
-            load_gates(0, std::false_type{});
+            load_gates(0, std::false_type{}, Set0{});
             static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
-                load_any(m_tag, 0, std::false_type{});
+                load_any(m_tag, 0, std::false_type{}, Set0{});
             });
             load_wu(0);
             if constexpr (DECAYED) {
-                if (wv == 0) gate_tables(0, 0);
+                if (wv == GW) gate_tables(0, 0, Set0{});
             }
         }
         int c = 0;
@@ -1003,11 +1205,14 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         }
     }
     if constexpr (VAR == V_NORM) {
-        if (a.z_out && split == 0 && wv == ZW && n == 0) {
+        if (a.z_out && split == 0 && n == 0) {
 #pragma unroll
-            for (int ti = 0; ti < NTI; ++ti)
+            for (int ti = 0; ti < NTI; ++ti) {
+                if (wv == R::zowner(ti)) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) a.z_out[(size_t)bh * DK + ti * 16 + 4 * g + e] = zacc[ti][e];
+                    for (int e = 0; e < 4; ++e) a.z_out[(size_t)bh * DK + ti * 16 + 4 * g + e] = zacc[ti][e];
+                }
+            }
         }
     }
 }
