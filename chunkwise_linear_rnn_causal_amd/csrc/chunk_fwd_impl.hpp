@@ -321,9 +321,12 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 
     // ---- registers of the next chunk(s): loads are issued one chunk ahead of
     // the staging that consumes them, so global latency overlaps the math.
-    // Two register sets when double buffered: the loads of chunk c+3 are issued
-    // while chunk c is computed, two chunks ahead of their staging.
-    constexpr int NPS = DB ? 2 : 1;
+    // Register sets of prefetched chunks. Double-buffered kernels with few
+    // loads per wave keep two: the loads of chunk c+3 are issued while chunk c
+    // is computed, two chunks ahead of their staging (short chunks need the
+    // deeper window to cover the memory latency). Otherwise one: chunk c+2.
+    constexpr int NPS = (DB && NSLOT <= 6) ? 2 : 1;
+    constexpr int AHEAD = NPS + 1;  // chunks between a load and the chunk being computed
     uint4 pre[NPS][NSLOT];
     float gpre[NPS][PER];
     Raw8<TM> wpre[NQR];           // gated delta: W row of this wave's U row block
@@ -902,22 +905,22 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 
     // ---- double-buffered chunk: tile set b = c & 1 holds chunk c; chunk c+1 is
     // staged into set b ^ 1 right after this wave's rows are done (no barrier in
-    // between) from register set (c+1) & 1, which is then refilled with chunk
-    // c+3 (and the log-gates likewise). P = c & 1 at compile time. FAST: chunks
-    // c .. c+3 are all full.
+    // between) from its register set, which is then refilled with chunk
+    // c+AHEAD (and the log-gates likewise). P = c & 1 at compile time. FAST:
+    // chunks c .. c+AHEAD are all full.
     auto chunk_db = [&](int c, auto fast_tag, auto par_tag) __attribute__((always_inline)) {
         constexpr bool FAST = decltype(fast_tag)::value;
         constexpr int P = decltype(par_tag)::value;
-        using Cur = std::integral_constant<int, P>;       // register set of chunks c, c+2
-        using Nxt = std::integral_constant<int, P ^ 1>;   // register set of chunks c+1, c+3
+        using Cur = std::integral_constant<int, P % NPS>;        // register set of chunk c+2
+        using Nxt = std::integral_constant<int, (P ^ 1) % NPS>;  // register set of chunks c+1, c+AHEAD
         using Check = std::bool_constant<!FAST>;
         TM *X = Tiles + P * Cfg::SET, *Xn = Tiles + (P ^ 1) * Cfg::SET;
         const float *T = Tg + (c % NTB) * 4 * C;
         __syncthreads();  // chunk c staged, its gate tables and S_prev visible; chunk c-1 done
         if constexpr (FAST) {
-            load_gates(c + 3, std::true_type{}, Nxt{});
+            load_gates(c + AHEAD, std::true_type{}, Nxt{});
         } else {
-            if (c + 3 < nchunks) load_gates(c + 3, std::false_type{}, Nxt{});
+            if (c + AHEAD < nchunks) load_gates(c + AHEAD, std::false_type{}, Nxt{});
         }
         frag wf[VAR == V_GDN ? NKS : 1];
         f32x4 ucur[VAR == V_GDN ? NTJW : 1];
@@ -939,9 +942,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
                 stage_any(m_tag, c + 1, Xn, Check{}, Nxt{});
                 if constexpr (FAST) {
-                    load_any(m_tag, c + 3, std::true_type{}, Nxt{});
+                    load_any(m_tag, c + AHEAD, std::true_type{}, Nxt{});
                 } else {
-                    if (c + 3 < nchunks) load_any(m_tag, c + 3, std::false_type{}, Nxt{});
+                    if (c + AHEAD < nchunks) load_any(m_tag, c + AHEAD, std::false_type{}, Nxt{});
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -1023,34 +1026,34 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         rows_of(w_tag, c, X, T, check_tag);
     };
     // State wave, chunk c (P = c & 1 at compile time): stage chunk c+1 into the
-    // other tile set from register set P^1 and refill that set with chunk c+3;
-    // then S <- update with chunk c, S_next^T into the other set, and the gate
-    // tables of chunk c+2 (log-gates of chunk c+3 prefetched). FAST: chunks
-    // c .. c+3 are full. The other tile set was last read by the rows of chunk
+    // other tile set from its register set and refill that set with chunk
+    // c+AHEAD; then S <- update with chunk c, S_next^T into the other set, and
+    // the gate tables of chunk c+2 (log-gates of chunk c+AHEAD prefetched).
+    // FAST: chunks c .. c+AHEAD are full. The other tile set was last read by the rows of chunk
     // c-1, which the barrier has retired.
     auto state_iter = [&](auto w_tag, int c, auto fast_tag, auto par_tag) __attribute__((always_inline)) {
         constexpr int W = decltype(w_tag)::value;
         constexpr bool FAST = decltype(fast_tag)::value;
         constexpr int P = decltype(par_tag)::value;
-        using Cur = std::integral_constant<int, P>;
-        using Nxt = std::integral_constant<int, P ^ 1>;
+        using Cur = std::integral_constant<int, P % NPS>;
+        using Nxt = std::integral_constant<int, (P ^ 1) % NPS>;
         using Check = std::bool_constant<!FAST>;
         const TM *X = Tiles + P * Cfg::SET;
         TM *Xn = Tiles + (P ^ 1) * Cfg::SET;
         __syncthreads();  // chunk c staged and visible; chunk c-1 done everywhere
         if constexpr (FAST) {
-            load_gates(c + 3, std::true_type{}, Nxt{});
+            load_gates(c + AHEAD, std::true_type{}, Nxt{});
         } else {
-            if (c + 3 < nchunks) load_gates(c + 3, std::false_type{}, Nxt{});
+            if (c + AHEAD < nchunks) load_gates(c + AHEAD, std::false_type{}, Nxt{});
         }
         const bool next = FAST || c + 1 < nchunks;
         if (next) {
             static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
                 stage_slot(w_tag, m_tag, c + 1, Xn, Check{}, Nxt{});
                 if constexpr (FAST) {
-                    load_slot(w_tag, m_tag, c + 3, std::true_type{}, Nxt{});
+                    load_slot(w_tag, m_tag, c + AHEAD, std::true_type{}, Nxt{});
                 } else {
-                    if (c + 3 < nchunks) load_slot(w_tag, m_tag, c + 3, std::false_type{}, Nxt{});
+                    if (c + AHEAD < nchunks) load_slot(w_tag, m_tag, c + AHEAD, std::false_type{}, Nxt{});
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
@@ -1084,37 +1087,44 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                 for (; c < nfull; ++c) row_iter(w_tag, c, std::false_type{});
                 for (; c < nchunks; ++c) row_iter(w_tag, c, std::true_type{});
             } else {
-                // chunks 0 and 1 into register sets 0 and 1; gate tables of
-                // chunks 0 and 1; chunk 0 staged and chunk 2 into set 0
+                // chunks 0 .. NPS-1 into register sets 0 .. NPS-1; gate tables
+                // of chunks 0 and 1; chunk 0 staged and chunk NPS into set 0
                 if (nchunks > 0) {
                     load_gates(0, std::false_type{}, Set0{});
                     static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
                         load_slot(w_tag, m_tag, 0, std::false_type{}, Set0{});
                     });
-                    if (nchunks > 1) {
-                        load_gates(1, std::false_type{}, Set1{});
-                        static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
-                            load_slot(w_tag, m_tag, 1, std::false_type{}, Set1{});
-                        });
+                    if constexpr (NPS == 2) {
+                        if (nchunks > 1) {
+                            load_gates(1, std::false_type{}, Set1{});
+                            static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                                load_slot(w_tag, m_tag, 1, std::false_type{}, Set1{});
+                            });
+                        }
                     }
                     if constexpr (DECAYED) {
-                        if (W == GW) {
-                            gate_tables(0, 0, Set0{});
-                            if (nchunks > 1) gate_tables(1, 1, Set1{});
+                        if (W == GW) gate_tables(0, 0, Set0{});
+                        if constexpr (NPS == 2) {
+                            if (W == GW && nchunks > 1) gate_tables(1, 1, Set1{});
+                            if (nchunks > 2) load_gates(2, std::false_type{}, Set0{});
+                        } else {
+                            if (nchunks > 1) {
+                                load_gates(1, std::false_type{}, Set0{});
+                                if (W == GW) gate_tables(1, 1, Set0{});
+                            }
                         }
-                        if (nchunks > 2) load_gates(2, std::false_type{}, Set0{});
                     }
                     __syncthreads();  // gate tables of chunk 0 visible
                     static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
                         stage_slot(w_tag, m_tag, 0, Tiles, std::true_type{}, Set0{});
-                        if (nchunks > 2) load_slot(w_tag, m_tag, 2, std::false_type{}, Set0{});
+                        if (nchunks > NPS) load_slot(w_tag, m_tag, NPS, std::false_type{}, Set0{});
                     });
                     write_sts(w_tag, Tiles);
                 }
                 int c = 0;
-                if (nfull >= 4) {
+                if (nfull >= AHEAD + 1) {
                     state_iter(w_tag, 0, std::true_type{}, P0{});
-                    for (c = 1; c + 1 <= nfull - 4; c += 2) {
+                    for (c = 1; c + 1 <= nfull - AHEAD - 1; c += 2) {
                         state_iter(w_tag, c, std::true_type{}, P1{});
                         state_iter(w_tag, c + 1, std::true_type{}, P0{});
                     }
@@ -1129,40 +1139,47 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             }
         });
     } else if constexpr (DB) {
-        // chunks 0 and 1 into register sets 0 and 1; chunk 0 staged; chunk 2
-        // into set 0; gate tables of chunks 0 and 1 built.
+        // chunks 0 .. NPS-1 into register sets 0 .. NPS-1; gate tables of
+        // chunks 0 and 1; chunk 0 staged and chunk NPS into set 0
         if (nchunks > 0) {
             load_gates(0, std::false_type{}, Set0{});
             static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
                 load_any(m_tag, 0, std::false_type{}, Set0{});
             });
-            if (nchunks > 1) {
-                load_gates(1, std::false_type{}, Set1{});
-                static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
-                    load_any(m_tag, 1, std::false_type{}, Set1{});
-                });
+            if constexpr (NPS == 2) {
+                if (nchunks > 1) {
+                    load_gates(1, std::false_type{}, Set1{});
+                    static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                        load_any(m_tag, 1, std::false_type{}, Set1{});
+                    });
+                }
             }
             load_wu(0);
             if constexpr (DECAYED) {
-                if (wv == GW) {
-                    gate_tables(0, 0, Set0{});
-                    if (nchunks > 1) gate_tables(1, 1, Set1{});
+                if (wv == GW) gate_tables(0, 0, Set0{});
+                if constexpr (NPS == 2) {
+                    if (wv == GW && nchunks > 1) gate_tables(1, 1, Set1{});
+                    if (nchunks > 2) load_gates(2, std::false_type{}, Set0{});
+                } else {
+                    if (nchunks > 1) {
+                        load_gates(1, std::false_type{}, Set0{});
+                        if (wv == GW) gate_tables(1, 1, Set0{});
+                    }
                 }
-                if (nchunks > 2) load_gates(2, std::false_type{}, Set0{});
             }
             __syncthreads();  // gate tables of chunk 0 visible
             static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
                 stage_any(m_tag, 0, Tiles, std::true_type{}, Set0{});
-                if (nchunks > 2) load_any(m_tag, 2, std::false_type{}, Set0{});
+                if (nchunks > NPS) load_any(m_tag, NPS, std::false_type{}, Set0{});
             });
             for_wave([&](auto w_tag) __attribute__((always_inline)) { write_sts(w_tag, Tiles); });
         }
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
         int c = 0;
-        if (nfull >= 4) {
+        if (nfull >= AHEAD + 1) {
             chunk_db(0, std::true_type{}, P0{});
-            for (c = 1; c + 1 <= nfull - 4; c += 2) {
+            for (c = 1; c + 1 <= nfull - AHEAD - 1; c += 2) {
                 chunk_db(c, std::true_type{}, P1{});
                 chunk_db(c + 1, std::true_type{}, P0{});
             }
