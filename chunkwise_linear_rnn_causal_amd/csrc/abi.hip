@@ -85,7 +85,7 @@ size_t chunk_workspace(la_variant var, la_dtype dt, int B, int H, int L, int d_k
 // For bf16 inputs and C = 64, 8-wave workgroups (wave pairs share a 16-row block
 // and split its columns) take 64 columns when that still gives at least one
 // workgroup per CU (fewer duplicate Q/K loads), else 32. The delta rule, whose
-// serial pass is the heaviest, falls back to 16-column, 4-wave workgroups when
+// serial pass is the heaviest, falls back to 16-column workgroups when
 // 32-column ones would leave CUs idle.
 struct Geometry {
     int dvt, nw;
@@ -94,7 +94,7 @@ constexpr int kNumCU = 256;
 
 Geometry choose_geometry(la_variant var, la_dtype dt, int64_t BH, int d_v, int C) {
     if (dt == LA_F32 || C == 128) return {32, 4};
-    if (var == LA_GATED_DELTA) return (BH * (d_v / 32) >= kNumCU) ? Geometry{32, 8} : Geometry{16, 4};
+    if (var == LA_GATED_DELTA) return (BH * (d_v / 32) >= kNumCU) ? Geometry{32, 8} : Geometry{16, 8};
     if (d_v % 64 == 0 && BH * (d_v / 64) >= kNumCU) return {64, 8};
     return {32, 8};
 }
@@ -117,7 +117,7 @@ hipError_t dispatch_chunk(la_variant var, int C, Geometry geo, const ChunkArgs &
         if constexpr (F32) return launch_chunk<V_GDN, TI, TO, DK, 32, 64, 4>(a, st);
         if constexpr (!F32) {
             if (geo.dvt == 32) return launch_chunk<V_GDN, TI, TO, DK, 32, 64, 8>(a, st);
-            return launch_chunk<V_GDN, TI, TO, DK, 16, 64, 4>(a, st);
+            return launch_chunk<V_GDN, TI, TO, DK, 16, 64, 8>(a, st);
         }
     }
     if (C == 128) {

@@ -18,7 +18,7 @@ template hipError_t launch_chunk<V_DECAY, bf16, bf16, 32, 32, 64, 8>(const Chunk
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 32, 64, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 32, 32, 128, 4>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_GDN, bf16, bf16, 32, 32, 64, 8>(const ChunkArgs &, hipStream_t);
-template hipError_t launch_chunk<V_GDN, bf16, bf16, 32, 16, 64, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_GDN, bf16, bf16, 32, 16, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 64, 32, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 64, 64, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 64, 32, 128, 4>(const ChunkArgs &, hipStream_t);
@@ -29,7 +29,7 @@ template hipError_t launch_chunk<V_DECAY, bf16, bf16, 64, 32, 64, 8>(const Chunk
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 64, 64, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 64, 32, 128, 4>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_GDN, bf16, bf16, 64, 32, 64, 8>(const ChunkArgs &, hipStream_t);
-template hipError_t launch_chunk<V_GDN, bf16, bf16, 64, 16, 64, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_GDN, bf16, bf16, 64, 16, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 128, 32, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 128, 64, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 128, 32, 128, 4>(const ChunkArgs &, hipStream_t);
@@ -40,7 +40,7 @@ template hipError_t launch_chunk<V_DECAY, bf16, bf16, 128, 32, 64, 8>(const Chun
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 128, 64, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 128, 32, 128, 4>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_GDN, bf16, bf16, 128, 32, 64, 8>(const ChunkArgs &, hipStream_t);
-template hipError_t launch_chunk<V_GDN, bf16, bf16, 128, 16, 64, 4>(const ChunkArgs &, hipStream_t);
+template hipError_t launch_chunk<V_GDN, bf16, bf16, 128, 16, 64, 8>(const ChunkArgs &, hipStream_t);
 
 // decode step: (variant, d_k, d_v)
 template hipError_t launch_decode<V_PLAIN, bf16, bf16, 32, 32>(const DecodeArgs &, hipStream_t);
