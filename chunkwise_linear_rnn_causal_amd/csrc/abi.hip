@@ -82,8 +82,9 @@ size_t chunk_workspace(la_variant var, la_dtype dt, int B, int H, int L, int d_k
 
 // Workgroup geometry of the chunk kernel: value columns per workgroup (DVT) and
 // waves per workgroup (NW). fp32 inputs and C = 128 use 4 waves over 32 columns.
-// For bf16 inputs and C = 64, 8-wave workgroups (wave pairs share a 16-row block
-// and split its columns) take 64 columns when that still gives at least one
+// For bf16 inputs and C = 64, 8-wave workgroups (four waves compute the 16-row
+// blocks, four stage the tiles and update the state) take 64 columns when that
+// still gives at least one
 // workgroup per CU (fewer duplicate Q/K loads), else 32. The delta rule, whose
 // serial pass is the heaviest, falls back to 16-column workgroups when
 // 32-column ones would leave CUs idle.

@@ -155,13 +155,16 @@ template <int N, typename F> __device__ __attribute__((always_inline)) inline vo
 // i covers 64/SEG whole rows of one tensor. Wave w issues loads w, w + NW, ...;
 // waves past the end repeat the last load (so every wave issues the same
 // memory operations and the wait counts stay exact) without staging it.
-template <typename TI, int DK, int DVT, int C, int NW, bool HAS_V>
+template <typename TI, int DK, int DVT, int C, int NW, bool HAS_V, bool HAS_Q = true>
 struct StageGeo {
     static constexpr int EPS = 16 / (int)sizeof(TI);   // input elements per segment
     static constexpr int SEGQ = DK / EPS, SEGV = DVT / EPS;
     static constexpr int NIQ = C * SEGQ / 64;           // wave loads per chunk for Q (and for K)
     static constexpr int NIV = HAS_V ? C * SEGV / 64 : 0;
-    static constexpr int NI = 2 * NIQ + NIV;
+    static constexpr int NQK = HAS_Q ? 2 : 1;           // staged tensors of width DK
+    static constexpr int NI = NQK * NIQ + NIV;
+    // first wave load of tensor kind (0 Q, 1 K, 2 V)
+    static constexpr int base(int kind) { return kind == 2 ? NQK * NIQ : (kind == 1 && HAS_Q ? NIQ : 0); }
     static constexpr int NSLOT = (NI + NW - 1) / NW;
     static_assert(64 % SEGQ == 0 && (!HAS_V || 64 % SEGV == 0) && NIQ * 64 == C * SEGQ &&
                   NIV * 64 == (HAS_V ? C * SEGV : 0), "staging geometry");
@@ -176,14 +179,14 @@ struct StageGeo {
         int i = w + NW * m;
         const bool real = i < NI;
         if (!real) i = NI - 1;
-        const int kind = i < NIQ ? 0 : (i < 2 * NIQ ? 1 : 2);
-        const int ii = kind == 2 ? i - 2 * NIQ : i - kind * NIQ;
+        const int kind = HAS_Q ? (i < NIQ ? 0 : (i < 2 * NIQ ? 1 : 2)) : (i < NIQ ? 1 : 2);
+        const int ii = i - base(kind);
         const int seg = kind == 2 ? SEGV : SEGQ;
         return Slot{real, kind, ii, seg, 64 / seg};
     }
 };
 
-template <int VAR, typename TM, int DK, int DVT, int C>
+template <int VAR, typename TM, int DK, int DVT, int C, bool QD = false>
 struct ChunkCfg {
     static constexpr bool DECAYED = (VAR == V_DECAY || VAR == V_GDN);
     static constexpr int PAD = 16 / (int)sizeof(TM);
@@ -191,9 +194,9 @@ struct ChunkCfg {
     using QT = RowTile<TM, DK, 8>;                        // Q: operand reads only
     using KT = RowTile<TM, DK, 16>;                       // K: operand and transpose reads
     using VT = RowTile<TM, DVT, DVT == 16 ? 0 : 16>;      // V, wV: transpose reads
-    // one set of tiles (Q, K, V, wV, S_prev^T), in elements
+    // one set of tiles (Q unless QD, K, V, wV, S_prev^T), in elements
     static constexpr int OQ = 0;
-    static constexpr int OK = OQ + C * QT::P;
+    static constexpr int OK = OQ + (QD ? 0 : C * QT::P);  // QD: Q is not staged
     static constexpr int OV = OK + C * KT::P;
     static constexpr int OVW = OV + C * VT::P;
     static constexpr int OS = OVW + (DECAYED ? C * VT::P : 0);
@@ -214,7 +217,15 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     using TM = typename OpOf<TI>::type;
     using MF = Mfma<TM>;
     using frag = typename MF::frag;
-    using Cfg = ChunkCfg<VAR, TM, DK, DVT, C>;
+    // C/8 waves with double-buffered tiles split the roles (mode 3). When the
+    // staging waves would otherwise carry many loads per chunk, the row waves
+    // load Q straight into operand registers (QD): each row block's queries are
+    // read by one wave only, so Q need not pass through LDS. (The delta rule's
+    // row waves also form U and stay on the staged path.)
+    constexpr bool SPLIT = NW == 2 * (C / 16) && ChunkCfg<VAR, TM, DK, DVT, C, true>::DB;
+    constexpr bool QD = SPLIT && sizeof(TM) == 2 && VAR != V_GDN &&
+                        StageGeo<TI, DK, DVT, C, NW / 2, true>::NSLOT > 6;
+    using Cfg = ChunkCfg<VAR, TM, DK, DVT, C, QD>;
     using QT = typename Cfg::QT;
     using KT = typename Cfg::KT;
     using VT = typename Cfg::VT;
@@ -222,9 +233,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     constexpr int NT = NW * 64;           // threads
     constexpr int E = MF::E;
     constexpr int NRB = C / 16;           // 16-row blocks per chunk
-    // C/8 waves with double-buffered tiles split the roles (mode 3)
-    using R = Roles<NW, NRB, NW == 2 * NRB && Cfg::DB>;
-    using Geo = StageGeo<TI, DK, DVT, C, R::NWS, VAR != V_GDN>;
+    using R = Roles<NW, NRB, SPLIT>;
+    using Geo = StageGeo<TI, DK, DVT, C, R::NWS, VAR != V_GDN, !QD>;
     constexpr bool DECAYED = Cfg::DECAYED;
     constexpr bool DB = Cfg::DB;
     constexpr int NTB = Cfg::NTB;
@@ -336,6 +346,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // block's start is uniform, so full-chunk loads use a scalar base)
     const uint32_t off_qk = ((lane / Geo::SEGQ) * DK + (lane % Geo::SEGQ) * EPS) * (uint32_t)sizeof(TI);
     const uint32_t off_v = ((lane / Geo::SEGV) * dv + (lane % Geo::SEGV) * EPS) * (uint32_t)sizeof(TI);
+    // QD (row waves): lane (g, n) holds q[rb*16 + n][g*DK/4 + 8ks + (0..7)] for
+    // k-step ks, as raw input two chunks ahead and as operands of this chunk.
+    uint4 qraw[QD ? 2 : 1][QD ? NKS : 1];
+    frag qcur[QD ? NKS : 1];
 
     const int nchunks = (L + C - 1) / C;
     const int nfull = L / C;  // chunks with all C rows valid
@@ -384,6 +398,32 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             for (int jt = 0; jt < NTJW; ++jt) {
                 const int tj = R::half(wv) * NTJW + jt;
                 upre[jt] = ld4<TM>(utg + srow * dv + tj * 16 + 4 * g);
+            }
+        }
+    };
+
+    // QD: queries of chunk c for this row wave's block into raw set QS; rows
+    // past L read row L - 1 (they only feed outputs that are not stored).
+    auto load_q = [&](int c, auto set_tag) __attribute__((always_inline)) {
+        if constexpr (QD) {
+            constexpr int QS = decltype(set_tag)::value;
+            const int t = min(c * C + R::rb(wv, 0) * 16 + n, L - 1);
+            const TI *p = qg + t * DK + g * (DK / 4);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) qraw[QS][ks] = *reinterpret_cast<const uint4 *>(p + ks * EPS);
+        }
+    };
+    auto cvt_q = [&](auto set_tag) __attribute__((always_inline)) {
+        if constexpr (QD) {
+            constexpr int QS = decltype(set_tag)::value;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const uint32_t w4[4] = {qraw[QS][ks].x, qraw[QS][ks].y, qraw[QS][ks].z, qraw[QS][ks].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    qcur[ks][2 * i] = (f16)bf16_lo(w4[i]);
+                    qcur[ks][2 * i + 1] = (f16)bf16_hi(w4[i]);
+                }
             }
         }
     };
@@ -537,7 +577,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             constexpr auto S = Geo::slot(0, M);
             const int i = (wv - WS0) + NWS * M;
             if (wv >= WS0 && i < Geo::NI) {
-                const int ii = S.kind == 2 ? i - 2 * Geo::NIQ : i - S.kind * Geo::NIQ;
+                const int ii = i - Geo::base(S.kind);
                 const int r = ii * S.rpi + lane / S.seg, seg = lane % S.seg;
                 const bool valid = !CHECK || cs * C + r < L;
                 const uint32_t w4[4] = {pre[PS][M].x, pre[PS][M].y, pre[PS][M].z, pre[PS][M].w};
@@ -588,7 +628,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             constexpr auto S = Geo::slot(0, M);
             int i = (wv - WS0) + NWS * M;
             i = i < Geo::NI ? i : Geo::NI - 1;  // repeat the last load past the end
-            const int ii = S.kind == 2 ? i - 2 * Geo::NIQ : i - S.kind * Geo::NIQ;
+            const int ii = i - Geo::base(S.kind);
             const TI *tb = S.kind == 0 ? qg : (S.kind == 1 ? kg : vg);
             const int pitch = S.kind == 2 ? dv : DK;
             if constexpr (FULL) {
@@ -688,7 +728,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             }
         };
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = ld_frag<TM>(&Qs[QT::at(rl, g * (DK / 4) + ks * E)]);
+        for (int ks = 0; ks < NKS; ++ks) {
+            if constexpr (QD) {
+                qf[ks] = qcur[ks];
+            } else {
+                qf[ks] = ld_frag<TM>(&Qs[QT::at(rl, g * (DK / 4) + ks * E)]);
+            }
+        }
 #pragma unroll
         for (int jt = 0; jt < NTJW; ++jt)
 #pragma unroll
@@ -1010,10 +1056,15 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // prologue and one per chunk (two for the delta rule).
     // Row wave, chunk c: the outputs of its row block (delta rule: first its
     // U rows, then a barrier).
-    auto row_iter = [&](auto w_tag, int c, auto check_tag) __attribute__((always_inline)) {
-        const TM *X = Tiles + (c & 1) * Cfg::SET;
+    auto row_iter = [&](auto w_tag, int c, auto check_tag, auto par_tag) __attribute__((always_inline)) {
+        constexpr int P = decltype(par_tag)::value;  // c & 1
+        const TM *X = Tiles + P * Cfg::SET;
         const float *T = Tg + (c % NTB) * 4 * C;
         __syncthreads();  // chunk c staged, its gate tables and S_prev visible
+        if constexpr (QD) {
+            cvt_q(par_tag);  // chunk c's queries, loaded two chunks ago
+            if (c + 2 < nchunks) load_q(c + 2, par_tag);
+        }
         if constexpr (VAR == V_GDN) {
             frag wf[NKS];
             f32x4 ucur[NTJW];
@@ -1080,12 +1131,31 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             constexpr int W = decltype(w_tag)::value;
             if constexpr (R::rows(W)) {
                 if (nchunks > 0) {
+                    load_q(0, P0{});
+                    if (nchunks > 1) load_q(1, P1{});
                     load_wu(0);
                     __syncthreads();  // prologue (the state waves' gate tables)
                 }
                 int c = 0;
-                for (; c < nfull; ++c) row_iter(w_tag, c, std::false_type{});
-                for (; c < nchunks; ++c) row_iter(w_tag, c, std::true_type{});
+                for (; c + 1 < nfull; c += 2) {
+                    row_iter(w_tag, c, std::false_type{}, P0{});
+                    row_iter(w_tag, c + 1, std::false_type{}, P1{});
+                }
+                for (; c < nchunks; ++c) {
+                    if (c < nfull) {
+                        if (c & 1) {
+                            row_iter(w_tag, c, std::false_type{}, P1{});
+                        } else {
+                            row_iter(w_tag, c, std::false_type{}, P0{});
+                        }
+                    } else {
+                        if (c & 1) {
+                            row_iter(w_tag, c, std::true_type{}, P1{});
+                        } else {
+                            row_iter(w_tag, c, std::true_type{}, P0{});
+                        }
+                    }
+                }
             } else {
                 // chunks 0 .. NPS-1 into register sets 0 .. NPS-1; gate tables
                 // of chunks 0 and 1; chunk 0 staged and chunk NPS into set 0
