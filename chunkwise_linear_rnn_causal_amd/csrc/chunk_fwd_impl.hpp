@@ -224,7 +224,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // row waves also form U and stay on the staged path.)
     constexpr bool SPLIT = NW == 2 * (C / 16) && ChunkCfg<VAR, TM, DK, DVT, C, true>::DB;
     constexpr bool QD = SPLIT && sizeof(TM) == 2 && VAR != V_GDN &&
-                        StageGeo<TI, DK, DVT, C, NW - C / 16, true>::NSLOT > 6;
+                        StageGeo<TI, DK, DVT, C, (NW > C / 16 ? NW - C / 16 : 1), true>::NSLOT > 6;
     using Cfg = ChunkCfg<VAR, TM, DK, DVT, C, QD>;
     using QT = typename Cfg::QT;
     using KT = typename Cfg::KT;
