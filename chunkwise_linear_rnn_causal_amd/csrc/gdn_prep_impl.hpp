@@ -80,10 +80,40 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     const float *lgg = a.lg ? a.lg + (size_t)bh * L : nullptr;
     const float *bg = a.beta + (size_t)bh * L;
 
-    // Gates: inclusive scan of the chunk's log-gates (one token per lane).
+    // Every global load of the chunk is issued first (log-gate, beta, K and V
+    // rows), so their latencies overlap. Staging unit u (one per thread) covers
+    // four consecutive tokens of one 8-channel column block. Rows past the end
+    // of the sequence are read from the last token (so every load is
+    // unconditional) and then zeroed.
     const int tl = t0 + lane;
     const float lgv = (lgg && tl < L) ? lgg[tl] : 0.f;
     const float bv = (tl < L) ? bg[tl] : 0.f;
+    constexpr int KCB = DK / 8, KCBL = KCB < 4 ? KCB : 4, KTQL = 16 / KCBL, KNCBG = KCB / KCBL;
+    constexpr int KUNITS = (C / 4) * KCB;
+    static_assert(KUNITS % 64 == 0 && KUNITS <= 256, "one K staging unit per thread, wave-uniform");
+    const int VCB = dv / 8;
+    const int VCBL = VCB < 4 ? VCB : 4, VTQL = 16 / VCBL, VNCBG = VCB / VCBL;
+    const int VUNITS = (C / 4) * VCB;  // multiple of 64, at most 256, for dv in {32, 64, 128}
+    const int gi = tid >> 4, l16 = tid & 15;
+    const int ktq = (gi / KNCBG) * KTQL + (l16 % KTQL), kcb = (gi % KNCBG) * KCBL + (l16 / KTQL);
+    const int vtq = (gi / VNCBG) * VTQL + (l16 % VTQL), vcb = (gi % VNCBG) * VCBL + (l16 / VTQL);
+    float kx[4][8], vx[4][8];
+    if (tid < KUNITS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * ktq + r;
+            ld8<TI>(kg + (size_t)(t < L ? t : L - 1) * DK + 8 * kcb, kx[r]);
+        }
+    }
+    if (tid < VUNITS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = t0 + 4 * vtq + r;
+            ld8<TI>(vg + (size_t)(t < L ? t : L - 1) * dv + 8 * vcb, vx[r]);
+        }
+    }
+
+    // Gates: inclusive scan of the chunk's log-gates (one token per lane).
     float G = lgv;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -96,60 +126,33 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     }
 
     // Stage K row-major, K transposed scaled by beta_s a_s, V transposed scaled by
-    // beta_s. Rows past the end of the sequence are read from the last token (so
-    // every load is unconditional) and then zeroed.
-    {
-        constexpr int CB = DK / 8, CBL = CB < 4 ? CB : 4, TQL = 16 / CBL, NCBG = CB / CBL;
-        constexpr int UNITS = (C / 4) * CB;
-        static_assert(UNITS % 64 == 0, "wave-uniform staging loop");
-        for (int u = tid; u < UNITS; u += 256) {
-            const int gi = u >> 4, l16 = u & 15;
-            const int tq = (gi / NCBG) * TQL + (l16 % TQL);
-            const int cb = (gi % NCBG) * CBL + (l16 / TQL);
-            float x[4][8], sc[4];
+    // beta_s (zero past the end of the sequence, where beta is zero too).
+    if (tid < KUNITS) {
+        float sc[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = t0 + 4 * tq + r;
-                ld8<TI>(kg + (size_t)(t < L ? t : L - 1) * DK + 8 * cb, x[r]);
+        for (int r = 0; r < 4; ++r) {
+            const int s = 4 * ktq + r;
+            if (t0 + s >= L) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kx[r][e] = 0.f;
             }
+            st8<TM>(&Ks[s * KP + 8 * kcb], kx[r]);
+            sc[r] = __shfl(bv, s, 64) * __expf(__shfl(G, s, 64));
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int s = 4 * tq + r;
-                if (t0 + s >= L) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[r][e] = 0.f;
-                }
-                st8<TM>(&Ks[s * KP + 8 * cb], x[r]);
-                sc[r] = __shfl(bv, s, 64) * __expf(__shfl(G, s, 64));
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                f32x4 col = {x[0][e] * sc[0], x[1][e] * sc[1], x[2][e] * sc[2], x[3][e] * sc[3]};
-                st4<TM>(&KTs[tidx<C, TM>(8 * cb + e, 4 * tq)], col);
-            }
+        for (int e = 0; e < 8; ++e) {
+            f32x4 col = {kx[0][e] * sc[0], kx[1][e] * sc[1], kx[2][e] * sc[2], kx[3][e] * sc[3]};
+            st4<TM>(&KTs[tidx<C, TM>(8 * kcb + e, 4 * ktq)], col);
         }
     }
-    {
-        const int CB = dv / 8;
-        const int CBL = CB < 4 ? CB : 4, TQL = 16 / CBL, NCBG = CB / CBL;
-        const int UNITS = (C / 4) * CB;  // multiple of 64 for dv in {32, 64, 96, 128}
-        for (int u = tid; u < UNITS; u += 256) {
-            const int gi = u >> 4, l16 = u & 15;
-            const int tq = (gi / NCBG) * TQL + (l16 % TQL);
-            const int cb = (gi % NCBG) * CBL + (l16 / TQL);
-            float x[4][8], sc[4];
+    if (tid < VUNITS) {
+        float sc[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = t0 + 4 * tq + r;
-                ld8<TI>(vg + (size_t)(t < L ? t : L - 1) * dv + 8 * cb, x[r]);
-            }
+        for (int r = 0; r < 4; ++r) sc[r] = __shfl(bv, 4 * vtq + r, 64);  // beta = 0 past the end
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sc[r] = __shfl(bv, 4 * tq + r, 64);  // beta = 0 past the end
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                f32x4 col = {x[0][e] * sc[0], x[1][e] * sc[1], x[2][e] * sc[2], x[3][e] * sc[3]};
-                st4<TM>(&VTs[tidx<C, TM>(8 * cb + e, 4 * tq)], col);
-            }
+        for (int e = 0; e < 8; ++e) {
+            f32x4 col = {vx[0][e] * sc[0], vx[1][e] * sc[1], vx[2][e] * sc[2], vx[3][e] * sc[3]};
+            st4<TM>(&VTs[tidx<C, TM>(8 * vcb + e, 4 * vtq)], col);
         }
     }
     __syncthreads();
@@ -231,8 +234,11 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     if (wv == 0) below_block(3, 0);
     __syncthreads();  // T complete; P is dead from here (To reuses it)
 
-    // T in the operand type, zero above the diagonal blocks.
-    for (int idx = tid; idx < C * C; idx += 256) {
+    // T in the operand type, zero above the diagonal blocks (unrolled so that
+    // the reads of a thread go out together).
+#pragma unroll
+    for (int i = 0; i < C * C / 256; ++i) {
+        const int idx = tid + 256 * i;
         const int r = idx / C, s = idx % C;
         To[r * OP + s] = from_f32<TM>((s >> 4) > (r >> 4) ? 0.f : Tm[r * TP + s]);
     }
