@@ -264,6 +264,15 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // Normalizer z of the previous chunk, double-buffered: fp16 path as hi and lo
     // halves (z = hi + lo to 2^-22) for the q . z MFMA; fp32 path in fp32.
     __shared__ __attribute__((aligned(16))) TM Zs[VAR == V_NORM ? (H ? 4 * DK : 2 * DK) : 1];
+    // OSTG (split roles, fp32 output, 32-column slices): each row wave passes
+    // its 16-row output block through a private LDS tile, so that every store
+    // instruction writes whole 128-byte lines (8 lanes x 16 bytes per row)
+    // instead of 16 half lines. With 64-column slices the row waves are the
+    // longer chain and the extra LDS round trip cost more than it saved; with
+    // 16 columns a row is only 64 bytes.
+    constexpr bool OSTG = R::MODE == 3 && sizeof(TO) == 4 && DVT == 32;
+    constexpr int OP = DVT + 4;  // row pitch of the output tile (floats)
+    __shared__ __attribute__((aligned(16))) float Ost[OSTG ? NRB * 16 * OP : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -883,9 +892,27 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 
         // rows of this block start at a uniform offset: scalar base + lane offset
         TO *ob = og + (size_t)(t0 + rb * 16) * dv + tj0 * 16;
-        if (!CHECK || t0 + rl < L) {
+        if constexpr (OSTG) {
+            // the wave's tile: written in accumulator layout, read back with
+            // LPR lanes per row (LDS operations of one wave complete in order)
+            float *Ow = Ost + rb * 16 * OP;
 #pragma unroll
-            for (int jt = 0; jt < NTJW; ++jt) st4<TO>(ob + (uint32_t)(n * dv + jt * 16 + 4 * g), oacc[jt]);
+            for (int jt = 0; jt < NTJW; ++jt) *reinterpret_cast<f32x4 *>(&Ow[n * OP + jt * 16 + 4 * g]) = oacc[jt];
+            __builtin_amdgcn_wave_barrier();
+            constexpr int LPR = NTJW * 4;     // lanes per output row (16 bytes each)
+            constexpr int RPI = 64 / LPR;     // rows per store instruction
+#pragma unroll
+            for (int h = 0; h < 16 / RPI; ++h) {
+                const int r = h * RPI + lane / LPR, cq = lane % LPR;
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(&Ow[r * OP + 4 * cq]);
+                if (!CHECK || t0 + rb * 16 + r < L) st4<TO>(ob + (uint32_t)(r * dv + 4 * cq), v);
+            }
+            __builtin_amdgcn_wave_barrier();
+        } else {
+            if (!CHECK || t0 + rl < L) {
+#pragma unroll
+                for (int jt = 0; jt < NTJW; ++jt) st4<TO>(ob + (uint32_t)(n * dv + jt * 16 + 4 * g), oacc[jt]);
+            }
         }
     };
 
