@@ -257,3 +257,40 @@ def test_wide_grid_geometry(var, B, H, dk, dv):
     assert_close(s, rs, TOL["bf16"], "state")
     if var == "normalized":
         assert_close(z, rz, 1e-5, "z")
+
+# Lengths that run the steady-state loop of the split-role kernels (prefetch two
+# or three chunks ahead, unrolled by the prefetch depth) and leave it at every
+# remainder, with and without a ragged last chunk.
+SCHEDULE_LENGTHS = [4 * 64 + 23, 5 * 64, 5 * 64 + 1, 6 * 64 + 40, 7 * 64 + 63, 8 * 64, 9 * 64 + 7]
+
+
+@pytest.mark.parametrize("L", SCHEDULE_LENGTHS)
+@pytest.mark.parametrize("var,dk,dv", [
+    ("plain", 64, 64),          # 32-column split roles, three prefetch sets
+    ("normalized", 64, 64),
+    ("decay", 64, 64),
+    ("gated_delta", 64, 64),    # 16-column split roles, three prefetch sets
+    ("decay", 128, 128),        # queries loaded straight into registers
+    ("gated_delta", 128, 128),  # one prefetch set
+])
+def test_split_role_schedules(var, dk, dv, L):
+    """Split-role chunk kernels through their steady-state loop and every exit
+    remainder, against the oracle (B=1, H=2, random initial state)."""
+    inp = W.make_chunk_inputs(var, "bf16", 1, 2, L, dk, dv, seed=17, with_state=True,
+                              with_z=(var == "normalized"))
+    o, s, z = gpu_chunk(inp, 64)
+    ro, rs, rz = oracle_chunk(inp)
+    assert_close(o, ro, TOL["bf16"], "o")
+    assert_close(s, rs, TOL["bf16"], "state")
+    if var == "normalized":
+        assert_close(z, rz, 1e-5, "z")
+
+
+def test_split_role_schedule_two_sets():
+    """Decay, d = 128, 128 heads: 64-column split roles with two prefetch sets
+    and direct queries, through the steady-state loop and a ragged tail."""
+    inp = W.make_chunk_inputs("decay", "bf16", 2, 64, 5 * 64 + 9, 128, 128, seed=19, with_state=True)
+    o, s, _ = gpu_chunk(inp, 64)
+    ro, rs, _ = oracle_chunk(inp)
+    assert_close(o, ro, TOL["bf16"], "o")
+    assert_close(s, rs, TOL["bf16"], "state")
