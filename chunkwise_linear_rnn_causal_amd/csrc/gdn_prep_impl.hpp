@@ -35,15 +35,19 @@ struct PrepCfg {
     static constexpr int OP = C + PAD;    // row pitch of T in the operand type
     static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
     static constexpr size_t up16(size_t x) { return (x + 15) / 16 * 16; }
-    // Lifetimes allow two aliases: K is dead once P is formed (its bytes then
-    // hold T in fp32), and P is dead once T is complete (its bytes then hold T
-    // in the operand type).
-    static constexpr size_t o_k = 0;
-    static constexpr size_t o_kt = o_k + up16(cmax(sizeof(TM) * C * KP, 4 * C * TP));
-    static constexpr size_t o_vt = o_kt + sizeof(TM) * DK * C;
-    static constexpr size_t o_p = o_vt + sizeof(TM) * DVMAX * C;
-    static constexpr size_t o_y = o_p + up16(cmax(4 * C * TP, sizeof(TM) * C * OP));
-    static constexpr size_t o_g = o_y + 4 * 4 * 256;
+    // Three regions, each reused as lifetimes end (about 50 KB at d_k = 128,
+    // so three workgroups fit on a CU):
+    //   A: K row-major (until P is formed), then T in fp32 (until it is
+    //      converted), then K^T scaled by beta a (for W);
+    //   B: P in fp32 (until T is complete), then T in the operand type;
+    //   C: the per-wave scratch of the off-diagonal blocks, then V^T scaled
+    //      by beta (for U~).
+    // K and V stay in registers from their load until the scaled transposes
+    // are staged, after T is converted.
+    static constexpr size_t o_a = 0;
+    static constexpr size_t o_p = o_a + up16(cmax(cmax(sizeof(TM) * C * KP, 4 * C * TP), sizeof(TM) * DK * C));
+    static constexpr size_t o_c = o_p + up16(cmax(4 * C * TP, sizeof(TM) * C * OP));
+    static constexpr size_t o_g = o_c + up16(cmax(4 * 4 * 256, sizeof(TM) * DVMAX * C));
     static constexpr size_t lds_bytes = o_g + 4 * 2 * C;
 };
 
@@ -62,13 +66,13 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     static_assert(C == 64 && NRB == NW, "one 16-row diagonal block of T per wave: C = 64");
 
     __shared__ __attribute__((aligned(16))) char lds[Cfg::lds_bytes];
-    TM *Ks = reinterpret_cast<TM *>(lds + Cfg::o_k);
-    float *Tm = reinterpret_cast<float *>(lds + Cfg::o_k);   // after P is formed
-    TM *KTs = reinterpret_cast<TM *>(lds + Cfg::o_kt);
-    TM *VTs = reinterpret_cast<TM *>(lds + Cfg::o_vt);
+    TM *Ks = reinterpret_cast<TM *>(lds + Cfg::o_a);
+    float *Tm = reinterpret_cast<float *>(lds + Cfg::o_a);   // after P is formed
+    TM *KTs = reinterpret_cast<TM *>(lds + Cfg::o_a);        // after T is converted
     float *Pm = reinterpret_cast<float *>(lds + Cfg::o_p);
     TM *To = reinterpret_cast<TM *>(lds + Cfg::o_p);         // after T is complete
-    float *Ysc = reinterpret_cast<float *>(lds + Cfg::o_y);
+    float *Ysc = reinterpret_cast<float *>(lds + Cfg::o_c);
+    TM *VTs = reinterpret_cast<TM *>(lds + Cfg::o_c);        // after T is converted
     float *Gs = reinterpret_cast<float *>(lds + Cfg::o_g);
     float *Bs = Gs + C;
 
@@ -125,10 +129,8 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
         Bs[lane] = bv;
     }
 
-    // Stage K row-major, K transposed scaled by beta_s a_s, V transposed scaled by
-    // beta_s (zero past the end of the sequence, where beta is zero too).
+    // Stage K row-major (zero past the end of the sequence).
     if (tid < KUNITS) {
-        float sc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int s = 4 * ktq + r;
@@ -137,22 +139,6 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
                 for (int e = 0; e < 8; ++e) kx[r][e] = 0.f;
             }
             st8<TM>(&Ks[s * KP + 8 * kcb], kx[r]);
-            sc[r] = __shfl(bv, s, 64) * __expf(__shfl(G, s, 64));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            f32x4 col = {kx[0][e] * sc[0], kx[1][e] * sc[1], kx[2][e] * sc[2], kx[3][e] * sc[3]};
-            st4<TM>(&KTs[tidx<C, TM>(8 * kcb + e, 4 * ktq)], col);
-        }
-    }
-    if (tid < VUNITS) {
-        float sc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = __shfl(bv, 4 * vtq + r, 64);  // beta = 0 past the end
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            f32x4 col = {vx[0][e] * sc[0], vx[1][e] * sc[1], vx[2][e] * sc[2], vx[3][e] * sc[3]};
-            st4<TM>(&VTs[tidx<C, TM>(8 * vcb + e, 4 * vtq)], col);
         }
     }
     __syncthreads();
@@ -241,6 +227,33 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
         const int idx = tid + 256 * i;
         const int r = idx / C, s = idx % C;
         To[r * OP + s] = from_f32<TM>((s >> 4) > (r >> 4) ? 0.f : Tm[r * TP + s]);
+    }
+    __syncthreads();  // T converted: region A (T in fp32) and C (scratch) are free
+
+    // Stage K transposed scaled by beta_s a_s and V transposed scaled by beta_s
+    // (zero past the end of the sequence, where beta is zero too).
+    if (tid < KUNITS) {
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int s = 4 * ktq + r;
+            sc[r] = __shfl(bv, s, 64) * __expf(__shfl(G, s, 64));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            f32x4 col = {kx[0][e] * sc[0], kx[1][e] * sc[1], kx[2][e] * sc[2], kx[3][e] * sc[3]};
+            st4<TM>(&KTs[tidx<C, TM>(8 * kcb + e, 4 * ktq)], col);
+        }
+    }
+    if (tid < VUNITS) {
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = __shfl(bv, 4 * vtq + r, 64);  // beta = 0 past the end
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            f32x4 col = {vx[0][e] * sc[0], vx[1][e] * sc[1], vx[2][e] * sc[2], vx[3][e] * sc[3]};
+            st4<TM>(&VTs[tidx<C, TM>(8 * vcb + e, 4 * vtq)], col);
+        }
     }
     __syncthreads();
 
