@@ -35,19 +35,20 @@ struct PrepCfg {
     static constexpr int OP = C + PAD;    // row pitch of T in the operand type
     static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
     static constexpr size_t up16(size_t x) { return (x + 15) / 16 * 16; }
-    // Three regions, each reused as lifetimes end (about 50 KB at d_k = 128,
-    // so three workgroups fit on a CU):
+    // Three regions, each reused as lifetimes end (about 38 KB at d_k = 128,
+    // so four workgroups fit on a CU):
     //   A: K row-major (until P is formed), then T in fp32 (until it is
-    //      converted), then K^T scaled by beta a (for W);
+    //      converted), then K^T scaled by beta a (for W), then V^T scaled by
+    //      beta (for U~);
     //   B: P in fp32 (until T is complete), then T in the operand type;
-    //   C: the per-wave scratch of the off-diagonal blocks, then V^T scaled
-    //      by beta (for U~).
-    // K and V stay in registers from their load until the scaled transposes
+    //   C: the per-wave scratch of the off-diagonal blocks.
+    // K and V stay in registers from their load until their scaled transposes
     // are staged, after T is converted.
     static constexpr size_t o_a = 0;
-    static constexpr size_t o_p = o_a + up16(cmax(cmax(sizeof(TM) * C * KP, 4 * C * TP), sizeof(TM) * DK * C));
+    static constexpr size_t o_p = o_a + up16(cmax(cmax(sizeof(TM) * C * KP, 4 * C * TP),
+                                                  sizeof(TM) * (DK > DVMAX ? DK : DVMAX) * C));
     static constexpr size_t o_c = o_p + up16(cmax(4 * C * TP, sizeof(TM) * C * OP));
-    static constexpr size_t o_g = o_c + up16(cmax(4 * 4 * 256, sizeof(TM) * DVMAX * C));
+    static constexpr size_t o_g = o_c + 4 * 4 * 256;
     static constexpr size_t lds_bytes = o_g + 4 * 2 * C;
 };
 
@@ -72,7 +73,7 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     float *Pm = reinterpret_cast<float *>(lds + Cfg::o_p);
     TM *To = reinterpret_cast<TM *>(lds + Cfg::o_p);         // after T is complete
     float *Ysc = reinterpret_cast<float *>(lds + Cfg::o_c);
-    TM *VTs = reinterpret_cast<TM *>(lds + Cfg::o_c);        // after T is converted
+    TM *VTs = reinterpret_cast<TM *>(lds + Cfg::o_a);        // after W is formed
     float *Gs = reinterpret_cast<float *>(lds + Cfg::o_g);
     float *Bs = Gs + C;
 
@@ -228,10 +229,10 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
         const int r = idx / C, s = idx % C;
         To[r * OP + s] = from_f32<TM>((s >> 4) > (r >> 4) ? 0.f : Tm[r * TP + s]);
     }
-    __syncthreads();  // T converted: region A (T in fp32) and C (scratch) are free
+    __syncthreads();  // T converted: region A (T in fp32) is free
 
-    // Stage K transposed scaled by beta_s a_s and V transposed scaled by beta_s
-    // (zero past the end of the sequence, where beta is zero too).
+    // Stage K transposed scaled by beta_s a_s (zero past the end of the
+    // sequence, where beta is zero too).
     if (tid < KUNITS) {
         float sc[4];
 #pragma unroll
@@ -243,16 +244,6 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
         for (int e = 0; e < 8; ++e) {
             f32x4 col = {kx[0][e] * sc[0], kx[1][e] * sc[1], kx[2][e] * sc[2], kx[3][e] * sc[3]};
             st4<TM>(&KTs[tidx<C, TM>(8 * kcb + e, 4 * ktq)], col);
-        }
-    }
-    if (tid < VUNITS) {
-        float sc[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = __shfl(bv, 4 * vtq + r, 64);  // beta = 0 past the end
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            f32x4 col = {vx[0][e] * sc[0], vx[1][e] * sc[1], vx[2][e] * sc[2], vx[3][e] * sc[3]};
-            st4<TM>(&VTs[tidx<C, TM>(8 * vcb + e, 4 * vtq)], col);
         }
     }
     __syncthreads();
@@ -270,6 +261,21 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
         }
         st4<TM>(wout + (size_t)(rb * 16 + n) * DK + cbk * 16 + 4 * g, d);
     }
+    __syncthreads();  // W formed: region A is free
+
+    // Stage V transposed scaled by beta_s (zero past the end, where beta is zero).
+    if (tid < VUNITS) {
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = __shfl(bv, 4 * vtq + r, 64);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            f32x4 col = {vx[0][e] * sc[0], vx[1][e] * sc[1], vx[2][e] * sc[2], vx[3][e] * sc[3]};
+            st4<TM>(&VTs[tidx<C, TM>(8 * vcb + e, 4 * vtq)], col);
+        }
+    }
+    __syncthreads();
+
     // U~ row-major, from transposed tiles D[j][r] = sum_s (beta V)[s][j] T[r][s];
     // lane holds r = rb*16 + n and four consecutive columns j = jb*16 + 4g + e.
     TM *uout = (TM *)a.ut + ((size_t)bh * a.Lp + t0) * dv;
