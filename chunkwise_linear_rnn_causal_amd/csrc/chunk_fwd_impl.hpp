@@ -119,13 +119,16 @@ template <int NTT, int NW> struct TileSplit {
     int cnt[NW];
     int maxcnt;
 };
-// extraz: normalizer channel blocks (each weighs one state tile).
+// extraz: normalizer channel blocks (each weighs one state tile); gates: the
+// gate-table wave's extra work in state tiles (split roles only).
 template <int NTT, int NW, int NRB, bool SPLIT>
-constexpr TileSplit<NTT, NW> make_tile_split(int extraz) {
+constexpr TileSplit<NTT, NW> make_tile_split(int extraz, int gates) {
     using R = Roles<NW, NRB, SPLIT>;
     TileSplit<NTT, NW> t{};
     for (int w = 0; w < NW; ++w) t.cnt[w] = 0;
-    auto load = [&](int w) { return R::score_tiles(w) + t.cnt[w] + R::zunits(w, extraz); };
+    auto load = [&](int w) {
+        return R::score_tiles(w) + t.cnt[w] + R::zunits(w, extraz) + (R::MODE == 3 && w == R::GW ? gates : 0);
+    };
     for (int i = 0; i < NTT; ++i) {
         int best = 0;
         for (int w = 1; w < NW; ++w)
@@ -249,7 +252,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     constexpr int NSLOT = Geo::NSLOT;
     constexpr int GW = R::GW;             // wave that builds the gate tables
     constexpr int WS0 = R::WS0, NWS = R::NWS;
-    constexpr auto TS = make_tile_split<NTI * NTJ, NW, NRB, R::MODE == 3>(VAR == V_NORM ? NTI : 0);
+    constexpr auto TS = make_tile_split<NTI * NTJ, NW, NRB, R::MODE == 3>(VAR == V_NORM ? NTI : 0, DECAYED ? 2 : 0);
     constexpr int NTS = TS.maxcnt;        // state tiles per wave (at most)
     static_assert(NTJW >= 1 && (R::MODE != 1 || NTJ % 2 == 0), "value slice too narrow for the roles");
     static_assert(VAR != V_GDN || ((R::MODE <= 1 || R::MODE == 3) && NRB == 4),
@@ -1125,18 +1128,30 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             if (c + AHEAD < nchunks) load_gates(c + AHEAD, std::false_type{}, Nxt{});
         }
         const bool next = FAST || c + 1 < nchunks;
-        if (next) {
-            static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
-                stage_slot(w_tag, m_tag, c + 1, Xn, Check{}, Nxt{});
-                if constexpr (FAST) {
-                    load_slot(w_tag, m_tag, c + AHEAD, std::true_type{}, Nxt{});
-                } else {
-                    if (c + AHEAD < nchunks) load_slot(w_tag, m_tag, c + AHEAD, std::false_type{}, Nxt{});
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            });
-        }
+        // slots [M0, M1) of chunk c+1
+        auto stage_range = [&](auto m0_tag, auto m1_tag) __attribute__((always_inline)) {
+            if (next) {
+                static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
+                    constexpr int M = decltype(m_tag)::value;
+                    if constexpr (M >= decltype(m0_tag)::value && M < decltype(m1_tag)::value) {
+                        stage_slot(w_tag, m_tag, c + 1, Xn, Check{}, Nxt{});
+                        if constexpr (FAST) {
+                            load_slot(w_tag, m_tag, c + AHEAD, std::true_type{}, Nxt{});
+                        } else {
+                            if (c + AHEAD < nchunks) load_slot(w_tag, m_tag, c + AHEAD, std::false_type{}, Nxt{});
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                });
+            }
+        };
+        // The delta rule's mid-chunk barrier waits for the row waves' U rows:
+        // half the staging goes before it (beside U), half after (beside the
+        // rows).
+        constexpr int MH = VAR == V_GDN ? NSLOT / 2 : NSLOT;
+        stage_range(std::integral_constant<int, 0>{}, std::integral_constant<int, MH>{});
         if constexpr (VAR == V_GDN) __syncthreads();  // U of chunk c visible
+        stage_range(std::integral_constant<int, MH>{}, std::integral_constant<int, NSLOT>{});
         const float eg = DECAYED ? Tsc[c % NTB] : 1.f;
         state_update(w_tag, c, X, eg);
         if (next) write_sts(w_tag, Xn);
