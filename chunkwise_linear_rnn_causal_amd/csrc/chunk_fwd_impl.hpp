@@ -22,22 +22,23 @@
 //      the state update. Operands that need the token index in the K slots
 //      (K^T and V^T) are read from the row-major tiles with the gfx950
 //      transpose load. When two chunks' tiles fit in LDS they are double
-//      buffered: chunk c+1 is staged while chunk c is computed and chunk c+2 is
-//      loaded into registers, with one barrier per chunk; otherwise a single
-//      buffer is staged between two barriers. Wave 0 builds the gate tables
-//      (G, exp(G), exp(g_C - G), exp(g_C)) ahead of the chunk that uses them.
-//   2. Query row blocks of 16 rows are assigned to waves by Roles: with C/8
-//      waves, wave pairs split the value columns of one row block; with C/32
-//      waves, each wave takes a row block and its mirror so the triangular score
-//      work balances. A wave computes the inter term (S^T Q^T on MFMA), the score
-//      tiles K_sb Q_rb^T for sb <= rb, masks/decays/rounds them in registers and
-//      feeds them straight back as the B operand of the intra term V^T A^T: the D
-//      layout of a score tile is exactly the B-operand layout of the next MFMA
-//      with the key index in the K slots. Output rows are lane-indexed, so the
+//      buffered: chunk c+1 is staged while chunk c is computed, with the loads
+//      two or three chunks ahead in registers and one barrier per chunk;
+//      otherwise a single buffer is staged between two barriers. The gate
+//      tables (G, exp(G), exp(g_C - G), exp(g_C)) are built ahead of the chunk
+//      that uses them.
+//   2. 16-row query blocks are assigned to waves by Roles. With C/8 waves and
+//      double buffering the roles split: four row waves compute the outputs,
+//      four staging waves stage, prefetch and carry the state. A row wave
+//      computes the inter term (S^T Q^T on MFMA), the score tiles K_sb Q_rb^T
+//      for sb <= rb, masks/decays/rounds them in registers and feeds them
+//      straight back as the B operand of the intra term V^T A^T: the D layout
+//      of a score tile is exactly the B-operand layout of the next MFMA with
+//      the key index in the K slots. Output rows are lane-indexed, so the
 //      per-row scales (exp(G_r), 1/den_r) are per-lane scalars and each lane
-//      stores four consecutive output columns.
+//      holds four consecutive output columns.
 //   3. S <- exp(g_C) S + K^T (w V) on MFMA into the accumulators; the state
-//      tiles are split greedily so waves with fewer score tiles take more.
+//      tiles are split greedily over the waves with the least other work.
 #pragma once
 
 #include <type_traits>
@@ -67,31 +68,25 @@ template <typename TM, int W, int PAD> struct RowTile {
 };
 
 // ---------------------------------------------------------------------------
-// Wave roles. Modes 0-2 give every wave output rows, state tiles and staging:
+// Wave roles. Modes 0 and 2 give every wave output rows, state tiles and
+// staging:
 //   0: C/16 waves, one 16-row block each;
-//   1: C/8 waves, wave pairs split the value columns of one row block. Waves w
-//      and w + 4 of a workgroup share a SIMD, so the second half of row block rb
-//      goes to wave 2*NRB - 1 - rb: every SIMD carries one light and one heavy
-//      row block;
 //   2: C/32 waves, each with a row block and its mirror.
-// Mode 3 (SPLIT, C/8 waves) separates the two chains of a chunk: waves 0..NRB-1
-// each compute all value columns of one row block (no score tile is computed
-// twice), while waves NRB.. stage the tiles, prefetch, update the state and the
+// Mode 3 (SPLIT: C/8 waves, double-buffered tiles) separates the two chains of
+// a chunk: waves 0..NRB-1 each compute all value columns of one row block,
+// while waves NRB.. stage the tiles, prefetch, update the state and the
 // normalizer and build the gate tables, so the state work runs beside the rows
 // instead of after them.
 template <int NW, int NRB, bool SPLIT = false> struct Roles {
-    static constexpr int MODE =
-        SPLIT ? 3 : (NW == NRB) ? 0 : (NW == 2 * NRB) ? 1 : (2 * NW == NRB) ? 2 : -1;
-    static_assert(MODE >= 0 && (MODE != 3 || NW == 2 * NRB), "wave count must be C/16, C/8 or C/32");
+    static constexpr int MODE = SPLIT ? 3 : (NW == NRB) ? 0 : (2 * NW == NRB) ? 2 : -1;
+    static_assert(MODE >= 0 && (MODE != 3 || NW == 2 * NRB),
+                  "wave count must be C/16 or C/32, or C/8 with double-buffered tiles");
     static constexpr int RBW = MODE == 2 ? 2 : 1;
     static constexpr bool rows(int w) { return MODE != 3 || w < NRB; }    // computes output rows
     static constexpr bool stages(int w) { return MODE != 3 || w >= NRB; } // stages tiles, owns state tiles
     static constexpr int rb(int w, int i) {
-        return MODE == 2 ? (i == 0 ? w : NRB - 1 - w)
-             : MODE == 1 ? (w < NRB ? w : 2 * NRB - 1 - w)
-             : MODE == 3 ? (w < NRB ? w : 0) : w;
+        return MODE == 2 ? (i == 0 ? w : NRB - 1 - w) : MODE == 3 ? (w < NRB ? w : 0) : w;
     }
-    static constexpr int half(int w) { return MODE == 1 ? w / NRB : 0; }
     // relative score work of wave w (16 x 16 score tiles); mode 3 keeps state
     // tiles off the row waves
     static constexpr int score_tiles(int w) {
@@ -243,7 +238,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     constexpr int NTB = Cfg::NTB;
     constexpr int KP = Cfg::KP;
     constexpr int NTI = DK / 16, NTJ = DVT / 16;
-    constexpr int NTJW = R::MODE == 1 ? NTJ / 2 : NTJ;  // output column tiles per wave
+    constexpr int NTJW = NTJ;             // output column tiles per row wave
     constexpr int NKS = DK / (4 * E);     // k-steps over channels
     constexpr int NTK = C / (4 * E);      // k-steps over tokens
     constexpr int PER = C / 64;           // tokens per lane in the gate scan
@@ -254,9 +249,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     constexpr int WS0 = R::WS0, NWS = R::NWS;
     constexpr auto TS = make_tile_split<NTI * NTJ, NW, NRB, R::MODE == 3>(VAR == V_NORM ? NTI : 0, DECAYED ? 2 : 0);
     constexpr int NTS = TS.maxcnt;        // state tiles per wave (at most)
-    static_assert(NTJW >= 1 && (R::MODE != 1 || NTJ % 2 == 0), "value slice too narrow for the roles");
-    static_assert(VAR != V_GDN || ((R::MODE <= 1 || R::MODE == 3) && NRB == 4),
-                  "delta rule: one U row block per wave (pair)");
+    static_assert(NTJW >= 1, "value slice narrower than one tile");
+    static_assert(VAR != V_GDN || ((R::MODE == 0 || R::MODE == 3) && NRB == 4),
+                  "delta rule: one U row block per wave");
 
     // Tile sets: [set][Q | K | V | wV | S_prev^T]. Gate tables per buffer:
     // [0] G_s, [1] exp(G_s), [2] w_s = exp(g_C - G_s), [3] exp(G_{end of s's
@@ -408,7 +403,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             for (int i = 0; i < NQR; ++i) wpre[i] = ld_raw8<TM>(wg + srow * DK + g * (DK / 4) + 8 * i);
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) {
-                const int tj = R::half(wv) * NTJW + jt;
+                const int tj = jt;
                 upre[jt] = ld4<TM>(utg + srow * dv + tj * 16 + 4 * g);
             }
         }
@@ -699,7 +694,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             const float ws = T[2 * C + s];
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) {
-                const int jj = (R::half(wv) * NTJW + jt) * 16;
+                const int jj = jt * 16;
                 f32x4 acc = ucur[jt];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
@@ -923,7 +918,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     auto rows_of = [&](auto w_tag, int c, const TM *X, const float *T, auto check_tag) __attribute__((always_inline)) {
         constexpr int W = decltype(w_tag)::value;
         if constexpr (!R::rows(W)) return;
-        row_block(std::integral_constant<int, R::rb(W, 0)>{}, std::integral_constant<int, R::half(W) * NTJW>{}, c,
+        row_block(std::integral_constant<int, R::rb(W, 0)>{}, std::integral_constant<int, 0>{}, c,
                   X, T, check_tag);
         if constexpr (R::RBW == 2)
             row_block(std::integral_constant<int, R::rb(W, 1)>{}, std::integral_constant<int, 0>{}, c, X, T,
