@@ -23,7 +23,7 @@
 //      (K^T and V^T) are read from the row-major tiles with the gfx950
 //      transpose load. When two chunks' tiles fit in LDS they are double
 //      buffered: chunk c+1 is staged while chunk c is computed, with the loads
-//      two or three chunks ahead in registers and one barrier per chunk;
+//      one or two chunks ahead in registers and one barrier per chunk;
 //      otherwise a single buffer is staged between two barriers. The gate
 //      tables (G, exp(G), exp(g_C - G), exp(g_C)) are built ahead of the chunk
 //      that uses them.
