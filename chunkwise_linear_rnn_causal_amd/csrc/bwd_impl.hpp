@@ -225,48 +225,61 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
     const int L = a.L, nchunks = (L + C - 1) / C;
-    const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
-    const int t0 = c * C, nv = min(C, L - t0);
-    const TI *qg = (const TI *)a.q + ((size_t)bh * L + t0) * DK;
-    const TI *kg = (const TI *)a.k + ((size_t)bh * L + t0) * DK;
-    const TI *vg = (const TI *)a.v + ((size_t)bh * L + t0) * DV;
-    const TI *og = (const TI *)a.dout + ((size_t)bh * L + t0) * DV;
-    const TM *hg = (const TM *)a.hs + ((size_t)bh * nchunks + c) * DK * DV;
-    const TM *dhg = (const TM *)a.dhs + ((size_t)bh * nchunks + c) * DK * DV;
-
-    // ---- stage the chunk
-    if constexpr (DECAY) {
-        if (wv == 0) {
-            const float G = wave_inclusive_sum(lane < nv ? a.lg[(size_t)bh * L + t0 + lane] : 0.f);
-            Gt[lane] = G;
-            if (lane == 63) Gend = G;
-        }
-    }
-    // every load of the chunk is issued before any is used
+    // Persistent: each workgroup takes chunks (batch-head, chunk) = item in
+    // steps of the grid size; the next item's rows and states are loaded into
+    // registers while the current one is computed.
+    const int items = a.BH * nchunks;
     constexpr int NQ = (C * SEGK + 511) / 512, NVV = (C * SEGV + 511) / 512, NS = (DV * SEGK + 511) / 512;
     Raw8<TI> rq[NQ], rk[NQ], rv[NVV], ro[NVV];
     Raw8<TM> rh[NS], rd[NS];
+    float rgl = 0.f;  // wave 0: the log-gate of token `lane`
+    auto fetch = [&](int item) __attribute__((always_inline)) {
+        const int bh = item / nchunks, c = item % nchunks;
+        const int t0 = c * C, nv = min(C, L - t0);
+        const TI *qg = (const TI *)a.q + ((size_t)bh * L + t0) * DK;
+        const TI *kg = (const TI *)a.k + ((size_t)bh * L + t0) * DK;
+        const TI *vg = (const TI *)a.v + ((size_t)bh * L + t0) * DV;
+        const TI *og = (const TI *)a.dout + ((size_t)bh * L + t0) * DV;
+        const TM *hg = (const TM *)a.hs + ((size_t)bh * nchunks + c) * DK * DV;
+        const TM *dhg = (const TM *)a.dhs + ((size_t)bh * nchunks + c) * DK * DV;
+        if constexpr (DECAY) {
+            if (wv == 0) rgl = lane < nv ? a.lg[(size_t)bh * L + t0 + lane] : 0.f;
+        }
 #pragma unroll
-    for (int m = 0; m < NQ; ++m) {
-        const int sid = tid + 512 * m, row = sid / SEGK, off = row * DK + 8 * (sid % SEGK);
-        const bool ok = sid < C * SEGK && row < nv;
-        rq[m] = ok ? ld_raw8<TI>(qg + off) : zero_raw8<TI>();
-        rk[m] = ok ? ld_raw8<TI>(kg + off) : zero_raw8<TI>();
-    }
+        for (int m = 0; m < NQ; ++m) {
+            const int sid = tid + 512 * m, row = sid / SEGK, off = row * DK + 8 * (sid % SEGK);
+            const bool ok = sid < C * SEGK && row < nv;
+            rq[m] = ok ? ld_raw8<TI>(qg + off) : zero_raw8<TI>();
+            rk[m] = ok ? ld_raw8<TI>(kg + off) : zero_raw8<TI>();
+        }
 #pragma unroll
-    for (int m = 0; m < NVV; ++m) {
-        const int sid = tid + 512 * m, row = sid / SEGV, off = row * DV + 8 * (sid % SEGV);
-        const bool ok = sid < C * SEGV && row < nv;
-        rv[m] = ok ? ld_raw8<TI>(vg + off) : zero_raw8<TI>();
-        ro[m] = ok ? ld_raw8<TI>(og + off) : zero_raw8<TI>();
-    }
+        for (int m = 0; m < NVV; ++m) {
+            const int sid = tid + 512 * m, row = sid / SEGV, off = row * DV + 8 * (sid % SEGV);
+            const bool ok = sid < C * SEGV && row < nv;
+            rv[m] = ok ? ld_raw8<TI>(vg + off) : zero_raw8<TI>();
+            ro[m] = ok ? ld_raw8<TI>(og + off) : zero_raw8<TI>();
+        }
 #pragma unroll
-    for (int m = 0; m < NS; ++m) {
-        const int sid = tid + 512 * m;
-        if (sid < DV * SEGK) {
-            const int off = (sid / SEGK) * DK + 8 * (sid % SEGK);
-            rh[m] = ld_raw8<TM>(hg + off);
-            rd[m] = ld_raw8<TM>(dhg + off);
+        for (int m = 0; m < NS; ++m) {
+            const int sid = tid + 512 * m;
+            if (sid < DV * SEGK) {
+                const int off = (sid / SEGK) * DK + 8 * (sid % SEGK);
+                rh[m] = ld_raw8<TM>(hg + off);
+                rd[m] = ld_raw8<TM>(dhg + off);
+            }
+        }
+    };
+
+    auto process = [&](int item, auto &&prefetch_next) __attribute__((always_inline)) {
+    const int bh = item / nchunks, c = item % nchunks;
+    const int t0 = c * C, nv = min(C, L - t0);
+    (void)c;
+    // ---- stage the chunk (its loads were issued one item ago)
+    if constexpr (DECAY) {
+        if (wv == 0) {
+            const float G = wave_inclusive_sum(rgl);
+            Gt[lane] = G;
+            if (lane == 63) Gend = G;
         }
     }
     auto put = [&](const Raw8<TI> &r, TM *dst) __attribute__((always_inline)) {
@@ -305,6 +318,7 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
+    prefetch_next();  // the registers are free: the next item's loads fly during the math
 
     const int w = wv & 3, half = wv >> 2;
     const float gend = DECAY ? Gend : 0.f;
@@ -538,8 +552,18 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
     rterm += __shfl_xor(rterm, 16, 64);
     rterm += __shfl_xor(rterm, 32, 64);
     if (g == 0) RT[half][s] = rterm;
-    __syncthreads();
+    __syncthreads();  // also: every wave is done with this item's tiles
     if (DECAY && tid < C && tid < nv) a.rterm[(size_t)bh * L + t0 + tid] = RT[0][tid] + RT[1][tid];
+    };
+
+    int item = blockIdx.x;
+    if (item < items) fetch(item);
+    for (; item < items; item += gridDim.x) {
+        const int nxt = item + gridDim.x;
+        process(item, [&]() __attribute__((always_inline)) {
+            if (nxt < items) fetch(nxt);
+        });
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -584,6 +608,10 @@ __global__ void __launch_bounds__(256) dgate_kernel(BwdArgs a) {
     }
 }
 
+// Workgroups of the persistent dq/dk/dv kernel: one per CU (its tiles take
+// most of a CU's LDS).
+constexpr int kBwdGrid = 256;
+
 template <typename TI, int DK, int DV, bool DECAY>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t st) {
     constexpr int DVT = DV >= 64 ? 64 : DV;  // value slices of the state scans
@@ -592,7 +620,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t st) {
     b.nsplit = DV / DVT;
     hipLaunchKernelGGL((state_scans_kernel<TI, DK, DVT, DECAY>), dim3(2 * a.BH * b.nsplit), dim3(256), 0, st, b);
     if (nchunks > 0)
-        hipLaunchKernelGGL((bwd_dqkv_kernel<TI, DK, DV, DECAY>), dim3(a.BH * nchunks), dim3(512), 0, st, b);
+        hipLaunchKernelGGL((bwd_dqkv_kernel<TI, DK, DV, DECAY>), dim3(min(a.BH * nchunks, kBwdGrid)), dim3(512), 0, st, b);
     if (DECAY && nchunks > 0 && a.glg) hipLaunchKernelGGL((dgate_kernel<DK>), dim3(a.BH), dim3(256), 0, st, b);
     return hipGetLastError();
 }
