@@ -68,7 +68,8 @@ def kernel_source_hash() -> str:
 
 
 # ---------------------------------------------------------------------------
-# algorithmic work per step (chunkwise method; see the design doc for the derivation)
+# algorithmic work per step (chunkwise method: flops of the chunk products,
+# bytes of every input read once and every output written once)
 # ---------------------------------------------------------------------------
 def chunk_work(c: dict) -> tuple[float, float]:
     """(flop, bytes) of one chunk forward over the workload, fp32 output + state."""
@@ -343,7 +344,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(independent batch-heads shard across GPUs with no exchange; see DESIGN.md).",
+              "(independent batch-heads would shard across GPUs with no exchange).",
               file=sys.stderr)
         return 2
     if args.copy_calibration:
