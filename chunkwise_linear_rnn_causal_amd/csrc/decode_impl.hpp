@@ -24,13 +24,24 @@
 
 namespace la {
 
+// Occupancy: the state in flight is what keeps HBM busy. Without the retrieval
+// pass a wave needs 65 registers when the compiler may use up to 72, which gives
+// 7 waves per SIMD (6 at its own choice of 74; 8 at 64 was no faster). The
+// delta rule holds the whole state across its barrier and is left to the
+// compiler (127 registers, 4 waves per SIMD; a cap at 5 waves spills), and so
+// is the per-channel gate with fp32 rows (a cap at 7 waves spills).
+template <int VAR, typename TI>
+constexpr int decode_min_waves() {
+    return (VAR == V_GDN || (VAR == V_VDECAY && sizeof(TI) == 4)) ? 1 : 7;
+}
+
 template <int VAR, typename TI, typename TO, int DK, int DV>
-__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_min_waves<VAR, TI>(), 8)))
+decode_kernel(DecodeArgs a) {
     constexpr int CG = DV / 4;        // 16-byte column groups per row
     constexpr int RG = 256 / CG;      // row groups
     constexpr int RPT = DK / RG;      // rows per thread
     static_assert(RPT >= 1 && DK % RG == 0, "shape");
-    constexpr int RGW = 64 / CG;      // row groups inside one wave
 
     __shared__ f32x4 red[4][CG];
 
@@ -107,7 +118,6 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         const f32x4 o = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
         st4<TO>((TO *)a.o + h * DV + 4 * tid, o);
     }
-    (void)RGW;
 }
 
 template <int VAR, typename TI, typename TO, int DK, int DV>
