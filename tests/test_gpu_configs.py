@@ -1,6 +1,6 @@
 """GPU parity at the full sizes of the workloads, in the launch configuration
 the benchmark times (la_chunk_fwd with C = 64 and a final-state output; 100
-back-to-back la_decode_step calls; one la_short_conv). The oracle checks sampled
+back-to-back la_decode_step calls, decay and delta rule; one la_short_conv). The oracle checks sampled
 batch-heads, which the seeded generator regenerates on their own (every (tensor,
 b, h) slice has its own random stream), the whole first decode step, and every
 element of the short convolution."""
@@ -43,24 +43,31 @@ def test_full_size_chunk_config(name):
     assert bool(torch.isfinite(o.float()).all())
 
 
-def test_full_size_decode_config():
+@pytest.mark.parametrize("variant", ["decay", "gated_delta"])
+def test_full_size_decode_config(variant):
+    """100 decode steps at the decode workload's shape; the delta rule runs at the
+    same shape with beta = sigmoid(N(0,1)) per sequence-head, as the benchmark times it."""
     c = W.CONFIGS["decode_decay_bf16_n512h32_d128"]
     N, H, dk, dv, steps = c["N"], c["H"], c["dk"], c["dv"], c["steps"]
-    print("[config] decode full size", flush=True)
+    delta = variant == "gated_delta"
+    print(f"[config] decode full size, {variant}", flush=True)
     S0 = W.make_decode_state(N, H, dk, dv, seed=0)
     S = dev(S0)
     heads = [(0, 0), (N - 1, H - 1), (N // 2, H // 3), (17, 5)]
-    hs = {name: [] for name in ("q", "k", "v", "lg")}
+    hs = {name: [] for name in ("q", "k", "v", "lg", "beta")}
     o_last = None
     for step in range(steps):
-        st = W.make_decode_step(N, H, dk, dv, step=step, seed=0)
-        o = la.la_decode_step("decay", dev(st.q), dev(st.k), dev(st.v), dev(st.log_gate), S)
-        for name, x in (("q", st.q), ("k", st.k), ("v", st.v), ("lg", st.log_gate)):
-            hs[name].append(np.stack([x[n, h] for n, h in heads]))
+        st = W.make_decode_step(N, H, dk, dv, step=step, seed=0, with_beta=delta)
+        o = la.la_decode_step(variant, dev(st.q), dev(st.k), dev(st.v), dev(st.log_gate), S,
+                              beta=dev(st.beta) if delta else None)
+        for name, x in (("q", st.q), ("k", st.k), ("v", st.v), ("lg", st.log_gate), ("beta", st.beta)):
+            if x is not None:
+                hs[name].append(np.stack([x[n, h] for n, h in heads]))
         if step == 0:
             torch.cuda.synchronize()
-            ro, rS = oracle.decode_step("decay", W.to_f64(st.q), W.to_f64(st.k), W.to_f64(st.v),
-                                        st.log_gate.astype(np.float64), S0)
+            ro, rS = oracle.decode_step(variant, W.to_f64(st.q), W.to_f64(st.k), W.to_f64(st.v),
+                                        st.log_gate.astype(np.float64), S0,
+                                        beta=st.beta.astype(np.float64) if delta else None)
             assert_close(host64(o), ro, TOL["bf16"], "step 1 o (all heads)")
             assert_close(host64(S), rS, 1e-4, "step 1 state (all heads)")
             del rS
@@ -68,13 +75,14 @@ def test_full_size_decode_config():
     torch.cuda.synchronize()
     Sref = np.stack([S0[n, h] for n, h in heads]).astype(np.float64)
     for step in range(steps):
-        ro, Sref = oracle.decode_step("decay", W.to_f64(hs["q"][step]), W.to_f64(hs["k"][step]),
-                                      W.to_f64(hs["v"][step]), hs["lg"][step].astype(np.float64), Sref)
+        ro, Sref = oracle.decode_step(variant, W.to_f64(hs["q"][step]), W.to_f64(hs["k"][step]),
+                                      W.to_f64(hs["v"][step]), hs["lg"][step].astype(np.float64), Sref,
+                                      beta=hs["beta"][step].astype(np.float64) if delta else None)
     got_o = np.stack([host64(o_last[n, h]) for n, h in heads])
     got_S = np.stack([host64(S[n, h]) for n, h in heads])
     e_o = assert_close(got_o, ro, TOL["bf16"], "step 100 o")
     e_s = assert_close(got_S, Sref, 1e-4, "step 100 state")
-    print(f"[config] decode step100 err_o={e_o:.2e} err_state={e_s:.2e}", flush=True)
+    print(f"[config] decode {variant} step100 err_o={e_o:.2e} err_state={e_s:.2e}", flush=True)
 
 
 def test_full_size_short_conv_config():
