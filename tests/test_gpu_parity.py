@@ -162,7 +162,7 @@ def test_associative_recall_on_gpu():
 # decode step
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("dk,dv", [(dk, dv) for dk in (32, 64, 128) for dv in (32, 64, 128)])
 @pytest.mark.parametrize("var", ["plain", "decay", "gated_delta", "deltanet"])
 def test_decode_matches_oracle(var, dt, dk, dv):
     """One-token steps, three in a row on the same state; "deltanet" is the delta

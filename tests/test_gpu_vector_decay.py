@@ -105,7 +105,7 @@ def test_vector_decay_wide_grid():
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("dk,dv", [(32, 32), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("dk,dv", [(dk, dv) for dk in (32, 64, 128) for dv in (32, 64, 128)])
 def test_vector_decay_decode(dt, dk, dv):
     """Three one-token steps in place with per-channel gates, against the oracle."""
     N, H = 5, 3
