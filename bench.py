@@ -118,10 +118,11 @@ def bwd_work(c: dict) -> tuple[float, float]:
 
 
 def decode_work(c: dict) -> tuple[float, float]:
-    """(flop, bytes) of ONE decode step over all sequence-heads."""
+    """(flop, bytes) of ONE decode step over all sequence-heads: the fp32 state read
+    and written, q, k, v in bf16, the fp32 log-gate, o out in bf16."""
     NH, dk, dv = c["N"] * c["H"], c["dk"], c["dv"]
     flop = 5.0 * dk * dv * NH                                    # gamma*S + k v^T, then S^T q
-    nbytes = NH * (2 * dk * dv * 4 + (2 * dk + dv) * 2 + 4 + dv * 4)
+    nbytes = NH * (2 * dk * dv * 4 + (2 * dk + dv) * 2 + 4 + dv * 2)
     return flop, nbytes
 
 
@@ -202,7 +203,7 @@ def bench_decode(name: str, steps: int, warmup: int, device, variant: str = "dec
                            range(nsteps)))
     ins = [(to_dev(h.q, device), to_dev(h.k, device), to_dev(h.v, device), to_dev(h.log_gate, device),
             to_dev(h.beta, device)) for h in host]
-    o = torch.empty((N, H, dv), dtype=torch.float32, device=device)
+    o = torch.empty((N, H, dv), dtype=torch.bfloat16, device=device)
     flop1, bytes1 = decode_work(c)
     if delta:  # + retrieval S^T k (2 d_k d_v flop) and beta (4 bytes) per head
         flop1 += 2.0 * dk * dv * N * H

@@ -45,8 +45,9 @@ def test_full_size_chunk_config(name):
 
 @pytest.mark.parametrize("variant", ["decay", "gated_delta"])
 def test_full_size_decode_config(variant):
-    """100 decode steps at the decode workload's shape; the delta rule runs at the
-    same shape with beta = sigmoid(N(0,1)) per sequence-head, as the benchmark times it."""
+    """100 decode steps at the decode workload's shape, bf16 output; the delta rule
+    runs at the same shape with beta = sigmoid(N(0,1)) per sequence-head, as the
+    benchmark times it."""
     c = W.CONFIGS["decode_decay_bf16_n512h32_d128"]
     N, H, dk, dv, steps = c["N"], c["H"], c["dk"], c["dv"], c["steps"]
     delta = variant == "gated_delta"
@@ -59,7 +60,7 @@ def test_full_size_decode_config(variant):
     for step in range(steps):
         st = W.make_decode_step(N, H, dk, dv, step=step, seed=0, with_beta=delta)
         o = la.la_decode_step(variant, dev(st.q), dev(st.k), dev(st.v), dev(st.log_gate), S,
-                              beta=dev(st.beta) if delta else None)
+                              beta=dev(st.beta) if delta else None, out_dtype=torch.bfloat16)
         for name, x in (("q", st.q), ("k", st.k), ("v", st.v), ("lg", st.log_gate), ("beta", st.beta)):
             if x is not None:
                 hs[name].append(np.stack([x[n, h] for n, h in heads]))

@@ -166,7 +166,8 @@ def test_associative_recall_on_gpu():
 @pytest.mark.parametrize("var", ["plain", "decay", "gated_delta", "deltanet"])
 def test_decode_matches_oracle(var, dt, dk, dv):
     """One-token steps, three in a row on the same state; "deltanet" is the delta
-    rule without a log-gate (alpha = 1)."""
+    rule without a log-gate (alpha = 1). With bf16 inputs the middle step writes
+    o in bf16."""
     N, H = 5, 3
     S0 = W.make_decode_state(N, H, dk, dv, seed=2)
     S = dev(S0)
@@ -176,7 +177,10 @@ def test_decode_matches_oracle(var, dt, dk, dv):
     for step in range(3):
         st = W.make_decode_step(N, H, dk, dv, step=step, seed=2, dtype=dt, with_beta=delta)
         lg = st.log_gate if var in ("decay", "gated_delta") else None
-        o = la.la_decode_step(kind, dev(st.q), dev(st.k), dev(st.v), dev(lg), S, beta=dev(st.beta))
+        o_bf16 = dt == "bf16" and step == 1
+        o = la.la_decode_step(kind, dev(st.q), dev(st.k), dev(st.v), dev(lg), S, beta=dev(st.beta),
+                              out_dtype=torch.bfloat16 if o_bf16 else None)
+        assert o.dtype == (torch.bfloat16 if o_bf16 else torch.float32)
         torch.cuda.synchronize()
         ro, Sref = oracle.decode_step(kind, W.to_f64(st.q), W.to_f64(st.k), W.to_f64(st.v),
                                       None if lg is None else lg.astype(np.float64), Sref,

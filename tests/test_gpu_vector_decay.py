@@ -107,7 +107,8 @@ def test_vector_decay_wide_grid():
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("dk,dv", [(dk, dv) for dk in (32, 64, 128) for dv in (32, 64, 128)])
 def test_vector_decay_decode(dt, dk, dv):
-    """Three one-token steps in place with per-channel gates, against the oracle."""
+    """Three one-token steps in place with per-channel gates, against the oracle;
+    with bf16 inputs the middle step writes o in bf16."""
     N, H = 5, 3
     S0 = W.make_decode_state(N, H, dk, dv, seed=37)
     S = dev(S0)
@@ -116,7 +117,10 @@ def test_vector_decay_decode(dt, dk, dv):
     for step in range(3):
         st = W.make_decode_step(N, H, dk, dv, step=step, seed=37, dtype=dt)
         lg = (np.log(1.0 / (1.0 + np.exp(-rng.normal(0.0, 1.0, size=(N, H, dk))))) / 16.0).astype(np.float32)
-        o = la.la_decode_step(VD, dev(st.q), dev(st.k), dev(st.v), dev(lg), S)
+        o_bf16 = dt == "bf16" and step == 1
+        o = la.la_decode_step(VD, dev(st.q), dev(st.k), dev(st.v), dev(lg), S,
+                              out_dtype=torch.bfloat16 if o_bf16 else None)
+        assert o.dtype == (torch.bfloat16 if o_bf16 else torch.float32)
         torch.cuda.synchronize()
         ro, Sref = oracle.decode_step(VD, W.to_f64(st.q), W.to_f64(st.k), W.to_f64(st.v),
                                       lg.astype(np.float64), Sref)
