@@ -1,8 +1,11 @@
-"""HIP graph capture of the entry points. They allocate nothing and issue no
-memset, copy or synchronisation on the stream, so a sequence of calls can be
-captured once and replayed. Each test replays its graph several times, with eager
-work and synchronisations between the replays, and checks every replay against
-the eager result bit for bit (the kernels are deterministic)."""
+"""HIP graph capture of the entry points, and independent calls on two streams.
+
+The entry points allocate nothing and issue no memset, copy or synchronisation on
+the stream, so a sequence of calls can be captured once and replayed. Each graph
+test replays its graph several times, with eager work and synchronisations
+between the replays, and checks every replay against the eager result bit for bit
+(the kernels are deterministic). Calls with their own buffers and workspaces may
+run on two streams at once."""
 import pytest
 import torch
 
@@ -100,3 +103,52 @@ def test_chunk_forward_in_a_graph(var):
         torch.cuda.synchronize()
         for name, t, r in zip(("o", "state", "z"), got, ref):
             assert torch.equal(t, r), f"replay {rep}: {name}"
+
+
+def test_independent_calls_on_two_streams():
+    """Two delta-rule forwards and two decode steps, each with its own buffers and
+    workspace, issued on two streams at once: the same bits as one after the other."""
+    print("[streams] two delta-rule forwards and two decode steps", flush=True)
+    B, H, L, dk, dv, C = 2, 4, 5 * 64 + 7, 128, 128, 64
+    calls = []
+    for seed in (31, 32):
+        inp = W.make_chunk_inputs("gated_delta", "bf16", B, H, L, dk, dv, seed=seed, with_state=True)
+        args = [dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.log_gate), dev(inp.beta), dev(inp.state_in)]
+        o = torch.empty((B, H, L, dv), dtype=torch.float32, device="cuda")
+        S = torch.empty((B, H, dk, dv), dtype=torch.float32, device="cuda")
+        ws = torch.empty(la.la_chunk_fwd_workspace_size("gated_delta", 1, B, H, L, dk, dv, C),
+                         dtype=torch.uint8, device="cuda")
+        calls.append((args, o, S, ws))
+    N, Hd = 32, 8
+    dec = []
+    for seed in (41, 42):
+        S0 = dev(W.make_decode_state(N, Hd, dk, dv, seed=seed))
+        st = W.make_decode_step(N, Hd, dk, dv, step=0, seed=seed)
+        dec.append((S0, S0.clone(), [dev(st.q), dev(st.k), dev(st.v), dev(st.log_gate)],
+                    torch.empty((N, Hd, dv), dtype=torch.float32, device="cuda")))
+
+    def run(i, stream):
+        (q, k, v, lg, be, s_in), o, S, ws = calls[i]
+        la.la_chunk_fwd("gated_delta", q, k, v, lg, be, state_in=s_in, C=C, o=o, state_out=S,
+                        workspace=ws, stream=stream)
+        _, Sd, (dq, dk_, dv_, dlg), do = dec[i]
+        la.la_decode_step("decay", dq, dk_, dv_, dlg, Sd, o=do, stream=stream)
+
+    cur = torch.cuda.current_stream()
+    for i in range(2):
+        run(i, cur)
+    torch.cuda.synchronize()
+    ref = [(c[1].clone(), c[2].clone(), d[1].clone(), d[3].clone()) for c, d in zip(calls, dec)]
+    for c, d in zip(calls, dec):
+        c[1].fill_(0)
+        c[2].fill_(0)
+        d[1].copy_(d[0])
+        d[3].fill_(0)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for i in range(2):
+        run(i, streams[i])
+    torch.cuda.synchronize()
+    for i, (c, d) in enumerate(zip(calls, dec)):
+        for name, got, r in zip(("o", "state", "decode state", "decode o"), (c[1], c[2], d[1], d[3]), ref[i]):
+            assert torch.equal(got, r), f"call {i}: {name}"
