@@ -3,26 +3,32 @@
 
 A step is one call of the hot path over one batch of synthetic input that is
 already resident in HBM:
-  - chunk workloads: one la_chunk_fwd (C = 64, fp32 output and final state);
+  - chunk workloads: one la_chunk_fwd (C = 64, the final state written; o in
+    bf16 where bf16 output meets the bf16 tolerance at full size, the decay and
+    delta-rule workloads, else fp32);
   - decode workload: 100 back-to-back la_decode_step calls (one "step" = 100
     tokens per sequence-head, as the workload is quoted).
   - short-convolution workload: one la_short_conv over q, k and v;
   - backward workload: one la_chunk_bwd (gradients of q, k, v and the gates).
-The headline workload (the JSON line's value) is the normalized kernel linear
-attention at B=8, H=16, L=2048, d=64; by default the other workloads are timed
-too and reported under "workloads". Every workload is timed with HIP
+The headline workload (the JSON line's value) is the largest single-GPU
+workload, gated linear attention with data-dependent scalar decay at B=4, H=32,
+L=8192, d=128; by default the other workloads are timed too and reported under
+"workloads". Every workload is timed with HIP
 events on the stream the kernels run on, over K timed steps after W warm-up steps.
 Working sets below twice the 256 MB Infinity Cache are rotated over several
 input copies so that the timed steps read HBM, not the cache.
 
-Roofline: the algorithmic bytes and flops of one step (inputs read once, outputs
-written once; flop counts of the chunkwise method, no credit for masking) divided
-by the measured time, against 8 TB/s HBM and 2.517 PFLOP/s dense fp16/bf16 MFMA.
+Roofline: the algorithmic bytes and flops of one step (q, k, v, the gates read
+once and o written once in bf16: the non-materialized lower bound; flop counts of
+the chunkwise method, no credit for masking) divided by the measured time,
+against 8 TB/s HBM and 2.517 PFLOP/s dense fp16/bf16 MFMA. The bytes the launch
+actually moves (fp32 o where the workload keeps it, and the final state) are
+reported beside them as "bytes_as_launched".
 `traffic` is filled from profiles/traffic.json when its recorded kernel-source
 hash matches the current sources, else null.
 
 The CPU baseline times the fp64 oracle (tests' reference implementation) over the
-whole headline workload on the host's cores.
+whole headline workload on every core of the process's CPU affinity set.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--only] [--no-cpu-baseline] [--copy-calibration BYTES]
@@ -45,7 +51,7 @@ sys.path.insert(0, ROOT)
 
 import workloads as W  # noqa: E402
 
-HEADLINE = "normalized_bf16_b8h16_l2048_d64"
+HEADLINE = "decay_bf16_b4h32_l8192_d128"
 METRIC = "tokens/sec + % bf16 MFMA peak (chunk fwd); decode state GB/s % of HBM peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2517.0     # 256 CU x 4096 flop/clk x 2.4 GHz, dense fp16/bf16
@@ -71,8 +77,18 @@ def kernel_source_hash() -> str:
 # algorithmic work per step (chunkwise method: flops of the chunk products,
 # bytes of every input read once and every output written once)
 # ---------------------------------------------------------------------------
-def chunk_work(c: dict) -> tuple[float, float]:
-    """(flop, bytes) of one chunk forward over the workload, fp32 output + state."""
+def o_dtype(c: dict) -> str:
+    """Output dtype the workload is benchmarked (and tested at full size) with."""
+    return c.get("o_dtype", "f32")
+
+
+def chunk_work(c: dict) -> tuple[float, float, float]:
+    """(flop, algorithmic bytes, bytes as launched) of one chunk forward.
+
+    Algorithmic bytes: q, k, v and the gates read once, o written once in the
+    input dtype (the non-materialized lower bound). As launched: o in the dtype
+    the launch writes (fp32 where bf16 output would break the tolerance) plus
+    the fp32 final state."""
     B, H, L, dk, dv, C = c["B"], c["H"], c["L"], c["dk"], c["dv"], c["C"]
     BH = B * H
     esz = 2 if c["dtype"] == "bf16" else 4
@@ -81,15 +97,16 @@ def chunk_work(c: dict) -> tuple[float, float]:
     else:
         per_tok = 2 * C * (dk + dv) + 4 * dk * dv
     flop = per_tok * BH * L
-    nbytes = BH * L * ((2 * dk + dv) * esz + dv * 4)           # q, k, v in; o out (fp32)
+    nbytes = BH * L * (2 * dk + dv) * esz                        # q, k, v in
     if c["variant"] in ("decay", "gated_delta"):
         nbytes += BH * L * 4                                     # log-gates
     if c["variant"] == "vector_decay":
         nbytes += BH * L * dk * 4                                # one log-gate per key channel
     if c["variant"] == "gated_delta":
         nbytes += BH * L * 4                                     # beta
-    nbytes += BH * dk * dv * 4                                   # final state
-    return flop, nbytes
+    algo = nbytes + BH * L * dv * esz                            # o out in the input dtype
+    launched = nbytes + BH * L * dv * (2 if o_dtype(c) == "bf16" else 4) + BH * dk * dv * 4
+    return flop, algo, launched
 
 
 def conv_work(c: dict) -> tuple[float, float]:
@@ -161,13 +178,14 @@ def bench_chunk(name: str, steps: int, warmup: int, device) -> dict:
     import chunkwise_linear_rnn_causal_amd as la
     c = W.CONFIGS[name]
     inp = W.config_chunk_inputs(name, seed=0)
-    flop, nbytes = chunk_work(c)
-    copies = max(1, min(4, math.ceil(2 * CACHE_BYTES / nbytes)))
+    flop, nbytes, launched = chunk_work(c)
+    copies = max(1, min(4, math.ceil(2 * CACHE_BYTES / launched)))
+    odt = torch.bfloat16 if o_dtype(c) == "bf16" else torch.float32
     sets = []
     for _ in range(copies):
         s = dict(q=to_dev(inp.q, device), k=to_dev(inp.k, device), v=to_dev(inp.v, device),
                  lg=to_dev(inp.log_gate, device), beta=to_dev(inp.beta, device))
-        s["o"] = torch.empty((c["B"], c["H"], c["L"], c["dv"]), dtype=torch.float32, device=device)
+        s["o"] = torch.empty((c["B"], c["H"], c["L"], c["dv"]), dtype=odt, device=device)
         s["S"] = torch.empty((c["B"], c["H"], c["dk"], c["dv"]), dtype=torch.float32, device=device)
         dt = 1 if c["dtype"] == "bf16" else 0
         wsb = la.la_chunk_fwd_workspace_size(c["variant"], dt, c["B"], c["H"], c["L"], c["dk"], c["dv"], c["C"])
@@ -184,8 +202,10 @@ def bench_chunk(name: str, steps: int, warmup: int, device) -> dict:
     t = ms / 1e3
     toks = c["B"] * c["L"]
     return dict(workload=name, variant=c["variant"], tokens_per_s=toks / t, ms_per_step=t * 1e3,
-                wall_ms_per_step=wall_ms, flop=flop, bytes=nbytes,
+                wall_ms_per_step=wall_ms, flop=flop, bytes=nbytes, bytes_as_launched=launched,
+                output_dtype=o_dtype(c),
                 achieved_gbs=nbytes / t / 1e9, achieved_tflops=flop / t / 1e12,
+                launched_gbs=launched / t / 1e9,
                 hbm_frac=nbytes / t / 1e9 / HBM_PEAK_GBS, mfma_frac=flop / t / 1e12 / MFMA_PEAK_TFLOPS,
                 roofline_frac=max(nbytes / (HBM_PEAK_GBS * 1e9), flop / (MFMA_PEAK_TFLOPS * 1e12)) / t,
                 input_copies=copies, B=c["B"], H=c["H"], L=c["L"], d_k=c["dk"], d_v=c["dv"], C=c["C"])
@@ -203,11 +223,13 @@ def bench_decode(name: str, steps: int, warmup: int, device, variant: str = "dec
                            range(nsteps)))
     ins = [(to_dev(h.q, device), to_dev(h.k, device), to_dev(h.v, device), to_dev(h.log_gate, device),
             to_dev(h.beta, device)) for h in host]
-    o = torch.empty((N, H, dv), dtype=torch.bfloat16, device=device)
+    # o in bf16 for the decay step (the workload's layout); the delta rule writes
+    # fp32 o, because bf16 rounding of its output alone reaches the bf16 tolerance
+    o = torch.empty((N, H, dv), dtype=torch.float32 if delta else torch.bfloat16, device=device)
     flop1, bytes1 = decode_work(c)
-    if delta:  # + retrieval S^T k (2 d_k d_v flop) and beta (4 bytes) per head
+    if delta:  # + retrieval S^T k (2 d_k d_v flop), beta (4 bytes) and fp32 o per head
         flop1 += 2.0 * dk * dv * N * H
-        bytes1 += 4 * N * H
+        bytes1 += 4 * N * H + 2 * dv * N * H
     stream = torch.cuda.current_stream(device)
 
     def step(_):
@@ -287,14 +309,25 @@ def bench_bwd(name: str, steps: int, warmup: int, device) -> dict:
                 C=c["C"])
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(name: str, min_seconds: float = 10.0) -> dict:
-    """Time the fp64 oracle over the whole workload on the host cores."""
+    """Time the fp64 oracle over the whole workload on every core of the affinity set."""
     import oracle
     c = W.CONFIGS[name]
     inp = W.config_chunk_inputs(name, seed=0)
     args = [inp.f64(x) for x in ("q", "k", "v")]
     kw = dict(log_gate=inp.f64("log_gate"), beta=inp.f64("beta"))
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores = len(os.sched_getaffinity(0))
     passes, t0 = 0, time.perf_counter()
     while True:
         oracle.forward(c["variant"], *args, threads=cores, **kw)
@@ -303,9 +336,10 @@ def cpu_baseline(name: str, min_seconds: float = 10.0) -> dict:
         if el >= min_seconds:
             break
     toks = c["B"] * c["L"] * passes
-    return dict(value=toks / el, unit="tokens/s", cores=cores, kind="oracle",
+    return dict(value=toks / el, unit="tokens/s", cores=cores, cpu_model=cpu_model(), kind="oracle",
                 sample=f"whole workload ({c['B'] * c['H']} batch-heads x {c['L']} tokens), "
-                       f"{passes} passes, {el:.1f} s wall, fp64 per-token recurrence")
+                       f"{passes} passes, {el:.1f} s wall, fp64 per-token recurrence, "
+                       f"OpenMP over batch-heads on {cores} threads")
 
 
 def traffic_for(workload: str):
@@ -389,6 +423,11 @@ def main() -> int:
         roof = dict(bound="mfma", achieved=head["achieved_tflops"], peak=MFMA_PEAK_TFLOPS,
                     unit="TFLOP/s", frac=head["achieved_tflops"] / MFMA_PEAK_TFLOPS)
     roof["traffic"] = traffic_for(args.workload)
+    if "bytes_as_launched" in head:
+        roof["algorithmic_bytes_per_launch"] = head["bytes"]
+        roof["bytes_as_launched"] = head["bytes_as_launched"]
+        roof["bytes_as_launched_note"] = ("o written in " + head["output_dtype"] +
+                                          " plus the fp32 final state; frac uses the algorithmic bytes")
 
     line = {
         "metric": METRIC,
@@ -406,7 +445,7 @@ def main() -> int:
         "config": {"workload": args.workload, "variant": c.get("variant"), "B": c.get("B"),
                    "H": c.get("H"), "L": c.get("L"), "d_k": c["dk"], "d_v": c["dv"], "C": c.get("C"),
                    "inputs": c["dtype"], "mfma_operands": "f16" if c["dtype"] == "bf16" else "f32",
-                   "accumulate": "f32", "output": "f32", "parallelism": "single-gpu"},
+                   "accumulate": "f32", "output": o_dtype(c), "parallelism": "single-gpu"},
         "roofline": roof,
         "mfma": {"achieved": head["achieved_tflops"], "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": head["mfma_frac"]},

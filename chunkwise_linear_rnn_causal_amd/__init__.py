@@ -92,6 +92,30 @@ def _ptr(x) -> Optional[int]:
     return x.data_ptr()
 
 
+def _check(name: str, x, shape, dtype, device, required: bool = False) -> None:
+    """Raise ValueError unless x is None (and not required) or a contiguous tensor of
+    exactly this shape and dtype on this device. Every pointer the library reads or
+    writes goes through here first, so a wrong shape, dtype or device is a Python
+    error instead of an out-of-bounds device access."""
+    if x is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {tuple(shape)}")
+    if x.dtype != dtype:
+        raise ValueError(f"{name} has dtype {x.dtype}, expected {dtype}")
+    if x.device != device:
+        raise ValueError(f"{name} is on {x.device}, expected {device}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_device(device) -> None:
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {device}")
+
+
 def _stream(dev, stream) -> Optional[int]:
     import torch
     if stream is None:
@@ -125,9 +149,26 @@ def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None,
     """
     import torch
     lib = load_library()
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
     B, H, L, d_k = q.shape
     d_v = v.shape[-1]
     dt = _dt(q)
+    f32, dev_ = torch.float32, q.device
+    _check("k", k, (B, H, L, d_k), q.dtype, dev_, required=True)
+    _check("v", v, (B, H, L, d_v), q.dtype, dev_, required=True)
+    gate_shape = (B, H, L, d_k) if variant == "vector_decay" else (B, H, L)
+    _check("log_gate", log_gate, gate_shape, f32, dev_)
+    _check("beta", beta, (B, H, L), f32, dev_)
+    _check("state_in", state_in, (B, H, d_k, d_v), f32, dev_)
+    _check("z_in", z_in, (B, H, d_k), f32, dev_)
+    if o is not None:
+        _check("o", o, (B, H, L, d_v), o.dtype, dev_)
+    _check("state_out", state_out, (B, H, d_k, d_v), f32, dev_)
+    _check("z_out", z_out, (B, H, d_k), f32, dev_)
+    _check_device(dev_)
     if o is None:
         o = torch.empty((B, H, L, d_v), dtype=out_dtype or torch.float32, device=q.device)
     if want_state and state_out is None:
@@ -140,6 +181,8 @@ def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None,
         if ws_bytes:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     else:
+        if workspace.device != dev_ or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
         ws_bytes = workspace.numel() * workspace.element_size()
     st = lib.la_chunk_fwd(VARIANTS[variant], dt, _dt(o), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
                           _ptr(beta), _ptr(state_in), _ptr(z_in), _ptr(o), _ptr(state_out),
@@ -156,8 +199,22 @@ def la_decode_step(variant: str, q, k, v, log_gate, state, *, o=None, out_dtype=
     updated in place. Returns o [N, H, d_v] (fp32 unless out_dtype/o say bf16)."""
     import torch
     lib = load_library()
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [N, H, d]")
     N, H, d_k = q.shape
     d_v = v.shape[-1]
+    f32, dev_ = torch.float32, q.device
+    _dt(q)
+    _check("k", k, (N, H, d_k), q.dtype, dev_, required=True)
+    _check("v", v, (N, H, d_v), q.dtype, dev_, required=True)
+    _check("log_gate", log_gate, (N, H, d_k) if variant == "vector_decay" else (N, H), f32, dev_)
+    _check("beta", beta, (N, H), f32, dev_)
+    _check("state", state, (N, H, d_k, d_v), f32, dev_, required=True)
+    if o is not None:
+        _check("o", o, (N, H, d_v), o.dtype, dev_)
+    _check_device(dev_)
     if o is None:
         o = torch.empty((N, H, d_v), dtype=out_dtype or torch.float32, device=q.device)
     st = lib.la_decode_step(VARIANTS[variant], _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
@@ -189,10 +246,23 @@ def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_sta
     """
     import torch
     lib = load_library()
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
     B, H, L, d_k = q.shape
     d_v = v.shape[-1]
     dt = _dt(q)
-    dev_ = q.device
+    dev_, f32 = q.device, torch.float32
+    _check("k", k, (B, H, L, d_k), q.dtype, dev_, required=True)
+    _check("v", v, (B, H, L, d_v), q.dtype, dev_, required=True)
+    _check("d_o", d_o, (B, H, L, d_v), q.dtype, dev_, required=True)
+    _check("log_gate", log_gate, (B, H, L), f32, dev_)
+    _check("state_in", state_in, (B, H, d_k, d_v), f32, dev_)
+    _check("d_state_out", d_state_out, (B, H, d_k, d_v), f32, dev_)
+    _check_device(dev_)
+    if workspace is not None and (workspace.device != dev_ or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on q's device")
     dq = torch.empty((B, H, L, d_k), dtype=torch.float32, device=dev_)
     dk = torch.empty((B, H, L, d_k), dtype=torch.float32, device=dev_)
     dv = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev_)
@@ -233,6 +303,8 @@ def la_short_conv(q=None, k=None, v=None, w_q=None, w_k=None, w_v=None, *, q_sta
     if not given or any((x is None) != (w is None) for x, w in zip(xs, ws)):
         raise ValueError("la_short_conv needs at least one of q, k, v, each with its taps")
     ref = given[0]
+    if ref.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
     B, H, L = ref.shape[:3]
     d_k = q.shape[-1] if q is not None else (k.shape[-1] if k is not None else 8)
     d_v = v.shape[-1] if v is not None else 8
@@ -240,6 +312,21 @@ def la_short_conv(q=None, k=None, v=None, w_q=None, w_k=None, w_v=None, *, q_sta
     outs = [q_out, k_out, v_out]
     sins = [q_state_in, k_state_in, v_state_in]
     souts = [q_state_out, k_state_out, v_state_out]
+    dev_, f32 = ref.device, torch.float32
+    _dt(ref)
+    for i, (nm, x, w) in enumerate(zip("qkv", xs, ws)):
+        if x is None:
+            for extra, what in ((sins[i], "state_in"), (outs[i], "out"), (souts[i], "state_out")):
+                if extra is not None:
+                    raise ValueError(f"{nm}_{what} given without {nm}")
+            continue
+        d = d_v if nm == "v" else d_k
+        _check(nm, x, (B, H, L, d), ref.dtype, dev_, required=True)
+        _check(f"w_{nm}", w, (H, d, K), f32, dev_, required=True)
+        _check(f"{nm}_state_in", sins[i], (B, H, K - 1, d), ref.dtype, dev_)
+        _check(f"{nm}_out", outs[i], (B, H, L, d), ref.dtype, dev_)
+        _check(f"{nm}_state_out", souts[i], (B, H, K - 1, d), ref.dtype, dev_)
+    _check_device(dev_)
     for i, x in enumerate(xs):
         if x is None:
             continue

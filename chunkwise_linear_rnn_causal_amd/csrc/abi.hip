@@ -53,6 +53,15 @@ size_t elem_size(la_dtype dt) { return dt == LA_BF16 ? 2 : 4; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// The kernels address the rows of one head with 32-bit element offsets (a
+// 64-bit base per head): every element offset inside a head, up to
+// ceil(L / C) * C rows of max(d_k, d_v) elements (per-channel gates: d_k per
+// token), must stay below 2^31.
+bool head_offsets_fit(int L, int C, int d_k, int d_v) {
+    const int64_t Lp = ((int64_t)L + C - 1) / C * C;
+    return Lp * (d_k > d_v ? d_k : d_v) <= INT32_MAX;
+}
+
 // Shape checks shared by the workspace query and the forward call.
 la_status check_chunk_shape(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v,
                             int C) {
@@ -67,6 +76,7 @@ la_status check_chunk_shape(la_variant var, la_dtype dt, int B, int H, int L, in
     if (dt == LA_F32 && d_k == 128 && C == 128) return LA_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
     if (BH * (d_v / 16) > INT32_MAX || BH * ((L + C - 1) / C) > INT32_MAX) return LA_ERR_UNSUPPORTED;
+    if (!head_offsets_fit(L, C, d_k, d_v)) return LA_ERR_UNSUPPORTED;
     return LA_OK;
 }
 
@@ -215,6 +225,7 @@ la_status check_bwd_shape(la_variant var, la_dtype dt, int B, int H, int L, int 
     if (dt == LA_F32 && !bwd_f32_fits(d_k, d_v)) return LA_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H, nch = (L + C - 1) / C;
     if (BH * nch > INT32_MAX || BH * 2 > INT32_MAX) return LA_ERR_UNSUPPORTED;
+    if (!head_offsets_fit(L, C, d_k, d_v)) return LA_ERR_UNSUPPORTED;
     return LA_OK;
 }
 

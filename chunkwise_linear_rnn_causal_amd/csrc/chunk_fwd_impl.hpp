@@ -259,9 +259,18 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     __shared__ __attribute__((aligned(16))) TM Tiles[Cfg::NB * Cfg::SET];
     __shared__ __attribute__((aligned(16))) float Tg[DECAYED ? NTB * 4 * C : 1];
     __shared__ float Tsc[DECAYED ? NTB : 1];
-    // Normalizer z of the previous chunk, double-buffered: fp16 path as hi and lo
-    // halves (z = hi + lo to 2^-22) for the q . z MFMA; fp32 path in fp32.
-    __shared__ __attribute__((aligned(16))) TM Zs[VAR == V_NORM ? (H ? 4 * DK : 2 * DK) : 1];
+    // Normalizer z of the previous chunk in fp32, double-buffered. q . z is taken
+    // on the VALU in fp32: z is a running sum that grows with the sequence and
+    // would leave the fp16 operand range.
+    __shared__ __attribute__((aligned(16))) float Zs[VAR == V_NORM ? 2 * DK : 1];
+    // fp16 operands: the carried state S_prev^T (and the delta rule's U) enter
+    // the MFMAs scaled by 2^-s, with s chosen per chunk from the largest |S| of
+    // the previous chunk's state (carry_shift), and the products are scaled back
+    // in fp32. Slot j % 3 holds each state-holding wave's max |S_j| (the state
+    // before chunk j); slots rotate over three chunks, so every slot is read
+    // only between barriers that order it after its writes and before its reuse.
+    constexpr bool SCALE = H;
+    __shared__ __attribute__((aligned(16))) float Smx[SCALE ? 3 * NW : 1];
     // OSTG (split roles, fp32 output, 32-column slices): each row wave passes
     // its 16-row output block through a private LDS tile, so that every store
     // instruction writes whole 128-byte lines (8 lanes x 16 bytes per row)
@@ -279,8 +288,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     const int j0 = split * DVT;
     const int L = a.L, dv = a.dv;
 
-    // Per-head bases; offsets inside a head are 32-bit (L * d < 2^31 is checked
-    // by the ABI layer).
+    // Per-head bases; offsets inside a head are 32-bit (the ABI layer refuses
+    // ceil(L / C) * C * max(d_k, d_v) >= 2^31).
     const TI *qg = (const TI *)a.q + (size_t)bh * L * DK;
     const TI *kg = (const TI *)a.k + (size_t)bh * L * DK;
     const TI *vg = (VAR == V_GDN) ? nullptr : (const TI *)a.v + (size_t)bh * L * dv + j0;
@@ -321,16 +330,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) zacc[ti][e] = a.z_in ? a.z_in[(size_t)bh * DK + ti * 16 + 4 * g + e] : 0.f;
         }
-        for (int i = tid; i < DK; i += NT) {
-            const float z = a.z_in ? a.z_in[(size_t)bh * DK + i] : 0.f;
-            if constexpr (H) {
-                const TM hi = from_f32<TM>(z);
-                Zs[i] = hi;
-                Zs[DK + i] = from_f32<TM>(z - to_f32<TM>(hi));
-            } else {
-                Zs[i] = z;
-            }
-        }
+        for (int i = tid; i < DK; i += NT) Zs[i] = a.z_in ? a.z_in[(size_t)bh * DK + i] : 0.f;
     }
     // Settle the prologue's loads here, so that no load is pending at the loop
     // head and the per-chunk waits can be exact (leaving output stores in flight).
@@ -650,13 +650,42 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         }
     };
 
-    // S_prev, transposed, in the operand type: X[OS + j*KP + i].
-    auto write_sts = [&](auto w_tag, TM *X) __attribute__((always_inline)) {
+    // S_prev, transposed, in the operand type and scaled by 2^-sh:
+    // X[OS + j*KP + i].
+    auto write_sts = [&](auto w_tag, TM *X, int sh) __attribute__((always_inline)) {
         constexpr int W = decltype(w_tag)::value;
+        const float sc = SCALE ? pow2i(-sh) : 1.f;
 #pragma unroll
         for (int m = 0; m < TS.cnt[W]; ++m) {
             const int tile = TS.start[W] + m, ti = tile / NTJ, tj = tile % NTJ;
-            st4<TM>(&X[Cfg::OS + (tj * 16 + n) * KP + ti * 16 + 4 * g], Sacc[m]);
+            st4<TM>(&X[Cfg::OS + (tj * 16 + n) * KP + ti * 16 + 4 * g], SCALE ? Sacc[m] * sc : Sacc[m]);
+        }
+    };
+    // max |S| over wave W's state tiles (the state before chunk j) into slot j % 3.
+    auto put_smax = [&](auto w_tag, int j) __attribute__((always_inline)) {
+        constexpr int W = decltype(w_tag)::value;
+        if constexpr (SCALE && TS.cnt[W] > 0) {
+            float m = 0.f;
+#pragma unroll
+            for (int t = 0; t < TS.cnt[W]; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(Sacc[t][e]));
+            m = wave_max_nonneg(m);
+            if (lane == 0) Smx[(j % 3) * NW + W] = m;
+        }
+    };
+    // Operand shift for a state whose magnitude is bounded by slot j's max
+    // (wave-uniform).
+    auto get_shift = [&](int j) __attribute__((always_inline)) -> int {
+        if constexpr (SCALE) {
+            const float *M = Smx + (j % 3) * NW;
+            float m = 0.f;
+            static_for<NW>([&](auto w_tag) __attribute__((always_inline)) {
+                if constexpr (TS.cnt[decltype(w_tag)::value] > 0) m = fmaxf(m, M[decltype(w_tag)::value]);
+            });
+            return __builtin_amdgcn_readfirstlane(carry_shift(m));
+        } else {
+            return 0;
         }
     };
 
@@ -685,17 +714,19 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // tiles, computed transposed, D[j][s] = sum_i S[i][j] (-W[s][i]), so that lane
     // (g, n) holds U[s = ub*16 + n][j = jj + 4g + e] and writes four consecutive
     // columns of the row-major V tile (and of the w_s-scaled copy).
+    // U is formed in the scale of S_prev^T (2^-sh): U 2^-sh = U~ 2^-sh - W (S_prev 2^-sh).
     auto gdn_u = [&](TM *X, const float *T, const frag (&wf)[VAR == V_GDN ? NKS : 1],
-                     const f32x4 (&ucur)[VAR == V_GDN ? NTJW : 1]) __attribute__((always_inline)) {
+                     const f32x4 (&ucur)[VAR == V_GDN ? NTJW : 1], int sh) __attribute__((always_inline)) {
         if constexpr (VAR == V_GDN) {
             if (!R::rows(wv)) return;
             const int ub = wv % NRB;
             const int s = ub * 16 + n;
             const float ws = T[2 * C + s];
+            const float sc = SCALE ? pow2i(-sh) : 1.f;
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) {
                 const int jj = jt * 16;
-                f32x4 acc = ucur[jt];
+                f32x4 acc = SCALE ? ucur[jt] * sc : ucur[jt];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
                     acc = MF::mma(ld_frag<TM>(&X[Cfg::OS + (jj + n) * KP + g * (DK / 4) + ks * E]), wf[ks], acc);
@@ -709,21 +740,21 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // chunk c, from tile set X. CHECK: rows past L are not stored.
     // Every LDS operand of the block is read before the math when the fragments
     // fit in registers (HOIST), so the reads overlap instead of each waiting.
+    // sh: shift of the S_prev^T operand (and of U for the delta rule).
     auto row_block = [&](auto rb_tag, auto tj_tag, int c, const TM *X, const float *T,
-                         auto check_tag) __attribute__((always_inline)) {
+                         auto check_tag, int sh) __attribute__((always_inline)) {
         constexpr int rb = decltype(rb_tag)::value;
         constexpr int tj0 = decltype(tj_tag)::value;
         constexpr bool CHECK = decltype(check_tag)::value;
         constexpr int FR = (int)sizeof(frag) / 4;  // VGPRs per fragment
         constexpr bool HOIST = H && FR * (NKS * (1 + NTJW + rb + 1) + NTJW * (rb / 2 + 1)) <= 80;
-        constexpr bool NZ = H && VAR == V_NORM;   // normalizer on MFMA (fp16 path)
+        constexpr bool NZ = H && VAR == V_NORM;   // rowsums of the rounded scores on MFMA (fp16 path)
         const TM *Qs = X + Cfg::OQ, *Ks = X + Cfg::OK, *Vs = X + Cfg::OV, *STs = X + Cfg::OS;
         const int t0 = c * C;
         const int rl = rb * 16 + n;   // chunk-local query row of this lane
 
         // ---- operands
         frag qf[NKS], sf[NTJW][NKS], kf[rb + 1][NKS], vf[rb / 2 + 1][NTJW];
-        frag zf[NZ ? 2 * NKS : 1];
         auto load_k = [&](int sb) __attribute__((always_inline)) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) kf[sb][ks] = ld_frag<TM>(&Ks[KT::at(sb * 16 + n, g * (DK / 4) + ks * E)]);
@@ -747,14 +778,6 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
                 sf[jt][ks] = ld_frag<TM>(&STs[((tj0 + jt) * 16 + n) * KP + g * (DK / 4) + ks * E]);
-        if constexpr (NZ) {
-            const TM *Zc = Zs + (c & 1) * 2 * DK;  // z of chunk c-1: hi halves, then lo halves
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                zf[2 * ks] = ld_frag<TM>(&Zc[g * (DK / 4) + ks * E]);
-                zf[2 * ks + 1] = ld_frag<TM>(&Zc[DK + g * (DK / 4) + ks * E]);
-            }
-        }
         if constexpr (HOIST) {
 #pragma unroll
             for (int sb = 0; sb <= rb; ++sb) load_k(sb);
@@ -772,22 +795,20 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) oacc[jt] = MF::mma(sf[jt][ks], qf[ks], oacc[jt]);
         }
+        // undo the operand scale of S_prev^T (the delta rule's U carries the same
+        // scale, so there the whole output is scaled back at the end)
+        const float us = (SCALE && VAR != V_GDN) ? pow2i(sh) : 1.f;
         if constexpr (DECAYED) {
-            const float er = T[C + rl];
+            const float er = T[C + rl] * us;
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= er;
-        }
-        // normalizer, fp16 path: den[r] = q_r . z_prev + rowsum_r, accumulated in
-        // a tile whose rows are all alike (every lane gets its row's value):
-        // q . z from z's hi and lo halves, rowsums from a ones operand below.
-        f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (NZ) {
+        } else if constexpr (SCALE) {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                dacc = MF::mma(zf[2 * ks], qf[ks], dacc);
-                dacc = MF::mma(zf[2 * ks + 1], qf[ks], dacc);
-            }
+            for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= us;
         }
+        // normalizer, fp16 path: the rowsums of the rounded scores, accumulated
+        // below in a tile whose rows are all alike (every lane gets its row's value).
+        f32x4 dacc = {0.f, 0.f, 0.f, 0.f};
 
         // score tiles D[s][r] = k_s . q_r for key blocks sb <= rb. Off the
         // diagonal, exp(G_r - G_s) = exp(G_r - G_e) exp(G_e - G_s) with e the
@@ -834,11 +855,19 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
             for (int p = 0; p < NRB / 2; ++p) {
                 if (2 * p <= rb) {
-                    frag bop;
+                    // normalized: scores as fp16 high + low parts (A = hi + lo to
+                    // about 2^-22), because the normalized output is a weighted
+                    // average whose weights would otherwise carry fp16's 2^-12
+                    // rounding into every output
+                    frag bop, blo;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         bop[e] = from_f32<TM>(sc[2 * p][e]);
                         bop[4 + e] = from_f32<TM>(sc[2 * p + 1][e]);
+                        if constexpr (NZ) {
+                            blo[e] = from_f32<TM>(sc[2 * p][e] - to_f32<TM>(bop[e]));
+                            blo[4 + e] = from_f32<TM>(sc[2 * p + 1][e] - to_f32<TM>(bop[4 + e]));
+                        }
                     }
                     if constexpr (!HOIST) load_v(p);
                     const bool hi = (2 * p + 1 <= rb);
@@ -850,8 +879,12 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                             for (int e = 0; e < 4; ++e) aop[4 + e] = from_f32<TM>(0.0f);
                         }
                         oacc[jt] = MF::mma(aop, bop, oacc[jt]);
+                        if constexpr (NZ) oacc[jt] = MF::mma(aop, blo, oacc[jt]);
                     }
-                    if constexpr (NZ) dacc = MF::mma(ones, bop, dacc);  // rowsums of the rounded scores
+                    if constexpr (NZ) {  // rowsums of the same split scores
+                        dacc = MF::mma(ones, bop, dacc);
+                        dacc = MF::mma(ones, blo, dacc);
+                    }
                 }
             }
         } else {
@@ -868,11 +901,14 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             }
         }
 
-        if constexpr (NZ) {
-            const float inv = 1.0f / dacc[0];
+        if constexpr (VAR == V_GDN && SCALE) {
+            const float ug = pow2i(sh);
 #pragma unroll
-            for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= inv;
-        } else if constexpr (VAR == V_NORM) {
+            for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= ug;
+        }
+        if constexpr (VAR == V_NORM) {
+            // den[r] = q_r . z_prev + rowsum_r: q . z in fp32 over this lane's
+            // channels, summed over the four lane groups
             const int zc = (c & 1) * DK;
             float qz = 0.f;
 #pragma unroll
@@ -880,9 +916,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int el = 0; el < E; ++el)
                     qz += frag_elem<TM>(qf[ks], el) * Zs[zc + g * (DK / 4) + ks * E + el];
-            float den = rowsum + qz;
+            float den = NZ ? qz : rowsum + qz;
             den += __shfl_xor(den, 16, 64);
             den += __shfl_xor(den, 32, 64);
+            if constexpr (NZ) den += dacc[0];
             const float inv = 1.0f / den;
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= inv;
@@ -915,25 +952,28 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     };
 
     // The rows of wave W.
-    auto rows_of = [&](auto w_tag, int c, const TM *X, const float *T, auto check_tag) __attribute__((always_inline)) {
+    auto rows_of = [&](auto w_tag, int c, const TM *X, const float *T, auto check_tag, int sh) __attribute__((always_inline)) {
         constexpr int W = decltype(w_tag)::value;
         if constexpr (!R::rows(W)) return;
         row_block(std::integral_constant<int, R::rb(W, 0)>{}, std::integral_constant<int, 0>{}, c,
-                  X, T, check_tag);
+                  X, T, check_tag, sh);
         if constexpr (R::RBW == 2)
             row_block(std::integral_constant<int, R::rb(W, 1)>{}, std::integral_constant<int, 0>{}, c, X, T,
-                      check_tag);
+                      check_tag, sh);
     };
 
     // State update S <- exp(g_C) S + K^T (w (.) V) of wave W's tiles from tile set
     // X, both operands read from the row-major tiles with the token index in the
     // K slots; then the normalizer carry z_next = z_prev + K^T 1 (each channel
-    // block in its owner wave).
-    auto state_update = [&](auto w_tag, int c, const TM *X, float eg) __attribute__((always_inline)) {
+    // block in its owner wave). sh: the delta rule's U tile is held at 2^-sh,
+    // so S is brought to that scale for the update and back afterwards.
+    auto state_update = [&](auto w_tag, int c, const TM *X, float eg, int sh) __attribute__((always_inline)) {
         constexpr int W = decltype(w_tag)::value;
+        constexpr bool USC = SCALE && VAR == V_GDN;
         if constexpr (DECAYED) {
+            const float f = USC ? eg * pow2i(-sh) : eg;
 #pragma unroll
-            for (int m = 0; m < TS.cnt[W]; ++m) Sacc[m] *= eg;
+            for (int m = 0; m < TS.cnt[W]; ++m) Sacc[m] *= f;
         }
         const TM *Ks = X + Cfg::OK;
         const TM *VW = X + (DECAYED ? Cfg::OVW : Cfg::OV);
@@ -944,8 +984,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             for (int ks = 0; ks < NTK; ++ks)
                 Sacc[m] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), tok_frag(VW, PV{}, ks, tj * 16), Sacc[m]);
         }
+        if constexpr (USC) {
+            const float f = pow2i(sh);
+#pragma unroll
+            for (int m = 0; m < TS.cnt[W]; ++m) Sacc[m] *= f;
+        }
         if constexpr (VAR == V_NORM && R::zunits(W, NTI) > 0) {
-            const int zn = ((c + 1) & 1) * (H ? 2 * DK : DK);
+            const int zn = ((c + 1) & 1) * DK;
             frag ones;
             if constexpr (E == 8) {
 #pragma unroll
@@ -958,17 +1003,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                 if constexpr (R::zowner(ti) == W) {
 #pragma unroll
                     for (int ks = 0; ks < NTK; ++ks) zacc[ti] = MF::mma(tok_frag(Ks, PK{}, ks, ti * 16), ones, zacc[ti]);
-                    if (n == 0) {
-                        if constexpr (H) {
-                            f32x4 lo;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) lo[e] = zacc[ti][e] - to_f32<TM>(from_f32<TM>(zacc[ti][e]));
-                            st4<TM>(&Zs[zn + ti * 16 + 4 * g], zacc[ti]);
-                            st4<TM>(&Zs[zn + DK + ti * 16 + 4 * g], lo);
-                        } else {
-                            *reinterpret_cast<f32x4 *>(&Zs[zn + ti * 16 + 4 * g]) = zacc[ti];
-                        }
-                    }
+                    if (n == 0) *reinterpret_cast<f32x4 *>(&Zs[zn + ti * 16 + 4 * g]) = zacc[ti];
                 }
             });
         }
@@ -988,6 +1023,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         TM *X = Tiles + P * Cfg::SET, *Xn = Tiles + (P ^ 1) * Cfg::SET;
         const float *T = Tg + (c % NTB) * 4 * C;
         __syncthreads();  // chunk c staged, its gate tables and S_prev visible; chunk c-1 done
+        // shifts of S_c^T (bounded by max |S_{c-1}|) and of S_{c+1}^T (by max |S_c|)
+        const int sh = get_shift(c > 0 ? c - 1 : 0), shn = get_shift(c);
         if constexpr (FAST) {
             load_gates(c + AHEAD, std::true_type{}, Nxt{});
         } else {
@@ -1003,12 +1040,12 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         // towards their use and expose their latency.
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (VAR == V_GDN) {
-            gdn_u(X, T, wf, ucur);
+            gdn_u(X, T, wf, ucur, sh);
             __syncthreads();  // U rows of every wave visible
         }
         const bool next = FAST || c + 1 < nchunks;
         const float eg = DECAYED ? Tsc[c % NTB] : 1.f;
-        for_wave([&](auto w_tag) __attribute__((always_inline)) { rows_of(w_tag, c, X, T, Check{}); });
+        for_wave([&](auto w_tag) __attribute__((always_inline)) { rows_of(w_tag, c, X, T, Check{}, sh); });
         if (next) {
             static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
                 stage_any(m_tag, c + 1, Xn, Check{}, Nxt{});
@@ -1021,8 +1058,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             });
         }
         for_wave([&](auto w_tag) __attribute__((always_inline)) {
-            state_update(w_tag, c, X, eg);
-            if (next) write_sts(w_tag, Xn);
+            state_update(w_tag, c, X, eg, sh);
+            put_smax(w_tag, c + 1);
+            if (next) write_sts(w_tag, Xn, shn);
         });
         if constexpr (DECAYED) {
             if (wv == GW && (FAST || c + 2 < nchunks)) gate_tables(c + 2, (c + 2) % NTB, Cur{});
@@ -1043,7 +1081,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         } else {
             if (c + 1 < nchunks) load_gates(c + 1, std::false_type{}, S0{});
         }
-        for_wave([&](auto w_tag) __attribute__((always_inline)) { write_sts(w_tag, X); });
+        const int sh = get_shift(c);  // exact: max |S_c| was written before the barrier
+        for_wave([&](auto w_tag) __attribute__((always_inline)) { write_sts(w_tag, X, sh); });
         static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
             stage_any(m_tag, c, X, Check{}, S0{});
             if constexpr (FAST) {
@@ -1062,13 +1101,14 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();  // staged tiles and STs visible
         if constexpr (VAR == V_GDN) {
-            gdn_u(X, T, wf, ucur);
+            gdn_u(X, T, wf, ucur, sh);
             __syncthreads();
         }
         const float eg = DECAYED ? Tsc[c % NTB] : 1.f;
         for_wave([&](auto w_tag) __attribute__((always_inline)) {
-            rows_of(w_tag, c, X, T, Check{});
-            state_update(w_tag, c, X, eg);
+            rows_of(w_tag, c, X, T, Check{}, sh);
+            state_update(w_tag, c, X, eg, sh);
+            put_smax(w_tag, c + 1);
         });
         if constexpr (DECAYED) {
             if (wv == GW && (FAST || c + 1 < nchunks)) gate_tables(c + 1, (c + 1) % NTB, S0{});
@@ -1086,6 +1126,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         const TM *X = Tiles + P * Cfg::SET;
         const float *T = Tg + (c % NTB) * 4 * C;
         __syncthreads();  // chunk c staged, its gate tables and S_prev visible
+        const int sh = get_shift(c > 0 ? c - 1 : 0);  // S_c^T is bounded by max |S_{c-1}|
         if constexpr (QD) {
             cvt_q(par_tag);  // chunk c's queries, loaded two chunks ago
             if (c + 2 < nchunks) load_q(c + 2, par_tag);
@@ -1096,10 +1137,10 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             take_wu(wf, ucur);
             if (c + 1 < nchunks) load_wu(c + 1);
             __builtin_amdgcn_sched_barrier(0);
-            gdn_u(const_cast<TM *>(X), T, wf, ucur);
+            gdn_u(const_cast<TM *>(X), T, wf, ucur, sh);
             __syncthreads();  // U rows visible to the state waves
         }
-        rows_of(w_tag, c, X, T, check_tag);
+        rows_of(w_tag, c, X, T, check_tag, sh);
     };
     // State wave, chunk c (P = c & 1 at compile time): stage chunk c+1 into the
     // other tile set from its register set and refill that set with chunk
@@ -1117,6 +1158,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         const TM *X = Tiles + P * Cfg::SET;
         TM *Xn = Tiles + (P ^ 1) * Cfg::SET;
         __syncthreads();  // chunk c staged and visible; chunk c-1 done everywhere
+        const int sh = VAR == V_GDN ? get_shift(c > 0 ? c - 1 : 0) : 0;  // U of chunk c
+        const int shn = get_shift(c);  // S_{c+1}^T, bounded by max |S_c|
         if constexpr (FAST) {
             load_gates(c + AHEAD, std::true_type{}, Nxt{});
         } else {
@@ -1148,8 +1191,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
         if constexpr (VAR == V_GDN) __syncthreads();  // U of chunk c visible
         stage_range(std::integral_constant<int, MH>{}, std::integral_constant<int, NSLOT>{});
         const float eg = DECAYED ? Tsc[c % NTB] : 1.f;
-        state_update(w_tag, c, X, eg);
-        if (next) write_sts(w_tag, Xn);
+        state_update(w_tag, c, X, eg, sh);
+        put_smax(w_tag, c + 1);
+        if (next) write_sts(w_tag, Xn, shn);
         if constexpr (DECAYED) {
             if (W == GW && (FAST || c + 2 < nchunks)) gate_tables(c + 2, (c + 2) % NTB, Cur{});
         }
@@ -1221,12 +1265,13 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                             }
                         }
                     }
-                    __syncthreads();  // gate tables of chunk 0 visible
+                    put_smax(w_tag, 0);
+                    __syncthreads();  // gate tables of chunk 0 and max |S_0| visible
                     static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
                         stage_slot(w_tag, m_tag, 0, Tiles, std::true_type{}, Set0{});
                         if (nchunks > NPS) load_slot(w_tag, m_tag, NPS, std::false_type{}, Set0{});
                     });
-                    write_sts(w_tag, Tiles);
+                    write_sts(w_tag, Tiles, get_shift(0));
                 }
                 int c = 0;
                 if (nfull >= AHEAD + 1) {
@@ -1274,12 +1319,14 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                     }
                 }
             }
-            __syncthreads();  // gate tables of chunk 0 visible
+            for_wave([&](auto w_tag) __attribute__((always_inline)) { put_smax(w_tag, 0); });
+            __syncthreads();  // gate tables of chunk 0 and max |S_0| visible
             static_for<NSLOT>([&](auto m_tag) __attribute__((always_inline)) {
                 stage_any(m_tag, 0, Tiles, std::true_type{}, Set0{});
                 if (nchunks > NPS) load_any(m_tag, NPS, std::false_type{}, Set0{});
             });
-            for_wave([&](auto w_tag) __attribute__((always_inline)) { write_sts(w_tag, Tiles); });
+            const int sh0 = get_shift(0);
+            for_wave([&](auto w_tag) __attribute__((always_inline)) { write_sts(w_tag, Tiles, sh0); });
         }
         using P0 = std::integral_constant<int, 0>;
         using P1 = std::integral_constant<int, 1>;
@@ -1308,6 +1355,7 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             if constexpr (DECAYED) {
                 if (wv == GW) gate_tables(0, 0, Set0{});
             }
+            for_wave([&](auto w_tag) __attribute__((always_inline)) { put_smax(w_tag, 0); });
         }
         int c = 0;
         if (nfull >= 2) {

@@ -280,6 +280,30 @@ __device__ inline float wave_inclusive_sum(float x) {
     return x;
 }
 
+// Maximum over the 64 lanes of a wave of non-negative values, with DPP only
+// (same row shifts and row broadcasts as wave_inclusive_sum; lane 63 ends with
+// the maximum of all lanes). Returned wave-uniform.
+__device__ inline float wave_max_nonneg(float x) {
+    x = fmaxf(x, dpp_f32<0x111>(0.f, x));
+    x = fmaxf(x, dpp_f32<0x112>(0.f, x));
+    x = fmaxf(x, dpp_f32<0x114>(0.f, x));
+    x = fmaxf(x, dpp_f32<0x118>(0.f, x));
+    x = fmaxf(x, dpp_f32<0x142, 0xa>(0.f, x));
+    x = fmaxf(x, dpp_f32<0x143, 0xc>(0.f, x));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// Power-of-two operand scaling of a carried quantity (state, pseudo-values) of
+// magnitude at most m: the shift s >= 0 with m * 2^-s < 2^8, so that the
+// quantity can grow 256-fold before its fp16 operand overflows (s = 0 below 2^8:
+// small values keep their fp16 representation). Scaling by 2^-s is exact.
+__device__ inline int carry_shift(float m) {
+    const int e = (int)((__float_as_uint(m) >> 23) & 0xffu);  // m < 2^(e - 126)
+    return min(max(e - 134, 0), 120);
+}
+// 2^s for |s| <= 126 (exact).
+__device__ inline float pow2i(int s) { return __uint_as_float((uint32_t)(127 + s) << 23); }
+
 // XCD-aware block order: consecutive virtual ids go to the same XCD (blocks are
 // handed to the 8 XCDs round-robin), so the d_v slices of one head share L2.
 __device__ inline int xcd_virtual_block() {

@@ -53,10 +53,18 @@
  *  - Numerics. fp32 inputs are computed on fp32 tensor-core operands. bf16
  *    inputs are computed on fp16 tensor-core operands with fp32 accumulation:
  *    bf16 values are exact in fp16 for magnitudes in [2^-14, 65504]; smaller
- *    ones keep an absolute error below 2^-25, larger ones (and intermediate
- *    scores or states beyond 65504) are outside the supported range. The state
- *    carried from chunk to chunk stays in fp32. Choose o_dt = LA_F32 when the
- *    output is compared at a tolerance finer than bf16's 2^-8 relative spacing.
+ *    ones keep an absolute error below 2^-25. The state carried from chunk to
+ *    chunk stays in fp32 and has no range limit of its own in la_chunk_fwd for
+ *    LA_PLAIN, LA_NORMALIZED, LA_DECAY and LA_GATED_DELTA: its fp16 operand
+ *    (and the delta rule's pseudo-values) is scaled per chunk by a power of two
+ *    chosen from the previous chunk's largest |S|, and the normalizer is
+ *    applied in fp32. What remains bounded is per chunk and set by the inputs:
+ *    the masked scores q_r . k_s of one chunk must stay below 65504, and the
+ *    state may grow at most 256-fold within one chunk (or to at most 65504
+ *    from below 256). LA_VECTOR_DECAY and la_chunk_bwd keep an unscaled fp16
+ *    state operand: states beyond 65504 are outside their supported range.
+ *    Choose o_dt = LA_F32 when the output is compared at a tolerance finer
+ *    than bf16's 2^-8 relative spacing.
  *  - No C++ exception crosses this boundary. Thread-safe for distinct streams.
  */
 #ifndef LINATTN_H
@@ -133,6 +141,9 @@ la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
  *   d_k         32, 64 or 128.   d_v  32, 64, 96 or 128 (a multiple of 32).
  *   C           chunk length: 64 or 128 (LA_GATED_DELTA, LA_VECTOR_DECAY: 64).
  *               L need not be a multiple of C; a ragged last chunk is handled.
+ *               Rows of one head are addressed with 32-bit offsets:
+ *               ceil(L / C) * C * max(d_k, d_v) >= 2^31 returns
+ *               LA_ERR_UNSUPPORTED.
  *               LA_VECTOR_DECAY with LA_F32 inputs supports d_k 32 and 64.
  *   workspace   device buffer of at least la_chunk_fwd_workspace_size() bytes
  *               (may be NULL when that size is 0), 256-byte aligned.

@@ -93,19 +93,25 @@ def forward(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in
     return o, s_out, z_out
 
 
-def decode_step(variant: str, q, k, v, log_gate, state, beta=None, threads: int = 0, lib=None):
+def decode_step(variant: str, q, k, v, log_gate, state, beta=None, threads: int = 0, lib=None,
+                copy: bool = True):
     """One in-place decode step on a copy of ``state``; returns (o, new_state).
 
     q, k: [..., dk]; v: [..., dv]; log_gate, beta: [...] ("vector_decay": log_gate
     [..., dk]); state: [..., dk, dv].
     beta is required for "gated_delta" (log_gate may then be None: alpha = 1).
+    copy=False updates ``state`` itself (a C-contiguous float64 array) in place.
     """
     lib = lib or load()
     q, k, v = _c64(q), _c64(k), _c64(v)
     lead = q.shape[:-1]
     dk, dv = q.shape[-1], v.shape[-1]
     NH = int(np.prod(lead)) if lead else 1
-    S = np.array(state, dtype=np.float64, copy=True, order="C")
+    if copy:
+        S = np.array(state, dtype=np.float64, copy=True, order="C")
+    else:
+        assert state.dtype == np.float64 and state.flags.c_contiguous
+        S = state
     lg = _c64(log_gate)
     be = _c64(beta)
     o = np.zeros(lead + (dv,), np.float64)

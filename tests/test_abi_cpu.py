@@ -61,6 +61,9 @@ def test_workspace_sizes():
     assert wsize(L=0) == (0, 0)
     assert wsize(C=128)[0] == UNSUPPORTED      # delta rule is built for C = 64
     assert la.load_library().la_chunk_fwd_workspace_size(GDN, BF16, 1, 1, 8, 64, 64, 64, None) == INVALID
+    # the largest head the 32-bit row offsets address, and one chunk more
+    assert wsize(B=1, H=1, L=2 ** 24 - 64, dk=128, dv=128)[0] == 0
+    assert wsize(B=1, H=1, L=2 ** 24 - 63, dk=128, dv=128)[0] == UNSUPPORTED
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -75,6 +78,9 @@ def test_workspace_sizes():
     (dict(dv=48), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
     (dict(C=32), UNSUPPORTED), (dict(C=256), UNSUPPORTED),
     (dict(dt=F32, dk=128, C=128), UNSUPPORTED),
+    # row offsets inside one head are 32-bit: ceil(L/C)*C*max(d_k, d_v) < 2^31
+    (dict(L=2 ** 24, dk=128, dv=32), UNSUPPORTED), (dict(L=2 ** 24 - 63, dk=32, dv=128), UNSUPPORTED),
+    (dict(L=2 ** 25 - 63, dk=64, dv=64), UNSUPPORTED),
     (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
     (dict(var=DECAY), INVALID),                       # decay needs a log-gate
     (dict(var=PLAIN, lg=FAKE + 0x100000), INVALID),   # gate given to an ungated variant
@@ -178,6 +184,7 @@ def test_bwd_workspace_size():
     assert bwd_wsize(C=128)[0] == UNSUPPORTED
     assert bwd_wsize(dt=F32, dk_=128, dv_=128)[0] == UNSUPPORTED
     assert bwd_wsize(dt=F32, dk_=128, dv_=32)[0] == 0
+    assert bwd_wsize(L=2 ** 24 - 63, dk_=128, dv_=128)[0] == UNSUPPORTED   # 32-bit head offsets
 
 
 @pytest.mark.parametrize("kw,expect", [

@@ -23,33 +23,39 @@ def test_several_gpus_refused():
     assert r.stdout == ""
 
 
-# (workload, bytes per unit, units per launch, final-state bytes, flop per unit)
+# (workload, algorithmic bytes per unit, units per launch, flop per unit,
+#  bytes per unit as launched (o in the launch's dtype), final-state bytes)
 CHUNK_WORK = [
-    # normalized d64: q, k, v bf16 in, o fp32 out
-    ("normalized_bf16_b8h16_l2048_d64", (2 * 64 + 64) * 2 + 64 * 4, 8 * 16 * 2048, 8 * 16 * 64 * 64 * 4,
-     2 * 64 * (64 + 64) + 4 * 64 * 64),
-    # decay d128: + one fp32 log-gate per token
-    ("decay_bf16_b4h32_l8192_d128", 384 * 2 + 512 + 4, 4 * 32 * 8192, 4 * 32 * 128 * 128 * 4,
-     2 * 64 * 256 + 4 * 128 * 128),
+    # normalized d64: q, k, v, o bf16; launched with o in fp32
+    ("normalized_bf16_b8h16_l2048_d64", (3 * 64 + 64) * 2, 8 * 16 * 2048, 2 * 64 * (64 + 64) + 4 * 64 * 64,
+     3 * 64 * 2 + 64 * 4, 8 * 16 * 64 * 64 * 4),
+    # decay d128: + one fp32 log-gate per token; launched with o in bf16
+    ("decay_bf16_b4h32_l8192_d128", 4 * 128 * 2 + 4, 4 * 32 * 8192, 2 * 64 * 256 + 4 * 128 * 128,
+     4 * 128 * 2 + 4, 4 * 32 * 128 * 128 * 4),
     # vector decay d128: + one fp32 log-gate per token and key channel
-    ("vector_decay_bf16_b4h32_l8192_d128", 384 * 2 + 128 * 4 + 512, 4 * 32 * 8192, 4 * 32 * 128 * 128 * 4,
-     2 * 64 * 256 + 4 * 128 * 128),
+    ("vector_decay_bf16_b4h32_l8192_d128", 4 * 128 * 2 + 128 * 4, 4 * 32 * 8192, 2 * 64 * 256 + 4 * 128 * 128,
+     3 * 128 * 2 + 128 * 4 + 128 * 4, 4 * 32 * 128 * 128 * 4),
     # gated delta d128: + log-gate and beta per token
-    ("gated_delta_bf16_b2h16_l8192_d128", 384 * 2 + 512 + 4 + 4, 2 * 16 * 8192, 2 * 16 * 128 * 128 * 4,
-     (2 * 64 * 64 * (3 * 128 + 2 * 128) + 6 * 64 * 128 * 128 + 64 ** 3 / 3) / 64),
+    ("gated_delta_bf16_b2h16_l8192_d128", 4 * 128 * 2 + 4 + 4, 2 * 16 * 8192,
+     (2 * 64 * 64 * (3 * 128 + 2 * 128) + 6 * 64 * 128 * 128 + 64 ** 3 / 3) / 64,
+     3 * 128 * 2 + 128 * 4 + 4 + 4, 2 * 16 * 128 * 128 * 4),
 ]
 
 
-@pytest.mark.parametrize("name,per_unit,units,state,flop_unit", CHUNK_WORK)
-def test_chunk_work(name, per_unit, units, state, flop_unit):
-    flop, nbytes = bench.chunk_work(W.CONFIGS[name])
-    assert nbytes == per_unit * units + state
+@pytest.mark.parametrize("name,per_unit,units,flop_unit,launched_unit,state", CHUNK_WORK)
+def test_chunk_work(name, per_unit, units, flop_unit, launched_unit, state):
+    flop, nbytes, launched = bench.chunk_work(W.CONFIGS[name])
+    assert nbytes == per_unit * units
+    assert launched == launched_unit * units + state
     assert flop == pytest.approx(flop_unit * units, rel=1e-12)
 
 
-def test_headline_bytes():
-    # 640 bytes per token-head over 262,144 token-heads plus a 2 MiB final state
-    assert bench.chunk_work(W.CONFIGS[bench.HEADLINE])[1] == 169_869_312
+def test_headline_is_the_largest_single_gpu_workload_with_survey_bytes():
+    # decay B4 H32 L8192 d128: q, k, v, o bf16 (1,073,741,824 B) + fp32 log-gates (4 MiB)
+    assert bench.HEADLINE == "decay_bf16_b4h32_l8192_d128"
+    assert bench.chunk_work(W.CONFIGS[bench.HEADLINE])[1] == 1_077_936_128
+    # the normalized workload: q, k, v, o bf16 = 134.2 MB
+    assert bench.chunk_work(W.CONFIGS["normalized_bf16_b8h16_l2048_d64"])[1] == 134_217_728
 
 
 def test_decode_work():

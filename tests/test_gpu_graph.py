@@ -123,16 +123,16 @@ def test_independent_calls_on_two_streams():
     dec = []
     for seed in (41, 42):
         S0 = dev(W.make_decode_state(N, Hd, dk, dv, seed=seed))
-        st = W.make_decode_step(N, Hd, dk, dv, step=0, seed=seed)
-        dec.append((S0, S0.clone(), [dev(st.q), dev(st.k), dev(st.v), dev(st.log_gate)],
+        st = W.make_decode_step(N, Hd, dk, dv, step=0, seed=seed, with_beta=True)
+        dec.append((S0, S0.clone(), [dev(st.q), dev(st.k), dev(st.v), dev(st.log_gate), dev(st.beta)],
                     torch.empty((N, Hd, dv), dtype=torch.float32, device="cuda")))
 
     def run(i, stream):
         (q, k, v, lg, be, s_in), o, S, ws = calls[i]
         la.la_chunk_fwd("gated_delta", q, k, v, lg, be, state_in=s_in, C=C, o=o, state_out=S,
                         workspace=ws, stream=stream)
-        _, Sd, (dq, dk_, dv_, dlg), do = dec[i]
-        la.la_decode_step("decay", dq, dk_, dv_, dlg, Sd, o=do, stream=stream)
+        _, Sd, (dq, dk_, dv_, dlg, dbe), do = dec[i]
+        la.la_decode_step("gated_delta", dq, dk_, dv_, dlg, Sd, o=do, beta=dbe, stream=stream)
 
     cur = torch.cuda.current_stream()
     for i in range(2):

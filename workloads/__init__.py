@@ -49,7 +49,7 @@ CONFIGS: Dict[str, dict] = {
         recipe="elu1"),
     "decay_bf16_b4h32_l8192_d128": dict(
         kind="chunk", variant="decay", dtype="bf16", B=4, H=32, L=8192, dk=128, dv=128, C=64,
-        recipe="gauss_scaled_gate"),
+        recipe="gauss_scaled_gate", o_dtype="bf16"),
     "decode_decay_bf16_n512h32_d128": dict(
         kind="decode", variant="decay", dtype="bf16", N=512, H=32, dk=128, dv=128, steps=100,
         recipe="decode"),
