@@ -22,8 +22,9 @@ HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "linattn.h")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 VARIANTS = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3, "vector_decay": 4}
-EXPORTS = ("la_chunk_fwd_workspace_size", "la_chunk_fwd", "la_chunk_bwd_workspace_size",
-           "la_chunk_bwd", "la_decode_step", "la_short_conv", "la_status_str", "la_abi_version")
+EXPORTS = ("la_chunk_fwd_workspace_size", "la_chunk_fwd", "la_chunk_fwd_noalloc",
+           "la_chunk_bwd_workspace_size", "la_chunk_bwd", "la_decode_step", "la_short_conv",
+           "la_status_str", "la_abi_version")
 
 _lib = None
 
@@ -52,6 +53,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_chunk_fwd.restype = i
     lib.la_chunk_fwd.argtypes = [i, i, i, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp,
                                  i, i, i, i, i, i, vp, sz, vp]
+    lib.la_chunk_fwd_noalloc.restype = i
+    lib.la_chunk_fwd_noalloc.argtypes = [i, i, i, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp,
+                                         i, i, i, i, i, i, vp]
     lib.la_decode_step.restype = i
     lib.la_decode_step.argtypes = [i, i, i, vp, vp, vp, fp, fp, fp, vp, i, i, i, i, vp]
     lib.la_chunk_bwd_workspace_size.restype = i
@@ -149,32 +153,11 @@ def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None,
     """
     import torch
     lib = load_library()
-    if variant not in VARIANTS:
-        raise ValueError(f"unknown variant {variant!r}")
-    if q.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be [B, H, L, d]")
-    B, H, L, d_k = q.shape
-    d_v = v.shape[-1]
+    B, H, L, d_k, d_v, o, state_out, z_out = _fwd_args(variant, q, k, v, log_gate, beta, state_in,
+                                                       z_in, o, out_dtype, state_out, z_out,
+                                                       want_state, want_z)
     dt = _dt(q)
-    f32, dev_ = torch.float32, q.device
-    _check("k", k, (B, H, L, d_k), q.dtype, dev_, required=True)
-    _check("v", v, (B, H, L, d_v), q.dtype, dev_, required=True)
-    gate_shape = (B, H, L, d_k) if variant == "vector_decay" else (B, H, L)
-    _check("log_gate", log_gate, gate_shape, f32, dev_)
-    _check("beta", beta, (B, H, L), f32, dev_)
-    _check("state_in", state_in, (B, H, d_k, d_v), f32, dev_)
-    _check("z_in", z_in, (B, H, d_k), f32, dev_)
-    if o is not None:
-        _check("o", o, (B, H, L, d_v), o.dtype, dev_)
-    _check("state_out", state_out, (B, H, d_k, d_v), f32, dev_)
-    _check("z_out", z_out, (B, H, d_k), f32, dev_)
-    _check_device(dev_)
-    if o is None:
-        o = torch.empty((B, H, L, d_v), dtype=out_dtype or torch.float32, device=q.device)
-    if want_state and state_out is None:
-        state_out = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=q.device)
-    if want_z and z_out is None:
-        z_out = torch.empty((B, H, d_k), dtype=torch.float32, device=q.device)
+    dev_ = q.device
     ws_bytes = 0
     if workspace is None:
         ws_bytes = la_chunk_fwd_workspace_size(variant, dt, B, H, L, d_k, d_v, C)
@@ -190,6 +173,60 @@ def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None,
                           _stream(q.device, stream))
     if st != LA_OK:
         raise LinAttnError(st, "la_chunk_fwd")
+    return o, state_out, z_out
+
+
+def _fwd_args(variant, q, k, v, log_gate, beta, state_in, z_in, o, out_dtype, state_out, z_out,
+              want_state, want_z):
+    """Check the tensors of a forward call and allocate the missing outputs.
+    Returns (B, H, L, d_k, d_v, o, state_out, z_out)."""
+    import torch
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, L, d_k = q.shape
+    d_v = v.shape[-1]
+    _dt(q)
+    f32, dev_ = torch.float32, q.device
+    _check("k", k, (B, H, L, d_k), q.dtype, dev_, required=True)
+    _check("v", v, (B, H, L, d_v), q.dtype, dev_, required=True)
+    gate_shape = (B, H, L, d_k) if variant == "vector_decay" else (B, H, L)
+    _check("log_gate", log_gate, gate_shape, f32, dev_)
+    _check("beta", beta, (B, H, L), f32, dev_)
+    _check("state_in", state_in, (B, H, d_k, d_v), f32, dev_)
+    _check("z_in", z_in, (B, H, d_k), f32, dev_)
+    if o is not None:
+        _check("o", o, (B, H, L, d_v), o.dtype, dev_)
+    _check("state_out", state_out, (B, H, d_k, d_v), f32, dev_)
+    _check("z_out", z_out, (B, H, d_k), f32, dev_)
+    _check_device(dev_)
+    if o is None:
+        o = torch.empty((B, H, L, d_v), dtype=out_dtype or torch.float32, device=dev_)
+    if want_state and state_out is None:
+        state_out = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev_)
+    if want_z and z_out is None:
+        z_out = torch.empty((B, H, d_k), dtype=torch.float32, device=dev_)
+    return B, H, L, d_k, d_v, o, state_out, z_out
+
+
+def la_chunk_fwd_noalloc(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in=None,
+                         *, C: int = 64, o=None, out_dtype=None, state_out=None, z_out=None,
+                         want_state: bool = False, want_z: bool = False, stream=None) -> Tuple:
+    """la_chunk_fwd without a workspace: the library's static per-device scratch
+    holds the delta rule's per-chunk products (for callers that cannot allocate).
+    Same arguments and results as la_chunk_fwd; pass o (and state_out, z_out) to
+    keep the call itself free of allocations. Calls that overlap on one device race."""
+    lib = load_library()
+    B, H, L, d_k, d_v, o, state_out, z_out = _fwd_args(variant, q, k, v, log_gate, beta, state_in,
+                                                       z_in, o, out_dtype, state_out, z_out,
+                                                       want_state, want_z)
+    st = lib.la_chunk_fwd_noalloc(VARIANTS[variant], _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(log_gate), _ptr(beta), _ptr(state_in), _ptr(z_in), _ptr(o),
+                                  _ptr(state_out), _ptr(z_out), B, H, L, d_k, d_v, C,
+                                  _stream(q.device, stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_chunk_fwd_noalloc")
     return o, state_out, z_out
 
 
@@ -343,6 +380,6 @@ def la_short_conv(q=None, k=None, v=None, w_q=None, w_k=None, w_v=None, *, q_sta
     return (*outs, *souts)
 
 
-__all__ = ["la_chunk_fwd", "la_chunk_fwd_workspace_size", "la_chunk_bwd", "la_chunk_bwd_workspace_size",
+__all__ = ["la_chunk_fwd", "la_chunk_fwd_workspace_size", "la_chunk_fwd_noalloc", "la_chunk_bwd", "la_chunk_bwd_workspace_size",
            "la_decode_step", "la_short_conv",
            "la_status_str", "la_abi_version", "LinAttnError", "VARIANTS", "load_library"]

@@ -15,6 +15,11 @@
 
 using namespace la;
 
+// Scratch of la_chunk_fwd_noalloc: every device that loads the library holds
+// one copy until the process ends. Host code uses the address that
+// hipGetSymbolAddress returns on the current device, never this name.
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -273,6 +278,176 @@ bool dtype_pair_ok(la_dtype dt, la_dtype o_dt) {
     return (dt == LA_BF16 && (o_dt == LA_F32 || o_dt == LA_BF16)) || (dt == LA_F32 && o_dt == LA_F32);
 }
 
+// ---- chunk forward: validation and launch, shared by la_chunk_fwd and
+// la_chunk_fwd_noalloc
+struct FwdCall {
+    la_variant var;
+    la_dtype dt, o_dt;
+    const void *q, *k, *v;
+    const float *log_gate, *beta, *state_in, *z_in;
+    void *o;
+    float *state_out, *z_out;
+    int B, H, L, d_k, d_v, C;
+};
+
+struct FwdSpans {
+    Span sp[10];
+    const Span *begin() const { return sp; }
+    const Span *end() const { return sp + 10; }
+};
+// Every buffer the call reads or writes (for overlap checks against a workspace).
+FwdSpans fwd_spans(const FwdCall &f) {
+    const int64_t BH = (int64_t)f.B * f.H;
+    const size_t es = elem_size(f.dt), g_b = (size_t)BH * f.L * 4;
+    const size_t s_b = (size_t)BH * f.d_k * f.d_v * 4, z_b = (size_t)BH * f.d_k * 4;
+    return FwdSpans{{{f.q, (size_t)BH * f.L * f.d_k * es}, {f.k, (size_t)BH * f.L * f.d_k * es},
+                     {f.v, (size_t)BH * f.L * f.d_v * es},
+                     {f.log_gate, f.var == LA_VECTOR_DECAY ? g_b * f.d_k : g_b}, {f.beta, g_b},
+                     {f.o, (size_t)BH * f.L * f.d_v * elem_size(f.o_dt)}, {f.state_in, s_b},
+                     {f.state_out, s_b}, {f.z_in, z_b}, {f.z_out, z_b}}};
+}
+
+la_status validate_fwd(const FwdCall &f) {
+    la_status s = check_chunk_shape(f.var, f.dt, f.B, f.H, f.L, f.d_k, f.d_v, f.C);
+    if (s != LA_OK) return s;
+    const la_variant var = f.var;
+    if (f.o_dt != LA_F32 && f.o_dt != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (!dtype_pair_ok(f.dt, f.o_dt)) return LA_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)f.B * f.H;
+    const size_t es = elem_size(f.dt), oes = elem_size(f.o_dt);
+    const bool has_tokens = f.L > 0;
+    // required / forbidden pointers
+    if (has_tokens && (!f.q || !f.k || !f.o)) return LA_ERR_INVALID_ARG;
+    if (has_tokens && !f.v) return LA_ERR_INVALID_ARG;
+    if ((var == LA_DECAY || var == LA_VECTOR_DECAY) && has_tokens && !f.log_gate) return LA_ERR_INVALID_ARG;
+    if ((var == LA_PLAIN || var == LA_NORMALIZED) && f.log_gate) return LA_ERR_INVALID_ARG;
+    if (var == LA_GATED_DELTA && has_tokens && !f.beta) return LA_ERR_INVALID_ARG;
+    if (var != LA_GATED_DELTA && f.beta) return LA_ERR_INVALID_ARG;
+    if (var != LA_NORMALIZED && (f.z_in || f.z_out)) return LA_ERR_INVALID_ARG;
+    // alignment
+    const void *ptrs[] = {f.q, f.k, f.v, f.o, f.log_gate, f.beta, f.state_in, f.z_in, f.state_out, f.z_out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
+    // aliasing: outputs must not overlap inputs (state_out == state_in is allowed)
+    const int L = f.L, d_k = f.d_k, d_v = f.d_v;
+    const size_t qk_b = (size_t)BH * L * d_k * es, v_b = (size_t)BH * L * d_v * es;
+    const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4, z_b = (size_t)BH * d_k * 4;
+    const size_t lg_b = var == LA_VECTOR_DECAY ? g_b * d_k : g_b;
+    const Span o_sp{f.o, (size_t)BH * L * d_v * oes}, so_sp{f.state_out, s_b}, zo_sp{f.z_out, z_b};
+    const Span ins[] = {{f.q, qk_b}, {f.k, qk_b}, {f.v, v_b}, {f.log_gate, lg_b}, {f.beta, g_b}, {f.z_in, z_b}};
+    for (const Span &in : ins) {
+        if (overlap(o_sp, in) || overlap(so_sp, in) || overlap(zo_sp, in)) return LA_ERR_INVALID_ARG;
+    }
+    if (overlap(o_sp, Span{f.state_in, s_b}) || overlap(o_sp, so_sp) || overlap(o_sp, zo_sp) ||
+        overlap(so_sp, zo_sp) || overlap(zo_sp, Span{f.state_in, s_b}))
+        return LA_ERR_INVALID_ARG;
+    if (f.state_out && f.state_in && f.state_out != f.state_in && overlap(so_sp, Span{f.state_in, s_b}))
+        return LA_ERR_INVALID_ARG;
+    return LA_OK;
+}
+
+// Launch the forward over tokens [p0, p0 + n) of every head (a piece of the
+// sequence; the whole sequence when p0 = 0 and n = L): pointers are advanced to
+// the piece, heads stay f.L rows apart, the state comes from s_in and goes to
+// s_out. ws: the delta rule's per-chunk products for this piece.
+la_status run_fwd(const FwdCall &f, int p0, int n, const float *s_in, float *s_out, void *ws,
+                  hipStream_t st) {
+    const la_variant var = f.var;
+    const la_dtype dt = f.dt;
+    const int64_t BH = (int64_t)f.B * f.H;
+    const size_t es = elem_size(dt), oes = elem_size(f.o_dt);
+    const int C = f.C, d_k = f.d_k, d_v = f.d_v;
+    const int nchunks = (n + C - 1) / C;
+    const int Lp = nchunks * C;
+    const int gw = var == LA_VECTOR_DECAY ? d_k : 1;  // gates per token
+    auto adv = [&](const void *p, size_t per_row) -> const void * {
+        return p ? static_cast<const char *>(p) + (size_t)p0 * per_row : nullptr;
+    };
+    ChunkArgs a{};
+    a.q = adv(f.q, d_k * es); a.k = adv(f.k, d_k * es); a.v = adv(f.v, d_v * es);
+    a.lg = static_cast<const float *>(adv(f.log_gate, 4 * gw));
+    a.s_in = s_in; a.z_in = f.z_in;
+    a.o = const_cast<void *>(adv(f.o, d_v * oes));
+    a.s_out = s_out; a.z_out = f.z_out;
+    const Geometry geo = choose_geometry(var, dt, BH, d_v, C);
+    a.BH = (int)BH; a.L = n; a.Lp = Lp; a.dv = d_v; a.nsplit = d_v / geo.dvt; a.ld = f.L;
+
+    if (var == LA_GATED_DELTA && n > 0) {
+        char *w = static_cast<char *>(ws);
+        a.w = w;
+        a.ut = w + gdn_w_bytes(dt, BH, Lp, d_k);
+        PrepArgs p{};
+        p.k = a.k; p.v = a.v; p.lg = a.lg; p.beta = static_cast<const float *>(adv(f.beta, 4));
+        p.w = const_cast<void *>(a.w); p.ut = const_cast<void *>(a.ut);
+        p.BH = (int)BH; p.L = n; p.Lp = Lp; p.dv = d_v; p.nchunks = nchunks; p.ld = f.L;
+        const hipError_t e = (dt == LA_BF16) ? dispatch_prep<bf16>(d_k, p, st)
+                                             : dispatch_prep<float>(d_k, p, st);
+        if (e != hipSuccess) return LA_ERR_HIP;
+    }
+    hipError_t e;
+    if (var == LA_VECTOR_DECAY) {  // the launcher picks its own value slices
+        if (dt == LA_F32)
+            e = dispatch_vdecay<float, float>(d_k, a, st);
+        else if (f.o_dt == LA_F32)
+            e = dispatch_vdecay<bf16, float>(d_k, a, st);
+        else
+            e = dispatch_vdecay<bf16, bf16>(d_k, a, st);
+        return from_hip(e);
+    }
+    if (dt == LA_F32)
+        e = dispatch_chunk_dk<float, float>(var, d_k, C, geo, a, st);
+    else if (f.o_dt == LA_F32)
+        e = dispatch_chunk_dk<bf16, float>(var, d_k, C, geo, a, st);
+    else
+        e = dispatch_chunk_dk<bf16, bf16>(var, d_k, C, geo, a, st);
+    return from_hip(e);
+}
+
+// ---- la_chunk_fwd_noalloc: the delta rule's per-chunk products (W, U~) live
+// in a static device array instead of a caller workspace.
+constexpr size_t kScratchBytes = sizeof(scratch);
+// Device address of `scratch` per device, from hipGetSymbolAddress on that
+// device (the host-side name of the array is not a device address).
+std::atomic<char *> g_scratch[kMaxDevices];
+
+la_status scratch_for_current_device(char **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return LA_ERR_UNSUPPORTED;
+    char *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return LA_ERR_HIP;
+        p = static_cast<char *>(addr);
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return LA_OK;
+}
+
+// Piece length (tokens, a multiple of C) whose delta-rule products fit the
+// scratch, with room for a carried state when the caller passes no state_out;
+// rows >= L means the whole sequence in one piece, 0 that one chunk does not fit.
+struct PiecePlan {
+    int rows;
+    size_t ws_bytes;  // products of one full piece (the carried state follows them)
+};
+PiecePlan plan_pieces(const FwdCall &f) {
+    const size_t whole = chunk_workspace(f.var, f.dt, f.B, f.H, f.L, f.d_k, f.d_v, f.C);
+    if (whole <= kScratchBytes) return PiecePlan{f.L > 0 ? f.L : 1, whole};
+    const int64_t BH = (int64_t)f.B * f.H;
+    const size_t carry = f.state_out ? 0 : round_up((size_t)BH * f.d_k * f.d_v * 4, 256);
+    const size_t per_row = (size_t)BH * (f.d_k + f.d_v) * elem_size(f.dt);
+    if (carry >= kScratchBytes) return PiecePlan{0, 0};
+    int64_t rows = (int64_t)((kScratchBytes - carry) / per_row) / f.C * f.C;
+    while (rows >= f.C) {
+        const size_t ws = chunk_workspace(f.var, f.dt, f.B, f.H, (int)rows, f.d_k, f.d_v, f.C);
+        if (ws + carry <= kScratchBytes) return PiecePlan{(int)rows, ws};
+        rows -= f.C;
+    }
+    return PiecePlan{0, 0};
+}
+
 }  // namespace
 
 extern "C" {
@@ -303,92 +478,61 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
                        const float *state_in, const float *z_in, void *o, float *state_out,
                        float *z_out, int B, int H, int L, int d_k, int d_v, int C, void *workspace,
                        size_t workspace_bytes, void *stream) {
-    la_status s = check_chunk_shape(var, dt, B, H, L, d_k, d_v, C);
+    const FwdCall f{var, dt, o_dt, q, k, v, log_gate, beta, state_in, z_in, o, state_out, z_out,
+                    B, H, L, d_k, d_v, C};
+    la_status s = validate_fwd(f);
     if (s != LA_OK) return s;
-    if (o_dt != LA_F32 && o_dt != LA_BF16) return LA_ERR_INVALID_ARG;
-    if (!dtype_pair_ok(dt, o_dt)) return LA_ERR_UNSUPPORTED;
-    const int64_t BH = (int64_t)B * H;
-    const size_t es = elem_size(dt), oes = elem_size(o_dt);
-    const bool has_tokens = L > 0;
-    // required / forbidden pointers
-    if (has_tokens && (!q || !k || !o)) return LA_ERR_INVALID_ARG;
-    if (has_tokens && !v) return LA_ERR_INVALID_ARG;
-    if ((var == LA_DECAY || var == LA_VECTOR_DECAY) && has_tokens && !log_gate) return LA_ERR_INVALID_ARG;
-    if ((var == LA_PLAIN || var == LA_NORMALIZED) && log_gate) return LA_ERR_INVALID_ARG;
-    if (var == LA_GATED_DELTA && has_tokens && !beta) return LA_ERR_INVALID_ARG;
-    if (var != LA_GATED_DELTA && beta) return LA_ERR_INVALID_ARG;
-    if (var != LA_NORMALIZED && (z_in || z_out)) return LA_ERR_INVALID_ARG;
-    // alignment
-    const void *ptrs[] = {q, k, v, o, log_gate, beta, state_in, z_in, state_out, z_out};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
-    // aliasing: outputs must not overlap inputs (state_out == state_in is allowed)
-    const size_t qk_b = (size_t)BH * L * d_k * es, v_b = (size_t)BH * L * d_v * es;
-    const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4, z_b = (size_t)BH * d_k * 4;
-    const size_t lg_b = var == LA_VECTOR_DECAY ? g_b * d_k : g_b;
-    const Span o_sp{o, (size_t)BH * L * d_v * oes}, so_sp{state_out, s_b}, zo_sp{z_out, z_b};
-    const Span ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {log_gate, lg_b}, {beta, g_b}, {z_in, z_b}};
-    for (const Span &in : ins) {
-        if (overlap(o_sp, in) || overlap(so_sp, in) || overlap(zo_sp, in)) return LA_ERR_INVALID_ARG;
-    }
-    if (overlap(o_sp, Span{state_in, s_b}) || overlap(o_sp, so_sp) || overlap(o_sp, zo_sp) ||
-        overlap(so_sp, zo_sp) || overlap(zo_sp, Span{state_in, s_b}))
-        return LA_ERR_INVALID_ARG;
-    if (state_out && state_in && state_out != state_in && overlap(so_sp, Span{state_in, s_b}))
-        return LA_ERR_INVALID_ARG;
-    // workspace
     const size_t need = chunk_workspace(var, dt, B, H, L, d_k, d_v, C);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return LA_ERR_INVALID_ARG;
         if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
         const Span ws{workspace, need};
-        for (const Span &in : ins)
-            if (overlap(ws, in)) return LA_ERR_INVALID_ARG;
-        if (overlap(ws, o_sp) || overlap(ws, so_sp) || overlap(ws, Span{state_in, s_b}))
-            return LA_ERR_INVALID_ARG;
+        for (const Span &sp : fwd_spans(f))
+            if (overlap(ws, sp)) return LA_ERR_INVALID_ARG;
     }
+    s = check_device();
+    if (s != LA_OK) return s;
+    return run_fwd(f, 0, L, state_in, state_out, workspace, reinterpret_cast<hipStream_t>(stream));
+}
 
+la_status la_chunk_fwd_noalloc(la_variant var, la_dtype dt, la_dtype o_dt, const void *q,
+                               const void *k, const void *v, const float *log_gate,
+                               const float *beta, const float *state_in, const float *z_in, void *o,
+                               float *state_out, float *z_out, int B, int H, int L, int d_k,
+                               int d_v, int C, void *stream) {
+    const FwdCall f{var, dt, o_dt, q, k, v, log_gate, beta, state_in, z_in, o, state_out, z_out,
+                    B, H, L, d_k, d_v, C};
+    la_status s = validate_fwd(f);
+    if (s != LA_OK) return s;
+    const PiecePlan plan = plan_pieces(f);
+    if (plan.rows == 0) return LA_ERR_UNSUPPORTED;  // one chunk of every head exceeds the scratch
     s = check_device();
     if (s != LA_OK) return s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-
-    const int nchunks = (L + C - 1) / C;
-    const int Lp = nchunks * C;
-    ChunkArgs a{};
-    a.q = q; a.k = k; a.v = v; a.lg = log_gate;
-    a.s_in = state_in; a.z_in = z_in; a.o = o; a.s_out = state_out; a.z_out = z_out;
-    const Geometry geo = choose_geometry(var, dt, BH, d_v, C);
-    a.BH = (int)BH; a.L = L; a.Lp = Lp; a.dv = d_v; a.nsplit = d_v / geo.dvt;
-
-    if (var == LA_GATED_DELTA && has_tokens) {
-        char *ws = static_cast<char *>(workspace);
-        a.w = ws;
-        a.ut = ws + gdn_w_bytes(dt, BH, Lp, d_k);
-        PrepArgs p{};
-        p.k = k; p.v = v; p.lg = log_gate; p.beta = beta;
-        p.w = const_cast<void *>(a.w); p.ut = const_cast<void *>(a.ut);
-        p.BH = (int)BH; p.L = L; p.Lp = Lp; p.dv = d_v; p.nchunks = nchunks;
-        const hipError_t e = (dt == LA_BF16) ? dispatch_prep<bf16>(d_k, p, st)
-                                             : dispatch_prep<float>(d_k, p, st);
-        if (e != hipSuccess) return LA_ERR_HIP;
+    if (plan.rows >= L) {  // no workspace needed, or one piece
+        char *scr = nullptr;
+        if (chunk_workspace(var, dt, B, H, L, d_k, d_v, C) > 0) {
+            s = scratch_for_current_device(&scr);
+            if (s != LA_OK) return s;
+        }
+        return run_fwd(f, 0, L, state_in, state_out, scr, st);
     }
-    hipError_t e;
-    if (var == LA_VECTOR_DECAY) {  // the launcher picks its own value slices
-        if (dt == LA_F32)
-            e = dispatch_vdecay<float, float>(d_k, a, st);
-        else if (o_dt == LA_F32)
-            e = dispatch_vdecay<bf16, float>(d_k, a, st);
-        else
-            e = dispatch_vdecay<bf16, bf16>(d_k, a, st);
-        return from_hip(e);
+    // Pieces of plan.rows tokens (a multiple of C), chained through the fp32
+    // state: in state_out when the caller wants it (in place from the second
+    // piece on), else in the scratch after the per-chunk products.
+    char *scr = nullptr;
+    s = scratch_for_current_device(&scr);
+    if (s != LA_OK) return s;
+    float *carry = state_out ? state_out : reinterpret_cast<float *>(scr + plan.ws_bytes);
+    for (int p0 = 0; p0 < L; p0 += plan.rows) {
+        const int n = L - p0 < plan.rows ? L - p0 : plan.rows;
+        const bool last = p0 + n == L;
+        const float *sin = p0 == 0 ? state_in : carry;
+        float *sout = last ? state_out : carry;
+        s = run_fwd(f, p0, n, sin, sout, scr, st);
+        if (s != LA_OK) return s;
     }
-    if (dt == LA_F32)
-        e = dispatch_chunk_dk<float, float>(var, d_k, C, geo, a, st);
-    else if (o_dt == LA_F32)
-        e = dispatch_chunk_dk<bf16, float>(var, d_k, C, geo, a, st);
-    else
-        e = dispatch_chunk_dk<bf16, bf16>(var, d_k, C, geo, a, st);
-    return from_hip(e);
+    return LA_OK;
 }
 
 la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void *q, const void *k,

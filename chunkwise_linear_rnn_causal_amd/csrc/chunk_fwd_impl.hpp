@@ -290,11 +290,11 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
 
     // Per-head bases; offsets inside a head are 32-bit (the ABI layer refuses
     // ceil(L / C) * C * max(d_k, d_v) >= 2^31).
-    const TI *qg = (const TI *)a.q + (size_t)bh * L * DK;
-    const TI *kg = (const TI *)a.k + (size_t)bh * L * DK;
-    const TI *vg = (VAR == V_GDN) ? nullptr : (const TI *)a.v + (size_t)bh * L * dv + j0;
-    TO *og = (TO *)a.o + (size_t)bh * L * dv + j0;
-    const float *lgg = (DECAYED && a.lg) ? a.lg + (size_t)bh * L : nullptr;
+    const TI *qg = (const TI *)a.q + (size_t)bh * a.ld * DK;
+    const TI *kg = (const TI *)a.k + (size_t)bh * a.ld * DK;
+    const TI *vg = (VAR == V_GDN) ? nullptr : (const TI *)a.v + (size_t)bh * a.ld * dv + j0;
+    TO *og = (TO *)a.o + (size_t)bh * a.ld * dv + j0;
+    const float *lgg = (DECAYED && a.lg) ? a.lg + (size_t)bh * a.ld : nullptr;
     const TM *wg = (VAR == V_GDN) ? (const TM *)a.w + (size_t)bh * a.Lp * DK : nullptr;
     const TM *utg = (VAR == V_GDN) ? (const TM *)a.ut + (size_t)bh * a.Lp * dv + j0 : nullptr;
 

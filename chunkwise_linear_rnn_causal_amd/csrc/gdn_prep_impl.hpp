@@ -80,10 +80,10 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
     const int bh = blockIdx.x / a.nchunks, c = blockIdx.x - bh * a.nchunks;
     const int t0 = c * C, L = a.L, dv = a.dv;
-    const TI *kg = (const TI *)a.k + (size_t)bh * L * DK;
-    const TI *vg = (const TI *)a.v + (size_t)bh * L * dv;
-    const float *lgg = a.lg ? a.lg + (size_t)bh * L : nullptr;
-    const float *bg = a.beta + (size_t)bh * L;
+    const TI *kg = (const TI *)a.k + (size_t)bh * a.ld * DK;
+    const TI *vg = (const TI *)a.v + (size_t)bh * a.ld * dv;
+    const float *lgg = a.lg ? a.lg + (size_t)bh * a.ld : nullptr;
+    const float *bg = a.beta + (size_t)bh * a.ld;
 
     // Every global load of the chunk is issued first (log-gate, beta, K and V
     // rows), so their latencies overlap. Staging unit u (one per thread) covers

@@ -20,6 +20,8 @@ struct ChunkArgs {
     const void *w;              // gated delta: W  [BH, Lp, DK] (operand type)
     const void *ut;             // gated delta: U~ [BH, Lp, dv] (operand type)
     int BH, L, Lp, dv, nsplit;  // Lp = ceil(L / C) * C; nsplit = dv / DVT (workgroups per head)
+    int ld;                     // rows between consecutive heads of q, k, v, o and the gates
+                                // (>= L; L unless a piece of a longer sequence is run)
 };
 
 // Chunk-parallel preparation of the gated delta rule (one block per chunk).
@@ -28,6 +30,7 @@ struct PrepArgs {
     const float *lg, *beta;     // [BH, L] (lg may be nullptr)
     void *w, *ut;               // outputs, layouts as in ChunkArgs
     int BH, L, Lp, dv, nchunks;
+    int ld;                     // rows between consecutive heads of k, v and the gates (>= L)
 };
 
 struct DecodeArgs {

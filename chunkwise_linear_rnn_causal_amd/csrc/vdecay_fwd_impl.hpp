@@ -126,11 +126,11 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
     const int vid = xcd_virtual_block();
     const int bh = vid / a.nsplit, split = vid % a.nsplit;
     const int L = a.L, dv = a.dv, j0 = split * DVT;
-    const TI *qg = (const TI *)a.q + (size_t)bh * L * DK;
-    const TI *kg = (const TI *)a.k + (size_t)bh * L * DK;
-    const TI *vg = (const TI *)a.v + (size_t)bh * L * dv + j0;
-    const float *lgg = a.lg + (size_t)bh * L * DK + wv * GW;  // this wave's gate channels
-    TO *og = (TO *)a.o + (size_t)bh * L * dv + j0;
+    const TI *qg = (const TI *)a.q + (size_t)bh * a.ld * DK;
+    const TI *kg = (const TI *)a.k + (size_t)bh * a.ld * DK;
+    const TI *vg = (const TI *)a.v + (size_t)bh * a.ld * dv + j0;
+    const float *lgg = a.lg + (size_t)bh * a.ld * DK + wv * GW;  // this wave's gate channels
+    TO *og = (TO *)a.o + (size_t)bh * a.ld * dv + j0;
     const int nchunks = (L + C - 1) / C;
     const int rb = wv < 4 ? wv : 7 - wv;  // query row block (waves w, w+4 share a SIMD)
     const int hh = wv >> 2;               // half of the value slice

@@ -250,6 +250,29 @@ la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k
                        int d_k, int d_v, int C, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/*
+ * la_chunk_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). The same arguments as la_chunk_fwd and the same
+ * results. The delta rule's per-chunk products go to a static device array of
+ * LA_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends; the call itself allocates nothing. When the whole
+ * sequence's products do not fit, the sequence is run in pieces of whole
+ * chunks, chained through the fp32 state (in state_out when given, else in the
+ * scratch), so any L works. LA_ERR_UNSUPPORTED when one chunk of every head
+ * does not fit (B*H*C*(d_k+d_v)*sizeof(input) plus the carried state above the
+ * scratch). Calls on one device share the scratch: calls that may overlap in
+ * time on one device (different streams, or host threads) race and must be
+ * serialized by the caller. Other variants need no scratch and run as
+ * la_chunk_fwd.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (64u << 20)
+la_status la_chunk_fwd_noalloc(la_variant var, la_dtype dt, la_dtype o_dt, const void *q,
+                               const void *k, const void *v, const float *log_gate,
+                               const float *beta, const float *state_in, const float *z_in, void *o,
+                               float *state_out, float *z_out, int B, int H, int L, int d_k,
+                               int d_v, int C, void *stream);
+
 /* Static string naming a status code. */
 const char *la_status_str(la_status s);
 

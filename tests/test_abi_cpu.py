@@ -97,6 +97,20 @@ def test_chunk_fwd_rejects(kw, expect):
     assert chunk(**kw) == expect
 
 
+def test_noalloc_refuses_problems_whose_chunk_exceeds_the_scratch():
+    lib = la.load_library()
+    G = 1 << 32  # fake, 16-byte aligned, far apart: validation fails first
+    # 4096 heads of d = 128: one chunk of products is 128 MiB, above the 64 MiB scratch
+    st = lib.la_chunk_fwd_noalloc(GDN, BF16, F32, G, 2 * G, 3 * G, None, 4 * G, None, None, 5 * G,
+                                  None, None, 64, 64, 64, 128, 128, 64, None)
+    assert st == UNSUPPORTED
+    # the same shape checks as la_chunk_fwd
+    assert lib.la_chunk_fwd_noalloc(GDN, BF16, F32, G, 2 * G, 3 * G, None, None, None, None, 5 * G,
+                                    None, None, 1, 1, 64, 64, 64, 64, None) == INVALID  # beta missing
+    assert lib.la_chunk_fwd_noalloc(GDN, BF16, F32, G, 2 * G, 3 * G, None, 4 * G, None, None, 5 * G,
+                                    None, None, 1, 1, 64, 48, 64, 64, None) == UNSUPPORTED
+
+
 def dec(var=DECAY, dt=BF16, odt=F32, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, lg=FAKE + 0x3000, beta=None,
         S=0x900000000, o=0x800000000, N=4, H=2, dk=128, dv=128):
     return la.load_library().la_decode_step(var, dt, odt, q, k, v, lg, beta, S, o, N, H, dk, dv, None)
