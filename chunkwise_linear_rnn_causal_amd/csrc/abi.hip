@@ -76,13 +76,26 @@ la_status check_chunk_shape(la_variant var, la_dtype dt, int B, int H, int L, in
     if (d_k != 32 && d_k != 64 && d_k != 128) return LA_ERR_UNSUPPORTED;
     if (d_v < 32 || d_v > 128 || d_v % 32 != 0) return LA_ERR_UNSUPPORTED;
     if (C != 64 && C != 128) return LA_ERR_UNSUPPORTED;
-    if ((var == LA_GATED_DELTA || var == LA_VECTOR_DECAY) && C != 64) return LA_ERR_UNSUPPORTED;
     if (var == LA_VECTOR_DECAY && dt == LA_F32 && d_k == 128) return LA_ERR_UNSUPPORTED;
-    if (dt == LA_F32 && d_k == 128 && C == 128) return LA_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
     if (BH * (d_v / 16) > INT32_MAX || BH * ((L + C - 1) / C) > INT32_MAX) return LA_ERR_UNSUPPORTED;
     if (!head_offsets_fit(L, C, d_k, d_v)) return LA_ERR_UNSUPPORTED;
     return LA_OK;
+}
+
+// Chunk length the kernels run for a requested C. The chunk form gives the same
+// result for every C (tensorplay "Talk Linear Attention", section 3.3: C sets
+// the schedule, not the value). A 128-token chunk of the delta rule, the
+// per-key-channel decay, and fp32 inputs with d_k = 128 (whose fp32 tiles do
+// not fit in LDS at 128 tokens) runs as two 64-token sub-chunks: for the delta
+// rule that is the block forward substitution of the chunk's 128 x 128 UT
+// system over its two halves, U_b = T_b (beta V_b - beta a K_b S_0 - P_ba U_a),
+// which is what the second sub-chunk evaluates with the state carried from the
+// first.
+int kernel_chunk(la_variant var, la_dtype dt, int d_k, int C) {
+    if (C == 128 && (var == LA_GATED_DELTA || var == LA_VECTOR_DECAY || (dt == LA_F32 && d_k == 128)))
+        return 64;
+    return C;
 }
 
 size_t gdn_w_bytes(la_dtype dt, int64_t BH, int64_t Lp, int d_k) {
@@ -91,6 +104,7 @@ size_t gdn_w_bytes(la_dtype dt, int64_t BH, int64_t Lp, int d_k) {
 
 size_t chunk_workspace(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v, int C) {
     if (var != LA_GATED_DELTA || L == 0) return 0;
+    C = kernel_chunk(var, dt, d_k, C);
     const int64_t BH = (int64_t)B * H, Lp = (int64_t)((L + C - 1) / C) * C;
     return gdn_w_bytes(dt, BH, Lp, d_k) + (size_t)BH * Lp * d_v * elem_size(dt);
 }
@@ -356,7 +370,7 @@ la_status run_fwd(const FwdCall &f, int p0, int n, const float *s_in, float *s_o
     const la_dtype dt = f.dt;
     const int64_t BH = (int64_t)f.B * f.H;
     const size_t es = elem_size(dt), oes = elem_size(f.o_dt);
-    const int C = f.C, d_k = f.d_k, d_v = f.d_v;
+    const int C = kernel_chunk(var, dt, f.d_k, f.C), d_k = f.d_k, d_v = f.d_v;
     const int nchunks = (n + C - 1) / C;
     const int Lp = nchunks * C;
     const int gw = var == LA_VECTOR_DECAY ? d_k : 1;  // gates per token
@@ -438,12 +452,13 @@ PiecePlan plan_pieces(const FwdCall &f) {
     const int64_t BH = (int64_t)f.B * f.H;
     const size_t carry = f.state_out ? 0 : round_up((size_t)BH * f.d_k * f.d_v * 4, 256);
     const size_t per_row = (size_t)BH * (f.d_k + f.d_v) * elem_size(f.dt);
+    const int kc = kernel_chunk(f.var, f.dt, f.d_k, f.C);
     if (carry >= kScratchBytes) return PiecePlan{0, 0};
-    int64_t rows = (int64_t)((kScratchBytes - carry) / per_row) / f.C * f.C;
-    while (rows >= f.C) {
+    int64_t rows = (int64_t)((kScratchBytes - carry) / per_row) / kc * kc;
+    while (rows >= kc) {
         const size_t ws = chunk_workspace(f.var, f.dt, f.B, f.H, (int)rows, f.d_k, f.d_v, f.C);
         if (ws + carry <= kScratchBytes) return PiecePlan{(int)rows, ws};
-        rows -= f.C;
+        rows -= kc;
     }
     return PiecePlan{0, 0};
 }

@@ -48,6 +48,13 @@
 
 namespace la {
 
+// Per-channel log-gates below this are taken as this value: the chunk form
+// rebases the decay around the middle of each 16-token block, and with every
+// gate in [-10, 0] each rebased factor stays below e^80, inside fp32. A gate of
+// e^-10 already damps the channel's history to 4.5e-5 per token, so the clamp
+// moves the result by at most that fraction of the damped history.
+constexpr float kMinChannelLogGate = -10.0f;
+
 // Score operand type: bf16 for bf16 inputs (the exponent range of fp32), fp32
 // for fp32 inputs.
 template <typename TI> struct ScoreOp;
@@ -222,7 +229,7 @@ __global__ void __launch_bounds__(512) vdecay_fwd_kernel(ChunkArgs a) {
         for (int u = 0; u < GW / 4; ++u) {
             f32x4 gsum;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) gsum[e] = wave_inclusive_sum(gl[u][e]);
+            for (int e = 0; e < 4; ++e) gsum[e] = wave_inclusive_sum(fmaxf(gl[u][e], kMinChannelLogGate));
             *reinterpret_cast<f32x4 *>(&Gs[lane * PG + wv * GW + 4 * u]) = gsum;
         }
         // the wave reads back the rows it just wrote (one wave's LDS operations

@@ -119,11 +119,12 @@ la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
  *   log_gate    [B,H,L] float32 log-gates l_t <= 0 (finite): required for
  *               LA_DECAY; optional for LA_GATED_DELTA (NULL = alpha 1); must be
  *               NULL for LA_PLAIN and LA_NORMALIZED. LA_VECTOR_DECAY takes
- *               [B,H,L,d_k] (one gate per key channel), required, with every
- *               entry in [-10, 0]: the chunk form rebases the per-channel decay
- *               around the middle of each 16-token block, and that range keeps
- *               every rebased factor below e^80 (results are unspecified
- *               outside it).
+ *               [B,H,L,d_k] (one gate per key channel), required, entries <= 0:
+ *               the chunk form rebases the per-channel decay around the middle
+ *               of each 16-token block, and entries below -10 are taken as -10
+ *               so that every rebased factor stays below e^80 (a gate of e^-10
+ *               already damps the channel's history to 4.5e-5 per token, so
+ *               the result moves by at most that fraction of the damped history).
  *   beta        [B,H,L] float32 in [0,1]: required for LA_GATED_DELTA, NULL
  *               otherwise.
  *   state_in    [B,H,d_k,d_v] float32 initial state, NULL = zero.

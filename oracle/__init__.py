@@ -46,6 +46,9 @@ def load(path: Optional[str] = None):
     lib.oracle_backward.argtypes = [ctypes.c_int, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
                                     L, L, L, L, ctypes.c_int]
     lib.oracle_backward.restype = ctypes.c_int
+    lib.oracle_backward_gdn.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                        L, L, L, L, ctypes.c_int]
+    lib.oracle_backward_gdn.restype = ctypes.c_int
     lib.oracle_short_conv.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, ctypes.c_int]
     lib.oracle_short_conv.restype = ctypes.c_int
     lib.oracle_abi_version.restype = ctypes.c_int
@@ -145,14 +148,18 @@ def short_conv(x, w, state_in=None, threads: int = 0, lib=None):
 
 
 def backward(variant: str, q, k, v, do, log_gate=None, state_in=None, d_state_out=None,
-             threads: int = 0, lib=None):
-    """Gradients through the forward recurrence (see ``oracle_backward``).
+             threads: int = 0, lib=None, beta=None):
+    """Gradients through the forward recurrence (see ``oracle_backward`` and, for
+    "gated_delta", ``oracle_backward_gdn``).
 
     q, k: [..., L, dk]; v, do: [..., L, dv]; log_gate: [..., L] ("vector_decay":
-    [..., L, dk]); state_in, d_state_out: [..., dk, dv]. Returns (dq, dk, dv,
-    d_log_gate or None, d_state_in) in float64.
+    [..., L, dk]); state_in, d_state_out: [..., dk, dv]; beta: [..., L]
+    ("gated_delta" only). Returns (dq, dk, dv, d_log_gate or None, d_state_in) in
+    float64, and for "gated_delta" d_beta as a sixth entry.
     """
     lib = lib or load()
+    if variant == "gated_delta":
+        return _backward_gdn(q, k, v, do, log_gate, beta, state_in, d_state_out, threads, lib)
     q, k, v, do = _c64(q), _c64(k), _c64(v), _c64(do)
     lead = q.shape[:-2]
     L, dk = q.shape[-2], q.shape[-1]
@@ -169,3 +176,25 @@ def backward(variant: str, q, k, v, do, log_gate=None, state_in=None, d_state_ou
     if st != 0:
         raise ValueError(f"oracle_backward failed with status {st}")
     return dq, dkk, dvv, dlg, dsi
+
+
+def _backward_gdn(q, k, v, do, log_gate, beta, state_in, d_state_out, threads, lib):
+    q, k, v, do = _c64(q), _c64(k), _c64(v), _c64(do)
+    lead = q.shape[:-2]
+    L, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    lg, be, s_in, dso = _c64(log_gate), _c64(beta), _c64(state_in), _c64(d_state_out)
+    assert be is not None and be.shape == lead + (L,)
+    dq = np.zeros(q.shape, np.float64)
+    dkk = np.zeros(k.shape, np.float64)
+    dvv = np.zeros(v.shape, np.float64)
+    dlg = np.zeros(lg.shape, np.float64) if lg is not None else None
+    dbe = np.zeros(be.shape, np.float64)
+    dsi = np.zeros(lead + (dk, dv), np.float64)
+    st = lib.oracle_backward_gdn(_p(q), _p(k), _p(v), _p(lg), _p(be), _p(s_in), _p(do), _p(dso),
+                                 _p(dq), _p(dkk), _p(dvv), _p(dlg), _p(dbe), _p(dsi), BH, L, dk, dv,
+                                 int(threads))
+    if st != 0:
+        raise ValueError(f"oracle_backward_gdn failed with status {st}")
+    return dq, dkk, dvv, dlg, dsi, dbe

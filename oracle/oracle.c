@@ -365,3 +365,128 @@ int oracle_backward(int variant, const double *q, const double *k, const double 
     }
     return status;
 }
+
+/*
+ * Backward pass of the gated delta rule for one batch-head, by reverse mode of
+ * the per-token recurrence (canonical orientation, as in run_head):
+ *   r_t = S_{t-1}^T k_t
+ *   S_t = a_t (S_{t-1} - b_t k_t r_t^T) + b_t k_t v_t^T = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T
+ *   o_t = S_t^T q_t,   a_t = exp(l_t) (1 without log-gates), b_t = beta_t
+ * (wln20 "LLM注意力优化：线性注意力", Gated DeltaNet section; tensorplay section 6.2).
+ * Every state S_0 .. S_L is kept (plain, not memory-lean). Walking t = L .. 1
+ * with G the gradient of the loss with respect to S_t:
+ *   G    += q_t do_t^T                       (o_t reads S_t)
+ *   dq_t  = S_t do_t
+ *   dv_t  = b G^T k                          (from b k v^T)
+ *   dk_t  = b G v - a b (G r + S_{t-1} G^T k) (from b k v^T and -a b k k^T S_{t-1})
+ *   db_t  = k^T G (v - a r)
+ *   da_t  = <G, S_{t-1}> - b (k^T G) . r,     dl_t = a da_t
+ *   G     = a (G - b k (k^T G))              (gradient of S_{t-1}; I - b k k^T is symmetric)
+ * and d_state_in = G at the end.
+ */
+static int bwd_head_gdn(const double *q, const double *k, const double *v, const double *lg,
+                        const double *be, const double *s_in, const double *dout,
+                        const double *ds_out, double *dq, double *dk, double *dv, double *dlg,
+                        double *dbe, double *ds_in, long L, long dk_, long dv_)
+{
+    const long D = dk_ * dv_;
+    double *S = (double *)malloc(sizeof(double) * (size_t)((L + 1) * D));
+    double *G = (double *)malloc(sizeof(double) * (size_t)D);
+    double *r = (double *)malloc(sizeof(double) * (size_t)dv_);
+    double *Gk = (double *)malloc(sizeof(double) * (size_t)dv_);
+    if (!S || !G || !r || !Gk) {
+        free(S); free(G); free(r); free(Gk);
+        return OR_NO_MEM;
+    }
+    for (long i = 0; i < D; ++i) S[i] = s_in ? s_in[i] : 0.0;
+    for (long t = 0; t < L; ++t) {
+        const double *Sp = S + t * D, *kt = k + t * dk_, *vt = v + t * dv_;
+        double *Sn = S + (t + 1) * D;
+        const double a = lg ? exp(lg[t]) : 1.0, b = be[t];
+        for (long j = 0; j < dv_; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < dk_; ++i) acc += Sp[i * dv_ + j] * kt[i];
+            r[j] = acc;
+        }
+        for (long i = 0; i < dk_; ++i)
+            for (long j = 0; j < dv_; ++j)
+                Sn[i * dv_ + j] = a * (Sp[i * dv_ + j] - b * kt[i] * r[j]) + kt[i] * b * vt[j];
+    }
+    for (long i = 0; i < D; ++i) G[i] = ds_out ? ds_out[i] : 0.0;
+    for (long t = L - 1; t >= 0; --t) {
+        const double *qt = q + t * dk_, *kt = k + t * dk_, *vt = v + t * dv_, *dot = dout + t * dv_;
+        const double *St = S + (t + 1) * D, *Sp = S + t * D;
+        const double a = lg ? exp(lg[t]) : 1.0, b = be[t];
+        for (long i = 0; i < dk_; ++i)
+            for (long j = 0; j < dv_; ++j) G[i * dv_ + j] += qt[i] * dot[j];
+        for (long i = 0; i < dk_; ++i) {
+            double acc = 0.0;
+            for (long j = 0; j < dv_; ++j) acc += St[i * dv_ + j] * dot[j];
+            dq[t * dk_ + i] = acc;
+        }
+        for (long j = 0; j < dv_; ++j) {
+            double rj = 0.0, gk = 0.0;
+            for (long i = 0; i < dk_; ++i) {
+                rj += Sp[i * dv_ + j] * kt[i];
+                gk += G[i * dv_ + j] * kt[i];
+            }
+            r[j] = rj;
+            Gk[j] = gk;
+            dv[t * dv_ + j] = b * gk;
+        }
+        for (long i = 0; i < dk_; ++i) {
+            double gv = 0.0, gr = 0.0, sgk = 0.0;
+            for (long j = 0; j < dv_; ++j) {
+                gv += G[i * dv_ + j] * vt[j];
+                gr += G[i * dv_ + j] * r[j];
+                sgk += Sp[i * dv_ + j] * Gk[j];
+            }
+            dk[t * dk_ + i] = b * gv - a * b * (gr + sgk);
+        }
+        double db = 0.0, gkr = 0.0, gs = 0.0;
+        for (long j = 0; j < dv_; ++j) {
+            db += Gk[j] * (vt[j] - a * r[j]);
+            gkr += Gk[j] * r[j];
+        }
+        for (long i = 0; i < D; ++i) gs += G[i] * Sp[i];
+        if (dbe) dbe[t] = db;
+        if (dlg) dlg[t] = a * (gs - b * gkr);
+        for (long i = 0; i < dk_; ++i)
+            for (long j = 0; j < dv_; ++j)
+                G[i * dv_ + j] = a * (G[i * dv_ + j] - b * kt[i] * Gk[j]);
+    }
+    if (ds_in) memcpy(ds_in, G, sizeof(double) * (size_t)D);
+    free(S); free(G); free(r); free(Gk);
+    return OR_OK;
+}
+
+/*
+ * Backward pass of the gated delta rule over BH batch-heads (see bwd_head_gdn).
+ * log_gate may be NULL (alpha = 1, DeltaNet); then d_log_gate is not written.
+ * Layouts as in oracle_backward; beta and d_beta [BH, L].
+ */
+int oracle_backward_gdn(const double *q, const double *k, const double *v, const double *log_gate,
+                        const double *beta, const double *state_in, const double *dout,
+                        const double *d_state_out, double *dq, double *dk, double *dv,
+                        double *d_log_gate, double *d_beta, double *d_state_in, long BH, long L,
+                        long dk_, long dv_, int nthreads)
+{
+    if (BH < 0 || L < 0 || dk_ <= 0 || dv_ <= 0) return OR_BAD_ARG;
+    if (BH > 0 && L > 0 && (!q || !k || !v || !beta || !dout || !dq || !dk || !dv)) return OR_BAD_ARG;
+    int status = OR_OK;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) reduction(max : status)
+#endif
+    for (long h = 0; h < BH; ++h) {
+        int st = bwd_head_gdn(q + h * L * dk_, k + h * L * dk_, v + h * L * dv_,
+                              log_gate ? log_gate + h * L : NULL, beta + h * L,
+                              state_in ? state_in + h * dk_ * dv_ : NULL, dout + h * L * dv_,
+                              d_state_out ? d_state_out + h * dk_ * dv_ : NULL, dq + h * L * dk_,
+                              dk + h * L * dk_, dv + h * L * dv_,
+                              (d_log_gate && log_gate) ? d_log_gate + h * L : NULL,
+                              d_beta ? d_beta + h * L : NULL,
+                              d_state_in ? d_state_in + h * dk_ * dv_ : NULL, L, dk_, dv_);
+        if (st > status) status = st;
+    }
+    return status;
+}

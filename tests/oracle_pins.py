@@ -746,6 +746,66 @@ def pin_backward_finite_differences(lib):
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (variant, ai, fd, an)
 
 
+def _gdn_bwd_case(r, B=2, L=9, dk=4, dv=3, gated=True):
+    q = r.standard_normal((B, L, dk))
+    k = r.standard_normal((B, L, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)          # unit keys, as the workload
+    v, do = r.standard_normal((B, L, dv)), r.standard_normal((B, L, dv))
+    lg = -0.6 * r.random((B, L)) if gated else None
+    be = 0.1 + 0.8 * r.random((B, L))
+    s0 = r.standard_normal((B, dk, dv))
+    dso = r.standard_normal((B, dk, dv))
+    return q, k, v, do, lg, be, s0, dso
+
+
+def pin_backward_gdn_finite_differences(lib):
+    """Gated delta rule: every gradient (q, k, v, log-gates, beta, initial state)
+    matches the central difference of the forward oracle's loss
+    <do, O> + <dS_L, S_L> along a random direction, with and without log-gates
+    (fp64, step 1e-6)."""
+    r = _rng(53)
+    for gated in (True, False):
+        q, k, v, do, lg, be, s0, dso = _gdn_bwd_case(r, gated=gated)
+
+        def loss(q_, k_, v_, lg_, be_, s0_):
+            o, s, _ = oracle.forward("gated_delta", q_, k_, v_, log_gate=lg_, beta=be_, state_in=s0_,
+                                     lib=lib)
+            return float((o * do).sum() + (s * dso).sum())
+
+        dq, dk, dv, dlg, dsi, dbe = oracle.backward("gated_delta", q, k, v, do, lg, s0, dso, lib=lib,
+                                                    beta=be)
+        assert (dlg is None) == (not gated)
+        eps = 1e-6
+        args = [q, k, v, lg, be, s0]
+        grads = [dq, dk, dv, dlg, dbe, dsi]
+        for ai, (x, gx) in enumerate(zip(args, grads)):
+            if x is None:
+                continue
+            u = r.standard_normal(x.shape)
+            plus, minus = list(args), list(args)
+            plus[ai], minus[ai] = x + eps * u, x - eps * u
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            an = float((gx * u).sum())
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (gated, ai, fd, an)
+
+
+def pin_backward_gdn_reductions(lib):
+    """beta = 0 leaves only the decay S_t = alpha_t S_{t-1}: dq, the log-gate
+    gradient and dS_0 equal the decay backward with zero keys, and dk, dv vanish.
+    A zero log-gate equals the ungated rule (alpha = 1, DeltaNet)."""
+    r = _rng(54)
+    q, k, v, do, lg, be, s0, dso = _gdn_bwd_case(r, L=11)
+    z = np.zeros_like(be)
+    dq, dk, dv, dlg, dsi, dbe = oracle.backward("gated_delta", q, k, v, do, lg, s0, dso, lib=lib, beta=z)
+    rq, _, _, rlg, rsi = oracle.backward("decay", q, np.zeros_like(k), v, do, lg, s0, dso, lib=lib)
+    assert _rel(dq, rq) <= 1e-13 and _rel(dlg, rlg) <= 1e-13 and _rel(dsi, rsi) <= 1e-13
+    assert np.abs(dk).max() == 0.0 and np.abs(dv).max() == 0.0
+    g0 = oracle.backward("gated_delta", q, k, v, do, np.zeros_like(lg), s0, dso, lib=lib, beta=be)
+    g1 = oracle.backward("gated_delta", q, k, v, do, None, s0, dso, lib=lib, beta=be)
+    for i in (0, 1, 2, 4, 5):
+        assert _rel(g0[i], g1[i]) <= 1e-14, i
+
+
 def pin_backward_plain_closed_form(lib):
     """PLAIN with an initial state: O = (Q K^T (.) M) V + Q S_0 and S_L = S_0 + K^T V
     give dQ = (dO V^T (.) M) K + dO S_0^T, dK = (dO V^T (.) M)^T Q + V dS_L^T,
@@ -798,4 +858,5 @@ ALL_PINS = [
     pin_vector_decay_parallel_form, pin_vector_decay_uniform_is_scalar, pin_vector_decay_fraction,
     pin_vector_decay_channel_isolation, pin_vector_decay_resume_and_decode,
     pin_backward_finite_differences, pin_backward_plain_closed_form, pin_backward_gate_identity,
+    pin_backward_gdn_finite_differences, pin_backward_gdn_reductions,
 ]

@@ -59,7 +59,8 @@ def test_workspace_sizes():
     w = -(-2 * 3 * 128 * 64 * 2 // 256) * 256
     assert st == 0 and n == w + 2 * 3 * 128 * 32 * 2
     assert wsize(L=0) == (0, 0)
-    assert wsize(C=128)[0] == UNSUPPORTED      # delta rule is built for C = 64
+    # C = 128: the delta rule runs its 128-token chunks as two 64-token sub-chunks
+    assert wsize(C=128) == wsize(C=64)
     assert la.load_library().la_chunk_fwd_workspace_size(GDN, BF16, 1, 1, 8, 64, 64, 64, None) == INVALID
     # the largest head the 32-bit row offsets address, and one chunk more
     assert wsize(B=1, H=1, L=2 ** 24 - 64, dk=128, dv=128)[0] == 0
@@ -69,7 +70,6 @@ def test_workspace_sizes():
 @pytest.mark.parametrize("kw,expect", [
     (dict(var=7), INVALID), (dict(dt=5), INVALID), (dict(odt=5), INVALID),
     (dict(var=VDECAY), INVALID),                      # per-channel decay needs its gates
-    (dict(var=VDECAY, lg=FAKE + 0x100000, C=128), UNSUPPORTED),
     (dict(var=VDECAY, lg=FAKE + 0x100000, dt=F32, dk=128), UNSUPPORTED),
     (dict(var=VDECAY, lg=FAKE + 0x100000, o=FAKE + 0x100000 + 0x7000), INVALID),  # o inside the gates
     (dict(dt=F32, odt=BF16), UNSUPPORTED),
@@ -77,7 +77,6 @@ def test_workspace_sizes():
     (dict(dk=48), UNSUPPORTED), (dict(dk=256), UNSUPPORTED),
     (dict(dv=48), UNSUPPORTED), (dict(dv=256), UNSUPPORTED),
     (dict(C=32), UNSUPPORTED), (dict(C=256), UNSUPPORTED),
-    (dict(dt=F32, dk=128, C=128), UNSUPPORTED),
     # row offsets inside one head are 32-bit: ceil(L/C)*C*max(d_k, d_v) < 2^31
     (dict(L=2 ** 24, dk=128, dv=32), UNSUPPORTED), (dict(L=2 ** 24 - 63, dk=32, dv=128), UNSUPPORTED),
     (dict(L=2 ** 25 - 63, dk=64, dv=64), UNSUPPORTED),

@@ -21,11 +21,7 @@ def _cases():
     for var in ("plain", "normalized", "decay", "gated_delta"):
         for dt in ("bf16", "f32"):
             for C in (64, 128):
-                if var == "gated_delta" and C != 64:
-                    continue
                 for dk, dv in SHAPES:
-                    if dt == "f32" and dk == 128 and C == 128:
-                        continue
                     out.append((var, dt, C, dk, dv))
     return out
 
@@ -110,14 +106,28 @@ def test_deterministic(var):
 def test_chunk_sizes_agree(var):
     """C = 64 and C = 128 compute the same result (tensorplay section 3.3: the
     chunk size changes the schedule, not the value)."""
-    if var == "gated_delta":
-        pytest.skip("the delta rule is built for C = 64")
     inp = W.make_chunk_inputs(var, "bf16", 1, 2, 500, 64, 64, seed=7)
     o64, s64, _ = gpu_chunk(inp, 64, state_in=False)
     o128, s128, _ = gpu_chunk(inp, 128, state_in=False)
     ro, rs, _ = oracle_chunk(inp, state_in=False)
     assert_close(o64, ro, TOL["bf16"], "C=64")
     assert_close(o128, ro, TOL["bf16"], "C=128")
+
+
+@pytest.mark.parametrize("var,dt,dk", [("gated_delta", "bf16", 128), ("gated_delta", "f32", 64),
+                                       ("vector_decay", "bf16", 128), ("decay", "f32", 128)])
+def test_c128_sub_chunk_schedule(var, dt, dk):
+    """Where a 128-token chunk runs as two 64-token sub-chunks (the delta rule:
+    block forward substitution of the 128 x 128 UT system; the per-channel gate;
+    fp32 tiles at d_k = 128), C = 128 gives the bits of C = 64, and both match
+    the oracle."""
+    inp = W.make_chunk_inputs(var, dt, 2, 2, 3 * 128 + 37, dk, 64, seed=14, with_state=True)
+    o64, s64, _ = gpu_chunk(inp, 64)
+    o128, s128, _ = gpu_chunk(inp, 128)
+    assert np.array_equal(o64, o128) and np.array_equal(s64, s128)
+    ro, rs, _ = oracle_chunk(inp)
+    assert_close(o128, ro, TOL[dt], "o")
+    assert_close(s128, rs, TOL[dt], "state")
 
 
 @pytest.mark.parametrize("var", ["plain", "normalized", "decay", "gated_delta"])
@@ -227,8 +237,6 @@ def test_bf16_output(var, C):
     """o_dt = bf16: the same kernels, with the output rounded to nearest even.
     Bound: the fp32-output tolerance plus bf16's rounding of each value
     (|err| <= 2e-2 RMS + 2^-8 |o|)."""
-    if var == "gated_delta" and C != 64:
-        pytest.skip("the delta rule is built for C = 64")
     inp = W.make_chunk_inputs(var, "bf16", 2, 2, 2 * C + 9, 128, 64, seed=12)
     q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
     o, _, _ = la.la_chunk_fwd(var, q, k, v, dev(inp.log_gate), dev(inp.beta), C=C,

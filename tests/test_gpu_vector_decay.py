@@ -140,3 +140,21 @@ def test_vector_decay_prefill_then_decode():
     ro, rs, _ = oracle_chunk(inp, state_in=False)
     assert_close(host64(o), ro[:, :, L], TOL["bf16"], "o")
     assert_close(host64(S), rs, TOL["bf16"], "state")
+
+
+@pytest.mark.parametrize("C", [64, 128])
+def test_vector_decay_gates_below_the_rebasing_range(C):
+    """Per-channel log-gates far below -10 (every eighth gate at -30, some whole
+    tokens at -60): the kernel takes them as -10, which damps the history to
+    4.5e-5 per token instead of less; the result stays within the bf16
+    tolerance of the oracle, which uses the gates as given."""
+    inp = W.make_chunk_inputs(VD, "bf16", 2, 2, 3 * 64 + 29, 128, 64, seed=41, with_state=True,
+                              recipe="gla_strong")
+    lg = inp.log_gate.copy()
+    lg[..., ::8] = -30.0
+    lg[:, :, 70:75, :] = -60.0
+    inp.log_gate = lg
+    o, s, _ = gpu_chunk(inp, C)
+    ro, rs, _ = oracle_chunk(inp)
+    assert_close(o, ro, TOL["bf16"], "o")
+    assert_close(s, rs, TOL["bf16"], "state")

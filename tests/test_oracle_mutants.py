@@ -40,6 +40,13 @@ MUTANTS = {
     "bwd_gate_grad_without_gate": ("if (dlg) dlg[t] = g * acc;", "if (dlg) dlg[t] = acc;"),
     "bwd_dv_transposed": ("for (long i = 0; i < dk_; ++i) acc += dS[i * dv_ + j] * kt[i];",
                           "for (long i = 0; i < dk_; ++i) acc += dS[(i % dv_) * dv_ + (j % dk_)] * kt[i];"),
+    "bwd_gdn_dk_missing_state_term": ("dk[t * dk_ + i] = b * gv - a * b * (gr + sgk);",
+                                      "dk[t * dk_ + i] = b * gv - a * b * gr;"),
+    "bwd_gdn_dbeta_without_retrieval": ("db += Gk[j] * (vt[j] - a * r[j]);", "db += Gk[j] * vt[j];"),
+    "bwd_gdn_state_grad_no_projection": ("G[i * dv_ + j] = a * (G[i * dv_ + j] - b * kt[i] * Gk[j]);",
+                                         "G[i * dv_ + j] = a * G[i * dv_ + j];"),
+    "bwd_gdn_gate_grad_sign": ("if (dlg) dlg[t] = a * (gs - b * gkr);", "if (dlg) dlg[t] = a * (gs + b * gkr);"),
+    "bwd_gdn_dv_without_beta": ("dv[t * dv_ + j] = b * gk;", "dv[t * dv_ + j] = gk;"),
     "conv_taps_reversed": ("acc += w[(h * d + c) * K + tau] * hist[(W + t - tau) * d + c];",
                            "acc += w[(h * d + c) * K + (K - 1 - tau)] * hist[(W + t - tau) * d + c];"),
     "conv_head_weights_shared": ("acc += w[(h * d + c) * K + tau]", "acc += w[c * K + tau]"),
