@@ -124,7 +124,7 @@ constexpr int kNumCU = 256;
 
 Geometry choose_geometry(la_variant var, la_dtype dt, int64_t BH, int d_v, int C) {
     if (dt == LA_F32 || C == 128) return {32, 4};
-    if (var == LA_GATED_DELTA) return (BH * (d_v / 32) >= kNumCU) ? Geometry{32, 8} : Geometry{16, 8};
+    if (var == LA_GATED_DELTA) return {16, 8};  // the chain kernel: 16-column slices
     if (d_v % 64 == 0 && BH * (d_v / 64) >= kNumCU) return {64, 8};
     return {32, 8};
 }
@@ -145,10 +145,7 @@ hipError_t dispatch_chunk(la_variant var, int C, Geometry geo, const ChunkArgs &
     constexpr bool F32 = sizeof(TI) == 4;
     if (var == LA_GATED_DELTA) {
         if constexpr (F32) return launch_chunk<V_GDN, TI, TO, DK, 32, 64, 4>(a, st);
-        if constexpr (!F32) {
-            if (geo.dvt == 32) return launch_chunk<V_GDN, TI, TO, DK, 32, 64, 8>(a, st);
-            return launch_chunk<V_GDN, TI, TO, DK, 16, 64, 8>(a, st);
-        }
+        if constexpr (!F32) return launch_gdn_fwd<TO, DK>(a, st);
     }
     if (C == 128) {
         if constexpr (!(F32 && DK == 128)) return launch_var<TI, TO, DK, 32, 128, 4>(var, a, st);

@@ -16,9 +16,11 @@
 // forms U = U~ - W S_prev.
 //
 // Layout of the results, in the tensor-core operand type (fp16 for bf16
-// inputs, fp32 for fp32 inputs): W row-major [BH, Lp, DK]; U~ row-major
-// [BH, Lp, dv] (the serial pass reads four consecutive columns per lane). Padded tokens
-// (t >= L) have beta = 0 and k = v = 0, which makes their rows of W and U~ zero.
+// inputs, fp32 for fp32 inputs): W row-major [BH, Lp, DK]; U~ [BH, Lp, dv]
+// elements, row-major for fp32 inputs (the serial pass reads four consecutive
+// columns per lane), and for bf16 inputs in the accumulator layout of the
+// serial pass (see the store below). Padded tokens (t >= L) have beta = 0 and
+// k = v = 0, which makes their rows of W and U~ zero.
 #pragma once
 
 #include "la_common.hpp"
@@ -276,20 +278,40 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     }
     __syncthreads();
 
-    // U~ row-major, from transposed tiles D[j][r] = sum_s (beta V)[s][j] T[r][s];
-    // lane holds r = rb*16 + n and four consecutive columns j = jb*16 + 4g + e.
-    TM *uout = (TM *)a.ut + ((size_t)bh * a.Lp + t0) * dv;
     const int NJB = dv / 16;
-    for (int tile = wv; tile < NRB * NJB; tile += NW) {
-        const int rb = tile / NJB, jb = tile % NJB;
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (sizeof(TI) == 2) {
+        // bf16 inputs: U~ in the accumulator layout of the serial pass
+        // (gdn_fwd_impl.hpp), tiles D[r][j] = sum_s T[r][s] (beta V)[s][j]: lane
+        // (g, n) holds rows r = rb*16 + 4g + e of column j = jb*16 + n, stored as
+        // [bh][chunk][jb][rb][lane][4] so that the serial pass loads 8 bytes per
+        // lane per row block.
+        TM *uout = (TM *)a.ut + ((size_t)bh * a.nchunks + c) * NJB * (NRB * 256);
+        for (int tile = wv; tile < NRB * NJB; tile += NW) {
+            const int rb = tile / NJB, jb = tile % NJB;
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NTK; ++ks) {
-            const int s0 = g * (C / 4) + ks * E;
-            d = MF::mma(ld_frag<TM>(&VTs[tidx<C, TM>(jb * 16 + n, s0)]),
-                        ld_frag<TM>(&To[(rb * 16 + n) * OP + s0]), d);
+            for (int ks = 0; ks < NTK; ++ks) {
+                const int s0 = g * (C / 4) + ks * E;
+                d = MF::mma(ld_frag<TM>(&To[(rb * 16 + n) * OP + s0]),
+                            ld_frag<TM>(&VTs[tidx<C, TM>(jb * 16 + n, s0)]), d);
+            }
+            st4<TM>(uout + (size_t)(jb * NRB + rb) * 256 + lane * 4, d);
         }
-        st4<TM>(uout + (size_t)(rb * 16 + n) * dv + jb * 16 + 4 * g, d);
+    } else {
+        // U~ row-major, from transposed tiles D[j][r] = sum_s (beta V)[s][j] T[r][s];
+        // lane holds r = rb*16 + n and four consecutive columns j = jb*16 + 4g + e.
+        TM *uout = (TM *)a.ut + ((size_t)bh * a.Lp + t0) * dv;
+        for (int tile = wv; tile < NRB * NJB; tile += NW) {
+            const int rb = tile / NJB, jb = tile % NJB;
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NTK; ++ks) {
+                const int s0 = g * (C / 4) + ks * E;
+                d = MF::mma(ld_frag<TM>(&VTs[tidx<C, TM>(jb * 16 + n, s0)]),
+                            ld_frag<TM>(&To[(rb * 16 + n) * OP + s0]), d);
+            }
+            st4<TM>(uout + (size_t)(rb * 16 + n) * dv + jb * 16 + 4 * g, d);
+        }
     }
 }
 

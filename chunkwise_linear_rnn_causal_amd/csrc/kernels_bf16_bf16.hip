@@ -17,8 +17,6 @@ template hipError_t launch_chunk<V_NORM, bf16, bf16, 32, 32, 128, 4>(const Chunk
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 32, 32, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 32, 64, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 32, 32, 128, 4>(const ChunkArgs &, hipStream_t);
-template hipError_t launch_chunk<V_GDN, bf16, bf16, 32, 32, 64, 8>(const ChunkArgs &, hipStream_t);
-template hipError_t launch_chunk<V_GDN, bf16, bf16, 32, 16, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 64, 32, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 64, 64, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 64, 32, 128, 4>(const ChunkArgs &, hipStream_t);
@@ -28,8 +26,6 @@ template hipError_t launch_chunk<V_NORM, bf16, bf16, 64, 32, 128, 4>(const Chunk
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 64, 32, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 64, 64, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 64, 32, 128, 4>(const ChunkArgs &, hipStream_t);
-template hipError_t launch_chunk<V_GDN, bf16, bf16, 64, 32, 64, 8>(const ChunkArgs &, hipStream_t);
-template hipError_t launch_chunk<V_GDN, bf16, bf16, 64, 16, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 128, 32, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 128, 64, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_PLAIN, bf16, bf16, 128, 32, 128, 4>(const ChunkArgs &, hipStream_t);
@@ -39,8 +35,6 @@ template hipError_t launch_chunk<V_NORM, bf16, bf16, 128, 32, 128, 4>(const Chun
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 128, 32, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 128, 64, 64, 8>(const ChunkArgs &, hipStream_t);
 template hipError_t launch_chunk<V_DECAY, bf16, bf16, 128, 32, 128, 4>(const ChunkArgs &, hipStream_t);
-template hipError_t launch_chunk<V_GDN, bf16, bf16, 128, 32, 64, 8>(const ChunkArgs &, hipStream_t);
-template hipError_t launch_chunk<V_GDN, bf16, bf16, 128, 16, 64, 8>(const ChunkArgs &, hipStream_t);
 
 // decode step: (variant, d_k, d_v)
 template hipError_t launch_decode<V_PLAIN, bf16, bf16, 32, 32>(const DecodeArgs &, hipStream_t);

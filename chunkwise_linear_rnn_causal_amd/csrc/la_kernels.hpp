@@ -82,6 +82,11 @@ hipError_t launch_chunk(const ChunkArgs &a, hipStream_t st);
 template <typename TI, int DK, int C>
 hipError_t launch_gdn_prep(const PrepArgs &a, hipStream_t st);
 
+// Serial chunk pass of the gated delta rule for bf16 inputs (C = 64, 16-column
+// value slices: a.nsplit = dv / 16), after launch_gdn_prep.
+template <typename TO, int DK>
+hipError_t launch_gdn_fwd(const ChunkArgs &a, hipStream_t st);
+
 // Chunk forward with one decay gate per key channel (C = 64, 32-column slices).
 template <typename TI, typename TO, int DK>
 hipError_t launch_vdecay(const ChunkArgs &a, hipStream_t st);
