@@ -247,7 +247,8 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     constexpr int NSLOT = Geo::NSLOT;
     constexpr int GW = R::GW;             // wave that builds the gate tables
     constexpr int WS0 = R::WS0, NWS = R::NWS;
-    constexpr auto TS = make_tile_split<NTI * NTJ, NW, NRB, R::MODE == 3>(VAR == V_NORM ? NTI : 0, DECAYED ? 2 : 0);
+    // the gate tables weigh about six state tiles (measured per role with cycle counters)
+    constexpr auto TS = make_tile_split<NTI * NTJ, NW, NRB, R::MODE == 3>(VAR == V_NORM ? NTI : 0, DECAYED ? 6 : 0);
     constexpr int NTS = TS.maxcnt;        // state tiles per wave (at most)
     static_assert(NTJW >= 1, "value slice narrower than one tile");
     static_assert(VAR != V_GDN || ((R::MODE == 0 || R::MODE == 3) && NRB == 4),
@@ -654,12 +655,18 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
     // X[OS + j*KP + i].
     auto write_sts = [&](auto w_tag, TM *X, int sh) __attribute__((always_inline)) {
         constexpr int W = decltype(w_tag)::value;
-        const float sc = SCALE ? pow2i(-sh) : 1.f;
+        auto put = [&](auto scaled) __attribute__((always_inline)) {
+            const float sc = decltype(scaled)::value ? pow2i(-sh) : 1.f;
 #pragma unroll
-        for (int m = 0; m < TS.cnt[W]; ++m) {
-            const int tile = TS.start[W] + m, ti = tile / NTJ, tj = tile % NTJ;
-            st4<TM>(&X[Cfg::OS + (tj * 16 + n) * KP + ti * 16 + 4 * g], SCALE ? Sacc[m] * sc : Sacc[m]);
-        }
+            for (int m = 0; m < TS.cnt[W]; ++m) {
+                const int tile = TS.start[W] + m, ti = tile / NTJ, tj = tile % NTJ;
+                st4<TM>(&X[Cfg::OS + (tj * 16 + n) * KP + ti * 16 + 4 * g],
+                        decltype(scaled)::value ? Sacc[m] * sc : Sacc[m]);
+            }
+        };
+        // the shift is wave-uniform and usually zero: skip the multiplies then
+        if (SCALE && sh != 0) put(std::true_type{});
+        else put(std::false_type{});
     };
     // max |S| over wave W's state tiles (the state before chunk j) into slot j % 3.
     auto put_smax = [&](auto w_tag, int j) __attribute__((always_inline)) {
