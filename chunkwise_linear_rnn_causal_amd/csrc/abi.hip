@@ -102,11 +102,22 @@ size_t gdn_w_bytes(la_dtype dt, int64_t BH, int64_t Lp, int d_k) {
     return round_up((size_t)BH * Lp * d_k * elem_size(dt), 256);
 }
 
+// U~ bytes, rounded up to 256 like W (the score fragments follow it).
+size_t gdn_ut_bytes(la_dtype dt, int64_t BH, int64_t Lp, int d_v) {
+    return round_up((size_t)BH * Lp * d_v * elem_size(dt), 256);
+}
+
+// Score fragments of the bf16 serial pass: 6 fragments of 64 lanes x 8 fp16
+// per 64-token chunk, i.e. 96 bytes per token.
+size_t gdn_mf_bytes(la_dtype dt, int64_t BH, int64_t Lp) {
+    return dt == LA_BF16 ? (size_t)BH * Lp * 96 : 0;
+}
+
 size_t chunk_workspace(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v, int C) {
     if (var != LA_GATED_DELTA || L == 0) return 0;
     C = kernel_chunk(var, dt, d_k, C);
     const int64_t BH = (int64_t)B * H, Lp = (int64_t)((L + C - 1) / C) * C;
-    return gdn_w_bytes(dt, BH, Lp, d_k) + (size_t)BH * Lp * d_v * elem_size(dt);
+    return gdn_w_bytes(dt, BH, Lp, d_k) + gdn_ut_bytes(dt, BH, Lp, d_v) + gdn_mf_bytes(dt, BH, Lp);
 }
 
 // Workgroup geometry of the chunk kernel: value columns per workgroup (DVT) and
@@ -387,9 +398,10 @@ la_status run_fwd(const FwdCall &f, int p0, int n, const float *s_in, float *s_o
         char *w = static_cast<char *>(ws);
         a.w = w;
         a.ut = w + gdn_w_bytes(dt, BH, Lp, d_k);
+        a.mf = dt == LA_BF16 ? w + gdn_w_bytes(dt, BH, Lp, d_k) + gdn_ut_bytes(dt, BH, Lp, d_v) : nullptr;
         PrepArgs p{};
-        p.k = a.k; p.v = a.v; p.lg = a.lg; p.beta = static_cast<const float *>(adv(f.beta, 4));
-        p.w = const_cast<void *>(a.w); p.ut = const_cast<void *>(a.ut);
+        p.q = a.q; p.k = a.k; p.v = a.v; p.lg = a.lg; p.beta = static_cast<const float *>(adv(f.beta, 4));
+        p.w = const_cast<void *>(a.w); p.ut = const_cast<void *>(a.ut); p.mf = const_cast<void *>(a.mf);
         p.BH = (int)BH; p.L = n; p.Lp = Lp; p.dv = d_v; p.nchunks = nchunks; p.ld = f.L;
         const hipError_t e = (dt == LA_BF16) ? dispatch_prep<bf16>(d_k, p, st)
                                              : dispatch_prep<float>(d_k, p, st);
@@ -448,7 +460,7 @@ PiecePlan plan_pieces(const FwdCall &f) {
     if (whole <= kScratchBytes) return PiecePlan{f.L > 0 ? f.L : 1, whole};
     const int64_t BH = (int64_t)f.B * f.H;
     const size_t carry = f.state_out ? 0 : round_up((size_t)BH * f.d_k * f.d_v * 4, 256);
-    const size_t per_row = (size_t)BH * (f.d_k + f.d_v) * elem_size(f.dt);
+    const size_t per_row = (size_t)BH * ((f.d_k + f.d_v) * elem_size(f.dt) + (f.dt == LA_BF16 ? 96 : 0));
     const int kc = kernel_chunk(f.var, f.dt, f.d_k, f.C);
     if (carry >= kScratchBytes) return PiecePlan{0, 0};
     int64_t rows = (int64_t)((kScratchBytes - carry) / per_row) / kc * kc;

@@ -3,8 +3,9 @@
 // Method (wln20 "LLM注意力优化：线性注意力", Gated DeltaNet section; tensorplay
 // "Talk Linear Attention", section 6.2, WY / UT chunk form). For chunk c with
 // chunk-local cumulative log-gate G_r, a_r = exp(G_r), Gamma_rs = exp(G_r - G_s)
-// and the per-chunk products W = T diag(beta a) K, U~ = T diag(beta) V of the
-// chunk-parallel preparation (gdn_prep_impl.hpp):
+// and the per-chunk products of the chunk-parallel preparation
+// (gdn_prep_impl.hpp): W = T diag(beta a) K, U~ = T diag(beta) V and the masked
+// decayed scores Gamma (.) Q K^T (.) M:
 //   U      = U~ - W S                      (the serial correction)
 //   O      = diag(a) Q S + (Gamma (.) Q K^T (.) M) U
 //   S_next = a_C S + K^T diag(a_C / a) U
@@ -24,17 +25,22 @@
 //    passes through LDS and has no barrier inside a chunk. It also owns the
 //    whole slice of S, so the fp16 operand scale (a power of two keeping the
 //    carried state inside fp16's range) comes from an exact wave maximum.
-//  - waves 1-3 stage Q, K and W of chunk c+1 into the other half of
+//  - waves 1-3 stage K and W of chunk c+1 into the other half of
 //    double-buffered LDS tiles (loads issued two chunks ahead) and build the
 //    gate tables.
-//  - waves 4-7, one per 16-row block, form the outputs: the inter term and the
-//    masked decayed scores of chunk c in iteration c, and the intra term
-//    (scores times U) of chunk c in iteration c+1, when the chain wave has
-//    left U's fragments in LDS; the fragment of S^T they need is the chain
-//    wave's B operand of S, written once per chunk.
-// One barrier per chunk. Operand K slots of Q, K and W rows follow the channel
-// order {32p + 4g + e, 32p + 16 + 4g + e} of S's fragments: two 8-byte LDS
-// reads per fragment.
+//  - waves 4-7, one per 16-row block, form the outputs: the inter term of
+//    chunk c in iteration c, and the intra term (scores times U) of chunk c in
+//    iteration c+1, when the chain wave has left U's fragments in LDS; the
+//    fragment of S^T they need is the chain wave's B operand of S, written
+//    once per chunk. Their query rows and score fragments come straight from
+//    global memory into registers (two chunks ahead), so the only LDS reads of
+//    these waves are S^T and U.
+// One barrier per chunk. Operand K slots of Q and W rows follow the channel
+// order {32p + 4g + e, 32p + 16 + 4g + e} of S's fragments (two 8-byte pieces
+// per fragment). The per-workgroup LDS traffic is what bounds the chunk period
+// (the serial chain's own MFMA work is 32 instructions per chunk), which is why
+// the scores, identical in every value slice of a head, are formed once by the
+// preparation instead of here.
 #pragma once
 
 #include <type_traits>
@@ -51,15 +57,16 @@ template <int DK> struct GdnCfg {
     static constexpr int NTI = DK / 16; // 16-channel tiles of the state slice
     static constexpr int NKS = DK / 32; // k-steps over channels
     static constexpr int NRB = C / 16;  // 16-row blocks
-    static constexpr int QP = DK + 8;   // row pitch of the Q and W tiles (fp16 elements)
+    static constexpr int WP = DK + 8;   // row pitch of the W tile (fp16 elements)
     static constexpr int KP = DK + 16;  // row pitch of the K tile (also read transposed)
-    static constexpr int OQ = 0, OK = OQ + C * QP, OW = OK + C * KP, SET = OW + C * QP;
+    static constexpr int OK = 0, OW = OK + C * KP, SET = OW + C * WP;
     // staging: wave loads of 1 KB (64 lanes x 16 bytes) per tensor and chunk
     static constexpr int SEG = DK / 8;            // 16-byte segments per row
     static constexpr int RPL = 64 / SEG;          // rows per wave load
     static constexpr int NI1 = C / RPL;           // wave loads per tensor
     static constexpr int NSW = 3;                 // staging waves
-    static constexpr int NSL = NI1;               // slots per staging wave (3 tensors / 3 waves)
+    static constexpr int NLD = 2 * NI1;           // wave loads per chunk (K and W)
+    static constexpr int NSL = (NLD + NSW - 1) / NSW;  // slots per staging wave
     static_assert(64 % SEG == 0 && NI1 * RPL == C, "staging geometry");
 };
 
@@ -74,25 +81,17 @@ __device__ inline f16x8 chan_frag(const f16 *X, int row, int p, int g) {
     return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// fp16 fragment from two accumulator tiles (tile lo in slots 0..3, hi in 4..7),
-// each element scaled by f.
-__device__ inline f16x8 pack_tiles(const f32x4 &lo, const f32x4 &hi, float f) {
-    return f16x8{(f16)(lo[0] * f), (f16)(lo[1] * f), (f16)(lo[2] * f), (f16)(lo[3] * f),
-                 (f16)(hi[0] * f), (f16)(hi[1] * f), (f16)(hi[2] * f), (f16)(hi[3] * f)};
-}
-
 template <typename TO, int DK>
 __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
     using Cfg = GdnCfg<DK>;
     using MF = Mfma<f16>;
     constexpr int C = Cfg::C, NTI = Cfg::NTI, NKS = Cfg::NKS, NRB = Cfg::NRB;
-    constexpr int QP = Cfg::QP, KP = Cfg::KP, SET = Cfg::SET;
+    constexpr int WP = Cfg::WP, KP = Cfg::KP, SET = Cfg::SET;
     constexpr int NSL = Cfg::NSL, SEG = Cfg::SEG, RPL = Cfg::RPL, NI1 = Cfg::NI1;
 
     __shared__ __attribute__((aligned(16))) f16 Tiles[2 * SET];
-    // gate tables per buffer: [0] G_s, [1] exp(G_s), [2] exp(g_C - G_s),
-    // [3] exp(G_{end of s's 16-block} - G_s); Tsc: exp(g_C)
-    __shared__ __attribute__((aligned(16))) float Tg[2 * 4 * C];
+    // gate tables per buffer: [0] exp(G_s), [1] exp(g_C - G_s); Tsc: exp(g_C)
+    __shared__ __attribute__((aligned(16))) float Tg[2 * 2 * C];
     __shared__ float Tsc[2];
     // chain -> output waves: S^T fragments of the state before chunk c (buffer
     // c & 1) with their shift, and U fragments of chunk c (buffer c & 1)
@@ -109,6 +108,7 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
     const int nchunks = (L + C - 1) / C;
 
     const bf16 *qg = (const bf16 *)a.q + (size_t)bh * a.ld * DK;
+    const f16 *mg = (const f16 *)a.mf + (size_t)bh * nchunks * (6 * 512);
     const bf16 *kg = (const bf16 *)a.k + (size_t)bh * a.ld * DK;
     const float *lgg = a.lg ? a.lg + (size_t)bh * a.ld : nullptr;
     const f16 *wg = (const f16 *)a.w + (size_t)bh * a.Lp * DK;
@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
         auto iter = [&](int c, auto par) __attribute__((always_inline)) {
             constexpr int P = decltype(par)::value;
             const f16 *X = Tiles + P * SET;
-            const float *T = Tg + P * 4 * C;
+            const float *T = Tg + P * 2 * C;
             const f16 *Ks = X + Cfg::OK, *Ws = X + Cfg::OW;
             // Every LDS operand of the chunk's chain is read up front (W for U, K^T
             // and the state-update weights), so the reads overlap each other and the
@@ -196,12 +196,12 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-                for (int p = 0; p < NKS; ++p) wf[rb][p] = chan_frag<QP>(Ws, rb * 16 + n, p, g);
+                for (int p = 0; p < NKS; ++p) wf[rb][p] = chan_frag<WP>(Ws, rb * 16 + n, p, g);
             f32x4 wlo[2], whi[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
-                wlo[q] = *reinterpret_cast<const f32x4 *>(&T[2 * C + 32 * q + 4 * g]);
-                whi[q] = *reinterpret_cast<const f32x4 *>(&T[2 * C + 32 * q + 16 + 4 * g]);
+                wlo[q] = *reinterpret_cast<const f32x4 *>(&T[C + 32 * q + 4 * g]);
+                whi[q] = *reinterpret_cast<const f32x4 *>(&T[C + 32 * q + 16 + 4 * g]);
             }
             const float eg = Tsc[P];
             __builtin_amdgcn_sched_barrier(0);
@@ -272,35 +272,36 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
         constexpr int sw = decltype(sw_tag)::value;
         uint4 pre[2][NSL];
         float gpre[2];
+        const float *gsrc = lgg ? lgg : reinterpret_cast<const float *>(kg);  // kg: at least L floats
         constexpr bool gate_wave = sw == 0;
-        // slot m of this wave: wave load i = sw + 3 m; tensor i / NI1 (0 Q, 1 K, 2 W)
+        // slot m of this wave: wave load i = sw + 3 m (the last wave load again past
+        // the end, so every staging wave has the same loads in flight); tensor
+        // i / NI1 (0 K, 1 W)
+        auto slot = [](int m) { return min(sw + Cfg::NSW * m, Cfg::NLD - 1); };
         auto load_chunk = [&](int c, int set) __attribute__((always_inline)) {
 #pragma unroll
             for (int m = 0; m < NSL; ++m) {
-                const int i = sw + 3 * m, kind = i / NI1, ii = i % NI1;  // compile-time after unrolling
+                const int i = slot(m), kind = i / NI1, ii = i % NI1;  // compile-time after unrolling
                 const int row = ii * RPL + lane / SEG, seg = lane % SEG;
                 const int t = c * C + row;
-                if (kind == 2) {
+                if (kind == 1)
                     pre[set][m] = *reinterpret_cast<const uint4 *>(wg + (size_t)t * DK + seg * 8);
-                } else {
-                    const bf16 *src = kind == 0 ? qg : kg;
-                    pre[set][m] = *reinterpret_cast<const uint4 *>(src + (size_t)min(t, L - 1) * DK + seg * 8);
-                }
+                else
+                    pre[set][m] = *reinterpret_cast<const uint4 *>(kg + (size_t)min(t, L - 1) * DK + seg * 8);
             }
-            if (gate_wave) {
-                const int t = c * C + lane;
-                gpre[set] = (lgg && t < L) ? lgg[t] : 0.f;
-            }
+            // unconditional as well, from a valid address when there is no gate; the
+            // value is masked where it is used (masking it here would wait for it here)
+            if (gate_wave) gpre[set] = gsrc[min(c * C + lane, L - 1)];
         };
         auto stage_chunk = [&](int c, int set, int buf) __attribute__((always_inline)) {
             f16 *X = Tiles + buf * SET;
 #pragma unroll
             for (int m = 0; m < NSL; ++m) {
-                const int i = sw + 3 * m, kind = i / NI1, ii = i % NI1;
+                const int i = slot(m), kind = i / NI1, ii = i % NI1;
                 const int row = ii * RPL + lane / SEG, seg = lane % SEG;
                 const uint4 w4 = pre[set][m];
-                if (kind == 2) {
-                    *reinterpret_cast<uint4 *>(&X[Cfg::OW + row * QP + seg * 8]) = w4;
+                if (kind == 1) {
+                    *reinterpret_cast<uint4 *>(&X[Cfg::OW + row * WP + seg * 8]) = w4;
                 } else {
                     // bf16 -> fp16 with the packed round-toward-zero conversion: every
                     // bf16 value in fp16's normal range converts exactly
@@ -311,44 +312,57 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
                         hw[k] = valid ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(u[k]), bf16_hi(u[k]))) : 0u;
-                    *reinterpret_cast<uint4 *>(&X[(kind == 0 ? Cfg::OQ + row * QP : Cfg::OK + row * KP) + seg * 8]) = h;
+                    *reinterpret_cast<uint4 *>(&X[Cfg::OK + row * KP + seg * 8]) = h;
                 }
             }
             if (gate_wave) {
                 // chunk-local inclusive prefix of the log-gates (rows past L: 0)
-                float *T = Tg + buf * 4 * C;
-                const float G = wave_inclusive_sum(gpre[set]);
+                float *T = Tg + buf * 2 * C;
+                const float G = wave_inclusive_sum((lgg && c * C + lane < L) ? gpre[set] : 0.f);
                 const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
-                const float e0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 15));
-                const float e1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 31));
-                const float e2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 47));
-                const float Ge = (lane < 16) ? e0 : (lane < 32) ? e1 : (lane < 48) ? e2 : gC;
-                T[lane] = G;
-                T[C + lane] = __expf(G);
-                T[2 * C + lane] = __expf(gC - G);
-                T[3 * C + lane] = __expf(Ge - G);
+                T[lane] = __expf(G);
+                T[C + lane] = __expf(gC - G);
                 if (lane == 0) Tsc[buf] = __expf(gC);
             }
         };
         // Loads are issued unconditionally (chunk indices past the end repeat the
         // last chunk), so every path leaves the same loads in flight and the wait
         // before each staged slot is exact: two chunks of loads stay in flight.
+        // (the fences keep the prologue's loads in this order, the one the loop
+        // assumes on entry: chunk 1 older than chunk 2)
         if (nchunks > 0) {
             load_chunk(0, 0);
             load_chunk(min(1, nchunks - 1), 1);
+            __builtin_amdgcn_sched_barrier(0);
             stage_chunk(0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
             load_chunk(min(2, nchunks - 1), 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();  // prologue
         // iteration c: stage chunk c+1 (register set (c+1) & 1) into buffer (c+1) & 1,
-        // then load chunk c+3 into that register set
+        // then load chunk c+3 into that register set. In the last iteration the
+        // staged chunk is a repeat of the last one, in the buffer no wave reads
+        // any more: staging stays unconditional, which keeps the wait counts exact.
         auto iter = [&](int c, auto par) __attribute__((always_inline)) {
             constexpr int P = decltype(par)::value;  // c & 1
-            if (c + 1 < nchunks) stage_chunk(c + 1, P ^ 1, P ^ 1);
+            stage_chunk(c + 1, P ^ 1, P ^ 1);
             load_chunk(min(c + 3, nchunks - 1), P ^ 1);
+            // no instruction crosses the barrier: a conversion hoisted above it
+            // would need the next register set a chunk early (a full wait)
+            __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
         };
+        // The first two iterations are peeled: the loop is then entered with its
+        // register sets in flight in the same order as at its back edge, which the
+        // compiler needs to keep the waits at one set (not every load) per chunk.
         int c = 0;
+        if (nchunks >= 2) {
+            iter(0, std::integral_constant<int, 0>{});
+            iter(1, std::integral_constant<int, 1>{});
+            c = 2;
+        }
         for (; c + 1 < nchunks; c += 2) {
             iter(c, std::integral_constant<int, 0>{});
             iter(c + 1, std::integral_constant<int, 1>{});
@@ -363,75 +377,75 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
         // ================= output waves: row block rb (a compile-time constant) =================
         auto out_role = [&](auto rb_tag) __attribute__((always_inline)) {
         constexpr int rb = decltype(rb_tag)::value;
+        constexpr int NP = rb / 2 + 1;                  // score fragments (rb, p), 2p <= rb
+        constexpr int F0 = rb + (rb > 2 ? rb - 2 : 0);  // index of fragment (rb, 0)
         const int r = rb * 16 + n;  // this lane's query row within the chunk
+        // Query row r in S's channel order (channels 32p + 4g .. + 3 and
+        // 32p + 16 + 4g .. + 3, raw bf16) and the score fragments, two register
+        // sets loaded two chunks ahead; chunk indices past the end repeat the
+        // last chunk, so every iteration leaves the same loads in flight.
+        uint2 qraw[2][NKS][2];
+        uint4 mraw[2][NP];
+        auto load = [&](int c, int set) __attribute__((always_inline)) {
+            const bf16 *qrow = qg + (size_t)min(c * C + r, L - 1) * DK + 4 * g;
+#pragma unroll
+            for (int p = 0; p < NKS; ++p) {
+                qraw[set][p][0] = *reinterpret_cast<const uint2 *>(qrow + 32 * p);
+                qraw[set][p][1] = *reinterpret_cast<const uint2 *>(qrow + 32 * p + 16);
+            }
+            const f16 *mrow = mg + (size_t)c * (6 * 512) + F0 * 512 + lane * 8;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) mraw[set][p] = *reinterpret_cast<const uint4 *>(mrow + p * 512);
+        };
         f32x4 oprev = {0.f, 0.f, 0.f, 0.f};
-        f16x8 bprev[2];
+        f16x8 bprev[NP];
         int shprev = 0;
         // intra term of the previous chunk from U's fragments, then its store
         auto finish_prev = [&](int cp, const f16x8 (&uf)[2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                if (2 * p <= rb) oprev = MF::mma(uf[p], bprev[p], oprev);
-            }
+            for (int p = 0; p < NP; ++p) oprev = MF::mma(uf[p], bprev[p], oprev);
             oprev *= pow2i(shprev);
             const int t = cp * C + r;
             if (t < L) st4<TO>(og + (size_t)t * dv + 4 * g, oprev);
         };
+        if (nchunks > 0) {
+            load(0, 0);
+            load(min(1, nchunks - 1), 1);
+        }
         __syncthreads();  // prologue
         auto iter = [&](int c, auto par) __attribute__((always_inline)) {
             constexpr int P = decltype(par)::value;
-            const f16 *X = Tiles + P * SET;
-            const float *T = Tg + P * 4 * C;
-            const f16 *Qs = X + Cfg::OQ, *Ks = X + Cfg::OK;
-            // every LDS operand first (queries, S^T, the key blocks of the scores)
-            f16x8 qf[NKS], sf[NKS], kf[rb + 1][NKS];
+            const float *T = Tg + P * 2 * C;
+            // this chunk's operands: queries converted to fp16 (round toward zero:
+            // exact for every bf16 value in fp16's normal range), score fragments,
+            // then S^T and U from LDS
+            f16x8 qf[NKS], mf[NP], sf[NKS], uf[2];
 #pragma unroll
             for (int p = 0; p < NKS; ++p) {
-                qf[p] = chan_frag<QP>(Qs, r, p, g);
-                sf[p] = Sf[P][p][lane];
+                const uint32_t u[4] = {qraw[P][p][0].x, qraw[P][p][0].y, qraw[P][p][1].x, qraw[P][p][1].y};
+                uint32_t h[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    h[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(u[k]), bf16_hi(u[k])));
+                qf[p] = __builtin_bit_cast(f16x8, make_uint4(h[0], h[1], h[2], h[3]));
             }
 #pragma unroll
-            for (int sb = 0; sb <= rb; ++sb)
+            for (int p = 0; p < NP; ++p) mf[p] = __builtin_bit_cast(f16x8, mraw[P][p]);
+            load(min(c + 2, nchunks - 1), P);
 #pragma unroll
-                for (int p = 0; p < NKS; ++p) kf[sb][p] = chan_frag<KP>(Ks, sb * 16 + n, p, g);
-            const int sh = Ssh[P];
-            const float Gr = T[r], er = -T[C + r];  // -: the fragments hold -S^T
-            f16x8 uf[2];
+            for (int p = 0; p < NKS; ++p) sf[p] = Sf[P][p][lane];
 #pragma unroll
             for (int p = 0; p < 2; ++p) uf[p] = Uf[P ^ 1][p][lane];
-            __builtin_amdgcn_sched_barrier(0);
+            const int sh = Ssh[P];
+            const float er = -T[r];  // -: the fragments hold -S^T
             if (c > 0) finish_prev(c - 1, uf);
             // inter term: O^T = S^T (a Q)^T at scale 2^-sh
             f32x4 oacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int p = 0; p < NKS; ++p) oacc = MF::mma(sf[p], qf[p], oacc);
-            oacc *= er;
-            // scores D[s][r] = k_s . q_r for key blocks sb <= rb, masked and decayed;
-            // off the diagonal exp(G_r - G_s) = exp(G_r - G_e) exp(G_e - G_s), e the
-            // last token of block sb (both factors <= 1)
-            f32x4 sc[NRB];
+            oprev = oacc * er;
 #pragma unroll
-            for (int sb = 0; sb < NRB; ++sb) {
-                sc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (sb <= rb) {
-#pragma unroll
-                    for (int p = 0; p < NKS; ++p) sc[sb] = MF::mma(kf[sb][p], qf[p], sc[sb]);
-                    if (sb == rb) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int sl = sb * 16 + 4 * g + e;
-                            sc[sb][e] = (sl > r) ? 0.f : sc[sb][e] * __expf(Gr - T[sl]);
-                        }
-                    } else {
-                        const float fr = __expf(Gr - T[sb * 16 + 15]);
-                        const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&T[3 * C + sb * 16 + 4 * g]);
-                        sc[sb] *= fr * b4;
-                    }
-                }
-            }
-#pragma unroll
-            for (int p = 0; p < 2; ++p) bprev[p] = pack_tiles(sc[2 * p], sc[2 * p + 1], 1.f);
-            oprev = oacc;
+            for (int p = 0; p < NP; ++p) bprev[p] = mf[p];
             shprev = sh;
             __syncthreads();
         };

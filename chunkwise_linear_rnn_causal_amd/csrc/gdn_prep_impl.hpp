@@ -21,6 +21,16 @@
 // columns per lane), and for bf16 inputs in the accumulator layout of the
 // serial pass (see the store below). Padded tokens (t >= L) have beta = 0 and
 // k = v = 0, which makes their rows of W and U~ zero.
+//
+// For bf16 inputs the kernel also forms the chunk's masked decayed scores,
+// M_rs = exp(G_r - G_s) (q_r . k_s) for s <= r and 0 above the diagonal, which
+// the serial pass needs in every value slice of a head: here they are formed
+// once per chunk. They come out of the same 16 x 16 tile loop as P (a tile of
+// M^T and the matching tile of P share the key fragment) and are stored as the
+// serial pass's MFMA operand fragments, [BH][chunk][6][64 lanes][8] fp16:
+// fragment (rb, p) holds, for lane (g, n), the scores of query row 16 rb + n
+// against keys {32p + 4g + e, 32p + 16 + 4g + e} (e = 0..3), for the six pairs
+// (rb, p) with 2p <= rb (fragment index rb + max(rb - 2, 0) + p).
 #pragma once
 
 #include "la_common.hpp"
@@ -55,7 +65,7 @@ struct PrepCfg {
 };
 
 template <typename TI, int DK, int C>
-__global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
+__global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
     using TM = typename OpOf<TI>::type;
     using MF = Mfma<TM>;
     using frag = typename MF::frag;
@@ -104,19 +114,36 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
     const int gi = tid >> 4, l16 = tid & 15;
     const int ktq = (gi / KNCBG) * KTQL + (l16 % KTQL), kcb = (gi % KNCBG) * KCBL + (l16 / KTQL);
     const int vtq = (gi / VNCBG) * VTQL + (l16 % VTQL), vcb = (gi % VNCBG) * VCBL + (l16 / VTQL);
-    float kx[4][8], vx[4][8];
+    // Score jobs of this wave (bf16 inputs): fragment (wv, 0), and on even waves
+    // (3, 1) or (2, 1); their query rows are loaded here with the rest.
+    const bool job1 = (wv & 1) == 0;
+    const int jrb1 = wv == 0 ? 3 : 2;
+    uint4 qx[2][NKS];
+    if constexpr (sizeof(TI) == 2) {
+        const TI *qg = (const TI *)a.q + (size_t)bh * a.ld * DK;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (j == 1 && !job1) break;
+            const int t = t0 + (j ? jrb1 : wv) * 16 + n;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                qx[j][ks] = *reinterpret_cast<const uint4 *>(qg + (size_t)(t < L ? t : L - 1) * DK + g * (DK / 4) + ks * E);
+        }
+    }
+    // K and V stay in their storage format until they are staged (fewer registers)
+    Raw8<TI> kr[4], vr[4];
     if (tid < KUNITS) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = t0 + 4 * ktq + r;
-            ld8<TI>(kg + (size_t)(t < L ? t : L - 1) * DK + 8 * kcb, kx[r]);
+            kr[r] = ld_raw8<TI>(kg + (size_t)(t < L ? t : L - 1) * DK + 8 * kcb);
         }
     }
     if (tid < VUNITS) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = t0 + 4 * vtq + r;
-            ld8<TI>(vg + (size_t)(t < L ? t : L - 1) * dv + 8 * vcb, vx[r]);
+            vr[r] = ld_raw8<TI>(vg + (size_t)(t < L ? t : L - 1) * dv + 8 * vcb);
         }
     }
 
@@ -139,29 +166,84 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
             const int s = 4 * ktq + r;
             if (t0 + s >= L) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) kx[r][e] = 0.f;
+                for (int i = 0; i < (int)(sizeof(TI) / 2); ++i) kr[r].v[i] = make_uint4(0u, 0u, 0u, 0u);
             }
-            st8<TM>(&Ks[s * KP + 8 * kcb], kx[r]);
+            float kx[8];
+            unpack8<TI>(kr[r], kx);
+            st8<TM>(&Ks[s * KP + 8 * kcb], kx);
         }
     }
     __syncthreads();
 
-    // P = strict_lower(diag(beta) (Gamma (.) K K^T)) from 16x16 tiles rb >= sb.
-    // D[r][s]: lane (g, n) holds r = rb*16 + 4g + e, s = sb*16 + n.
-    for (int tile = wv; tile < NRB * (NRB + 1) / 2; tile += NW) {
-        int rb = 0, rem = tile;
-        while (rem > rb) { rem -= rb + 1; ++rb; }
-        const int sb = rem;
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    // P = strict_lower(diag(beta) (Gamma (.) K K^T)) from the 16x16 tiles rb >= sb,
+    // taken as score jobs (rb, p): the tiles (rb, 2p) and (rb, 2p + 1) that lie on
+    // or below the diagonal. Wave 0 takes (0, 0) and (3, 1), wave 1 (1, 0), wave 2
+    // (2, 0) and (2, 1), wave 3 (3, 0): three, two, three and two tiles.
+    // P tile D[r][s]: lane (g, n) holds r = rb*16 + 4g + e, s = sb*16 + n.
+    // Score tile (bf16) D[s][r] = k_s . q_r: s = sb*16 + 4g + e, r = rb*16 + n; off
+    // the diagonal block exp(G_r - G_s) = exp(G_r - G_e) exp(G_e - G_s), e the last
+    // token of block sb (both factors <= 1).
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            d = MF::mma(ld_frag<TM>(&Ks[(rb * 16 + n) * KP + g * (DK / 4) + ks * E]),
-                        ld_frag<TM>(&Ks[(sb * 16 + n) * KP + g * (DK / 4) + ks * E]), d);
-        const int s = sb * 16 + n;
+    for (int j = 0; j < 2; ++j) {
+        if (j == 1 && !job1) break;
+        const int rb = j ? jrb1 : wv, p = j;
+        typename MF::frag qf[NKS];
+        if constexpr (sizeof(TI) == 2) {
+            // bf16 -> fp16 with the packed round-toward-zero conversion (exact for
+            // every bf16 value in fp16's normal range); rows past L are zero
+            const bool valid = t0 + rb * 16 + n < L;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = rb * 16 + 4 * g + e;
-            Pm[r * TP + s] = (s < r) ? Bs[r] * __expf(Gs[r] - Gs[s]) * d[e] : 0.f;
+            for (int ks = 0; ks < NKS; ++ks) {
+                const uint32_t u[4] = {qx[j][ks].x, qx[j][ks].y, qx[j][ks].z, qx[j][ks].w};
+                uint32_t h[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    h[i] = valid ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(u[i]), bf16_hi(u[i]))) : 0u;
+                qf[ks] = __builtin_bit_cast(f16x8, make_uint4(h[0], h[1], h[2], h[3]));
+            }
+        }
+        f32x4 ms[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const int sb = 2 * p + hb;
+            ms[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (sb > rb) continue;
+            f32x4 d = {0.f, 0.f, 0.f, 0.f}, e4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const typename MF::frag kb = ld_frag<TM>(&Ks[(sb * 16 + n) * KP + g * (DK / 4) + ks * E]);
+                d = MF::mma(ld_frag<TM>(&Ks[(rb * 16 + n) * KP + g * (DK / 4) + ks * E]), kb, d);
+                if constexpr (sizeof(TI) == 2) e4 = MF::mma(kb, qf[ks], e4);
+            }
+            {
+                const int s = sb * 16 + n;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = rb * 16 + 4 * g + e;
+                    Pm[r * TP + s] = (s < r) ? Bs[r] * __expf(Gs[r] - Gs[s]) * d[e] : 0.f;
+                }
+            }
+            if constexpr (sizeof(TI) == 2) {
+                const int r = rb * 16 + n;
+                const float Gr = Gs[r];
+                if (sb == rb) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = sb * 16 + 4 * g + e;
+                        ms[hb][e] = (s > r) ? 0.f : e4[e] * __expf(Gr - Gs[s]);
+                    }
+                } else {
+                    const float Ge = Gs[sb * 16 + 15];
+                    const float fr = __expf(Gr - Ge);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ms[hb][e] = e4[e] * (fr * __expf(Ge - Gs[sb * 16 + 4 * g + e]));
+                }
+            }
+        }
+        if constexpr (sizeof(TI) == 2) {
+            const int f = rb + (rb > 2 ? rb - 2 : 0) + p;
+            f16 *mo = (f16 *)a.mf + (((size_t)bh * a.nchunks + c) * 6 + f) * 512 + lane * 8;
+            *reinterpret_cast<f16x8 *>(mo) = pack_tiles(ms[0], ms[1], 1.f);
         }
     }
     __syncthreads();  // P complete; K row-major is dead from here (Tm reuses it)
@@ -242,6 +324,9 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
             const int s = 4 * ktq + r;
             sc[r] = __shfl(bv, s, 64) * __expf(__shfl(G, s, 64));
         }
+        float kx[4][8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) unpack8<TI>(kr[r], kx[r]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             f32x4 col = {kx[0][e] * sc[0], kx[1][e] * sc[1], kx[2][e] * sc[2], kx[3][e] * sc[3]};
@@ -270,6 +355,9 @@ __global__ void __launch_bounds__(256) gdn_prep_kernel(PrepArgs a) {
         float sc[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sc[r] = __shfl(bv, 4 * vtq + r, 64);
+        float vx[4][8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) unpack8<TI>(vr[r], vx[r]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             f32x4 col = {vx[0][e] * sc[0], vx[1][e] * sc[1], vx[2][e] * sc[2], vx[3][e] * sc[3]};

@@ -257,6 +257,13 @@ __device__ inline f16x8 tr_frag(const f16 *X, int r0, int col0, int lane) {
     return f16x8{ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
 }
 
+// fp16 fragment from two accumulator tiles (tile lo in slots 0..3, hi in 4..7),
+// each element scaled by f.
+__device__ inline f16x8 pack_tiles(const f32x4 &lo, const f32x4 &hi, float f) {
+    return f16x8{(f16)(lo[0] * f), (f16)(lo[1] * f), (f16)(lo[2] * f), (f16)(lo[3] * f),
+                 (f16)(hi[0] * f), (f16)(hi[1] * f), (f16)(hi[2] * f), (f16)(hi[3] * f)};
+}
+
 // DPP move of a float (row_mask / bank_mask select written rows / banks; lanes
 // whose source is invalid or masked keep `old`).
 template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>

@@ -19,6 +19,8 @@ struct ChunkArgs {
     float *z_out;               // [BH, DK] or nullptr (normalized only)
     const void *w;              // gated delta: W  [BH, Lp, DK] (operand type)
     const void *ut;             // gated delta: U~ [BH, Lp, dv] (operand type)
+    const void *mf;             // gated delta, bf16: masked decayed score fragments
+                                // [BH, Lp / 64, 6, 64, 8] fp16 (gdn_prep_impl.hpp)
     int BH, L, Lp, dv, nsplit;  // Lp = ceil(L / C) * C; nsplit = dv / DVT (workgroups per head)
     int ld;                     // rows between consecutive heads of q, k, v, o and the gates
                                 // (>= L; L unless a piece of a longer sequence is run)
@@ -26,9 +28,9 @@ struct ChunkArgs {
 
 // Chunk-parallel preparation of the gated delta rule (one block per chunk).
 struct PrepArgs {
-    const void *k, *v;          // [BH, L, DK], [BH, L, dv]
+    const void *q, *k, *v;      // [BH, L, DK], [BH, L, DK], [BH, L, dv] (q: bf16 inputs only)
     const float *lg, *beta;     // [BH, L] (lg may be nullptr)
-    void *w, *ut;               // outputs, layouts as in ChunkArgs
+    void *w, *ut, *mf;          // outputs, layouts as in ChunkArgs (mf: bf16 inputs only)
     int BH, L, Lp, dv, nchunks;
     int ld;                     // rows between consecutive heads of k, v and the gates (>= L)
 };
@@ -83,7 +85,8 @@ template <typename TI, int DK, int C>
 hipError_t launch_gdn_prep(const PrepArgs &a, hipStream_t st);
 
 // Serial chunk pass of the gated delta rule for bf16 inputs (C = 64, 16-column
-// value slices: a.nsplit = dv / 16), after launch_gdn_prep.
+// value slices: a.nsplit = dv / 16), after launch_gdn_prep (which writes a.w,
+// a.ut and a.mf).
 template <typename TO, int DK>
 hipError_t launch_gdn_fwd(const ChunkArgs &a, hipStream_t st);
 

@@ -105,9 +105,10 @@ typedef enum la_dtype {
  * Zero for LA_PLAIN, LA_NORMALIZED, LA_DECAY and LA_VECTOR_DECAY, which run in
  * one fused pass.
  * LA_GATED_DELTA runs a chunk-parallel preparation pass first and stores its
- * per-chunk products (W and U~ of the chunkwise delta-rule form) there:
- * B*H*ceil(L/C)*C*d_k elements (rounded up to 256 bytes) plus B*H*ceil(L/C)*C*d_v
- * elements, 2 bytes each for bf16 inputs and 4 for fp32.
+ * per-chunk products there: W and U~ of the chunkwise delta-rule form,
+ * B*H*Lp*d_k and B*H*Lp*d_v elements (2 bytes each for bf16 inputs, 4 for
+ * fp32), each rounded up to 256 bytes, with Lp = ceil(L/64)*64; for bf16 inputs
+ * also the chunk's masked decayed scores, 96 bytes per token (B*H*Lp*96).
  * Returns LA_ERR_INVALID_ARG / LA_ERR_UNSUPPORTED like la_chunk_fwd.
  */
 la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H, int L,
@@ -261,8 +262,8 @@ la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k
  * sequence's products do not fit, the sequence is run in pieces of whole
  * chunks, chained through the fp32 state (in state_out when given, else in the
  * scratch), so any L works. LA_ERR_UNSUPPORTED when one chunk of every head
- * does not fit (B*H*C*(d_k+d_v)*sizeof(input) plus the carried state above the
- * scratch). Calls on one device share the scratch: calls that may overlap in
+ * does not fit (the workspace of a 64-token sequence plus the carried state
+ * above the scratch). Calls on one device share the scratch: calls that may overlap in
  * time on one device (different streams, or host threads) race and must be
  * serialized by the caller. Other variants need no scratch and run as
  * la_chunk_fwd.

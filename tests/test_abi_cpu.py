@@ -54,10 +54,13 @@ def test_workspace_sizes():
     # one fused pass for the variants without the delta rule
     for var in (PLAIN, NORM, DECAY):
         assert wsize(var=var) == (0, 0)
-    # delta rule: W [BH, Lp, dk] (rounded to 256 B) + U~ [BH, Lp, dv], Lp = 128
+    # delta rule: W [BH, Lp, dk] + U~ [BH, Lp, dv] (each rounded to 256 B), Lp = 128,
+    # and for bf16 the score fragments, 96 bytes per token
+    up = lambda x: -(-x // 256) * 256
     st, n = wsize()
-    w = -(-2 * 3 * 128 * 64 * 2 // 256) * 256
-    assert st == 0 and n == w + 2 * 3 * 128 * 32 * 2
+    assert st == 0 and n == up(2 * 3 * 128 * 64 * 2) + up(2 * 3 * 128 * 32 * 2) + 2 * 3 * 128 * 96
+    st, n = wsize(dt=F32, L=37, dv=32)
+    assert st == 0 and n == up(2 * 3 * 64 * 64 * 4) + up(2 * 3 * 64 * 32 * 4)
     assert wsize(L=0) == (0, 0)
     # C = 128: the delta rule runs its 128-token chunks as two 64-token sub-chunks
     assert wsize(C=128) == wsize(C=64)
