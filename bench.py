@@ -127,10 +127,16 @@ def bwd_work(c: dict) -> tuple[float, float]:
     B, H, L, dk, dv, C = c["B"], c["H"], c["L"], c["dk"], c["dv"], c["C"]
     BH = B * H
     esz = 2 if c["dtype"] == "bf16" else 4
-    flop = 2.0 * (2 * C * (dk + dv) + 4 * dk * dv) * BH * L
+    if c["variant"] == "gated_delta":
+        fwd = (2 * C * C * (3 * dk + 2 * dv) + 6 * C * dk * dv + C ** 3 / 3) / C
+    else:
+        fwd = 2 * C * (dk + dv) + 4 * dk * dv
+    flop = 2.0 * fwd * BH * L
     nbytes = BH * L * ((2 * dk + 2 * dv) * esz + (2 * dk + dv) * 4)
-    if c["variant"] == "decay":
+    if c["variant"] in ("decay", "gated_delta"):
         nbytes += 2 * BH * L * 4                                 # gates in, gate gradient out
+    if c["variant"] == "gated_delta":
+        nbytes += 2 * BH * L * 4                                 # beta in, its gradient out
     return flop, nbytes
 
 
@@ -288,14 +294,14 @@ def bench_bwd(name: str, steps: int, warmup: int, device) -> dict:
                               seed=0, recipe=c["recipe"])
     do = W.make_backward_dout(c["dtype"], c["B"], c["H"], c["L"], c["dv"], seed=0)
     flop, nbytes = bwd_work(c)
-    q, k, v, lg, dO = (to_dev(x, device) for x in (inp.q, inp.k, inp.v, inp.log_gate, do))
+    q, k, v, lg, be, dO = (to_dev(x, device) for x in (inp.q, inp.k, inp.v, inp.log_gate, inp.beta, do))
     dt = 1 if c["dtype"] == "bf16" else 0
     ws = torch.empty(la.la_chunk_bwd_workspace_size(c["variant"], dt, c["B"], c["H"], c["L"], c["dk"],
                                                     c["dv"], c["C"]), dtype=torch.uint8, device=device)
     stream = torch.cuda.current_stream(device)
 
     def step(_):
-        la.la_chunk_bwd(c["variant"], q, k, v, dO, lg, workspace=ws, stream=stream)
+        la.la_chunk_bwd(c["variant"], q, k, v, dO, lg, beta=be, workspace=ws, stream=stream)
 
     ms, wall_ms = time_steps(step, steps, warmup, stream)
     t = ms / 1e3

@@ -61,7 +61,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_chunk_bwd_workspace_size.restype = i
     lib.la_chunk_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.la_chunk_bwd.restype = i
-    lib.la_chunk_bwd.argtypes = [i, i, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp, fp, fp,
+    lib.la_chunk_bwd.argtypes = [i, i, vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
                                  i, i, i, i, i, i, vp, sz, vp]
     lib.la_short_conv.restype = i
     lib.la_short_conv.argtypes = [i, vp, vp, vp, fp, fp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -273,13 +273,15 @@ def la_chunk_bwd_workspace_size(variant: str, dtype_code: int, B: int, H: int, L
 
 
 def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_state_out=None, *,
-                 C: int = 64, want_d_log_gate: bool = True, want_d_state_in: bool = False,
-                 workspace=None, stream=None) -> Tuple:
-    """Backward pass of la_chunk_fwd ("plain" or "decay").
+                 beta=None, C: int = 64, want_d_log_gate: bool = True, want_d_state_in: bool = False,
+                 want_d_beta: bool = True, workspace=None, stream=None) -> Tuple:
+    """Backward pass of la_chunk_fwd ("plain", "decay", or "gated_delta" in bf16).
 
     q, k: [B, H, L, d_k]; v, d_o: [B, H, L, d_v] (bf16 or fp32, one dtype);
-    log_gate: [B, H, L] fp32 ("decay"); state_in, d_state_out: [B, H, d_k, d_v] fp32.
-    Returns (dq, dk, dv, d_log_gate or None, d_state_in or None), all fp32.
+    log_gate: [B, H, L] fp32 ("decay"; optional for "gated_delta"); beta: [B, H, L]
+    fp32 ("gated_delta"); state_in, d_state_out: [B, H, d_k, d_v] fp32.
+    Returns (dq, dk, dv, d_log_gate or None, d_state_in or None), all fp32, and for
+    "gated_delta" d_beta (or None) as a sixth entry.
     """
     import torch
     lib = load_library()
@@ -291,12 +293,16 @@ def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_sta
     d_v = v.shape[-1]
     dt = _dt(q)
     dev_, f32 = q.device, torch.float32
+    gdn = variant == "gated_delta"
     _check("k", k, (B, H, L, d_k), q.dtype, dev_, required=True)
     _check("v", v, (B, H, L, d_v), q.dtype, dev_, required=True)
     _check("d_o", d_o, (B, H, L, d_v), q.dtype, dev_, required=True)
     _check("log_gate", log_gate, (B, H, L), f32, dev_)
+    _check("beta", beta, (B, H, L), f32, dev_, required=gdn)
     _check("state_in", state_in, (B, H, d_k, d_v), f32, dev_)
     _check("d_state_out", d_state_out, (B, H, d_k, d_v), f32, dev_)
+    if not gdn and beta is not None:
+        raise ValueError("beta is taken by the gated delta rule only")
     _check_device(dev_)
     if workspace is not None and (workspace.device != dev_ or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous tensor on q's device")
@@ -304,18 +310,21 @@ def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_sta
     dk = torch.empty((B, H, L, d_k), dtype=torch.float32, device=dev_)
     dv = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev_)
     dlg = (torch.empty((B, H, L), dtype=torch.float32, device=dev_)
-           if (variant == "decay" and want_d_log_gate) else None)
+           if (log_gate is not None and variant in ("decay", "gated_delta") and want_d_log_gate) else None)
+    dbe = torch.empty((B, H, L), dtype=torch.float32, device=dev_) if (gdn and want_d_beta) else None
     dsi = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev_) if want_d_state_in else None
     if workspace is None:
         ws_bytes = la_chunk_bwd_workspace_size(variant, dt, B, H, L, d_k, d_v, C)
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev_)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.la_chunk_bwd(VARIANTS[variant], dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate),
+    st = lib.la_chunk_bwd(VARIANTS[variant], dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(beta),
                           _ptr(state_in), _ptr(d_o), _ptr(d_state_out), _ptr(dq), _ptr(dk), _ptr(dv),
-                          _ptr(dlg), _ptr(dsi), B, H, L, d_k, d_v, C, _ptr(workspace), ws_bytes,
+                          _ptr(dlg), _ptr(dbe), _ptr(dsi), B, H, L, d_k, d_v, C, _ptr(workspace), ws_bytes,
                           _stream(dev_, stream))
     if st != LA_OK:
         raise LinAttnError(st, "la_chunk_bwd")
+    if gdn:
+        return dq, dk, dv, dlg, dsi, dbe
     return dq, dk, dv, dlg, dsi
 
 

@@ -245,7 +245,8 @@ la_status check_bwd_shape(la_variant var, la_dtype dt, int B, int H, int L, int 
     if (var < LA_PLAIN || var > LA_VECTOR_DECAY) return LA_ERR_INVALID_ARG;
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || L < 0) return LA_ERR_INVALID_ARG;
-    if (var != LA_PLAIN && var != LA_DECAY) return LA_ERR_UNSUPPORTED;
+    if (var != LA_PLAIN && var != LA_DECAY && !(var == LA_GATED_DELTA && dt == LA_BF16))
+        return LA_ERR_UNSUPPORTED;
     if (C != 64) return LA_ERR_UNSUPPORTED;
     if ((d_k != 32 && d_k != 64 && d_k != 128) || (d_v != 32 && d_v != 64 && d_v != 128))
         return LA_ERR_UNSUPPORTED;
@@ -257,10 +258,12 @@ la_status check_bwd_shape(la_variant var, la_dtype dt, int B, int H, int L, int 
 }
 
 struct BwdLayout {
-    size_t hs, dhs, s_last, rterm, total;
+    size_t hs, dhs, s_last, rterm, w, u, du, t, total;
 };
-BwdLayout bwd_layout(la_dtype dt, int64_t BH, int L, int d_k, int d_v) {
-    const int64_t nch = (L + 63) / 64;
+// Every array starts on a 256-byte boundary. The delta rule adds W [BH, Lp, d_k],
+// U~ / U and A_m^T dO / dU [BH, Lp, d_v] and T [BH, nchunks, 64, 64], in fp16.
+BwdLayout bwd_layout(la_variant var, la_dtype dt, int64_t BH, int L, int d_k, int d_v) {
+    const int64_t nch = (L + 63) / 64, Lp = nch * 64;
     BwdLayout w{};
     const size_t st = (size_t)BH * nch * d_k * d_v * elem_size(dt);
     w.hs = 0;
@@ -268,7 +271,31 @@ BwdLayout bwd_layout(la_dtype dt, int64_t BH, int L, int d_k, int d_v) {
     w.s_last = w.dhs + round_up(st, 256);
     w.rterm = w.s_last + round_up((size_t)BH * d_k * d_v * 4, 256);
     w.total = w.rterm + round_up((size_t)BH * L * 4, 256);
+    if (var == LA_GATED_DELTA) {
+        w.w = w.total;
+        w.u = w.w + round_up((size_t)BH * Lp * d_k * 2, 256);
+        w.du = w.u + round_up((size_t)BH * Lp * d_v * 2, 256);
+        w.t = w.du + round_up((size_t)BH * Lp * d_v * 2, 256);
+        w.total = w.t + round_up((size_t)BH * nch * 64 * 64 * 2, 256);
+    }
     return w;
+}
+
+hipError_t dispatch_gdn_bwd(int d_k, int d_v, const BwdArgs &a, hipStream_t st) {
+#define LA_GDN_BWD_DV(DK)                                          \
+    switch (d_v) {                                                 \
+        case 32: return launch_gdn_bwd<DK, 32>(a, st);             \
+        case 64: return launch_gdn_bwd<DK, 64>(a, st);             \
+        case 128: return launch_gdn_bwd<DK, 128>(a, st);           \
+    }                                                              \
+    break;
+    switch (d_k) {
+        case 32: LA_GDN_BWD_DV(32)
+        case 64: LA_GDN_BWD_DV(64)
+        case 128: LA_GDN_BWD_DV(128)
+    }
+#undef LA_GDN_BWD_DV
+    return hipErrorInvalidValue;
 }
 
 template <typename TI, bool DECAY>
@@ -703,36 +730,40 @@ la_status la_chunk_bwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
     const la_status s = check_bwd_shape(var, dt, B, H, L, d_k, d_v, C);
     if (s != LA_OK) return s;
     if (!bytes) return LA_ERR_INVALID_ARG;
-    *bytes = bwd_layout(dt, (int64_t)B * H, L, d_k, d_v).total;
+    *bytes = bwd_layout(var, dt, (int64_t)B * H, L, d_k, d_v).total;
     return LA_OK;
 }
 
 la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k, const void *v,
-                       const float *log_gate, const float *state_in, const void *d_o,
-                       const float *d_state_out, float *dq, float *dk, float *dv, float *d_log_gate,
-                       float *d_state_in, int B, int H, int L, int d_k, int d_v, int C,
-                       void *workspace, size_t workspace_bytes, void *stream) {
+                       const float *log_gate, const float *beta, const float *state_in,
+                       const void *d_o, const float *d_state_out, float *dq, float *dk, float *dv,
+                       float *d_log_gate, float *d_beta, float *d_state_in, int B, int H, int L,
+                       int d_k, int d_v, int C, void *workspace, size_t workspace_bytes,
+                       void *stream) {
     la_status s = check_bwd_shape(var, dt, B, H, L, d_k, d_v, C);
     if (s != LA_OK) return s;
-    const bool tok = L > 0;
+    const bool tok = L > 0, gdn = var == LA_GATED_DELTA;
     if (tok && (!q || !k || !v || !d_o || !dq || !dk || !dv)) return LA_ERR_INVALID_ARG;
     if (var == LA_DECAY && tok && !log_gate) return LA_ERR_INVALID_ARG;
     if (var == LA_PLAIN && (log_gate || d_log_gate)) return LA_ERR_INVALID_ARG;
-    const void *ptrs[] = {q, k, v, log_gate, state_in, d_o, d_state_out, dq, dk, dv, d_log_gate, d_state_in};
+    if (d_log_gate && !log_gate && tok) return LA_ERR_INVALID_ARG;
+    if (gdn ? (tok && !beta) : (beta || d_beta)) return LA_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, k, v, log_gate, beta, state_in, d_o, d_state_out, dq, dk, dv,
+                          d_log_gate, d_beta, d_state_in};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
     const int64_t BH = (int64_t)B * H;
     const size_t es = elem_size(dt);
     const size_t qk_b = (size_t)BH * L * d_k * es, v_b = (size_t)BH * L * d_v * es;
     const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4;
-    const BwdLayout lay = bwd_layout(dt, BH, L, d_k, d_v);
+    const BwdLayout lay = bwd_layout(var, dt, BH, L, d_k, d_v);
     if (!workspace || workspace_bytes < lay.total) return LA_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
-    const Span ins[] = {{q, qk_b}, {k, qk_b}, {v, v_b}, {log_gate, g_b}, {state_in, s_b}, {d_o, v_b},
-                        {d_state_out, s_b}};
+    const Span ins[] = {{q, qk_b},    {k, qk_b},        {v, v_b},   {log_gate, g_b},
+                        {beta, g_b}, {state_in, s_b}, {d_o, v_b}, {d_state_out, s_b}};
     const Span outs[] = {{dq, (size_t)BH * L * d_k * 4}, {dk, (size_t)BH * L * d_k * 4},
-                         {dv, (size_t)BH * L * d_v * 4}, {d_log_gate, g_b}, {d_state_in, s_b},
-                         {workspace, lay.total}};
+                         {dv, (size_t)BH * L * d_v * 4}, {d_log_gate, g_b}, {d_beta, g_b},
+                         {d_state_in, s_b}, {workspace, lay.total}};
     for (size_t o = 0; o < sizeof(outs) / sizeof(outs[0]); ++o) {
         for (const Span &in : ins)
             if (overlap(outs[o], in)) return LA_ERR_INVALID_ARG;
@@ -753,10 +784,16 @@ la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k
     a.rterm = reinterpret_cast<float *>(ws + lay.rterm);
     a.BH = (int)BH; a.L = L; a.dv = d_v; a.nsplit = 1;
     hipError_t e;
-    if (dt == LA_BF16)
+    if (gdn) {
+        a.beta = beta; a.gbeta = d_beta;
+        a.w = ws + lay.w; a.u = ws + lay.u; a.du = ws + lay.du; a.t = ws + lay.t;
+        a.nchunks = (L + 63) / 64; a.Lp = a.nchunks * 64;
+        e = dispatch_gdn_bwd(d_k, d_v, a, st);
+    } else if (dt == LA_BF16) {
         e = var == LA_DECAY ? dispatch_bwd<bf16, true>(d_k, d_v, a, st) : dispatch_bwd<bf16, false>(d_k, d_v, a, st);
-    else
+    } else {
         e = var == LA_DECAY ? dispatch_bwd<float, true>(d_k, d_v, a, st) : dispatch_bwd<float, false>(d_k, d_v, a, st);
+    }
     return from_hip(e);
 }
 

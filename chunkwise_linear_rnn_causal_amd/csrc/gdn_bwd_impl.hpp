@@ -1,0 +1,667 @@
+// gdn_bwd_impl.hpp -- backward pass of the gated delta rule (gfx950), bf16
+// inputs, fp16 MFMA operands with fp32 accumulation, C = 64.
+//
+// Forward, per chunk (wln20 "LLM注意力优化：线性注意力", Gated DeltaNet section;
+// tensorplay "Talk Linear Attention", section 6.2, WY / UT chunk form), with
+// chunk-local cumulative log-gate G_r, a_r = e^{G_r}, Gamma_rs = e^{G_r - G_s},
+// the state S_0 before the chunk, K^ = diag(a_C / a) K and Q^ = diag(a) Q:
+//   B_k = Gamma (.) K K^T, strictly lower;  P = diag(beta) B_k;  T = (I + P)^-1
+//   R = V - diag(a) K S_0;  U = T diag(beta) R  (= U~ - W S_0)
+//   A_m = Gamma (.) Q K^T, lower with the diagonal
+//   O = Q^ S_0 + A_m U;  S_C = a_C S_0 + K^^T U.
+// Reverse mode, given dO and dS_C = dLoss/dS_C:
+//   dU   = A_m^T dO + K^ dS_C
+//   dS_0 = a_C dS_C + Q^^T dO - W^T dU        (the reverse serial step)
+//   dY   = T^T dU;  dv = diag(beta) dY
+//   X    = dY S_0^T
+//   dA'  = Gamma (.) (dO U^T), lower with the diagonal
+//   dB'  = -diag(beta) Gamma (.) (dY U^T), strictly lower;  Bsym = dB' + dB'^T
+//   dq   = diag(a) dO S_0^T + dA' K
+//   dk   = dA'^T Q + diag(a_C / a) U dS_C^T - diag(a beta) X + Bsym K
+//   dbeta_r = dY_r . v_r - a_r (k_r . X_r) - sum_s (dY U^T)_rs (B_k)_rs
+// (the last from U = diag(beta) (R - B_k U)). The loss depends on the gates only
+// through q_t e^{G_t}, v_t e^{-G_t} and the final state e^{G_L} S'_L of the
+// gate-free recurrence in the variables S'_t = S_t e^{-G_t}, so
+//   dl_t = sum_{u >= t} (q_u . dq_u - v_u . dv_u) + <dS_L, S_L>.
+// The gate of token t + 1 multiplies only the state S_t, so the same sum from
+// the first token after a chunk on is <dS_end, S_end> of the state at the end
+// of the chunk and its gradient: inside chunk c
+//   dl_t = sum_{u = t}^{end of c} (q_u . dq_u - v_u . dv_u) + <dS_end(c), S_end(c)>,
+// which keeps the sum to at most 64 terms (a sum over the whole sequence would
+// add up the rounding of L terms whose total is much smaller than their sizes).
+// The per-chunk states are recomputed (tensorplay section 4.1.2: stored per
+// chunk for back-propagation) by two serial scans over the chunks that share
+// one form: X' = a_C X + M^T Z (+ E), Z = Y~ + sigma N X, with
+//   forward: X = S,  N = W,  sigma = -1, Y~ = U~,       M = K^,  E = 0       (Z = U)
+//   reverse: X = dS, N = K^, sigma = +1, Y~ = A_m^T dO, M = -W,  E = Q^^T dO (Z = dU)
+//
+// Launches (launch_gdn_bwd):
+//   gdn_prep_kernel<bf16, DK, 64, true>  W, U~ (row-major) and T per chunk.
+//   gdn_bwd_dut_kernel  A_m^T dO per chunk.
+//   gdn_bwd_scan_kernel  forward and reverse scans in one launch, one workgroup
+//       per (direction, head, 32-column value slice); each stores X per chunk
+//       (S before the chunk / dS after it) and overwrites U~ with U (A_m^T dO
+//       with dU) in place.
+//   gdn_bwd_grad_kernel  one workgroup (8 waves) per (head, chunk): dq, dk, dv,
+//       dbeta and the log-gate gradient.
+#pragma once
+
+#include "gdn_prep_impl.hpp"
+#include "la_common.hpp"
+#include "la_kernels.hpp"
+
+namespace la {
+
+namespace gdnb {
+
+constexpr int C = 64;
+
+// Operand fragment with the "natural" K-slot map: slot e of lane group g holds
+// k0 + 8g + e (one 16-byte read of a row whose K index runs along it).
+template <int P> __device__ inline f16x8 nat_frag(const f16 *X, int row, int k0, int g) {
+    return *reinterpret_cast<const f16x8 *>(X + row * P + k0 + 8 * g);
+}
+// Operand fragment with the "paired" K-slot map of tr_frag: slots 0..3 of group
+// g hold k0 + 4g + e, slots 4..7 hold k0 + 16 + 4g + e (two 8-byte reads).
+template <int P> __device__ inline f16x8 pair_frag(const f16 *X, int row, int k0, int g) {
+    const f16x4 a = *reinterpret_cast<const f16x4 *>(X + row * P + k0 + 4 * g);
+    const f16x4 b = *reinterpret_cast<const f16x4 *>(X + row * P + k0 + 16 + 4 * g);
+    return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+// Paired-map fragment whose K index runs down the columns of a row-major tile:
+// X[k0 + map][col0 + n].
+template <int P> __device__ inline f16x8 col_frag(const f16 *X, int k0, int col0, int lane) {
+    return tr_frag<P>(X, k0 + 4 * ((lane >> 4) & 3), col0, lane);
+}
+
+__device__ inline uint4 bf16x8_to_f16x8(uint4 w) {
+    // packed round-toward-zero conversion: exact for bf16 values in fp16's
+    // normal range; below it the error stays under 2^-24
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        h[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(u[i]), bf16_hi(u[i])));
+    return make_uint4(h[0], h[1], h[2], h[3]);
+}
+// eight bf16 values times f, rounded to fp16
+__device__ inline uint4 bf16x8_scaled_f16(uint4 w, float f) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f16 lo = (f16)(bf16_lo(u[i]) * f), hi = (f16)(bf16_hi(u[i]) * f);
+        h[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return make_uint4(h[0], h[1], h[2], h[3]);
+}
+
+// sum over the 16 lanes of a lane group (n = 0..15)
+__device__ inline float group16_sum(float x) {
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+
+// Rows [t0, t0 + C) of a bf16 [L][D] head into a fp16 LDS tile of pitch P
+// (rows past L zero), NT threads; all loads are issued before any store.
+template <int D, int P, int NT>
+__device__ inline void stage_bf16(f16 *dst, const bf16 *src, int t0, int L, int tid) {
+    constexpr int SEG = D / 8, TOT = C * SEG, N = (TOT + NT - 1) / NT;
+    uint4 r[N];
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        const int idx = tid + NT * m, row = idx / SEG, seg = idx % SEG;
+        if (TOT % NT == 0 || idx < TOT)
+            r[m] = *reinterpret_cast<const uint4 *>(src + (size_t)min(t0 + row, L - 1) * D + seg * 8);
+    }
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        const int idx = tid + NT * m, row = idx / SEG, seg = idx % SEG;
+        if (TOT % NT == 0 || idx < TOT)
+            *reinterpret_cast<uint4 *>(dst + row * P + seg * 8) =
+                t0 + row < L ? bf16x8_to_f16x8(r[m]) : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+// C rows of an fp16 [.][D] array (row stride D) into an LDS tile of pitch P.
+template <int D, int P, int NT>
+__device__ inline void stage_f16(f16 *dst, const f16 *src, int tid) {
+    constexpr int SEG = D / 8, TOT = C * SEG, N = (TOT + NT - 1) / NT;
+    uint4 r[N];
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        const int idx = tid + NT * m, row = idx / SEG, seg = idx % SEG;
+        if (TOT % NT == 0 || idx < TOT) r[m] = *reinterpret_cast<const uint4 *>(src + (size_t)row * D + seg * 8);
+    }
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        const int idx = tid + NT * m, row = idx / SEG, seg = idx % SEG;
+        if (TOT % NT == 0 || idx < TOT) *reinterpret_cast<uint4 *>(dst + row * P + seg * 8) = r[m];
+    }
+}
+
+}  // namespace gdnb
+
+// ---------------------------------------------------------------------------
+// A_m^T dO per chunk: [BH, Lp, DV] fp16 into a.du. One workgroup (4 waves) per
+// (head, chunk).
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) gdn_bwd_dut_kernel(BwdArgs a) {
+    using namespace gdnb;
+    using MF = Mfma<f16>;
+    constexpr int KP = DK + 16, VP = DV + 16, AP = C + 16;
+    __shared__ __attribute__((aligned(16))) f16 Qs[C * KP];
+    __shared__ __attribute__((aligned(16))) f16 Ks[C * KP];
+    __shared__ __attribute__((aligned(16))) f16 Os[C * VP];
+    __shared__ __attribute__((aligned(16))) f16 At[C * AP];  // A_m^T: [s][r]
+    __shared__ float Gs[C];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
+    const int bh = blockIdx.x / a.nchunks, c = blockIdx.x - bh * a.nchunks;
+    const int L = a.L, t0 = c * C;
+    stage_bf16<DK, KP, 256>(Qs, (const bf16 *)a.q + (size_t)bh * L * DK, t0, L, tid);
+    stage_bf16<DK, KP, 256>(Ks, (const bf16 *)a.k + (size_t)bh * L * DK, t0, L, tid);
+    stage_bf16<DV, VP, 256>(Os, (const bf16 *)a.dout + (size_t)bh * L * DV, t0, L, tid);
+    if (wv == 0) {
+        const float l = (a.lg && t0 + lane < L) ? a.lg[(size_t)bh * L + t0 + lane] : 0.f;
+        Gs[lane] = wave_inclusive_sum(l);
+    }
+    __syncthreads();
+
+    // A_m^T tiles D[s][r] = k_s . q_r, masked (s <= r) and decayed
+    for (int tile = wv; tile < 16; tile += 4) {
+        const int sb = tile >> 2, rb = tile & 3;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        if (sb <= rb) {
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks)
+                d = MF::mma(nat_frag<KP>(Ks, sb * 16 + n, ks * 32, g), nat_frag<KP>(Qs, rb * 16 + n, ks * 32, g), d);
+        }
+        const int r = rb * 16 + n;
+        const float Gr = Gs[r];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = sb * 16 + 4 * g + e;
+            At[s * AP + r] = (f16)(s <= r ? d[e] * __expf(Gr - Gs[s]) : 0.f);
+        }
+    }
+    __syncthreads();
+
+    // (A_m^T dO)^T tiles D[j][s] = sum_r dO[r][j] A_m^T[s][r]; lane holds
+    // j = jb*16 + 4g + e, s = sb*16 + n: four consecutive columns of row s
+    f16 *du = (f16 *)a.du + ((size_t)bh * a.Lp + t0) * DV;
+    for (int tile = wv; tile < (DV / 16) * 4; tile += 4) {
+        const int jb = tile >> 2, sb = tile & 3;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            if (kk * 32 + 31 < sb * 16) continue;  // rows r < s only
+            d = MF::mma(col_frag<VP>(Os, kk * 32, jb * 16, lane), pair_frag<AP>(At, sb * 16 + n, kk * 32, g), d);
+        }
+        st4<f16>(du + (size_t)(sb * 16 + n) * DV + jb * 16 + 4 * g, d);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The two serial scans. Workgroup b < BH * NS runs the forward scan of head
+// b / NS, value columns [32 (b % NS), +32); the others the reverse scan.
+template <int DK, int DV>
+struct GdnScanCfg {
+    static constexpr int DVT = 32, NS = DV / DVT;
+    static constexpr int C = gdnb::C, KP = DK + 16, YP = DVT + 16, XP = DVT + 16;
+    // per buffer: W, K^, Q^ (reverse), Y~, dO (reverse)
+    static constexpr int OW = 0, OK = C * KP, OQ = 2 * C * KP, OY = 3 * C * KP, OO = OY + C * YP,
+                         SET = OO + C * YP;
+    static constexpr int XS = 2 * SET, ZS = XS + DK * XP, TOTAL = ZS + C * YP;  // fp16 elements
+    static constexpr int NKL = C * DK / 8 / 256;  // 16-byte loads per thread per C x DK tile
+    static_assert(NKL >= 1 && NKL * 256 * 8 == gdnb::C * DK, "scan staging geometry");
+};
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) gdn_bwd_scan_kernel(BwdArgs a) {
+    using namespace gdnb;
+    using MF = Mfma<f16>;
+    using Cfg = GdnScanCfg<DK, DV>;
+    constexpr int DVT = Cfg::DVT, NS = Cfg::NS, KP = Cfg::KP, YP = Cfg::YP, XP = Cfg::XP;
+    constexpr int NKL = Cfg::NKL, SEGK = DK / 8, SEGY = DVT / 8;
+    constexpr int NTI = DK / 16;  // state row tiles; the slice has 2 column tiles
+    __shared__ __attribute__((aligned(16))) f16 lds[Cfg::TOTAL];
+    __shared__ float Eg[2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
+    const bool rev = blockIdx.x >= a.BH * NS;
+    const int b = rev ? blockIdx.x - a.BH * NS : blockIdx.x;
+    const int bh = b / NS, j0 = (b % NS) * DVT;
+    const int L = a.L, nch = a.nchunks;
+    const bf16 *kg = (const bf16 *)a.k + (size_t)bh * L * DK;
+    const bf16 *qg = (const bf16 *)a.q + (size_t)bh * L * DK;
+    const bf16 *og = (const bf16 *)a.dout + (size_t)bh * L * DV + j0;
+    const f16 *wg = (const f16 *)a.w + (size_t)bh * a.Lp * DK;
+    f16 *yg = (f16 *)(rev ? a.du : a.u) + (size_t)bh * a.Lp * DV + j0;
+    f16 *xg = (f16 *)(rev ? a.dhs : a.hs) + (size_t)bh * nch * DK * DV + j0;
+    const float *lgg = a.lg ? a.lg + (size_t)bh * L : nullptr;
+    f16 *Xs = lds + Cfg::XS, *Zs = lds + Cfg::ZS;
+
+    // X: tiles (ti, tj) = (wv + 4m) / 2, % 2 in fp32 accumulators; lane holds
+    // rows i = 16 ti + 4g + e, column j = 16 tj + n of the slice
+    constexpr int TPW = NTI * 2 / 4;
+    f32x4 X[TPW];
+    {
+        const float *x0 = rev ? a.ds_out : a.s_in;
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int tile = wv + 4 * m, ti = tile >> 1, tj = tile & 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                X[m][e] = x0 ? x0[(size_t)bh * DK * DV + (size_t)(ti * 16 + 4 * g + e) * DV + j0 + tj * 16 + n] : 0.f;
+        }
+    }
+    auto write_x = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int tile = wv + 4 * m, ti = tile >> 1, tj = tile & 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Xs[(ti * 16 + 4 * g + e) * XP + tj * 16 + n] = (f16)X[m][e];
+        }
+    };
+    write_x();
+
+    // prefetch registers of one chunk: W and K rows (NKL each), Y~ (one), and
+    // for the reverse scan Q rows (NKL) and dO (one); the chunk's log-gates
+    uint4 pw[NKL], pk[NKL], pq[NKL], py, po;
+    float pl;
+    auto load = [&](int c) __attribute__((always_inline)) {
+        const int t0 = c * C;
+#pragma unroll
+        for (int m = 0; m < NKL; ++m) {
+            const int idx = tid + 256 * m, row = idx / SEGK, seg = idx % SEGK;
+            pw[m] = *reinterpret_cast<const uint4 *>(wg + (size_t)(t0 + row) * DK + seg * 8);
+            pk[m] = *reinterpret_cast<const uint4 *>(kg + (size_t)min(t0 + row, L - 1) * DK + seg * 8);
+            if (rev) pq[m] = *reinterpret_cast<const uint4 *>(qg + (size_t)min(t0 + row, L - 1) * DK + seg * 8);
+        }
+        {
+            const int row = tid / SEGY, seg = tid % SEGY;
+            py = *reinterpret_cast<const uint4 *>(yg + (size_t)(t0 + row) * DV + seg * 8);
+            if (rev) po = *reinterpret_cast<const uint4 *>(og + (size_t)min(t0 + row, L - 1) * DV + seg * 8);
+        }
+        pl = (lgg && t0 + lane < L) ? lgg[t0 + lane] : 0.f;
+    };
+    auto stage = [&](int c, int buf) __attribute__((always_inline)) {
+        f16 *S = lds + buf * Cfg::SET;
+        const int t0 = c * C;
+        const float G = wave_inclusive_sum(pl);
+        const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
+#pragma unroll
+        for (int m = 0; m < NKL; ++m) {
+            const int idx = tid + 256 * m, row = idx / SEGK, seg = idx % SEGK;
+            const float Gr = __shfl(G, row, 64);
+            const bool valid = t0 + row < L;
+            *reinterpret_cast<uint4 *>(S + Cfg::OW + row * KP + seg * 8) = pw[m];
+            *reinterpret_cast<uint4 *>(S + Cfg::OK + row * KP + seg * 8) =
+                valid ? bf16x8_scaled_f16(pk[m], __expf(gC - Gr)) : make_uint4(0u, 0u, 0u, 0u);
+            if (rev)
+                *reinterpret_cast<uint4 *>(S + Cfg::OQ + row * KP + seg * 8) =
+                    valid ? bf16x8_scaled_f16(pq[m], __expf(Gr)) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        {
+            const int row = tid / SEGY, seg = tid % SEGY;
+            *reinterpret_cast<uint4 *>(S + Cfg::OY + row * YP + seg * 8) = py;
+            if (rev)
+                *reinterpret_cast<uint4 *>(S + Cfg::OO + row * YP + seg * 8) =
+                    t0 + row < L ? bf16x8_to_f16x8(po) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (tid == 0) Eg[buf] = __expf(gC);
+    };
+
+    if (nch > 0) {
+        load(rev ? nch - 1 : 0);
+        stage(rev ? nch - 1 : 0, 0);
+        if (nch > 1) load(rev ? nch - 2 : 1);
+    }
+    __syncthreads();
+    for (int i = 0; i < nch; ++i) {
+        const int buf = i & 1, c = rev ? nch - 1 - i : i;
+        const f16 *S = lds + buf * Cfg::SET;
+        // (1) X (S before chunk c, or dS after it) to the workspace
+#pragma unroll
+        for (int m = 0; m < (DK * SEGY + 255) / 256; ++m) {
+            const int idx = tid + 256 * m, row = idx / SEGY, seg = idx % SEGY;
+            if (idx < DK * SEGY)
+                *reinterpret_cast<uint4 *>(xg + ((size_t)c * DK + row) * DV + seg * 8) =
+                    *reinterpret_cast<const uint4 *>(Xs + row * XP + seg * 8);
+        }
+        // (2) Z = Y~ + sigma N X: row block wv, both column tiles
+        {
+            const f16 *N = S + (rev ? Cfg::OK : Cfg::OW);
+            f32x4 z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                const f16x8 nf = pair_frag<KP>(N, wv * 16 + n, ks * 32, g);
+#pragma unroll
+                for (int tj = 0; tj < 2; ++tj) z[tj] = MF::mma(nf, col_frag<XP>(Xs, ks * 32, tj * 16, lane), z[tj]);
+            }
+            // D layout: rows r = 16 wv + 4g + e, column j = 16 tj + n
+#pragma unroll
+            for (int tj = 0; tj < 2; ++tj) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = wv * 16 + 4 * g + e, j = tj * 16 + n;
+                    const float y = (float)S[Cfg::OY + r * YP + j];
+                    Zs[r * YP + j] = (f16)(rev ? y + z[tj][e] : y - z[tj][e]);
+                }
+            }
+        }
+        __syncthreads();
+        // (3) Z (U or dU) to the workspace, over Y~
+        {
+            const int row = tid / SEGY, seg = tid % SEGY;
+            *reinterpret_cast<uint4 *>(yg + (size_t)(c * C + row) * DV + seg * 8) =
+                *reinterpret_cast<const uint4 *>(Zs + row * YP + seg * 8);
+        }
+        // (4) X' = a_C X + M^T Z (+ Q^^T dO)
+        {
+            const float eg = Eg[buf];
+            const f16 *M = S + (rev ? Cfg::OW : Cfg::OK);
+#pragma unroll
+            for (int m = 0; m < TPW; ++m) X[m] *= eg;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const f16x8 zf[2] = {col_frag<YP>(Zs, kk * 32, 0, lane), col_frag<YP>(Zs, kk * 32, 16, lane)};
+                f16x8 of[2];
+                if (rev) {
+                    of[0] = col_frag<YP>(S + Cfg::OO, kk * 32, 0, lane);
+                    of[1] = col_frag<YP>(S + Cfg::OO, kk * 32, 16, lane);
+                }
+#pragma unroll
+                for (int m = 0; m < TPW; ++m) {
+                    const int tile = wv + 4 * m, ti = tile >> 1, tj = tile & 1;
+                    f16x8 mf = col_frag<KP>(M, kk * 32, ti * 16, lane);
+                    if (rev) {
+                        mf = neg_frag<f16>(mf);
+                        X[m] = MF::mma(col_frag<KP>(S + Cfg::OQ, kk * 32, ti * 16, lane), of[tj], X[m]);
+                    }
+                    X[m] = MF::mma(mf, zf[tj], X[m]);
+                }
+            }
+        }
+        write_x();
+        // (5) stage the next chunk, then load the one after it
+        if (i + 1 < nch) {
+            stage(rev ? c - 1 : c + 1, buf ^ 1);
+            if (i + 2 < nch) load(rev ? c - 2 : c + 2);
+        }
+        __syncthreads();
+    }
+    // final X: the forward scan's S_L, the reverse scan's dS_0
+    float *xo = rev ? a.gs_in : a.s_last;
+    if (xo) {
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int tile = wv + 4 * m, ti = tile >> 1, tj = tile & 1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                xo[(size_t)bh * DK * DV + (size_t)(ti * 16 + 4 * g + e) * DV + j0 + tj * 16 + n] = X[m][e];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk gradients: one workgroup (8 waves) per (head, chunk).
+template <int DK, int DV>
+struct GdnGradCfg {
+    static constexpr int KP = DK + 16, VP = DV + 16, AP = gdnb::C + 16, C = gdnb::C;
+    static constexpr int OQ = 0, OK = OQ + C * KP, OO = OK + C * KP, OU = OO + C * VP, ODU = OU + C * VP,
+                         OY = ODU + C * VP, OT = OY + C * VP, OA = OT + C * AP, OB = OA + C * AP,
+                         TOTAL = OB + C * AP;  // fp16 elements
+};
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(512) gdn_bwd_grad_kernel(BwdArgs a) {
+    using namespace gdnb;
+    using MF = Mfma<f16>;
+    using Cfg = GdnGradCfg<DK, DV>;
+    constexpr int KP = Cfg::KP, VP = Cfg::VP, AP = Cfg::AP;
+    constexpr int NIB = DK / 16, RPW = NIB / 2;  // column blocks of dq / dk; row blocks per wave
+    __shared__ __attribute__((aligned(16))) f16 lds[Cfg::TOTAL];
+    // per-token partial sums, each slot written once (a fixed summation order):
+    // dY . v per pair of waves, (dY U^T) . B_k per key block, k . X and q . dq
+    // per column block; then q . dq - v . dv per token, and per-wave partials of
+    // <dS_end, S_end>
+    __shared__ float Gs[C], Bt[C], rYV[2][C], rYB[4][C], rKX[NIB][C], rQD[NIB][C], dGs[C], bpart[8];
+
+    f16 *Qs = lds + Cfg::OQ, *Ks = lds + Cfg::OK, *Os = lds + Cfg::OO, *Us = lds + Cfg::OU;
+    f16 *dUs = lds + Cfg::ODU, *dYs = lds + Cfg::OY, *Ts = lds + Cfg::OT, *dAs = lds + Cfg::OA,
+        *Bss = lds + Cfg::OB;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
+    const int nch = a.nchunks, bh = blockIdx.x / nch, c = blockIdx.x - bh * nch;
+    const int L = a.L, t0 = c * C;
+    const int ib = wv % NIB, rb0 = (wv / NIB) * RPW;
+
+    // B fragments of S_0 and dS_C for this wave's column block (natural map over j)
+    f16x8 sf[DV / 32], df[DV / 32];
+    {
+        const size_t off = ((size_t)bh * nch + c) * DK * DV + (size_t)(ib * 16 + n) * DV + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < DV / 32; ++ks) {
+            sf[ks] = *reinterpret_cast<const f16x8 *>((const f16 *)a.hs + off + ks * 32);
+            df[ks] = *reinterpret_cast<const f16x8 *>((const f16 *)a.dhs + off + ks * 32);
+        }
+    }
+    // <dS_end, S_end> of this chunk: dS after it (the reverse scan's) and S
+    // before the next chunk (the last chunk: the final state and d_state_out, in fp32)
+    const bool last = c == nch - 1;
+    float bdot = 0.f;
+    {
+        constexpr int NP = (DK * DV / 8 + 511) / 512;
+        if (!last) {
+            const f16 *dh = (const f16 *)a.dhs + ((size_t)bh * nch + c) * DK * DV;
+            const f16 *hn = (const f16 *)a.hs + ((size_t)bh * nch + c + 1) * DK * DV;
+            f16x8 x[NP], y[NP];
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+                const int idx = tid + 512 * m;
+                if (idx < DK * DV / 8) {
+                    x[m] = *reinterpret_cast<const f16x8 *>(dh + idx * 8);
+                    y[m] = *reinterpret_cast<const f16x8 *>(hn + idx * 8);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < NP; ++m) {
+                if (tid + 512 * m < DK * DV / 8) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bdot = fmaf((float)x[m][e], (float)y[m][e], bdot);
+                }
+            }
+        } else if (a.ds_out) {
+            const float *dh = a.ds_out + (size_t)bh * DK * DV, *hn = a.s_last + (size_t)bh * DK * DV;
+            for (int idx = tid; idx < DK * DV / 4; idx += 512) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(dh + idx * 4);
+                const f32x4 y = *reinterpret_cast<const f32x4 *>(hn + idx * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bdot = fmaf(x[e], y[e], bdot);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) bdot += __shfl_xor(bdot, off, 64);
+    }
+    stage_bf16<DK, KP, 512>(Qs, (const bf16 *)a.q + (size_t)bh * L * DK, t0, L, tid);
+    stage_bf16<DK, KP, 512>(Ks, (const bf16 *)a.k + (size_t)bh * L * DK, t0, L, tid);
+    stage_bf16<DV, VP, 512>(Os, (const bf16 *)a.dout + (size_t)bh * L * DV, t0, L, tid);
+    stage_f16<DV, VP, 512>(Us, (const f16 *)a.u + ((size_t)bh * a.Lp + t0) * DV, tid);
+    stage_f16<DV, VP, 512>(dUs, (const f16 *)a.du + ((size_t)bh * a.Lp + t0) * DV, tid);
+    stage_f16<C, AP, 512>(Ts, (const f16 *)a.t + ((size_t)bh * nch + c) * C * C, tid);
+    if (wv == 0) {
+        const bool valid = t0 + lane < L;
+        const float l = (a.lg && valid) ? a.lg[(size_t)bh * L + t0 + lane] : 0.f;
+        Gs[lane] = wave_inclusive_sum(l);
+        Bt[lane] = valid ? a.beta[(size_t)bh * L + t0 + lane] : 0.f;
+    }
+    if (lane == 0) bpart[wv] = bdot;
+    __syncthreads();
+    const float gC = Gs[C - 1];
+    const bf16 *vg = (const bf16 *)a.v + (size_t)bh * L * DV;
+
+    // (1a) dY = T^T dU; dv = diag(beta) dY; dY . v. Wave w's tiles all lie in row
+    // block w % 4.
+    float yv[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int tile = wv; tile < 4 * (DV / 16); tile += 8) {
+        const int rb = tile & 3, jb = tile >> 2;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            if (kk * 32 + 31 < rb * 16) continue;  // T^T[r][s] = 0 for s < r
+            d = MF::mma(col_frag<AP>(Ts, kk * 32, rb * 16, lane), col_frag<VP>(dUs, kk * 32, jb * 16, lane), d);
+        }
+        const int j = jb * 16 + n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rb * 16 + 4 * g + e, t = t0 + r;
+            dYs[r * VP + j] = (f16)d[e];
+            if (t < L) {
+                a.gv[((size_t)bh * L + t) * DV + j] = Bt[r] * d[e];
+                yv[e] = fmaf(d[e], (float)vg[(size_t)t * DV + j], yv[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float x = group16_sum(yv[e]);
+        if (n == 0) rYV[wv >> 2][(wv & 3) * 16 + 4 * g + e] = x;
+    }
+    // (1b) dA' = Gamma (.) (dO U^T), lower with the diagonal
+    for (int tile = wv; tile < 16; tile += 8) {
+        const int rb = tile >> 2, sb = tile & 3;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        if (sb <= rb) {
+#pragma unroll
+            for (int ks = 0; ks < DV / 32; ++ks)
+                d = MF::mma(nat_frag<VP>(Os, rb * 16 + n, ks * 32, g), nat_frag<VP>(Us, sb * 16 + n, ks * 32, g), d);
+        }
+        const int s = sb * 16 + n;
+        const float Gsv = Gs[s];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rb * 16 + 4 * g + e;
+            dAs[r * AP + s] = (f16)(s <= r ? d[e] * __expf(Gs[r] - Gsv) : 0.f);
+        }
+    }
+    __syncthreads();
+
+    // (2) dY U^T and B_k on the lower tiles: (dY U^T) . B_k per row and key
+    // block, Bsym = dB' + dB'^T
+    for (int tile = wv; tile < 16; tile += 8) {
+        const int rb = tile >> 2, sb = tile & 3;
+        if (sb > rb) continue;
+        f32x4 yu = {0.f, 0.f, 0.f, 0.f}, kk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DV / 32; ++ks)
+            yu = MF::mma(nat_frag<VP>(dYs, rb * 16 + n, ks * 32, g), nat_frag<VP>(Us, sb * 16 + n, ks * 32, g), yu);
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks)
+            kk = MF::mma(nat_frag<KP>(Ks, rb * 16 + n, ks * 32, g), nat_frag<KP>(Ks, sb * 16 + n, ks * 32, g), kk);
+        const int s = sb * 16 + n;
+        const float Gsv = Gs[s];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rb * 16 + 4 * g + e;
+            const bool strict = s < r;
+            const float gam = strict ? __expf(Gs[r] - Gsv) : 0.f;
+            const float part = group16_sum(yu[e] * gam * kk[e]);
+            if (n == 0) rYB[sb][r] = part;
+            const f16 db = (f16)(-Bt[r] * gam * yu[e]);
+            if (s <= r) Bss[r * AP + s] = db;
+            if (strict) Bss[s * AP + r] = db;
+        }
+    }
+    __syncthreads();
+
+    // (3) dq and dk for column block ib, row blocks rb0 .. rb0 + RPW - 1
+    for (int u = 0; u < RPW; ++u) {
+        const int rb = rb0 + u;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f}, dq = {0.f, 0.f, 0.f, 0.f}, dk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DV / 32; ++ks) {
+            x = MF::mma(nat_frag<VP>(dYs, rb * 16 + n, ks * 32, g), sf[ks], x);
+            dq = MF::mma(nat_frag<VP>(Os, rb * 16 + n, ks * 32, g), sf[ks], dq);
+            dk = MF::mma(nat_frag<VP>(Us, rb * 16 + n, ks * 32, g), df[ks], dk);
+        }
+        // rows r = rb*16 + 4g + e (tokens), column i = ib*16 + n
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rb * 16 + 4 * g + e;
+            const float Gr = Gs[r], ar = __expf(Gr);
+            dq[e] *= ar;
+            dk[e] = dk[e] * __expf(gC - Gr) - ar * Bt[r] * x[e];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const f16x8 kcol = col_frag<KP>(Ks, kk * 32, ib * 16, lane);
+            dq = MF::mma(pair_frag<AP>(dAs, rb * 16 + n, kk * 32, g), kcol, dq);
+            dk = MF::mma(col_frag<AP>(dAs, kk * 32, rb * 16, lane), col_frag<KP>(Qs, kk * 32, ib * 16, lane), dk);
+            dk = MF::mma(pair_frag<AP>(Bss, rb * 16 + n, kk * 32, g), kcol, dk);
+        }
+        const int i = ib * 16 + n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rb * 16 + 4 * g + e, t = t0 + r;
+            if (t < L) {
+                a.gq[((size_t)bh * L + t) * DK + i] = dq[e];
+                a.gk[((size_t)bh * L + t) * DK + i] = dk[e];
+            }
+            const float qd = group16_sum(dq[e] * (float)Qs[r * KP + i]);
+            const float kx = group16_sum(x[e] * (float)Ks[r * KP + i]);
+            if (n == 0) {
+                rQD[ib][r] = qd;
+                rKX[ib][r] = kx;
+            }
+        }
+    }
+    __syncthreads();
+
+    // (4) per token: dbeta, then the log-gate gradient (suffix sum within the chunk)
+    if (tid < C) {
+        const int r = tid, t = t0 + r;
+        const float yv = rYV[0][r] + rYV[1][r];
+        float yb = 0.f, kx = 0.f, qd = 0.f;
+        for (int sb = 0; sb <= r / 16; ++sb) yb += rYB[sb][r];
+#pragma unroll
+        for (int i = 0; i < NIB; ++i) {
+            kx += rKX[i][r];
+            qd += rQD[i][r];
+        }
+        if (a.gbeta && t < L) a.gbeta[(size_t)bh * L + t] = yv - __expf(Gs[r]) * kx - yb;
+        dGs[r] = t < L ? qd - Bt[r] * yv : 0.f;
+    }
+    if (!a.glg) return;
+    __syncthreads();
+    if (tid < C && t0 + tid < L) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc += bpart[i];
+        for (int u = C - 1; u >= tid; --u) acc += dGs[u];
+        a.glg[(size_t)bh * L + t0 + tid] = acc;
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st) {
+    using Cfg = GdnScanCfg<DK, DV>;
+    const int nch = a.nchunks;
+    if (nch > 0) {
+        PrepArgs p{};
+        p.k = a.k; p.v = a.v; p.lg = a.lg; p.beta = a.beta;
+        p.w = a.w; p.ut = a.u; p.t = a.t;
+        p.BH = a.BH; p.L = a.L; p.Lp = a.Lp; p.dv = DV; p.nchunks = nch; p.ld = a.L;
+        hipLaunchKernelGGL((gdn_prep_kernel<bf16, DK, 64, true>), dim3(a.BH * nch), dim3(256), 0, st, p);
+        hipLaunchKernelGGL((gdn_bwd_dut_kernel<DK, DV>), dim3(a.BH * nch), dim3(256), 0, st, a);
+    }
+    hipLaunchKernelGGL((gdn_bwd_scan_kernel<DK, DV>), dim3(2 * a.BH * Cfg::NS), dim3(256), 0, st, a);
+    if (nch > 0) {
+        hipLaunchKernelGGL((gdn_bwd_grad_kernel<DK, DV>), dim3(a.BH * nch), dim3(512), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace la

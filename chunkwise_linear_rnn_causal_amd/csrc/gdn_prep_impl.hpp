@@ -64,7 +64,9 @@ struct PrepCfg {
     static constexpr size_t lds_bytes = o_g + 4 * 2 * C;
 };
 
-template <typename TI, int DK, int C>
+// BWD: the backward pass's preparation (gdn_bwd_impl.hpp): U~ row-major for
+// every input type, no score fragments, and T stored as well.
+template <typename TI, int DK, int C, bool BWD = false>
 __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
     using TM = typename OpOf<TI>::type;
     using MF = Mfma<TM>;
@@ -77,6 +79,8 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
     constexpr int NKS = DK / (4 * E);
     constexpr int NTK = C / (4 * E);
     static_assert(C == 64 && NRB == NW, "one 16-row diagonal block of T per wave: C = 64");
+    // score fragments and U~ in the serial pass's accumulator layout: bf16 forward
+    constexpr bool SC = sizeof(TI) == 2 && !BWD;
 
     __shared__ __attribute__((aligned(16))) char lds[Cfg::lds_bytes];
     TM *Ks = reinterpret_cast<TM *>(lds + Cfg::o_a);
@@ -119,7 +123,7 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
     const bool job1 = (wv & 1) == 0;
     const int jrb1 = wv == 0 ? 3 : 2;
     uint4 qx[2][NKS];
-    if constexpr (sizeof(TI) == 2) {
+    if constexpr (SC) {
         const TI *qg = (const TI *)a.q + (size_t)bh * a.ld * DK;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -188,7 +192,7 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
         if (j == 1 && !job1) break;
         const int rb = j ? jrb1 : wv, p = j;
         typename MF::frag qf[NKS];
-        if constexpr (sizeof(TI) == 2) {
+        if constexpr (SC) {
             // bf16 -> fp16 with the packed round-toward-zero conversion (exact for
             // every bf16 value in fp16's normal range); rows past L are zero
             const bool valid = t0 + rb * 16 + n < L;
@@ -213,7 +217,7 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
             for (int ks = 0; ks < NKS; ++ks) {
                 const typename MF::frag kb = ld_frag<TM>(&Ks[(sb * 16 + n) * KP + g * (DK / 4) + ks * E]);
                 d = MF::mma(ld_frag<TM>(&Ks[(rb * 16 + n) * KP + g * (DK / 4) + ks * E]), kb, d);
-                if constexpr (sizeof(TI) == 2) e4 = MF::mma(kb, qf[ks], e4);
+                if constexpr (SC) e4 = MF::mma(kb, qf[ks], e4);
             }
             {
                 const int s = sb * 16 + n;
@@ -223,7 +227,7 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
                     Pm[r * TP + s] = (s < r) ? Bs[r] * __expf(Gs[r] - Gs[s]) * d[e] : 0.f;
                 }
             }
-            if constexpr (sizeof(TI) == 2) {
+            if constexpr (SC) {
                 const int r = rb * 16 + n;
                 const float Gr = Gs[r];
                 if (sb == rb) {
@@ -240,7 +244,7 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
                 }
             }
         }
-        if constexpr (sizeof(TI) == 2) {
+        if constexpr (SC) {
             const int f = rb + (rb > 2 ? rb - 2 : 0) + p;
             f16 *mo = (f16 *)a.mf + (((size_t)bh * a.nchunks + c) * 6 + f) * 512 + lane * 8;
             *reinterpret_cast<f16x8 *>(mo) = pack_tiles(ms[0], ms[1], 1.f);
@@ -314,6 +318,16 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
         To[r * OP + s] = from_f32<TM>((s >> 4) > (r >> 4) ? 0.f : Tm[r * TP + s]);
     }
     __syncthreads();  // T converted: region A (T in fp32) is free
+    if constexpr (BWD) {
+        // T row-major, [bh][chunk][C][C] in the operand type (16 bytes per piece)
+        constexpr int EP = 16 / (int)sizeof(TM);
+        TM *tout = (TM *)a.t + ((size_t)bh * a.nchunks + c) * C * C;
+#pragma unroll
+        for (int i = 0; i < C * C / EP / 256; ++i) {
+            const int idx = tid + 256 * i, r = idx / (C / EP), s0 = (idx % (C / EP)) * EP;
+            *reinterpret_cast<uint4 *>(tout + r * C + s0) = *reinterpret_cast<const uint4 *>(&To[r * OP + s0]);
+        }
+    }
 
     // Stage K transposed scaled by beta_s a_s (zero past the end of the
     // sequence, where beta is zero too).
@@ -367,7 +381,7 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
     __syncthreads();
 
     const int NJB = dv / 16;
-    if constexpr (sizeof(TI) == 2) {
+    if constexpr (SC) {
         // bf16 inputs: U~ in the accumulator layout of the serial pass
         // (gdn_fwd_impl.hpp), tiles D[r][j] = sum_s T[r][s] (beta V)[s][j]: lane
         // (g, n) holds rows r = rb*16 + 4g + e of column j = jb*16 + n, stored as

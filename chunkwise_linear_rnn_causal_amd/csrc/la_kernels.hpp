@@ -31,6 +31,7 @@ struct PrepArgs {
     const void *q, *k, *v;      // [BH, L, DK], [BH, L, DK], [BH, L, dv] (q: bf16 inputs only)
     const float *lg, *beta;     // [BH, L] (lg may be nullptr)
     void *w, *ut, *mf;          // outputs, layouts as in ChunkArgs (mf: bf16 inputs only)
+    void *t;                    // backward preparation only: T = (I + P)^-1 [BH, nchunks, C, C]
     int BH, L, Lp, dv, nchunks;
     int ld;                     // rows between consecutive heads of k, v and the gates (>= L)
 };
@@ -72,7 +73,16 @@ struct BwdArgs {
     void *hs, *dhs;                // workspace: per-chunk states / state gradients [BH, nchunks, DK, dv] (operand type)
     float *s_last;                 // workspace: final state [BH, DK, dv]
     float *rterm;                  // workspace: q . dq - k . dk per token [BH, L]
+                                   // (gated delta rule: q . dq - v . dv)
     int BH, L, dv, nsplit;
+    // gated delta rule only (gdn_bwd_impl.hpp); operand-type (fp16) workspace arrays
+    const float *beta;             // [BH, L]
+    float *gbeta;                  // gradient of beta [BH, L] or nullptr
+    void *w;                       // W [BH, Lp, DK]
+    void *u;                       // U~ [BH, Lp, dv], overwritten with U by the forward scan
+    void *du;                      // A_m^T dO [BH, Lp, dv], overwritten with dU by the reverse scan
+    void *t;                       // T [BH, nchunks, C, C]
+    int Lp, nchunks;
 };
 
 // TI: input type (bf16 or float); TO: output type (float or bf16); DVT: value
@@ -102,6 +112,12 @@ template <typename T> constexpr int conv_tile() { return sizeof(T) == 2 ? 8 : 4;
 
 template <typename TI, int DK, int DV, bool DECAY>
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t st);
+
+// Backward pass of the gated delta rule, bf16 inputs (C = 64): preparation,
+// A_m^T dO, the forward and reverse state scans, the per-chunk gradients and the
+// log-gate gradient (gdn_bwd_impl.hpp).
+template <int DK, int DV>
+hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
 
 template <typename T, int K>
 hipError_t launch_short_conv(const ConvArgs &a, unsigned blocks, hipStream_t st);

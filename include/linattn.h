@@ -76,7 +76,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 1
+#define LA_ABI_VERSION 2
 
 typedef enum la_status {
     LA_OK = 0,
@@ -220,37 +220,45 @@ la_status la_short_conv(la_dtype dt, const void *q, const void *k, const void *v
 
 /*
  * Backward pass of la_chunk_fwd (training): gradients of a scalar loss with
- * respect to q, k, v, the log-gates and the initial state, given d_o =
+ * respect to q, k, v, the log-gates, beta and the initial state, given d_o =
  * dLoss/do and optionally d_state_out = dLoss/d(final state). Reverse-mode of
- * the recurrence above, in its chunk form (tensorplay section 3.2). The forward
+ * the recurrence above, in its chunk form (tensorplay section 3.2; for the
+ * delta rule the WY / UT chunk form of tensorplay section 6.2). The forward
  * states are recomputed from q, k, v, one per chunk, into the workspace, as in
  * the materialized form of tensorplay section 4.1.2 (per-chunk states stored,
  * recomputed for back-propagation instead of kept from the forward). With G
- * the cumulative log-gate the loss sees only differences G_r - G_s and G_L, so
- * d_log_gate_t = sum_{u>=t} (q_u . dq_u - k_u . dk_u) + <d_state_out, S_L>.
- *   var          LA_PLAIN or LA_DECAY (others: LA_ERR_UNSUPPORTED).
+ * the cumulative log-gate, the loss sees the gates only through
+ * q_t e^{G_t}, k_t e^{-G_t} (LA_GATED_DELTA: v_t e^{-G_t}) and e^{G_L}, so
+ * d_log_gate_t = sum_{u>=t} (q_u . dq_u - k_u . dk_u) + <d_state_out, S_L>
+ * (LA_GATED_DELTA: q_u . dq_u - v_u . dv_u).
+ *   var          LA_PLAIN, LA_DECAY, or LA_GATED_DELTA with dt = LA_BF16
+ *                (others: LA_ERR_UNSUPPORTED).
  *   dt           dtype of q, k, v and d_o (LA_BF16 or LA_F32); every gradient
  *                is float32.
- *   q, k, v, log_gate, state_in   as given to la_chunk_fwd.
+ *   q, k, v, log_gate, beta, state_in   as given to la_chunk_fwd (beta:
+ *                LA_GATED_DELTA only, required when L > 0; log_gate optional
+ *                there, NULL = DeltaNet).
  *   d_o          [B,H,L,d_v] in dt, required when L > 0.
  *   d_state_out  [B,H,d_k,d_v] float32 or NULL (zero).
  *   dq, dk       [B,H,L,d_k] float32; dv [B,H,L,d_v] float32; required when L > 0.
- *   d_log_gate   [B,H,L] float32 (LA_DECAY only) or NULL (not computed).
+ *   d_log_gate   [B,H,L] float32 or NULL (not computed); only with a log_gate.
+ *   d_beta       [B,H,L] float32 or NULL (not computed); LA_GATED_DELTA only.
  *   d_state_in   [B,H,d_k,d_v] float32 or NULL (not written).
  *   C            64. d_k, d_v in {32, 64, 128}.
  *   workspace    at least la_chunk_bwd_workspace_size() bytes, 256-byte aligned:
  *                per-chunk states and state gradients (operand precision), the
- *                final state and one float per token.
+ *                final state and one float per token; for LA_GATED_DELTA also
+ *                W, U~, A_m^T d_o (later U and dU) and T per chunk, in fp16.
  * Outputs and the workspace must not overlap any input or each other.
  */
 la_status la_chunk_bwd_workspace_size(la_variant var, la_dtype dt, int B, int H, int L,
                                       int d_k, int d_v, int C, size_t *bytes);
 la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k,
-                       const void *v, const float *log_gate, const float *state_in,
-                       const void *d_o, const float *d_state_out, float *dq, float *dk,
-                       float *dv, float *d_log_gate, float *d_state_in, int B, int H, int L,
-                       int d_k, int d_v, int C, void *workspace, size_t workspace_bytes,
-                       void *stream);
+                       const void *v, const float *log_gate, const float *beta,
+                       const float *state_in, const void *d_o, const float *d_state_out,
+                       float *dq, float *dk, float *dv, float *d_log_gate, float *d_beta,
+                       float *d_state_in, int B, int H, int L, int d_k, int d_v, int C,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * la_chunk_fwd without a workspace argument, for callers that cannot allocate

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.la_abi_version() == 1
+    assert la.la_abi_version() == 2
     assert la.la_status_str(0) == "LA_OK"
     assert la.la_status_str(1) == "LA_ERR_INVALID_ARG"
     assert la.la_status_str(2) == "LA_ERR_UNSUPPORTED"
@@ -177,11 +177,11 @@ def test_short_conv_valid_arguments_reach_the_device_check(kw):
     assert conv(**kw) not in (INVALID,)
 
 
-def bwd(var=DECAY, dt=BF16, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lg=FAKE + 0x300000, s_in=None,
-        do=FAKE + 0x400000, dso=None, dq=0x800000000, dk=0x810000000, dv=0x820000000, dlg=None, dsi=None,
-        B=1, H=2, L=128, dk_=64, dv_=64, C=64, ws=0x900000000, ws_bytes=1 << 30):
-    return la.load_library().la_chunk_bwd(var, dt, q, k, v, lg, s_in, do, dso, dq, dk, dv, dlg, dsi, B, H, L,
-                                          dk_, dv_, C, ws, ws_bytes, None)
+def bwd(var=DECAY, dt=BF16, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lg=FAKE + 0x300000, beta=None,
+        s_in=None, do=FAKE + 0x400000, dso=None, dq=0x800000000, dk=0x810000000, dv=0x820000000, dlg=None,
+        dbeta=None, dsi=None, B=1, H=2, L=128, dk_=64, dv_=64, C=64, ws=0x900000000, ws_bytes=1 << 30):
+    return la.load_library().la_chunk_bwd(var, dt, q, k, v, lg, beta, s_in, do, dso, dq, dk, dv, dlg, dbeta,
+                                          dsi, B, H, L, dk_, dv_, C, ws, ws_bytes, None)
 
 
 def bwd_wsize(var=DECAY, dt=BF16, B=2, H=3, L=100, dk_=64, dv_=32, C=64):
@@ -196,7 +196,11 @@ def test_bwd_workspace_size():
     r = lambda x: -(-x // 256) * 256
     states = r(6 * 2 * 64 * 32 * 2)
     assert st == 0 and n == 2 * states + r(6 * 64 * 32 * 4) + r(6 * 100 * 4)
-    assert bwd_wsize(var=GDN)[0] == UNSUPPORTED
+    # delta rule (bf16 only): also W [BH, Lp, dk], U~ and A_m^T dO [BH, Lp, dv] and T [BH, nch, 64, 64], fp16
+    st, n = bwd_wsize(var=GDN)
+    assert st == 0 and n == (2 * states + r(6 * 64 * 32 * 4) + r(6 * 100 * 4) + r(6 * 128 * 64 * 2)
+                             + 2 * r(6 * 128 * 32 * 2) + r(6 * 2 * 64 * 64 * 2))
+    assert bwd_wsize(var=GDN, dt=F32)[0] == UNSUPPORTED
     assert bwd_wsize(C=128)[0] == UNSUPPORTED
     assert bwd_wsize(dt=F32, dk_=128, dv_=128)[0] == UNSUPPORTED
     assert bwd_wsize(dt=F32, dk_=128, dv_=32)[0] == 0
@@ -215,6 +219,13 @@ def test_bwd_workspace_size():
     (dict(dk=0x800000000 + 0x1000), INVALID),           # dk inside dq
     (dict(dsi=0x900000000 + 0x100), INVALID),           # d_state_in inside the workspace
     (dict(q=FAKE + 4), INVALID),
+    (dict(beta=FAKE + 0x500000), INVALID),              # beta is the delta rule's
+    (dict(dbeta=0x830000000), INVALID),
+    (dict(var=GDN), INVALID),                           # the delta rule needs beta
+    (dict(var=GDN, dt=F32, beta=FAKE + 0x500000), UNSUPPORTED),
+    (dict(var=GDN, lg=None, beta=FAKE + 0x500000, dlg=0x830000000), INVALID),  # no gates, no gate gradient
+    (dict(var=GDN, beta=FAKE + 0x500000, dbeta=FAKE + 0x500000 + 0x40), INVALID),  # d_beta inside beta
+    (dict(var=GDN, beta=FAKE + 0x500008), INVALID),     # misaligned beta
 ])
 def test_chunk_bwd_rejects(kw, expect):
     assert bwd(**kw) == expect
@@ -224,3 +235,5 @@ def test_chunk_bwd_valid_arguments_reach_the_device_check():
     assert bwd() not in (INVALID, UNSUPPORTED)
     assert bwd(var=PLAIN, lg=None) not in (INVALID, UNSUPPORTED)
     assert bwd(L=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None) not in (INVALID, UNSUPPORTED)
+    assert bwd(var=GDN, beta=FAKE + 0x500000, dbeta=0x830000000, dlg=0x840000000) not in (INVALID, UNSUPPORTED)
+    assert bwd(var=GDN, lg=None, beta=FAKE + 0x500000) not in (INVALID, UNSUPPORTED)

@@ -64,6 +64,10 @@ CONFIGS: Dict[str, dict] = {
     "decay_bwd_bf16_b4h32_l8192_d128": dict(
         kind="bwd", variant="decay", dtype="bf16", B=4, H=32, L=8192, dk=128, dv=128, C=64,
         recipe="gauss_scaled_gate"),
+    # the backward pass of the delta-rule workload (output gradient dO ~ N(0, 1))
+    "gated_delta_bwd_bf16_b2h16_l8192_d128": dict(
+        kind="bwd", variant="gated_delta", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, C=64,
+        recipe="gdn"),
     # the short convolution in front of the delta rule, at that workload's q, k, v shapes
     "short_conv_qkv_bf16_b2h16_l8192_d128_k4": dict(
         kind="conv", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, K=4, recipe="conv"),
