@@ -56,6 +56,10 @@ namespace gdnb {
 
 constexpr int C = 64;
 
+// 16 bytes as a native vector (copies of HIP's uint4 struct can become memory
+// copies that keep a register array in scratch)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // Operand fragment with the "natural" K-slot map: slot e of lane group g holds
 // k0 + 8g + e (one 16-byte read of a row whose K index runs along it).
 template <int P> __device__ inline f16x8 nat_frag(const f16 *X, int row, int k0, int g) {
@@ -74,26 +78,24 @@ template <int P> __device__ inline f16x8 col_frag(const f16 *X, int k0, int col0
     return tr_frag<P>(X, k0 + 4 * ((lane >> 4) & 3), col0, lane);
 }
 
-__device__ inline uint4 bf16x8_to_f16x8(uint4 w) {
+__device__ inline u32x4 bf16x8_to_f16x8(u32x4 w) {
     // packed round-toward-zero conversion: exact for bf16 values in fp16's
     // normal range; below it the error stays under 2^-24
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-    uint32_t h[4];
+    u32x4 h;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        h[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(u[i]), bf16_hi(u[i])));
-    return make_uint4(h[0], h[1], h[2], h[3]);
+        h[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w[i]), bf16_hi(w[i])));
+    return h;
 }
 // eight bf16 values times f, rounded to fp16
-__device__ inline uint4 bf16x8_scaled_f16(uint4 w, float f) {
-    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-    uint32_t h[4];
+__device__ inline u32x4 bf16x8_scaled_f16(u32x4 w, float f) {
+    u32x4 h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const f16 lo = (f16)(bf16_lo(u[i]) * f), hi = (f16)(bf16_hi(u[i]) * f);
+        const f16 lo = (f16)(bf16_lo(w[i]) * f), hi = (f16)(bf16_hi(w[i]) * f);
         h[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
-    return make_uint4(h[0], h[1], h[2], h[3]);
+    return h;
 }
 
 // sum over the 16 lanes of a lane group (n = 0..15)
@@ -110,35 +112,35 @@ __device__ inline float group16_sum(float x) {
 template <int D, int P, int NT>
 __device__ inline void stage_bf16(f16 *dst, const bf16 *src, int t0, int L, int tid) {
     constexpr int SEG = D / 8, TOT = C * SEG, N = (TOT + NT - 1) / NT;
-    uint4 r[N];
+    u32x4 r[N];
 #pragma unroll
     for (int m = 0; m < N; ++m) {
         const int idx = tid + NT * m, row = idx / SEG, seg = idx % SEG;
         if (TOT % NT == 0 || idx < TOT)
-            r[m] = *reinterpret_cast<const uint4 *>(src + (size_t)min(t0 + row, L - 1) * D + seg * 8);
+            r[m] = *reinterpret_cast<const u32x4 *>(src + (size_t)min(t0 + row, L - 1) * D + seg * 8);
     }
 #pragma unroll
     for (int m = 0; m < N; ++m) {
         const int idx = tid + NT * m, row = idx / SEG, seg = idx % SEG;
         if (TOT % NT == 0 || idx < TOT)
-            *reinterpret_cast<uint4 *>(dst + row * P + seg * 8) =
-                t0 + row < L ? bf16x8_to_f16x8(r[m]) : make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<u32x4 *>(dst + row * P + seg * 8) =
+                t0 + row < L ? bf16x8_to_f16x8(r[m]) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 // C rows of an fp16 [.][D] array (row stride D) into an LDS tile of pitch P.
 template <int D, int P, int NT>
 __device__ inline void stage_f16(f16 *dst, const f16 *src, int tid) {
     constexpr int SEG = D / 8, TOT = C * SEG, N = (TOT + NT - 1) / NT;
-    uint4 r[N];
+    u32x4 r[N];
 #pragma unroll
     for (int m = 0; m < N; ++m) {
         const int idx = tid + NT * m, row = idx / SEG, seg = idx % SEG;
-        if (TOT % NT == 0 || idx < TOT) r[m] = *reinterpret_cast<const uint4 *>(src + (size_t)row * D + seg * 8);
+        if (TOT % NT == 0 || idx < TOT) r[m] = *reinterpret_cast<const u32x4 *>(src + (size_t)row * D + seg * 8);
     }
 #pragma unroll
     for (int m = 0; m < N; ++m) {
         const int idx = tid + NT * m, row = idx / SEG, seg = idx % SEG;
-        if (TOT % NT == 0 || idx < TOT) *reinterpret_cast<uint4 *>(dst + row * P + seg * 8) = r[m];
+        if (TOT % NT == 0 || idx < TOT) *reinterpret_cast<u32x4 *>(dst + row * P + seg * 8) = r[m];
     }
 }
 
@@ -206,7 +208,10 @@ __global__ void __launch_bounds__(256) gdn_bwd_dut_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // The two serial scans. Workgroup b < BH * NS runs the forward scan of head
-// b / NS, value columns [32 (b % NS), +32); the others the reverse scan.
+// b / NS, value columns [32 (b % NS), +32); the others the reverse scan. Eight
+// waves: waves 0-3 run the serial chain (the Z and X products), waves 4-7 store
+// X and Z to the workspace and stage the next chunk (loads one chunk ahead), so
+// the chain does not wait on memory. Two barriers per chunk.
 template <int DK, int DV>
 struct GdnScanCfg {
     static constexpr int DVT = 32, NS = DV / DVT;
@@ -215,196 +220,238 @@ struct GdnScanCfg {
     static constexpr int OW = 0, OK = C * KP, OQ = 2 * C * KP, OY = 3 * C * KP, OO = OY + C * YP,
                          SET = OO + C * YP;
     static constexpr int XS = 2 * SET, ZS = XS + DK * XP, TOTAL = ZS + C * YP;  // fp16 elements
-    static constexpr int NKL = C * DK / 8 / 256;  // 16-byte loads per thread per C x DK tile
-    static_assert(NKL >= 1 && NKL * 256 * 8 == gdnb::C * DK, "scan staging geometry");
+    static constexpr int NKL = C * DK / 8 / 256;  // 16-byte loads per staging thread per C x DK tile
+    static_assert(NKL >= 1 && NKL * 256 * 8 == C * DK, "scan staging geometry");
 };
 
-template <int DK, int DV>
-__global__ void __launch_bounds__(256) gdn_bwd_scan_kernel(BwdArgs a) {
+template <int DK, int DV, bool REV>
+__device__ __attribute__((always_inline)) inline void gdn_scan(const BwdArgs &a, int b, f16 *lds, float *Eg) {
     using namespace gdnb;
     using MF = Mfma<f16>;
     using Cfg = GdnScanCfg<DK, DV>;
     constexpr int DVT = Cfg::DVT, NS = Cfg::NS, KP = Cfg::KP, YP = Cfg::YP, XP = Cfg::XP;
     constexpr int NKL = Cfg::NKL, SEGK = DK / 8, SEGY = DVT / 8;
-    constexpr int NTI = DK / 16;  // state row tiles; the slice has 2 column tiles
-    __shared__ __attribute__((aligned(16))) f16 lds[Cfg::TOTAL];
-    __shared__ float Eg[2];
-
+    constexpr int NTI = DK / 16, RT = (NTI + 3) / 4;  // state row tiles; per chain wave
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
-    const bool rev = blockIdx.x >= a.BH * NS;
-    const int b = rev ? blockIdx.x - a.BH * NS : blockIdx.x;
     const int bh = b / NS, j0 = (b % NS) * DVT;
     const int L = a.L, nch = a.nchunks;
-    const bf16 *kg = (const bf16 *)a.k + (size_t)bh * L * DK;
-    const bf16 *qg = (const bf16 *)a.q + (size_t)bh * L * DK;
-    const bf16 *og = (const bf16 *)a.dout + (size_t)bh * L * DV + j0;
-    const f16 *wg = (const f16 *)a.w + (size_t)bh * a.Lp * DK;
-    f16 *yg = (f16 *)(rev ? a.du : a.u) + (size_t)bh * a.Lp * DV + j0;
-    f16 *xg = (f16 *)(rev ? a.dhs : a.hs) + (size_t)bh * nch * DK * DV + j0;
-    const float *lgg = a.lg ? a.lg + (size_t)bh * L : nullptr;
+    f16 *yg = (f16 *)(REV ? a.du : a.u) + (size_t)bh * a.Lp * DV + j0;
+    f16 *xg = (f16 *)(REV ? a.dhs : a.hs) + (size_t)bh * nch * DK * DV + j0;
     f16 *Xs = lds + Cfg::XS, *Zs = lds + Cfg::ZS;
 
-    // X: tiles (ti, tj) = (wv + 4m) / 2, % 2 in fp32 accumulators; lane holds
-    // rows i = 16 ti + 4g + e, column j = 16 tj + n of the slice
-    constexpr int TPW = NTI * 2 / 4;
-    f32x4 X[TPW];
-    {
-        const float *x0 = rev ? a.ds_out : a.s_in;
+    if (wv < 4) {
+        // ===== chain waves: X row tiles wv + 4m, both 16-column tiles; lane holds
+        // rows i = 16 ti + 4g + e, column j = 16 tj + n of the slice
+        f32x4 X[RT][2];
+        const float *x0 = REV ? a.ds_out : a.s_in;
 #pragma unroll
-        for (int m = 0; m < TPW; ++m) {
-            const int tile = wv + 4 * m, ti = tile >> 1, tj = tile & 1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                X[m][e] = x0 ? x0[(size_t)bh * DK * DV + (size_t)(ti * 16 + 4 * g + e) * DV + j0 + tj * 16 + n] : 0.f;
-        }
-    }
-    auto write_x = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int m = 0; m < TPW; ++m) {
-            const int tile = wv + 4 * m, ti = tile >> 1, tj = tile & 1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Xs[(ti * 16 + 4 * g + e) * XP + tj * 16 + n] = (f16)X[m][e];
-        }
-    };
-    write_x();
-
-    // prefetch registers of one chunk: W and K rows (NKL each), Y~ (one), and
-    // for the reverse scan Q rows (NKL) and dO (one); the chunk's log-gates
-    uint4 pw[NKL], pk[NKL], pq[NKL], py, po;
-    float pl;
-    auto load = [&](int c) __attribute__((always_inline)) {
-        const int t0 = c * C;
-#pragma unroll
-        for (int m = 0; m < NKL; ++m) {
-            const int idx = tid + 256 * m, row = idx / SEGK, seg = idx % SEGK;
-            pw[m] = *reinterpret_cast<const uint4 *>(wg + (size_t)(t0 + row) * DK + seg * 8);
-            pk[m] = *reinterpret_cast<const uint4 *>(kg + (size_t)min(t0 + row, L - 1) * DK + seg * 8);
-            if (rev) pq[m] = *reinterpret_cast<const uint4 *>(qg + (size_t)min(t0 + row, L - 1) * DK + seg * 8);
-        }
-        {
-            const int row = tid / SEGY, seg = tid % SEGY;
-            py = *reinterpret_cast<const uint4 *>(yg + (size_t)(t0 + row) * DV + seg * 8);
-            if (rev) po = *reinterpret_cast<const uint4 *>(og + (size_t)min(t0 + row, L - 1) * DV + seg * 8);
-        }
-        pl = (lgg && t0 + lane < L) ? lgg[t0 + lane] : 0.f;
-    };
-    auto stage = [&](int c, int buf) __attribute__((always_inline)) {
-        f16 *S = lds + buf * Cfg::SET;
-        const int t0 = c * C;
-        const float G = wave_inclusive_sum(pl);
-        const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
-#pragma unroll
-        for (int m = 0; m < NKL; ++m) {
-            const int idx = tid + 256 * m, row = idx / SEGK, seg = idx % SEGK;
-            const float Gr = __shfl(G, row, 64);
-            const bool valid = t0 + row < L;
-            *reinterpret_cast<uint4 *>(S + Cfg::OW + row * KP + seg * 8) = pw[m];
-            *reinterpret_cast<uint4 *>(S + Cfg::OK + row * KP + seg * 8) =
-                valid ? bf16x8_scaled_f16(pk[m], __expf(gC - Gr)) : make_uint4(0u, 0u, 0u, 0u);
-            if (rev)
-                *reinterpret_cast<uint4 *>(S + Cfg::OQ + row * KP + seg * 8) =
-                    valid ? bf16x8_scaled_f16(pq[m], __expf(Gr)) : make_uint4(0u, 0u, 0u, 0u);
-        }
-        {
-            const int row = tid / SEGY, seg = tid % SEGY;
-            *reinterpret_cast<uint4 *>(S + Cfg::OY + row * YP + seg * 8) = py;
-            if (rev)
-                *reinterpret_cast<uint4 *>(S + Cfg::OO + row * YP + seg * 8) =
-                    t0 + row < L ? bf16x8_to_f16x8(po) : make_uint4(0u, 0u, 0u, 0u);
-        }
-        if (tid == 0) Eg[buf] = __expf(gC);
-    };
-
-    if (nch > 0) {
-        load(rev ? nch - 1 : 0);
-        stage(rev ? nch - 1 : 0, 0);
-        if (nch > 1) load(rev ? nch - 2 : 1);
-    }
-    __syncthreads();
-    for (int i = 0; i < nch; ++i) {
-        const int buf = i & 1, c = rev ? nch - 1 - i : i;
-        const f16 *S = lds + buf * Cfg::SET;
-        // (1) X (S before chunk c, or dS after it) to the workspace
-#pragma unroll
-        for (int m = 0; m < (DK * SEGY + 255) / 256; ++m) {
-            const int idx = tid + 256 * m, row = idx / SEGY, seg = idx % SEGY;
-            if (idx < DK * SEGY)
-                *reinterpret_cast<uint4 *>(xg + ((size_t)c * DK + row) * DV + seg * 8) =
-                    *reinterpret_cast<const uint4 *>(Xs + row * XP + seg * 8);
-        }
-        // (2) Z = Y~ + sigma N X: row block wv, both column tiles
-        {
-            const f16 *N = S + (rev ? Cfg::OK : Cfg::OW);
-            f32x4 z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int ks = 0; ks < DK / 32; ++ks) {
-                const f16x8 nf = pair_frag<KP>(N, wv * 16 + n, ks * 32, g);
-#pragma unroll
-                for (int tj = 0; tj < 2; ++tj) z[tj] = MF::mma(nf, col_frag<XP>(Xs, ks * 32, tj * 16, lane), z[tj]);
-            }
-            // D layout: rows r = 16 wv + 4g + e, column j = 16 tj + n
+        for (int m = 0; m < RT; ++m) {
+            const int ti = wv + 4 * m;
 #pragma unroll
             for (int tj = 0; tj < 2; ++tj) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = wv * 16 + 4 * g + e, j = tj * 16 + n;
-                    const float y = (float)S[Cfg::OY + r * YP + j];
-                    Zs[r * YP + j] = (f16)(rev ? y + z[tj][e] : y - z[tj][e]);
-                }
+                for (int e = 0; e < 4; ++e)
+                    X[m][tj][e] = (x0 && ti < NTI)
+                        ? x0[(size_t)bh * DK * DV + (size_t)(ti * 16 + 4 * g + e) * DV + j0 + tj * 16 + n] : 0.f;
             }
         }
-        __syncthreads();
-        // (3) Z (U or dU) to the workspace, over Y~
-        {
-            const int row = tid / SEGY, seg = tid % SEGY;
-            *reinterpret_cast<uint4 *>(yg + (size_t)(c * C + row) * DV + seg * 8) =
-                *reinterpret_cast<const uint4 *>(Zs + row * YP + seg * 8);
-        }
-        // (4) X' = a_C X + M^T Z (+ Q^^T dO)
-        {
-            const float eg = Eg[buf];
-            const f16 *M = S + (rev ? Cfg::OW : Cfg::OK);
+        auto write_x = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int m = 0; m < TPW; ++m) X[m] *= eg;
+            for (int m = 0; m < RT; ++m) {
+                const int ti = wv + 4 * m;
+                if (NTI % 4 != 0 && ti >= NTI) continue;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const f16x8 zf[2] = {col_frag<YP>(Zs, kk * 32, 0, lane), col_frag<YP>(Zs, kk * 32, 16, lane)};
-                f16x8 of[2];
-                if (rev) {
-                    of[0] = col_frag<YP>(S + Cfg::OO, kk * 32, 0, lane);
-                    of[1] = col_frag<YP>(S + Cfg::OO, kk * 32, 16, lane);
-                }
+                for (int tj = 0; tj < 2; ++tj) {
 #pragma unroll
-                for (int m = 0; m < TPW; ++m) {
-                    const int tile = wv + 4 * m, ti = tile >> 1, tj = tile & 1;
-                    f16x8 mf = col_frag<KP>(M, kk * 32, ti * 16, lane);
-                    if (rev) {
-                        mf = neg_frag<f16>(mf);
-                        X[m] = MF::mma(col_frag<KP>(S + Cfg::OQ, kk * 32, ti * 16, lane), of[tj], X[m]);
-                    }
-                    X[m] = MF::mma(mf, zf[tj], X[m]);
+                    for (int e = 0; e < 4; ++e) Xs[(ti * 16 + 4 * g + e) * XP + tj * 16 + n] = (f16)X[m][tj][e];
                 }
             }
-        }
+        };
         write_x();
-        // (5) stage the next chunk, then load the one after it
-        if (i + 1 < nch) {
-            stage(rev ? c - 1 : c + 1, buf ^ 1);
-            if (i + 2 < nch) load(rev ? c - 2 : c + 2);
-        }
-        __syncthreads();
-    }
-    // final X: the forward scan's S_L, the reverse scan's dS_0
-    float *xo = rev ? a.gs_in : a.s_last;
-    if (xo) {
+        __syncthreads();  // prologue
+        for (int i = 0; i < nch; ++i) {
+            const f16 *S = lds + (i & 1) * Cfg::SET;
+            // Z = Y~ + sigma N X, row block wv
+            {
+                const f16 *N = S + (REV ? Cfg::OK : Cfg::OW);
+                f32x4 z[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                f16x8 nf[DK / 32], xf[DK / 32][2];
 #pragma unroll
-        for (int m = 0; m < TPW; ++m) {
-            const int tile = wv + 4 * m, ti = tile >> 1, tj = tile & 1;
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    nf[ks] = pair_frag<KP>(N, wv * 16 + n, ks * 32, g);
+                    xf[ks][0] = col_frag<XP>(Xs, ks * 32, 0, lane);
+                    xf[ks][1] = col_frag<XP>(Xs, ks * 32, 16, lane);
+                }
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                xo[(size_t)bh * DK * DV + (size_t)(ti * 16 + 4 * g + e) * DV + j0 + tj * 16 + n] = X[m][e];
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    z[0] = MF::mma(nf[ks], xf[ks][0], z[0]);
+                    z[1] = MF::mma(nf[ks], xf[ks][1], z[1]);
+                }
+#pragma unroll
+                for (int tj = 0; tj < 2; ++tj) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = wv * 16 + 4 * g + e, j = tj * 16 + n;
+                        const float y = (float)S[Cfg::OY + r * YP + j];
+                        Zs[r * YP + j] = (f16)(REV ? y + z[tj][e] : y - z[tj][e]);
+                    }
+                }
+            }
+            __syncthreads();
+            // X' = a_C X + M^T Z (+ Q^^T dO)
+            {
+                const float eg = Eg[i & 1];
+                const f16 *M = S + (REV ? Cfg::OW : Cfg::OK);
+#pragma unroll
+                for (int m = 0; m < RT; ++m) {
+                    X[m][0] *= eg;
+                    X[m][1] *= eg;
+                }
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const f16x8 z0 = col_frag<YP>(Zs, kk * 32, 0, lane), z1 = col_frag<YP>(Zs, kk * 32, 16, lane);
+                    f16x8 o0, o1;
+                    if constexpr (REV) {
+                        o0 = col_frag<YP>(S + Cfg::OO, kk * 32, 0, lane);
+                        o1 = col_frag<YP>(S + Cfg::OO, kk * 32, 16, lane);
+                    }
+#pragma unroll
+                    for (int m = 0; m < RT; ++m) {
+                        const int ti = wv + 4 * m;
+                        if (NTI % 4 != 0 && ti >= NTI) continue;
+                        f16x8 mf = col_frag<KP>(M, kk * 32, ti * 16, lane);
+                        if constexpr (REV) {
+                            mf = neg_frag<f16>(mf);
+                            const f16x8 qf = col_frag<KP>(S + Cfg::OQ, kk * 32, ti * 16, lane);
+                            X[m][0] = MF::mma(qf, o0, X[m][0]);
+                            X[m][1] = MF::mma(qf, o1, X[m][1]);
+                        }
+                        X[m][0] = MF::mma(mf, z0, X[m][0]);
+                        X[m][1] = MF::mma(mf, z1, X[m][1]);
+                    }
+                }
+            }
+            write_x();
+            __syncthreads();
+        }
+        // final X: the forward scan's S_L, the reverse scan's dS_0
+        float *xo = REV ? a.gs_in : a.s_last;
+        if (xo) {
+#pragma unroll
+            for (int m = 0; m < RT; ++m) {
+                const int ti = wv + 4 * m;
+                if (ti >= NTI) continue;
+#pragma unroll
+                for (int tj = 0; tj < 2; ++tj) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        xo[(size_t)bh * DK * DV + (size_t)(ti * 16 + 4 * g + e) * DV + j0 + tj * 16 + n] = X[m][tj][e];
+                }
+            }
+        }
+    } else {
+        // ===== staging waves (256 threads): loads one chunk ahead, staging,
+        // stores of X and Z
+        const int st = tid - 256;
+        const bf16 *kg = (const bf16 *)a.k + (size_t)bh * L * DK;
+        const bf16 *qg = (const bf16 *)a.q + (size_t)bh * L * DK;
+        const bf16 *og = (const bf16 *)a.dout + (size_t)bh * L * DV + j0;
+        const f16 *wg = (const f16 *)a.w + (size_t)bh * a.Lp * DK;
+        // Every load is unconditional and every masking an arithmetic select, so
+        // no branch separates a load from its use and the waits stay exact:
+        // without a gate the (finite) beta row is read and multiplied by zero.
+        const float *lgg = (a.lg ? a.lg : a.beta) + (size_t)bh * L;
+        const float lsc = a.lg ? 1.f : 0.f;
+        u32x4 pw[NKL], pk[NKL], pq[NKL], py, po;
+        float pl;
+        auto load = [&](int c) __attribute__((always_inline)) {
+            const int t0 = c * C;
+#pragma unroll
+            for (int m = 0; m < NKL; ++m) {
+                const int idx = st + 256 * m, row = idx / SEGK, seg = idx % SEGK;
+                pw[m] = *reinterpret_cast<const u32x4 *>(wg + (size_t)(t0 + row) * DK + seg * 8);
+                pk[m] = *reinterpret_cast<const u32x4 *>(kg + (size_t)min(t0 + row, L - 1) * DK + seg * 8);
+                if constexpr (REV)
+                    pq[m] = *reinterpret_cast<const u32x4 *>(qg + (size_t)min(t0 + row, L - 1) * DK + seg * 8);
+            }
+            {
+                const int row = st / SEGY, seg = st % SEGY;
+                py = *reinterpret_cast<const u32x4 *>(yg + (size_t)(t0 + row) * DV + seg * 8);
+                if constexpr (REV)
+                    po = *reinterpret_cast<const u32x4 *>(og + (size_t)min(t0 + row, L - 1) * DV + seg * 8);
+            }
+            pl = lgg[min(t0 + lane, L - 1)];
+        };
+        auto stage = [&](int c, int buf) __attribute__((always_inline)) {
+            f16 *S = lds + buf * Cfg::SET;
+            const int t0 = c * C;
+            const float G = wave_inclusive_sum(t0 + lane < L ? pl * lsc : 0.f);
+            const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
+#pragma unroll
+            for (int m = 0; m < NKL; ++m) {
+                const int idx = st + 256 * m, row = idx / SEGK, seg = idx % SEGK;
+                const float Gr = __shfl(G, row, 64);
+                const float vz = t0 + row < L ? 1.f : 0.f;  // rows past the end: zero
+                *reinterpret_cast<u32x4 *>(S + Cfg::OW + row * KP + seg * 8) = pw[m];
+                *reinterpret_cast<u32x4 *>(S + Cfg::OK + row * KP + seg * 8) =
+                    bf16x8_scaled_f16(pk[m], vz * __expf(gC - Gr));
+                if constexpr (REV)
+                    *reinterpret_cast<u32x4 *>(S + Cfg::OQ + row * KP + seg * 8) =
+                        bf16x8_scaled_f16(pq[m], vz * __expf(Gr));
+            }
+            {
+                const int row = st / SEGY, seg = st % SEGY;
+                *reinterpret_cast<u32x4 *>(S + Cfg::OY + row * YP + seg * 8) = py;
+                if constexpr (REV) {
+                    const uint32_t msk = t0 + row < L ? 0xffffffffu : 0u;
+                    *reinterpret_cast<u32x4 *>(S + Cfg::OO + row * YP + seg * 8) = bf16x8_to_f16x8(po) & msk;
+                }
+            }
+            if (st == 0) Eg[buf] = __expf(gC);
+        };
+        // chunk of step i; steps past the end repeat the last chunk, so the loads
+        // and the staging of the step after the last are unconditional (into the
+        // buffer no wave reads any more)
+        auto cidx = [&](int i) { i = min(i, nch - 1); return REV ? nch - 1 - i : i; };
+        if (nch > 0) {
+            load(cidx(0));
+            stage(cidx(0), 0);
+            load(cidx(1));
+        }
+        __syncthreads();  // prologue
+        for (int i = 0; i < nch; ++i) {
+            const int c = cidx(i);
+            // X (S before chunk c, or dS after it) to the workspace
+#pragma unroll
+            for (int m = 0; m < (DK * SEGY + 255) / 256; ++m) {
+                const int idx = st + 256 * m, row = idx / SEGY, seg = idx % SEGY;
+                if ((DK * SEGY) % 256 == 0 || idx < DK * SEGY)
+                    *reinterpret_cast<u32x4 *>(xg + ((size_t)c * DK + row) * DV + seg * 8) =
+                        *reinterpret_cast<const u32x4 *>(Xs + row * XP + seg * 8);
+            }
+            stage(cidx(i + 1), (i + 1) & 1);
+            load(cidx(i + 2));
+            __syncthreads();
+            // Z (U or dU) to the workspace, over Y~
+            {
+                const int row = st / SEGY, seg = st % SEGY;
+                *reinterpret_cast<u32x4 *>(yg + (size_t)(c * C + row) * DV + seg * 8) =
+                    *reinterpret_cast<const u32x4 *>(Zs + row * YP + seg * 8);
+            }
+            __syncthreads();
         }
     }
+}
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(512) gdn_bwd_scan_kernel(BwdArgs a) {
+    using Cfg = GdnScanCfg<DK, DV>;
+    __shared__ __attribute__((aligned(16))) f16 lds[Cfg::TOTAL];
+    __shared__ float Eg[2];
+    if (blockIdx.x < a.BH * Cfg::NS)
+        gdn_scan<DK, DV, false>(a, blockIdx.x, lds, Eg);
+    else
+        gdn_scan<DK, DV, true>(a, blockIdx.x - a.BH * Cfg::NS, lds, Eg);
 }
 
 // ---------------------------------------------------------------------------
@@ -657,7 +704,7 @@ hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st) {
         hipLaunchKernelGGL((gdn_prep_kernel<bf16, DK, 64, true>), dim3(a.BH * nch), dim3(256), 0, st, p);
         hipLaunchKernelGGL((gdn_bwd_dut_kernel<DK, DV>), dim3(a.BH * nch), dim3(256), 0, st, a);
     }
-    hipLaunchKernelGGL((gdn_bwd_scan_kernel<DK, DV>), dim3(2 * a.BH * Cfg::NS), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gdn_bwd_scan_kernel<DK, DV>), dim3(2 * a.BH * Cfg::NS), dim3(512), 0, st, a);
     if (nch > 0) {
         hipLaunchKernelGGL((gdn_bwd_grad_kernel<DK, DV>), dim3(a.BH * nch), dim3(512), 0, st, a);
     }
