@@ -844,6 +844,29 @@ def pin_backward_gate_identity(lib):
         assert _rel(dlg, ref) <= 1e-12, (variant, _rel(dlg, ref))
 
 
+def pin_backward_gdn_gate_identity(lib):
+    """Gated delta rule: in the variables S'_t = S_t e^{-G_t} the recurrence is
+    gate-free with queries q_t e^{G_t} and values v_t e^{-G_t}, and the final state
+    is e^{G_L} S'_L, so dl_t = sum_{u >= t} (q_u . dq_u - v_u . dv_u) + <dS_L, S_L>.
+    The gate of token t + 1 multiplies only S_t, so the same sum from any token t + 1
+    on is <dS_t, S_t> of the state after token t and its gradient: taking the state
+    after token 7 from a forward run over the first 8 tokens and its gradient from
+    the backward of the remaining tokens started from it."""
+    r = _rng(55)
+    q, k, v, do, lg, be, s0, dso = _gdn_bwd_case(r, L=17)
+    dq, dk, dv, dlg, dsi, dbe = oracle.backward("gated_delta", q, k, v, do, lg, s0, dso, lib=lib, beta=be)
+    _, sL, _ = oracle.forward("gated_delta", q, k, v, log_gate=lg, beta=be, state_in=s0, lib=lib)
+    per = (q * dq).sum(-1) - (v * dv).sum(-1)
+    ref = np.flip(np.cumsum(np.flip(per, 1), 1), 1) + (dso * sL).sum((-1, -2))[:, None]
+    assert _rel(dlg, ref) <= 1e-12, _rel(dlg, ref)
+    m = 8
+    _, s8, _ = oracle.forward("gated_delta", q[:, :m], k[:, :m], v[:, :m], log_gate=lg[:, :m], beta=be[:, :m],
+                              state_in=s0, lib=lib)
+    tail = oracle.backward("gated_delta", q[:, m:], k[:, m:], v[:, m:], do[:, m:], lg[:, m:], s8, dso, lib=lib,
+                           beta=be[:, m:])
+    assert _rel(dlg[:, m], (tail[4] * s8).sum((-1, -2))) <= 1e-12
+
+
 ALL_PINS = [
     pin_plain_quadratic, pin_plain_fraction_bruteforce, pin_plain_final_state,
     pin_normalized_quadratic, pin_normalized_constant_v, pin_normalized_hull,
@@ -858,5 +881,5 @@ ALL_PINS = [
     pin_vector_decay_parallel_form, pin_vector_decay_uniform_is_scalar, pin_vector_decay_fraction,
     pin_vector_decay_channel_isolation, pin_vector_decay_resume_and_decode,
     pin_backward_finite_differences, pin_backward_plain_closed_form, pin_backward_gate_identity,
-    pin_backward_gdn_finite_differences, pin_backward_gdn_reductions,
+    pin_backward_gdn_finite_differences, pin_backward_gdn_reductions, pin_backward_gdn_gate_identity,
 ]
