@@ -256,6 +256,60 @@ def bench_decode(name: str, steps: int, warmup: int, device, variant: str = "dec
                 N=N, H=H, d_k=dk, d_v=dv, decode_launches_per_step=nsteps)
 
 
+def bench_convfwd(name: str, steps: int, warmup: int, device) -> dict:
+    """The delta rule with the short convolution fused into its preparation
+    (la_chunk_fwd_conv), and, for comparison on the same inputs, the unfused
+    sequence la_short_conv then la_chunk_fwd (reported as unfused_ms_per_step)."""
+    import torch
+    import chunkwise_linear_rnn_causal_amd as la
+    c = W.CONFIGS[name]
+    B, H, L, dk, dv, K = c["B"], c["H"], c["L"], c["dk"], c["dv"], c["K"]
+    inp = W.make_chunk_inputs(c["variant"], c["dtype"], B, H, L, dk, dv, seed=0, recipe=c["recipe"])
+    taps = [to_dev(t, device) for t in W.make_conv_inputs(c["dtype"], 1, H, 1, dk, dv, K, seed=0).taps]
+    gc = dict(c, kind="chunk")
+    flop, nbytes, launched = chunk_work(gc)
+    flop += 2.0 * K * (2 * dk + dv) * B * H * L
+    copies = max(1, min(4, math.ceil(2 * CACHE_BYTES / launched)))
+    sets = []
+    for _ in range(copies):
+        st = dict(q=to_dev(inp.q, device), k=to_dev(inp.k, device), v=to_dev(inp.v, device),
+                  lg=to_dev(inp.log_gate, device), beta=to_dev(inp.beta, device))
+        st["o"] = torch.empty((B, H, L, dv), dtype=torch.float32, device=device)
+        st["S"] = torch.empty((B, H, dk, dv), dtype=torch.float32, device=device)
+        sets.append(st)
+    ws = torch.empty(la.la_chunk_fwd_conv_workspace_size(c["variant"], 1, B, H, L, dk, dv, c["C"], K),
+                     dtype=torch.uint8, device=device)
+    stream = torch.cuda.current_stream(device)
+
+    def step(i):
+        st = sets[i % copies]
+        la.la_chunk_fwd_conv(c["variant"], st["q"], st["k"], st["v"], *taps, st["lg"], st["beta"], C=c["C"],
+                             o=st["o"], state_out=st["S"], workspace=ws, stream=stream)
+
+    ms, wall_ms = time_steps(step, steps, warmup, stream)
+    # unfused: the standalone convolution into bf16 buffers, then the forward
+    ys = [torch.empty_like(sets[0][x]) for x in ("q", "k", "v")]
+    wsf = torch.empty(la.la_chunk_fwd_workspace_size(c["variant"], 1, B, H, L, dk, dv, c["C"]),
+                      dtype=torch.uint8, device=device)
+
+    def step_unfused(i):
+        st = sets[i % copies]
+        la.la_short_conv(st["q"], st["k"], st["v"], *taps, q_out=ys[0], k_out=ys[1], v_out=ys[2], stream=stream)
+        la.la_chunk_fwd(c["variant"], ys[0], ys[1], ys[2], st["lg"], st["beta"], C=c["C"], o=st["o"],
+                        state_out=st["S"], workspace=wsf, stream=stream)
+
+    ms_u, _ = time_steps(step_unfused, steps, warmup, stream)
+    t = ms / 1e3
+    toks = B * L
+    return dict(workload=name, variant="conv_" + c["variant"], tokens_per_s=toks / t, ms_per_step=t * 1e3,
+                wall_ms_per_step=wall_ms, unfused_ms_per_step=ms_u, flop=flop, bytes=nbytes,
+                bytes_as_launched=launched, output_dtype="f32",
+                achieved_gbs=nbytes / t / 1e9, achieved_tflops=flop / t / 1e12,
+                hbm_frac=nbytes / t / 1e9 / HBM_PEAK_GBS, mfma_frac=flop / t / 1e12 / MFMA_PEAK_TFLOPS,
+                roofline_frac=max(nbytes / (HBM_PEAK_GBS * 1e9), flop / (MFMA_PEAK_TFLOPS * 1e12)) / t,
+                input_copies=copies, B=B, H=H, L=L, d_k=dk, d_v=dv, C=c["C"], K=K)
+
+
 def bench_conv(name: str, steps: int, warmup: int, device) -> dict:
     import torch
     import chunkwise_linear_rnn_causal_amd as la
@@ -405,7 +459,8 @@ def main() -> int:
         print(f"[bench] {name}", file=sys.stderr, flush=True)
         steps = args.steps if kind != "decode" else max(1, min(args.steps, 5))
         warm = args.warmup if kind != "decode" else max(1, min(args.warmup, 2))
-        fn = {"chunk": bench_chunk, "decode": bench_decode, "conv": bench_conv, "bwd": bench_bwd}[kind]
+        fn = {"chunk": bench_chunk, "decode": bench_decode, "conv": bench_conv, "bwd": bench_bwd,
+              "convfwd": bench_convfwd}[kind]
         results[name] = fn(name, steps, warm, device)
         r = results[name]
         print(f"[bench] {name}: {r['ms_per_step']:.4f} ms/step, {r['achieved_gbs']:.0f} GB/s, "

@@ -24,6 +24,7 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
 VARIANTS = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3, "vector_decay": 4}
 EXPORTS = ("la_chunk_fwd_workspace_size", "la_chunk_fwd", "la_chunk_fwd_noalloc",
            "la_chunk_bwd_workspace_size", "la_chunk_bwd", "la_decode_step", "la_short_conv",
+           "la_chunk_fwd_conv", "la_chunk_fwd_conv_workspace_size",
            "la_status_str", "la_abi_version")
 
 _lib = None
@@ -64,6 +65,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_chunk_bwd.argtypes = [i, i, vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
                                  i, i, i, i, i, i, vp, sz, vp]
     lib.la_short_conv.restype = i
+    lib.la_chunk_fwd_conv_workspace_size.restype = i
+    lib.la_chunk_fwd_conv_workspace_size.argtypes = [i, i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.la_chunk_fwd_conv.restype = i
+    lib.la_chunk_fwd_conv.argtypes = [i, i, i, vp, vp, vp, fp, fp, fp, i, vp, vp, vp, vp, vp, vp, fp, fp, fp,
+                                      vp, fp, i, i, i, i, i, i, vp, sz, vp]
     lib.la_short_conv.argtypes = [i, vp, vp, vp, fp, fp, fp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   i, i, i, i, i, i, vp]
     _lib = lib
@@ -328,6 +334,79 @@ def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_sta
     return dq, dk, dv, dlg, dsi
 
 
+def la_chunk_fwd_conv_workspace_size(variant: str, dtype_code: int, B: int, H: int, L: int, d_k: int,
+                                     d_v: int, C: int = 64, K: int = 4) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().la_chunk_fwd_conv_workspace_size(VARIANTS[variant], dtype_code, B, H, L, d_k, d_v, C,
+                                                         K, ctypes.byref(out))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_chunk_fwd_conv_workspace_size")
+    return out.value
+
+
+def la_chunk_fwd_conv(variant: str, q, k, v, w_q, w_k, w_v, log_gate=None, beta=None, state_in=None, *,
+                      q_win_in=None, k_win_in=None, v_win_in=None, want_windows: bool = False,
+                      q_win_out=None, k_win_out=None, v_win_out=None, C: int = 64,
+                      want_state: bool = False, out_dtype=None, o=None, state_out=None, workspace=None,
+                      stream=None) -> Tuple:
+    """The gated delta rule's forward with the short convolution of q, k, v fused in
+    front (raw bf16 inputs; taps w_*: [H, d, K] fp32; windows [B, H, K-1, d] bf16).
+
+    Returns (o, state_out or None, (q_win, k_win, v_win) or None).
+    """
+    import torch
+    lib = load_library()
+    if variant not in VARIANTS:
+        raise ValueError(f"unknown variant {variant!r}")
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, L, d_k = q.shape
+    d_v = v.shape[-1]
+    K = w_q.shape[-1]
+    dt = _dt(q)
+    dev_, f32 = q.device, torch.float32
+    _check("k", k, (B, H, L, d_k), q.dtype, dev_, required=True)
+    _check("v", v, (B, H, L, d_v), q.dtype, dev_, required=True)
+    _check("w_q", w_q, (H, d_k, K), f32, dev_, required=True)
+    _check("w_k", w_k, (H, d_k, K), f32, dev_, required=True)
+    _check("w_v", w_v, (H, d_v, K), f32, dev_, required=True)
+    _check("log_gate", log_gate, (B, H, L), f32, dev_)
+    _check("beta", beta, (B, H, L), f32, dev_, required=L > 0)
+    _check("state_in", state_in, (B, H, d_k, d_v), f32, dev_)
+    for nm, x, d in (("q_win_in", q_win_in, d_k), ("k_win_in", k_win_in, d_k), ("v_win_in", v_win_in, d_v),
+                     ("q_win_out", q_win_out, d_k), ("k_win_out", k_win_out, d_k), ("v_win_out", v_win_out, d_v)):
+        _check(nm, x, (B, H, K - 1, d), q.dtype, dev_)
+    _check_device(dev_)
+    if o is None:
+        o = torch.empty((B, H, L, d_v), dtype=out_dtype if out_dtype is not None else torch.float32, device=dev_)
+    elif o.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("o must be float32 or bfloat16")
+    _check("o", o, (B, H, L, d_v), o.dtype, dev_)
+    s_out = state_out
+    if s_out is None and want_state:
+        s_out = torch.empty((B, H, d_k, d_v), dtype=f32, device=dev_)
+    _check("state_out", s_out, (B, H, d_k, d_v), f32, dev_)
+    if want_windows:
+        q_win_out = q_win_out if q_win_out is not None else torch.empty((B, H, K - 1, d_k), dtype=q.dtype, device=dev_)
+        k_win_out = k_win_out if k_win_out is not None else torch.empty((B, H, K - 1, d_k), dtype=q.dtype, device=dev_)
+        v_win_out = v_win_out if v_win_out is not None else torch.empty((B, H, K - 1, d_v), dtype=q.dtype, device=dev_)
+    if workspace is None:
+        ws_bytes = la_chunk_fwd_conv_workspace_size(variant, dt, B, H, L, d_k, d_v, C, K)
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev_)
+    elif workspace.device != dev_ or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.la_chunk_fwd_conv(VARIANTS[variant], dt, _dt(o), _ptr(q), _ptr(k), _ptr(v), _ptr(w_q), _ptr(w_k),
+                               _ptr(w_v), K, _ptr(q_win_in), _ptr(k_win_in), _ptr(v_win_in), _ptr(q_win_out),
+                               _ptr(k_win_out), _ptr(v_win_out), _ptr(log_gate), _ptr(beta), _ptr(state_in),
+                               _ptr(o), _ptr(s_out), B, H, L, d_k, d_v, C, _ptr(workspace), ws_bytes,
+                               _stream(dev_, stream))
+    if st != LA_OK:
+        raise LinAttnError(st, "la_chunk_fwd_conv")
+    wins = (q_win_out, k_win_out, v_win_out) if want_windows else None
+    return o, s_out, wins
+
+
 def la_short_conv(q=None, k=None, v=None, w_q=None, w_k=None, w_v=None, *, q_state_in=None,
                   k_state_in=None, v_state_in=None, q_out=None, k_out=None, v_out=None,
                   q_state_out=None, k_state_out=None, v_state_out=None, want_state: bool = False,
@@ -390,5 +469,6 @@ def la_short_conv(q=None, k=None, v=None, w_q=None, w_k=None, w_v=None, *, q_sta
 
 
 __all__ = ["la_chunk_fwd", "la_chunk_fwd_workspace_size", "la_chunk_fwd_noalloc", "la_chunk_bwd", "la_chunk_bwd_workspace_size",
+           "la_chunk_fwd_conv", "la_chunk_fwd_conv_workspace_size",
            "la_decode_step", "la_short_conv",
            "la_status_str", "la_abi_version", "LinAttnError", "VARIANTS", "load_library"]

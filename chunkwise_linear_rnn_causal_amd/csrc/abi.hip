@@ -399,8 +399,17 @@ la_status validate_fwd(const FwdCall &f) {
 // sequence; the whole sequence when p0 = 0 and n = L): pointers are advanced to
 // the piece, heads stay f.L rows apart, the state comes from s_in and goes to
 // s_out. ws: the delta rule's per-chunk products for this piece.
+// The short convolution fused into the delta rule's preparation: taps, windows
+// and the workspace arrays of the convolved q and k.
+struct ConvSpec {
+    const float *w[3];
+    const void *win[3];
+    void *qc, *kc;
+    int H, K;
+};
+
 la_status run_fwd(const FwdCall &f, int p0, int n, const float *s_in, float *s_out, void *ws,
-                  hipStream_t st) {
+                  hipStream_t st, const ConvSpec *cv = nullptr) {
     const la_variant var = f.var;
     const la_dtype dt = f.dt;
     const int64_t BH = (int64_t)f.B * f.H;
@@ -430,6 +439,14 @@ la_status run_fwd(const FwdCall &f, int p0, int n, const float *s_in, float *s_o
         p.q = a.q; p.k = a.k; p.v = a.v; p.lg = a.lg; p.beta = static_cast<const float *>(adv(f.beta, 4));
         p.w = const_cast<void *>(a.w); p.ut = const_cast<void *>(a.ut); p.mf = const_cast<void *>(a.mf);
         p.BH = (int)BH; p.L = n; p.Lp = Lp; p.dv = d_v; p.nchunks = nchunks; p.ld = f.L;
+        if (cv) {  // bf16 only (validated by the caller)
+            for (int i = 0; i < 3; ++i) {
+                p.cw[i] = cv->w[i];
+                p.cwin[i] = cv->win[i];
+            }
+            p.qc = cv->qc; p.kc = cv->kc; p.H = cv->H; p.K = cv->K;
+            a.qc = cv->qc; a.kc = cv->kc;
+        }
         const hipError_t e = (dt == LA_BF16) ? dispatch_prep<bf16>(d_k, p, st)
                                              : dispatch_prep<float>(d_k, p, st);
         if (e != hipSuccess) return LA_ERR_HIP;
@@ -586,6 +603,131 @@ la_status la_chunk_fwd_noalloc(la_variant var, la_dtype dt, la_dtype o_dt, const
     return LA_OK;
 }
 
+// ---- la_chunk_fwd_conv: the delta rule with the short convolution fused into
+// its preparation. Workspace: la_chunk_fwd's, then the convolved q and k (fp16,
+// [BH, Lp, d_k] each), then the discarded outputs of the window update (at most
+// 3 rows of q, k, v per head).
+size_t conv_fused_workspace(int B, int H, int L, int d_k, int d_v, int C) {
+    const int64_t BH = (int64_t)B * H, Lp = (int64_t)((L + 63) / 64) * 64;
+    return chunk_workspace(LA_GATED_DELTA, LA_BF16, B, H, L, d_k, d_v, C) +
+           2 * round_up((size_t)BH * Lp * d_k * 2, 256) + round_up((size_t)BH * 3 * (2 * d_k + d_v) * 2, 256);
+}
+
+la_status check_conv_fused(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v, int C, int K) {
+    const la_status s = check_chunk_shape(var, dt, B, H, L, d_k, d_v, C);
+    if (s != LA_OK) return s;
+    if (K < 1) return LA_ERR_INVALID_ARG;
+    if (var != LA_GATED_DELTA || dt != LA_BF16 || K > 4) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
+la_status la_chunk_fwd_conv_workspace_size(la_variant var, la_dtype dt, int B, int H, int L, int d_k,
+                                           int d_v, int C, int K, size_t *bytes) {
+    if (!bytes) return LA_ERR_INVALID_ARG;
+    const la_status s = check_conv_fused(var, dt, B, H, L, d_k, d_v, C, K);
+    if (s != LA_OK) return s;
+    *bytes = conv_fused_workspace(B, H, L, d_k, d_v, C);
+    return LA_OK;
+}
+
+la_status la_chunk_fwd_conv(la_variant var, la_dtype dt, la_dtype o_dt, const void *q, const void *k,
+                            const void *v, const float *w_q, const float *w_k, const float *w_v, int K,
+                            const void *q_win_in, const void *k_win_in, const void *v_win_in,
+                            void *q_win_out, void *k_win_out, void *v_win_out, const float *log_gate,
+                            const float *beta, const float *state_in, void *o, float *state_out, int B,
+                            int H, int L, int d_k, int d_v, int C, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+    la_status s = check_conv_fused(var, dt, B, H, L, d_k, d_v, C, K);
+    if (s != LA_OK) return s;
+    const FwdCall f{var, dt, o_dt, q, k, v, log_gate, beta, state_in, nullptr, o, state_out, nullptr,
+                    B, H, L, d_k, d_v, C};
+    s = validate_fwd(f);
+    if (s != LA_OK) return s;
+    if (!w_q || !w_k || !w_v) return LA_ERR_INVALID_ARG;
+    const int64_t BH = (int64_t)B * H;
+    const int d[3] = {d_k, d_k, d_v};
+    const float *taps[3] = {w_q, w_k, w_v};
+    const void *win_in[3] = {q_win_in, k_win_in, v_win_in};
+    void *win_out[3] = {q_win_out, k_win_out, v_win_out};
+    const void *ptrs[] = {w_q, w_k, w_v, q_win_in, k_win_in, v_win_in, q_win_out, k_win_out, v_win_out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
+    const size_t need = conv_fused_workspace(B, H, L, d_k, d_v, C);
+    if (!workspace || workspace_bytes < need) return LA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
+    // aliasing: the workspace and the outgoing windows overlap no other buffer;
+    // an outgoing window may equal its own incoming window (updated in place)
+    Span in_sp[16], out_sp[4];
+    int ni = 0, no = 0;
+    for (const Span &sp : fwd_spans(f)) in_sp[ni++] = sp;  // includes o and state_out
+    for (int i = 0; i < 3; ++i) {
+        const size_t wb = (size_t)BH * (K - 1) * d[i] * 2;
+        in_sp[ni++] = Span{taps[i], (size_t)H * d[i] * K * 4};
+        if (win_in[i] != win_out[i]) in_sp[ni++] = Span{win_in[i], wb};
+        out_sp[no++] = Span{win_out[i], wb};
+        if (win_out[i] && win_in[i] && win_out[i] != win_in[i] && overlap(Span{win_out[i], wb}, Span{win_in[i], wb}))
+            return LA_ERR_INVALID_ARG;
+    }
+    out_sp[no++] = Span{workspace, need};
+    for (int o2 = 0; o2 < no; ++o2) {
+        for (int i = 0; i < ni; ++i)
+            if (overlap(out_sp[o2], in_sp[i])) return LA_ERR_INVALID_ARG;
+        for (int o3 = o2 + 1; o3 < no; ++o3)
+            if (overlap(out_sp[o2], out_sp[o3])) return LA_ERR_INVALID_ARG;
+    }
+    // the forward's own outputs must not overlap the taps or incoming windows
+    const Span fo[] = {{o, (size_t)BH * L * d_v * elem_size(o_dt)}, {state_out, (size_t)BH * d_k * d_v * 4}};
+    for (const Span &x : fo)
+        for (int i = 0; i < 3; ++i)
+            if (overlap(x, Span{taps[i], (size_t)H * d[i] * K * 4}) ||
+                overlap(x, Span{win_in[i], (size_t)BH * (K - 1) * d[i] * 2}))
+                return LA_ERR_INVALID_ARG;
+
+    s = check_device();
+    if (s != LA_OK) return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(workspace);
+    const int64_t Lp = (int64_t)((L + 63) / 64) * 64;
+    const size_t base = chunk_workspace(var, dt, B, H, L, d_k, d_v, C);
+    const size_t qk = round_up((size_t)BH * Lp * d_k * 2, 256);
+    ConvSpec cv{};
+    for (int i = 0; i < 3; ++i) {
+        cv.w[i] = taps[i];
+        cv.win[i] = K > 1 ? win_in[i] : nullptr;
+    }
+    cv.qc = w + base; cv.kc = w + base + qk; cv.H = H; cv.K = K;
+    s = run_fwd(f, 0, L, state_in, state_out, workspace, st, &cv);
+    if (s != LA_OK) return s;
+    // outgoing windows: the short convolution kernel over the last min(L, K - 1)
+    // tokens (the incoming window as well when L < K - 1); its outputs are dropped
+    if (K > 1 && (q_win_out || k_win_out || v_win_out)) {
+        const int n = L < K - 1 ? L : K - 1;
+        char *ydrop = w + base + 2 * qk;
+        ConvArgs a{};
+        ConvTensor *slots[3] = {&a.t0, &a.t1, &a.t2};
+        const void *xs[3] = {q, k, v};
+        int nt = 0;
+        int64_t blk[3] = {0, 0, 0}, total = 0;
+        const int tt = conv_tile<bf16>();
+        const int64_t NT = n > 0 ? ((int64_t)n + tt - 1) / tt : 1;
+        size_t yoff = 0;
+        for (int i = 0; i < 3; ++i) {
+            if (!win_out[i]) continue;
+            const void *x = xs[i] ? static_cast<const char *>(xs[i]) + (size_t)(L - n) * d[i] * 2 : nullptr;
+            *slots[nt] = ConvTensor{x, ydrop + yoff, n < K - 1 ? win_in[i] : nullptr, win_out[i], taps[i], d[i]};
+            yoff += (size_t)BH * 3 * d[i] * 2;
+            blk[nt] = (BH * NT * (d[i] / 8) + 255) / 256;
+            total += blk[nt];
+            ++nt;
+        }
+        a.blk1 = (unsigned)(nt > 1 ? blk[0] : total);
+        a.blk2 = (unsigned)(nt > 2 ? blk[0] + blk[1] : total);
+        a.BH = (int)BH; a.H = H; a.L = n; a.NT = (int)NT; a.ldx = L;
+        if (dispatch_short_conv<bf16>(K, a, (unsigned)total, st) != hipSuccess) return LA_ERR_HIP;
+    }
+    return LA_OK;
+}
+
 la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void *q, const void *k,
                          const void *v, const float *log_gate, const float *beta, float *state,
                          void *o, int N, int H, int d_k, int d_v, void *stream) {
@@ -719,7 +861,7 @@ la_status la_short_conv(la_dtype dt, const void *q, const void *k, const void *v
         *slots[i] = ConvTensor{use[i].x, use[i].y, use[i].si, use[i].so, use[i].w, use[i].d};
     a.blk1 = (unsigned)(n > 1 ? blk[0] : total);
     a.blk2 = (unsigned)(n > 2 ? blk[0] + blk[1] : total);
-    a.BH = (int)BH; a.H = H; a.L = L; a.NT = (int)NT;
+    a.BH = (int)BH; a.H = H; a.L = L; a.NT = (int)NT; a.ldx = L;
     const hipError_t e = dt == LA_BF16 ? dispatch_short_conv<bf16>(K, a, (unsigned)total, st)
                                        : dispatch_short_conv<float>(K, a, (unsigned)total, st);
     return from_hip(e);

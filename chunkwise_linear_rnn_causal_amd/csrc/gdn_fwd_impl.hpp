@@ -81,7 +81,10 @@ __device__ inline f16x8 chan_frag(const f16 *X, int row, int p, int g) {
     return f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-template <typename TO, int DK>
+// QK16: q and k come as fp16 rows of the workspace (a.qc, a.kc, [BH, Lp, DK];
+// the short convolution fused into the preparation writes them) instead of bf16
+// inputs.
+template <typename TO, int DK, bool QK16>
 __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
     using Cfg = GdnCfg<DK>;
     using MF = Mfma<f16>;
@@ -107,9 +110,18 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
     const int L = a.L, dv = a.dv;
     const int nchunks = (L + C - 1) / C;
 
-    const bf16 *qg = (const bf16 *)a.q + (size_t)bh * a.ld * DK;
+    // q and k as raw 16-bit words: bf16 inputs, or fp16 rows of the workspace
+    const uint16_t *qg = QK16 ? (const uint16_t *)a.qc + (size_t)bh * a.Lp * DK
+                              : (const uint16_t *)a.q + (size_t)bh * a.ld * DK;
+    // two packed 16-bit values to two packed fp16 values: bf16 with the packed
+    // round-toward-zero conversion (exact for every bf16 value in fp16's normal
+    // range); fp16 as they are
+    auto to_h2 = [](uint32_t u) __attribute__((always_inline)) {
+        return QK16 ? u : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(u), bf16_hi(u)));
+    };
     const f16 *mg = (const f16 *)a.mf + (size_t)bh * nchunks * (6 * 512);
-    const bf16 *kg = (const bf16 *)a.k + (size_t)bh * a.ld * DK;
+    const uint16_t *kg = QK16 ? (const uint16_t *)a.kc + (size_t)bh * a.Lp * DK
+                              : (const uint16_t *)a.k + (size_t)bh * a.ld * DK;
     const float *lgg = a.lg ? a.lg + (size_t)bh * a.ld : nullptr;
     const f16 *wg = (const f16 *)a.w + (size_t)bh * a.Lp * DK;
     TO *og = (TO *)a.o + (size_t)bh * a.ld * dv + j0;
@@ -311,7 +323,7 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
                     uint32_t *hw = reinterpret_cast<uint32_t *>(&h);
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        hw[k] = valid ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(u[k]), bf16_hi(u[k]))) : 0u;
+                        hw[k] = valid ? to_h2(u[k]) : 0u;
                     *reinterpret_cast<uint4 *>(&X[Cfg::OK + row * KP + seg * 8]) = h;
                 }
             }
@@ -387,7 +399,7 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
         uint2 qraw[2][NKS][2];
         uint4 mraw[2][NP];
         auto load = [&](int c, int set) __attribute__((always_inline)) {
-            const bf16 *qrow = qg + (size_t)min(c * C + r, L - 1) * DK + 4 * g;
+            const uint16_t *qrow = qg + (size_t)min(c * C + r, L - 1) * DK + 4 * g;
 #pragma unroll
             for (int p = 0; p < NKS; ++p) {
                 qraw[set][p][0] = *reinterpret_cast<const uint2 *>(qrow + 32 * p);
@@ -426,7 +438,7 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
                 uint32_t h[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    h[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(u[k]), bf16_hi(u[k])));
+                    h[k] = to_h2(u[k]);
                 qf[p] = __builtin_bit_cast(f16x8, make_uint4(h[0], h[1], h[2], h[3]));
             }
 #pragma unroll
@@ -475,7 +487,10 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
 template <typename TO, int DK>
 hipError_t launch_gdn_fwd(const ChunkArgs &a, hipStream_t st) {
     const int blocks = a.BH * a.nsplit;
-    hipLaunchKernelGGL((gdn_fwd_kernel<TO, DK>), dim3(blocks), dim3(512), 0, st, a);
+    if (a.qc)
+        hipLaunchKernelGGL((gdn_fwd_kernel<TO, DK, true>), dim3(blocks), dim3(512), 0, st, a);
+    else
+        hipLaunchKernelGGL((gdn_fwd_kernel<TO, DK, false>), dim3(blocks), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@
 
 namespace la {
 
-template <typename TM, int DK, int C>
+template <typename TM, int DK, int C, bool CONV = false>
 struct PrepCfg {
     static constexpr int DVMAX = 128;
     static constexpr int PAD = 16 / (int)sizeof(TM);
@@ -57,21 +57,62 @@ struct PrepCfg {
     // K and V stay in registers from their load until their scaled transposes
     // are staged, after T is converted.
     static constexpr size_t o_a = 0;
+    // With the fused short convolution, region B first holds each tensor's raw
+    // rows with a halo of HALO rows before the chunk (bf16, pitch RP); still four
+    // workgroups per CU at d_k = 128.
+    static constexpr int HALO = 3, RP = (DK > DVMAX ? DK : DVMAX) + 8;
     static constexpr size_t o_p = o_a + up16(cmax(cmax(sizeof(TM) * C * KP, 4 * C * TP),
                                                   sizeof(TM) * (DK > DVMAX ? DK : DVMAX) * C));
-    static constexpr size_t o_c = o_p + up16(cmax(4 * C * TP, sizeof(TM) * C * OP));
+    static constexpr size_t o_c = o_p + up16(cmax(cmax(4 * C * TP, sizeof(TM) * C * OP),
+                                                  CONV ? 2 * (C + HALO) * RP : 0));
     static constexpr size_t o_g = o_c + 4 * 4 * 256;
     static constexpr size_t lds_bytes = o_g + 4 * 2 * C;
 };
 
+// The fused short convolution (wln20 "LLM注意力优化：线性注意力", DeltaNet
+// section: a kernel-4 causal depthwise convolution in front of the delta rule):
+// y_t = sum_{tau < K} w_tau x_{t - tau} per channel, for 4 consecutive tokens
+// s0 .. s0 + 3 of the chunk and the 8 channels [8 cb, 8 cb + 8), from a raw bf16
+// tile whose row j is token t0 - 3 + j (7 packed rows read once). tv: the 8
+// channels' taps, 8 K consecutive floats (tap tau of channel e at e K + tau).
+// Rows whose bit in `valid` is clear (at or past L) come out zero. fp16 results.
+template <int K>
+__device__ inline void conv4_rows(const bf16 *raw, int RP, int s0, int cb,
+                                  const float __attribute__((ext_vector_type(4))) (&tv)[2 * K], unsigned valid,
+                                  Raw8<f16> (&out)[4]) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 xr[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) xr[j] = *reinterpret_cast<const u32x4 *>(raw + (s0 + j) * RP + cb * 8);
+    auto xval = [&](int j, int e) __attribute__((always_inline)) {
+        const uint32_t w = xr[j][e >> 1];
+        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    };
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float acc = 0.f;
+#pragma unroll
+            for (int tau = 0; tau < K; ++tau) acc = fmaf(tv[(e * K + tau) / 4][(e * K + tau) % 4], xval(r + 3 - tau, e), acc);
+            h[e] = (f16)((valid >> r) & 1u ? acc : 0.f);
+        }
+        out[r].v[0] = __builtin_bit_cast(uint4, h);
+    }
+}
+
 // BWD: the backward pass's preparation (gdn_bwd_impl.hpp): U~ row-major for
 // every input type, no score fragments, and T stored as well.
-template <typename TI, int DK, int C, bool BWD = false>
-__global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
+// KT > 0: the short convolution with KT taps fused in front (bf16 forward only;
+// q, k, v are raw inputs, see PrepArgs).
+template <typename TI, int DK, int C, bool BWD = false, int KT = 0>
+__global__ void __launch_bounds__(256, KT > 0 ? 3 : 4) gdn_prep_kernel(PrepArgs a) {
+    constexpr bool CONV = KT > 0;
     using TM = typename OpOf<TI>::type;
     using MF = Mfma<TM>;
-    using frag = typename MF::frag;
-    using Cfg = PrepCfg<TM, DK, C>;
+    using Cfg = PrepCfg<TM, DK, C, CONV>;
+    static_assert(!CONV || (sizeof(TI) == 2 && !BWD), "the fused convolution: bf16 forward");
     constexpr int E = MF::E;
     constexpr int NW = 4;
     constexpr int NRB = C / 16;
@@ -92,6 +133,7 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
     TM *VTs = reinterpret_cast<TM *>(lds + Cfg::o_a);        // after W is formed
     float *Gs = reinterpret_cast<float *>(lds + Cfg::o_g);
     float *Bs = Gs + C;
+    bf16 *Raw = reinterpret_cast<bf16 *>(lds + Cfg::o_p);    // CONV: raw rows, before P
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
     const int bh = blockIdx.x / a.nchunks, c = blockIdx.x - bh * a.nchunks;
@@ -123,7 +165,7 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
     const bool job1 = (wv & 1) == 0;
     const int jrb1 = wv == 0 ? 3 : 2;
     uint4 qx[2][NKS];
-    if constexpr (SC) {
+    if constexpr (SC && !CONV) {
         const TI *qg = (const TI *)a.q + (size_t)bh * a.ld * DK;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -136,6 +178,95 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
     }
     // K and V stay in their storage format until they are staged (fewer registers)
     Raw8<TI> kr[4], vr[4];
+    // CONV: the convolved K and V rows of this thread's units, in fp16
+    Raw8<f16> kc[4], vc[4];
+    if constexpr (CONV) {
+        // Each tensor's C rows plus HALO rows before the chunk pass through region
+        // B as raw bf16 (rows before the sequence from the window, or zero; rows
+        // at or past L are never used by a kept output); each thread then
+        // convolves its staging unit's 4 rows x 8 channels from there.
+        constexpr int HALO = Cfg::HALO, RP = Cfg::RP, RROWS = C + HALO;
+        const int h = bh % a.H;
+        constexpr int K = KT;
+        // the raw rows of q, k and v are all loaded up front (their latencies
+        // overlap); each tensor then passes through region B in turn
+        constexpr int NMAX = (RROWS * 16 + 255) / 256;  // d <= 128
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 rq[NMAX], rk[NMAX], rv[NMAX];
+        auto load_raw = [&](int which, int d, u32x4 (&r)[NMAX]) __attribute__((always_inline)) {
+            const bf16 *x = (const bf16 *)(which == 0 ? a.q : which == 1 ? a.k : a.v) + (size_t)bh * a.ld * d;
+            const int seg = d / 8;
+#pragma unroll
+            for (int m = 0; m < NMAX; ++m) {
+                const int idx = tid + 256 * m, row = idx / seg, sg = idx % seg, t = t0 - HALO + row;
+                r[m] = *reinterpret_cast<const u32x4 *>(x + (size_t)min(max(t, 0), L - 1) * d + sg * 8);
+            }
+        };
+        // rows before the sequence (chunk 0 only) come from the window, or are zero
+        auto stage_raw = [&](int which, int d, const u32x4 (&r)[NMAX]) __attribute__((always_inline)) {
+            const bf16 *win = (const bf16 *)a.cwin[which];
+            const int seg = d / 8, tot = RROWS * seg;
+#pragma unroll
+            for (int m = 0; m < NMAX; ++m) {
+                const int idx = tid + 256 * m, row = idx / seg, sg = idx % seg, t = t0 - HALO + row;
+                if (idx >= tot) continue;
+                u32x4 val = r[m];
+                if (t < 0) {
+                    val = u32x4{0u, 0u, 0u, 0u};
+                    if (win && t >= -(K - 1))
+                        val = *reinterpret_cast<const u32x4 *>(win + ((size_t)bh * (K - 1) + (K - 1) + t) * d + sg * 8);
+                }
+                *reinterpret_cast<u32x4 *>(Raw + row * RP + sg * 8) = val;
+            }
+        };
+        // taps of a unit's 8 channels: 8 K consecutive floats, loaded as vectors
+        // up front with the raw rows
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
+        auto load_taps = [&](int which, int d, int cb, f32x4v (&tv)[2 * K]) __attribute__((always_inline)) {
+            const f32x4v *w = reinterpret_cast<const f32x4v *>(a.cw[which] + ((size_t)h * d + cb * 8) * K);
+#pragma unroll
+            for (int i = 0; i < 2 * K; ++i) tv[i] = w[i];
+        };
+        // loads run ahead of the convolution: the raw rows one tensor ahead, the
+        // taps just before they are needed (registers)
+        f32x4v tq[2 * K], tk[2 * K], tvv[2 * K];
+        load_raw(1, DK, rk);
+        if (tid < KUNITS) load_taps(1, DK, kcb, tk);
+        load_raw(2, dv, rv);
+        // K: convolved into kc, the workspace copy (fp16) and, below, the LDS tile
+        stage_raw(1, DK, rk);
+        __syncthreads();
+        // bit r: token 4 tq + r of the chunk lies before L
+        auto valid4 = [&](int tq) { return (unsigned)((1 << max(0, min(4, L - t0 - 4 * tq))) - 1); };
+        if (tid < KUNITS) {
+            conv4_rows<K>(Raw, RP, 4 * ktq, kcb, tk, valid4(ktq), kc);
+            f16 *ko = (f16 *)a.kc + ((size_t)bh * a.Lp + t0) * DK;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                *reinterpret_cast<uint4 *>(ko + (size_t)(4 * ktq + r) * DK + 8 * kcb) = kc[r].v[0];
+        }
+        load_raw(0, DK, rq);
+        if (tid < VUNITS) load_taps(2, dv, vcb, tvv);
+        __syncthreads();
+        // V: convolved into vc
+        stage_raw(2, dv, rv);
+        __syncthreads();
+        if (tid < VUNITS) conv4_rows<K>(Raw, RP, 4 * vtq, vcb, tvv, valid4(vtq), vc);
+        if (tid < KUNITS) load_taps(0, DK, kcb, tq);
+        __syncthreads();
+        // Q: convolved into the workspace copy, which the score jobs read back
+        // after the next barrier
+        stage_raw(0, DK, rq);
+        __syncthreads();
+        if (tid < KUNITS) {
+            Raw8<f16> y[4];
+            conv4_rows<K>(Raw, RP, 4 * ktq, kcb, tq, valid4(ktq), y);
+            f16 *qo = (f16 *)a.qc + ((size_t)bh * a.Lp + t0) * DK;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4 *>(qo + (size_t)(4 * ktq + r) * DK + 8 * kcb) = y[r].v[0];
+        }
+        // (the barrier before the scores follows the K staging below)
+    } else {
     if (tid < KUNITS) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -149,6 +280,7 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
             const int t = t0 + 4 * vtq + r;
             vr[r] = ld_raw8<TI>(vg + (size_t)(t < L ? t : L - 1) * dv + 8 * vcb);
         }
+    }
     }
 
     // Gates: inclusive scan of the chunk's log-gates (one token per lane).
@@ -164,7 +296,10 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
     }
 
     // Stage K row-major (zero past the end of the sequence).
-    if (tid < KUNITS) {
+    if (CONV && tid < KUNITS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4 *>(&Ks[(4 * ktq + r) * KP + 8 * kcb]) = kc[r].v[0];
+    } else if (tid < KUNITS) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int s = 4 * ktq + r;
@@ -192,7 +327,11 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
         if (j == 1 && !job1) break;
         const int rb = j ? jrb1 : wv, p = j;
         typename MF::frag qf[NKS];
-        if constexpr (SC) {
+        if constexpr (CONV) {
+            const f16 *qrow = (const f16 *)a.qc + ((size_t)bh * a.Lp + t0 + rb * 16 + n) * DK + g * (DK / 4);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) qf[ks] = ld_frag<TM>(qrow + ks * E);
+        } else if constexpr (SC) {
             // bf16 -> fp16 with the packed round-toward-zero conversion (exact for
             // every bf16 value in fp16's normal range); rows past L are zero
             const bool valid = t0 + rb * 16 + n < L;
@@ -340,7 +479,12 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
         }
         float kx[4][8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) unpack8<TI>(kr[r], kx[r]);
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (CONV)
+                unpack8<f16>(kc[r], kx[r]);
+            else
+                unpack8<TI>(kr[r], kx[r]);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             f32x4 col = {kx[0][e] * sc[0], kx[1][e] * sc[1], kx[2][e] * sc[2], kx[3][e] * sc[3]};
@@ -371,7 +515,12 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
         for (int r = 0; r < 4; ++r) sc[r] = __shfl(bv, 4 * vtq + r, 64);
         float vx[4][8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) unpack8<TI>(vr[r], vx[r]);
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (CONV)
+                unpack8<f16>(vc[r], vx[r]);
+            else
+                unpack8<TI>(vr[r], vx[r]);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             f32x4 col = {vx[0][e] * sc[0], vx[1][e] * sc[1], vx[2][e] * sc[2], vx[3][e] * sc[3]};
@@ -420,6 +569,18 @@ __global__ void __launch_bounds__(256, 4) gdn_prep_kernel(PrepArgs a) {
 template <typename TI, int DK, int C>
 hipError_t launch_gdn_prep(const PrepArgs &a, hipStream_t st) {
     const int blocks = a.BH * a.nchunks;
+    if constexpr (sizeof(TI) == 2) {
+        if (a.cw[0]) {
+            switch (a.K) {
+                case 1: hipLaunchKernelGGL((gdn_prep_kernel<TI, DK, C, false, 1>), dim3(blocks), dim3(256), 0, st, a); break;
+                case 2: hipLaunchKernelGGL((gdn_prep_kernel<TI, DK, C, false, 2>), dim3(blocks), dim3(256), 0, st, a); break;
+                case 3: hipLaunchKernelGGL((gdn_prep_kernel<TI, DK, C, false, 3>), dim3(blocks), dim3(256), 0, st, a); break;
+                case 4: hipLaunchKernelGGL((gdn_prep_kernel<TI, DK, C, false, 4>), dim3(blocks), dim3(256), 0, st, a); break;
+                default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((gdn_prep_kernel<TI, DK, C>), dim3(blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }

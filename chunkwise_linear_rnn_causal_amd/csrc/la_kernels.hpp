@@ -21,6 +21,8 @@ struct ChunkArgs {
     const void *ut;             // gated delta: U~ [BH, Lp, dv] (operand type)
     const void *mf;             // gated delta, bf16: masked decayed score fragments
                                 // [BH, Lp / 64, 6, 64, 8] fp16 (gdn_prep_impl.hpp)
+    const void *qc, *kc;        // gated delta, bf16, short convolution fused into the
+                                // preparation: convolved q, k [BH, Lp, DK] fp16, or nullptr
     int BH, L, Lp, dv, nsplit;  // Lp = ceil(L / C) * C; nsplit = dv / DVT (workgroups per head)
     int ld;                     // rows between consecutive heads of q, k, v, o and the gates
                                 // (>= L; L unless a piece of a longer sequence is run)
@@ -32,6 +34,14 @@ struct PrepArgs {
     const float *lg, *beta;     // [BH, L] (lg may be nullptr)
     void *w, *ut, *mf;          // outputs, layouts as in ChunkArgs (mf: bf16 inputs only)
     void *t;                    // backward preparation only: T = (I + P)^-1 [BH, nchunks, C, C]
+    // short causal convolution fused into the preparation (bf16 inputs, forward):
+    // q, k, v are the raw inputs, convolved here with taps cw [H, d, K] (fp32) and
+    // the windows cwin [BH, K - 1, d] (bf16, nullptr = zeros) of the inputs before
+    // the sequence; the convolved q and k go to qc, kc [BH, Lp, DK] (fp16)
+    const float *cw[3];
+    const void *cwin[3];
+    void *qc, *kc;
+    int H, K;
     int BH, L, Lp, dv, nchunks;
     int ld;                     // rows between consecutive heads of k, v and the gates (>= L)
 };
@@ -59,6 +69,7 @@ struct ConvArgs {
     ConvTensor t0, t1, t2;
     unsigned blk1, blk2;        // first block of tensors 1 and 2 (unused ones: past the grid)
     int BH, H, L, NT;           // NT = max(1, ceil(L / TT)) token tiles
+    int ldx;                    // rows between consecutive heads of x (>= L)
 };
 
 // Backward pass of the chunk forward (C = 64). Gradients are fp32.

@@ -56,7 +56,7 @@ __global__ void __launch_bounds__(256) short_conv_kernel(ConvArgs a) {
         }
     }
 
-    const T *x = (const T *)t.x + bh * (size_t)L * d + c0;
+    const T *x = (const T *)t.x + bh * (size_t)a.ldx * d + c0;
     const T *s_in = t.s_in ? (const T *)t.s_in + bh * (size_t)W * d + c0 : nullptr;
     const int t0 = tile * TT;
 

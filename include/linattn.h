@@ -219,6 +219,47 @@ la_status la_short_conv(la_dtype dt, const void *q, const void *k, const void *v
                         int d_v, int K, void *stream);
 
 /*
+ * la_chunk_fwd of the gated delta rule with the causal depthwise short
+ * convolution of q, k and v fused in front (wln20 "LLM注意力优化：线性注意力",
+ * DeltaNet section: a kernel-4 short convolution precedes the delta rule). The
+ * result is la_chunk_fwd(q', k', v', ...) with x'_t = sum_{tau < K} w[h][c][tau]
+ * x_{t - tau} per channel, x_{-j} taken from the incoming window (the inputs
+ * before the sequence) or zero, as la_short_conv defines it. The preparation
+ * pass reads the raw q, k, v once and convolves them on the way in; the
+ * convolved q and k (fp16) go to the workspace for the serial pass, and v' is
+ * used where it is formed. The convolved values are rounded to fp16, not bf16.
+ *   var, dt      LA_GATED_DELTA and LA_BF16 (others: LA_ERR_UNSUPPORTED).
+ *   o_dt, q, k, v, log_gate, beta, state_in, o, state_out, B, H, L, d_k, d_v, C
+ *                as for la_chunk_fwd; q, k, v are the raw (unconvolved) inputs.
+ *   w_q, w_k, w_v  taps [H, d, K] float32 (d = d_k, d_k, d_v), all required;
+ *                tap tau multiplies the input tau tokens back.
+ *   K            1..4 (K > 4: LA_ERR_UNSUPPORTED; K < 1: LA_ERR_INVALID_ARG).
+ *   *_win_in     [B, H, K-1, d] bf16, the K-1 inputs before the sequence, oldest
+ *                first, or NULL (zeros).
+ *   *_win_out    [B, H, K-1, d] bf16 or NULL (not written): the K-1 most recent
+ *                raw inputs after this call, ready to be the next call's window.
+ *                May equal the same tensor's *_win_in (updated in place); must
+ *                not otherwise overlap any buffer.
+ *   workspace    at least la_chunk_fwd_conv_workspace_size() bytes, 256-byte
+ *                aligned: la_chunk_fwd's workspace, then the convolved q and k,
+ *                B*H*Lp*d_k fp16 each (Lp = ceil(L/64)*64, each rounded up to 256
+ *                bytes), then B*H*3*(2 d_k + d_v) fp16 for the window update.
+ * Errors as la_chunk_fwd; nothing is launched on error. Launches: the
+ * preparation (convolution included), the serial pass, and when a window is
+ * requested one short-convolution launch over the last min(L, K-1) tokens.
+ */
+la_status la_chunk_fwd_conv_workspace_size(la_variant var, la_dtype dt, int B, int H, int L,
+                                           int d_k, int d_v, int C, int K, size_t *bytes);
+la_status la_chunk_fwd_conv(la_variant var, la_dtype dt, la_dtype o_dt, const void *q,
+                            const void *k, const void *v, const float *w_q, const float *w_k,
+                            const float *w_v, int K, const void *q_win_in, const void *k_win_in,
+                            const void *v_win_in, void *q_win_out, void *k_win_out,
+                            void *v_win_out, const float *log_gate, const float *beta,
+                            const float *state_in, void *o, float *state_out, int B, int H, int L,
+                            int d_k, int d_v, int C, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/*
  * Backward pass of la_chunk_fwd (training): gradients of a scalar loss with
  * respect to q, k, v, the log-gates, beta and the initial state, given d_o =
  * dLoss/do and optionally d_state_out = dLoss/d(final state). Reverse-mode of

@@ -237,3 +237,46 @@ def test_chunk_bwd_valid_arguments_reach_the_device_check():
     assert bwd(L=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None) not in (INVALID, UNSUPPORTED)
     assert bwd(var=GDN, beta=FAKE + 0x500000, dbeta=0x830000000, dlg=0x840000000) not in (INVALID, UNSUPPORTED)
     assert bwd(var=GDN, lg=None, beta=FAKE + 0x500000) not in (INVALID, UNSUPPORTED)
+
+
+def conv_fwd(var=GDN, dt=BF16, odt=F32, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, wq=FAKE + 0x300000,
+             wk=FAKE + 0x310000, wv=FAKE + 0x320000, K=4, qwi=None, kwi=None, vwi=None, qwo=None, kwo=None,
+             vwo=None, lg=FAKE + 0x400000, beta=FAKE + 0x410000, s_in=None, o=0x800000000, s_out=None,
+             B=1, H=2, L=128, dk=64, dv=64, C=64, ws=0x900000000, ws_bytes=1 << 30):
+    return la.load_library().la_chunk_fwd_conv(var, dt, odt, q, k, v, wq, wk, wv, K, qwi, kwi, vwi, qwo, kwo,
+                                               vwo, lg, beta, s_in, o, s_out, B, H, L, dk, dv, C, ws,
+                                               ws_bytes, None)
+
+
+def test_conv_fused_workspace_size():
+    out = ctypes.c_size_t(0)
+    lib = la.load_library()
+    assert lib.la_chunk_fwd_conv_workspace_size(GDN, BF16, 2, 3, 100, 64, 32, 64, 4, ctypes.byref(out)) == 0
+    up = lambda x: -(-x // 256) * 256
+    base = up(6 * 128 * 64 * 2) + up(6 * 128 * 32 * 2) + 6 * 128 * 96
+    assert out.value == base + 2 * up(6 * 128 * 64 * 2) + up(6 * 3 * (2 * 64 + 32) * 2)
+    for var, dt, K in ((DECAY, BF16, 4), (GDN, F32, 4), (GDN, BF16, 5)):
+        assert lib.la_chunk_fwd_conv_workspace_size(var, dt, 2, 3, 100, 64, 32, 64, K, ctypes.byref(out)) == UNSUPPORTED
+    assert lib.la_chunk_fwd_conv_workspace_size(GDN, BF16, 2, 3, 100, 64, 32, 64, 0, ctypes.byref(out)) == INVALID
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(var=DECAY, beta=None), UNSUPPORTED), (dict(dt=F32), UNSUPPORTED), (dict(K=5), UNSUPPORTED),
+    (dict(K=0), INVALID), (dict(wq=None), INVALID), (dict(wv=None), INVALID), (dict(beta=None), INVALID),
+    (dict(ws=None), INVALID), (dict(ws_bytes=1024), INVALID), (dict(ws=0x900000010), INVALID),
+    (dict(qwi=FAKE + 0x500008), INVALID),                         # misaligned window
+    (dict(kwo=FAKE + 0x100000), INVALID),                         # outgoing window inside k
+    (dict(qwo=0x800000000 + 0x100), INVALID),                     # outgoing window inside o
+    (dict(vwo=0x900000000 + 0x1000), INVALID),                    # outgoing window inside the workspace
+    (dict(o=FAKE + 0x300000), INVALID),                           # o over the taps
+    (dict(qwi=FAKE + 0x600000, kwo=FAKE + 0x600000 + 0x10), INVALID),  # window out inside another's window in
+])
+def test_conv_fused_rejects(kw, expect):
+    assert conv_fwd(**kw) == expect
+
+
+def test_conv_fused_valid_arguments_reach_the_device_check():
+    assert conv_fwd() not in (INVALID, UNSUPPORTED)
+    assert conv_fwd(qwi=FAKE + 0x600000, qwo=FAKE + 0x600000) not in (INVALID, UNSUPPORTED)  # in place
+    assert conv_fwd(lg=None, K=1) not in (INVALID, UNSUPPORTED)
+    assert conv_fwd(L=0, q=None, k=None, v=None, o=None, beta=None) not in (INVALID, UNSUPPORTED)

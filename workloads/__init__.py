@@ -68,6 +68,10 @@ CONFIGS: Dict[str, dict] = {
     "gated_delta_bwd_bf16_b2h16_l8192_d128": dict(
         kind="bwd", variant="gated_delta", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, C=64,
         recipe="gdn"),
+    # the delta-rule workload with a K = 4 short convolution of q, k, v fused in front
+    "conv_gated_delta_bf16_b2h16_l8192_d128_k4": dict(
+        kind="convfwd", variant="gated_delta", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, C=64, K=4,
+        recipe="gdn"),
     # the short convolution in front of the delta rule, at that workload's q, k, v shapes
     "short_conv_qkv_bf16_b2h16_l8192_d128_k4": dict(
         kind="conv", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, K=4, recipe="conv"),
