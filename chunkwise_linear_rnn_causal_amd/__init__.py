@@ -62,7 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.la_chunk_bwd_workspace_size.restype = i
     lib.la_chunk_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.la_chunk_bwd.restype = i
-    lib.la_chunk_bwd.argtypes = [i, i, vp, vp, vp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp,
+    lib.la_chunk_bwd.argtypes = [i, i, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                                  i, i, i, i, i, i, vp, sz, vp]
     lib.la_short_conv.restype = i
     lib.la_chunk_fwd_conv_workspace_size.restype = i
@@ -279,15 +279,17 @@ def la_chunk_bwd_workspace_size(variant: str, dtype_code: int, B: int, H: int, L
 
 
 def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_state_out=None, *,
-                 beta=None, C: int = 64, want_d_log_gate: bool = True, want_d_state_in: bool = False,
-                 want_d_beta: bool = True, workspace=None, stream=None) -> Tuple:
+                 beta=None, z_in=None, d_z_out=None, C: int = 64, want_d_log_gate: bool = True,
+                 want_d_state_in: bool = False, want_d_beta: bool = True, want_d_z_in: bool = False,
+                 workspace=None, stream=None) -> Tuple:
     """Backward pass of la_chunk_fwd ("plain", "decay", or "gated_delta" in bf16).
 
     q, k: [B, H, L, d_k]; v, d_o: [B, H, L, d_v] (bf16 or fp32, one dtype);
     log_gate: [B, H, L] fp32 ("decay"; optional for "gated_delta"); beta: [B, H, L]
     fp32 ("gated_delta"); state_in, d_state_out: [B, H, d_k, d_v] fp32.
     Returns (dq, dk, dv, d_log_gate or None, d_state_in or None), all fp32, and for
-    "gated_delta" d_beta (or None) as a sixth entry.
+    "gated_delta" d_beta (or None) as a sixth entry. "normalized" takes z_in and
+    d_z_out ([B, H, d_k] fp32) and returns d_z_in (or None) as the sixth entry.
     """
     import torch
     lib = load_library()
@@ -307,8 +309,13 @@ def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_sta
     _check("beta", beta, (B, H, L), f32, dev_, required=gdn)
     _check("state_in", state_in, (B, H, d_k, d_v), f32, dev_)
     _check("d_state_out", d_state_out, (B, H, d_k, d_v), f32, dev_)
+    _check("z_in", z_in, (B, H, d_k), f32, dev_)
+    _check("d_z_out", d_z_out, (B, H, d_k), f32, dev_)
     if not gdn and beta is not None:
         raise ValueError("beta is taken by the gated delta rule only")
+    norm = variant == "normalized"
+    if not norm and (z_in is not None or d_z_out is not None):
+        raise ValueError("z_in and d_z_out are taken by the normalized variant only")
     _check_device(dev_)
     if workspace is not None and (workspace.device != dev_ or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous tensor on q's device")
@@ -319,18 +326,21 @@ def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_sta
            if (log_gate is not None and variant in ("decay", "gated_delta") and want_d_log_gate) else None)
     dbe = torch.empty((B, H, L), dtype=torch.float32, device=dev_) if (gdn and want_d_beta) else None
     dsi = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev_) if want_d_state_in else None
+    dzi = torch.empty((B, H, d_k), dtype=torch.float32, device=dev_) if (norm and want_d_z_in) else None
     if workspace is None:
         ws_bytes = la_chunk_bwd_workspace_size(variant, dt, B, H, L, d_k, d_v, C)
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev_)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib.la_chunk_bwd(VARIANTS[variant], dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_gate), _ptr(beta),
-                          _ptr(state_in), _ptr(d_o), _ptr(d_state_out), _ptr(dq), _ptr(dk), _ptr(dv),
-                          _ptr(dlg), _ptr(dbe), _ptr(dsi), B, H, L, d_k, d_v, C, _ptr(workspace), ws_bytes,
-                          _stream(dev_, stream))
+                          _ptr(state_in), _ptr(z_in), _ptr(d_o), _ptr(d_state_out), _ptr(d_z_out), _ptr(dq),
+                          _ptr(dk), _ptr(dv), _ptr(dlg), _ptr(dbe), _ptr(dsi), _ptr(dzi), B, H, L, d_k, d_v, C,
+                          _ptr(workspace), ws_bytes, _stream(dev_, stream))
     if st != LA_OK:
         raise LinAttnError(st, "la_chunk_bwd")
     if gdn:
         return dq, dk, dv, dlg, dsi, dbe
+    if norm:
+        return dq, dk, dv, None, dsi, dzi
     return dq, dk, dv, dlg, dsi
 
 

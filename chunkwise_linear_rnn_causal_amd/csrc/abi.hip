@@ -12,6 +12,7 @@
 #include "../../include/linattn.h"
 #include "la_common.hpp"
 #include "la_kernels.hpp"
+#include "norm_bwd_impl.hpp"
 
 using namespace la;
 
@@ -245,12 +246,13 @@ la_status check_bwd_shape(la_variant var, la_dtype dt, int B, int H, int L, int 
     if (var < LA_PLAIN || var > LA_VECTOR_DECAY) return LA_ERR_INVALID_ARG;
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || L < 0) return LA_ERR_INVALID_ARG;
-    if (var != LA_PLAIN && var != LA_DECAY && !(var == LA_GATED_DELTA && dt == LA_BF16))
+    if (var != LA_PLAIN && var != LA_DECAY && var != LA_NORMALIZED && !(var == LA_GATED_DELTA && dt == LA_BF16))
         return LA_ERR_UNSUPPORTED;
     if (C != 64) return LA_ERR_UNSUPPORTED;
     if ((d_k != 32 && d_k != 64 && d_k != 128) || (d_v != 32 && d_v != 64 && d_v != 128))
         return LA_ERR_UNSUPPORTED;
-    if (dt == LA_F32 && !bwd_f32_fits(d_k, d_v)) return LA_ERR_UNSUPPORTED;
+    // fp32 operand tiles (the normalized variant always computes on them)
+    if ((dt == LA_F32 || var == LA_NORMALIZED) && !bwd_f32_fits(d_k, d_v)) return LA_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H, nch = (L + C - 1) / C;
     if (BH * nch > INT32_MAX || BH * 2 > INT32_MAX) return LA_ERR_UNSUPPORTED;
     if (!head_offsets_fit(L, C, d_k, d_v)) return LA_ERR_UNSUPPORTED;
@@ -258,13 +260,15 @@ la_status check_bwd_shape(la_variant var, la_dtype dt, int B, int H, int L, int 
 }
 
 struct BwdLayout {
-    size_t hs, dhs, s_last, rterm, w, u, du, t, total;
+    size_t hs, dhs, s_last, rterm, w, u, du, t, o, den, rho, g, ksum, gqsum, up, total;
 };
 // Every array starts on a 256-byte boundary. The delta rule adds W [BH, Lp, d_k],
 // U~ / U and A_m^T dO / dU [BH, Lp, d_v] and T [BH, nchunks, 64, 64], in fp16.
 BwdLayout bwd_layout(la_variant var, la_dtype dt, int64_t BH, int L, int d_k, int d_v) {
     const int64_t nch = (L + 63) / 64, Lp = nch * 64;
     BwdLayout w{};
+    const la_dtype in_dt = dt;
+    if (var == LA_NORMALIZED) dt = LA_F32;  // states in the fp32 operand precision
     const size_t st = (size_t)BH * nch * d_k * d_v * elem_size(dt);
     w.hs = 0;
     w.dhs = round_up(st, 256);
@@ -278,7 +282,50 @@ BwdLayout bwd_layout(la_variant var, la_dtype dt, int64_t BH, int L, int d_k, in
         w.t = w.du + round_up((size_t)BH * Lp * d_v * 2, 256);
         w.total = w.t + round_up((size_t)BH * nch * 64 * 64 * 2, 256);
     }
+    if (var == LA_NORMALIZED) {  // the forward's output and denominators, rho, g, chunk sums
+        const size_t tok = round_up((size_t)BH * L * 4, 256), cs = round_up((size_t)BH * nch * d_k * 4, 256);
+        w.o = w.total;
+        w.den = w.o + round_up((size_t)BH * L * d_v * 4, 256);
+        w.rho = w.den + tok;
+        w.g = w.rho + tok;
+        w.ksum = w.g + tok;
+        w.gqsum = w.ksum + cs;
+        w.total = w.gqsum + cs;
+        if (in_dt == LA_BF16) {  // fp32 copies of q, k, v and d_o
+            const size_t qk = round_up((size_t)BH * L * d_k * 4, 256), vb = round_up((size_t)BH * L * d_v * 4, 256);
+            w.up = w.total;
+            w.total += 2 * qk + 2 * vb;
+        }
+    }
     return w;
+}
+
+template <typename TI>
+hipError_t dispatch_norm_pre(int d_k, int d_v, const NormArgs &a, hipStream_t st) {
+#define LA_NORM_DV(DK)                                                   \
+    switch (d_v) {                                                       \
+        case 32: return launch_norm_bwd_pre<TI, DK, 32>(a, st);          \
+        case 64: return launch_norm_bwd_pre<TI, DK, 64>(a, st);          \
+        case 128: return launch_norm_bwd_pre<TI, DK, 128>(a, st);        \
+    }                                                                    \
+    break;
+    switch (d_k) {
+        case 32: LA_NORM_DV(32)
+        case 64: LA_NORM_DV(64)
+        case 128: LA_NORM_DV(128)
+    }
+#undef LA_NORM_DV
+    return hipErrorInvalidValue;
+}
+
+template <typename TI>
+hipError_t dispatch_norm_post(int d_k, const NormArgs &a, hipStream_t st) {
+    switch (d_k) {
+        case 32: return launch_norm_bwd_post<TI, 32>(a, st);
+        case 64: return launch_norm_bwd_post<TI, 64>(a, st);
+        case 128: return launch_norm_bwd_post<TI, 128>(a, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t dispatch_gdn_bwd(int d_k, int d_v, const BwdArgs &a, hipStream_t st) {
@@ -409,7 +456,7 @@ struct ConvSpec {
 };
 
 la_status run_fwd(const FwdCall &f, int p0, int n, const float *s_in, float *s_out, void *ws,
-                  hipStream_t st, const ConvSpec *cv = nullptr) {
+                  hipStream_t st, const ConvSpec *cv = nullptr, float *den_out = nullptr) {
     const la_variant var = f.var;
     const la_dtype dt = f.dt;
     const int64_t BH = (int64_t)f.B * f.H;
@@ -427,6 +474,7 @@ la_status run_fwd(const FwdCall &f, int p0, int n, const float *s_in, float *s_o
     a.s_in = s_in; a.z_in = f.z_in;
     a.o = const_cast<void *>(adv(f.o, d_v * oes));
     a.s_out = s_out; a.z_out = f.z_out;
+    a.den_out = den_out ? den_out + p0 : nullptr;
     const Geometry geo = choose_geometry(var, dt, BH, d_v, C);
     a.BH = (int)BH; a.L = n; a.Lp = Lp; a.dv = d_v; a.nsplit = d_v / geo.dvt; a.ld = f.L;
 
@@ -878,34 +926,36 @@ la_status la_chunk_bwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
 
 la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k, const void *v,
                        const float *log_gate, const float *beta, const float *state_in,
-                       const void *d_o, const float *d_state_out, float *dq, float *dk, float *dv,
-                       float *d_log_gate, float *d_beta, float *d_state_in, int B, int H, int L,
+                       const float *z_in, const void *d_o, const float *d_state_out,
+                       const float *d_z_out, float *dq, float *dk, float *dv, float *d_log_gate,
+                       float *d_beta, float *d_state_in, float *d_z_in, int B, int H, int L,
                        int d_k, int d_v, int C, void *workspace, size_t workspace_bytes,
                        void *stream) {
     la_status s = check_bwd_shape(var, dt, B, H, L, d_k, d_v, C);
     if (s != LA_OK) return s;
-    const bool tok = L > 0, gdn = var == LA_GATED_DELTA;
+    const bool tok = L > 0, gdn = var == LA_GATED_DELTA, norm = var == LA_NORMALIZED;
     if (tok && (!q || !k || !v || !d_o || !dq || !dk || !dv)) return LA_ERR_INVALID_ARG;
     if (var == LA_DECAY && tok && !log_gate) return LA_ERR_INVALID_ARG;
-    if (var == LA_PLAIN && (log_gate || d_log_gate)) return LA_ERR_INVALID_ARG;
+    if ((var == LA_PLAIN || norm) && (log_gate || d_log_gate)) return LA_ERR_INVALID_ARG;
     if (d_log_gate && !log_gate && tok) return LA_ERR_INVALID_ARG;
     if (gdn ? (tok && !beta) : (beta || d_beta)) return LA_ERR_INVALID_ARG;
-    const void *ptrs[] = {q, k, v, log_gate, beta, state_in, d_o, d_state_out, dq, dk, dv,
-                          d_log_gate, d_beta, d_state_in};
+    if (!norm && (z_in || d_z_out || d_z_in)) return LA_ERR_INVALID_ARG;
+    const void *ptrs[] = {q, k, v, log_gate, beta, state_in, z_in, d_o, d_state_out, d_z_out, dq, dk, dv,
+                          d_log_gate, d_beta, d_state_in, d_z_in};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
     const int64_t BH = (int64_t)B * H;
     const size_t es = elem_size(dt);
     const size_t qk_b = (size_t)BH * L * d_k * es, v_b = (size_t)BH * L * d_v * es;
-    const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4;
+    const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4, z_b = (size_t)BH * d_k * 4;
     const BwdLayout lay = bwd_layout(var, dt, BH, L, d_k, d_v);
     if (!workspace || workspace_bytes < lay.total) return LA_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
-    const Span ins[] = {{q, qk_b},    {k, qk_b},        {v, v_b},   {log_gate, g_b},
-                        {beta, g_b}, {state_in, s_b}, {d_o, v_b}, {d_state_out, s_b}};
+    const Span ins[] = {{q, qk_b},    {k, qk_b},        {v, v_b},    {log_gate, g_b},    {beta, g_b},
+                        {state_in, s_b}, {z_in, z_b},   {d_o, v_b},  {d_state_out, s_b}, {d_z_out, z_b}};
     const Span outs[] = {{dq, (size_t)BH * L * d_k * 4}, {dk, (size_t)BH * L * d_k * 4},
                          {dv, (size_t)BH * L * d_v * 4}, {d_log_gate, g_b}, {d_beta, g_b},
-                         {d_state_in, s_b}, {workspace, lay.total}};
+                         {d_state_in, s_b}, {d_z_in, z_b}, {workspace, lay.total}};
     for (size_t o = 0; o < sizeof(outs) / sizeof(outs[0]); ++o) {
         for (const Span &in : ins)
             if (overlap(outs[o], in)) return LA_ERR_INVALID_ARG;
@@ -925,18 +975,58 @@ la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k
     a.s_last = reinterpret_cast<float *>(ws + lay.s_last);
     a.rterm = reinterpret_cast<float *>(ws + lay.rterm);
     a.BH = (int)BH; a.L = L; a.dv = d_v; a.nsplit = 1;
+    const int nch = (L + 63) / 64;
     hipError_t e;
     if (gdn) {
         a.beta = beta; a.gbeta = d_beta;
         a.w = ws + lay.w; a.u = ws + lay.u; a.du = ws + lay.du; a.t = ws + lay.t;
-        a.nchunks = (L + 63) / 64; a.Lp = a.nchunks * 64;
-        e = dispatch_gdn_bwd(d_k, d_v, a, st);
-    } else if (dt == LA_BF16) {
-        e = var == LA_DECAY ? dispatch_bwd<bf16, true>(d_k, d_v, a, st) : dispatch_bwd<bf16, false>(d_k, d_v, a, st);
-    } else {
-        e = var == LA_DECAY ? dispatch_bwd<float, true>(d_k, d_v, a, st) : dispatch_bwd<float, false>(d_k, d_v, a, st);
+        a.nchunks = nch; a.Lp = nch * 64;
+        return from_hip(dispatch_gdn_bwd(d_k, d_v, a, st));
     }
-    return from_hip(e);
+    NormArgs na{};
+    la_dtype idt = dt;  // the dtype the kernels read
+    if (norm && dt == LA_BF16) {
+        // fp32 copies of the inputs and of d_o (fp32 operands, see norm_bwd_impl.hpp)
+        float *up = reinterpret_cast<float *>(ws + lay.up);
+        const size_t nq = (size_t)BH * L * d_k, nv = (size_t)BH * L * d_v;
+        float *q32 = up, *k32 = up + round_up(nq * 4, 256) / 4;
+        float *v32 = k32 + round_up(nq * 4, 256) / 4, *o32 = v32 + round_up(nv * 4, 256) / 4;
+        if (launch_upcast(q, q32, nq, st) != hipSuccess || launch_upcast(k, k32, nq, st) != hipSuccess ||
+            launch_upcast(v, v32, nv, st) != hipSuccess || launch_upcast(d_o, o32, nv, st) != hipSuccess)
+            return LA_ERR_HIP;
+        q = q32; k = k32; v = v32; d_o = o32;
+        a.q = q; a.k = k; a.v = v; a.dout = d_o;
+        idt = LA_F32;
+    }
+    if (norm) {
+        // the forward pass (its output in fp32 and its denominators), then rho, g
+        // and the chunk sums, the plain backward on rho-scaled dO rows, and the
+        // normalizer terms
+        na.q = q; na.k = k; na.dout = d_o;
+        na.o = reinterpret_cast<const float *>(ws + lay.o);
+        na.den = reinterpret_cast<const float *>(ws + lay.den);
+        na.z_in = z_in; na.dz_out = d_z_out; na.dz_in = d_z_in;
+        na.rho = reinterpret_cast<float *>(ws + lay.rho);
+        na.g = reinterpret_cast<float *>(ws + lay.g);
+        na.ksum = reinterpret_cast<float *>(ws + lay.ksum);
+        na.gqsum = reinterpret_cast<float *>(ws + lay.gqsum);
+        na.gq = dq; na.gk = dk; na.BH = (int)BH; na.L = L; na.nchunks = nch;
+        if (tok) {
+            const FwdCall f{LA_NORMALIZED, idt, LA_F32, q, k, v, nullptr, nullptr, state_in, z_in,
+                            ws + lay.o, nullptr, nullptr, B, H, L, d_k, d_v, 64};
+            s = run_fwd(f, 0, L, state_in, nullptr, nullptr, st, nullptr, reinterpret_cast<float *>(ws + lay.den));
+            if (s != LA_OK) return s;
+            e = dispatch_norm_pre<float>(d_k, d_v, na, st);
+            if (e != hipSuccess) return LA_ERR_HIP;
+        }
+        a.rho = na.rho;
+    }
+    if (idt == LA_BF16)
+        e = var == LA_DECAY ? dispatch_bwd<bf16, true>(d_k, d_v, a, st) : dispatch_bwd<bf16, false>(d_k, d_v, a, st);
+    else
+        e = var == LA_DECAY ? dispatch_bwd<float, true>(d_k, d_v, a, st) : dispatch_bwd<float, false>(d_k, d_v, a, st);
+    if (e != hipSuccess || !norm) return from_hip(e);
+    return from_hip(dispatch_norm_post<float>(d_k, na, st));
 }
 
 }  // extern "C"

@@ -84,6 +84,9 @@ __device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &
 
     Raw8<TI> rx[NXS], ry[NYS];
     float rg = 0.f;
+    // reverse scan of the normalized variant: dO rows scaled by rho (1 / den)
+    const float *rho = FWD ? nullptr : (a.rho ? a.rho + (size_t)bh * L : nullptr);
+    float rr[NYS];
     auto load = [&](int c) __attribute__((always_inline)) {
         const int t0 = c * C, nv = min(C, L - t0);
 #pragma unroll
@@ -97,6 +100,7 @@ __device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &
             const int sid = tid + 256 * m, row = sid / SEGY;
             ry[m] = (sid < C * SEGY && row < nv) ? ld_raw8<TI>(yg + (size_t)(t0 + row) * dv + 8 * (sid % SEGY))
                                                  : zero_raw8<TI>();
+            rr[m] = (rho && sid < C * SEGY && row < nv) ? rho[t0 + row] : 1.f;
         }
         if constexpr (DECAY) rg = lane < nv ? lg[t0 + lane] : 0.f;
     };
@@ -143,6 +147,10 @@ __device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &
             if (sid < C * SEGY) {
                 float y[8];
                 unpack8<TI>(ry[m], y);
+                if (rho) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] *= rr[m];
+                }
                 st8<TM>(&Ys[(sid / SEGY) * PY + 8 * (sid % SEGY)], y);
             }
         }
@@ -231,6 +239,7 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
     const int items = a.BH * nchunks;
     constexpr int NQ = (C * SEGK + 511) / 512, NVV = (C * SEGV + 511) / 512, NS = (DV * SEGK + 511) / 512;
     Raw8<TI> rq[NQ], rk[NQ], rv[NVV], ro[NVV];
+    float rro[NVV];  // normalized variant: the dO rows' scale rho (1 / den)
     Raw8<TM> rh[NS], rd[NS];
     float rgl = 0.f;  // wave 0: the log-gate of token `lane`
     auto fetch = [&](int item) __attribute__((always_inline)) {
@@ -258,6 +267,7 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
             const bool ok = sid < C * SEGV && row < nv;
             rv[m] = ok ? ld_raw8<TI>(vg + off) : zero_raw8<TI>();
             ro[m] = ok ? ld_raw8<TI>(og + off) : zero_raw8<TI>();
+            rro[m] = (a.rho && ok) ? a.rho[(size_t)bh * L + t0 + row] : 1.f;
         }
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
@@ -302,7 +312,15 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
         if (sid < C * SEGV) {
             const int o = (sid / SEGV) * PV + 8 * (sid % SEGV);
             put(rv[m], &Vs[o]);
-            put(ro[m], &Os[o]);
+            if (a.rho) {
+                float x[8];
+                unpack8<TI>(ro[m], x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] *= rro[m];
+                st8<TM>(&Os[o], x);
+            } else {
+                put(ro[m], &Os[o]);
+            }
         }
     }
 #pragma unroll

@@ -930,6 +930,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
             const float inv = 1.0f / den;
 #pragma unroll
             for (int jt = 0; jt < NTJW; ++jt) oacc[jt] *= inv;
+            // the denominators, for the backward pass (one value slice writes them)
+            if (a.den_out && split == 0 && g == 0 && (!CHECK || t0 + rl < L))
+                a.den_out[(size_t)bh * a.ld + t0 + rl] = den;
         }
 
         // rows of this block start at a uniform offset: scalar base + lane offset

@@ -21,6 +21,8 @@ struct ChunkArgs {
     const void *ut;             // gated delta: U~ [BH, Lp, dv] (operand type)
     const void *mf;             // gated delta, bf16: masked decayed score fragments
                                 // [BH, Lp / 64, 6, 64, 8] fp16 (gdn_prep_impl.hpp)
+    float *den_out;             // normalized: the per-token denominators [BH, L] (for the
+                                // backward pass) or nullptr
     const void *qc, *kc;        // gated delta, bf16, short convolution fused into the
                                 // preparation: convolved q, k [BH, Lp, DK] fp16, or nullptr
     int BH, L, Lp, dv, nsplit;  // Lp = ceil(L / C) * C; nsplit = dv / DVT (workgroups per head)
@@ -94,6 +96,9 @@ struct BwdArgs {
     void *du;                      // A_m^T dO [BH, Lp, dv], overwritten with dU by the reverse scan
     void *t;                       // T [BH, nchunks, C, C]
     int Lp, nchunks;
+    // normalized variant (norm_bwd_impl.hpp): rows of dO scaled by rho [BH, L]
+    // (1 / denominator) where the plain kernels stage them, or nullptr
+    const float *rho;
 };
 
 // TI: input type (bf16 or float); TO: output type (float or bf16); DVT: value
@@ -129,6 +134,15 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t st);
 // log-gate gradient (gdn_bwd_impl.hpp).
 template <int DK, int DV>
 hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
+
+// Backward pass of the normalized variant around the plain one
+// (norm_bwd_impl.hpp): rho, g and the chunk sums before it, the normalizer terms
+// after it.
+struct NormArgs;
+template <typename TI, int DK, int DV>
+hipError_t launch_norm_bwd_pre(const NormArgs &a, hipStream_t st);
+template <typename TI, int DK>
+hipError_t launch_norm_bwd_post(const NormArgs &a, hipStream_t st);
 
 template <typename T, int K>
 hipError_t launch_short_conv(const ConvArgs &a, unsigned blocks, hipStream_t st);

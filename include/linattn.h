@@ -272,8 +272,19 @@ la_status la_chunk_fwd_conv(la_variant var, la_dtype dt, la_dtype o_dt, const vo
  * q_t e^{G_t}, k_t e^{-G_t} (LA_GATED_DELTA: v_t e^{-G_t}) and e^{G_L}, so
  * d_log_gate_t = sum_{u>=t} (q_u . dq_u - k_u . dk_u) + <d_state_out, S_L>
  * (LA_GATED_DELTA: q_u . dq_u - v_u . dv_u).
- *   var          LA_PLAIN, LA_DECAY, or LA_GATED_DELTA with dt = LA_BF16
- *                (others: LA_ERR_UNSUPPORTED).
+ *   var          LA_PLAIN, LA_NORMALIZED, LA_DECAY, or LA_GATED_DELTA with
+ *                dt = LA_BF16 (LA_VECTOR_DECAY: LA_ERR_UNSUPPORTED). For
+ *                LA_NORMALIZED, o = n / den with n the plain output and
+ *                den_t = q_t . z_t, so the output gradient splits into the plain
+ *                backward of do_t / den_t and a normalizer term with
+ *                g_t = -(do_t . o_t) / den_t: dq_t += g_t z_t,
+ *                dk_j += sum_{t>=j} g_t q_t + d_z_out, d_z_in = sum_t g_t q_t +
+ *                d_z_out (proig-chaa sections 13-14); the forward pass is rerun
+ *                for o and den. It computes on fp32 operands (bf16 inputs are
+ *                upcast into the workspace): at the first tokens the two terms of
+ *                dq cancel to a fraction of their size, below what fp16 operands
+ *                resolve at the 2e-2 bound. Shapes: d_k * d_v <= 4096, or
+ *                (32, 128) and (128, 32) (else LA_ERR_UNSUPPORTED).
  *   dt           dtype of q, k, v and d_o (LA_BF16 or LA_F32); every gradient
  *                is float32.
  *   q, k, v, log_gate, beta, state_in   as given to la_chunk_fwd (beta:
@@ -285,20 +296,28 @@ la_status la_chunk_fwd_conv(la_variant var, la_dtype dt, la_dtype o_dt, const vo
  *   d_log_gate   [B,H,L] float32 or NULL (not computed); only with a log_gate.
  *   d_beta       [B,H,L] float32 or NULL (not computed); LA_GATED_DELTA only.
  *   d_state_in   [B,H,d_k,d_v] float32 or NULL (not written).
+ *   z_in, d_z_out  [B,H,d_k] float32 or NULL (zero): the normalizer given to
+ *                la_chunk_fwd and the gradient of the final normalizer
+ *                (LA_NORMALIZED only).
+ *   d_z_in       [B,H,d_k] float32 or NULL (not written; LA_NORMALIZED only).
  *   C            64. d_k, d_v in {32, 64, 128}.
  *   workspace    at least la_chunk_bwd_workspace_size() bytes, 256-byte aligned:
  *                per-chunk states and state gradients (operand precision), the
  *                final state and one float per token; for LA_GATED_DELTA also
- *                W, U~, A_m^T d_o (later U and dU) and T per chunk, in fp16.
+ *                W, U~, A_m^T d_o (later U and dU) and T per chunk, in fp16; for
+ *                LA_NORMALIZED also the forward's output in fp32, four floats
+ *                per token, two d_k vectors per chunk, and for bf16 inputs fp32
+ *                copies of q, k, v and d_o (its states are fp32).
  * Outputs and the workspace must not overlap any input or each other.
  */
 la_status la_chunk_bwd_workspace_size(la_variant var, la_dtype dt, int B, int H, int L,
                                       int d_k, int d_v, int C, size_t *bytes);
 la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k,
                        const void *v, const float *log_gate, const float *beta,
-                       const float *state_in, const void *d_o, const float *d_state_out,
-                       float *dq, float *dk, float *dv, float *d_log_gate, float *d_beta,
-                       float *d_state_in, int B, int H, int L, int d_k, int d_v, int C,
+                       const float *state_in, const float *z_in, const void *d_o,
+                       const float *d_state_out, const float *d_z_out, float *dq, float *dk,
+                       float *dv, float *d_log_gate, float *d_beta, float *d_state_in,
+                       float *d_z_in, int B, int H, int L, int d_k, int d_v, int C,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*

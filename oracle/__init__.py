@@ -49,6 +49,9 @@ def load(path: Optional[str] = None):
     lib.oracle_backward_gdn.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
                                         L, L, L, L, ctypes.c_int]
     lib.oracle_backward_gdn.restype = ctypes.c_int
+    lib.oracle_backward_norm.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp,
+                                         ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_long, ctypes.c_int]
+    lib.oracle_backward_norm.restype = ctypes.c_int
     lib.oracle_short_conv.argtypes = [dp, dp, dp, dp, dp, L, L, L, L, L, ctypes.c_int]
     lib.oracle_short_conv.restype = ctypes.c_int
     lib.oracle_abi_version.restype = ctypes.c_int
@@ -148,18 +151,21 @@ def short_conv(x, w, state_in=None, threads: int = 0, lib=None):
 
 
 def backward(variant: str, q, k, v, do, log_gate=None, state_in=None, d_state_out=None,
-             threads: int = 0, lib=None, beta=None):
+             threads: int = 0, lib=None, beta=None, z_in=None, d_z_out=None):
     """Gradients through the forward recurrence (see ``oracle_backward`` and, for
     "gated_delta", ``oracle_backward_gdn``).
 
     q, k: [..., L, dk]; v, do: [..., L, dv]; log_gate: [..., L] ("vector_decay":
     [..., L, dk]); state_in, d_state_out: [..., dk, dv]; beta: [..., L]
     ("gated_delta" only). Returns (dq, dk, dv, d_log_gate or None, d_state_in) in
-    float64, and for "gated_delta" d_beta as a sixth entry.
+    float64, and for "gated_delta" d_beta as a sixth entry. For "normalized" (z_in,
+    d_z_out: [..., dk]) the sixth entry is d_z_in and the fourth is None.
     """
     lib = lib or load()
     if variant == "gated_delta":
         return _backward_gdn(q, k, v, do, log_gate, beta, state_in, d_state_out, threads, lib)
+    if variant == "normalized":
+        return _backward_norm(q, k, v, do, state_in, z_in, d_state_out, d_z_out, threads, lib)
     q, k, v, do = _c64(q), _c64(k), _c64(v), _c64(do)
     lead = q.shape[:-2]
     L, dk = q.shape[-2], q.shape[-1]
@@ -198,3 +204,22 @@ def _backward_gdn(q, k, v, do, log_gate, beta, state_in, d_state_out, threads, l
     if st != 0:
         raise ValueError(f"oracle_backward_gdn failed with status {st}")
     return dq, dkk, dvv, dlg, dsi, dbe
+
+
+def _backward_norm(q, k, v, do, state_in, z_in, d_state_out, d_z_out, threads, lib):
+    q, k, v, do = _c64(q), _c64(k), _c64(v), _c64(do)
+    lead = q.shape[:-2]
+    L, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    s_in, zi, dso, dzo = _c64(state_in), _c64(z_in), _c64(d_state_out), _c64(d_z_out)
+    dq = np.zeros(q.shape, np.float64)
+    dkk = np.zeros(k.shape, np.float64)
+    dvv = np.zeros(v.shape, np.float64)
+    dsi = np.zeros(lead + (dk, dv), np.float64)
+    dzi = np.zeros(lead + (dk,), np.float64)
+    st = lib.oracle_backward_norm(_p(q), _p(k), _p(v), _p(s_in), _p(zi), _p(do), _p(dso), _p(dzo), _p(dq),
+                                  _p(dkk), _p(dvv), _p(dsi), _p(dzi), BH, L, dk, dv, int(threads))
+    if st != 0:
+        raise ValueError(f"oracle_backward_norm failed with status {st}")
+    return dq, dkk, dvv, None, dsi, dzi

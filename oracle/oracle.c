@@ -367,6 +367,110 @@ int oracle_backward(int variant, const double *q, const double *k, const double 
 }
 
 /*
+ * Backward pass of the normalized variant for one batch-head, by reverse mode of
+ * the per-token recurrence (proig-chaa "线性注意力：从 Softmax Attention 到 Kernel
+ * Attention 的本质变化", sections 13-14: the kernel form with its normalizer):
+ *   S_t = S_{t-1} + k_t v_t^T,  z_t = z_{t-1} + k_t,
+ *   n_t = S_t^T q_t,  den_t = q_t . z_t,  o_t = n_t / den_t.
+ * Every state S_0 .. S_L and normalizer z_0 .. z_L is kept. Walking t = L .. 1
+ * with G = dLoss/dS_t and Z = dLoss/dz_t (both carried unchanged to t - 1, since
+ * S_{t-1} and z_{t-1} enter with the identity):
+ *   dn    = do_t / den_t,  dden = -(do_t . n_t) / den_t^2
+ *   G    += q_t dn^T,      Z   += dden q_t
+ *   dq_t  = S_t dn + dden z_t
+ *   dk_t  = G v_t + Z,     dv_t = G^T k_t
+ * and finally dS_0 = G, dz_0 = Z.
+ */
+static int bwd_head_norm(const double *q, const double *k, const double *v, const double *s_in,
+                         const double *z_in, const double *dout, const double *ds_out,
+                         const double *dz_out, double *dq, double *dk, double *dv, double *ds_in,
+                         double *dz_in, long L, long dk_, long dv_)
+{
+    const long D = dk_ * dv_;
+    double *S = (double *)malloc(sizeof(double) * (size_t)((L + 1) * D));
+    double *z = (double *)malloc(sizeof(double) * (size_t)((L + 1) * dk_));
+    double *G = (double *)malloc(sizeof(double) * (size_t)D);
+    double *Z = (double *)malloc(sizeof(double) * (size_t)dk_);
+    double *n = (double *)malloc(sizeof(double) * (size_t)dv_);
+    double *dn = (double *)malloc(sizeof(double) * (size_t)dv_);
+    if (!S || !z || !G || !Z || !n || !dn) {
+        free(S); free(z); free(G); free(Z); free(n); free(dn);
+        return OR_NO_MEM;
+    }
+    for (long i = 0; i < D; ++i) S[i] = s_in ? s_in[i] : 0.0;
+    for (long i = 0; i < dk_; ++i) z[i] = z_in ? z_in[i] : 0.0;
+    for (long t = 0; t < L; ++t) {
+        const double *Sp = S + t * D, *zp = z + t * dk_;
+        double *Sn = S + (t + 1) * D, *zn = z + (t + 1) * dk_;
+        for (long i = 0; i < dk_; ++i) {
+            for (long j = 0; j < dv_; ++j) Sn[i * dv_ + j] = Sp[i * dv_ + j] + k[t * dk_ + i] * v[t * dv_ + j];
+            zn[i] = zp[i] + k[t * dk_ + i];
+        }
+    }
+    for (long i = 0; i < D; ++i) G[i] = ds_out ? ds_out[i] : 0.0;
+    for (long i = 0; i < dk_; ++i) Z[i] = dz_out ? dz_out[i] : 0.0;
+    for (long t = L - 1; t >= 0; --t) {
+        const double *qt = q + t * dk_, *kt = k + t * dk_, *vt = v + t * dv_, *dot = dout + t * dv_;
+        const double *St = S + (t + 1) * D, *zt = z + (t + 1) * dk_;
+        double den = 0.0;
+        for (long i = 0; i < dk_; ++i) den += qt[i] * zt[i];
+        double don = 0.0;
+        for (long j = 0; j < dv_; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < dk_; ++i) acc += St[i * dv_ + j] * qt[i];
+            n[j] = acc;
+            dn[j] = dot[j] / den;
+            don += dot[j] * acc;
+        }
+        const double dden = -don / (den * den);
+        for (long i = 0; i < dk_; ++i) {
+            for (long j = 0; j < dv_; ++j) G[i * dv_ + j] += qt[i] * dn[j];
+            Z[i] += dden * qt[i];
+        }
+        for (long i = 0; i < dk_; ++i) {
+            double acc = 0.0;
+            for (long j = 0; j < dv_; ++j) acc += St[i * dv_ + j] * dn[j];
+            dq[t * dk_ + i] = acc + dden * zt[i];
+            double gv = 0.0;
+            for (long j = 0; j < dv_; ++j) gv += G[i * dv_ + j] * vt[j];
+            dk[t * dk_ + i] = gv + Z[i];
+        }
+        for (long j = 0; j < dv_; ++j) {
+            double acc = 0.0;
+            for (long i = 0; i < dk_; ++i) acc += G[i * dv_ + j] * kt[i];
+            dv[t * dv_ + j] = acc;
+        }
+    }
+    if (ds_in) memcpy(ds_in, G, sizeof(double) * (size_t)D);
+    if (dz_in) memcpy(dz_in, Z, sizeof(double) * (size_t)dk_);
+    free(S); free(z); free(G); free(Z); free(n); free(dn);
+    return OR_OK;
+}
+
+int oracle_backward_norm(const double *q, const double *k, const double *v, const double *state_in,
+                         const double *z_in, const double *dout, const double *d_state_out,
+                         const double *d_z_out, double *dq, double *dk, double *dv, double *d_state_in,
+                         double *d_z_in, long BH, long L, long dk_, long dv_, int nthreads)
+{
+    if (BH < 0 || L < 0 || dk_ <= 0 || dv_ <= 0) return OR_BAD_ARG;
+    if (BH > 0 && L > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv)) return OR_BAD_ARG;
+    int status = OR_OK;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : omp_get_max_threads()) reduction(max : status)
+#endif
+    for (long h = 0; h < BH; ++h) {
+        int st = bwd_head_norm(q + h * L * dk_, k + h * L * dk_, v + h * L * dv_,
+                               state_in ? state_in + h * dk_ * dv_ : NULL, z_in ? z_in + h * dk_ : NULL,
+                               dout + h * L * dv_, d_state_out ? d_state_out + h * dk_ * dv_ : NULL,
+                               d_z_out ? d_z_out + h * dk_ : NULL, dq + h * L * dk_, dk + h * L * dk_,
+                               dv + h * L * dv_, d_state_in ? d_state_in + h * dk_ * dv_ : NULL,
+                               d_z_in ? d_z_in + h * dk_ : NULL, L, dk_, dv_);
+        if (st > status) status = st;
+    }
+    return status;
+}
+
+/*
  * Backward pass of the gated delta rule for one batch-head, by reverse mode of
  * the per-token recurrence (canonical orientation, as in run_head):
  *   r_t = S_{t-1}^T k_t

@@ -867,6 +867,62 @@ def pin_backward_gdn_gate_identity(lib):
     assert _rel(dlg[:, m], (tail[4] * s8).sum((-1, -2))) <= 1e-12
 
 
+def _norm_bwd_case(r, B=2, L=9, dk=4, dv=3):
+    """Positive features (elu + 1 of Gaussians), so every denominator is positive."""
+    phi = lambda x: np.where(x > 0, x + 1.0, np.exp(x))
+    q, k = phi(r.standard_normal((B, L, dk))), phi(r.standard_normal((B, L, dk)))
+    v, do = r.standard_normal((B, L, dv)), r.standard_normal((B, L, dv))
+    z0 = phi(r.standard_normal((B, dk)))
+    s0 = r.standard_normal((B, dk, dv))
+    dso, dzo = r.standard_normal((B, dk, dv)), r.standard_normal((B, dk))
+    return q, k, v, do, s0, z0, dso, dzo
+
+
+def pin_backward_norm_finite_differences(lib):
+    """Normalized variant: every gradient (q, k, v, initial state and normalizer)
+    matches the central difference of the forward oracle's loss
+    <do, O> + <dS_L, S_L> + <dz_L, z_L> along a random direction (fp64, step 1e-6)."""
+    r = _rng(56)
+    q, k, v, do, s0, z0, dso, dzo = _norm_bwd_case(r)
+
+    def loss(q_, k_, v_, s0_, z0_):
+        o, s, z = oracle.forward("normalized", q_, k_, v_, state_in=s0_, z_in=z0_, lib=lib)
+        return float((o * do).sum() + (s * dso).sum() + (z * dzo).sum())
+
+    dq, dk, dv, dlg, dsi, dzi = oracle.backward("normalized", q, k, v, do, None, s0, dso, lib=lib, z_in=z0,
+                                                d_z_out=dzo)
+    assert dlg is None
+    eps = 1e-6
+    args = [q, k, v, s0, z0]
+    for ai, (x, gx) in enumerate(zip(args, [dq, dk, dv, dsi, dzi])):
+        u = r.standard_normal(x.shape)
+        plus, minus = list(args), list(args)
+        plus[ai], minus[ai] = x + eps * u, x - eps * u
+        fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+        an = float((gx * u).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (ai, fd, an)
+
+
+def pin_backward_norm_constant_v(lib):
+    """Normalized variant with every value equal to c and S_0 = z_0 c^T: each output
+    is exactly c whatever q and k are (the weights sum to one, proig-chaa section
+    14), so the gradients of <do, O> with respect to q and k vanish, and dv_t is
+    the sum over s >= t of (q_s . k_t / den_s) do_s."""
+    r = _rng(57)
+    q, k, _, do, _, z0, _, _ = _norm_bwd_case(r, L=7)
+    c = r.standard_normal(3)
+    v = np.broadcast_to(c, (2, 7, 3)).copy()
+    s0 = z0[:, :, None] * c[None, None, :]
+    dq, dk, dv, _, _, _ = oracle.backward("normalized", q, k, v, do, None, s0, None, lib=lib, z_in=z0)
+    scale = np.abs(do).max() * np.abs(c).max() / min(q.min(), k.min())
+    assert np.abs(dq).max() <= 1e-13 * scale and np.abs(dk).max() <= 1e-13 * scale
+    z = z0[:, None, :] + np.cumsum(k, axis=1)
+    den = (q * z).sum(-1)
+    w = np.einsum("bsi,bti->bst", q, k) / den[:, :, None]          # [b, s, t]: q_s . k_t / den_s
+    ref = np.einsum("bst,bsj->btj", np.triu(np.ones((7, 7)))[None].transpose(0, 2, 1) * w, do)
+    assert _rel(dv, ref) <= 1e-12, _rel(dv, ref)
+
+
 ALL_PINS = [
     pin_plain_quadratic, pin_plain_fraction_bruteforce, pin_plain_final_state,
     pin_normalized_quadratic, pin_normalized_constant_v, pin_normalized_hull,
@@ -882,4 +938,5 @@ ALL_PINS = [
     pin_vector_decay_channel_isolation, pin_vector_decay_resume_and_decode,
     pin_backward_finite_differences, pin_backward_plain_closed_form, pin_backward_gate_identity,
     pin_backward_gdn_finite_differences, pin_backward_gdn_reductions, pin_backward_gdn_gate_identity,
+    pin_backward_norm_finite_differences, pin_backward_norm_constant_v,
 ]

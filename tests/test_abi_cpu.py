@@ -178,10 +178,11 @@ def test_short_conv_valid_arguments_reach_the_device_check(kw):
 
 
 def bwd(var=DECAY, dt=BF16, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, lg=FAKE + 0x300000, beta=None,
-        s_in=None, do=FAKE + 0x400000, dso=None, dq=0x800000000, dk=0x810000000, dv=0x820000000, dlg=None,
-        dbeta=None, dsi=None, B=1, H=2, L=128, dk_=64, dv_=64, C=64, ws=0x900000000, ws_bytes=1 << 30):
-    return la.load_library().la_chunk_bwd(var, dt, q, k, v, lg, beta, s_in, do, dso, dq, dk, dv, dlg, dbeta,
-                                          dsi, B, H, L, dk_, dv_, C, ws, ws_bytes, None)
+        s_in=None, z_in=None, do=FAKE + 0x400000, dso=None, dzo=None, dq=0x800000000, dk=0x810000000,
+        dv=0x820000000, dlg=None, dbeta=None, dsi=None, dzi=None, B=1, H=2, L=128, dk_=64, dv_=64, C=64,
+        ws=0x900000000, ws_bytes=1 << 30):
+    return la.load_library().la_chunk_bwd(var, dt, q, k, v, lg, beta, s_in, z_in, do, dso, dzo, dq, dk, dv, dlg,
+                                          dbeta, dsi, dzi, B, H, L, dk_, dv_, C, ws, ws_bytes, None)
 
 
 def bwd_wsize(var=DECAY, dt=BF16, B=2, H=3, L=100, dk_=64, dv_=32, C=64):
@@ -201,6 +202,14 @@ def test_bwd_workspace_size():
     assert st == 0 and n == (2 * states + r(6 * 64 * 32 * 4) + r(6 * 100 * 4) + r(6 * 128 * 64 * 2)
                              + 2 * r(6 * 128 * 32 * 2) + r(6 * 2 * 64 * 64 * 2))
     assert bwd_wsize(var=GDN, dt=F32)[0] == UNSUPPORTED
+    # normalized: also the forward's fp32 output, den, rho, g per token, two d_k sums per chunk
+    # (fp32 operands: fp32 states, and for bf16 inputs fp32 copies of q, k, v, d_o)
+    st, n = bwd_wsize(var=NORM)
+    states32 = r(6 * 2 * 64 * 32 * 4)
+    assert st == 0 and n == (2 * states32 + r(6 * 64 * 32 * 4) + r(6 * 100 * 4) + r(6 * 100 * 32 * 4)
+                             + 3 * r(6 * 100 * 4) + 2 * r(6 * 2 * 64 * 4)
+                             + 2 * r(6 * 100 * 64 * 4) + 2 * r(6 * 100 * 32 * 4))
+    assert bwd_wsize(var=NORM, dk_=128, dv_=128)[0] == UNSUPPORTED
     assert bwd_wsize(C=128)[0] == UNSUPPORTED
     assert bwd_wsize(dt=F32, dk_=128, dv_=128)[0] == UNSUPPORTED
     assert bwd_wsize(dt=F32, dk_=128, dv_=32)[0] == 0
@@ -208,7 +217,9 @@ def test_bwd_workspace_size():
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(var=9), INVALID), (dict(var=NORM), UNSUPPORTED), (dict(var=VDECAY), UNSUPPORTED),
+    (dict(var=9), INVALID), (dict(var=NORM), INVALID), (dict(var=VDECAY), UNSUPPORTED),
+    (dict(z_in=FAKE + 0x600000), INVALID),              # the normalizer is the normalized variant's
+    (dict(var=NORM, lg=None, dzi=FAKE + 0x400000), INVALID),   # d_z_in inside d_o
     (dict(C=128), UNSUPPORTED), (dict(dk_=96), UNSUPPORTED), (dict(B=0), INVALID),
     (dict(lg=None), INVALID),                           # decay needs its gates
     (dict(var=PLAIN), INVALID),                         # plain takes no gates
@@ -237,6 +248,8 @@ def test_chunk_bwd_valid_arguments_reach_the_device_check():
     assert bwd(L=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None) not in (INVALID, UNSUPPORTED)
     assert bwd(var=GDN, beta=FAKE + 0x500000, dbeta=0x830000000, dlg=0x840000000) not in (INVALID, UNSUPPORTED)
     assert bwd(var=GDN, lg=None, beta=FAKE + 0x500000) not in (INVALID, UNSUPPORTED)
+    assert bwd(var=NORM, lg=None, z_in=FAKE + 0x600000, dzo=FAKE + 0x610000,
+               dzi=0x830000000) not in (INVALID, UNSUPPORTED)
 
 
 def conv_fwd(var=GDN, dt=BF16, odt=F32, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, wq=FAKE + 0x300000,
