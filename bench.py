@@ -135,6 +135,8 @@ def bwd_work(c: dict) -> tuple[float, float]:
     nbytes = BH * L * ((2 * dk + 2 * dv) * esz + (2 * dk + dv) * 4)
     if c["variant"] in ("decay", "gated_delta"):
         nbytes += 2 * BH * L * 4                                 # gates in, gate gradient out
+    if c["variant"] == "vector_decay":
+        nbytes += 2 * BH * L * dk * 4                            # per-channel gates in, their gradient out
     if c["variant"] == "gated_delta":
         nbytes += 2 * BH * L * 4                                 # beta in, its gradient out
     return flop, nbytes

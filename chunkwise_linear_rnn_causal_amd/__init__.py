@@ -282,10 +282,12 @@ def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_sta
                  beta=None, z_in=None, d_z_out=None, C: int = 64, want_d_log_gate: bool = True,
                  want_d_state_in: bool = False, want_d_beta: bool = True, want_d_z_in: bool = False,
                  workspace=None, stream=None) -> Tuple:
-    """Backward pass of la_chunk_fwd ("plain", "decay", or "gated_delta" in bf16).
+    """Backward pass of la_chunk_fwd ("plain", "normalized", "decay", or
+    "gated_delta" and "vector_decay" in bf16).
 
     q, k: [B, H, L, d_k]; v, d_o: [B, H, L, d_v] (bf16 or fp32, one dtype);
-    log_gate: [B, H, L] fp32 ("decay"; optional for "gated_delta"); beta: [B, H, L]
+    log_gate: [B, H, L] fp32 ("decay"; optional for "gated_delta"; [B, H, L, d_k]
+    for "vector_decay"); beta: [B, H, L]
     fp32 ("gated_delta"); state_in, d_state_out: [B, H, d_k, d_v] fp32.
     Returns (dq, dk, dv, d_log_gate or None, d_state_in or None), all fp32, and for
     "gated_delta" d_beta (or None) as a sixth entry. "normalized" takes z_in and
@@ -305,7 +307,9 @@ def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_sta
     _check("k", k, (B, H, L, d_k), q.dtype, dev_, required=True)
     _check("v", v, (B, H, L, d_v), q.dtype, dev_, required=True)
     _check("d_o", d_o, (B, H, L, d_v), q.dtype, dev_, required=True)
-    _check("log_gate", log_gate, (B, H, L), f32, dev_)
+    vec = variant == "vector_decay"
+    gshape = (B, H, L, d_k) if vec else (B, H, L)
+    _check("log_gate", log_gate, gshape, f32, dev_)
     _check("beta", beta, (B, H, L), f32, dev_, required=gdn)
     _check("state_in", state_in, (B, H, d_k, d_v), f32, dev_)
     _check("d_state_out", d_state_out, (B, H, d_k, d_v), f32, dev_)
@@ -322,8 +326,9 @@ def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_sta
     dq = torch.empty((B, H, L, d_k), dtype=torch.float32, device=dev_)
     dk = torch.empty((B, H, L, d_k), dtype=torch.float32, device=dev_)
     dv = torch.empty((B, H, L, d_v), dtype=torch.float32, device=dev_)
-    dlg = (torch.empty((B, H, L), dtype=torch.float32, device=dev_)
-           if (log_gate is not None and variant in ("decay", "gated_delta") and want_d_log_gate) else None)
+    dlg = (torch.empty(gshape, dtype=torch.float32, device=dev_)
+           if (log_gate is not None and variant in ("decay", "gated_delta", "vector_decay") and want_d_log_gate)
+           else None)
     dbe = torch.empty((B, H, L), dtype=torch.float32, device=dev_) if (gdn and want_d_beta) else None
     dsi = torch.empty((B, H, d_k, d_v), dtype=torch.float32, device=dev_) if want_d_state_in else None
     dzi = torch.empty((B, H, d_k), dtype=torch.float32, device=dev_) if (norm and want_d_z_in) else None

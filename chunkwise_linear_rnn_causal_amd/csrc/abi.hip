@@ -246,8 +246,7 @@ la_status check_bwd_shape(la_variant var, la_dtype dt, int B, int H, int L, int 
     if (var < LA_PLAIN || var > LA_VECTOR_DECAY) return LA_ERR_INVALID_ARG;
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || L < 0) return LA_ERR_INVALID_ARG;
-    if (var != LA_PLAIN && var != LA_DECAY && var != LA_NORMALIZED && !(var == LA_GATED_DELTA && dt == LA_BF16))
-        return LA_ERR_UNSUPPORTED;
+    if ((var == LA_GATED_DELTA || var == LA_VECTOR_DECAY) && dt != LA_BF16) return LA_ERR_UNSUPPORTED;
     if (C != 64) return LA_ERR_UNSUPPORTED;
     if ((d_k != 32 && d_k != 64 && d_k != 128) || (d_v != 32 && d_v != 64 && d_v != 128))
         return LA_ERR_UNSUPPORTED;
@@ -325,6 +324,23 @@ hipError_t dispatch_norm_post(int d_k, const NormArgs &a, hipStream_t st) {
         case 64: return launch_norm_bwd_post<TI, 64>(a, st);
         case 128: return launch_norm_bwd_post<TI, 128>(a, st);
     }
+    return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_vdecay_bwd(int d_k, int d_v, const BwdArgs &a, hipStream_t st) {
+#define LA_VD_BWD_DV(DK)                                           \
+    switch (d_v) {                                                 \
+        case 32: return launch_vdecay_bwd<DK, 32>(a, st);          \
+        case 64: return launch_vdecay_bwd<DK, 64>(a, st);          \
+        case 128: return launch_vdecay_bwd<DK, 128>(a, st);        \
+    }                                                              \
+    break;
+    switch (d_k) {
+        case 32: LA_VD_BWD_DV(32)
+        case 64: LA_VD_BWD_DV(64)
+        case 128: LA_VD_BWD_DV(128)
+    }
+#undef LA_VD_BWD_DV
     return hipErrorInvalidValue;
 }
 
@@ -934,8 +950,9 @@ la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k
     la_status s = check_bwd_shape(var, dt, B, H, L, d_k, d_v, C);
     if (s != LA_OK) return s;
     const bool tok = L > 0, gdn = var == LA_GATED_DELTA, norm = var == LA_NORMALIZED;
+    const bool vec = var == LA_VECTOR_DECAY;
     if (tok && (!q || !k || !v || !d_o || !dq || !dk || !dv)) return LA_ERR_INVALID_ARG;
-    if (var == LA_DECAY && tok && !log_gate) return LA_ERR_INVALID_ARG;
+    if ((var == LA_DECAY || vec) && tok && !log_gate) return LA_ERR_INVALID_ARG;
     if ((var == LA_PLAIN || norm) && (log_gate || d_log_gate)) return LA_ERR_INVALID_ARG;
     if (d_log_gate && !log_gate && tok) return LA_ERR_INVALID_ARG;
     if (gdn ? (tok && !beta) : (beta || d_beta)) return LA_ERR_INVALID_ARG;
@@ -948,13 +965,14 @@ la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k
     const size_t es = elem_size(dt);
     const size_t qk_b = (size_t)BH * L * d_k * es, v_b = (size_t)BH * L * d_v * es;
     const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4, z_b = (size_t)BH * d_k * 4;
+    const size_t lg_b = vec ? g_b * d_k : g_b;  // per-channel gates: [B, H, L, d_k]
     const BwdLayout lay = bwd_layout(var, dt, BH, L, d_k, d_v);
     if (!workspace || workspace_bytes < lay.total) return LA_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LA_ERR_INVALID_ARG;
-    const Span ins[] = {{q, qk_b},    {k, qk_b},        {v, v_b},    {log_gate, g_b},    {beta, g_b},
+    const Span ins[] = {{q, qk_b},    {k, qk_b},        {v, v_b},    {log_gate, lg_b},   {beta, g_b},
                         {state_in, s_b}, {z_in, z_b},   {d_o, v_b},  {d_state_out, s_b}, {d_z_out, z_b}};
     const Span outs[] = {{dq, (size_t)BH * L * d_k * 4}, {dk, (size_t)BH * L * d_k * 4},
-                         {dv, (size_t)BH * L * d_v * 4}, {d_log_gate, g_b}, {d_beta, g_b},
+                         {dv, (size_t)BH * L * d_v * 4}, {d_log_gate, lg_b}, {d_beta, g_b},
                          {d_state_in, s_b}, {d_z_in, z_b}, {workspace, lay.total}};
     for (size_t o = 0; o < sizeof(outs) / sizeof(outs[0]); ++o) {
         for (const Span &in : ins)
@@ -977,6 +995,7 @@ la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k
     a.BH = (int)BH; a.L = L; a.dv = d_v; a.nsplit = 1;
     const int nch = (L + 63) / 64;
     hipError_t e;
+    if (vec) return from_hip(dispatch_vdecay_bwd(d_k, d_v, a, st));
     if (gdn) {
         a.beta = beta; a.gbeta = d_beta;
         a.w = ws + lay.w; a.u = ws + lay.u; a.du = ws + lay.du; a.t = ws + lay.t;

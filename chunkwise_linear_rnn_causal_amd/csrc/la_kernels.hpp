@@ -77,11 +77,11 @@ struct ConvArgs {
 // Backward pass of the chunk forward (C = 64). Gradients are fp32.
 struct BwdArgs {
     const void *q, *k, *v, *dout;  // [BH, L, DK], [BH, L, DK], [BH, L, dv], [BH, L, dv] (input type)
-    const float *lg;               // [BH, L] log-gates or nullptr (plain)
+    const float *lg;               // [BH, L] log-gates or nullptr (plain); [BH, L, DK] per channel
     const float *s_in;             // [BH, DK, dv] initial state or nullptr
     const float *ds_out;           // [BH, DK, dv] gradient of the final state or nullptr
     float *gq, *gk, *gv;           // gradients of q, k, v: [BH, L, DK], [BH, L, DK], [BH, L, dv]
-    float *glg;                    // gradient of the log-gates [BH, L] or nullptr
+    float *glg;                    // gradient of the log-gates (the shape of lg) or nullptr
     float *gs_in;                  // gradient of the initial state [BH, DK, dv] or nullptr
     void *hs, *dhs;                // workspace: per-chunk states / state gradients [BH, nchunks, DK, dv] (operand type)
     float *s_last;                 // workspace: final state [BH, DK, dv]
@@ -134,6 +134,12 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t st);
 // log-gate gradient (gdn_bwd_impl.hpp).
 template <int DK, int DV>
 hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
+
+// Backward pass of the per-key-channel decay, bf16 inputs (C = 64): the forward
+// and reverse state scans, then the per-chunk gradients with the gate gradient
+// (vdecay_bwd_impl.hpp). BwdArgs::lg and ::glg are [BH, L, DK] there.
+template <int DK, int DV>
+hipError_t launch_vdecay_bwd(const BwdArgs &a, hipStream_t st);
 
 // Backward pass of the normalized variant around the plain one
 // (norm_bwd_impl.hpp): rho, g and the chunk sums before it, the normalizer terms

@@ -272,8 +272,16 @@ la_status la_chunk_fwd_conv(la_variant var, la_dtype dt, la_dtype o_dt, const vo
  * q_t e^{G_t}, k_t e^{-G_t} (LA_GATED_DELTA: v_t e^{-G_t}) and e^{G_L}, so
  * d_log_gate_t = sum_{u>=t} (q_u . dq_u - k_u . dk_u) + <d_state_out, S_L>
  * (LA_GATED_DELTA: q_u . dq_u - v_u . dv_u).
- *   var          LA_PLAIN, LA_NORMALIZED, LA_DECAY, or LA_GATED_DELTA with
- *                dt = LA_BF16 (LA_VECTOR_DECAY: LA_ERR_UNSUPPORTED). For
+ *   var          LA_PLAIN, LA_NORMALIZED, LA_DECAY, or LA_GATED_DELTA and
+ *                LA_VECTOR_DECAY with dt = LA_BF16 (LA_F32: LA_ERR_UNSUPPORTED).
+ *                LA_VECTOR_DECAY: the gate-difference identity holds per key
+ *                channel, restarted at every chunk end c:
+ *                d_log_gate_t[i] = sum_{u>=t in the chunk} (q_u[i] dq_u[i] -
+ *                k_u[i] dk_u[i]) + sum_j dS_c[i][j] S_c[i][j], with S_c the state
+ *                after the chunk and dS_c its gradient (tensorplay section 5.2,
+ *                the per-channel form (Q (.) B)(K / B)^T); gates below -10 are
+ *                taken at -10, as in la_chunk_fwd, and the gradient reported for
+ *                them is the one at -10. For
  *                LA_NORMALIZED, o = n / den with n the plain output and
  *                den_t = q_t . z_t, so the output gradient splits into the plain
  *                backward of do_t / den_t and a normalizer term with
@@ -287,13 +295,15 @@ la_status la_chunk_fwd_conv(la_variant var, la_dtype dt, la_dtype o_dt, const vo
  *                (32, 128) and (128, 32) (else LA_ERR_UNSUPPORTED).
  *   dt           dtype of q, k, v and d_o (LA_BF16 or LA_F32); every gradient
  *                is float32.
- *   q, k, v, log_gate, beta, state_in   as given to la_chunk_fwd (beta:
+ *   q, k, v, log_gate, beta, state_in   as given to la_chunk_fwd (log_gate
+ *                [B,H,L,d_k] for LA_VECTOR_DECAY, required when L > 0; beta:
  *                LA_GATED_DELTA only, required when L > 0; log_gate optional
  *                there, NULL = DeltaNet).
  *   d_o          [B,H,L,d_v] in dt, required when L > 0.
  *   d_state_out  [B,H,d_k,d_v] float32 or NULL (zero).
  *   dq, dk       [B,H,L,d_k] float32; dv [B,H,L,d_v] float32; required when L > 0.
- *   d_log_gate   [B,H,L] float32 or NULL (not computed); only with a log_gate.
+ *   d_log_gate   [B,H,L] float32 ([B,H,L,d_k] for LA_VECTOR_DECAY) or NULL (not
+ *                computed); only with a log_gate.
  *   d_beta       [B,H,L] float32 or NULL (not computed); LA_GATED_DELTA only.
  *   d_state_in   [B,H,d_k,d_v] float32 or NULL (not written).
  *   z_in, d_z_out  [B,H,d_k] float32 or NULL (zero): the normalizer given to

@@ -202,6 +202,9 @@ def test_bwd_workspace_size():
     assert st == 0 and n == (2 * states + r(6 * 64 * 32 * 4) + r(6 * 100 * 4) + r(6 * 128 * 64 * 2)
                              + 2 * r(6 * 128 * 32 * 2) + r(6 * 2 * 64 * 64 * 2))
     assert bwd_wsize(var=GDN, dt=F32)[0] == UNSUPPORTED
+    # per-channel decay (bf16 only): the decay layout
+    assert bwd_wsize(var=VDECAY) == bwd_wsize()
+    assert bwd_wsize(var=VDECAY, dt=F32)[0] == UNSUPPORTED
     # normalized: also the forward's fp32 output, den, rho, g per token, two d_k sums per chunk
     # (fp32 operands: fp32 states, and for bf16 inputs fp32 copies of q, k, v, d_o)
     st, n = bwd_wsize(var=NORM)
@@ -217,7 +220,9 @@ def test_bwd_workspace_size():
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(var=9), INVALID), (dict(var=NORM), INVALID), (dict(var=VDECAY), UNSUPPORTED),
+    (dict(var=9), INVALID), (dict(var=NORM), INVALID), (dict(var=VDECAY, dt=F32), UNSUPPORTED),
+    (dict(var=VDECAY, lg=None), INVALID),               # the per-channel decay needs its gates
+    (dict(var=VDECAY, dlg=FAKE + 0x300000 + 0x8000), INVALID),  # d_log_gate inside the [B,H,L,d_k] gates
     (dict(z_in=FAKE + 0x600000), INVALID),              # the normalizer is the normalized variant's
     (dict(var=NORM, lg=None, dzi=FAKE + 0x400000), INVALID),   # d_z_in inside d_o
     (dict(C=128), UNSUPPORTED), (dict(dk_=96), UNSUPPORTED), (dict(B=0), INVALID),
@@ -248,6 +253,7 @@ def test_chunk_bwd_valid_arguments_reach_the_device_check():
     assert bwd(L=0, q=None, k=None, v=None, do=None, dq=None, dk=None, dv=None) not in (INVALID, UNSUPPORTED)
     assert bwd(var=GDN, beta=FAKE + 0x500000, dbeta=0x830000000, dlg=0x840000000) not in (INVALID, UNSUPPORTED)
     assert bwd(var=GDN, lg=None, beta=FAKE + 0x500000) not in (INVALID, UNSUPPORTED)
+    assert bwd(var=VDECAY, dlg=0x830000000) not in (INVALID, UNSUPPORTED)
     assert bwd(var=NORM, lg=None, z_in=FAKE + 0x600000, dzo=FAKE + 0x610000,
                dzi=0x830000000) not in (INVALID, UNSUPPORTED)
 

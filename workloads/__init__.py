@@ -68,6 +68,10 @@ CONFIGS: Dict[str, dict] = {
     "gated_delta_bwd_bf16_b2h16_l8192_d128": dict(
         kind="bwd", variant="gated_delta", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, C=64,
         recipe="gdn"),
+    # the backward pass of the per-key-channel decay workload (output gradient dO ~ N(0, 1))
+    "vector_decay_bwd_bf16_b4h32_l8192_d128": dict(
+        kind="bwd", variant="vector_decay", dtype="bf16", B=4, H=32, L=8192, dk=128, dv=128, C=64,
+        recipe="gla"),
     # the backward pass of the normalized workload (output gradient dO ~ N(0, 1))
     "normalized_bwd_bf16_b8h16_l2048_d64": dict(
         kind="bwd", variant="normalized", dtype="bf16", B=8, H=16, L=2048, dk=64, dv=64, C=64,
