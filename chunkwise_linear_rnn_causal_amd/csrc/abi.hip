@@ -801,7 +801,8 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
     if (!dtype_pair_ok(dt, o_dt)) return LA_ERR_UNSUPPORTED;
     if (var == LA_NORMALIZED) return LA_ERR_UNSUPPORTED;
     if (N < 1 || H < 1) return LA_ERR_INVALID_ARG;
-    if ((int64_t)N * H > INT32_MAX) return LA_ERR_UNSUPPORTED;
+    // (the delta rule launches two workgroups per sequence-head)
+    if ((int64_t)N * H > (var == LA_GATED_DELTA ? INT32_MAX / 2 : INT32_MAX)) return LA_ERR_UNSUPPORTED;
     if ((d_k != 32 && d_k != 64 && d_k != 128) || (d_v != 32 && d_v != 64 && d_v != 128))
         return LA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !state || !o) return LA_ERR_INVALID_ARG;

@@ -13,10 +13,12 @@
 // The delta rule needs the retrieval r over all rows before any row is updated:
 // the state stays in registers between the two reductions. The fp32 state dominates the
 // traffic (2 x d_k x d_v x 4 bytes per head and step), so the kernel is a
-// streaming read-modify-write: one 256-thread workgroup per head, each thread
+// streaming read-modify-write: one 256-thread workgroup per head (or head and
+// value-column slice), each thread
 // owning d_k / RG consecutive rows of one 16-byte column group, all of its state
 // loads issued before any arithmetic, non-temporal loads and stores for the state
 // (it is touched once per step), and a shuffle + LDS reduction of o over rows.
+// The delta rule runs two workgroups per head, each on half of the value columns.
 #pragma once
 
 #include "la_common.hpp"
@@ -24,29 +26,41 @@
 
 namespace la {
 
+// Value columns per workgroup. The retrieval r = S^T k of the delta rule is per
+// value column, so a head's columns split over workgroups with no exchange; the
+// delta rule holds its state slice across the retrieval barrier, and halving the
+// slice halves the registers that holds (64 columns at d_v = 128: 8 rows of
+// 16 bytes per thread instead of 16).
+template <int VAR, int DV>
+constexpr int decode_cols() {
+    return (VAR == V_GDN && DV > 32) ? DV / 2 : DV;
+}
+
 // Occupancy: the state in flight is what keeps HBM busy. Without the retrieval
 // pass a wave needs 65 registers when the compiler may use up to 72, which gives
-// 7 waves per SIMD (6 at its own choice of 74; 8 at 64 was no faster). The
-// delta rule holds the whole state across its barrier and is left to the
-// compiler (127 registers, 4 waves per SIMD; a cap at 5 waves spills), and so
-// is the per-channel gate with fp32 rows (a cap at 7 waves spills).
+// 7 waves per SIMD (6 at its own choice of 74; 8 at 64 was no faster). The delta
+// rule on half-width slices fits the same bound. The per-channel gate with fp32
+// rows is left to the compiler (a cap at 7 waves spills).
 template <int VAR, typename TI>
 constexpr int decode_min_waves() {
-    return (VAR == V_GDN || (VAR == V_VDECAY && sizeof(TI) == 4)) ? 1 : 7;
+    return (VAR == V_VDECAY && sizeof(TI) == 4) ? 1 : 7;
 }
 
 template <int VAR, typename TI, typename TO, int DK, int DV>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(decode_min_waves<VAR, TI>(), 8)))
 decode_kernel(DecodeArgs a) {
-    constexpr int CG = DV / 4;        // 16-byte column groups per row
+    constexpr int CW = decode_cols<VAR, DV>();  // value columns of this workgroup
+    constexpr int NSL = DV / CW;
+    constexpr int CG = CW / 4;        // 16-byte column groups per row
     constexpr int RG = 256 / CG;      // row groups
     constexpr int RPT = DK / RG;      // rows per thread
     static_assert(RPT >= 1 && DK % RG == 0, "shape");
 
     __shared__ f32x4 red[4][CG];
 
-    const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
-    const size_t h = blockIdx.x;
+    const int tid = threadIdx.x, rg = tid / CG;
+    const size_t h = blockIdx.x / NSL;
+    const int cg = tid % CG + (int)(blockIdx.x % NSL) * CG;  // column group within the head's row
     float *S = a.S + h * DK * DV + (size_t)rg * RPT * DV + 4 * cg;
 
     f32x4 s[RPT];
@@ -73,9 +87,10 @@ decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
         }
-        if ((tid & 63) < CG) buf[wv][cg] = acc;
+        const int lc = tid % CG;
+        if ((tid & 63) < CG) buf[wv][lc] = acc;
         __syncthreads();
-        return buf[0][cg] + buf[1][cg] + buf[2][cg] + buf[3][cg];
+        return buf[0][lc] + buf[1][lc] + buf[2][lc] + buf[3][lc];
     };
 
     // new state column group: ns = al * s + kr * u (u per column group)
@@ -112,17 +127,18 @@ decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
     }
-    if ((tid & 63) < CG) red[wv][cg] = acc;
+    if ((tid & 63) < CG) red[wv][tid % CG] = acc;
     __syncthreads();
     if (tid < CG) {
         const f32x4 o = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-        st4<TO>((TO *)a.o + h * DV + 4 * tid, o);
+        st4<TO>((TO *)a.o + h * DV + 4 * cg, o);
     }
 }
 
 template <int VAR, typename TI, typename TO, int DK, int DV>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL((decode_kernel<VAR, TI, TO, DK, DV>), dim3(a.NH), dim3(256), 0, st, a);
+    constexpr int NSL = DV / decode_cols<VAR, DV>();
+    hipLaunchKernelGGL((decode_kernel<VAR, TI, TO, DK, DV>), dim3(a.NH * NSL), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
