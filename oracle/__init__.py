@@ -21,7 +21,7 @@ import numpy as np
 
 from . import build as _build
 
-VARIANT_ID = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3, "vector_decay": 4}
+VARIANT_ID = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3, "vector_decay": 4, "kda": 5}
 
 _lib = None
 _lib_path = None
@@ -74,7 +74,7 @@ def forward(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in
     """Run the recurrence over every leading (batch, head) slice.
 
     q, k: [..., L, dk]; v: [..., L, dv]; log_gate, beta: [..., L]
-    ("vector_decay": log_gate [..., L, dk]); state_in: [..., dk, dv]; z_in: [..., dk]. Returns (o [..., L, dv],
+    ("vector_decay", "kda": log_gate [..., L, dk]); state_in: [..., dk, dv]; z_in: [..., dk]. Returns (o [..., L, dv],
     state_out [..., dk, dv], z_out [..., dk]) in float64.
     """
     lib = lib or load()
@@ -86,7 +86,7 @@ def forward(variant: str, q, k, v, log_gate=None, beta=None, state_in=None, z_in
     assert k.shape == q.shape and v.shape[:-1] == q.shape[:-1]
     lg, be = _c64(log_gate), _c64(beta)
     s_in, zi = _c64(state_in), _c64(z_in)
-    lg_shape = lead + ((L, dk) if variant == "vector_decay" else (L,))
+    lg_shape = lead + ((L, dk) if variant in ("vector_decay", "kda") else (L,))
     for x, shp in ((lg, lg_shape), (be, lead + (L,)), (s_in, lead + (dk, dv)), (zi, lead + (dk,))):
         assert x is None or x.shape == shp, (x.shape, shp)
     o = np.zeros(lead + (L, dv), np.float64)
@@ -103,8 +103,8 @@ def decode_step(variant: str, q, k, v, log_gate, state, beta=None, threads: int 
                 copy: bool = True):
     """One in-place decode step on a copy of ``state``; returns (o, new_state).
 
-    q, k: [..., dk]; v: [..., dv]; log_gate, beta: [...] ("vector_decay": log_gate
-    [..., dk]); state: [..., dk, dv].
+    q, k: [..., dk]; v: [..., dv]; log_gate, beta: [...] ("vector_decay", "kda":
+    log_gate [..., dk]); state: [..., dk, dv].
     beta is required for "gated_delta" (log_gate may then be None: alpha = 1).
     copy=False updates ``state`` itself (a C-contiguous float64 array) in place.
     """

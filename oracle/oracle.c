@@ -32,6 +32,13 @@
  *                This is the transpose of S'_t = S'_{t-1} alpha_t (I - beta_t k_t
  *                k_t^T) + beta_t v_t k_t^T, o_t = S'_t q_t (wln20, Gated DeltaNet
  *                section; tensorplay section 6.2 reparameterised delta rule).
+ *   KDA          S <- Diag(exp(l)) S, l in R^{dk}; r = S^T k; S <- S + beta k (v - r)^T;
+ *                o = S^T q. That is S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1}
+ *                + beta_t k_t v_t^T (wln20, Kimi Delta Attention section: the
+ *                gated delta rule with the scalar gate widened to a diagonal one,
+ *                read in the d_k x d_v orientation, where the diagonal acts on
+ *                the key channels and the delta-rule factor multiplies from the
+ *                left, as the page writes it).
  *
  * Inputs are float64 copies of exactly the values the GPU reads (bf16 or fp32
  * widened without rounding). Gates are log-gates l = log(gamma) or log(alpha);
@@ -39,7 +46,7 @@
  *
  * Layouts (all row-major, contiguous):
  *   q, k  [BH, L, dk]     v, o  [BH, L, dv]     log_gate, beta  [BH, L]
- *   (VECTOR_DECAY: log_gate [BH, L, dk])
+ *   (VECTOR_DECAY, KDA: log_gate [BH, L, dk])
  *   state_in, state_out  [BH, dk, dv]          z_in, z_out  [BH, dk]
  * NULL state_in / z_in mean zero; NULL state_out / z_out mean "not returned".
  */
@@ -55,6 +62,7 @@
 #define OR_DECAY 2
 #define OR_GATED_DELTA 3
 #define OR_VECTOR_DECAY 4
+#define OR_KDA 5
 
 #define OR_OK 0
 #define OR_BAD_ARG 1
@@ -101,6 +109,21 @@ static int run_head(int variant, const double *q, const double *k, const double 
                 for (long j = 0; j < dv; ++j)
                     S[i * dv + j] = g * S[i * dv + j] + kt[i] * vt[j];
             }
+        } else if (variant == OR_KDA) {
+            /* the per-channel decay first, then the delta rule on the decayed state */
+            const double bk = beta[t];
+            for (long i = 0; i < dk; ++i) {
+                const double ai = exp(lg[t * dk + i]);
+                for (long j = 0; j < dv; ++j) S[i * dv + j] *= ai;
+            }
+            for (long j = 0; j < dv; ++j) {
+                double rj = 0.0;
+                for (long i = 0; i < dk; ++i) rj += kt[i] * S[i * dv + j];
+                r[j] = rj;
+            }
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j)
+                    S[i * dv + j] += bk * kt[i] * (vt[j] - r[j]);
         } else { /* OR_GATED_DELTA */
             double a = lg ? exp(lg[t]) : 1.0;
             double b = beta[t];
@@ -140,12 +163,13 @@ int oracle_forward(int variant, const double *q, const double *k, const double *
                    const double *z_in, double *o, double *state_out, double *z_out,
                    long BH, long L, long dk, long dv, int nthreads)
 {
-    if (variant < OR_PLAIN || variant > OR_VECTOR_DECAY) return OR_BAD_ARG;
+    if (variant < OR_PLAIN || variant > OR_KDA) return OR_BAD_ARG;
     if (BH < 0 || L < 0 || dk <= 0 || dv <= 0) return OR_BAD_ARG;
     if ((BH > 0 && L > 0) && (!q || !k || !v || !o)) return OR_BAD_ARG;
-    if ((variant == OR_DECAY || variant == OR_VECTOR_DECAY) && L > 0 && !log_gate) return OR_BAD_ARG;
-    const long gstride = variant == OR_VECTOR_DECAY ? L * dk : L;
-    if (variant == OR_GATED_DELTA && L > 0 && !beta) return OR_BAD_ARG;
+    if ((variant == OR_DECAY || variant == OR_VECTOR_DECAY || variant == OR_KDA) && L > 0 && !log_gate)
+        return OR_BAD_ARG;
+    const long gstride = (variant == OR_VECTOR_DECAY || variant == OR_KDA) ? L * dk : L;
+    if ((variant == OR_GATED_DELTA || variant == OR_KDA) && L > 0 && !beta) return OR_BAD_ARG;
 
     int status = OR_OK;
 #ifdef _OPENMP
@@ -171,19 +195,21 @@ int oracle_forward(int variant, const double *q, const double *k, const double *
  *   GATED_DELTA                   r = S^T k; S <- a (S - b k r^T) + b k v^T,
  *                                 a = exp(l) (1 when log_gate is NULL), b = beta
  *                                 (wln20 Gated DeltaNet section)
+ *   KDA                           S <- Diag(exp(l)) S; r = S^T k; S <- S + b k (v - r)^T,
+ *                                 l [dk] per head (wln20 Kimi Delta Attention section)
  * then o = S^T q. Layouts: q, k [NH, dk]; v, o [NH, dv]; log_gate, beta [NH];
- * state [NH, dk, dv] (VECTOR_DECAY: log_gate [NH, dk]).
+ * state [NH, dk, dv] (VECTOR_DECAY, KDA: log_gate [NH, dk]).
  */
 int oracle_decode_step(int variant, const double *q, const double *k, const double *v,
                        const double *log_gate, const double *beta, double *state, double *o,
                        long NH, long dk, long dv, int nthreads)
 {
     if (variant != OR_PLAIN && variant != OR_DECAY && variant != OR_GATED_DELTA &&
-        variant != OR_VECTOR_DECAY)
+        variant != OR_VECTOR_DECAY && variant != OR_KDA)
         return OR_BAD_ARG;
-    if ((variant == OR_DECAY || variant == OR_VECTOR_DECAY) && !log_gate) return OR_BAD_ARG;
-    const long gstride = variant == OR_VECTOR_DECAY ? dk : 1;
-    if (variant == OR_GATED_DELTA && !beta) return OR_BAD_ARG;
+    if ((variant == OR_DECAY || variant == OR_VECTOR_DECAY || variant == OR_KDA) && !log_gate) return OR_BAD_ARG;
+    const long gstride = (variant == OR_VECTOR_DECAY || variant == OR_KDA) ? dk : 1;
+    if ((variant == OR_GATED_DELTA || variant == OR_KDA) && !beta) return OR_BAD_ARG;
     if (NH < 0 || dk <= 0 || dv <= 0 || !state) return OR_BAD_ARG;
     int status = OR_OK;
 #ifdef _OPENMP

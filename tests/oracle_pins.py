@@ -424,6 +424,115 @@ def pin_gdn_chunkwise_wy(lib):
 
 
 # ---------------------------------------------------------------------------
+# KDA: the delta rule with a per-key-channel gate
+# ---------------------------------------------------------------------------
+def kda_chunkwise_wy(q, k, v, lg, beta, C, s0=None):
+    """Chunk form of Kimi Delta Attention, S_t = (I - beta_t k_t k_t^T) Diag(alpha_t)
+    S_{t-1} + beta_t k_t v_t^T (wln20, Kimi Delta Attention section), worked out
+    like the scalar-gate WY form: with the per-channel gate the update is
+    S_t = Diag(alpha_t) S_{t-1} + k_t u_t^T, u_t = beta_t (v_t - S_{t-1}^T (alpha_t (.) k_t)).
+    Within a chunk, with G_r the per-channel log-gate cumsum and Gam_r = exp(G_r),
+    S_{t-1}^T (alpha_t (.) k_t) = S_0^T (Gam_t (.) k_t) + sum_{s<t} u_s (Gam_t (.) k_t).(k_s / Gam_s),
+    so (I + diag(beta) A) U = diag(beta) (V - (K (.) Gam) S_0), A = strict_lower((K (.) Gam)(K / Gam)^T):
+      T = (I + diag(beta) A)^-1,  W = T diag(beta) (K (.) Gam),  U~ = T diag(beta) V,  U = U~ - W S_0
+      O = (Q (.) Gam) S_0 + tril((Q (.) Gam)(K / Gam)^T) U
+      S_C = Diag(Gam_C) S_0 + (K (.) Gam_C / Gam)^T U"""
+    L, dk = q.shape
+    dv = v.shape[1]
+    S = np.zeros((dk, dv)) if s0 is None else s0.copy()
+    o = np.zeros((L, dv))
+    for c0 in range(0, L, C):
+        sl = slice(c0, min(L, c0 + C))
+        Q, K, V, b = q[sl], k[sl], v[sl], beta[sl]
+        n = Q.shape[0]
+        Gam = np.exp(np.cumsum(lg[sl], axis=0))
+        A = np.tril((K * Gam) @ (K / Gam).T, -1)
+        T = np.linalg.inv(np.eye(n) + b[:, None] * A)
+        W = T @ (b[:, None] * (K * Gam))
+        U = T @ (b[:, None] * V) - W @ S
+        o[sl] = (Q * Gam) @ S + np.tril((Q * Gam) @ (K / Gam).T) @ U
+        S = Gam[-1][:, None] * S + (K * (Gam[-1] / Gam)).T @ U
+    return o, S
+
+
+def _kda_inputs(seed, L, dk, dv, gate_scale=1.0):
+    r = _rng(seed)
+    q, k = _unit(r.standard_normal((L, dk))), _unit(r.standard_normal((L, dk)))
+    v = r.standard_normal((L, dv))
+    lg = np.log(1.0 / (1.0 + np.exp(-r.normal(3.0, 1.0, (L, dk))))) * gate_scale
+    beta = 1.0 / (1.0 + np.exp(-r.normal(0.0, 1.0, L)))
+    s0 = r.standard_normal((dk, dv)) * 0.3
+    return q, k, v, lg, beta, s0
+
+
+def pin_kda_chunkwise_wy(lib):
+    """The chunk algebra above equals the oracle's recurrence for C in {1, 4, 16, L}
+    (tensorplay section 3.3: C = 1 is the recurrent form, C = L the parallel one)."""
+    L, dk, dv = 48, 8, 6
+    q, k, v, lg, beta, s0 = _kda_inputs(30, L, dk, dv)
+    o, s, _ = oracle.forward("kda", q[None], k[None], v[None], log_gate=lg[None], beta=beta[None],
+                             state_in=s0[None], lib=lib)
+    for C in (1, 4, 16, L):
+        oc, sc = kda_chunkwise_wy(q, k, v, lg, beta, C, s0)
+        assert _rel(o[0], oc) <= 1e-10, (C, _rel(o[0], oc))
+        assert _rel(s[0], sc) <= 1e-10, C
+
+
+def pin_kda_uniform_gate_is_gdn(lib):
+    """The same gate on every key channel is the scalar-gate delta rule: Diag(alpha)
+    = alpha I commutes with (I - beta k k^T)."""
+    L, dk, dv = 23, 6, 5
+    q, k, v, lg, beta, s0 = _kda_inputs(31, L, dk, dv)
+    g1 = lg[:, 0]
+    o1, s1, _ = oracle.forward("kda", q[None], k[None], v[None], log_gate=np.repeat(g1[:, None], dk, 1)[None],
+                               beta=beta[None], state_in=s0[None], lib=lib)
+    o2, s2, _ = oracle.forward("gated_delta", q[None], k[None], v[None], log_gate=g1[None], beta=beta[None],
+                               state_in=s0[None], lib=lib)
+    assert _rel(o1, o2) <= 1e-12 and _rel(s1, s2) <= 1e-12
+
+
+def pin_kda_beta_zero_pure_decay(lib):
+    """beta == 0: nothing is written, S_t = Diag(prod alpha) S_0 channel by channel."""
+    L, dk, dv = 15, 4, 3
+    q, k, v, lg, _, s0 = _kda_inputs(32, L, dk, dv)
+    o, s, _ = oracle.forward("kda", q[None], k[None], v[None], log_gate=lg[None], beta=np.zeros((1, L)),
+                             state_in=s0[None], lib=lib)
+    Gam = np.exp(np.cumsum(lg, axis=0))
+    assert _rel(o[0], (q * Gam) @ s0) <= 1e-12
+    assert _rel(s[0], Gam[-1][:, None] * s0) <= 1e-12
+
+
+def pin_kda_unit_key_overwrite(lib):
+    """beta = 1 with a unit key overwrites what the key retrieves, whatever the
+    gate: S_t^T k_t = (Diag(alpha) S)^T (I - k k^T) k + v (k . k) = v_t."""
+    L, dk, dv = 9, 5, 4
+    q, k, v, lg, _, s0 = _kda_inputs(33, L, dk, dv, gate_scale=4.0)
+    for t in range(1, L + 1):
+        _, s, _ = oracle.forward("kda", q[None, :t], k[None, :t], v[None, :t], log_gate=lg[None, :t],
+                                 beta=np.ones((1, t)), state_in=s0[None], lib=lib)
+        assert np.max(np.abs(s[0].T @ k[t - 1] - v[t - 1])) <= 1e-12
+
+
+def pin_kda_decode_and_resume(lib):
+    """The decode step continues a prefill exactly, and a split sequence carried
+    through the state equals one pass."""
+    L, dk, dv = 20, 6, 5
+    q, k, v, lg, beta, s0 = _kda_inputs(34, L, dk, dv)
+    o, s, _ = oracle.forward("kda", q[None], k[None], v[None], log_gate=lg[None], beta=beta[None],
+                             state_in=s0[None], lib=lib)
+    t = 13
+    op, sp, _ = oracle.forward("kda", q[None, :t], k[None, :t], v[None, :t], log_gate=lg[None, :t],
+                               beta=beta[None, :t], state_in=s0[None], lib=lib)
+    od, sd = oracle.decode_step("kda", q[None, t], k[None, t], v[None, t], lg[None, t], sp, beta=beta[None, t],
+                                lib=lib)
+    oc, _ = kda_chunkwise_wy(q[: t + 1], k[: t + 1], v[: t + 1], lg[: t + 1], beta[: t + 1], 4, s0)
+    assert _rel(od[0], oc[t]) <= 1e-10
+    ob, sb, _ = oracle.forward("kda", q[None, t:], k[None, t:], v[None, t:], log_gate=lg[None, t:],
+                               beta=beta[None, t:], state_in=sp, lib=lib)
+    assert _rel(np.concatenate([op[0], ob[0]]), o[0]) <= 1e-12 and _rel(sb, s) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
 # DECODE and state carry
 # ---------------------------------------------------------------------------
 def pin_decode_one_decay_step(lib):
@@ -939,4 +1048,6 @@ ALL_PINS = [
     pin_backward_finite_differences, pin_backward_plain_closed_form, pin_backward_gate_identity,
     pin_backward_gdn_finite_differences, pin_backward_gdn_reductions, pin_backward_gdn_gate_identity,
     pin_backward_norm_finite_differences, pin_backward_norm_constant_v,
+    pin_kda_chunkwise_wy, pin_kda_uniform_gate_is_gdn, pin_kda_beta_zero_pure_decay,
+    pin_kda_unit_key_overwrite, pin_kda_decode_and_resume,
 ]

@@ -34,6 +34,11 @@ MUTANTS = {
                                      "double g = exp(lg[t * dk + (dk - 1 - i)]);"),
     "vector_gate_one_token_late": ("double g = exp(lg[t * dk + i]);",
                                    "double g = exp(lg[(t > 0 ? t - 1 : 0) * dk + i]);"),
+    "kda_gate_dropped": ("for (long j = 0; j < dv; ++j) S[i * dv + j] *= ai;", "(void)ai;"),
+    "kda_gate_of_channel_zero": ("const double ai = exp(lg[t * dk + i]);", "const double ai = exp(lg[t * dk]);"),
+    "kda_write_sign": ("S[i * dv + j] += bk * kt[i] * (vt[j] - r[j]);", "S[i * dv + j] += bk * kt[i] * (vt[j] + r[j]);"),
+    "kda_retrieve_before_decay": ("for (long i = 0; i < dk; ++i) rj += kt[i] * S[i * dv + j];",
+                                  "for (long i = 0; i < dk; ++i) rj += kt[i] * S[i * dv + j] / exp(lg[t * dk + i]);"),
     "bwd_dq_reads_old_state": ("for (long j = 0; j < dv_; ++j) acc += Sa[i * dv_ + j] * dot[j];",
                                "for (long j = 0; j < dv_; ++j) acc += Sb[i * dv_ + j] * dot[j];"),
     "bwd_state_grad_not_decayed": ("for (long i = 0; i < D; ++i) dS[i] *= g;", "(void)g;"),
