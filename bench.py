@@ -92,7 +92,7 @@ def chunk_work(c: dict) -> tuple[float, float, float]:
     B, H, L, dk, dv, C = c["B"], c["H"], c["L"], c["dk"], c["dv"], c["C"]
     BH = B * H
     esz = 2 if c["dtype"] == "bf16" else 4
-    if c["variant"] == "gated_delta":
+    if c["variant"] in ("gated_delta", "kda"):
         per_tok = (2 * C * C * (3 * dk + 2 * dv) + 6 * C * dk * dv + C ** 3 / 3) / C
     else:
         per_tok = 2 * C * (dk + dv) + 4 * dk * dv
@@ -100,9 +100,9 @@ def chunk_work(c: dict) -> tuple[float, float, float]:
     nbytes = BH * L * (2 * dk + dv) * esz                        # q, k, v in
     if c["variant"] in ("decay", "gated_delta"):
         nbytes += BH * L * 4                                     # log-gates
-    if c["variant"] == "vector_decay":
+    if c["variant"] in ("vector_decay", "kda"):
         nbytes += BH * L * dk * 4                                # one log-gate per key channel
-    if c["variant"] == "gated_delta":
+    if c["variant"] in ("gated_delta", "kda"):
         nbytes += BH * L * 4                                     # beta
     algo = nbytes + BH * L * dv * esz                            # o out in the input dtype
     launched = nbytes + BH * L * dv * (2 if o_dtype(c) == "bf16" else 4) + BH * dk * dv * 4

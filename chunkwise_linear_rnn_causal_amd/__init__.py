@@ -21,7 +21,9 @@ LIB_PATH = os.path.join(HERE, "liblinattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "linattn.h")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
-VARIANTS = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3, "vector_decay": 4}
+VARIANTS = {"plain": 0, "normalized": 1, "decay": 2, "gated_delta": 3, "vector_decay": 4, "kda": 5}
+# variants with one log-gate per key channel
+_PER_CHANNEL = ("vector_decay", "kda")
 EXPORTS = ("la_chunk_fwd_workspace_size", "la_chunk_fwd", "la_chunk_fwd_noalloc",
            "la_chunk_bwd_workspace_size", "la_chunk_bwd", "la_decode_step", "la_short_conv",
            "la_chunk_fwd_conv", "la_chunk_fwd_conv_workspace_size",
@@ -150,7 +152,7 @@ def la_chunk_fwd(variant: str, q, k, v, log_gate=None, beta=None, state_in=None,
     """Chunkwise causal linear-attention forward.
 
     q, k: [B, H, L, d_k]; v: [B, H, L, d_v] (bf16 or fp32, contiguous, on the GPU).
-    log_gate, beta: [B, H, L] fp32 ("vector_decay": log_gate [B, H, L, d_k]);
+    log_gate, beta: [B, H, L] fp32 ("vector_decay", "kda": log_gate [B, H, L, d_k]);
     state_in: [B, H, d_k, d_v] fp32;
     z_in: [B, H, d_k] fp32. Returns (o, state_out or None, z_out or None).
     o is fp32 unless out_dtype=torch.bfloat16 (bf16 inputs only) or a bf16 ``o``
@@ -197,7 +199,7 @@ def _fwd_args(variant, q, k, v, log_gate, beta, state_in, z_in, o, out_dtype, st
     f32, dev_ = torch.float32, q.device
     _check("k", k, (B, H, L, d_k), q.dtype, dev_, required=True)
     _check("v", v, (B, H, L, d_v), q.dtype, dev_, required=True)
-    gate_shape = (B, H, L, d_k) if variant == "vector_decay" else (B, H, L)
+    gate_shape = (B, H, L, d_k) if variant in _PER_CHANNEL else (B, H, L)
     _check("log_gate", log_gate, gate_shape, f32, dev_)
     _check("beta", beta, (B, H, L), f32, dev_)
     _check("state_in", state_in, (B, H, d_k, d_v), f32, dev_)
@@ -252,7 +254,7 @@ def la_decode_step(variant: str, q, k, v, log_gate, state, *, o=None, out_dtype=
     _dt(q)
     _check("k", k, (N, H, d_k), q.dtype, dev_, required=True)
     _check("v", v, (N, H, d_v), q.dtype, dev_, required=True)
-    _check("log_gate", log_gate, (N, H, d_k) if variant == "vector_decay" else (N, H), f32, dev_)
+    _check("log_gate", log_gate, (N, H, d_k) if variant in _PER_CHANNEL else (N, H), f32, dev_)
     _check("beta", beta, (N, H), f32, dev_)
     _check("state", state, (N, H, d_k, d_v), f32, dev_, required=True)
     if o is not None:
@@ -307,8 +309,7 @@ def la_chunk_bwd(variant: str, q, k, v, d_o, log_gate=None, state_in=None, d_sta
     _check("k", k, (B, H, L, d_k), q.dtype, dev_, required=True)
     _check("v", v, (B, H, L, d_v), q.dtype, dev_, required=True)
     _check("d_o", d_o, (B, H, L, d_v), q.dtype, dev_, required=True)
-    vec = variant == "vector_decay"
-    gshape = (B, H, L, d_k) if vec else (B, H, L)
+    gshape = (B, H, L, d_k) if variant in _PER_CHANNEL else (B, H, L)
     _check("log_gate", log_gate, gshape, f32, dev_)
     _check("beta", beta, (B, H, L), f32, dev_, required=gdn)
     _check("state_in", state_in, (B, H, d_k, d_v), f32, dev_)

@@ -71,9 +71,10 @@ bool head_offsets_fit(int L, int C, int d_k, int d_v) {
 // Shape checks shared by the workspace query and the forward call.
 la_status check_chunk_shape(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v,
                             int C) {
-    if (var < LA_PLAIN || var > LA_VECTOR_DECAY) return LA_ERR_INVALID_ARG;
+    if (var < LA_PLAIN || var > LA_KDA) return LA_ERR_INVALID_ARG;
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || L < 0) return LA_ERR_INVALID_ARG;
+    if (var == LA_KDA && dt != LA_BF16) return LA_ERR_UNSUPPORTED;  // fp16 serial pass only
     if (d_k != 32 && d_k != 64 && d_k != 128) return LA_ERR_UNSUPPORTED;
     if (d_v < 32 || d_v > 128 || d_v % 32 != 0) return LA_ERR_UNSUPPORTED;
     if (C != 64 && C != 128) return LA_ERR_UNSUPPORTED;
@@ -94,7 +95,7 @@ la_status check_chunk_shape(la_variant var, la_dtype dt, int B, int H, int L, in
 // which is what the second sub-chunk evaluates with the state carried from the
 // first.
 int kernel_chunk(la_variant var, la_dtype dt, int d_k, int C) {
-    if (C == 128 && (var == LA_GATED_DELTA || var == LA_VECTOR_DECAY || (dt == LA_F32 && d_k == 128)))
+    if (C == 128 && (var == LA_GATED_DELTA || var == LA_KDA || var == LA_VECTOR_DECAY || (dt == LA_F32 && d_k == 128)))
         return 64;
     return C;
 }
@@ -114,11 +115,18 @@ size_t gdn_mf_bytes(la_dtype dt, int64_t BH, int64_t Lp) {
     return dt == LA_BF16 ? (size_t)BH * Lp * 96 : 0;
 }
 
+// KDA adds the pre-scaled q and k (fp16 [BH, Lp, d_k] each) and the per-chunk
+// state decay (fp32 [BH, Lp / 64, d_k]) after the delta rule's arrays.
+size_t kda_qk_bytes(int64_t BH, int64_t Lp, int d_k) { return round_up((size_t)BH * Lp * d_k * 2, 256); }
+size_t kda_cdec_bytes(int64_t BH, int64_t Lp, int d_k) { return round_up((size_t)BH * (Lp / 64) * d_k * 4, 256); }
+
 size_t chunk_workspace(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v, int C) {
-    if (var != LA_GATED_DELTA || L == 0) return 0;
+    if ((var != LA_GATED_DELTA && var != LA_KDA) || L == 0) return 0;
     C = kernel_chunk(var, dt, d_k, C);
     const int64_t BH = (int64_t)B * H, Lp = (int64_t)((L + C - 1) / C) * C;
-    return gdn_w_bytes(dt, BH, Lp, d_k) + gdn_ut_bytes(dt, BH, Lp, d_v) + gdn_mf_bytes(dt, BH, Lp);
+    size_t b = gdn_w_bytes(dt, BH, Lp, d_k) + gdn_ut_bytes(dt, BH, Lp, d_v) + gdn_mf_bytes(dt, BH, Lp);
+    if (var == LA_KDA) b += 2 * kda_qk_bytes(BH, Lp, d_k) + kda_cdec_bytes(BH, Lp, d_k);
+    return b;
 }
 
 // Workgroup geometry of the chunk kernel: value columns per workgroup (DVT) and
@@ -136,7 +144,7 @@ constexpr int kNumCU = 256;
 
 Geometry choose_geometry(la_variant var, la_dtype dt, int64_t BH, int d_v, int C) {
     if (dt == LA_F32 || C == 128) return {32, 4};
-    if (var == LA_GATED_DELTA) return {16, 8};  // the chain kernel: 16-column slices
+    if (var == LA_GATED_DELTA || var == LA_KDA) return {16, 8};  // the chain kernel: 16-column slices
     if (d_v % 64 == 0 && BH * (d_v / 64) >= kNumCU) return {64, 8};
     return {32, 8};
 }
@@ -158,6 +166,10 @@ hipError_t dispatch_chunk(la_variant var, int C, Geometry geo, const ChunkArgs &
     if (var == LA_GATED_DELTA) {
         if constexpr (F32) return launch_chunk<V_GDN, TI, TO, DK, 32, 64, 4>(a, st);
         if constexpr (!F32) return launch_gdn_fwd<TO, DK>(a, st);
+    }
+    if (var == LA_KDA) {  // bf16 only (checked); the prepared q, k and decay are in a
+        if constexpr (!F32) return launch_gdn_fwd<TO, DK>(a, st);
+        return hipErrorInvalidValue;
     }
     if (C == 128) {
         if constexpr (!(F32 && DK == 128)) return launch_var<TI, TO, DK, 32, 128, 4>(var, a, st);
@@ -243,7 +255,8 @@ constexpr int kBwdF32MaxState = 4096;
 bool bwd_f32_fits(int d_k, int d_v) { return d_k * d_v <= kBwdF32MaxState || d_k + d_v == 160; }
 
 la_status check_bwd_shape(la_variant var, la_dtype dt, int B, int H, int L, int d_k, int d_v, int C) {
-    if (var < LA_PLAIN || var > LA_VECTOR_DECAY) return LA_ERR_INVALID_ARG;
+    if (var < LA_PLAIN || var > LA_KDA) return LA_ERR_INVALID_ARG;
+    if (var == LA_KDA) return LA_ERR_UNSUPPORTED;  // no KDA backward
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || L < 0) return LA_ERR_INVALID_ARG;
     if ((var == LA_GATED_DELTA || var == LA_VECTOR_DECAY) && dt != LA_BF16) return LA_ERR_UNSUPPORTED;
@@ -414,7 +427,7 @@ FwdSpans fwd_spans(const FwdCall &f) {
     const size_t s_b = (size_t)BH * f.d_k * f.d_v * 4, z_b = (size_t)BH * f.d_k * 4;
     return FwdSpans{{{f.q, (size_t)BH * f.L * f.d_k * es}, {f.k, (size_t)BH * f.L * f.d_k * es},
                      {f.v, (size_t)BH * f.L * f.d_v * es},
-                     {f.log_gate, f.var == LA_VECTOR_DECAY ? g_b * f.d_k : g_b}, {f.beta, g_b},
+                     {f.log_gate, (f.var == LA_VECTOR_DECAY || f.var == LA_KDA) ? g_b * f.d_k : g_b}, {f.beta, g_b},
                      {f.o, (size_t)BH * f.L * f.d_v * elem_size(f.o_dt)}, {f.state_in, s_b},
                      {f.state_out, s_b}, {f.z_in, z_b}, {f.z_out, z_b}}};
 }
@@ -431,10 +444,12 @@ la_status validate_fwd(const FwdCall &f) {
     // required / forbidden pointers
     if (has_tokens && (!f.q || !f.k || !f.o)) return LA_ERR_INVALID_ARG;
     if (has_tokens && !f.v) return LA_ERR_INVALID_ARG;
-    if ((var == LA_DECAY || var == LA_VECTOR_DECAY) && has_tokens && !f.log_gate) return LA_ERR_INVALID_ARG;
+    if ((var == LA_DECAY || var == LA_VECTOR_DECAY || var == LA_KDA) && has_tokens && !f.log_gate)
+        return LA_ERR_INVALID_ARG;
     if ((var == LA_PLAIN || var == LA_NORMALIZED) && f.log_gate) return LA_ERR_INVALID_ARG;
-    if (var == LA_GATED_DELTA && has_tokens && !f.beta) return LA_ERR_INVALID_ARG;
-    if (var != LA_GATED_DELTA && f.beta) return LA_ERR_INVALID_ARG;
+    const bool delta = var == LA_GATED_DELTA || var == LA_KDA;
+    if (delta && has_tokens && !f.beta) return LA_ERR_INVALID_ARG;
+    if (!delta && f.beta) return LA_ERR_INVALID_ARG;
     if (var != LA_NORMALIZED && (f.z_in || f.z_out)) return LA_ERR_INVALID_ARG;
     // alignment
     const void *ptrs[] = {f.q, f.k, f.v, f.o, f.log_gate, f.beta, f.state_in, f.z_in, f.state_out, f.z_out};
@@ -444,7 +459,7 @@ la_status validate_fwd(const FwdCall &f) {
     const int L = f.L, d_k = f.d_k, d_v = f.d_v;
     const size_t qk_b = (size_t)BH * L * d_k * es, v_b = (size_t)BH * L * d_v * es;
     const size_t g_b = (size_t)BH * L * 4, s_b = (size_t)BH * d_k * d_v * 4, z_b = (size_t)BH * d_k * 4;
-    const size_t lg_b = var == LA_VECTOR_DECAY ? g_b * d_k : g_b;
+    const size_t lg_b = (var == LA_VECTOR_DECAY || var == LA_KDA) ? g_b * d_k : g_b;
     const Span o_sp{f.o, (size_t)BH * L * d_v * oes}, so_sp{f.state_out, s_b}, zo_sp{f.z_out, z_b};
     const Span ins[] = {{f.q, qk_b}, {f.k, qk_b}, {f.v, v_b}, {f.log_gate, lg_b}, {f.beta, g_b}, {f.z_in, z_b}};
     for (const Span &in : ins) {
@@ -480,7 +495,7 @@ la_status run_fwd(const FwdCall &f, int p0, int n, const float *s_in, float *s_o
     const int C = kernel_chunk(var, dt, f.d_k, f.C), d_k = f.d_k, d_v = f.d_v;
     const int nchunks = (n + C - 1) / C;
     const int Lp = nchunks * C;
-    const int gw = var == LA_VECTOR_DECAY ? d_k : 1;  // gates per token
+    const int gw = (var == LA_VECTOR_DECAY || var == LA_KDA) ? d_k : 1;  // gates per token
     auto adv = [&](const void *p, size_t per_row) -> const void * {
         return p ? static_cast<const char *>(p) + (size_t)p0 * per_row : nullptr;
     };
@@ -494,6 +509,28 @@ la_status run_fwd(const FwdCall &f, int p0, int n, const float *s_in, float *s_o
     const Geometry geo = choose_geometry(var, dt, BH, d_v, C);
     a.BH = (int)BH; a.L = n; a.Lp = Lp; a.dv = d_v; a.nsplit = d_v / geo.dvt; a.ld = f.L;
 
+    if (var == LA_KDA && n > 0) {
+        // the preparation folds the per-channel gates into W, the scores, q and k
+        // and the per-chunk state decay; the serial pass runs without a scalar gate
+        char *w = static_cast<char *>(ws);
+        const size_t wb = gdn_w_bytes(dt, BH, Lp, d_k), ub = gdn_ut_bytes(dt, BH, Lp, d_v);
+        const size_t mb = gdn_mf_bytes(dt, BH, Lp), qkb = kda_qk_bytes(BH, Lp, d_k);
+        PrepArgs p{};
+        p.q = a.q; p.k = a.k; p.v = a.v; p.lg = a.lg; p.beta = static_cast<const float *>(adv(f.beta, 4));
+        p.w = w; p.ut = w + wb; p.mf = w + wb + ub;
+        p.qc = w + wb + ub + mb; p.kc = w + wb + ub + mb + qkb;
+        p.cdec = reinterpret_cast<float *>(w + wb + ub + mb + 2 * qkb);
+        p.BH = (int)BH; p.L = n; p.Lp = Lp; p.dv = d_v; p.nchunks = nchunks; p.ld = f.L;
+        hipError_t e = hipErrorInvalidValue;
+        switch (d_k) {
+            case 32: e = launch_kda_prep<32>(p, st); break;
+            case 64: e = launch_kda_prep<64>(p, st); break;
+            case 128: e = launch_kda_prep<128>(p, st); break;
+        }
+        if (e != hipSuccess) return LA_ERR_HIP;
+        a.w = p.w; a.ut = p.ut; a.mf = p.mf; a.qc = p.qc; a.kc = p.kc; a.cdec = p.cdec;
+        a.lg = nullptr;
+    }
     if (var == LA_GATED_DELTA && n > 0) {
         char *w = static_cast<char *>(ws);
         a.w = w;
@@ -795,20 +832,21 @@ la_status la_chunk_fwd_conv(la_variant var, la_dtype dt, la_dtype o_dt, const vo
 la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void *q, const void *k,
                          const void *v, const float *log_gate, const float *beta, float *state,
                          void *o, int N, int H, int d_k, int d_v, void *stream) {
-    if (var < LA_PLAIN || var > LA_VECTOR_DECAY) return LA_ERR_INVALID_ARG;
+    if (var < LA_PLAIN || var > LA_KDA) return LA_ERR_INVALID_ARG;
     if (dt != LA_F32 && dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (o_dt != LA_F32 && o_dt != LA_BF16) return LA_ERR_INVALID_ARG;
     if (!dtype_pair_ok(dt, o_dt)) return LA_ERR_UNSUPPORTED;
     if (var == LA_NORMALIZED) return LA_ERR_UNSUPPORTED;
     if (N < 1 || H < 1) return LA_ERR_INVALID_ARG;
-    // (the delta rule launches two workgroups per sequence-head)
-    if ((int64_t)N * H > (var == LA_GATED_DELTA ? INT32_MAX / 2 : INT32_MAX)) return LA_ERR_UNSUPPORTED;
+    // (the delta rules launch two workgroups per sequence-head)
+    const bool delta = var == LA_GATED_DELTA || var == LA_KDA;
+    if ((int64_t)N * H > (delta ? INT32_MAX / 2 : INT32_MAX)) return LA_ERR_UNSUPPORTED;
     if ((d_k != 32 && d_k != 64 && d_k != 128) || (d_v != 32 && d_v != 64 && d_v != 128))
         return LA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !state || !o) return LA_ERR_INVALID_ARG;
-    if ((var == LA_DECAY || var == LA_VECTOR_DECAY) && !log_gate) return LA_ERR_INVALID_ARG;
+    if ((var == LA_DECAY || var == LA_VECTOR_DECAY || var == LA_KDA) && !log_gate) return LA_ERR_INVALID_ARG;
     if (var == LA_PLAIN && log_gate) return LA_ERR_INVALID_ARG;
-    if ((var == LA_GATED_DELTA) != (beta != nullptr)) return LA_ERR_INVALID_ARG;
+    if (delta != (beta != nullptr)) return LA_ERR_INVALID_ARG;
     const void *ptrs[] = {q, k, v, o, log_gate, beta, state};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return LA_ERR_INVALID_ARG;
@@ -817,7 +855,7 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
     const Span o_sp{o, (size_t)NH * d_v * elem_size(o_dt)}, s_sp{state, (size_t)NH * d_k * d_v * 4};
     const Span ins[] = {{q, (size_t)NH * d_k * es}, {k, (size_t)NH * d_k * es},
                         {v, (size_t)NH * d_v * es},
-                        {log_gate, (size_t)NH * 4 * (var == LA_VECTOR_DECAY ? d_k : 1)},
+                        {log_gate, (size_t)NH * 4 * ((var == LA_VECTOR_DECAY || var == LA_KDA) ? d_k : 1)},
                         {beta, (size_t)NH * 4}};
     for (const Span &in : ins)
         if (overlap(o_sp, in) || overlap(s_sp, in)) return LA_ERR_INVALID_ARG;
@@ -832,6 +870,10 @@ la_status la_decode_step(la_variant var, la_dtype dt, la_dtype o_dt, const void 
         if (dt == LA_F32) e = dispatch_decode<V_VDECAY, float, float>(d_k, d_v, a, st);
         else if (o_dt == LA_F32) e = dispatch_decode<V_VDECAY, bf16, float>(d_k, d_v, a, st);
         else e = dispatch_decode<V_VDECAY, bf16, bf16>(d_k, d_v, a, st);
+    } else if (var == LA_KDA) {
+        if (dt == LA_F32) e = dispatch_decode<V_KDA, float, float>(d_k, d_v, a, st);
+        else if (o_dt == LA_F32) e = dispatch_decode<V_KDA, bf16, float>(d_k, d_v, a, st);
+        else e = dispatch_decode<V_KDA, bf16, bf16>(d_k, d_v, a, st);
     } else if (var == LA_GATED_DELTA) {
         if (dt == LA_F32) e = dispatch_decode<V_GDN, float, float>(d_k, d_v, a, st);
         else if (o_dt == LA_F32) e = dispatch_decode<V_GDN, bf16, float>(d_k, d_v, a, st);

@@ -10,6 +10,9 @@
 //   gated delta rule          r = S^T k;  S <- alpha S + k (beta (v - alpha r))^T
 //                             (wln20, Gated DeltaNet section, d_k x d_v orientation:
 //                             alpha (S - beta k r^T) + beta k v^T regrouped)
+//   KDA                       r = (Diag(alpha) S)^T k;  S <- Diag(alpha) S + k (beta (v - r))^T
+//                             (wln20, Kimi Delta Attention section: the delta rule
+//                             with one gate per key channel)
 // The delta rule needs the retrieval r over all rows before any row is updated:
 // the state stays in registers between the two reductions. The fp32 state dominates the
 // traffic (2 x d_k x d_v x 4 bytes per head and step), so the kernel is a
@@ -18,7 +21,7 @@
 // owning d_k / RG consecutive rows of one 16-byte column group, all of its state
 // loads issued before any arithmetic, non-temporal loads and stores for the state
 // (it is touched once per step), and a shuffle + LDS reduction of o over rows.
-// The delta rule runs two workgroups per head, each on half of the value columns.
+// The delta rules run two workgroups per head, each on half of the value columns.
 #pragma once
 
 #include "la_common.hpp"
@@ -33,7 +36,7 @@ namespace la {
 // 16 bytes per thread instead of 16).
 template <int VAR, int DV>
 constexpr int decode_cols() {
-    return (VAR == V_GDN && DV > 32) ? DV / 2 : DV;
+    return ((VAR == V_GDN || VAR == V_KDA) && DV > 32) ? DV / 2 : DV;
 }
 
 // Occupancy: the state in flight is what keeps HBM busy. Without the retrieval
@@ -96,8 +99,8 @@ decode_kernel(DecodeArgs a) {
     // new state column group: ns = al * s + kr * u (u per column group)
     float al = 1.f;
     f32x4 u = vv;
-    float alr[VAR == V_VDECAY ? RPT : 1];  // per-row (key channel) gates
-    if constexpr (VAR == V_VDECAY) {
+    float alr[(VAR == V_VDECAY || VAR == V_KDA) ? RPT : 1];  // per-row (key channel) gates
+    if constexpr (VAR == V_VDECAY || VAR == V_KDA) {
         const float *lp = a.lg + h * DK + rg * RPT;
 #pragma unroll
         for (int m = 0; m < RPT; ++m) alr[m] = __expf(lp[m]);
@@ -113,11 +116,21 @@ decode_kernel(DecodeArgs a) {
         const f32x4 r = rows_total(racc, rred);  // r = S^T k for this column group
         u = be * (vv - al * r);
     }
+    if constexpr (VAR == V_KDA) {
+        // r = (Diag(alpha) S)^T k: the retrieval reads the decayed state
+        __shared__ f32x4 rred[4][CG];
+        const float be = a.beta[h];
+        f32x4 racc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) racc += (kr[m] * alr[m]) * s[m];
+        const f32x4 r = rows_total(racc, rred);
+        u = be * (vv - r);
+    }
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
-        const f32x4 ns = (VAR == V_VDECAY ? alr[m] : al) * s[m] + kr[m] * u;
+        const f32x4 ns = ((VAR == V_VDECAY || VAR == V_KDA) ? alr[m] : al) * s[m] + kr[m] * u;
         __builtin_nontemporal_store(ns, reinterpret_cast<f32x4 *>(S + (size_t)m * DV));
         acc += qr[m] * ns;
     }

@@ -84,7 +84,10 @@ __device__ inline f16x8 chan_frag(const f16 *X, int row, int p, int g) {
 // QK16: q and k come as fp16 rows of the workspace (a.qc, a.kc, [BH, Lp, DK];
 // the short convolution fused into the preparation writes them) instead of bf16
 // inputs.
-template <typename TO, int DK, bool QK16>
+// VEC: Kimi Delta Attention (kda_prep_impl.hpp). The preparation folds the
+// per-channel gates into q, k, W and the scores, and the state's rows decay by
+// the chunk's Gam_C (a.cdec) instead of a scalar exp(g_C); there is no scalar gate.
+template <typename TO, int DK, bool QK16, bool VEC = false>
 __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
     using Cfg = GdnCfg<DK>;
     using MF = Mfma<f16>;
@@ -96,6 +99,8 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
     // gate tables per buffer: [0] exp(G_s), [1] exp(g_C - G_s); Tsc: exp(g_C)
     __shared__ __attribute__((aligned(16))) float Tg[2 * 2 * C];
     __shared__ float Tsc[2];
+    // VEC: the state's per-channel decay of chunk c (buffer c & 1)
+    __shared__ __attribute__((aligned(16))) float Cd[2][VEC ? DK : 4];
     // chain -> output waves: S^T fragments of the state before chunk c (buffer
     // c & 1) with their shift, and U fragments of chunk c (buffer c & 1)
     __shared__ __attribute__((aligned(16))) f16x8 Sf[2][NKS][64];
@@ -252,6 +257,10 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
             for (int q = 0; q < 2; ++q) ub[q] = pack_tiles(U[2 * q] * wlo[q], U[2 * q + 1] * whi[q], 1.f);
 #pragma unroll
             for (int ti = 0; ti < NTI; ++ti) St[ti] *= eg;
+            if constexpr (VEC) {
+#pragma unroll
+                for (int ti = 0; ti < NTI; ++ti) St[ti] *= *reinterpret_cast<const f32x4 *>(&Cd[P][ti * 16 + 4 * g]);
+            }
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -284,6 +293,8 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
         constexpr int sw = decltype(sw_tag)::value;
         uint4 pre[2][NSL];
         float gpre[2];
+        constexpr int NCD = (DK + 63) / 64;
+        float cpre[2][NCD];
         const float *gsrc = lgg ? lgg : reinterpret_cast<const float *>(kg);  // kg: at least L floats
         constexpr bool gate_wave = sw == 0;
         // slot m of this wave: wave load i = sw + 3 m (the last wave load again past
@@ -304,6 +315,13 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
             // unconditional as well, from a valid address when there is no gate; the
             // value is masked where it is used (masking it here would wait for it here)
             if (gate_wave) gpre[set] = gsrc[min(c * C + lane, L - 1)];
+            if constexpr (VEC) {
+                if (gate_wave) {
+#pragma unroll
+                    for (int i = 0; i < NCD; ++i)
+                        cpre[set][i] = a.cdec[((size_t)bh * nchunks + c) * DK + min(lane + 64 * i, DK - 1)];
+                }
+            }
         };
         auto stage_chunk = [&](int c, int set, int buf) __attribute__((always_inline)) {
             f16 *X = Tiles + buf * SET;
@@ -335,6 +353,11 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
                 T[lane] = __expf(G);
                 T[C + lane] = __expf(gC - G);
                 if (lane == 0) Tsc[buf] = __expf(gC);
+                if constexpr (VEC) {
+#pragma unroll
+                    for (int i = 0; i < NCD; ++i)
+                        if (lane + 64 * i < DK) Cd[buf][lane + 64 * i] = cpre[set][i];
+                }
             }
         };
         // Loads are issued unconditionally (chunk indices past the end repeat the
@@ -487,7 +510,9 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
 template <typename TO, int DK>
 hipError_t launch_gdn_fwd(const ChunkArgs &a, hipStream_t st) {
     const int blocks = a.BH * a.nsplit;
-    if (a.qc)
+    if (a.cdec)
+        hipLaunchKernelGGL((gdn_fwd_kernel<TO, DK, true, true>), dim3(blocks), dim3(512), 0, st, a);
+    else if (a.qc)
         hipLaunchKernelGGL((gdn_fwd_kernel<TO, DK, true>), dim3(blocks), dim3(512), 0, st, a);
     else
         hipLaunchKernelGGL((gdn_fwd_kernel<TO, DK, false>), dim3(blocks), dim3(512), 0, st, a);

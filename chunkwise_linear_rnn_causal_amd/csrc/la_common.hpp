@@ -22,7 +22,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-enum Variant { V_PLAIN = 0, V_NORM = 1, V_DECAY = 2, V_GDN = 3, V_VDECAY = 4 };
+enum Variant { V_PLAIN = 0, V_NORM = 1, V_DECAY = 2, V_GDN = 3, V_VDECAY = 4, V_KDA = 5 };
 
 // MFMA traits per storage/operand type.
 template <typename T> struct Mfma;

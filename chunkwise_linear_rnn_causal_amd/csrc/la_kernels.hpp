@@ -24,7 +24,10 @@ struct ChunkArgs {
     float *den_out;             // normalized: the per-token denominators [BH, L] (for the
                                 // backward pass) or nullptr
     const void *qc, *kc;        // gated delta, bf16, short convolution fused into the
-                                // preparation: convolved q, k [BH, Lp, DK] fp16, or nullptr
+                                // preparation: convolved q, k [BH, Lp, DK] fp16, or nullptr;
+                                // KDA: q (.) Gam and k (.) Gam_C / Gam (kda_prep_impl.hpp)
+    const float *cdec;          // KDA: the state's per-channel decay per chunk, Gam_C
+                                // [BH, Lp / 64, DK], or nullptr
     int BH, L, Lp, dv, nsplit;  // Lp = ceil(L / C) * C; nsplit = dv / DVT (workgroups per head)
     int ld;                     // rows between consecutive heads of q, k, v, o and the gates
                                 // (>= L; L unless a piece of a longer sequence is run)
@@ -44,6 +47,7 @@ struct PrepArgs {
     const void *cwin[3];
     void *qc, *kc;
     int H, K;
+    float *cdec;                // KDA preparation: Gam_C per chunk [BH, nchunks, DK]
     int BH, L, Lp, dv, nchunks;
     int ld;                     // rows between consecutive heads of k, v and the gates (>= L)
 };
@@ -134,6 +138,12 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t st);
 // log-gate gradient (gdn_bwd_impl.hpp).
 template <int DK, int DV>
 hipError_t launch_gdn_bwd(const BwdArgs &a, hipStream_t st);
+
+// Chunk-parallel preparation of Kimi Delta Attention, bf16 inputs (C = 64): W, U~,
+// the score fragments, the pre-scaled q and k and the per-chunk state decay, for
+// the delta rule's serial pass (kda_prep_impl.hpp). PrepArgs::lg is [BH, L, DK].
+template <int DK>
+hipError_t launch_kda_prep(const PrepArgs &a, hipStream_t st);
 
 // Backward pass of the per-key-channel decay, bf16 inputs (C = 64): the forward
 // and reverse state scans, then the per-chunk gradients with the gate gradient

@@ -28,6 +28,12 @@
  *                   pages' S'_t = S'_{t-1} alpha_t (I - beta_t k_t k_t^T) +
  *                   beta_t v_t k_t^T (wln20, Gated DeltaNet section; tensorplay
  *                   section 6.2); outputs are identical.
+ *   LA_KDA          Kimi Delta Attention: the gated delta rule with one gate per
+ *                   key channel, S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1}
+ *                   + beta_t k_t v_t^T, alpha_t = exp(l_t), l_t in R^{d_k},
+ *                   o_t = S_t^T q_t (wln20, Kimi Delta Attention section, read in
+ *                   the d_k x d_v orientation: the diagonal gate acts on the key
+ *                   channels and the delta-rule factor multiplies from the left).
  *
  * la_chunk_fwd evaluates these in the chunkwise-parallel form (tensorplay
  * section 3.2): per chunk of C tokens an intra-chunk masked product, an
@@ -76,7 +82,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 2
+#define LA_ABI_VERSION 3
 
 typedef enum la_status {
     LA_OK = 0,
@@ -92,7 +98,8 @@ typedef enum la_variant {
     LA_NORMALIZED = 1,
     LA_DECAY = 2,
     LA_GATED_DELTA = 3,
-    LA_VECTOR_DECAY = 4
+    LA_VECTOR_DECAY = 4,
+    LA_KDA = 5
 } la_variant;
 
 typedef enum la_dtype {
@@ -109,6 +116,10 @@ typedef enum la_dtype {
  * B*H*Lp*d_k and B*H*Lp*d_v elements (2 bytes each for bf16 inputs, 4 for
  * fp32), each rounded up to 256 bytes, with Lp = ceil(L/64)*64; for bf16 inputs
  * also the chunk's masked decayed scores, 96 bytes per token (B*H*Lp*96).
+ * LA_KDA (bf16 inputs) stores the same three arrays, then q and k with the
+ * per-channel gates folded in (2 * B*H*Lp*d_k fp16, each rounded up to 256
+ * bytes) and the state's per-channel decay of every chunk (B*H*(Lp/64)*d_k
+ * float32, rounded up to 256 bytes).
  * Returns LA_ERR_INVALID_ARG / LA_ERR_UNSUPPORTED like la_chunk_fwd.
  */
 la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H, int L,
@@ -126,8 +137,12 @@ la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
  *               so that every rebased factor stays below e^80 (a gate of e^-10
  *               already damps the channel's history to 4.5e-5 per token, so
  *               the result moves by at most that fraction of the damped history).
- *   beta        [B,H,L] float32 in [0,1]: required for LA_GATED_DELTA, NULL
- *               otherwise.
+ *               LA_KDA takes [B,H,L,d_k] too, required, with the same -10
+ *               floor: its chunk form factors the decay between 16-token blocks
+ *               at the block edges (every factor <= 1, fp16 operands) and takes
+ *               the 16-token diagonal blocks in fp32 around their middle token.
+ *   beta        [B,H,L] float32 in [0,1]: required for LA_GATED_DELTA and LA_KDA,
+ *               NULL otherwise.
  *   state_in    [B,H,d_k,d_v] float32 initial state, NULL = zero.
  *   z_in        [B,H,d_k] float32 initial normalizer (LA_NORMALIZED only),
  *               NULL = zero. Must be NULL for the other variants.
@@ -141,12 +156,15 @@ la_status la_chunk_fwd_workspace_size(la_variant var, la_dtype dt, int B, int H,
  *   B, H, L     batch, heads, tokens: B, H >= 1; L >= 0 (L = 0 only copies
  *               state_in/z_in, or zeros, to state_out/z_out).
  *   d_k         32, 64 or 128.   d_v  32, 64, 96 or 128 (a multiple of 32).
- *   C           chunk length: 64 or 128 (LA_GATED_DELTA, LA_VECTOR_DECAY: 64).
+ *   C           chunk length: 64 or 128 (LA_GATED_DELTA, LA_KDA and
+ *               LA_VECTOR_DECAY run 128 as two 64-token chunks, which gives the
+ *               same result).
  *               L need not be a multiple of C; a ragged last chunk is handled.
  *               Rows of one head are addressed with 32-bit offsets:
  *               ceil(L / C) * C * max(d_k, d_v) >= 2^31 returns
  *               LA_ERR_UNSUPPORTED.
  *               LA_VECTOR_DECAY with LA_F32 inputs supports d_k 32 and 64.
+ *               LA_KDA takes LA_BF16 inputs only (LA_F32: LA_ERR_UNSUPPORTED).
  *   workspace   device buffer of at least la_chunk_fwd_workspace_size() bytes
  *               (may be NULL when that size is 0), 256-byte aligned.
  */
@@ -167,11 +185,13 @@ la_status la_chunk_fwd(la_variant var, la_dtype dt, la_dtype o_dt, const void *q
  *                   (wln20 Gated DeltaNet section, d_k x d_v orientation)
  *   LA_VECTOR_DECAY S <- Diag(exp(l)) S + k v^T, l [N,H,d_k] (tensorplay
  *                   section 5.1)
+ *   LA_KDA          r = (Diag(exp(l)) S)^T k;  S <- Diag(exp(l)) S + beta k (v - r)^T,
+ *                   l [N,H,d_k] (wln20 Kimi Delta Attention section)
  *   q, k [N,H,d_k], v [N,H,d_v] in dtype dt; o [N,H,d_v] in dtype o_dt (the
  *   step itself is computed in fp32); log_gate [N,H] float32 (required for
  *   LA_DECAY, optional for LA_GATED_DELTA, NULL for LA_PLAIN; [N,H,d_k] and
- *   required for LA_VECTOR_DECAY); beta [N,H] float32,
- *   required for LA_GATED_DELTA and NULL otherwise; state [N,H,d_k,d_v] float32,
+ *   required for LA_VECTOR_DECAY and LA_KDA); beta [N,H] float32,
+ *   required for LA_GATED_DELTA and LA_KDA and NULL otherwise; state [N,H,d_k,d_v] float32,
  *   read and written in place. o must not overlap the state or inputs.
  *   N, H >= 1; d_k, d_v in {32, 64, 128}. LA_NORMALIZED is not supported.
  */
@@ -274,6 +294,7 @@ la_status la_chunk_fwd_conv(la_variant var, la_dtype dt, la_dtype o_dt, const vo
  * (LA_GATED_DELTA: q_u . dq_u - v_u . dv_u).
  *   var          LA_PLAIN, LA_NORMALIZED, LA_DECAY, or LA_GATED_DELTA and
  *                LA_VECTOR_DECAY with dt = LA_BF16 (LA_F32: LA_ERR_UNSUPPORTED).
+ *                LA_KDA has no backward (LA_ERR_UNSUPPORTED).
  *                LA_VECTOR_DECAY: the gate-difference identity holds per key
  *                channel, restarted at every chunk end c:
  *                d_log_gate_t[i] = sum_{u>=t in the chunk} (q_u[i] dq_u[i] -
@@ -334,7 +355,7 @@ la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k
  * la_chunk_fwd without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation). The same arguments as la_chunk_fwd and the same
- * results. The delta rule's per-chunk products go to a static device array of
+ * results. The delta rules' per-chunk products (LA_GATED_DELTA, LA_KDA) go to a static device array of
  * LA_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
  * until the process ends; the call itself allocates nothing. When the whole
  * sequence's products do not fit, the sequence is run in pieces of whole

@@ -7,7 +7,7 @@ import pytest
 
 import chunkwise_linear_rnn_causal_amd as la
 
-PLAIN, NORM, DECAY, GDN, VDECAY = 0, 1, 2, 3, 4
+PLAIN, NORM, DECAY, GDN, VDECAY, KDA = 0, 1, 2, 3, 4, 5
 F32, BF16 = 0, 1
 INVALID, UNSUPPORTED = la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED
 FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert la.la_abi_version() == 2
+    assert la.la_abi_version() == 3
     assert la.la_status_str(0) == "LA_OK"
     assert la.la_status_str(1) == "LA_ERR_INVALID_ARG"
     assert la.la_status_str(2) == "LA_ERR_UNSUPPORTED"
@@ -68,10 +68,22 @@ def test_workspace_sizes():
     # the largest head the 32-bit row offsets address, and one chunk more
     assert wsize(B=1, H=1, L=2 ** 24 - 64, dk=128, dv=128)[0] == 0
     assert wsize(B=1, H=1, L=2 ** 24 - 63, dk=128, dv=128)[0] == UNSUPPORTED
+    # KDA (bf16 only): the delta rule's arrays, then q and k with the gates folded in
+    # (fp16 [BH, Lp, dk] each) and the per-chunk state decay (fp32 [BH, Lp / 64, dk])
+    st, n = wsize(var=KDA)
+    assert st == 0 and n == (up(2 * 3 * 128 * 64 * 2) + up(2 * 3 * 128 * 32 * 2) + 2 * 3 * 128 * 96
+                             + 2 * up(2 * 3 * 128 * 64 * 2) + up(2 * 3 * 2 * 64 * 4))
+    assert wsize(var=KDA, dt=F32)[0] == UNSUPPORTED
+    assert wsize(var=KDA, C=128) == wsize(var=KDA, C=64)
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(var=7), INVALID), (dict(dt=5), INVALID), (dict(odt=5), INVALID),
+    (dict(var=7), INVALID),
+    (dict(var=KDA, beta=FAKE + 0x200000), INVALID),   # KDA needs its gates
+    (dict(var=KDA, lg=FAKE + 0x100000), INVALID),     # and beta
+    (dict(var=KDA, lg=FAKE + 0x100000, beta=FAKE + 0x200000, dt=F32), UNSUPPORTED),
+    (dict(var=KDA, lg=FAKE + 0x100000, beta=FAKE + 0x200000, o=FAKE + 0x100000 + 0x7000), INVALID),  # o in the gates
+    (dict(var=KDA, lg=FAKE + 0x100000, beta=FAKE + 0x200000), INVALID),  # workspace missing (dict(dt=5), INVALID), (dict(odt=5), INVALID),
     (dict(var=VDECAY), INVALID),                      # per-channel decay needs its gates
     (dict(var=VDECAY, lg=FAKE + 0x100000, dt=F32, dk=128), UNSUPPORTED),
     (dict(var=VDECAY, lg=FAKE + 0x100000, o=FAKE + 0x100000 + 0x7000), INVALID),  # o inside the gates
@@ -99,6 +111,12 @@ def test_chunk_fwd_rejects(kw, expect):
     assert chunk(**kw) == expect
 
 
+def test_kda_valid_arguments_reach_the_device_check():
+    assert chunk(var=KDA, lg=FAKE + 0x100000, beta=FAKE + 0x200000, ws=0x700000000,
+                 ws_bytes=1 << 30) not in (INVALID, UNSUPPORTED)
+    assert dec(var=KDA, beta=FAKE + 0x5000) not in (INVALID, UNSUPPORTED)
+
+
 def test_noalloc_refuses_problems_whose_chunk_exceeds_the_scratch():
     lib = la.load_library()
     G = 1 << 32  # fake, 16-byte aligned, far apart: validation fails first
@@ -124,6 +142,9 @@ def dec(var=DECAY, dt=BF16, odt=F32, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, l
     (dict(var=VDECAY, o=FAKE + 0x3800), INVALID),     # o inside the [N,H,d_k] gates
     (dict(var=GDN), INVALID),                         # delta rule needs beta
     (dict(var=GDN, beta=FAKE + 0x5000, o=FAKE + 0x5000), INVALID),  # o overlaps beta
+    (dict(var=KDA), INVALID),                         # KDA needs beta
+    (dict(var=KDA, beta=FAKE + 0x5000, lg=None), INVALID),  # and its gates
+    (dict(var=KDA, beta=FAKE + 0x5000, o=FAKE + 0x3800), INVALID),  # o inside the [N,H,d_k] gates
     (dict(odt=7), INVALID), (dict(dt=F32, odt=BF16), UNSUPPORTED),
     (dict(N=0), INVALID), (dict(dk=96), UNSUPPORTED), (dict(dv=16), UNSUPPORTED),
     (dict(q=None), INVALID), (dict(S=None), INVALID), (dict(lg=None), INVALID),
@@ -254,6 +275,7 @@ def test_chunk_bwd_valid_arguments_reach_the_device_check():
     assert bwd(var=GDN, beta=FAKE + 0x500000, dbeta=0x830000000, dlg=0x840000000) not in (INVALID, UNSUPPORTED)
     assert bwd(var=GDN, lg=None, beta=FAKE + 0x500000) not in (INVALID, UNSUPPORTED)
     assert bwd(var=VDECAY, dlg=0x830000000) not in (INVALID, UNSUPPORTED)
+    assert bwd(var=KDA, beta=FAKE + 0x500000) == UNSUPPORTED  # no KDA backward
     assert bwd(var=NORM, lg=None, z_in=FAKE + 0x600000, dzo=FAKE + 0x610000,
                dzi=0x830000000) not in (INVALID, UNSUPPORTED)
 

@@ -52,7 +52,8 @@ def test_noalloc_matches_the_workspace_entry_point():
     assert torch.equal(o, o_ref) and torch.equal(s, s_ref)
 
 
-@pytest.mark.parametrize("var,dt", [("gated_delta", "f32"), ("decay", "bf16"), ("normalized", "bf16")])
+@pytest.mark.parametrize("var,dt", [("gated_delta", "f32"), ("decay", "bf16"), ("normalized", "bf16"),
+                                    ("kda", "bf16")])
 def test_noalloc_one_piece_is_bit_exact(var, dt):
     print(f"[noalloc] {var} {dt} one piece", flush=True)
     inp = W.make_chunk_inputs(var, dt, 2, 3, 201, 64, 64, seed=34, with_state=True)

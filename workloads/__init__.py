@@ -36,7 +36,7 @@ TAG_Q, TAG_K, TAG_V, TAG_GATE, TAG_BETA, TAG_STATE = 1, 2, 3, 4, 5, 6
 TAG_CONV_W, TAG_CONV_WINDOW = 7, 8
 TAG_DOUT = 9
 
-VARIANTS = ("plain", "normalized", "decay", "gated_delta", "vector_decay")
+VARIANTS = ("plain", "normalized", "decay", "gated_delta", "vector_decay", "kda")
 
 # The five workloads, each named by what it is. "recipe" selects the input
 # distribution (see _draw_slice); sizes are the ones the workloads are quoted at.
@@ -60,6 +60,11 @@ CONFIGS: Dict[str, dict] = {
     "vector_decay_bf16_b4h32_l8192_d128": dict(
         kind="chunk", variant="vector_decay", dtype="bf16", B=4, H=32, L=8192, dk=128, dv=128, C=64,
         recipe="gla"),
+    # Kimi Delta Attention at the delta-rule workload's shapes: its inputs, with the
+    # gate drawn independently for every key channel
+    "kda_bf16_b2h16_l8192_d128": dict(
+        kind="chunk", variant="kda", dtype="bf16", B=2, H=16, L=8192, dk=128, dv=128, C=64,
+        recipe="kda"),
     # the backward pass of the decay workload (output gradient dO ~ N(0, 1))
     "decay_bwd_bf16_b4h32_l8192_d128": dict(
         kind="bwd", variant="decay", dtype="bf16", B=4, H=32, L=8192, dk=128, dv=128, C=64,
@@ -92,6 +97,7 @@ DEFAULT_RECIPE = {
     "decay": "gauss_scaled_gate",
     "gated_delta": "gdn",
     "vector_decay": "gla",
+    "kda": "kda",
 }
 
 
@@ -147,7 +153,7 @@ def _draw_slice(recipe: str, tag: int, seed: int, b: int, h: int, L: int, d: int
             return (x / np.float32(math.sqrt(d))).astype(np.float32)
         if recipe == "elu1":
             return _elu1(x) if tag in (TAG_Q, TAG_K) else x
-        if recipe == "gdn":
+        if recipe in ("gdn", "kda", "kda_gla", "kda_strong"):
             return _l2_rows(x) if tag in (TAG_Q, TAG_K) else x
         raise ValueError(recipe)
     if tag == TAG_GATE:
@@ -156,26 +162,34 @@ def _draw_slice(recipe: str, tag: int, seed: int, b: int, h: int, L: int, d: int
         if recipe == "gla":
             # alpha = sigmoid(x)^(1/tau) per key channel, tau = 16: l = log sigmoid(x) / 16
             return (_sigmoid_log(rng.normal(0.0, 1.0, size=(L, d))).astype(np.float64) / 16.0).astype(np.float32)
-        if recipe == "gla_strong":
+        if recipe == "gla_strong" or recipe == "kda_strong":
             # per-channel gates spread over the whole supported range [-10, 0]
             return (-10.0 * rng.random((L, d)) ** 3).astype(np.float32)
+        if recipe == "kda":
+            # the delta rule's gate alpha = sigmoid(N(4, 1)), one per key channel
+            return _sigmoid_log(rng.normal(4.0, 1.0, size=(L, d)))
+        if recipe == "kda_gla":
+            return (_sigmoid_log(rng.normal(0.0, 1.0, size=(L, d))).astype(np.float64) / 16.0).astype(np.float32)
         raise ValueError(recipe)
     if tag == TAG_BETA:
         return _sigmoid(rng.normal(0.0, 1.0, size=L))
     raise ValueError(tag)
 
 
+KDA_RECIPES = ("kda", "kda_gla", "kda_strong")
+
+
 def recipe_has_gate(recipe: str) -> bool:
-    return recipe in ("gauss_scaled_gate", "gdn", "gla", "gla_strong")
+    return recipe in ("gauss_scaled_gate", "gdn", "gla", "gla_strong") + KDA_RECIPES
 
 
 def recipe_gate_width(recipe: str, dk: int) -> int:
     """Gates per token: one (scalar decay) or one per key channel."""
-    return dk if recipe in ("gla", "gla_strong") else 1
+    return dk if recipe in ("gla", "gla_strong") + KDA_RECIPES else 1
 
 
 def recipe_has_beta(recipe: str) -> bool:
-    return recipe == "gdn"
+    return recipe in ("gdn",) + KDA_RECIPES
 
 
 @dataclass
