@@ -46,7 +46,7 @@ namespace la {
 // are loaded into registers while the current chunk is folded in; every wave
 // scans the chunk's gates itself (rows in lanes), so no barrier guards them.
 template <typename TI, int DK, int DVT, bool FWD, bool DECAY>
-__device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &a, int blk) {
+__device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &a, int blk, void *lds) {
     using TM = typename OpOf<TI>::type;
     using MF = Mfma<TM>;
     using frag = typename MF::frag;
@@ -57,8 +57,10 @@ __device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &
     constexpr int NTK = C / (4 * E);
     constexpr int SEGX = DK / 8, SEGY = DVT / 8;
     constexpr int NXS = (C * SEGX + 255) / 256, NYS = (C * SEGY + 255) / 256;
-    __shared__ __align__(16) TM Xs[C * PX];
-    __shared__ __align__(16) TM Ys[C * PY];
+    // double-buffered operand tiles: chunk it is staged into buffer it & 1, whose
+    // last reader (chunk it - 2) is behind the barrier of chunk it - 1
+    TM(*Xs)[C * PX] = reinterpret_cast<TM(*)[C * PX]>(lds);
+    TM(*Ys)[C * PY] = reinterpret_cast<TM(*)[C * PY]>(static_cast<TM *>(lds) + 2 * C * PX);
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
     const int bh = blk / a.nsplit, split = blk % a.nsplit;
@@ -82,38 +84,76 @@ __device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &
         }
     }
 
-    Raw8<TI> rx[NXS], ry[NYS];
-    float rg = 0.f;
+    // Prefetch registers, NSET sets: chunk it + NSET is loaded while chunk it is
+    // folded in (with two, a load has a whole chunk of work to arrive). Every load is
+    // unconditional (rows past the end re-read the last row; masks zero them
+    // where the registers are used; chunks past the end re-read the last one,
+    // unused), so the compiler counts the loads in flight exactly and waits for
+    // a set only where it is used.
+    constexpr int NSET = 2;                  // register sets
+    constexpr int NU = (int)sizeof(TI) / 2;  // 16-byte words per 8 elements
+    u32x4 rx[NSET][NXS][NU], ry[NSET][NYS][NU];
+    uint32_t kxm[NSET][NXS], kym[NSET][NYS], kg[NSET];
+    float rg[NSET];
     // reverse scan of the normalized variant: dO rows scaled by rho (1 / den)
     const float *rho = FWD ? nullptr : (a.rho ? a.rho + (size_t)bh * L : nullptr);
-    float rr[NYS];
-    auto load = [&](int c) __attribute__((always_inline)) {
-        const int t0 = c * C, nv = min(C, L - t0);
+    float rr[NSET][NYS];
+    auto chunk_of = [&](int it) __attribute__((always_inline)) {
+        it = min(it, nchunks - 1);
+        return FWD ? it : nchunks - 1 - it;
+    };
+    auto load = [&](auto set_tag, int it) __attribute__((always_inline)) {
+        constexpr int P = decltype(set_tag)::value % NSET;
+        const int t0 = chunk_of(it) * C, nv = min(C, L - t0);
+        const TI *px[NXS], *py[NYS];
 #pragma unroll
         for (int m = 0; m < NXS; ++m) {
-            const int sid = tid + 256 * m, row = sid / SEGX;
-            rx[m] = (sid < C * SEGX && row < nv) ? ld_raw8<TI>(xg + (size_t)(t0 + row) * DK + 8 * (sid % SEGX))
-                                                 : zero_raw8<TI>();
+            const int sid = min(tid + 256 * m, C * SEGX - 1), row = sid / SEGX;
+            kxm[P][m] = (tid + 256 * m < C * SEGX && row < nv) ? 0xffffffffu : 0u;
+            px[m] = xg + (size_t)(t0 + min(row, nv - 1)) * DK + 8 * (sid % SEGX);
         }
 #pragma unroll
         for (int m = 0; m < NYS; ++m) {
-            const int sid = tid + 256 * m, row = sid / SEGY;
-            ry[m] = (sid < C * SEGY && row < nv) ? ld_raw8<TI>(yg + (size_t)(t0 + row) * dv + 8 * (sid % SEGY))
-                                                 : zero_raw8<TI>();
-            rr[m] = (rho && sid < C * SEGY && row < nv) ? rho[t0 + row] : 1.f;
+            const int sid = min(tid + 256 * m, C * SEGY - 1), row = sid / SEGY;
+            kym[P][m] = (tid + 256 * m < C * SEGY && row < nv) ? 0xffffffffu : 0u;
+            py[m] = yg + (size_t)(t0 + min(row, nv - 1)) * dv + 8 * (sid % SEGY);
+            rr[P][m] = rho ? rho[t0 + min(row, nv - 1)] : 1.f;
         }
-        if constexpr (DECAY) rg = lane < nv ? lg[t0 + lane] : 0.f;
+#pragma unroll
+        for (int m = 0; m < NXS; ++m)
+#pragma unroll
+            for (int i = 0; i < NU; ++i) rx[P][m][i] = reinterpret_cast<const u32x4 *>(px[m])[i];
+#pragma unroll
+        for (int m = 0; m < NYS; ++m)
+#pragma unroll
+            for (int i = 0; i < NU; ++i) ry[P][m][i] = reinterpret_cast<const u32x4 *>(py[m])[i];
+        if constexpr (DECAY) {
+            kg[P] = lane < nv ? 0xffffffffu : 0u;
+            rg[P] = lg[t0 + min(lane, nv - 1)];
+        }
     };
-    if (nchunks > 0) load(FWD ? 0 : nchunks - 1);
+    // eight prefetched elements, masked, as Raw8
+    auto take = [&](const u32x4 (&r)[NU], uint32_t k) __attribute__((always_inline)) -> Raw8<TI> {
+        Raw8<TI> o;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const u32x4 w = r[i] & k;
+            o.v[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        return o;
+    };
 
-    for (int it = 0; it < nchunks; ++it) {
-        const int c = FWD ? it : nchunks - 1 - it;
+    // chunk `it` of the scan from tile buffer B and register set B % NSET
+    auto step = [&](auto set_tag, int it) __attribute__((always_inline)) {
+        constexpr int B = decltype(set_tag)::value;  // tile buffer
+        constexpr int P = B % NSET;                  // register set
+        const int c = chunk_of(it);
         // store the state this chunk starts from (forward) / ends at (backward), transposed
         TM *hc = hs + (size_t)c * DK * dv;
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int tile = wv + 4 * m;
-            if (tile < NTILE) {
+            if (NTILE % 4 == 0 || tile < NTILE) {
                 const int ti = tile / NTJ, tj = tile % NTJ;
                 st4<TM>(hc + (size_t)(j0 + tj * 16 + n) * DK + ti * 16 + 4 * g, Sacc[m]);
             }
@@ -121,24 +161,23 @@ __device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &
         // the chunk's gate prefix, rows in lanes (every wave)
         float G = 0.f, gend = 0.f;
         if constexpr (DECAY) {
-            G = wave_inclusive_sum(rg);
+            G = wave_inclusive_sum(__uint_as_float(__float_as_uint(rg[P]) & kg[P]));
             gend = __shfl(G, 63, 64);
         }
-        __syncthreads();  // the previous chunk's operand reads are done
 #pragma unroll
         for (int m = 0; m < NXS; ++m) {
             const int sid = tid + 256 * m;
             if (sid < C * SEGX) {
                 const int row = sid / SEGX;
                 float x[8];
-                unpack8<TI>(rx[m], x);
+                unpack8<TI>(take(rx[P][m], kxm[P][m]), x);
                 if constexpr (DECAY) {
                     const float Gr = __shfl(G, row, 64);
                     const float f = FWD ? __expf(gend - Gr) : __expf(Gr);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) x[e] *= f;
                 }
-                st8<TM>(&Xs[row * PX + 8 * (sid % SEGX)], x);
+                st8<TM>(&Xs[B][row * PX + 8 * (sid % SEGX)], x);
             }
         }
 #pragma unroll
@@ -146,37 +185,56 @@ __device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &
             const int sid = tid + 256 * m;
             if (sid < C * SEGY) {
                 float y[8];
-                unpack8<TI>(ry[m], y);
+                unpack8<TI>(take(ry[P][m], kym[P][m]), y);
                 if (rho) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) y[e] *= rr[m];
+                    for (int e = 0; e < 8; ++e) y[e] *= rr[P][m];
                 }
-                st8<TM>(&Ys[(sid / SEGY) * PY + 8 * (sid % SEGY)], y);
+                st8<TM>(&Ys[B][(sid / SEGY) * PY + 8 * (sid % SEGY)], y);
             }
         }
-        if (it + 1 < nchunks) load(FWD ? c + 1 : c - 1);
-        __syncthreads();
+        // keep the loads after the last reads of this set: hoisted above them they
+        // would need fresh registers, copied back at the loop head after a wait
+        __builtin_amdgcn_sched_barrier(0);
+        load(set_tag, it + NSET);
+        __syncthreads();  // buffer B staged
         const float eg = DECAY ? __expf(gend) : 1.f;
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int tile = wv + 4 * m;
-            if (tile < NTILE) {
+            if (NTILE % 4 == 0 || tile < NTILE) {
                 const int ti = tile / NTJ, tj = tile % NTJ;
                 Sacc[m] *= eg;
 #pragma unroll
                 for (int ks = 0; ks < NTK; ++ks) {
                     frag xa, yb;
                     if constexpr (H) {
-                        xa = tr_frag<PX>(Xs, 32 * ks + 4 * g, ti * 16, lane);
-                        yb = tr_frag<PY>(Ys, 32 * ks + 4 * g, tj * 16, lane);
+                        xa = tr_frag<PX>(Xs[B], 32 * ks + 4 * g, ti * 16, lane);
+                        yb = tr_frag<PY>(Ys[B], 32 * ks + 4 * g, tj * 16, lane);
                     } else {
-                        xa = Xs[(4 * ks + g) * PX + ti * 16 + n];
-                        yb = Ys[(4 * ks + g) * PY + tj * 16 + n];
+                        xa = Xs[B][(4 * ks + g) * PX + ti * 16 + n];
+                        yb = Ys[B][(4 * ks + g) * PY + tj * 16 + n];
                     }
                     Sacc[m] = MF::mma(xa, yb, Sacc[m]);
                 }
             }
         }
+    };
+
+    // settle the initial state's loads, so that no load of the prologue is pending
+    // at the loop head and the waits inside the loop count only the prefetch
+    __builtin_amdgcn_s_waitcnt(0);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    if (nchunks > 0) {
+        load(S0{}, 0);
+        if constexpr (NSET == 2) load(S1{}, 1);
+        int it = 0;
+        for (; it + 1 < nchunks; it += 2) {
+            step(S0{}, it);
+            step(S1{}, it + 1);
+        }
+        if (it < nchunks) step(S0{}, it);
     }
     // forward: the final state S_L; backward: dLoss/dS_0
     float *out = FWD ? a.s_last : a.gs_in;
@@ -197,12 +255,17 @@ __device__ __attribute__((always_inline)) inline void state_scan(const BwdArgs &
 // The two scans are independent; one launch runs both, the forward one on the
 // first BH * nsplit workgroups.
 template <typename TI, int DK, int DVT, bool DECAY>
-__global__ void __launch_bounds__(256) state_scans_kernel(BwdArgs a) {
-    const int per = a.BH * a.nsplit;
-    if ((int)blockIdx.x < per)
-        state_scan<TI, DK, DVT, true, DECAY>(a, blockIdx.x);
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) state_scans_kernel(BwdArgs a) {
+    // both directions' tiles: two buffers of X (C x PX) and Y (C x PY) in the operand type
+    using TM = typename OpOf<TI>::type;
+    constexpr int PAD = sizeof(TM) == 2 ? 16 : 4;
+    __shared__ __align__(16) TM lds[2 * 64 * (DK + PAD + DVT + PAD)];
+    // value slices of one head on one XCD: they share its rows through that L2
+    const int per = a.BH * a.nsplit, vid = xcd_virtual_block();
+    if (vid < per)
+        state_scan<TI, DK, DVT, true, DECAY>(a, vid, lds);
     else
-        state_scan<TI, DK, DVT, false, DECAY>(a, blockIdx.x - per);
+        state_scan<TI, DK, DVT, false, DECAY>(a, vid - per, lds);
 }
 
 // ---------------------------------------------------------------------------

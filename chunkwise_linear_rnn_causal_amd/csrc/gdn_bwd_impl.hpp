@@ -448,10 +448,12 @@ __global__ void __launch_bounds__(512) gdn_bwd_scan_kernel(BwdArgs a) {
     using Cfg = GdnScanCfg<DK, DV>;
     __shared__ __attribute__((aligned(16))) f16 lds[Cfg::TOTAL];
     __shared__ float Eg[2];
-    if (blockIdx.x < a.BH * Cfg::NS)
-        gdn_scan<DK, DV, false>(a, blockIdx.x, lds, Eg);
+    // value slices of one head on one XCD: they share its rows through that L2
+    const int vid = xcd_virtual_block();
+    if (vid < a.BH * Cfg::NS)
+        gdn_scan<DK, DV, false>(a, vid, lds, Eg);
     else
-        gdn_scan<DK, DV, true>(a, blockIdx.x - a.BH * Cfg::NS, lds, Eg);
+        gdn_scan<DK, DV, true>(a, vid - a.BH * Cfg::NS, lds, Eg);
 }
 
 // ---------------------------------------------------------------------------

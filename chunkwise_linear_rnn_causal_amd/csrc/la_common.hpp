@@ -21,6 +21,9 @@ typedef _Float16 f16;
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 raw bytes as a native vector (copies of HIP's uint4 struct can become memory
+// copies that keep a register array in scratch)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum Variant { V_PLAIN = 0, V_NORM = 1, V_DECAY = 2, V_GDN = 3, V_VDECAY = 4, V_KDA = 5 };
 

@@ -60,7 +60,7 @@ namespace la {
 // state scan over the chunks: S <- Diag(e^{G_end}) S + X^T Y with
 // X = k (.) e^{G_end - G}, Y = v (forward) or X = q (.) e^{G}, Y = dO (backward).
 template <int DK, int DVT, bool FWD>
-__device__ __attribute__((always_inline)) inline void vd_scan(const BwdArgs &a, int blk) {
+__device__ __attribute__((always_inline)) inline void vd_scan(const BwdArgs &a, int blk, f16 *lds) {
     using MF = Mfma<f16>;
     using frag = MF::frag;
     constexpr int C = 64;
@@ -70,9 +70,11 @@ __device__ __attribute__((always_inline)) inline void vd_scan(const BwdArgs &a, 
     constexpr int CW = DK / 4, NXU = CW / 8;  // channels per wave; 16-byte units of a row's share
     constexpr int SEGY = DVT / 8, NYS = (C * SEGY + 255) / 256;
     static_assert(CW % 8 == 0, "channel share");
-    __shared__ __align__(16) f16 Xs[C * PX];
-    __shared__ __align__(16) f16 Ys[C * PY];
-    __shared__ __align__(16) float Eend[DK];
+    // double-buffered operand tiles: chunk it is staged into buffer it & 1, whose
+    // last reader (chunk it - 2) is behind the barrier of chunk it - 1
+    f16(*Xs)[C * PX] = reinterpret_cast<f16(*)[C * PX]>(lds);
+    f16(*Ys)[C * PY] = reinterpret_cast<f16(*)[C * PY]>(lds + 2 * C * PX);
+    float(*Eend)[DK] = reinterpret_cast<float(*)[DK]>(lds + 2 * C * (PX + PY));
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
     const int bh = blk / a.nsplit, split = blk % a.nsplit;
@@ -96,95 +98,125 @@ __device__ __attribute__((always_inline)) inline void vd_scan(const BwdArgs &a, 
         }
     }
 
-    uint4 rx[NXU];     // row `lane`: this wave's CW channels (bf16)
-    f32x4 rg[CW / 4];  // their log-gates
-    Raw8<bf16> ry[NYS];
-    auto load = [&](int c) __attribute__((always_inline)) {
-        const int t0 = c * C, nv = min(C, L - t0);
-        const bool ok = lane < nv;
-        const size_t row = (size_t)(t0 + lane) * DK;
-#pragma unroll
-        for (int u = 0; u < NXU; ++u)
-            rx[u] = ok ? reinterpret_cast<const uint4 *>(xg + row)[u] : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int u = 0; u < CW / 4; ++u)
-            rg[u] = ok ? *reinterpret_cast<const f32x4 *>(lg + row + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+    // Prefetch registers: chunk it + NSET is loaded while chunk it is folded in.
+    // Every load is
+    // unconditional (rows past the end re-read the last row; the masks kx, ky
+    // zero them where the registers are used; chunks past the end re-read the
+    // last one, unused), so the compiler counts the loads in flight exactly and
+    // waits for a set only where it is used.
+    constexpr int NSET = 1;  // register sets (two need more than 256 VGPRs)
+    u32x4 rx[NSET][NXU];     // row `lane`: this wave's CW channels (bf16)
+    u32x4 rg[NSET][CW / 4];  // their log-gates (fp32 bits)
+    u32x4 ry[NSET][NYS];
+    uint32_t kx[NSET], ky[NSET][NYS];
+    auto chunk_of = [&](int it) __attribute__((always_inline)) {
+        it = min(it, nchunks - 1);
+        return FWD ? it : nchunks - 1 - it;
+    };
+    auto load = [&](auto set_tag, int it) __attribute__((always_inline)) {
+        constexpr int P = decltype(set_tag)::value % NSET;
+        const int t0 = chunk_of(it) * C, nv = min(C, L - t0);
+        kx[P] = lane < nv ? 0xffffffffu : 0u;
+        const size_t row = (size_t)(t0 + min(lane, nv - 1)) * DK;
+        const u32x4 *py[NYS];
 #pragma unroll
         for (int m = 0; m < NYS; ++m) {
-            const int sid = tid + 256 * m, r = sid / SEGY;
-            ry[m] = (sid < C * SEGY && r < nv) ? ld_raw8<bf16>(yg + (size_t)(t0 + r) * dv + 8 * (sid % SEGY))
-                                               : zero_raw8<bf16>();
+            const int sid = min(tid + 256 * m, C * SEGY - 1), r = sid / SEGY;
+            ky[P][m] = (tid + 256 * m < C * SEGY && r < nv) ? 0xffffffffu : 0u;
+            py[m] = reinterpret_cast<const u32x4 *>(yg + (size_t)(t0 + min(r, nv - 1)) * dv + 8 * (sid % SEGY));
         }
+        const u32x4 *px = reinterpret_cast<const u32x4 *>(xg + row);
+        const u32x4 *pg = reinterpret_cast<const u32x4 *>(lg + row);
+#pragma unroll
+        for (int m = 0; m < NYS; ++m) ry[P][m] = *py[m];
+#pragma unroll
+        for (int u = 0; u < NXU; ++u) rx[P][u] = px[u];
+#pragma unroll
+        for (int u = 0; u < CW / 4; ++u) rg[P][u] = pg[u];
     };
-    if (nchunks > 0) load(FWD ? 0 : nchunks - 1);
 
-    for (int it = 0; it < nchunks; ++it) {
-        const int c = FWD ? it : nchunks - 1 - it;
+    // chunk `it` of the scan from tile buffer B and register set B % NSET
+    auto step = [&](auto set_tag, int it) __attribute__((always_inline)) {
+        constexpr int B = decltype(set_tag)::value;  // tile buffer
+        constexpr int P = B % NSET;                  // register set
+        const int c = chunk_of(it);
         // the state this chunk starts from (forward) / ends at (backward), transposed
         f16 *hc = hs + (size_t)c * DK * dv;
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int tile = wv + 4 * m;
-            if (tile < NTILE) {
+            if (NTILE % 4 == 0 || tile < NTILE) {
                 const int ti = tile / NTJ, tj = tile % NTJ;
                 st4<f16>(hc + (size_t)(j0 + tj * 16 + n) * DK + ti * 16 + 4 * g, Sacc[m]);
             }
         }
         // per channel: gate prefix over the rows (lanes), the chunk's total, and the
-        // scaled operand row
-        float x[CW], gend[CW];
+        // scaled operand row, staged 8 channels at a time
 #pragma unroll
         for (int u = 0; u < NXU; ++u) {
             Raw8<bf16> r8;
-            r8.v[0] = rx[u];
-            float t8[8];
-            unpack8<bf16>(r8, t8);
+            const u32x4 w = rx[P][u] & kx[P];
+            r8.v[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            float x[8];
+            unpack8<bf16>(r8, x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[8 * u + e] = t8[e];
-        }
-#pragma unroll
-        for (int i = 0; i < CW; ++i) {
-            const float G = wave_inclusive_sum(fmaxf(rg[i / 4][i % 4], kMinChannelLogGate));
-            gend[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
-            x[i] *= __expf(FWD ? gend[i] - G : G);
-        }
-        __syncthreads();  // the previous chunk's operand reads are done
-#pragma unroll
-        for (int u = 0; u < NXU; ++u) {
-            float t8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) t8[e] = x[8 * u + e];
-            st8<f16>(&Xs[lane * PX + wv * CW + 8 * u], t8);
-        }
-        if (lane == 0) {
-#pragma unroll
-            for (int i = 0; i < CW; ++i) Eend[wv * CW + i] = __expf(gend[i]);
+            for (int e = 0; e < 8; ++e) {
+                const int i = 8 * u + e;
+                const float G =
+                    wave_inclusive_sum(fmaxf(__uint_as_float(rg[P][i / 4][i % 4] & kx[P]), kMinChannelLogGate));
+                const float gend = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
+                x[e] *= __expf(FWD ? gend - G : G);
+                if (lane == 0) Eend[B][wv * CW + i] = __expf(gend);
+            }
+            st8<f16>(&Xs[B][lane * PX + wv * CW + 8 * u], x);
         }
 #pragma unroll
         for (int m = 0; m < NYS; ++m) {
             const int sid = tid + 256 * m;
             if (sid < C * SEGY) {
                 float y[8];
-                unpack8<bf16>(ry[m], y);
-                st8<f16>(&Ys[(sid / SEGY) * PY + 8 * (sid % SEGY)], y);
+                Raw8<bf16> r8;
+                const u32x4 w = ry[P][m] & ky[P][m];
+                r8.v[0] = make_uint4(w[0], w[1], w[2], w[3]);
+                unpack8<bf16>(r8, y);
+                st8<f16>(&Ys[B][(sid / SEGY) * PY + 8 * (sid % SEGY)], y);
             }
         }
-        if (it + 1 < nchunks) load(FWD ? c + 1 : c - 1);
-        __syncthreads();
+        // keep the loads after the last reads of this set: hoisted above them they
+        // would need fresh registers, copied back at the loop head after a wait
+        __builtin_amdgcn_sched_barrier(0);
+        load(set_tag, it + NSET);
+        __syncthreads();  // buffer B staged
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
             const int tile = wv + 4 * m;
-            if (tile < NTILE) {
+            if (NTILE % 4 == 0 || tile < NTILE) {
                 const int ti = tile / NTJ, tj = tile % NTJ;
-                Sacc[m] *= *reinterpret_cast<const f32x4 *>(&Eend[ti * 16 + 4 * g]);
+                Sacc[m] *= *reinterpret_cast<const f32x4 *>(&Eend[B][ti * 16 + 4 * g]);
 #pragma unroll
                 for (int ks = 0; ks < NTK; ++ks) {
-                    const frag xa = tr_frag<PX>(Xs, 32 * ks + 4 * g, ti * 16, lane);
-                    const frag yb = tr_frag<PY>(Ys, 32 * ks + 4 * g, tj * 16, lane);
+                    const frag xa = tr_frag<PX>(Xs[B], 32 * ks + 4 * g, ti * 16, lane);
+                    const frag yb = tr_frag<PY>(Ys[B], 32 * ks + 4 * g, tj * 16, lane);
                     Sacc[m] = MF::mma(xa, yb, Sacc[m]);
                 }
             }
         }
+    };
+
+    // settle the initial state's loads, so that no load of the prologue is pending
+    // at the loop head and the waits inside the loop count only the prefetch
+    __builtin_amdgcn_s_waitcnt(0);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    if (nchunks > 0) {
+        load(S0{}, 0);
+        if constexpr (NSET == 2) load(S1{}, 1);
+        int it = 0;
+        for (; it + 1 < nchunks; it += 2) {
+            step(S0{}, it);
+            step(S1{}, it + 1);
+        }
+        if (it < nchunks) step(S0{}, it);
     }
     // forward: the final state S_L; backward: dLoss/dS_0
     float *out = FWD ? a.s_last : a.gs_in;
@@ -206,11 +238,15 @@ __device__ __attribute__((always_inline)) inline void vd_scan(const BwdArgs &a, 
 // workgroups.
 template <int DK, int DVT>
 __global__ void __launch_bounds__(256) vd_scans_kernel(BwdArgs a) {
-    const int per = a.BH * a.nsplit;
-    if ((int)blockIdx.x < per)
-        vd_scan<DK, DVT, true>(a, blockIdx.x);
+    // both directions' tiles: two buffers of X (C x (DK + 16)) and Y (C x (DVT + 16))
+    // in fp16, then two rows of DK gate factors
+    __shared__ __align__(16) f16 lds[2 * 64 * (DK + 16 + DVT + 16) + 4 * DK];
+    // value slices of one head on one XCD: they share its rows and gates through that L2
+    const int per = a.BH * a.nsplit, vid = xcd_virtual_block();
+    if (vid < per)
+        vd_scan<DK, DVT, true>(a, vid, lds);
     else
-        vd_scan<DK, DVT, false>(a, blockIdx.x - per);
+        vd_scan<DK, DVT, false>(a, vid - per, lds);
 }
 
 // ---------------------------------------------------------------------------
