@@ -399,14 +399,18 @@ __global__ void __launch_bounds__(256, KT > 0 ? 3 : 4) gdn_prep_kernel(PrepArgs 
     // holding column n of the block in registers (the four lane groups compute
     // the same column; group 0 writes it).
     {
+        // column by column: once T[s][n] is known it enters every later row's
+        // sum, so the serial chain is one fma per row (each row's sum still
+        // adds its terms in the order s = 0, 1, ...)
         const int base = 16 * wv;
-        float tc[16];
+        float tc[16], acc[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = 0.f;
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-            for (int s = 0; s < r; ++s) acc = fmaf(Pm[(base + r) * TP + base + s], tc[s], acc);
-            tc[r] = (r == n) ? 1.f : ((r < n) ? 0.f : -acc);
+        for (int s = 0; s < 16; ++s) {
+            tc[s] = (s == n) ? 1.f : ((s < n) ? 0.f : -acc[s]);
+#pragma unroll
+            for (int r = s + 1; r < 16; ++r) acc[r] = fmaf(Pm[(base + r) * TP + base + s], tc[s], acc[r]);
         }
         if (g == 0) {
 #pragma unroll

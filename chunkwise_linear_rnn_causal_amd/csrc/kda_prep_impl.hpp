@@ -180,8 +180,9 @@ __global__ void __launch_bounds__(256, 2) kda_prep_kernel(PrepArgs a) {
             // diagonal block, rebased around its middle token (the K slot of step
             // 8u + e is channel c0 + e of this lane's token, in A and B alike)
             const float x = __expf(gr[e] - gm[e]);
-            pd = __builtin_amdgcn_mfma_f32_16x16x4f32(k8[e] * x, k8[e] / x, pd, 0, 0, 0);
-            md = __builtin_amdgcn_mfma_f32_16x16x4f32(k8[e] / x, q8[e] * x, md, 0, 0, 0);
+            const float kx = k8[e] * __builtin_amdgcn_rcpf(x);  // a correctly rounded divide costs ten instructions
+            pd = __builtin_amdgcn_mfma_f32_16x16x4f32(k8[e] * x, kx, pd, 0, 0, 0);
+            md = __builtin_amdgcn_mfma_f32_16x16x4f32(kx, q8[e] * x, md, 0, 0, 0);
         }
         float kcv[8];
 #pragma unroll
@@ -258,14 +259,18 @@ __global__ void __launch_bounds__(256, 2) kda_prep_kernel(PrepArgs a) {
     // substitution (wave w, lane n holding column n), the blocks below as
     // T_ij = -T_ii sum_{j <= k < i} P_ik T_kj on fp32 MFMA
     {
+        // column by column: once T[s][n] is known it enters every later row's
+        // sum, so the serial chain is one fma per row (each row's sum still
+        // adds its terms in the order s = 0, 1, ...)
         const int base = 16 * wv;
-        float tc[16];
+        float tc[16], acc[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = 0.f;
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-            for (int s = 0; s < r; ++s) acc = fmaf(Pm[(base + r) * TP + base + s], tc[s], acc);
-            tc[r] = (r == n) ? 1.f : ((r < n) ? 0.f : -acc);
+        for (int s = 0; s < 16; ++s) {
+            tc[s] = (s == n) ? 1.f : ((s < n) ? 0.f : -acc[s]);
+#pragma unroll
+            for (int r = s + 1; r < 16; ++r) acc[r] = fmaf(Pm[(base + r) * TP + base + s], tc[s], acc[r]);
         }
         if (g == 0) {
 #pragma unroll
