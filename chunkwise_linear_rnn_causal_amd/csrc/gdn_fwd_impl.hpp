@@ -26,15 +26,16 @@
 //    whole slice of S, so the fp16 operand scale (a power of two keeping the
 //    carried state inside fp16's range) comes from an exact wave maximum.
 //  - waves 1-3 stage K and W of chunk c+1 into the other half of
-//    double-buffered LDS tiles (loads issued two chunks ahead) and build the
-//    gate tables.
+//    double-buffered LDS tiles (loads issued two chunks ahead).
 //  - waves 4-7, one per 16-row block, form the outputs: the inter term of
 //    chunk c in iteration c, and the intra term (scores times U) of chunk c in
 //    iteration c+1, when the chain wave has left U's fragments in LDS; the
 //    fragment of S^T they need is the chain wave's B operand of S, written
 //    once per chunk. Their query rows and score fragments come straight from
 //    global memory into registers (two chunks ahead), so the only LDS reads of
-//    these waves are S^T and U.
+//    these waves are S^T and U. The first of them, whose block has the fewest
+//    scores, also builds the gate tables of the next chunk (cycle counters per
+//    role showed the gate tables making their staging wave the longest role).
 // One barrier per chunk. Operand K slots of Q and W rows follow the channel
 // order {32p + 4g + e, 32p + 16 + 4g + e} of S's fragments (two 8-byte pieces
 // per fragment). The per-workgroup LDS traffic is what bounds the chunk period
@@ -292,11 +293,6 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
         auto stage_role = [&](auto sw_tag) __attribute__((always_inline)) {
         constexpr int sw = decltype(sw_tag)::value;
         uint4 pre[2][NSL];
-        float gpre[2];
-        constexpr int NCD = (DK + 63) / 64;
-        float cpre[2][NCD];
-        const float *gsrc = lgg ? lgg : reinterpret_cast<const float *>(kg);  // kg: at least L floats
-        constexpr bool gate_wave = sw == 0;
         // slot m of this wave: wave load i = sw + 3 m (the last wave load again past
         // the end, so every staging wave has the same loads in flight); tensor
         // i / NI1 (0 K, 1 W)
@@ -311,16 +307,6 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
                     pre[set][m] = *reinterpret_cast<const uint4 *>(wg + (size_t)t * DK + seg * 8);
                 else
                     pre[set][m] = *reinterpret_cast<const uint4 *>(kg + (size_t)min(t, L - 1) * DK + seg * 8);
-            }
-            // unconditional as well, from a valid address when there is no gate; the
-            // value is masked where it is used (masking it here would wait for it here)
-            if (gate_wave) gpre[set] = gsrc[min(c * C + lane, L - 1)];
-            if constexpr (VEC) {
-                if (gate_wave) {
-#pragma unroll
-                    for (int i = 0; i < NCD; ++i)
-                        cpre[set][i] = a.cdec[((size_t)bh * nchunks + c) * DK + min(lane + 64 * i, DK - 1)];
-                }
             }
         };
         auto stage_chunk = [&](int c, int set, int buf) __attribute__((always_inline)) {
@@ -345,21 +331,8 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
                     *reinterpret_cast<uint4 *>(&X[Cfg::OK + row * KP + seg * 8]) = h;
                 }
             }
-            if (gate_wave) {
-                // chunk-local inclusive prefix of the log-gates (rows past L: 0)
-                float *T = Tg + buf * 2 * C;
-                const float G = wave_inclusive_sum((lgg && c * C + lane < L) ? gpre[set] : 0.f);
-                const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
-                T[lane] = __expf(G);
-                T[C + lane] = __expf(gC - G);
-                if (lane == 0) Tsc[buf] = __expf(gC);
-                if constexpr (VEC) {
-#pragma unroll
-                    for (int i = 0; i < NCD; ++i)
-                        if (lane + 64 * i < DK) Cd[buf][lane + 64 * i] = cpre[set][i];
-                }
-            }
         };
+
         // Loads are issued unconditionally (chunk indices past the end repeat the
         // last chunk), so every path leaves the same loads in flight and the wait
         // before each staged slot is exact: two chunks of loads stay in flight.
@@ -421,6 +394,14 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
         // last chunk, so every iteration leaves the same loads in flight.
         uint2 qraw[2][NKS][2];
         uint4 mraw[2][NP];
+        // The first output wave (the one with the least work) also builds the gate
+        // tables: in iteration c those of chunk c+1, from log-gates loaded with
+        // that chunk's queries (and, for VEC, the chunk's per-channel state decay).
+        constexpr bool GT = rb == 0;
+        constexpr int NCD = (DK + 63) / 64;
+        float gpre[2];
+        float cpre[2][NCD];
+        const float *gsrc = lgg ? lgg : reinterpret_cast<const float *>(kg);  // kg: at least L floats
         auto load = [&](int c, int set) __attribute__((always_inline)) {
             const uint16_t *qrow = qg + (size_t)min(c * C + r, L - 1) * DK + 4 * g;
 #pragma unroll
@@ -431,6 +412,32 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
             const f16 *mrow = mg + (size_t)c * (6 * 512) + F0 * 512 + lane * 8;
 #pragma unroll
             for (int p = 0; p < NP; ++p) mraw[set][p] = *reinterpret_cast<const uint4 *>(mrow + p * 512);
+            if constexpr (GT) {
+                // unconditional, from a valid address when there is no gate; the value
+                // is masked where it is used (masking it here would wait for it here)
+                gpre[set] = gsrc[min(c * C + lane, L - 1)];
+                if constexpr (VEC) {
+#pragma unroll
+                    for (int i = 0; i < NCD; ++i)
+                        cpre[set][i] = a.cdec[((size_t)bh * nchunks + c) * DK + min(lane + 64 * i, DK - 1)];
+                }
+            }
+        };
+        // gate tables of chunk c from register set `set` into buffer `buf`: the
+        // chunk-local inclusive prefix G of the log-gates (rows past L: 0), exp(G),
+        // exp(g_C - G) and exp(g_C)
+        auto gate_tables = [&](int c, int set, int buf) __attribute__((always_inline)) {
+            float *T = Tg + buf * 2 * C;
+            const float G = wave_inclusive_sum((lgg && c * C + lane < L) ? gpre[set] : 0.f);
+            const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
+            T[lane] = __expf(G);
+            T[C + lane] = __expf(gC - G);
+            if (lane == 0) Tsc[buf] = __expf(gC);
+            if constexpr (VEC) {
+#pragma unroll
+                for (int i = 0; i < NCD; ++i)
+                    if (lane + 64 * i < DK) Cd[buf][lane + 64 * i] = cpre[set][i];
+            }
         };
         f32x4 oprev = {0.f, 0.f, 0.f, 0.f};
         f16x8 bprev[NP];
@@ -446,6 +453,7 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
         if (nchunks > 0) {
             load(0, 0);
             load(min(1, nchunks - 1), 1);
+            if constexpr (GT) gate_tables(0, 0, 0);
         }
         __syncthreads();  // prologue
         auto iter = [&](int c, auto par) __attribute__((always_inline)) {
@@ -482,6 +490,9 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
 #pragma unroll
             for (int p = 0; p < NP; ++p) bprev[p] = mf[p];
             shprev = sh;
+            // chunk c+1's tables into the other buffer, last read in iteration c-1
+            // (past the end: a repeat of the last chunk that no wave reads)
+            if constexpr (GT) gate_tables(c + 1, P ^ 1, P ^ 1);
             __syncthreads();
         };
         int c = 0;

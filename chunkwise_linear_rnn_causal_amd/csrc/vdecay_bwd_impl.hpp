@@ -526,7 +526,8 @@ __global__ void __launch_bounds__(512) vd_bwd_grad_kernel(BwdArgs a) {
         for (int t = 0; t < DK / 4; ++t) {
             const int ch = 4 * t + g;
             const float x = __expf(Gs[r * PG + ch] - Gs[mid * PG + ch]);
-            atD = MS::mma(rawf(Qr, r * PK + ch) * x, rawf(Kr, r * PK + ch) / x, atD);
+            // a hardware reciprocal: a correctly rounded divide costs ten instructions
+            atD = MS::mma(rawf(Qr, r * PK + ch) * x, rawf(Kr, r * PK + ch) * __builtin_amdgcn_rcpf(x), atD);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
