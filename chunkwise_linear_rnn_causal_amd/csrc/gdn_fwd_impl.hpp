@@ -215,13 +215,22 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
             for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
                 for (int p = 0; p < NKS; ++p) wf[rb][p] = chan_frag<WP>(Ws, rb * 16 + n, p, g);
+            // the scalar gate's weights and decay; VEC has no scalar gate (both are 1)
+            // and reads the per-channel decay of its state rows instead
             f32x4 wlo[2], whi[2];
+            float eg = 1.f;
+            f32x4 cd[VEC ? NTI : 1];
+            if constexpr (VEC) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                wlo[q] = *reinterpret_cast<const f32x4 *>(&T[C + 32 * q + 4 * g]);
-                whi[q] = *reinterpret_cast<const f32x4 *>(&T[C + 32 * q + 16 + 4 * g]);
+                for (int ti = 0; ti < NTI; ++ti) cd[ti] = *reinterpret_cast<const f32x4 *>(&Cd[P][ti * 16 + 4 * g]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    wlo[q] = *reinterpret_cast<const f32x4 *>(&T[C + 32 * q + 4 * g]);
+                    whi[q] = *reinterpret_cast<const f32x4 *>(&T[C + 32 * q + 16 + 4 * g]);
+                }
+                eg = Tsc[P];
             }
-            const float eg = Tsc[P];
             __builtin_amdgcn_sched_barrier(0);
             // U 2^-sh = U~ 2^-sh + W (-St)
             f32x4 U[NRB];
@@ -255,12 +264,13 @@ __global__ void __launch_bounds__(512) gdn_fwd_kernel(ChunkArgs a) {
             // as they are for the output waves
             f16x8 ub[2];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) ub[q] = pack_tiles(U[2 * q] * wlo[q], U[2 * q + 1] * whi[q], 1.f);
+            for (int q = 0; q < 2; ++q)
+                ub[q] = VEC ? pack_tiles(U[2 * q], U[2 * q + 1], 1.f)
+                            : pack_tiles(U[2 * q] * wlo[q], U[2 * q + 1] * whi[q], 1.f);
 #pragma unroll
-            for (int ti = 0; ti < NTI; ++ti) St[ti] *= eg;
-            if constexpr (VEC) {
-#pragma unroll
-                for (int ti = 0; ti < NTI; ++ti) St[ti] *= *reinterpret_cast<const f32x4 *>(&Cd[P][ti * 16 + 4 * g]);
+            for (int ti = 0; ti < NTI; ++ti) {
+                if constexpr (VEC) St[ti] *= cd[ti];
+                else St[ti] *= eg;
             }
 #pragma unroll
             for (int q = 0; q < 2; ++q)
