@@ -50,7 +50,7 @@ def test_chunk_work(name, per_unit, units, flop_unit, launched_unit, state):
     assert flop == pytest.approx(flop_unit * units, rel=1e-12)
 
 
-def test_headline_is_the_largest_single_gpu_workload_with_survey_bytes():
+def test_headline_is_the_largest_single_gpu_workload_with_algorithmic_bytes():
     # decay B4 H32 L8192 d128: q, k, v, o bf16 (1,073,741,824 B) + fp32 log-gates (4 MiB)
     assert bench.HEADLINE == "decay_bf16_b4h32_l8192_d128"
     assert bench.chunk_work(W.CONFIGS[bench.HEADLINE])[1] == 1_077_936_128
