@@ -272,7 +272,7 @@ la_status check_bwd_shape(la_variant var, la_dtype dt, int B, int H, int L, int 
 }
 
 struct BwdLayout {
-    size_t hs, dhs, s_last, rterm, w, u, du, t, o, den, rho, g, ksum, gqsum, up, total;
+    size_t hs, dhs, s_last, rterm, xterm, w, u, du, t, o, den, rho, g, ksum, gqsum, up, total;
 };
 // Every array starts on a 256-byte boundary. The delta rule adds W [BH, Lp, d_k],
 // U~ / U and A_m^T dO / dU [BH, Lp, d_v] and T [BH, nchunks, 64, 64], in fp16.
@@ -286,7 +286,8 @@ BwdLayout bwd_layout(la_variant var, la_dtype dt, int64_t BH, int L, int d_k, in
     w.dhs = round_up(st, 256);
     w.s_last = w.dhs + round_up(st, 256);
     w.rterm = w.s_last + round_up((size_t)BH * d_k * d_v * 4, 256);
-    w.total = w.rterm + round_up((size_t)BH * L * 4, 256);
+    w.xterm = w.rterm + round_up((size_t)BH * L * 4, 256);
+    w.total = w.xterm + round_up((size_t)BH * nch * 4, 256);
     if (var == LA_GATED_DELTA) {
         w.w = w.total;
         w.u = w.w + round_up((size_t)BH * Lp * d_k * 2, 256);
@@ -1035,6 +1036,7 @@ la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k
     a.hs = ws + lay.hs; a.dhs = ws + lay.dhs;
     a.s_last = reinterpret_cast<float *>(ws + lay.s_last);
     a.rterm = reinterpret_cast<float *>(ws + lay.rterm);
+    a.xterm = reinterpret_cast<float *>(ws + lay.xterm);
     a.BH = (int)BH; a.L = L; a.dv = d_v; a.nsplit = 1;
     const int nch = (L + 63) / 64;
     hipError_t e;

@@ -26,9 +26,10 @@
 //       taken transposed (dQ^T = K^T dP^T, ...) so that the 16 x 16 score-like
 //       tiles dP = dO V^T, A = Q K^T leave the MFMA in exactly the B-operand
 //       layout of the next product, as in the forward kernel. It also writes
-//       q_t . dq_t - k_t . dk_t per token.
-//   dgate_kernel  one workgroup per head: reverse prefix sum of those terms plus
-//       <dS_L, S_L>.
+//       q_t . dq_t - k_t . dk_t per token and, for the scalar decay,
+//       <dH_c, H_{c+1}> per chunk.
+//   dgate_kernel  one workgroup per head: per chunk, the reverse prefix sum of
+//       those terms within the chunk, started from <dH_c, H_{c+1}>.
 #pragma once
 
 #include <type_traits>
@@ -292,6 +293,7 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
     __shared__ __align__(16) TM Ds[DV * PK];  // dH_c^T [dv][dk]
     __shared__ float Gt[C];
     __shared__ float RT[2][C];
+    __shared__ float XP[8];  // per wave: its share of <dH_c, H_{c+1}>
     __shared__ float Gend;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, n = lane & 15;
@@ -330,7 +332,7 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
             const bool ok = sid < C * SEGV && row < nv;
             rv[m] = ok ? ld_raw8<TI>(vg + off) : zero_raw8<TI>();
             ro[m] = ok ? ld_raw8<TI>(og + off) : zero_raw8<TI>();
-            rro[m] = (a.rho && ok) ? a.rho[(size_t)bh * L + t0 + row] : 1.f;
+            if constexpr (!DECAY) rro[m] = (a.rho && ok) ? a.rho[(size_t)bh * L + t0 + row] : 1.f;
         }
 #pragma unroll
         for (int m = 0; m < NS; ++m) {
@@ -375,7 +377,7 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
         if (sid < C * SEGV) {
             const int o = (sid / SEGV) * PV + 8 * (sid % SEGV);
             put(rv[m], &Vs[o]);
-            if (a.rho) {
+            if (!DECAY && a.rho) {  // the normalized variant (no gates)
                 float x[8];
                 unpack8<TI>(ro[m], x);
 #pragma unroll
@@ -386,6 +388,7 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
             }
         }
     }
+    float xterm = 0.f;  // this thread's share of <dH_c, H_c> (scalar decay)
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
         const int sid = tid + 512 * m;
@@ -395,6 +398,23 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
             for (int u = 0; u < (int)(sizeof(TM) / 2); ++u) {
                 reinterpret_cast<uint4 *>(&Hs[o])[u] = rh[m].v[u];
                 reinterpret_cast<uint4 *>(&Ds[o])[u] = rd[m].v[u];
+            }
+            if constexpr (DECAY) {
+                if constexpr (H) {  // fp16 pairs, products exact, sums in fp32
+                    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                    const uint32_t wh[4] = {rh[m].v[0].x, rh[m].v[0].y, rh[m].v[0].z, rh[m].v[0].w};
+                    const uint32_t wd[4] = {rd[m].v[0].x, rd[m].v[0].y, rd[m].v[0].z, rd[m].v[0].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        xterm = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, wh[i]), __builtin_bit_cast(h2, wd[i]),
+                                                       xterm, false);
+                } else {
+                    float xh[8], xd[8];
+                    unpack8<TM>(rh[m], xh);
+                    unpack8<TM>(rd[m], xd);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xterm += xh[e] * xd[e];
+                }
             }
         }
     }
@@ -524,6 +544,7 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
                 acc[q_] = MF::mma(tok(Ds, PKt{}, ks, ct * 16), trn(Vs, PV, s, ks), acc[q_]);
             acc[q_] *= ws;
         }
+
         // dP tiles D[r][s] = sum_j dO[r][j] V[s][j] for query blocks rbk >= w
         f32x4 dp[NRB];
 #pragma unroll
@@ -583,6 +604,18 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
                 acc[q_] = MF::mma(nat(Ds, PK, jt * 16 + n, ks, DK), nat(Ks, PK, s, ks, DK), acc[q_]);
             acc[q_] *= ws;
         }
+        // <dH_c, H_{c+1}> = e^{g_C} <dH_c, H_c> + sum_s v_s . (the state term of dv_s),
+        // since H_{c+1} = e^{g_C} H_c + sum_s e^{g_C - G_s} k_s v_s^T
+        if constexpr (DECAY) {
+            xterm *= __expf(gend);
+#pragma unroll
+            for (int q_ = 0; q_ < NJW; ++q_) {
+                const int jt = half * NJW + q_;
+                const f32x4 vr = ld4<TM>(&Vs[s * PV + jt * 16 + 4 * g]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xterm += acc[q_][e] * vr[e];
+            }
+        }
         // A tiles D[r][s] = sum_c Q[r][c] K[s][c] for query blocks rbk >= w
         f32x4 at[NRB];
 #pragma unroll
@@ -633,8 +666,19 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
     rterm += __shfl_xor(rterm, 16, 64);
     rterm += __shfl_xor(rterm, 32, 64);
     if (g == 0) RT[half][s] = rterm;
+    if constexpr (DECAY) {
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) xterm += __shfl_xor(xterm, off, 64);
+        if (lane == 0) XP[wv] = xterm;
+    }
     __syncthreads();  // also: every wave is done with this item's tiles
     if (DECAY && tid < C && tid < nv) a.rterm[(size_t)bh * L + t0 + tid] = RT[0][tid] + RT[1][tid];
+    if (DECAY && tid == 0) {
+        float x = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x += XP[i];
+        a.xterm[(size_t)bh * nchunks + c] = x;
+    }
     };
 
     int item = blockIdx.x;
@@ -648,44 +692,22 @@ __global__ void __launch_bounds__(512) bwd_dqkv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dl_t = sum_{u >= t} rterm_u + <dS_L, S_L>, one workgroup (256 threads) per head
+// dl_t = sum_{u >= t in t's chunk} rterm_u + <dH_c, H_{c+1}>: the gates of chunk c
+// reach the loss only through q_t e^{G_t}, k_t e^{-G_t} and the factor e^{g_C} of
+// the state the chunk hands on, so the suffix restarts at every chunk end (a
+// suffix over the whole sequence adds up the rounding of every later token's
+// term). One workgroup (256 threads) per head, one chunk per thread.
 template <int DK>
 __global__ void __launch_bounds__(256) dgate_kernel(BwdArgs a) {
-    constexpr int dk = DK;
-    __shared__ float part[256];
-    __shared__ float base;
-    const int tid = threadIdx.x, bh = blockIdx.x, L = a.L, dv = a.dv;
-    // <dS_L, S_L> over the head's dk x dv state
-    float acc = 0.f;
-    if (a.ds_out) {
-        const float *x = a.ds_out + (size_t)bh * dk * dv, *y = a.s_last + (size_t)bh * dk * dv;
-        for (int i = tid; i < dk * dv; i += 256) acc += x[i] * y[i];
-    }
-    part[tid] = acc;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if (tid < off) part[tid] += part[tid + off];
-        __syncthreads();
-    }
-    if (tid == 0) base = part[0];
-    __syncthreads();
-    // reverse scan: thread tid owns tokens [tid * per, (tid + 1) * per)
-    const int per = (L + 255) / 256;
-    const int b0 = min(L, tid * per), b1 = min(L, b0 + per);
+    const int bh = blockIdx.x, L = a.L, nchunks = (L + 63) / 64;
     const float *rt = a.rterm + (size_t)bh * L;
-    float tot = 0.f;
-    for (int t = b0; t < b1; ++t) tot += rt[t];
-    __syncthreads();
-    part[tid] = tot;
-    __syncthreads();
-    // exclusive suffix over the threads after this one
-    float after = 0.f;
-    for (int j = tid + 1; j < 256; ++j) after += part[j];
-    float run = base + after;
     float *dl = a.glg + (size_t)bh * L;
-    for (int t = b1 - 1; t >= b0; --t) {
-        run += rt[t];
-        dl[t] = run;
+    for (int c = threadIdx.x; c < nchunks; c += 256) {
+        float run = a.xterm[(size_t)bh * nchunks + c];
+        for (int t = min(L, 64 * c + 64) - 1; t >= 64 * c; --t) {
+            run += rt[t];
+            dl[t] = run;
+        }
     }
 }
 

@@ -90,6 +90,7 @@ struct BwdArgs {
     void *hs, *dhs;                // workspace: per-chunk states / state gradients [BH, nchunks, DK, dv] (operand type)
     float *s_last;                 // workspace: final state [BH, DK, dv]
     float *rterm;                  // workspace: q . dq - k . dk per token [BH, L]
+    float *xterm;                  // workspace (scalar decay): <dH_c, H_{c+1}> per chunk [BH, nchunks]
                                    // (gated delta rule: q . dq - v . dv)
     int BH, L, dv, nsplit;
     // gated delta rule only (gdn_bwd_impl.hpp); operand-type (fp16) workspace arrays

@@ -936,7 +936,12 @@ def pin_backward_gate_identity(lib):
     """The output and final state depend on the cumulative log-gates G only through
     differences G_r - G_s (and G_L for the final state), so
     dl_t = sum_{u >= t} (q_u . dq_u - k_u . dk_u) + <dS_L, S_L>, summed over the key
-    channel for the scalar gate and per channel for the vector gate."""
+    channel for the scalar gate and per channel for the vector gate. The gate of
+    token m multiplies only the state after token m - 1, so the sum may restart
+    there: for t < m, dl_t = sum_{t <= u < m} (q_u . dq_u - k_u . dk_u) + <dS_m, S_m>,
+    with S_m the state after the first m tokens and dS_m its gradient (from the
+    backward of the remaining tokens started from S_m) -- the form the kernels use
+    at every chunk end."""
     r = _rng(52)
     for variant in ("decay", "vector_decay"):
         q, k, v, do, lg, s0, dso = _bwd_case(r, variant, L=17)
@@ -951,6 +956,15 @@ def pin_backward_gate_identity(lib):
             tail = tail[:, None, :]
         ref = np.flip(np.cumsum(np.flip(per, 1), 1), 1) + tail
         assert _rel(dlg, ref) <= 1e-12, (variant, _rel(dlg, ref))
+        for m in (4, 8, 12):
+            _, sm, _ = oracle.forward(variant, q[:, :m], k[:, :m], v[:, :m], log_gate=lg[:, :m], state_in=s0,
+                                      lib=lib)
+            dsm = oracle.backward(variant, q[:, m:], k[:, m:], v[:, m:], do[:, m:], lg[:, m:], sm, dso,
+                                  lib=lib)[4]
+            head = (dsm * sm).sum(-1)                      # [B, dk]
+            head = head.sum(-1)[:, None] if variant == "decay" else head[:, None, :]
+            restart = np.flip(np.cumsum(np.flip(per[:, :m], 1), 1), 1) + head
+            assert _rel(dlg[:, :m], restart) <= 1e-12, (variant, m, _rel(dlg[:, :m], restart))
 
 
 def pin_backward_gdn_gate_identity(lib):
