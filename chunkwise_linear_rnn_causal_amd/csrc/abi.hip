@@ -1055,9 +1055,7 @@ la_status la_chunk_bwd(la_variant var, la_dtype dt, const void *q, const void *k
         const size_t nq = (size_t)BH * L * d_k, nv = (size_t)BH * L * d_v;
         float *q32 = up, *k32 = up + round_up(nq * 4, 256) / 4;
         float *v32 = k32 + round_up(nq * 4, 256) / 4, *o32 = v32 + round_up(nv * 4, 256) / 4;
-        if (launch_upcast(q, q32, nq, st) != hipSuccess || launch_upcast(k, k32, nq, st) != hipSuccess ||
-            launch_upcast(v, v32, nv, st) != hipSuccess || launch_upcast(d_o, o32, nv, st) != hipSuccess)
-            return LA_ERR_HIP;
+        if (launch_upcast4(q, k, v, d_o, q32, k32, v32, o32, nq, nv, st) != hipSuccess) return LA_ERR_HIP;
         q = q32; k = k32; v = v32; d_o = o32;
         a.q = q; a.k = k; a.v = v; a.dout = d_o;
         idt = LA_F32;

@@ -145,20 +145,43 @@ __global__ void __launch_bounds__(DK) norm_apply_kernel(NormArgs a) {
 }
 
 // bf16 -> fp32 copy (the normalized backward computes on fp32 operands)
+// q, k, v and dO widened to fp32 in one launch: blockIdx.y picks the tensor.
+// Each thread takes U groups of 8 elements a grid stride apart and issues all
+// its loads before its stores.
+struct UpcastArgs {
+    const bf16 *x[4];
+    float *y[4];
+    size_t n8[4];
+};
+
 template <int UNUSED = 0>
-__global__ void __launch_bounds__(256) upcast_bf16_kernel(const bf16 *x, float *y, size_t n8) {
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (size_t)gridDim.x * 256) {
-        float v[8];
-        ld8<bf16>(x + i * 8, v);
-        st8<float>(y + i * 8, v);
+__global__ void __launch_bounds__(256) upcast_bf16_kernel(UpcastArgs a) {
+    constexpr int U = 4;
+    const int t = blockIdx.y;
+    const bf16 *x = a.x[t];
+    float *y = a.y[t];
+    const size_t n8 = a.n8[t], stride = (size_t)gridDim.x * 256;
+    for (size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x; i0 < n8; i0 += U * stride) {
+        float v[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * stride < n8) ld8<bf16>(x + (i0 + u * stride) * 8, v[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * stride < n8) st8<float>(y + (i0 + u * stride) * 8, v[u]);
     }
 }
 
-inline hipError_t launch_upcast(const void *x, float *y, size_t n, hipStream_t st) {
-    const size_t n8 = n / 8;  // n is a multiple of 8 (d_k, d_v are)
+// nq elements each of q and k, nv each of v and dO (multiples of 8: d_k and d_v are)
+inline hipError_t launch_upcast4(const void *q, const void *k, const void *v, const void *d_o, float *q32,
+                                 float *k32, float *v32, float *o32, size_t nq, size_t nv, hipStream_t st) {
+    UpcastArgs a{{(const bf16 *)q, (const bf16 *)k, (const bf16 *)v, (const bf16 *)d_o},
+                 {q32, k32, v32, o32},
+                 {nq / 8, nq / 8, nv / 8, nv / 8}};
+    const size_t n8 = std::max(nq, nv) / 8;
     if (n8 == 0) return hipSuccess;
-    const unsigned blocks = (unsigned)std::min<size_t>((n8 + 255) / 256, 4096);
-    hipLaunchKernelGGL(upcast_bf16_kernel<>, dim3(blocks), dim3(256), 0, st, (const bf16 *)x, y, n8);
+    const unsigned blocks = (unsigned)std::min<size_t>((n8 + 255) / 256, 2048);
+    hipLaunchKernelGGL(upcast_bf16_kernel<>, dim3(blocks, 4), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
