@@ -213,15 +213,16 @@ def bwd_wsize(var=DECAY, dt=BF16, B=2, H=3, L=100, dk_=64, dv_=32, C=64):
 
 
 def test_bwd_workspace_size():
-    # per-chunk states and state gradients (fp16 operands for bf16), final state, one float per token
+    # per-chunk states and state gradients (fp16 operands for bf16), final state, one float per
+    # token, one float per chunk (<dH_c, H_{c+1}>, where the gate gradient's suffix restarts)
     st, n = bwd_wsize()
     r = lambda x: -(-x // 256) * 256
     states = r(6 * 2 * 64 * 32 * 2)
-    assert st == 0 and n == 2 * states + r(6 * 64 * 32 * 4) + r(6 * 100 * 4)
+    base = 2 * states + r(6 * 64 * 32 * 4) + r(6 * 100 * 4) + r(6 * 2 * 4)
+    assert st == 0 and n == base
     # delta rule (bf16 only): also W [BH, Lp, dk], U~ and A_m^T dO [BH, Lp, dv] and T [BH, nch, 64, 64], fp16
     st, n = bwd_wsize(var=GDN)
-    assert st == 0 and n == (2 * states + r(6 * 64 * 32 * 4) + r(6 * 100 * 4) + r(6 * 128 * 64 * 2)
-                             + 2 * r(6 * 128 * 32 * 2) + r(6 * 2 * 64 * 64 * 2))
+    assert st == 0 and n == base + r(6 * 128 * 64 * 2) + 2 * r(6 * 128 * 32 * 2) + r(6 * 2 * 64 * 64 * 2)
     assert bwd_wsize(var=GDN, dt=F32)[0] == UNSUPPORTED
     # per-channel decay (bf16 only): the decay layout
     assert bwd_wsize(var=VDECAY) == bwd_wsize()
@@ -230,7 +231,7 @@ def test_bwd_workspace_size():
     # (fp32 operands: fp32 states, and for bf16 inputs fp32 copies of q, k, v, d_o)
     st, n = bwd_wsize(var=NORM)
     states32 = r(6 * 2 * 64 * 32 * 4)
-    assert st == 0 and n == (2 * states32 + r(6 * 64 * 32 * 4) + r(6 * 100 * 4) + r(6 * 100 * 32 * 4)
+    assert st == 0 and n == (2 * states32 + r(6 * 64 * 32 * 4) + r(6 * 100 * 4) + r(6 * 2 * 4) + r(6 * 100 * 32 * 4)
                              + 3 * r(6 * 100 * 4) + 2 * r(6 * 2 * 64 * 4)
                              + 2 * r(6 * 100 * 64 * 4) + 2 * r(6 * 100 * 32 * 4))
     assert bwd_wsize(var=NORM, dk_=128, dv_=128)[0] == UNSUPPORTED
