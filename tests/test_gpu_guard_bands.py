@@ -177,3 +177,34 @@ def test_short_conv_writes_stay_in_bounds(L):
         outs[i].check(f"conv out {i}")
         wouts[i].check(f"conv window {i}")
         assert torch.equal(outs[i].view, ref[i]) and torch.equal(wouts[i].view, ref[3 + i])
+
+
+@pytest.mark.parametrize("L", [17, 65, 147])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_conv_fused_forward_writes_stay_in_bounds(L, odt):
+    """The delta rule with the short convolution fused: o, the state, the three
+    carried windows and the workspace, each between guard bands."""
+    from test_gpu_conv_fused import _case
+    B, H, d, K = 1, 3, 128, 4
+    print(f"[guard] conv-fused L{L} o={odt}", flush=True)
+    inp, taps, wins, lg = _case(B, H, L, d, d, K, 75, windows=True, gate=True, state=True)
+    args = [dev(x) for x in (inp.q, inp.k, inp.v)] + [dev(t) for t in taps] + [dev(lg), dev(inp.beta),
+                                                                             dev(inp.state_in)]
+    win_in = dict(q_win_in=dev(wins[0]), k_win_in=dev(wins[1]), v_win_in=dev(wins[2]))
+    o = Guarded((B, H, L, d), odt)
+    s = Guarded((B, H, d, d), torch.float32)
+    wo = [Guarded((B, H, K - 1, d), torch.bfloat16) for _ in range(3)]
+    ws_bytes = la.la_chunk_fwd_conv_workspace_size("gated_delta", 1, B, H, L, d, d, 64, K)
+    ws = Guarded((ws_bytes,), torch.uint8) if ws_bytes else None
+    la.la_chunk_fwd_conv("gated_delta", *args, **win_in, o=o.view, state_out=s.view,
+                         q_win_out=wo[0].view, k_win_out=wo[1].view, v_win_out=wo[2].view,
+                         workspace=ws.view if ws else None)
+    ref_o, ref_s, ref_w = la.la_chunk_fwd_conv("gated_delta", *args, **win_in, out_dtype=odt, want_state=True,
+                                               want_windows=True)
+    torch.cuda.synchronize()
+    for g, what in [(o, "o"), (s, "state_out"), (ws, "workspace")] + [(w, f"window {i}") for i, w in enumerate(wo)]:
+        if g is not None:
+            g.check(f"conv-fused {what}")
+    assert torch.equal(o.view, ref_o) and torch.equal(s.view, ref_s)
+    for i in range(3):
+        assert torch.equal(wo[i].view, ref_w[i])
