@@ -208,3 +208,28 @@ def test_conv_fused_forward_writes_stay_in_bounds(L, odt):
     assert torch.equal(o.view, ref_o) and torch.equal(s.view, ref_s)
     for i in range(3):
         assert torch.equal(wo[i].view, ref_w[i])
+
+
+@pytest.mark.parametrize("var", ["decay", "gated_delta", "normalized"])
+@pytest.mark.parametrize("L", [17, 147])
+def test_noalloc_forward_writes_stay_in_bounds(var, L):
+    """The allocation-free forward: its outputs between guard bands, the same bits
+    as the forward with a caller workspace."""
+    B, H, d = 1, 3, 128 if var != "normalized" else 64
+    print(f"[guard] noalloc {var} L{L}", flush=True)
+    inp = W.make_chunk_inputs(var, "bf16", B, H, L, d, d, seed=76, with_state=True, with_z=(var == "normalized"))
+    args = [dev(x) for x in (inp.q, inp.k, inp.v, inp.log_gate, inp.beta, inp.state_in)]
+    z_in = dev(inp.z_in) if var == "normalized" else None
+    o = Guarded((B, H, L, d), torch.float32)
+    s = Guarded((B, H, d, d), torch.float32)
+    z = Guarded((B, H, d), torch.float32) if var == "normalized" else None
+    la.la_chunk_fwd_noalloc(var, *args, z_in, o=o.view, state_out=s.view, z_out=z.view if z else None)
+    ref_o, ref_s, ref_z = la.la_chunk_fwd(var, *args, z_in, out_dtype=torch.float32, want_state=True,
+                                          want_z=z is not None)
+    torch.cuda.synchronize()
+    for g, what in ((o, "o"), (s, "state_out"), (z, "z_out")):
+        if g is not None:
+            g.check(f"noalloc {var} {what}")
+    assert torch.equal(o.view, ref_o) and torch.equal(s.view, ref_s)
+    if z is not None:
+        assert torch.equal(z.view, ref_z)
