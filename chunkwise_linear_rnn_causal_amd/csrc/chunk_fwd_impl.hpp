@@ -1248,6 +1248,9 @@ __global__ void __launch_bounds__(NW * 64) chunk_fwd_kernel(ChunkArgs a) {
                     }
                 }
             } else {
+                // The staging waves issue ahead of the row waves that share their
+                // SIMDs: their loads and the state update feed the next chunk.
+                __builtin_amdgcn_s_setprio(1);
                 // chunks 0 .. NPS-1 into register sets 0 .. NPS-1; gate tables
                 // of chunks 0 and 1; chunk 0 staged and chunk NPS into set 0
                 if (nchunks > 0) {
